@@ -1,0 +1,200 @@
+"""CPU oracle for CondConv-style dynamic convolution (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (the HIP library and
+its Python binding) never imports, links or calls it, and this package
+imports nothing from the product.
+
+The arithmetic lives in ``dynconv_oracle.c`` (plain C, double precision,
+OpenMP over independent outputs). This module only builds that file with the
+host compiler, loads it with ctypes and marshals numpy arrays. Each function
+cites the passage of the pages it follows:
+
+* routing - global average pool, FC with bias, sigmoid or softmax(z/T):
+  "input-dependent attentions" (KernelWarehouse: Rethinking the Design of
+  Dynamic Convolution, abstract) and "temperature-degraded kernel attention"
+  (FMDConv: Fast multi-attention dynamic convolution, abstract). The pages
+  give no formula for the router; the plainest reading is used.
+* mixing - W_b = sum_i alpha_bi E_i: "a linear mixture of n static kernels
+  weighted with their input-dependent attentions" (KernelWarehouse, abstract).
+* convolution - one ordinary convolution per example with its own kernel:
+  "specialized convolutional kernels for each example" (CondConv:
+  Conditionally Parameterized Convolutions, abstract).
+
+Parity pins live in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dynconv_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+SIGMOID = 0
+SOFTMAX = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with the host C compiler (gcc, OpenMP)."""
+    if not force and os.path.exists(_LIB_PATH) and (
+        os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC)
+    ):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int
+    i64 = ctypes.c_long
+    lib.oracle_threads.restype = i32
+    lib.oracle_gap.argtypes = [i32, i32, i32, i32, P, P]
+    lib.oracle_route.argtypes = [i32, i32, i32, i32, i32, P, P, P, i32,
+                                 ctypes.c_double, P, P, P]
+    lib.oracle_mix.argtypes = [i32, i32, i64, P, P, P]
+    lib.oracle_conv.argtypes = [i32] * 10 + [P, P, P]
+    lib.oracle_forward.argtypes = [i32] * 11 + [P, P, P, P]
+    lib.oracle_forward_points.argtypes = [i32] * 11 + [P, P, P, i64, P, P]
+    for f in (lib.oracle_gap, lib.oracle_route, lib.oracle_mix, lib.oracle_conv,
+              lib.oracle_forward, lib.oracle_forward_points):
+        f.restype = i32
+    _lib = lib
+    return lib
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid arguments (rc={rc})")
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_threads())
+
+
+def out_size(n: int, k: int, stride: int, pad: int) -> int:
+    if stride < 1 or pad < 0:
+        raise ValueError("oracle: stride must be >= 1 and pad >= 0")
+    return (n + 2 * pad - k) // stride + 1
+
+
+def gap(x) -> np.ndarray:
+    """Global average pool over H, W of x[B, C, H, W] (float64 result)."""
+    x = _f32(x)
+    B, C, H, W = x.shape
+    out = np.empty((B, C), np.float64)
+    _check(_load().oracle_gap(B, C, H, W, _ptr(x), _ptr(out)), "gap")
+    return out
+
+
+def route(x, fc_w, fc_b=None, mode: int = SIGMOID, temperature: float = 1.0):
+    """Attentions alpha[B, n] from GAP -> FC(+bias) -> sigmoid | softmax(z/T).
+
+    Returns (alpha, gap, z), all float64.
+    """
+    x = _f32(x)
+    fc_w = _f32(fc_w)
+    B, C, H, W = x.shape
+    n = fc_w.shape[0]
+    assert fc_w.shape == (n, C)
+    fb = None if fc_b is None else _f32(fc_b)
+    if fb is not None:
+        assert fb.shape == (n,)
+    alpha = np.empty((B, n), np.float64)
+    g = np.empty((B, C), np.float64)
+    z = np.empty((B, n), np.float64)
+    rc = _load().oracle_route(B, C, H, W, n, _ptr(x), _ptr(fc_w),
+                              None if fb is None else _ptr(fb), int(mode),
+                              float(temperature), _ptr(g), _ptr(z), _ptr(alpha))
+    _check(rc, "route")
+    return alpha, g, z
+
+
+def mix(alpha, experts) -> np.ndarray:
+    """W_b = sum_i alpha[b, i] * E_i for experts[n, ...]; result [B, ...] float64."""
+    alpha = _f64(alpha)
+    experts = _f32(experts)
+    B, n = alpha.shape
+    assert experts.shape[0] == n
+    wsize = int(np.prod(experts.shape[1:]))
+    out = np.empty((B,) + experts.shape[1:], np.float64)
+    _check(_load().oracle_mix(B, n, wsize, _ptr(alpha), _ptr(experts), _ptr(out)), "mix")
+    return out
+
+
+def conv(x, wb, stride: int = 1, pad: int = 0, groups: int = 1) -> np.ndarray:
+    """Per-example convolution of x[B, Cin, H, W] with wb[B, Cout, Cin/g, kh, kw]."""
+    x = _f32(x)
+    wb = _f64(wb)
+    B, Cin, H, W = x.shape
+    _, Cout, cpg, kh, kw = wb.shape
+    assert wb.shape[0] == B and cpg * groups == Cin
+    Ho, Wo = out_size(H, kh, stride, pad), out_size(W, kw, stride, pad)
+    y = np.empty((B, Cout, Ho, Wo), np.float64)
+    rc = _load().oracle_conv(B, Cin, H, W, Cout, kh, kw, stride, pad, groups,
+                             _ptr(x), _ptr(wb), _ptr(y))
+    _check(rc, "conv")
+    return y
+
+
+def forward(x, experts, alpha, stride: int = 1, pad: int = 0, groups: int = 1) -> np.ndarray:
+    """The dynamic convolution layer for given attentions (mix, then convolve)."""
+    x = _f32(x)
+    experts = _f32(experts)
+    alpha = _f64(alpha)
+    B, Cin, H, W = x.shape
+    n, Cout, cpg, kh, kw = experts.shape
+    assert alpha.shape == (B, n) and cpg * groups == Cin
+    Ho, Wo = out_size(H, kh, stride, pad), out_size(W, kw, stride, pad)
+    y = np.empty((B, Cout, Ho, Wo), np.float64)
+    rc = _load().oracle_forward(B, Cin, H, W, Cout, kh, kw, stride, pad, groups, n,
+                                _ptr(x), _ptr(experts), _ptr(alpha), _ptr(y))
+    _check(rc, "forward")
+    return y
+
+
+def forward_points(x, experts, alpha, idx, stride: int = 1, pad: int = 0,
+                   groups: int = 1) -> np.ndarray:
+    """Selected outputs y[b, o, r, s] of the layer; idx is an int array [m, 4]."""
+    x = _f32(x)
+    experts = _f32(experts)
+    alpha = _f64(alpha)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32).reshape(-1, 4))
+    B, Cin, H, W = x.shape
+    n, Cout, cpg, kh, kw = experts.shape
+    assert alpha.shape == (B, n) and cpg * groups == Cin
+    out = np.empty(idx.shape[0], np.float64)
+    rc = _load().oracle_forward_points(B, Cin, H, W, Cout, kh, kw, stride, pad, groups,
+                                       n, _ptr(x), _ptr(experts), _ptr(alpha),
+                                       idx.shape[0], _ptr(idx), _ptr(out))
+    _check(rc, "forward_points")
+    return out
