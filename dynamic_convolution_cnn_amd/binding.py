@@ -1,0 +1,220 @@
+"""ctypes binding of libdynconv.so (the C ABI in include/dynconv.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+The library is loaded on first use; if it is missing this module raises
+(there is no CPU fallback).
+
+The functions carry the C entry points' names. Tensors must be contiguous,
+on the GPU, bf16 or float32 (attentions and router weights float32).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdynconv.so")
+
+DYNCONV_OK = 0
+DYNCONV_ERR_INVALID_ARG = 1
+DYNCONV_ERR_UNSUPPORTED = 2
+DYNCONV_ERR_WORKSPACE = 3
+DYNCONV_ERR_HIP = 4
+
+DYNCONV_F32 = 0
+DYNCONV_BF16 = 1
+
+DYNCONV_SIGMOID = 0
+DYNCONV_SOFTMAX = 1
+
+DYNCONV_POLICY_AUTO = 0
+DYNCONV_POLICY_PREMIX = 1
+DYNCONV_POLICY_FUSED = 2
+
+# Every symbol include/dynconv.h declares.
+EXPORTED = (
+    "dynconv_route", "dynconv_route_workspace_bytes", "dynconv_mix", "dynconv_forward",
+    "dynconv_forward_workspace_bytes", "dynconv_forward_policy", "dynconv_status_string",
+    "dynconv_last_error", "dynconv_abi_version",
+)
+
+
+class dynconv_desc_t(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("B", "Cin", "H", "W", "Cout", "kh", "kw", "stride", "pad", "groups", "n",
+                 "dtype")]
+
+
+class DynconvError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {status_string(status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library with typed entry points (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m dynamic_convolution_cnn_amd.build` "
+            "(the dynamic convolution has no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(dynconv_desc_t)
+    i32, f32, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.dynconv_route.argtypes = [D, P, P, P, i32, f32, P, P, sz, P]
+    L.dynconv_route.restype = i32
+    L.dynconv_route_workspace_bytes.argtypes = [D]
+    L.dynconv_route_workspace_bytes.restype = sz
+    L.dynconv_mix.argtypes = [D, P, P, P, P]
+    L.dynconv_mix.restype = i32
+    L.dynconv_forward.argtypes = [D, i32, P, P, P, P, P, sz, P]
+    L.dynconv_forward.restype = i32
+    L.dynconv_forward_workspace_bytes.argtypes = [D, i32]
+    L.dynconv_forward_workspace_bytes.restype = sz
+    L.dynconv_forward_policy.argtypes = [D]
+    L.dynconv_forward_policy.restype = i32
+    L.dynconv_status_string.argtypes = [i32]
+    L.dynconv_status_string.restype = ctypes.c_char_p
+    L.dynconv_last_error.argtypes = []
+    L.dynconv_last_error.restype = ctypes.c_char_p
+    L.dynconv_abi_version.argtypes = []
+    L.dynconv_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().dynconv_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().dynconv_last_error().decode()
+
+
+def make_desc(B, Cin, H, W, Cout=1, kh=1, kw=1, stride=1, pad=0, groups=1, n=1,
+              dtype=DYNCONV_BF16) -> dynconv_desc_t:
+    return dynconv_desc_t(B, Cin, H, W, Cout, kh, kw, stride, pad, groups, n, dtype)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DYNCONV_BF16
+    if t.dtype == torch.float32:
+        return DYNCONV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != DYNCONV_OK:
+        raise DynconvError(status, where, last_error())
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return given, 0
+    if given is not None:
+        return given, given.numel() * given.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def layer_desc(x: torch.Tensor, experts: torch.Tensor, stride: int, pad: int,
+               groups: int) -> dynconv_desc_t:
+    B, Cin, H, W = x.shape
+    n, Cout, cpg, kh, kw = experts.shape
+    return make_desc(B, Cin, H, W, Cout, kh, kw, stride, pad, groups, n, _dtype_code(x))
+
+
+def dynconv_route_workspace_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_route_workspace_bytes(ctypes.byref(desc)))
+
+
+def dynconv_forward_workspace_bytes(desc: dynconv_desc_t, policy: int = DYNCONV_POLICY_AUTO) -> int:
+    return int(lib().dynconv_forward_workspace_bytes(ctypes.byref(desc), int(policy)))
+
+
+def dynconv_forward_policy(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_forward_policy(ctypes.byref(desc)))
+
+
+def dynconv_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def dynconv_last_error() -> str:
+    return last_error()
+
+
+def dynconv_abi_version() -> int:
+    return int(lib().dynconv_abi_version())
+
+
+def dynconv_route(x: torch.Tensor, fc_w: torch.Tensor, fc_b: Optional[torch.Tensor],
+                  mode: int = DYNCONV_SIGMOID, temperature: float = 1.0,
+                  alpha: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """alpha[B, n] (float32) from GAP -> FC(+bias) -> sigmoid | softmax(z / T)."""
+    B, Cin, H, W = x.shape
+    n = fc_w.shape[0]
+    desc = make_desc(B, Cin, H, W, n=n, dtype=_dtype_code(x))
+    if alpha is None:
+        alpha = torch.empty((B, n), dtype=torch.float32, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_route_workspace_bytes(desc), x.device, workspace)
+    _check(lib().dynconv_route(ctypes.byref(desc), _ptr(x), _ptr(fc_w), _ptr(fc_b), int(mode),
+                               float(temperature), _ptr(alpha), _ptr(ws), ws_bytes,
+                               _stream(stream)), "dynconv_route")
+    return alpha
+
+
+def dynconv_mix(alpha: torch.Tensor, experts: torch.Tensor, groups: int = 1,
+                mixed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mixed[b] = sum_i alpha[b, i] experts[i]; experts [n, Cout, Cin/g, kh, kw]."""
+    B = alpha.shape[0]
+    n, Cout, cpg, kh, kw = experts.shape
+    # H = W = kh, kw-sized input keeps the descriptor valid; mixing reads only the kernel shape
+    desc = make_desc(B, cpg * groups, kh, kw, Cout, kh, kw, 1, 0, groups, n, _dtype_code(experts))
+    if mixed is None:
+        mixed = torch.empty((B, Cout, cpg, kh, kw), dtype=experts.dtype, device=experts.device)
+    _check(lib().dynconv_mix(ctypes.byref(desc), _ptr(alpha), _ptr(experts), _ptr(mixed),
+                             _stream(stream)), "dynconv_mix")
+    return mixed
+
+
+def dynconv_forward(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
+                    stride: int = 1, pad: int = 0, groups: int = 1,
+                    policy: int = DYNCONV_POLICY_AUTO, y: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[b] = conv(x[b], sum_i alpha[b, i] experts[i]) for every example."""
+    desc = layer_desc(x, experts, stride, pad, groups)
+    Ho = (desc.H + 2 * pad - desc.kh) // stride + 1
+    Wo = (desc.W + 2 * pad - desc.kw) // stride + 1
+    if y is None:
+        y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_forward_workspace_bytes(desc, policy), x.device, workspace)
+    _check(lib().dynconv_forward(ctypes.byref(desc), int(policy), _ptr(x), _ptr(experts),
+                                 _ptr(alpha), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "dynconv_forward")
+    return y

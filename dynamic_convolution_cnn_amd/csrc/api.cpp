@@ -1,0 +1,282 @@
+// Host side of the C ABI declared in include/dynconv.h: argument checks,
+// path selection, workspace carving and kernel dispatch. Every check runs
+// before the first HIP call, so an invalid call touches neither the device
+// nor any output (and needs no GPU at all).
+#include "dynconv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dynconv_status_t fail(dynconv_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dynconv_status_t ok() {
+    g_err[0] = '\0';
+    return DYNCONV_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr long kMaxElems = (1L << 31) - 1;  // per tensor
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Shape checks shared by every entry point. On success fills `g`.
+dynconv_status_t check_desc(const dynconv_desc_t *d, dynconv::Geom &g, bool need_conv) {
+    if (!d) return fail(DYNCONV_ERR_INVALID_ARG, "desc is NULL");
+    if (d->B < 1 || d->Cin < 1 || d->H < 1 || d->W < 1 || d->n < 1)
+        return fail(DYNCONV_ERR_INVALID_ARG, "B, Cin, H, W and n must be >= 1 (got B=%d Cin=%d H=%d W=%d n=%d)",
+                    d->B, d->Cin, d->H, d->W, d->n);
+    if (d->dtype != DYNCONV_F32 && d->dtype != DYNCONV_BF16)
+        return fail(DYNCONV_ERR_INVALID_ARG, "dtype %d is not a dynconv_dtype_t", d->dtype);
+    g = dynconv::Geom{};
+    g.B = d->B; g.Cin = d->Cin; g.H = d->H; g.W = d->W; g.n = d->n;
+    g.bf16 = d->dtype == DYNCONV_BF16;
+    if ((long)d->B * d->Cin * d->H * d->W > kMaxElems)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "x has more than 2^31-1 elements");
+    g.n_pad = (d->n + 1) & ~1;
+    g.Cin_pad = (d->Cin + 31) / 32 * 32;
+    if (!need_conv) return DYNCONV_OK;
+    if (d->Cout < 1 || d->kh < 1 || d->kw < 1 || d->stride < 1 || d->pad < 0 || d->groups < 1)
+        return fail(DYNCONV_ERR_INVALID_ARG,
+                    "Cout, kh, kw, stride, groups must be >= 1 and pad >= 0 (got Cout=%d kh=%d kw=%d stride=%d pad=%d groups=%d)",
+                    d->Cout, d->kh, d->kw, d->stride, d->pad, d->groups);
+    if (d->Cin % d->groups || d->Cout % d->groups)
+        return fail(DYNCONV_ERR_INVALID_ARG, "groups=%d must divide Cin=%d and Cout=%d", d->groups,
+                    d->Cin, d->Cout);
+    const long Ho = ((long)d->H + 2L * d->pad - d->kh) / d->stride + 1;
+    const long Wo = ((long)d->W + 2L * d->pad - d->kw) / d->stride + 1;
+    if ((long)d->H + 2L * d->pad < d->kh || (long)d->W + 2L * d->pad < d->kw || Ho < 1 || Wo < 1)
+        return fail(DYNCONV_ERR_INVALID_ARG, "kernel %dx%d larger than padded input %dx%d", d->kh,
+                    d->kw, d->H + 2 * d->pad, d->W + 2 * d->pad);
+    if (d->groups != 1 && !(d->groups == d->Cin && d->Cin == d->Cout))
+        return fail(DYNCONV_ERR_UNSUPPORTED,
+                    "groups=%d: only groups == 1 or depthwise (groups == Cin == Cout) are implemented",
+                    d->groups);
+    if ((long)d->B * d->Cout * Ho * Wo > kMaxElems)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "y has more than 2^31-1 elements");
+    const long wsize = (long)d->Cout * (d->Cin / d->groups) * d->kh * d->kw;
+    if (wsize * d->n > kMaxElems || wsize * d->B > kMaxElems)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "expert bank or mixed kernels exceed 2^31-1 elements");
+    g.Cout = d->Cout; g.KH = d->kh; g.KW = d->kw; g.stride = d->stride; g.pad = d->pad;
+    g.groups = d->groups;
+    g.Ho = (int)Ho; g.Wo = (int)Wo; g.P = (int)(Ho * Wo); g.KT = d->kh * d->kw;
+    g.cpg = d->Cin / d->groups;
+    return DYNCONV_OK;
+}
+
+long kernel_elems(const dynconv::Geom &g) { return (long)g.Cout * g.cpg * g.KT; }
+size_t esize(const dynconv::Geom &g) { return g.bf16 ? 2 : 4; }
+bool depthwise(const dynconv::Geom &g) { return g.groups != 1; }
+
+// Resolve AUTO and check that the chosen path exists for this layer.
+dynconv_status_t resolve_policy(const dynconv::Geom &g, int32_t policy, int32_t &out) {
+    if (policy != DYNCONV_POLICY_AUTO && policy != DYNCONV_POLICY_PREMIX &&
+        policy != DYNCONV_POLICY_FUSED)
+        return fail(DYNCONV_ERR_INVALID_ARG, "policy %d is not a dynconv_policy_t", policy);
+    if (depthwise(g)) {
+        if (!dynconv::depthwise_supported(g))
+            return fail(DYNCONV_ERR_UNSUPPORTED,
+                        "depthwise layer: kernel taps must be <= 64 and the padded plane must fit in 64 KB of LDS");
+        out = policy == DYNCONV_POLICY_AUTO ? DYNCONV_POLICY_FUSED : policy;
+        return DYNCONV_OK;
+    }
+    if (!g.bf16) {
+        if (policy == DYNCONV_POLICY_FUSED)
+            return fail(DYNCONV_ERR_UNSUPPORTED, "float32 layers have no fused path");
+        out = DYNCONV_POLICY_PREMIX;
+        return DYNCONV_OK;
+    }
+    if (g.n_pad > 16)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "bf16 layers with groups == 1 support n <= 16 experts (got %d)", g.n);
+    const bool fused_ok = dynconv::fused_conv_supported(g);
+    const bool premix_ok = dynconv::premix_conv_supported(g);
+    if (policy == DYNCONV_POLICY_FUSED) {
+        if (!fused_ok)
+            return fail(DYNCONV_ERR_UNSUPPORTED,
+                        "fused path needs Ho*Wo <= 208 and the 4 example tiles in LDS (Ho*Wo=%d)", g.P);
+        out = policy;
+        return DYNCONV_OK;
+    }
+    if (policy == DYNCONV_POLICY_PREMIX) {
+        if (!premix_ok)
+            return fail(DYNCONV_ERR_UNSUPPORTED, "premix path: input row band does not fit in LDS");
+        out = policy;
+        return DYNCONV_OK;
+    }
+    // AUTO: fuse when one example's mixed kernel is at least its input plus output.
+    const long wb_bytes = kernel_elems(g) * (long)esize(g);
+    const long xy_bytes = ((long)g.Cin * g.H * g.W + (long)g.Cout * g.P) * (long)esize(g);
+    if (fused_ok && wb_bytes >= xy_bytes) out = DYNCONV_POLICY_FUSED;
+    else if (premix_ok) out = DYNCONV_POLICY_PREMIX;
+    else if (fused_ok) out = DYNCONV_POLICY_FUSED;
+    else return fail(DYNCONV_ERR_UNSUPPORTED, "no convolution path fits this layer in LDS");
+    return DYNCONV_OK;
+}
+
+// Workspace of the resolved policy; pieces are 256-byte aligned.
+size_t forward_ws(const dynconv::Geom &g, int32_t policy) {
+    if (depthwise(g))
+        return policy == DYNCONV_POLICY_PREMIX ? round_up((size_t)g.B * kernel_elems(g) * esize(g), kWsAlign) : 0;
+    if (!g.bf16) return round_up((size_t)g.B * kernel_elems(g) * sizeof(float), kWsAlign);
+    size_t ws = round_up(dynconv::packed_experts_bytes(g), kWsAlign);
+    if (policy == DYNCONV_POLICY_PREMIX) ws += round_up(dynconv::premixed_bytes(g), kWsAlign);
+    return ws;
+}
+
+dynconv_status_t hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(DYNCONV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dynconv_abi_version(void) { return 1; }
+
+const char *dynconv_status_string(dynconv_status_t s) {
+    switch (s) {
+    case DYNCONV_OK: return "ok";
+    case DYNCONV_ERR_INVALID_ARG: return "invalid argument";
+    case DYNCONV_ERR_UNSUPPORTED: return "unsupported layer";
+    case DYNCONV_ERR_WORKSPACE: return "workspace missing or too small";
+    case DYNCONV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *dynconv_last_error(void) { return g_err; }
+
+size_t dynconv_route_workspace_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, false) != DYNCONV_OK) return 0;
+    return round_up((size_t)g.B * g.Cin * sizeof(float), kWsAlign);
+}
+
+dynconv_status_t dynconv_route(const dynconv_desc_t *desc, const void *x, const float *fc_w,
+                               const float *fc_b, int32_t mode, float temperature, float *alpha,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, false);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !fc_w || !alpha)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, fc_w and alpha must not be NULL");
+    if (!aligned16(x) || !aligned16(fc_w) || !aligned16(alpha) || (fc_b && !aligned16(fc_b)))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (mode != DYNCONV_SIGMOID && mode != DYNCONV_SOFTMAX)
+        return fail(DYNCONV_ERR_INVALID_ARG, "mode %d is not a dynconv_route_mode_t", mode);
+    if (mode == DYNCONV_SOFTMAX && !(temperature > 0.f && std::isfinite(temperature)))
+        return fail(DYNCONV_ERR_INVALID_ARG, "softmax temperature must be finite and > 0");
+    if (g.n > 256) return fail(DYNCONV_ERR_UNSUPPORTED, "routing supports n <= 256 experts (got %d)", g.n);
+    const size_t need = dynconv_route_workspace_bytes(desc);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE, "route needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(dynconv::launch_route(g, x, fc_w, fc_b, mode, temperature,
+                                            static_cast<float *>(workspace), alpha, st),
+                      "dynconv_route launch");
+}
+
+dynconv_status_t dynconv_mix(const dynconv_desc_t *desc, const float *alpha, const void *experts,
+                             void *mixed, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!alpha || !experts || !mixed)
+        return fail(DYNCONV_ERR_INVALID_ARG, "alpha, experts and mixed must not be NULL");
+    if (!aligned16(alpha) || !aligned16(experts) || !aligned16(mixed))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, mixed, st),
+                      "dynconv_mix launch");
+}
+
+int32_t dynconv_forward_policy(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK) return -1;
+    int32_t p;
+    if (resolve_policy(g, DYNCONV_POLICY_AUTO, p) != DYNCONV_OK) return -1;
+    return p;
+}
+
+size_t dynconv_forward_workspace_bytes(const dynconv_desc_t *desc, int32_t policy) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK) return 0;
+    int32_t p;
+    if (resolve_policy(g, policy, p) != DYNCONV_OK) return 0;
+    return forward_ws(g, p);
+}
+
+dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy, const void *x,
+                                 const void *experts, const float *alpha, void *y,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !experts || !alpha || !y)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, experts, alpha and y must not be NULL");
+    if (!aligned16(x) || !aligned16(experts) || !aligned16(alpha) || !aligned16(y))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    int32_t p;
+    s = resolve_policy(g, policy, p);
+    if (s != DYNCONV_OK) return s;
+    const size_t need = forward_ws(g, p);
+    if (need > 0 && (workspace_bytes < need || !workspace || !aligned16(workspace)))
+        return fail(DYNCONV_ERR_WORKSPACE, "forward needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    hipError_t e;
+    if (depthwise(g)) {
+        const void *wm = nullptr;
+        if (p == DYNCONV_POLICY_PREMIX) {
+            e = dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, ws, st);
+            if (e != hipSuccess) return hip_status(e, "dynconv_forward mix launch");
+            wm = ws;
+        }
+        return hip_status(dynconv::launch_conv_depthwise(g, x, experts, alpha, wm, y, st),
+                          "dynconv_forward depthwise launch");
+    }
+    if (!g.bf16) {
+        e = dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, ws, st);
+        if (e != hipSuccess) return hip_status(e, "dynconv_forward mix launch");
+        return hip_status(dynconv::launch_conv_direct_f32(g, static_cast<const float *>(x),
+                                                          reinterpret_cast<const float *>(ws),
+                                                          static_cast<float *>(y), st),
+                          "dynconv_forward conv launch");
+    }
+    uint16_t *packed = reinterpret_cast<uint16_t *>(ws);
+    e = dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), packed, st);
+    if (e != hipSuccess) return hip_status(e, "dynconv_forward pack launch");
+    if (p == DYNCONV_POLICY_FUSED)
+        return hip_status(dynconv::launch_conv_fused(g, static_cast<const uint16_t *>(x), packed,
+                                                     alpha, static_cast<uint16_t *>(y), st),
+                          "dynconv_forward fused launch");
+    uint16_t *wt = reinterpret_cast<uint16_t *>(ws + round_up(dynconv::packed_experts_bytes(g), kWsAlign));
+    e = dynconv::launch_premix(g, alpha, packed, wt, st);
+    if (e != hipSuccess) return hip_status(e, "dynconv_forward premix launch");
+    return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
+                                                  static_cast<uint16_t *>(y), st),
+                      "dynconv_forward conv launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,464 @@
+// Per-example convolution as an implicit GEMM on bf16 MFMA (gfx950).
+//
+// For one example b the convolution is a GEMM (CondConv: Conditionally
+// Parameterized Convolutions, abstract: one ordinary convolution per example
+// with that example's own kernel):
+//   Y_b[p][o] = sum_k X_b[p][k] * W_b[k][o],  p = output position (r, s),
+//   o = output channel, k = (tap t = (u, v), input channel c).
+// The contraction runs in chunks of 32 input channels; within a chunk, one
+// v_mfma_f32_16x16x32_bf16 per (16 positions x 16 channels) tile and tap.
+//
+// Operands:
+//   A (positions x channels) comes from LDS. Each chunk of 32 input
+//     channels of the example's input rows is staged once into an LDS tile
+//     laid out [input row][input col][channel] (80-byte position stride: 32
+//     channels + 16 bytes of padding, so eight consecutive positions fall in
+//     eight distinct 16-byte bank groups). The zero halo of the padding is
+//     written once. All kh*kw taps then read their A fragments from the same
+//     tile with one 128-bit LDS read per lane (8 channels of one position):
+//     the im2col expansion never exists in memory.
+//   B (channels x output channels) is read straight from global memory into
+//     registers, 16 bytes per lane (8 channels of one output channel):
+//     - premix kernel: from the mixed kernels wt[b][t][o][cp];
+//     - fused kernel: mixed on the fly from the packed expert bank
+//       packed[t][o][cp][ip] with bf16 dot2 instructions, so the per-example
+//       kernel never reaches memory (the mixing of W_b = sum_i alpha_bi E_i,
+//       KernelWarehouse abstract, moves into the GEMM's operand load).
+//
+// Work split:
+//   premix: a workgroup owns one example, a tile of MT = NW*FM*16 output
+//     positions and NT = FN*16 output channels; wave w owns FM position
+//     fragments and all FN channel fragments, so the B fragments are shared
+//     by all waves through L1 and each A fragment is read by one wave.
+//   fused: a workgroup owns 4 examples (one per wave) and NT output
+//     channels; a wave covers all positions of its example (P <= FM*16), so
+//     each mixed kernel element is produced exactly once. The 4 examples of
+//     a workgroup share the expert tile through L1, and workgroups that read
+//     the same expert slice are placed on the same XCD (L2).
+// Output: D fragments hold 4 consecutive positions of one channel per lane,
+// stored as 8-byte bf16 vectors into NCHW y.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dynconv {
+namespace {
+
+constexpr int kPosStride = 40;  // bf16 per LDS position (32 channels + pad)
+constexpr int kChunk = 32;      // input channels per K chunk
+constexpr int kLdsBudget = 160 * 1024;
+
+struct ConvArgs {
+    int B, Cin, H, W, Cout, KH, KW, stride, pad, Ho, Wo, P, KT, Cin_pad, n;
+    int ncols;      // LDS tile columns = W + 2 * pad (column j <-> input column j - pad)
+    int tile_rows;  // LDS tile rows
+    int n_ptiles, n_otiles, n_btiles;
+    long x_bstride;  // Cin * H * W
+};
+
+// Blocks are dispatched round-robin over the 8 XCDs: block i runs on XCD
+// i % 8. Give each XCD a contiguous range of logical tile ids so that tiles
+// sharing data (same example, or same expert slice) share one L2.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+    if (total % 8 != 0) return id;
+    return (id % 8) * (total / 8) + id / 8;
+}
+
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
+    return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+// Stage input channels [c0, c0 + 32) of one example (rows [h_lo, h_hi) of
+// the image) into the LDS tile whose row 0 is input row h_tile0. Channels
+// >= Cin are written as zeros. Task order (position pair fastest, then row,
+// then 8-channel group) makes consecutive lanes read consecutive words of
+// one channel plane.
+template <bool PAIRED>
+__device__ __forceinline__ void stage_chunk(const uint16_t *__restrict__ xb,
+                                            uint16_t *__restrict__ tile, const ConvArgs &a,
+                                            int c0, int h_lo, int h_hi, int h_tile0, int tid,
+                                            int nthreads) {
+    const int HW = a.H * a.W;
+    const int nrows = h_hi - h_lo;
+    if (nrows <= 0) return;
+    if constexpr (PAIRED) {
+        const int pairs = a.W >> 1;
+        const int per_g = nrows * pairs;
+        const int ntasks = 4 * per_g;
+        for (int task = tid; task < ntasks; task += nthreads) {
+            const int g = task / per_g;
+            const int rem = task - g * per_g;
+            const int row = rem / pairs;
+            const int pr = rem - row * pairs;
+            const int h = h_lo + row;
+            const int cb = c0 + 8 * g;
+            const uint32_t *src =
+                reinterpret_cast<const uint32_t *>(xb + (long)cb * HW + h * a.W + 2 * pr);
+            uint32_t w[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                w[k] = (cb + k < a.Cin) ? src[(long)k * (HW >> 1)] : 0u;
+            u32x4_t o0, o1;
+            o0.x = lo_pair(w[0], w[1]); o0.y = lo_pair(w[2], w[3]);
+            o0.z = lo_pair(w[4], w[5]); o0.w = lo_pair(w[6], w[7]);
+            o1.x = hi_pair(w[0], w[1]); o1.y = hi_pair(w[2], w[3]);
+            o1.z = hi_pair(w[4], w[5]); o1.w = hi_pair(w[6], w[7]);
+            uint16_t *dst = tile + ((h - h_tile0) * a.ncols + 2 * pr + a.pad) * kPosStride + 8 * g;
+            *reinterpret_cast<u32x4_t *>(dst) = o0;
+            *reinterpret_cast<u32x4_t *>(dst + kPosStride) = o1;
+        }
+    } else {
+        const int per_g = nrows * a.W;
+        const int ntasks = 4 * per_g;
+        for (int task = tid; task < ntasks; task += nthreads) {
+            const int g = task / per_g;
+            const int rem = task - g * per_g;
+            const int row = rem / a.W;
+            const int col = rem - row * a.W;
+            const int h = h_lo + row;
+            const int cb = c0 + 8 * g;
+            const uint16_t *src = xb + (long)cb * HW + h * a.W + col;
+            uint32_t e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = (cb + k < a.Cin) ? (uint32_t)src[(long)k * HW] : 0u;
+            u32x4_t o;
+            o.x = e[0] | (e[1] << 16); o.y = e[2] | (e[3] << 16);
+            o.z = e[4] | (e[5] << 16); o.w = e[6] | (e[7] << 16);
+            uint16_t *dst = tile + ((h - h_tile0) * a.ncols + col + a.pad) * kPosStride + 8 * g;
+            *reinterpret_cast<u32x4_t *>(dst) = o;
+        }
+    }
+}
+
+__device__ __forceinline__ void zero_lds(uint16_t *p, int elems, int tid, int nthreads) {
+    u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < elems / 8; i += nthreads) reinterpret_cast<u32x4_t *>(p)[i] = z;
+}
+
+// D fragment -> y: lane holds positions pbase..pbase+3 of channel o.
+__device__ __forceinline__ void store_frag(uint16_t *__restrict__ y, const ConvArgs &a, int b,
+                                           int o, int pbase, const f32x4_t &d) {
+    if (o >= a.Cout || pbase >= a.P) return;
+    uint16_t *yo = y + ((long)b * a.Cout + o) * a.P;
+    if ((a.P & 3) == 0 && pbase + 3 < a.P) {
+        u32x2_t v;
+        v.x = pack_bf16x2(d[0], d[1]);
+        v.y = pack_bf16x2(d[2], d[3]);
+        *reinterpret_cast<u32x2_t *>(yo + pbase) = v;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (pbase + j < a.P) yo[pbase + j] = f32_to_bf16(d[j]);
+    }
+}
+
+template <int FM, int FN, int NW, bool PAIRED>
+__global__ __launch_bounds__(NW * 64) void conv_premix_kernel(const uint16_t *__restrict__ x,
+                                                              const uint16_t *__restrict__ wt,
+                                                              uint16_t *__restrict__ y,
+                                                              ConvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t tile[];
+    constexpr int MT = NW * FM * 16;
+    constexpr int NT = FN * 16;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_b = a.n_ptiles * a.n_otiles;
+    const int b = logical / per_b;
+    const int rem = logical - b * per_b;
+    const int pt = rem / a.n_otiles;
+    const int ot = rem - pt * a.n_otiles;
+    const int p0 = pt * MT, o0 = ot * NT;
+    const int r_first = p0 / a.Wo;
+    const int h_tile0 = r_first * a.stride - a.pad;
+    const int h_lo = max(0, h_tile0), h_hi = min(a.H, h_tile0 + a.tile_rows);
+
+    zero_lds(tile, a.tile_rows * a.ncols * kPosStride, tid, NW * 64);
+
+    int aoff[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int p = min(p0 + (wave * FM + fm) * 16 + lr, a.P - 1);
+        const int r = p / a.Wo;
+        const int s = p - r * a.Wo;
+        aoff[fm] = (((r - r_first) * a.stride) * a.ncols + s * a.stride) * kPosStride + 8 * lg;
+    }
+    const uint16_t *xb = x + (long)b * a.x_bstride;
+    const uint16_t *wb = wt + (long)b * a.KT * a.Cout * a.Cin_pad;
+    long wrow[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) wrow[fn] = (long)min(o0 + fn * 16 + lr, a.Cout - 1) * a.Cin_pad + 8 * lg;
+
+    f32x4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = 0; c0 < a.Cin_pad; c0 += kChunk) {
+        __syncthreads();
+        stage_chunk<PAIRED>(xb, tile, a, c0, h_lo, h_hi, h_tile0, tid, NW * 64);
+        __syncthreads();
+        for (int t = 0; t < a.KT; ++t) {
+            const int u = t / a.KW, v = t - u * a.KW;
+            const int toff = (u * a.ncols + v) * kPosStride;
+            const uint16_t *wtap = wb + (long)t * a.Cout * a.Cin_pad + c0;
+            bf16x8_t bfr[FN];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                bfr[fn] = *reinterpret_cast<const bf16x8_t *>(wtap + wrow[fn]);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const bf16x8_t afr = *reinterpret_cast<const bf16x8_t *>(tile + aoff[fm] + toff);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], acc[fm][fn], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            store_frag(y, a, b, o0 + fn * 16 + lr, p0 + (wave * FM + fm) * 16 + 4 * lg, acc[fm][fn]);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Fused: 4 waves = 4 examples; all positions of an example in one wave.
+template <int FM, int FN, int NP2, bool PAIRED>
+__global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restrict__ x,
+                                                         const uint32_t *__restrict__ packed,
+                                                         const float *__restrict__ alpha,
+                                                         uint16_t *__restrict__ y, ConvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    constexpr int NT = FN * 16;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int ot = logical / a.n_btiles;
+    const int bt = logical - ot * a.n_btiles;
+    const int b_raw = bt * 4 + wave;
+    const bool valid = b_raw < a.B;
+    const int b = valid ? b_raw : a.B - 1;
+    const int o0 = ot * NT;
+    const int tile_elems = a.tile_rows * a.ncols * kPosStride;
+    uint16_t *tile = lds + wave * tile_elems;
+
+    zero_lds(tile, tile_elems, lane, 64);
+
+    // attentions of example b as bf16 high/low pairs
+    uint32_t ahi[NP2], alo[NP2];
+#pragma unroll
+    for (int p = 0; p < NP2; ++p) {
+        const float a0 = 2 * p < a.n ? alpha[(long)b * a.n + 2 * p] : 0.f;
+        const float a1 = 2 * p + 1 < a.n ? alpha[(long)b * a.n + 2 * p + 1] : 0.f;
+        ahi[p] = pack_bf16x2(a0, a1);
+        alo[p] = pack_bf16x2(a0 - bf16_lo(ahi[p]), a1 - bf16_hi(ahi[p]));
+    }
+
+    int aoff[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int p = min(fm * 16 + lr, a.P - 1);
+        const int r = p / a.Wo;
+        const int s = p - r * a.Wo;
+        aoff[fm] = ((r * a.stride) * a.ncols + s * a.stride) * kPosStride + 8 * lg;
+    }
+    const uint16_t *xb = x + (long)b * a.x_bstride;
+    long prow[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        prow[fn] = ((long)min(o0 + fn * 16 + lr, a.Cout - 1) * a.Cin_pad + 8 * lg) * NP2;
+
+    f32x4_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // input rows the tile holds (rows below the last output's reach are not needed)
+    const int h_tile0 = -a.pad;
+    const int h_hi = min(a.H, h_tile0 + a.tile_rows);
+    for (int c0 = 0; c0 < a.Cin_pad; c0 += kChunk) {
+        __syncthreads();
+        stage_chunk<PAIRED>(xb, tile, a, c0, 0, h_hi, h_tile0, lane, 64);
+        __syncthreads();
+        for (int t = 0; t < a.KT; ++t) {
+            const int u = t / a.KW, v = t - u * a.KW;
+            const int toff = (u * a.ncols + v) * kPosStride;
+            const uint32_t *ptap = packed + ((long)t * a.Cout * a.Cin_pad + c0) * NP2;
+            bf16x8_t bfr[FN];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                uint32_t w[8 * NP2];
+                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(ptap + prow[fn]);
+#pragma unroll
+                for (int q = 0; q < 2 * NP2; ++q) {
+                    const u32x4_t v4 = src[q];
+                    w[4 * q + 0] = v4.x; w[4 * q + 1] = v4.y;
+                    w[4 * q + 2] = v4.z; w[4 * q + 3] = v4.w;
+                }
+                float f[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int p = 0; p < NP2; ++p) s = dot2(w[c * NP2 + p], ahi[p], s);
+#pragma unroll
+                    for (int p = 0; p < NP2; ++p) s = dot2(w[c * NP2 + p], alo[p], s);
+                    f[c] = s;
+                }
+                u32x4_t pk;
+                pk.x = pack_bf16x2(f[0], f[1]); pk.y = pack_bf16x2(f[2], f[3]);
+                pk.z = pack_bf16x2(f[4], f[5]); pk.w = pack_bf16x2(f[6], f[7]);
+                bfr[fn] = __builtin_bit_cast(bf16x8_t, pk);
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const bf16x8_t afr = *reinterpret_cast<const bf16x8_t *>(tile + aoff[fm] + toff);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], acc[fm][fn], 0, 0, 0);
+            }
+        }
+    }
+    if (!valid) return;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            store_frag(y, a, b, o0 + fn * 16 + lr, fm * 16 + 4 * lg, acc[fm][fn]);
+}
+
+ConvArgs base_args(const Geom &g) {
+    ConvArgs a{};
+    a.B = g.B; a.Cin = g.Cin; a.H = g.H; a.W = g.W; a.Cout = g.Cout;
+    a.KH = g.KH; a.KW = g.KW; a.stride = g.stride; a.pad = g.pad;
+    a.Ho = g.Ho; a.Wo = g.Wo; a.P = g.P; a.KT = g.KT; a.Cin_pad = g.Cin_pad; a.n = g.n;
+    a.ncols = g.W + 2 * g.pad;
+    a.x_bstride = (long)g.Cin * g.H * g.W;
+    return a;
+}
+
+// Premix tile shapes: (FM, FN, NW) -> MT = NW*FM*16 positions, NT = FN*16 channels.
+struct PremixCfg { int FM, FN, NW; };
+constexpr PremixCfg kPremixLarge{7, 4, 7};  // MT 784, NT 64
+constexpr PremixCfg kPremixSmall{2, 4, 7};  // MT 224, NT 64
+
+int tile_rows_for(const Geom &g, int MT) {
+    int rows_out = (MT - 1) / g.Wo + 2;
+    if (rows_out > g.Ho) rows_out = g.Ho;
+    return (rows_out - 1) * g.stride + g.KH;
+}
+
+size_t premix_lds_bytes(const Geom &g, const PremixCfg &c) {
+    const int MT = c.NW * c.FM * 16;
+    return (size_t)tile_rows_for(g, MT) * (g.W + 2 * g.pad) * kPosStride * sizeof(uint16_t);
+}
+
+PremixCfg pick_premix(const Geom &g) {
+    return g.P >= 512 ? kPremixLarge : kPremixSmall;
+}
+
+bool paired_ok(const Geom &g) { return (g.W % 2) == 0; }
+
+template <typename K>
+void set_lds(K kern, size_t bytes) {
+    hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int FM, int FN, int NW>
+hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
+                             hipStream_t stream) {
+    ConvArgs a = base_args(g);
+    constexpr int MT = NW * FM * 16, NT = FN * 16;
+    a.tile_rows = tile_rows_for(g, MT);
+    a.n_ptiles = ceil_div(g.P, MT);
+    a.n_otiles = ceil_div(g.Cout, NT);
+    const size_t lds = (size_t)a.tile_rows * a.ncols * kPosStride * sizeof(uint16_t);
+    const long blocks = (long)g.B * a.n_ptiles * a.n_otiles;
+    if (paired_ok(g)) {
+        auto k = conv_premix_kernel<FM, FN, NW, true>;
+        set_lds(k, lds);
+        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a);
+    } else {
+        auto k = conv_premix_kernel<FM, FN, NW, false>;
+        set_lds(k, lds);
+        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a);
+    }
+    return hipGetLastError();
+}
+
+constexpr int kFusedFM = 13;  // positions per example <= 208
+constexpr int kFusedFN = 4;   // 64 output channels per workgroup
+
+size_t fused_lds_bytes(const Geom &g) {
+    const int tile_rows = (g.Ho - 1) * g.stride + g.KH;
+    return 4 * (size_t)tile_rows * (g.W + 2 * g.pad) * kPosStride * sizeof(uint16_t);
+}
+
+template <int NP2>
+hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *packed,
+                           const float *alpha, uint16_t *y, hipStream_t stream) {
+    ConvArgs a = base_args(g);
+    a.tile_rows = (g.Ho - 1) * g.stride + g.KH;
+    a.n_btiles = ceil_div(g.B, 4);
+    a.n_otiles = ceil_div(g.Cout, kFusedFN * 16);
+    const size_t lds = fused_lds_bytes(g);
+    const long blocks = (long)a.n_btiles * a.n_otiles;
+    if (paired_ok(g)) {
+        auto k = conv_fused_kernel<kFusedFM, kFusedFN, NP2, true>;
+        set_lds(k, lds);
+        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
+    } else {
+        auto k = conv_fused_kernel<kFusedFM, kFusedFN, NP2, false>;
+        set_lds(k, lds);
+        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool premix_conv_supported(const Geom &g) {
+    return g.bf16 && g.groups == 1 && g.n_pad <= 16 &&
+           premix_lds_bytes(g, pick_premix(g)) <= (size_t)kLdsBudget;
+}
+
+hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
+                              hipStream_t stream) {
+    const PremixCfg c = pick_premix(g);
+    if (c.FM == kPremixLarge.FM)
+        return launch_premix_cfg<kPremixLarge.FM, kPremixLarge.FN, kPremixLarge.NW>(g, x, wt, y, stream);
+    return launch_premix_cfg<kPremixSmall.FM, kPremixSmall.FN, kPremixSmall.NW>(g, x, wt, y, stream);
+}
+
+bool fused_conv_supported(const Geom &g) {
+    return g.bf16 && g.groups == 1 && g.n_pad <= 16 && g.P <= kFusedFM * 16 &&
+           fused_lds_bytes(g) <= (size_t)kLdsBudget;
+}
+
+hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *packed,
+                             const float *alpha, uint16_t *y, hipStream_t stream) {
+    const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
+    switch (g.n_pad / 2) {
+    case 1: return launch_fused_np<1>(g, x, pk, alpha, y, stream);
+    case 2: return launch_fused_np<2>(g, x, pk, alpha, y, stream);
+    case 3: return launch_fused_np<3>(g, x, pk, alpha, y, stream);
+    case 4: return launch_fused_np<4>(g, x, pk, alpha, y, stream);
+    case 5: return launch_fused_np<5>(g, x, pk, alpha, y, stream);
+    case 6: return launch_fused_np<6>(g, x, pk, alpha, y, stream);
+    case 7: return launch_fused_np<7>(g, x, pk, alpha, y, stream);
+    case 8: return launch_fused_np<8>(g, x, pk, alpha, y, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dynconv

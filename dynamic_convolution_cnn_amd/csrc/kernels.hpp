@@ -1,0 +1,75 @@
+// Launchers of the gfx950 kernels, called by the host-side C ABI (api.cpp).
+// Every launcher only enqueues work on `stream`; argument checking is done
+// by the caller before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dynconv {
+
+// Layer geometry after validation (sizes in elements).
+struct Geom {
+    int B, Cin, H, W, Cout, KH, KW, stride, pad, groups, n;
+    int Ho, Wo;
+    int P;        // Ho * Wo, output positions per channel plane
+    int KT;       // KH * KW taps
+    int cpg;      // Cin / groups, input channels per group
+    int Cin_pad;  // Cin rounded up to a multiple of 32 (MFMA K chunk)
+    int n_pad;    // n rounded up to an even count (expert pairs)
+    bool bf16;    // element type of x, experts, mixed kernels and y
+};
+
+// ---- routing -------------------------------------------------------------
+// gap[B*Cin] (float) = channel means of x; then alpha[B,n] from the FC and
+// the nonlinearity. `gap` is caller-provided scratch of B*Cin floats.
+hipError_t launch_route(const Geom &g, const void *x, const float *fc_w,
+                        const float *fc_b, int mode, float temperature,
+                        float *gap, float *alpha, hipStream_t stream);
+
+// ---- mixing --------------------------------------------------------------
+// mixed[b, e] = sum_i alpha[b, i] * experts[i, e], natural layout, wsize
+// elements per expert; element type per g.bf16.
+hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha,
+                              const void *experts, void *mixed, hipStream_t stream);
+
+// Expert bank to the kernel-ready layout packed[t][o][cp][ip] (bf16):
+// t = tap, o = output channel, cp < Cin_pad (zero for cp >= Cin),
+// ip < n_pad (zero for ip >= n). Expert pairs sit in one 32-bit word.
+size_t packed_experts_bytes(const Geom &g);
+hipError_t launch_pack_experts(const Geom &g, const uint16_t *experts,
+                               uint16_t *packed, hipStream_t stream);
+
+// Mixed kernels in the convolution's layout wt[b][t][o][cp] (bf16) from
+// the packed bank.
+size_t premixed_bytes(const Geom &g);
+hipError_t launch_premix(const Geom &g, const float *alpha, const uint16_t *packed,
+                         uint16_t *wt, hipStream_t stream);
+
+// ---- convolution -----------------------------------------------------------
+// Implicit-GEMM bf16 MFMA convolution with mixed kernels read from `wt`.
+bool premix_conv_supported(const Geom &g);
+hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt,
+                              uint16_t *y, hipStream_t stream);
+
+// Implicit-GEMM bf16 MFMA convolution that mixes each kernel tile from the
+// packed bank in registers (no mixed kernel in memory).
+bool fused_conv_supported(const Geom &g);
+hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *packed,
+                             const float *alpha, uint16_t *y, hipStream_t stream);
+
+// Direct float32 convolution (groups == 1) with mixed kernels in natural
+// layout [B][Cout][Cin][KH][KW].
+hipError_t launch_conv_direct_f32(const Geom &g, const float *x, const float *wmixed,
+                                  float *y, hipStream_t stream);
+
+// Depthwise convolution (groups == Cin == Cout). With `wmixed` == nullptr
+// each plane's taps are mixed in the kernel from experts and alpha;
+// otherwise they are read from wmixed [B][C][KH][KW].
+bool depthwise_supported(const Geom &g);
+hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
+                                 const float *alpha, const void *wmixed, void *y,
+                                 hipStream_t stream);
+
+}  // namespace dynconv

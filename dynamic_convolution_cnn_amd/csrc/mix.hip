@@ -1,0 +1,279 @@
+// Mixing: each example's kernel is a linear mixture of the n static expert
+// kernels weighted by its attentions, W_b = sum_i alpha[b,i] E_i
+// (KernelWarehouse: Rethinking the Design of Dynamic Convolution, abstract).
+//
+// mix_natural_kernel: the stand-alone mix in the experts' own layout. Each
+//   thread owns 8 consecutive kernel elements and a tile of BT examples: it
+//   reads its 8 elements of every expert once (16-32 byte loads), widens
+//   them to float once, and writes BT mixed vectors, so the expert bank is
+//   read once per batch tile while the B mixed kernels stream out.
+// pack_experts_kernel: the expert bank in the layout the MFMA convolution
+//   reads, packed[t][o][cp][ip]: tap-major, channels contiguous and padded
+//   to the 32-wide K chunk, expert pairs sharing one 32-bit word so that a
+//   bf16 dot2 instruction mixes two experts at once.
+// premix_kernel: mixed kernels in the convolution's layout wt[b][t][o][cp],
+//   computed from the packed bank with bf16 dot2 instructions.
+//
+// Precision: natural mixing sums in float32 in expert order and rounds
+// once. The dot2 mixes split each float32 attention into a bf16 high part
+// and a bf16 low part (alpha = hi + lo up to 2^-17 relative), so two dot2
+// terms per expert pair keep the attentions' precision well below the
+// final bf16 rounding of the mixed kernel.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dynconv {
+namespace {
+
+constexpr int kMixThreads = 256;
+constexpr int kMixBT = 8;     // examples per thread in the natural mix
+constexpr int kMixChunk = 4;  // experts widened per pass
+
+template <typename T>
+struct Vec8;  // 8 consecutive elements
+template <> struct Vec8<uint16_t> {
+    u32x4_t v;
+    __device__ __forceinline__ void load(const uint16_t *p) {
+        v = *reinterpret_cast<const u32x4_t *>(p);
+    }
+    __device__ __forceinline__ void widen(float f[8]) const {
+        f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+        f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+    }
+    static __device__ __forceinline__ void store(uint16_t *p, const float f[8]) {
+        u32x4_t o;
+        o.x = pack_bf16x2(f[0], f[1]); o.y = pack_bf16x2(f[2], f[3]);
+        o.z = pack_bf16x2(f[4], f[5]); o.w = pack_bf16x2(f[6], f[7]);
+        *reinterpret_cast<u32x4_t *>(p) = o;
+    }
+};
+template <> struct Vec8<float> {
+    f32x4_t a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = reinterpret_cast<const f32x4_t *>(p)[0];
+        b = reinterpret_cast<const f32x4_t *>(p)[1];
+    }
+    __device__ __forceinline__ void widen(float f[8]) const {
+        f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+        f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    }
+    static __device__ __forceinline__ void store(float *p, const float f[8]) {
+        f32x4_t o0 = {f[0], f[1], f[2], f[3]}, o1 = {f[4], f[5], f[6], f[7]};
+        reinterpret_cast<f32x4_t *>(p)[0] = o0;
+        reinterpret_cast<f32x4_t *>(p)[1] = o1;
+    }
+};
+
+// Vector path: wsize % 8 == 0. grid.x over 8-element vectors, grid.y over
+// batch tiles of kMixBT examples.
+template <typename T>
+__global__ __launch_bounds__(kMixThreads) void mix_natural_kernel(
+    const float *__restrict__ alpha, const T *__restrict__ experts, T *__restrict__ mixed,
+    int B, int n, long wsize) {
+    const long nvec = wsize / 8;
+    const long v = (long)blockIdx.x * kMixThreads + threadIdx.x;
+    if (v >= nvec) return;
+    const int b0 = blockIdx.y * kMixBT;
+    const int nb = min(kMixBT, B - b0);
+    float acc[kMixBT][8];
+#pragma unroll
+    for (int j = 0; j < kMixBT; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[j][k] = 0.f;
+    for (int i0 = 0; i0 < n; i0 += kMixChunk) {
+        float e[kMixChunk][8];
+#pragma unroll
+        for (int ii = 0; ii < kMixChunk; ++ii) {
+            if (i0 + ii < n) {
+                Vec8<T> q;
+                q.load(experts + (long)(i0 + ii) * wsize + v * 8);
+                q.widen(e[ii]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kMixBT; ++j) {
+            if (j < nb) {
+                const float *a = alpha + (long)(b0 + j) * n + i0;
+#pragma unroll
+                for (int ii = 0; ii < kMixChunk; ++ii) {
+                    if (i0 + ii < n) {
+                        const float aj = a[ii];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) acc[j][k] = fmaf(aj, e[ii][k], acc[j][k]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kMixBT; ++j)
+        if (j < nb) Vec8<T>::store(mixed + (long)(b0 + j) * wsize + v * 8, acc[j]);
+}
+
+// Scalar path for any wsize: one element per thread, all examples.
+template <typename T>
+__global__ __launch_bounds__(kMixThreads) void mix_scalar_kernel(
+    const float *__restrict__ alpha, const T *__restrict__ experts, T *__restrict__ mixed,
+    int B, int n, long wsize) {
+    const long e = (long)blockIdx.x * kMixThreads + threadIdx.x;
+    if (e >= wsize) return;
+    for (int b = blockIdx.y; b < B; b += gridDim.y) {
+        float acc = 0.f;
+        for (int i = 0; i < n; ++i)
+            acc = fmaf(alpha[(long)b * n + i], Elem<T>::to_f32(experts[(long)i * wsize + e]), acc);
+        mixed[(long)b * wsize + e] = Elem<T>::from_f32(acc);
+    }
+}
+
+// One 32-bit output word (an expert pair) per thread.
+// experts[i][o][c][t] (c < cpg = Cin for groups == 1) -> packed[t][o][cp][ip]
+__global__ __launch_bounds__(256) void pack_experts_kernel(const uint16_t *__restrict__ e,
+                                                           uint32_t *__restrict__ packed,
+                                                           int n, int Cout, int Cin, int KT,
+                                                           int Cin_pad, int np2) {
+    const long total = (long)KT * Cout * Cin_pad * np2;
+    const long d = (long)blockIdx.x * 256 + threadIdx.x;
+    if (d >= total) return;
+    const int p = (int)(d % np2);
+    long r = d / np2;
+    const int c = (int)(r % Cin_pad);
+    r /= Cin_pad;
+    const int o = (int)(r % Cout);
+    const int t = (int)(r / Cout);
+    uint32_t lo = 0, hi = 0;
+    if (c < Cin) {
+        const long wsize = (long)Cout * Cin * KT;
+        const long off = ((long)o * Cin + c) * KT + t;
+        const int i0 = 2 * p, i1 = 2 * p + 1;
+        if (i0 < n) lo = e[(long)i0 * wsize + off];
+        if (i1 < n) hi = e[(long)i1 * wsize + off];
+    }
+    packed[d] = lo | (hi << 16);
+}
+
+__device__ __forceinline__ void split_alpha(float a0, float a1, uint32_t &hi, uint32_t &lo) {
+    hi = pack_bf16x2(a0, a1);
+    lo = pack_bf16x2(a0 - bf16_lo(hi), a1 - bf16_hi(hi));
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// premix: thread -> one 8-channel vector of wt[b][t][o][cp], for kPremixBT
+// examples. NP2 = n_pad / 2 expert pairs (compile-time).
+constexpr int kPremixBT = 4;
+template <int NP2>
+__global__ __launch_bounds__(256) void premix_kernel(const float *__restrict__ alpha,
+                                                     const uint32_t *__restrict__ packed,
+                                                     uint16_t *__restrict__ wt, int B, int n,
+                                                     long nvec /* KT*Cout*Cin_pad/8 */) {
+    const long v = (long)blockIdx.x * 256 + threadIdx.x;
+    if (v >= nvec) return;
+    const int b0 = blockIdx.y * kPremixBT;
+    // 8 channels x NP2 words, contiguous
+    uint32_t w[8][NP2];
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(packed + v * 8 * NP2);
+#pragma unroll
+    for (int q = 0; q < 2 * NP2; ++q) {
+        const u32x4_t t = src[q];
+        const int base = q * 4;
+        w[(base + 0) / NP2][(base + 0) % NP2] = t.x;
+        w[(base + 1) / NP2][(base + 1) % NP2] = t.y;
+        w[(base + 2) / NP2][(base + 2) % NP2] = t.z;
+        w[(base + 3) / NP2][(base + 3) % NP2] = t.w;
+    }
+    for (int j = 0; j < kPremixBT; ++j) {
+        const int b = b0 + j;
+        if (b >= B) break;
+        uint32_t ahi[NP2], alo[NP2];
+#pragma unroll
+        for (int p = 0; p < NP2; ++p) {
+            const float a0 = 2 * p < n ? alpha[(long)b * n + 2 * p] : 0.f;
+            const float a1 = 2 * p + 1 < n ? alpha[(long)b * n + 2 * p + 1] : 0.f;
+            split_alpha(a0, a1, ahi[p], alo[p]);
+        }
+        float f[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float s = 0.f;
+#pragma unroll
+            for (int p = 0; p < NP2; ++p) s = dot2(w[c][p], ahi[p], s);
+#pragma unroll
+            for (int p = 0; p < NP2; ++p) s = dot2(w[c][p], alo[p], s);
+            f[c] = s;
+        }
+        Vec8<uint16_t>::store(wt + ((long)b * nvec + v) * 8, f);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha, const void *experts,
+                              void *mixed, hipStream_t stream) {
+    if (wsize % 8 == 0) {
+        const long nvec = wsize / 8;
+        dim3 grid((unsigned)((nvec + kMixThreads - 1) / kMixThreads),
+                  (unsigned)((g.B + kMixBT - 1) / kMixBT));
+        if (g.bf16)
+            hipLaunchKernelGGL(mix_natural_kernel<uint16_t>, grid, dim3(kMixThreads), 0, stream,
+                               alpha, static_cast<const uint16_t *>(experts),
+                               static_cast<uint16_t *>(mixed), g.B, g.n, wsize);
+        else
+            hipLaunchKernelGGL(mix_natural_kernel<float>, grid, dim3(kMixThreads), 0, stream,
+                               alpha, static_cast<const float *>(experts),
+                               static_cast<float *>(mixed), g.B, g.n, wsize);
+    } else {
+        dim3 grid((unsigned)((wsize + kMixThreads - 1) / kMixThreads),
+                  (unsigned)min(g.B, 64));
+        if (g.bf16)
+            hipLaunchKernelGGL(mix_scalar_kernel<uint16_t>, grid, dim3(kMixThreads), 0, stream,
+                               alpha, static_cast<const uint16_t *>(experts),
+                               static_cast<uint16_t *>(mixed), g.B, g.n, wsize);
+        else
+            hipLaunchKernelGGL(mix_scalar_kernel<float>, grid, dim3(kMixThreads), 0, stream,
+                               alpha, static_cast<const float *>(experts),
+                               static_cast<float *>(mixed), g.B, g.n, wsize);
+    }
+    return hipGetLastError();
+}
+
+size_t packed_experts_bytes(const Geom &g) {
+    return (size_t)g.KT * g.Cout * g.Cin_pad * g.n_pad * sizeof(uint16_t);
+}
+
+hipError_t launch_pack_experts(const Geom &g, const uint16_t *experts, uint16_t *packed,
+                               hipStream_t stream) {
+    const int np2 = g.n_pad / 2;
+    const long total = (long)g.KT * g.Cout * g.Cin_pad * np2;
+    hipLaunchKernelGGL(pack_experts_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, experts, reinterpret_cast<uint32_t *>(packed), g.n, g.Cout,
+                       g.Cin, g.KT, g.Cin_pad, np2);
+    return hipGetLastError();
+}
+
+size_t premixed_bytes(const Geom &g) {
+    return (size_t)g.B * g.KT * g.Cout * g.Cin_pad * sizeof(uint16_t);
+}
+
+hipError_t launch_premix(const Geom &g, const float *alpha, const uint16_t *packed,
+                         uint16_t *wt, hipStream_t stream) {
+    const long nvec = (long)g.KT * g.Cout * g.Cin_pad / 8;
+    dim3 grid((unsigned)((nvec + 255) / 256), (unsigned)((g.B + kPremixBT - 1) / kPremixBT));
+    const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
+    switch (g.n_pad / 2) {
+    case 1: hipLaunchKernelGGL(premix_kernel<1>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 2: hipLaunchKernelGGL(premix_kernel<2>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 3: hipLaunchKernelGGL(premix_kernel<3>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 4: hipLaunchKernelGGL(premix_kernel<4>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 5: hipLaunchKernelGGL(premix_kernel<5>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 6: hipLaunchKernelGGL(premix_kernel<6>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 7: hipLaunchKernelGGL(premix_kernel<7>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 8: hipLaunchKernelGGL(premix_kernel<8>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dynconv

@@ -1,0 +1,174 @@
+// Routing: input-dependent attentions of each example (KernelWarehouse:
+// Rethinking the Design of Dynamic Convolution, abstract: "input-dependent
+// attentions"; FMDConv, abstract: temperature-scaled kernel attention).
+//
+//   gap[b,c] = mean_{h,w} x[b,c,h,w]
+//   z[b,i]   = sum_c fc_w[i,c] gap[b,c] + fc_b[i]
+//   alpha    = sigmoid(z)  or  softmax_i(z / T)
+//
+// Two kernels. The pooling kernel streams x once from HBM with 8-16 byte
+// vector loads: every channel plane is reduced by a group of lanes (16-64
+// lanes, sized to the plane) so that many planes are in flight per CU and
+// the chip is filled even at small batch. The FC kernel is tiny (one wave
+// per example). No atomics: sums run in a fixed order, so the result is
+// deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dynconv {
+namespace {
+
+constexpr int kGapThreads = 256;
+
+// VEC elements per load (VEC * sizeof(T) bytes); LPR lanes per plane.
+template <typename T, int VEC, int LPR>
+__global__ __launch_bounds__(kGapThreads) void gap_kernel(const T *__restrict__ x,
+                                                          float *__restrict__ gap,
+                                                          long rows, int hw) {
+    constexpr int kRowsPerBlock = kGapThreads / LPR;
+    const int lane_in_row = threadIdx.x % LPR;
+    const long row = (long)blockIdx.x * kRowsPerBlock + threadIdx.x / LPR;
+    const bool active = row < rows;
+    const long r = active ? row : rows - 1;
+    const int nvec = hw / VEC;
+    const T *p = x + r * (long)hw;
+    float s = 0.f;
+    if constexpr (sizeof(T) == 2 && VEC == 8) {
+        const u32x4_t *v = reinterpret_cast<const u32x4_t *>(p);
+#pragma unroll 4
+        for (int i = lane_in_row; i < nvec; i += LPR) {
+            u32x4_t q = __builtin_nontemporal_load(v + i);
+            s += (bf16_lo(q.x) + bf16_hi(q.x)) + (bf16_lo(q.y) + bf16_hi(q.y)) +
+                 ((bf16_lo(q.z) + bf16_hi(q.z)) + (bf16_lo(q.w) + bf16_hi(q.w)));
+        }
+    } else if constexpr (sizeof(T) == 2 && VEC == 4) {
+        const u32x2_t *v = reinterpret_cast<const u32x2_t *>(p);
+#pragma unroll 4
+        for (int i = lane_in_row; i < nvec; i += LPR) {
+            u32x2_t q = __builtin_nontemporal_load(v + i);
+            s += (bf16_lo(q.x) + bf16_hi(q.x)) + (bf16_lo(q.y) + bf16_hi(q.y));
+        }
+    } else if constexpr (sizeof(T) == 4 && VEC == 4) {
+        const f32x4_t *v = reinterpret_cast<const f32x4_t *>(p);
+#pragma unroll 4
+        for (int i = lane_in_row; i < nvec; i += LPR) {
+            f32x4_t q = __builtin_nontemporal_load(v + i);
+            s += (q[0] + q[1]) + (q[2] + q[3]);
+        }
+    } else {
+        static_assert(VEC == 1, "unsupported vector width");
+#pragma unroll 4
+        for (int i = lane_in_row; i < nvec; i += LPR) s += Elem<T>::to_f32(p[i]);
+    }
+    s = group_sum<LPR>(s);
+    if (active && lane_in_row == 0) gap[row] = s / (float)hw;
+}
+
+// One wave per example; lane j owns experts j, j+64, ... (at most kMaxJ per lane).
+constexpr int kMaxJ = 4;
+__global__ __launch_bounds__(256) void route_fc_kernel(const float *__restrict__ gap,
+                                                       const float *__restrict__ fc_w,
+                                                       const float *__restrict__ fc_b,
+                                                       float *__restrict__ alpha, int B,
+                                                       int C, int n, int mode, float temp) {
+    const int b = blockIdx.x * 4 + threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
+    if (b >= B) return;  // whole wave leaves together; no barriers below
+    const float *gb = gap + (long)b * C;
+    float z[kMaxJ];
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) {
+        const int i = lane + 64 * j;
+        float acc = 0.f;
+        if (i < n) {
+            const float *w = fc_w + (long)i * C;
+            for (int c = 0; c < C; ++c) acc = fmaf(w[c], gb[c], acc);
+            if (fc_b) acc += fc_b[i];
+        }
+        z[j] = acc;
+    }
+    if (mode == 0) {
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+            const int i = lane + 64 * j;
+            if (i < n) {
+                float a;
+                if (z[j] >= 0.f) {
+                    a = 1.f / (1.f + expf(-z[j]));
+                } else {
+                    const float e = expf(z[j]);
+                    a = e / (1.f + e);
+                }
+                alpha[(long)b * n + i] = a;
+            }
+        }
+    } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j)
+            if (lane + 64 * j < n) m = fmaxf(m, z[j] / temp);
+        m = wave_max(m);
+        float e[kMaxJ];
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+            e[j] = (lane + 64 * j < n) ? expf(z[j] / temp - m) : 0.f;
+            s += e[j];
+        }
+        s = wave_sum(s);
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+            const int i = lane + 64 * j;
+            if (i < n) alpha[(long)b * n + i] = e[j] / s;
+        }
+    }
+}
+
+template <typename T, int VEC>
+hipError_t launch_gap_vec(const T *x, float *gap, long rows, int hw, hipStream_t s) {
+    const int nvec = hw / VEC;
+    // lanes per plane: about 4 vectors per lane, between 8 and 64 lanes
+    int lpr = 8;
+    while (lpr < 64 && lpr * 4 < nvec) lpr *= 2;
+    auto go = [&](auto kern, int l) {
+        const long blocks = (rows + (kGapThreads / l) - 1) / (kGapThreads / l);
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kGapThreads), 0, s, x, gap,
+                           rows, hw);
+        return hipGetLastError();
+    };
+    switch (lpr) {
+    case 8: return go(gap_kernel<T, VEC, 8>, 8);
+    case 16: return go(gap_kernel<T, VEC, 16>, 16);
+    case 32: return go(gap_kernel<T, VEC, 32>, 32);
+    default: return go(gap_kernel<T, VEC, 64>, 64);
+    }
+}
+
+}  // namespace
+
+static_assert(kMaxJ * 64 >= 256, "route kernel covers n <= 256");
+
+hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const float *fc_b,
+                        int mode, float temperature, float *gap, float *alpha,
+                        hipStream_t stream) {
+    const long rows = (long)g.B * g.Cin;
+    const int hw = g.H * g.W;
+    hipError_t e;
+    if (g.bf16) {
+        const uint16_t *xb = static_cast<const uint16_t *>(x);
+        if (hw % 8 == 0) e = launch_gap_vec<uint16_t, 8>(xb, gap, rows, hw, stream);
+        else if (hw % 4 == 0) e = launch_gap_vec<uint16_t, 4>(xb, gap, rows, hw, stream);
+        else e = launch_gap_vec<uint16_t, 1>(xb, gap, rows, hw, stream);
+    } else {
+        const float *xf = static_cast<const float *>(x);
+        if (hw % 4 == 0) e = launch_gap_vec<float, 4>(xf, gap, rows, hw, stream);
+        else e = launch_gap_vec<float, 1>(xf, gap, rows, hw, stream);
+    }
+    if (e != hipSuccess) return e;
+    const float temp = mode == 1 ? temperature : 1.0f;
+    hipLaunchKernelGGL(route_fc_kernel, dim3((g.B + 3) / 4), dim3(256), 0, stream, gap, fc_w,
+                       fc_b, alpha, g.B, g.Cin, g.n, mode, temp);
+    return hipGetLastError();
+}
+
+}  // namespace dynconv

@@ -1,0 +1,158 @@
+/*
+ * dynconv.h - C ABI of the MI355X (gfx950) CondConv-style dynamic convolution.
+ *
+ * The method (CondConv: Conditionally Parameterized Convolutions, abstract;
+ * KernelWarehouse: Rethinking the Design of Dynamic Convolution, abstract):
+ * each example b gets its own convolution kernel, a linear mixture
+ *     W_b = sum_i alpha[b,i] * E_i
+ * of n static expert kernels E_0..E_{n-1}, weighted by input-dependent
+ * attentions alpha[b,:]; the layer output is one ordinary convolution of the
+ * example with W_b. The attentions come from a router: global average pool
+ * of the layer input, a fully connected layer with bias, then a sigmoid or a
+ * softmax of the logits divided by a temperature (FMDConv: Fast
+ * multi-attention dynamic convolution, abstract, "temperature ... kernel
+ * attention"; the pages give no further detail of the router).
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every tensor pointer is a DEVICE pointer into memory the
+ *     caller owns (for example a torch tensor's data_ptr()), densely packed
+ *     in the row-major layout stated per argument. The library never
+ *     allocates, frees or keeps a pointer after the call returns.
+ *   - Alignment: tensor pointers must be 16-byte aligned.
+ *   - Element types: x, experts, mixed kernels and y share desc->dtype
+ *     (DYNCONV_F32: IEEE float32; DYNCONV_BF16: bfloat16). Attentions and
+ *     router weights are always float32. bf16 arithmetic accumulates in
+ *     float32; mixed kernels are rounded to bf16 (nearest-even) before the
+ *     convolution's products; outputs are rounded to the output type.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     default stream) and the call returns without waiting. The library
+ *     never synchronizes. Calls on one stream run in order.
+ *   - Errors: every argument is checked on the host before anything is
+ *     enqueued. On any error nothing is launched and no output is written;
+ *     dynconv_last_error() then describes the failure (thread-local text).
+ *     DYNCONV_ERR_HIP reports a failed launch (hipGetLastError after the
+ *     launch). No C++ exception crosses this interface.
+ *   - State: the library holds no state between calls besides the
+ *     thread-local error text; calls from several threads are safe.
+ *   - Supported shapes: groups == 1, or depthwise (groups == Cin == Cout).
+ *     Other groupings return DYNCONV_ERR_UNSUPPORTED.
+ */
+#ifndef DYNCONV_H
+#define DYNCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DYNCONV_OK = 0,
+    DYNCONV_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad enum, misalignment */
+    DYNCONV_ERR_UNSUPPORTED = 2, /* valid layer this library does not implement */
+    DYNCONV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    DYNCONV_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} dynconv_status_t;
+
+typedef enum { DYNCONV_F32 = 0, DYNCONV_BF16 = 1 } dynconv_dtype_t;
+
+/* Router nonlinearity: sigmoid of the logits (attentions not normalised),
+ * or softmax of logits / temperature (attentions sum to 1). */
+typedef enum { DYNCONV_SIGMOID = 0, DYNCONV_SOFTMAX = 1 } dynconv_route_mode_t;
+
+/* How dynconv_forward builds each example's kernel.
+ *   PREMIX: one kernel writes every W_b to the workspace, the convolution
+ *           reads it back (cheap when W_b is small next to the activations).
+ *   FUSED:  the convolution mixes W_b tile by tile from the expert bank as
+ *           it goes; W_b never reaches memory (when W_b per example is at
+ *           least the example's activations, the ResNet-50-shaped case).
+ *   AUTO:   FUSED when the fused kernel supports the shape and one
+ *           example's mixed kernel is at least as large as its input plus
+ *           output; otherwise PREMIX. */
+typedef enum {
+    DYNCONV_POLICY_AUTO = 0,
+    DYNCONV_POLICY_PREMIX = 1,
+    DYNCONV_POLICY_FUSED = 2
+} dynconv_policy_t;
+
+/* Layer descriptor. Output size: Ho = (H + 2*pad - kh)/stride + 1, likewise
+ * Wo; both must be >= 1. Convolution is cross-correlation with zero padding,
+ * dilation 1 and no bias. */
+typedef struct {
+    int32_t B;       /* examples in the batch, >= 1 */
+    int32_t Cin;     /* input channels */
+    int32_t H, W;    /* input height, width */
+    int32_t Cout;    /* output channels */
+    int32_t kh, kw;  /* kernel height, width */
+    int32_t stride;  /* >= 1, both directions */
+    int32_t pad;     /* >= 0, zero padding on every side */
+    int32_t groups;  /* 1, or Cin (== Cout) for depthwise */
+    int32_t n;       /* experts, >= 1 */
+    int32_t dtype;   /* dynconv_dtype_t */
+} dynconv_desc_t;
+
+/* Routing: alpha[b,i] for every example.
+ *   gap[b,c] = mean over h,w of x[b,c,h,w]
+ *   z[b,i]   = sum_c fc_w[i,c] * gap[b,c] + fc_b[i]
+ *   alpha    = sigmoid(z)                       (mode DYNCONV_SIGMOID)
+ *            = softmax over i of z[b,i] / temperature (mode DYNCONV_SOFTMAX)
+ * (KernelWarehouse abstract: "input-dependent attentions"; FMDConv abstract:
+ * temperature-scaled kernel attention.)
+ * Arguments: x [B,Cin,H,W] (dtype), fc_w [n,Cin] float32, fc_b [n] float32 or
+ * NULL for no bias, temperature > 0 (ignored for sigmoid), alpha [B,n]
+ * float32 (written). workspace: device memory of at least
+ * dynconv_route_workspace_bytes(desc) bytes (may be NULL when that is 0);
+ * its contents on entry do not matter and are clobbered. Only desc->B, Cin,
+ * H, W, n and dtype are read. The result is deterministic: no atomics. */
+dynconv_status_t dynconv_route(const dynconv_desc_t *desc, const void *x,
+                               const float *fc_w, const float *fc_b,
+                               int32_t mode, float temperature, float *alpha,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+size_t dynconv_route_workspace_bytes(const dynconv_desc_t *desc);
+
+/* Mixing: mixed[b] = sum_i alpha[b,i] * experts[i] for every example
+ * (KernelWarehouse abstract: a linear mixture of n static kernels).
+ * experts [n,Cout,Cin/groups,kh,kw] (dtype), alpha [B,n] float32,
+ * mixed [B,Cout,Cin/groups,kh,kw] (dtype, written). Sums run in float32 in
+ * expert order; bf16 results are rounded to nearest-even once. */
+dynconv_status_t dynconv_mix(const dynconv_desc_t *desc, const float *alpha,
+                             const void *experts, void *mixed, void *stream);
+
+/* The layer: y[b] = conv(x[b], sum_i alpha[b,i] * experts[i]) for every
+ * example (CondConv abstract: a specialised kernel per example, mixed once,
+ * then one ordinary convolution). x [B,Cin,H,W], experts
+ * [n,Cout,Cin/groups,kh,kw], y [B,Cout,Ho,Wo] (all dtype); alpha [B,n]
+ * float32, typically written by dynconv_route (one routing may feed several
+ * layers). policy: dynconv_policy_t; DYNCONV_POLICY_AUTO unless a test needs
+ * a particular path (FUSED returns DYNCONV_ERR_UNSUPPORTED for shapes the
+ * fused kernel does not cover). workspace: at least
+ * dynconv_forward_workspace_bytes(desc, policy) bytes of device memory
+ * (contents on entry do not matter; clobbered). Deterministic: two calls on
+ * the same inputs give bitwise-equal y. */
+dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy,
+                                 const void *x, const void *experts,
+                                 const float *alpha, void *y, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+size_t dynconv_forward_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
+
+/* The policy DYNCONV_POLICY_AUTO resolves to for this layer
+ * (DYNCONV_POLICY_PREMIX or DYNCONV_POLICY_FUSED), or -1 for an invalid or
+ * unsupported descriptor. */
+int32_t dynconv_forward_policy(const dynconv_desc_t *desc);
+
+/* Static text for a status code (never NULL). */
+const char *dynconv_status_string(dynconv_status_t status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *dynconv_last_error(void);
+
+/* ABI version: bumped whenever a signature or layout above changes. */
+int32_t dynconv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYNCONV_H */

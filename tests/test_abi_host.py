@@ -1,0 +1,164 @@
+"""The C ABI on the host (no GPU needed).
+
+The library must load, export every entry point include/dynconv.h declares,
+and reject every invalid call with the right status before anything touches
+the device. The pointers passed here are fake (aligned, never dereferenced):
+each call fails its checks before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_convolution_cnn_amd import binding as bd
+from dynamic_convolution_cnn_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dynconv.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def _lib():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.skip("libdynconv.so not built (run python -m dynamic_convolution_cnn_amd.build)")
+    return bd.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dynconv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(bd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert L.dynconv_abi_version() == 1
+
+
+def test_status_strings():
+    _lib()
+    for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported layer"),
+                       (3, "workspace missing or too small"), (4, "HIP runtime error")]:
+        assert bd.status_string(code) == text
+    assert bd.status_string(99) == "unknown status"
+
+
+def good_desc(**kw):
+    d = dict(B=2, Cin=16, H=8, W=8, Cout=16, kh=3, kw=3, stride=1, pad=1, groups=1, n=4,
+             dtype=bd.DYNCONV_BF16)
+    d.update(kw)
+    return bd.make_desc(**d)
+
+
+def fwd(desc, policy=0, x=FAKE, e=FAKE, a=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return _lib().dynconv_forward(ctypes.byref(desc), policy, x, e, a, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("B", 0), ("Cin", 0), ("H", 0), ("W", -1), ("Cout", 0), ("kh", 0), ("kw", 0),
+    ("stride", 0), ("pad", -1), ("groups", 0), ("n", 0), ("dtype", 7), ("groups", 3),
+    ("kh", 11),   # larger than the padded input
+])
+def test_forward_rejects_invalid_descriptor(field, value):
+    d = good_desc(**{field: value})
+    assert fwd(d) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bd.last_error() != ""
+
+
+def test_forward_rejects_null_and_misaligned_pointers():
+    d = good_desc()
+    assert _lib().dynconv_forward(None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == bd.DYNCONV_ERR_INVALID_ARG
+    for kw in ("x", "e", "a", "y"):
+        assert fwd(d, **{kw: None}) == bd.DYNCONV_ERR_INVALID_ARG
+        assert fwd(d, **{kw: MISALIGNED}) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fwd(d, policy=9) == bd.DYNCONV_ERR_INVALID_ARG
+
+
+def test_forward_unsupported_layers():
+    # grouped but not depthwise
+    assert fwd(good_desc(Cin=16, Cout=32, groups=2)) == bd.DYNCONV_ERR_UNSUPPORTED
+    # depthwise needs Cin == Cout
+    assert fwd(good_desc(Cin=16, Cout=32, groups=16)) == bd.DYNCONV_ERR_UNSUPPORTED
+    # float32 has no fused path
+    assert fwd(good_desc(dtype=bd.DYNCONV_F32), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
+    # fused path covers at most 208 output positions
+    assert fwd(good_desc(H=32, W=32), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
+    # bf16 groups == 1 supports up to 16 experts
+    assert fwd(good_desc(n=17)) == bd.DYNCONV_ERR_UNSUPPORTED
+
+
+def test_forward_workspace_checks():
+    d = good_desc()
+    need = bd.dynconv_forward_workspace_bytes(d)
+    assert need > 0
+    assert fwd(d, ws_bytes=need - 1) == bd.DYNCONV_ERR_WORKSPACE
+    assert fwd(d, ws=None) == bd.DYNCONV_ERR_WORKSPACE
+    assert fwd(d, ws=MISALIGNED) == bd.DYNCONV_ERR_WORKSPACE
+    # depthwise with in-kernel mixing needs none
+    dw = good_desc(Cin=8, Cout=8, groups=8, kh=5, kw=5, pad=2)
+    assert bd.dynconv_forward_workspace_bytes(dw) == 0
+
+
+def test_route_checks():
+    L = _lib()
+    d = good_desc()
+    ws = bd.dynconv_route_workspace_bytes(d)
+    assert ws >= 2 * 16 * 4
+
+    def route(desc=d, x=FAKE, w=FAKE, b=FAKE, mode=0, t=1.0, a=FAKE, wsp=FAKE, wsb=ws):
+        return L.dynconv_route(ctypes.byref(desc) if desc is not None else None, x, w, b, mode,
+                               t, a, wsp, wsb, None)
+
+    assert route(desc=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(x=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(w=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(b=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(mode=2) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(mode=1, t=0.0) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(mode=1, t=float("inf")) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(wsb=ws - 1) == bd.DYNCONV_ERR_WORKSPACE
+    assert route(wsp=None) == bd.DYNCONV_ERR_WORKSPACE
+    assert route(desc=good_desc(n=257)) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert route(desc=good_desc(B=0)) == bd.DYNCONV_ERR_INVALID_ARG
+
+
+def test_mix_checks():
+    L = _lib()
+    d = good_desc()
+    assert L.dynconv_mix(ctypes.byref(d), None, FAKE, FAKE, None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert L.dynconv_mix(ctypes.byref(d), FAKE, MISALIGNED, FAKE, None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert L.dynconv_mix(ctypes.byref(good_desc(n=0)), FAKE, FAKE, FAKE, None) == bd.DYNCONV_ERR_INVALID_ARG
+
+
+def test_policy_choice_per_workload():
+    """AUTO fuses only where one example's mixed kernel outweighs its activations."""
+    _lib()
+    want = {"tiny": [bd.DYNCONV_POLICY_PREMIX],
+            "resnet18_3x3": [bd.DYNCONV_POLICY_PREMIX],
+            "effnet_b0_mbconv": [bd.DYNCONV_POLICY_PREMIX, bd.DYNCONV_POLICY_FUSED,
+                                 bd.DYNCONV_POLICY_PREMIX],
+            "resnet50_3x3": [bd.DYNCONV_POLICY_FUSED],
+            "many_expert_softmax": [bd.DYNCONV_POLICY_PREMIX]}
+    for key, pol in want.items():
+        w = inputs.WORKLOADS[key]
+        got = []
+        for L in w.layers:
+            d = bd.make_desc(w.B, L.Cin, L.H, L.W, L.Cout, L.k, L.k, L.stride, L.pad, L.groups, w.n,
+                             bd.DYNCONV_BF16 if w.dtype == "bf16" else bd.DYNCONV_F32)
+            got.append(bd.dynconv_forward_policy(d))
+            assert bd.dynconv_forward_workspace_bytes(d) >= 0
+        assert got == pol, key
+
+
+def test_invalid_call_writes_nothing_and_sets_message():
+    d = good_desc(stride=0)
+    assert fwd(d) == bd.DYNCONV_ERR_INVALID_ARG
+    assert "stride" in bd.last_error()
