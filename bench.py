@@ -1,0 +1,235 @@
+#!/usr/bin/env python
+"""Benchmark of the dynamic convolution hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident
+in HBM: routing (GAP -> FC -> sigmoid/softmax), packing of the expert bank,
+and the per-example convolution with mixed kernels (fused into the MFMA
+convolution for the ResNet-50-shaped layer). Default workload: the
+ResNet-50-shaped 3x3 layer, B=256, 256->256 channels, 14x14, n=4 experts,
+bf16 storage with float32 accumulation.
+
+Prints ONE JSON line with images/s (value), TFLOP/s against the bf16 MFMA
+peak, the roofline of the dominant kernel (timed live with HIP events on the
+stream the kernels run on) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload KEY] [--no-cpu-baseline]
+    python bench.py --profile       # short run for rocprofv3 (no CPU leg)
+    python bench.py --calib-copy    # plain device copy of known size (counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dynamic-conv images/s + TFLOP/s (% bf16 MFMA peak), ResNet-50 3x3 layer n=4"
+PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+ROTATE_BYTES = 640 << 20        # rotating input/output sets larger than L2 + MALL
+
+# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE on the headline workload, scaled by the plain-copy calibration. Valid only
+# for the kernel source it was taken on (sha256 of the file below); otherwise null.
+TRAFFIC = {
+    "resnet50_3x3": None,
+}
+KERNEL_SOURCE = os.path.join(ROOT, "dynamic_convolution_cnn_amd", "csrc", "conv_mfma.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="resnet50_3x3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true", help="few steps, no CPU leg")
+    ap.add_argument("--calib-copy", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def calib_copy():
+    """A plain device-to-device copy of 256 MiB, five times (for FETCH/WRITE_SIZE scaling)."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "copies": 5}))
+
+
+def to_dev(a, dtype):
+    import numpy as np
+    import torch
+    from dynamic_convolution_cnn_amd import inputs
+    a = np.ascontiguousarray(a, np.float32)
+    if dtype == "bf16":
+        return torch.from_numpy(inputs.f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(w, d):
+    """The oracle (route + mix + conv in fp64) on one full batch, on the host's cores."""
+    import oracle
+    t0 = time.perf_counter()
+    alpha, _, _ = oracle.route(d["x"], d["fc_w"], d["fc_b"], w.route_mode, w.temperature)
+    h = d["x"]
+    for L, e in zip(w.layers, d["experts"]):
+        h = oracle.forward(h, e, alpha, L.stride, L.pad, L.groups)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.B / dt, 3), "unit": "images/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"one full batch of {w.B} examples of {w.key} (route + mix + conv, "
+                      f"float64 direct loops), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by example: see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+    import numpy as np
+    import torch
+    from dynamic_convolution_cnn_amd import binding as bd
+    from dynamic_convolution_cnn_amd import inputs
+
+    if args.profile:
+        args.steps, args.warmup, args.no_cpu_baseline = min(args.steps, 10), min(args.warmup, 3), True
+    w = inputs.WORKLOADS[args.workload]
+    d = inputs.make_inputs(w, seed=0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    # one static copy of the weights; R rotating sets of activations
+    experts = [to_dev(e, w.dtype) for e in d["experts"]]
+    fc_w, fc_b = to_dev(d["fc_w"], "f32"), to_dev(d["fc_b"], "f32")
+    x0 = to_dev(d["x"], w.dtype)
+    esz = 2 if w.dtype == "bf16" else 4
+    set_bytes = sum(w.B * (L.Cin * L.H * L.W + L.Cout * L.Ho * L.Wo) * esz for L in w.layers)
+    R = max(1, math.ceil(ROTATE_BYTES / set_bytes))
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    descs, packed, ws, outs, pols = [], [], [], [], []
+    for L, e in zip(w.layers, experts):
+        desc = bd.make_desc(w.B, L.Cin, L.H, L.W, L.Cout, L.k, L.k, L.stride, L.pad, L.groups, w.n,
+                            bd.DYNCONV_BF16 if w.dtype == "bf16" else bd.DYNCONV_F32)
+        pol = bd.dynconv_forward_policy(desc)
+        pk = bd.dynconv_packed_experts_bytes(desc)
+        packed.append(torch.empty(pk, dtype=torch.uint8, device=dev) if pk else None)
+        nb = (bd.dynconv_forward_packed_workspace_bytes(desc, pol) if pk
+              else bd.dynconv_forward_workspace_bytes(desc, pol))
+        ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
+        outs.append([torch.empty((w.B, L.Cout, L.Ho, L.Wo), dtype=x0.dtype, device=dev)
+                     for _ in range(R)])
+        descs.append(desc)
+        pols.append(pol)
+    alphas = [torch.empty((w.B, w.n), dtype=torch.float32, device=dev) for _ in range(R)]
+    route_ws = torch.empty(bd.dynconv_route_workspace_bytes(descs[0]), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        s = i % R
+        if ev is not None:
+            ev[0].record(stream)
+        bd.dynconv_route(xs[s], fc_w, fc_b, w.route_mode, w.temperature, alpha=alphas[s],
+                         workspace=route_ws)
+        if ev is not None:
+            ev[1].record(stream)
+        h = xs[s]
+        for li, desc in enumerate(descs):
+            if packed[li] is not None:
+                bd.dynconv_pack_experts(desc, experts[li], packed[li])
+                if ev is not None and li == 0:
+                    ev[2].record(stream)
+                bd.dynconv_forward_packed(desc, h, packed[li], alphas[s], policy=pols[li],
+                                          y=outs[li][s], workspace=ws[li])
+            else:
+                if ev is not None and li == 0:
+                    ev[2].record(stream)
+                bd.dynconv_forward(h, experts[li], alphas[s], w.layers[li].stride,
+                                   w.layers[li].pad, w.layers[li].groups, policy=pols[li],
+                                   y=outs[li][s], workspace=ws[li])
+            if ev is not None and li == 0:
+                ev[3].record(stream)
+            h = outs[li][s]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, events around route / pack / first conv in every step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    pack_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    conv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    L0 = w.layers[0]
+    conv_flops0 = 2 * w.B * L0.macs_per_example()
+    flops_all = w.conv_flops()
+    images_s = w.B / (ms_per_step * 1e-3)
+    route_bytes = w.B * L0.Cin * L0.H * L0.W * esz + w.B * w.n * 4
+    conv_tflops = conv_flops0 / (conv_ms * 1e-3) / 1e12
+    traffic = None
+    t = TRAFFIC.get(w.key)
+    if t and t.get("source_sha") == source_sha():
+        traffic = t["bytes_per_launch"]
+    pol_name = {bd.DYNCONV_POLICY_FUSED: "fused", bd.DYNCONV_POLICY_PREMIX: "premix"}
+    out = {
+        "metric": METRIC,
+        "value": round(images_s, 1),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded numpy draws, shapes of the pages' networks; no dataset)",
+        "config": {"workload": w.key, "title": w.title, "B": w.B, "n": w.n,
+                   "layers": [dict(Cin=L.Cin, Cout=L.Cout, H=L.H, W=L.W, k=L.k, stride=L.stride,
+                                   pad=L.pad, groups=L.groups) for L in w.layers],
+                   "routing": "softmax(z/T)" if w.route_mode else "sigmoid",
+                   "policy": [pol_name.get(p, str(p)) for p in pols],
+                   "rotating_sets": R},
+        "tflops_step": round(flops_all / (ms_per_step * 1e-3) / 1e12, 2),
+        "pct_bf16_peak_step": round(100 * flops_all / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernels_us": {"route": round(route_ms * 1e3, 2), "pack": round(pack_ms * 1e3, 2),
+                       "conv_layer0": round(conv_ms * 1e3, 2)},
+        "route_hbm": {"GB/s": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
+                      "frac": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
+        "roofline": {"kernel": "conv layer 0 (" + pol_name.get(pols[0], "") + ")",
+                     "bound": "mfma", "achieved": round(conv_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -39,7 +39,8 @@ DYNCONV_POLICY_FUSED = 2
 EXPORTED = (
     "dynconv_route", "dynconv_route_workspace_bytes", "dynconv_mix", "dynconv_forward",
     "dynconv_forward_workspace_bytes", "dynconv_forward_policy", "dynconv_status_string",
-    "dynconv_last_error", "dynconv_abi_version",
+    "dynconv_last_error", "dynconv_abi_version", "dynconv_packed_experts_bytes",
+    "dynconv_pack_experts", "dynconv_forward_packed", "dynconv_forward_packed_workspace_bytes",
 )
 
 
@@ -89,6 +90,14 @@ def lib():
     L.dynconv_last_error.restype = ctypes.c_char_p
     L.dynconv_abi_version.argtypes = []
     L.dynconv_abi_version.restype = i32
+    L.dynconv_packed_experts_bytes.argtypes = [D]
+    L.dynconv_packed_experts_bytes.restype = sz
+    L.dynconv_pack_experts.argtypes = [D, P, P, sz, P]
+    L.dynconv_pack_experts.restype = i32
+    L.dynconv_forward_packed.argtypes = [D, i32, P, P, P, P, P, sz, P]
+    L.dynconv_forward_packed.restype = i32
+    L.dynconv_forward_packed_workspace_bytes.argtypes = [D, i32]
+    L.dynconv_forward_packed_workspace_bytes.restype = sz
     _lib = L
     return L
 
@@ -217,4 +226,42 @@ def dynconv_forward(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
     _check(lib().dynconv_forward(ctypes.byref(desc), int(policy), _ptr(x), _ptr(experts),
                                  _ptr(alpha), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "dynconv_forward")
+    return y
+
+
+def dynconv_packed_experts_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_packed_experts_bytes(ctypes.byref(desc)))
+
+
+def dynconv_forward_packed_workspace_bytes(desc: dynconv_desc_t,
+                                           policy: int = DYNCONV_POLICY_AUTO) -> int:
+    return int(lib().dynconv_forward_packed_workspace_bytes(ctypes.byref(desc), int(policy)))
+
+
+def dynconv_pack_experts(desc: dynconv_desc_t, experts: torch.Tensor,
+                         packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The expert bank in the layout the bf16 MFMA convolution reads (uint8 bytes)."""
+    nbytes = dynconv_packed_experts_bytes(desc)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=experts.device)
+    _check(lib().dynconv_pack_experts(ctypes.byref(desc), _ptr(experts), _ptr(packed),
+                                      packed.numel() * packed.element_size(), _stream(stream)),
+           "dynconv_pack_experts")
+    return packed
+
+
+def dynconv_forward_packed(desc: dynconv_desc_t, x: torch.Tensor, packed: torch.Tensor,
+                           alpha: torch.Tensor, policy: int = DYNCONV_POLICY_AUTO,
+                           y: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dynconv_forward with a bank packed by dynconv_pack_experts."""
+    Ho = (desc.H + 2 * desc.pad - desc.kh) // desc.stride + 1
+    Wo = (desc.W + 2 * desc.pad - desc.kw) // desc.stride + 1
+    if y is None:
+        y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_forward_packed_workspace_bytes(desc, policy), x.device,
+                              workspace)
+    _check(lib().dynconv_forward_packed(ctypes.byref(desc), int(policy), _ptr(x), _ptr(packed),
+                                        _ptr(alpha), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "dynconv_forward_packed")
     return y

@@ -146,6 +146,25 @@ dynconv_status_t hip_status(hipError_t e, const char *what) {
     return ok();
 }
 
+bool packable(const dynconv::Geom &g) { return g.bf16 && g.groups == 1 && g.n_pad <= 16; }
+
+// bf16, groups == 1: the convolution from a packed bank. `ws` holds the
+// premixed kernels for the PREMIX policy.
+dynconv_status_t forward_from_packed(const dynconv::Geom &g, int32_t p, const void *x,
+                                     const uint16_t *packed, const float *alpha, void *y,
+                                     char *ws, hipStream_t st) {
+    if (p == DYNCONV_POLICY_FUSED)
+        return hip_status(dynconv::launch_conv_fused(g, static_cast<const uint16_t *>(x), packed,
+                                                     alpha, static_cast<uint16_t *>(y), st),
+                          "fused convolution launch");
+    uint16_t *wt = reinterpret_cast<uint16_t *>(ws);
+    hipError_t e = dynconv::launch_premix(g, alpha, packed, wt, st);
+    if (e != hipSuccess) return hip_status(e, "premix launch");
+    return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
+                                                  static_cast<uint16_t *>(y), st),
+                      "convolution launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,16 +286,65 @@ dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy, con
     uint16_t *packed = reinterpret_cast<uint16_t *>(ws);
     e = dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), packed, st);
     if (e != hipSuccess) return hip_status(e, "dynconv_forward pack launch");
-    if (p == DYNCONV_POLICY_FUSED)
-        return hip_status(dynconv::launch_conv_fused(g, static_cast<const uint16_t *>(x), packed,
-                                                     alpha, static_cast<uint16_t *>(y), st),
-                          "dynconv_forward fused launch");
-    uint16_t *wt = reinterpret_cast<uint16_t *>(ws + round_up(dynconv::packed_experts_bytes(g), kWsAlign));
-    e = dynconv::launch_premix(g, alpha, packed, wt, st);
-    if (e != hipSuccess) return hip_status(e, "dynconv_forward premix launch");
-    return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
-                                                  static_cast<uint16_t *>(y), st),
-                      "dynconv_forward conv launch");
+    return forward_from_packed(g, p, x, packed, alpha, y,
+                               ws + round_up(dynconv::packed_experts_bytes(g), kWsAlign), st);
+}
+
+size_t dynconv_packed_experts_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK || !packable(g)) return 0;
+    return dynconv::packed_experts_bytes(g);
+}
+
+dynconv_status_t dynconv_pack_experts(const dynconv_desc_t *desc, const void *experts,
+                                      void *packed, size_t packed_bytes, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!packable(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "packing applies to bf16 layers with groups == 1 and n <= 16");
+    if (!experts || !packed) return fail(DYNCONV_ERR_INVALID_ARG, "experts and packed must not be NULL");
+    if (!aligned16(experts) || !aligned16(packed))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (packed_bytes < dynconv::packed_experts_bytes(g))
+        return fail(DYNCONV_ERR_INVALID_ARG, "packed holds %zu bytes, %zu needed", packed_bytes,
+                    dynconv::packed_experts_bytes(g));
+    return hip_status(dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts),
+                                                   static_cast<uint16_t *>(packed),
+                                                   static_cast<hipStream_t>(stream)),
+                      "dynconv_pack_experts launch");
+}
+
+size_t dynconv_forward_packed_workspace_bytes(const dynconv_desc_t *desc, int32_t policy) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK || !packable(g)) return 0;
+    int32_t p;
+    if (resolve_policy(g, policy, p) != DYNCONV_OK) return 0;
+    return p == DYNCONV_POLICY_PREMIX ? round_up(dynconv::premixed_bytes(g), kWsAlign) : 0;
+}
+
+dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t policy,
+                                        const void *x, const void *packed, const float *alpha,
+                                        void *y, void *workspace, size_t workspace_bytes,
+                                        void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !packed || !alpha || !y)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, packed, alpha and y must not be NULL");
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(alpha) || !aligned16(y))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (!packable(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "packed experts apply to bf16 layers with groups == 1 and n <= 16");
+    int32_t p;
+    s = resolve_policy(g, policy, p);
+    if (s != DYNCONV_OK) return s;
+    const size_t need = p == DYNCONV_POLICY_PREMIX ? round_up(dynconv::premixed_bytes(g), kWsAlign) : 0;
+    if (need > 0 && (workspace_bytes < need || !workspace || !aligned16(workspace)))
+        return fail(DYNCONV_ERR_WORKSPACE, "forward_packed needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    return forward_from_packed(g, p, x, static_cast<const uint16_t *>(packed), alpha, y,
+                               static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

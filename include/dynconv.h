@@ -137,6 +137,31 @@ dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy,
                                  size_t workspace_bytes, void *stream);
 size_t dynconv_forward_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
 
+/* Expert bank in the layout the bf16 MFMA convolution reads (bf16 layers with
+ * groups == 1 only): packed[t][o][c'][i'] with t = kh*kw tap (row-major),
+ * o = output channel, c' < Cin rounded up to 32 (zero beyond Cin), and
+ * i' < n rounded up to even (zero beyond n), so that two experts' values of
+ * one kernel element share a 32-bit word. A pure layout transform of the
+ * static experts: a bank can be packed once and then reused by
+ * dynconv_forward_packed for every batch. dynconv_forward packs internally on
+ * every call. experts [n,Cout,Cin,kh,kw] bf16; packed: device memory of at
+ * least dynconv_packed_experts_bytes(desc) bytes (written). Unsupported
+ * layers return DYNCONV_ERR_UNSUPPORTED (and 0 bytes). */
+size_t dynconv_packed_experts_bytes(const dynconv_desc_t *desc);
+dynconv_status_t dynconv_pack_experts(const dynconv_desc_t *desc, const void *experts,
+                                      void *packed, size_t packed_bytes, void *stream);
+
+/* dynconv_forward with an expert bank already packed by dynconv_pack_experts
+ * (bf16, groups == 1). Same arguments, policies and results as
+ * dynconv_forward; the workspace holds only what the policy needs besides
+ * the packed bank (the premixed kernels for DYNCONV_POLICY_PREMIX, nothing
+ * for DYNCONV_POLICY_FUSED). */
+dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t policy,
+                                        const void *x, const void *packed,
+                                        const float *alpha, void *y, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+size_t dynconv_forward_packed_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
+
 /* The policy DYNCONV_POLICY_AUTO resolves to for this layer
  * (DYNCONV_POLICY_PREMIX or DYNCONV_POLICY_FUSED), or -1 for an invalid or
  * unsupported descriptor. */

@@ -162,3 +162,26 @@ def test_invalid_call_writes_nothing_and_sets_message():
     d = good_desc(stride=0)
     assert fwd(d) == bd.DYNCONV_ERR_INVALID_ARG
     assert "stride" in bd.last_error()
+
+
+def test_pack_and_forward_packed_checks():
+    L = _lib()
+    d = good_desc()
+    nb = bd.dynconv_packed_experts_bytes(d)
+    # 9 taps x 16 out x 32 padded in-channels x 4 experts x 2 bytes
+    assert nb == 9 * 16 * 32 * 4 * 2
+    assert L.dynconv_pack_experts(ctypes.byref(d), FAKE, FAKE, nb - 1, None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert L.dynconv_pack_experts(ctypes.byref(d), None, FAKE, nb, None) == bd.DYNCONV_ERR_INVALID_ARG
+    f32 = good_desc(dtype=bd.DYNCONV_F32)
+    assert bd.dynconv_packed_experts_bytes(f32) == 0
+    assert L.dynconv_pack_experts(ctypes.byref(f32), FAKE, FAKE, nb, None) == bd.DYNCONV_ERR_UNSUPPORTED
+    dw = good_desc(Cin=8, Cout=8, groups=8)
+    assert L.dynconv_pack_experts(ctypes.byref(dw), FAKE, FAKE, nb, None) == bd.DYNCONV_ERR_UNSUPPORTED
+    fp = L.dynconv_forward_packed
+    assert fp(ctypes.byref(d), 0, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fp(ctypes.byref(f32), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == bd.DYNCONV_ERR_UNSUPPORTED
+    need = bd.dynconv_forward_packed_workspace_bytes(d, bd.DYNCONV_POLICY_PREMIX)
+    assert need == 2 * 9 * 16 * 32 * 2
+    assert fp(ctypes.byref(d), bd.DYNCONV_POLICY_PREMIX, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+              None) == bd.DYNCONV_ERR_WORKSPACE
+    assert bd.dynconv_forward_packed_workspace_bytes(d, bd.DYNCONV_POLICY_FUSED) == 0

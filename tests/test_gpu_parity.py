@@ -318,3 +318,24 @@ def test_permuted_batch_permutes_output():
     y = run_layer(d["x"], e, alpha, L, "bf16").cpu()
     yp = run_layer(d["x"][perm], e, alpha[perm], L, "bf16").cpu()
     assert torch.equal(yp.view(torch.int16), y[perm].view(torch.int16))
+
+
+@pytest.mark.parametrize("key,B", [("resnet50_3x3", 8), ("many_expert_softmax", 3),
+                                   ("resnet18_3x3", 2)])
+def test_packed_api_matches_forward(key, B):
+    """pack once + forward_packed gives bitwise the same y as forward (both policies)."""
+    w = inputs.WORKLOADS[key]
+    d = inputs.make_inputs(w, B=B)
+    L, e = w.layers[0], d["experts"][0]
+    alpha = to_dev(inputs.forced_alpha(B, w.n, "uniform"), "f32")
+    x, ed = to_dev(d["x"], "bf16"), to_dev(e, "bf16")
+    desc = bd.layer_desc(x, ed, L.stride, L.pad, L.groups)
+    say("packed api", key)
+    packed = bd.dynconv_pack_experts(desc, ed)
+    for pol in (bd.DYNCONV_POLICY_PREMIX, bd.DYNCONV_POLICY_FUSED):
+        if pol == bd.DYNCONV_POLICY_FUSED and L.Ho * L.Wo > 208:
+            continue
+        y1 = bd.dynconv_forward_packed(desc, x, packed, alpha, policy=pol)
+        y2 = bd.dynconv_forward(x, ed, alpha, L.stride, L.pad, L.groups, policy=pol)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
