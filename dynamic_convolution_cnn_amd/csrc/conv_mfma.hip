@@ -37,6 +37,8 @@
 //     the same expert slice are placed on the same XCD (L2).
 // Output: D fragments hold 4 consecutive positions of one channel per lane,
 // stored as 8-byte bf16 vectors into NCHW y.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -230,8 +232,116 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// Fused: 4 waves = 4 examples; all positions of an example in one wave.
-template <int FM, int FN, int NP2, bool PAIRED>
+// Staging split in two phases so that the loads of the next chunk can be in
+// flight while the current chunk computes: stage_load issues the global loads
+// of this lane's tasks into registers, stage_store writes them to the tile.
+// Paired layout only (W even); a lane owns tasks lane, lane + 64, ...
+template <int XT>
+__device__ __forceinline__ void stage_load_paired(const uint16_t *__restrict__ xb,
+                                                  const ConvArgs &a, int c0, int nrows, int lane,
+                                                  uint32_t (&r)[XT][8]) {
+    const int HW = a.H * a.W;
+    const int pairs = a.W >> 1;
+    const int per_g = nrows * pairs;
+    const int ntasks = 4 * per_g;
+#pragma unroll
+    for (int k = 0; k < XT; ++k) {
+        const int task = lane + 64 * k;
+        if (task < ntasks) {
+            const int g = task / per_g;
+            const int rem = task - g * per_g;
+            const int row = rem / pairs;
+            const int pr = rem - row * pairs;
+            const int cb = c0 + 8 * g;
+            const uint32_t *src =
+                reinterpret_cast<const uint32_t *>(xb + (long)cb * HW + row * a.W + 2 * pr);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[k][j] = (cb + j < a.Cin) ? src[(long)j * (HW >> 1)] : 0u;
+        }
+    }
+}
+
+template <int XT>
+__device__ __forceinline__ void stage_store_paired(uint16_t *__restrict__ tile, const ConvArgs &a,
+                                                   int nrows, int h_tile0, int lane,
+                                                   const uint32_t (&r)[XT][8]) {
+    const int pairs = a.W >> 1;
+    const int per_g = nrows * pairs;
+    const int ntasks = 4 * per_g;
+#pragma unroll
+    for (int k = 0; k < XT; ++k) {
+        const int task = lane + 64 * k;
+        if (task < ntasks) {
+            const int g = task / per_g;
+            const int rem = task - g * per_g;
+            const int row = rem / pairs;
+            const int pr = rem - row * pairs;
+            u32x4_t o0, o1;
+            o0.x = lo_pair(r[k][0], r[k][1]); o0.y = lo_pair(r[k][2], r[k][3]);
+            o0.z = lo_pair(r[k][4], r[k][5]); o0.w = lo_pair(r[k][6], r[k][7]);
+            o1.x = hi_pair(r[k][0], r[k][1]); o1.y = hi_pair(r[k][2], r[k][3]);
+            o1.z = hi_pair(r[k][4], r[k][5]); o1.w = hi_pair(r[k][6], r[k][7]);
+            uint16_t *dst = tile + ((row - h_tile0) * a.ncols + 2 * pr + a.pad) * kPosStride + 8 * g;
+            *reinterpret_cast<u32x4_t *>(dst) = o0;
+            *reinterpret_cast<u32x4_t *>(dst + kPosStride) = o1;
+        }
+    }
+}
+
+// Packed expert words of one (tap, chunk) step for this lane's FN fragments.
+template <int FN, int NP2>
+__device__ __forceinline__ void load_packed(const uint32_t *__restrict__ packed, const ConvArgs &a,
+                                            int t, int c0, const long (&prow)[FN],
+                                            uint32_t (&w)[FN][8 * NP2]) {
+    const uint32_t *ptap = packed + ((long)t * a.Cout * a.Cin_pad + c0) * NP2;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(ptap + prow[fn]);
+#pragma unroll
+        for (int q = 0; q < 2 * NP2; ++q) {
+            const u32x4_t v4 = src[q];
+            w[fn][4 * q + 0] = v4.x; w[fn][4 * q + 1] = v4.y;
+            w[fn][4 * q + 2] = v4.z; w[fn][4 * q + 3] = v4.w;
+        }
+    }
+}
+
+// B fragments of one step: W_b[c][o] = sum_i alpha_bi E_i[c][o] over the 8
+// channels this lane holds, as two bf16 dot2 chains (attention high and low
+// parts), rounded once to bf16.
+template <int FN, int NP2>
+__device__ __forceinline__ void mix_frags(const uint32_t (&w)[FN][8 * NP2], const uint32_t (&ahi)[NP2],
+                                          const uint32_t (&alo)[NP2], bf16x8_t (&bfr)[FN]) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        float f[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float s = 0.f;
+#pragma unroll
+            for (int p = 0; p < NP2; ++p) s = dot2(w[fn][c * NP2 + p], ahi[p], s);
+#pragma unroll
+            for (int p = 0; p < NP2; ++p) s = dot2(w[fn][c * NP2 + p], alo[p], s);
+            f[c] = s;
+        }
+        u32x4_t pk;
+        pk.x = pack_bf16x2(f[0], f[1]); pk.y = pack_bf16x2(f[2], f[3]);
+        pk.z = pack_bf16x2(f[4], f[5]); pk.w = pack_bf16x2(f[6], f[7]);
+        bfr[fn] = __builtin_bit_cast(bf16x8_t, pk);
+    }
+}
+
+// Fused: 4 waves = 4 examples; all positions of an example in one wave. Each
+// wave owns a private LDS tile, so no workgroup barrier is needed: LDS
+// operations of one wave execute in program order.
+//
+// Software pipeline over steps s = (chunk c, tap t):
+//   - the packed expert words of step s+2 load while step s computes;
+//   - the B fragments of step s+1 are mixed (VALU) while the MFMAs of step s
+//     run (independent instructions the scheduler interleaves);
+//   - the input chunk c+1 loads into registers during chunk c and is written
+//     to the tile after the last tap of chunk c has read it.
+template <int FM, int FN, int NP2, int XT>
 __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ packed,
                                                          const float *__restrict__ alpha,
@@ -284,48 +394,49 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
 
     // input rows the tile holds (rows below the last output's reach are not needed)
     const int h_tile0 = -a.pad;
-    const int h_hi = min(a.H, h_tile0 + a.tile_rows);
-    for (int c0 = 0; c0 < a.Cin_pad; c0 += kChunk) {
-        __syncthreads();
-        stage_chunk<PAIRED>(xb, tile, a, c0, 0, h_hi, h_tile0, lane, 64);
-        __syncthreads();
-        for (int t = 0; t < a.KT; ++t) {
-            const int u = t / a.KW, v = t - u * a.KW;
-            const int toff = (u * a.ncols + v) * kPosStride;
-            const uint32_t *ptap = packed + ((long)t * a.Cout * a.Cin_pad + c0) * NP2;
-            bf16x8_t bfr[FN];
+    const int nrows = min(a.H, h_tile0 + a.tile_rows);
+    const int nchunks = a.Cin_pad / kChunk;
+    const int nsteps = nchunks * a.KT;
+
+    uint32_t xr[XT][8];
+    stage_load_paired<XT>(xb, a, 0, nrows, lane, xr);
+    stage_store_paired<XT>(tile, a, nrows, h_tile0, lane, xr);
+
+    uint32_t w[FN][8 * NP2];
+    bf16x8_t bcur[FN], bnext[FN];
+    load_packed<FN, NP2>(packed, a, 0, 0, prow, w);
+    mix_frags<FN, NP2>(w, ahi, alo, bcur);
+    if (nsteps > 1) load_packed<FN, NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
+
+    int t = 0, c0 = 0;
+    for (int s = 0; s < nsteps; ++s) {
+        if (t == 0 && c0 + kChunk < a.Cin_pad)
+            stage_load_paired<XT>(xb, a, c0 + kChunk, nrows, lane, xr);
+        const int u = t / a.KW, v = t - u * a.KW;
+        const int toff = (u * a.ncols + v) * kPosStride;
+        bf16x8_t afr[FM];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                uint32_t w[8 * NP2];
-                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(ptap + prow[fn]);
+        for (int fm = 0; fm < FM; ++fm)
+            afr[fm] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[fm] + toff);
 #pragma unroll
-                for (int q = 0; q < 2 * NP2; ++q) {
-                    const u32x4_t v4 = src[q];
-                    w[4 * q + 0] = v4.x; w[4 * q + 1] = v4.y;
-                    w[4 * q + 2] = v4.z; w[4 * q + 3] = v4.w;
-                }
-                float f[8];
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int p = 0; p < NP2; ++p) s = dot2(w[c * NP2 + p], ahi[p], s);
-#pragma unroll
-                    for (int p = 0; p < NP2; ++p) s = dot2(w[c * NP2 + p], alo[p], s);
-                    f[c] = s;
-                }
-                u32x4_t pk;
-                pk.x = pack_bf16x2(f[0], f[1]); pk.y = pack_bf16x2(f[2], f[3]);
-                pk.z = pack_bf16x2(f[4], f[5]); pk.w = pack_bf16x2(f[6], f[7]);
-                bfr[fn] = __builtin_bit_cast(bf16x8_t, pk);
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[fm], bcur[fn], acc[fm][fn], 0, 0, 0);
+        if (s + 1 < nsteps) {
+            mix_frags<FN, NP2>(w, ahi, alo, bnext);
+            if (s + 2 < nsteps) {
+                const int s2 = s + 2;
+                const int c2 = s2 / a.KT;
+                load_packed<FN, NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
             }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const bf16x8_t afr = *reinterpret_cast<const bf16x8_t *>(tile + aoff[fm] + toff);
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[fn], acc[fm][fn], 0, 0, 0);
-            }
+            for (int fn = 0; fn < FN; ++fn) bcur[fn] = bnext[fn];
+        }
+        if (++t == a.KT) {
+            t = 0;
+            if (c0 + kChunk < a.Cin_pad) stage_store_paired<XT>(tile, a, nrows, h_tile0, lane, xr);
+            c0 += kChunk;
         }
     }
     if (!valid) return;
@@ -397,31 +508,31 @@ hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *w
 }
 
 constexpr int kFusedFM = 13;  // positions per example <= 208
-constexpr int kFusedFN = 4;   // 64 output channels per workgroup
+constexpr int kFusedXT = 8;   // staging tasks per lane: 4 * rows * W/2 <= 512
+// Output-channel fragments per workgroup: 64 channels for up to 4 experts;
+// fewer as the packed words per step (8 * NP2 per fragment) grow, to stay
+// within the register file.
+constexpr int fused_fn(int np2) { return np2 <= 2 ? 4 : (np2 <= 4 ? 2 : 1); }
+
+int fused_tile_rows(const Geom &g) { return (g.Ho - 1) * g.stride + g.KH; }
 
 size_t fused_lds_bytes(const Geom &g) {
-    const int tile_rows = (g.Ho - 1) * g.stride + g.KH;
-    return 4 * (size_t)tile_rows * (g.W + 2 * g.pad) * kPosStride * sizeof(uint16_t);
+    return 4 * (size_t)fused_tile_rows(g) * (g.W + 2 * g.pad) * kPosStride * sizeof(uint16_t);
 }
 
 template <int NP2>
 hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *packed,
                            const float *alpha, uint16_t *y, hipStream_t stream) {
     ConvArgs a = base_args(g);
-    a.tile_rows = (g.Ho - 1) * g.stride + g.KH;
+    a.tile_rows = fused_tile_rows(g);
     a.n_btiles = ceil_div(g.B, 4);
-    a.n_otiles = ceil_div(g.Cout, kFusedFN * 16);
+    constexpr int FN = fused_fn(NP2);
+    a.n_otiles = ceil_div(g.Cout, FN * 16);
     const size_t lds = fused_lds_bytes(g);
     const long blocks = (long)a.n_btiles * a.n_otiles;
-    if (paired_ok(g)) {
-        auto k = conv_fused_kernel<kFusedFM, kFusedFN, NP2, true>;
-        set_lds(k, lds);
-        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
-    } else {
-        auto k = conv_fused_kernel<kFusedFM, kFusedFN, NP2, false>;
-        set_lds(k, lds);
-        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
-    }
+    auto k = conv_fused_kernel<kFusedFM, FN, NP2, kFusedXT>;
+    set_lds(k, lds);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
     return hipGetLastError();
 }
 
@@ -441,7 +552,9 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
 }
 
 bool fused_conv_supported(const Geom &g) {
+    const int rows = std::min(g.H, fused_tile_rows(g) - g.pad);
     return g.bf16 && g.groups == 1 && g.n_pad <= 16 && g.P <= kFusedFM * 16 &&
+           g.W % 2 == 0 && 4 * rows * (g.W / 2) <= 64 * kFusedXT &&
            fused_lds_bytes(g) <= (size_t)kLdsBudget;
 }
 

@@ -64,29 +64,47 @@ __global__ __launch_bounds__(kGapThreads) void gap_kernel(const T *__restrict__ 
     if (active && lane_in_row == 0) gap[row] = s / (float)hw;
 }
 
-// One wave per example; lane j owns experts j, j+64, ... (at most kMaxJ per lane).
-constexpr int kMaxJ = 4;
+// One wave per example. Lanes run over channels (coalesced reads of gap and
+// fc_w) and keep partial logits for up to 16 experts at a time; a fixed
+// butterfly reduction finishes each logit. Logits go through LDS so that
+// lane j then owns experts j, j+64, ... for the nonlinearity.
+constexpr int kMaxJ = 4;     // n <= 256
+constexpr int kIChunk = 16;  // experts per pass over the channels
 __global__ __launch_bounds__(256) void route_fc_kernel(const float *__restrict__ gap,
                                                        const float *__restrict__ fc_w,
                                                        const float *__restrict__ fc_b,
                                                        float *__restrict__ alpha, int B,
                                                        int C, int n, int mode, float temp) {
-    const int b = blockIdx.x * 4 + threadIdx.x / 64;
+    __shared__ float zs[4][64 * kMaxJ];
+    const int wv = threadIdx.x / 64;
+    const int b = blockIdx.x * 4 + wv;
     const int lane = threadIdx.x % 64;
     if (b >= B) return;  // whole wave leaves together; no barriers below
     const float *gb = gap + (long)b * C;
+    for (int i0 = 0; i0 < n; i0 += kIChunk) {
+        float part[kIChunk];
+#pragma unroll
+        for (int ii = 0; ii < kIChunk; ++ii) part[ii] = 0.f;
+        for (int c = lane; c < C; c += 64) {
+            const float gc = gb[c];
+#pragma unroll
+            for (int ii = 0; ii < kIChunk; ++ii)
+                if (i0 + ii < n) part[ii] = fmaf(fc_w[(long)(i0 + ii) * C + c], gc, part[ii]);
+        }
+#pragma unroll
+        for (int ii = 0; ii < kIChunk; ++ii) {
+            if (i0 + ii < n) {
+                const float zt = wave_sum(part[ii]);
+                if (lane == 0) zs[wv][i0 + ii] = zt + (fc_b ? fc_b[i0 + ii] : 0.f);
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float z[kMaxJ];
 #pragma unroll
-    for (int j = 0; j < kMaxJ; ++j) {
-        const int i = lane + 64 * j;
-        float acc = 0.f;
-        if (i < n) {
-            const float *w = fc_w + (long)i * C;
-            for (int c = 0; c < C; ++c) acc = fmaf(w[c], gb[c], acc);
-            if (fc_b) acc += fc_b[i];
-        }
-        z[j] = acc;
-    }
+    for (int j = 0; j < kMaxJ; ++j) z[j] = (lane + 64 * j < n) ? zs[wv][lane + 64 * j] : 0.f;
     if (mode == 0) {
 #pragma unroll
         for (int j = 0; j < kMaxJ; ++j) {

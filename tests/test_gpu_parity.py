@@ -247,8 +247,13 @@ def test_forward_ragged_bf16(case, policy):
     e = inputs.bf16_round(rng.standard_normal((n, Cout, Cin, kh, kw), dtype=np.float32))
     alpha = rng.uniform(-1, 1, (B, n)).astype(np.float32)
     say("ragged", case, "policy", policy)
-    y = bd.dynconv_forward(to_dev(x, "bf16"), to_dev(e, "bf16"), to_dev(alpha, "f32"), st, p, 1,
-                           policy=policy)
+    try:
+        y = bd.dynconv_forward(to_dev(x, "bf16"), to_dev(e, "bf16"), to_dev(alpha, "f32"), st, p,
+                               1, policy=policy)
+    except bd.DynconvError as err:
+        if err.status == bd.DYNCONV_ERR_UNSUPPORTED and policy == bd.DYNCONV_POLICY_FUSED:
+            pytest.skip(f"fused path declines this layer: {err}")
+        raise
     torch.cuda.synchronize()
     ref = oracle.forward(x, e, alpha, st, p, 1)
     check(from_dev(y), ref, TOL["bf16"], f"ragged {case} policy {policy}")
