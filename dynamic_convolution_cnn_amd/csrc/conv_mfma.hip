@@ -232,14 +232,22 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// Staging split in two phases so that the loads of the next chunk can be in
-// flight while the current chunk computes: stage_load issues the global loads
-// of this lane's tasks into registers, stage_store writes them to the tile.
-// Paired layout only (W even); a lane owns tasks lane, lane + 64, ...
+// Input staging of the fused kernel, split in two phases so that the loads
+// of the next chunk are in flight while the current chunk computes:
+// stage_load issues a lane's global loads into registers, stage_store writes
+// them to the tile. The per-task source and destination offsets do not
+// depend on the chunk and are computed once (StageMap). Paired layout only
+// (W even): a task is 2 neighbouring positions x 8 channels; lane owns tasks
+// lane, lane + 64, ...
 template <int XT>
-__device__ __forceinline__ void stage_load_paired(const uint16_t *__restrict__ xb,
-                                                  const ConvArgs &a, int c0, int nrows, int lane,
-                                                  uint32_t (&r)[XT][8]) {
+struct StageMap {
+    int src[XT];  // element offset from the chunk's first channel plane
+    int dst[XT];  // element offset in the tile; -1: no task
+};
+
+template <int XT>
+__device__ __forceinline__ void stage_map(const ConvArgs &a, int nrows, int h_tile0, int lane,
+                                          StageMap<XT> &m) {
     const int HW = a.H * a.W;
     const int pairs = a.W >> 1;
     const int per_g = nrows * pairs;
@@ -247,130 +255,143 @@ __device__ __forceinline__ void stage_load_paired(const uint16_t *__restrict__ x
 #pragma unroll
     for (int k = 0; k < XT; ++k) {
         const int task = lane + 64 * k;
-        if (task < ntasks) {
-            const int g = task / per_g;
-            const int rem = task - g * per_g;
-            const int row = rem / pairs;
-            const int pr = rem - row * pairs;
-            const int cb = c0 + 8 * g;
-            const uint32_t *src =
-                reinterpret_cast<const uint32_t *>(xb + (long)cb * HW + row * a.W + 2 * pr);
+        const int g = task / per_g;
+        const int rem = task - g * per_g;
+        const int row = rem / pairs;
+        const int pr = rem - row * pairs;
+        const bool ok = task < ntasks;
+        m.src[k] = ok ? 8 * g * HW + row * a.W + 2 * pr : 0;
+        m.dst[k] = ok ? ((row - h_tile0) * a.ncols + 2 * pr + a.pad) * kPosStride + 8 * g : -1;
+    }
+}
+
+template <int XT>
+__device__ __forceinline__ void stage_load(const uint16_t *__restrict__ xc, const ConvArgs &a,
+                                           int c0, const StageMap<XT> &m, uint32_t (&r)[XT][8]) {
+    const int HW2 = (a.H * a.W) >> 1;  // words per channel plane
+    const bool tail = c0 + kChunk > a.Cin;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) r[k][j] = (cb + j < a.Cin) ? src[(long)j * (HW >> 1)] : 0u;
+    for (int k = 0; k < XT; ++k) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(xc + m.src[k]);
+        if (!tail) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[k][j] = src[(long)j * HW2];
+        } else {
+            // channel of word j is c0 + 8g + j; 8g is the tile offset modulo kPosStride
+            const int cb = c0 + (m.dst[k] >= 0 ? m.dst[k] % kPosStride : 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int jj = min(j, max(a.Cin - 1 - cb, 0));
+                const uint32_t v = src[(long)jj * HW2];
+                r[k][j] = cb + j < a.Cin ? v : 0u;
+            }
         }
     }
 }
 
 template <int XT>
-__device__ __forceinline__ void stage_store_paired(uint16_t *__restrict__ tile, const ConvArgs &a,
-                                                   int nrows, int h_tile0, int lane,
-                                                   const uint32_t (&r)[XT][8]) {
-    const int pairs = a.W >> 1;
-    const int per_g = nrows * pairs;
-    const int ntasks = 4 * per_g;
+__device__ __forceinline__ void stage_store(uint16_t *__restrict__ tile, const StageMap<XT> &m,
+                                            const uint32_t (&r)[XT][8]) {
 #pragma unroll
     for (int k = 0; k < XT; ++k) {
-        const int task = lane + 64 * k;
-        if (task < ntasks) {
-            const int g = task / per_g;
-            const int rem = task - g * per_g;
-            const int row = rem / pairs;
-            const int pr = rem - row * pairs;
+        if (m.dst[k] >= 0) {
             u32x4_t o0, o1;
             o0.x = lo_pair(r[k][0], r[k][1]); o0.y = lo_pair(r[k][2], r[k][3]);
             o0.z = lo_pair(r[k][4], r[k][5]); o0.w = lo_pair(r[k][6], r[k][7]);
             o1.x = hi_pair(r[k][0], r[k][1]); o1.y = hi_pair(r[k][2], r[k][3]);
             o1.z = hi_pair(r[k][4], r[k][5]); o1.w = hi_pair(r[k][6], r[k][7]);
-            uint16_t *dst = tile + ((row - h_tile0) * a.ncols + 2 * pr + a.pad) * kPosStride + 8 * g;
-            *reinterpret_cast<u32x4_t *>(dst) = o0;
-            *reinterpret_cast<u32x4_t *>(dst + kPosStride) = o1;
+            *reinterpret_cast<u32x4_t *>(tile + m.dst[k]) = o0;
+            *reinterpret_cast<u32x4_t *>(tile + m.dst[k] + kPosStride) = o1;
         }
     }
 }
 
-// Packed expert words of one (tap, chunk) step for this lane's FN fragments.
-template <int FN, int NP2>
+// Packed expert words of one (tap, chunk) step for this lane's fragment:
+// 8 channels x NP2 expert pairs.
+template <int NP2>
 __device__ __forceinline__ void load_packed(const uint32_t *__restrict__ packed, const ConvArgs &a,
-                                            int t, int c0, const long (&prow)[FN],
-                                            uint32_t (&w)[FN][8 * NP2]) {
-    const uint32_t *ptap = packed + ((long)t * a.Cout * a.Cin_pad + c0) * NP2;
+                                            int t, int c0, long prow, uint32_t (&w)[8 * NP2]) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+        packed + ((long)t * a.Cout * a.Cin_pad + c0) * NP2 + prow);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(ptap + prow[fn]);
-#pragma unroll
-        for (int q = 0; q < 2 * NP2; ++q) {
-            const u32x4_t v4 = src[q];
-            w[fn][4 * q + 0] = v4.x; w[fn][4 * q + 1] = v4.y;
-            w[fn][4 * q + 2] = v4.z; w[fn][4 * q + 3] = v4.w;
-        }
+    for (int q = 0; q < 2 * NP2; ++q) {
+        const u32x4_t v4 = src[q];
+        w[4 * q + 0] = v4.x; w[4 * q + 1] = v4.y;
+        w[4 * q + 2] = v4.z; w[4 * q + 3] = v4.w;
     }
 }
 
-// B fragments of one step: W_b[c][o] = sum_i alpha_bi E_i[c][o] over the 8
-// channels this lane holds, as two bf16 dot2 chains (attention high and low
-// parts), rounded once to bf16.
-template <int FN, int NP2>
-__device__ __forceinline__ void mix_frags(const uint32_t (&w)[FN][8 * NP2], const uint32_t (&ahi)[NP2],
-                                          const uint32_t (&alo)[NP2], bf16x8_t (&bfr)[FN]) {
+// One B fragment: W_b[c][o] = sum_i alpha_bi E_i[c][o] over this lane's 8
+// channels, as two bf16 dot2 chains (attention high and low parts), rounded
+// once to bf16.
+template <int NP2>
+__device__ __forceinline__ u32x4_t mix_frag(const uint32_t (&w)[8 * NP2], const uint32_t *ahi,
+                                            const uint32_t *alo) {
+    float f[8];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-        float f[8];
+    for (int c = 0; c < 8; ++c) {
+        float s = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float s = 0.f;
+        for (int p = 0; p < NP2; ++p) s = dot2(w[c * NP2 + p], ahi[p], s);
 #pragma unroll
-            for (int p = 0; p < NP2; ++p) s = dot2(w[fn][c * NP2 + p], ahi[p], s);
-#pragma unroll
-            for (int p = 0; p < NP2; ++p) s = dot2(w[fn][c * NP2 + p], alo[p], s);
-            f[c] = s;
-        }
-        u32x4_t pk;
-        pk.x = pack_bf16x2(f[0], f[1]); pk.y = pack_bf16x2(f[2], f[3]);
-        pk.z = pack_bf16x2(f[4], f[5]); pk.w = pack_bf16x2(f[6], f[7]);
-        bfr[fn] = __builtin_bit_cast(bf16x8_t, pk);
+        for (int p = 0; p < NP2; ++p) s = dot2(w[c * NP2 + p], alo[p], s);
+        f[c] = s;
     }
+    u32x4_t pk;
+    pk.x = pack_bf16x2(f[0], f[1]); pk.y = pack_bf16x2(f[2], f[3]);
+    pk.z = pack_bf16x2(f[4], f[5]); pk.w = pack_bf16x2(f[6], f[7]);
+    return pk;
 }
 
-// Fused: 4 waves = 4 examples; all positions of an example in one wave. Each
-// wave owns a private LDS tile, so no workgroup barrier is needed: LDS
-// operations of one wave execute in program order.
-//
-// Software pipeline over steps s = (chunk c, tap t):
-//   - the packed expert words of step s+2 load while step s computes;
-//   - the B fragments of step s+1 are mixed (VALU) while the MFMAs of step s
-//     run (independent instructions the scheduler interleaves);
-//   - the input chunk c+1 loads into registers during chunk c and is written
-//     to the tile after the last tap of chunk c has read it.
-template <int FM, int FN, int NP2, int XT>
+// Fused: a workgroup owns 4 examples and 64 output channels; 4 waves.
+//   - Mixing is split by output channels: wave w mixes the 16-channel
+//     fragment w for all 4 examples (the expert tile is read once per
+//     workgroup) and writes the 4 bf16 B fragments to a double-buffered LDS
+//     stage;
+//   - the MFMAs are split by examples: wave w convolves example w over all
+//     its positions (P <= FM*16) and all 64 channels, reading its 4 B
+//     fragments from the stage and its A fragments from its own input tile.
+// Software pipeline over steps s = (chunk c, tap t), one barrier per step:
+// the MFMAs of step s run while the B fragments of step s+1 are mixed and
+// the expert words of step s+2 load; the next input chunk loads into
+// registers during a chunk and is written to the tile after its last tap.
+template <int FM, int NP2, int XT>
 __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ packed,
                                                          const float *__restrict__ alpha,
                                                          uint16_t *__restrict__ y, ConvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    constexpr int NT = FN * 16;
+    constexpr int FN = 4;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int ot = logical / a.n_btiles;
     const int bt = logical - ot * a.n_btiles;
+    const int o0 = ot * FN * 16;
+    const int tile_elems = a.tile_rows * a.ncols * kPosStride;
+    uint16_t *tile = lds + wave * tile_elems;
+    // B stage: [2 buffers][4 examples][4 fragments][64 lanes] x 16 bytes
+    u32x4_t *bstage = reinterpret_cast<u32x4_t *>(lds + 4 * tile_elems);
+    auto bslot = [&](int buf, int e, int fn) { return bstage + ((buf * 4 + e) * FN + fn) * 64 + lane; };
+
+    // attentions of the workgroup's 4 examples as bf16 high/low pairs
+    uint32_t ahi[4][NP2], alo[4][NP2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int be = min(bt * 4 + e, a.B - 1);
+#pragma unroll
+        for (int p = 0; p < NP2; ++p) {
+            const float a0 = 2 * p < a.n ? alpha[(long)be * a.n + 2 * p] : 0.f;
+            const float a1 = 2 * p + 1 < a.n ? alpha[(long)be * a.n + 2 * p + 1] : 0.f;
+            ahi[e][p] = pack_bf16x2(a0, a1);
+            alo[e][p] = pack_bf16x2(a0 - bf16_lo(ahi[e][p]), a1 - bf16_hi(ahi[e][p]));
+        }
+    }
     const int b_raw = bt * 4 + wave;
     const bool valid = b_raw < a.B;
     const int b = valid ? b_raw : a.B - 1;
-    const int o0 = ot * NT;
-    const int tile_elems = a.tile_rows * a.ncols * kPosStride;
-    uint16_t *tile = lds + wave * tile_elems;
 
     zero_lds(tile, tile_elems, lane, 64);
-
-    // attentions of example b as bf16 high/low pairs
-    uint32_t ahi[NP2], alo[NP2];
-#pragma unroll
-    for (int p = 0; p < NP2; ++p) {
-        const float a0 = 2 * p < a.n ? alpha[(long)b * a.n + 2 * p] : 0.f;
-        const float a1 = 2 * p + 1 < a.n ? alpha[(long)b * a.n + 2 * p + 1] : 0.f;
-        ahi[p] = pack_bf16x2(a0, a1);
-        alo[p] = pack_bf16x2(a0 - bf16_lo(ahi[p]), a1 - bf16_hi(ahi[p]));
-    }
 
     int aoff[FM];
 #pragma unroll
@@ -381,10 +402,7 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
         aoff[fm] = ((r * a.stride) * a.ncols + s * a.stride) * kPosStride + 8 * lg;
     }
     const uint16_t *xb = x + (long)b * a.x_bstride;
-    long prow[FN];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-        prow[fn] = ((long)min(o0 + fn * 16 + lr, a.Cout - 1) * a.Cin_pad + 8 * lg) * NP2;
+    const long prow = ((long)min(o0 + wave * 16 + lr, a.Cout - 1) * a.Cin_pad + 8 * lg) * NP2;
 
     f32x4_t acc[FM][FN];
 #pragma unroll
@@ -397,47 +415,54 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
     const int nrows = min(a.H, h_tile0 + a.tile_rows);
     const int nchunks = a.Cin_pad / kChunk;
     const int nsteps = nchunks * a.KT;
+    const int HW = a.H * a.W;
 
+    StageMap<XT> smap;
+    stage_map<XT>(a, nrows, h_tile0, lane, smap);
     uint32_t xr[XT][8];
-    stage_load_paired<XT>(xb, a, 0, nrows, lane, xr);
-    stage_store_paired<XT>(tile, a, nrows, h_tile0, lane, xr);
+    stage_load<XT>(xb, a, 0, smap, xr);
+    stage_store<XT>(tile, smap, xr);
 
-    uint32_t w[FN][8 * NP2];
-    bf16x8_t bcur[FN], bnext[FN];
-    load_packed<FN, NP2>(packed, a, 0, 0, prow, w);
-    mix_frags<FN, NP2>(w, ahi, alo, bcur);
-    if (nsteps > 1) load_packed<FN, NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
+    uint32_t w[8 * NP2];
+    load_packed<NP2>(packed, a, 0, 0, prow, w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *bslot(0, e, wave) = mix_frag<NP2>(w, ahi[e], alo[e]);
+    if (nsteps > 1) load_packed<NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
+    __syncthreads();
 
     int t = 0, c0 = 0;
     for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
         if (t == 0 && c0 + kChunk < a.Cin_pad)
-            stage_load_paired<XT>(xb, a, c0 + kChunk, nrows, lane, xr);
+            stage_load<XT>(xb + (long)(c0 + kChunk) * HW, a, c0 + kChunk, smap, xr);
         const int u = t / a.KW, v = t - u * a.KW;
         const int toff = (u * a.ncols + v) * kPosStride;
+        bf16x8_t bfr[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) bfr[fn] = __builtin_bit_cast(bf16x8_t, *bslot(buf, wave, fn));
         bf16x8_t afr[FM];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
             afr[fm] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[fm] + toff);
+        if (s + 1 < nsteps) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *bslot(buf ^ 1, e, wave) = mix_frag<NP2>(w, ahi[e], alo[e]);
+            if (s + 2 < nsteps) {
+                const int c2 = (s + 2) / a.KT;
+                load_packed<NP2>(packed, a, s + 2 - c2 * a.KT, c2 * kChunk, prow, w);
+            }
+        }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[fm], bcur[fn], acc[fm][fn], 0, 0, 0);
-        if (s + 1 < nsteps) {
-            mix_frags<FN, NP2>(w, ahi, alo, bnext);
-            if (s + 2 < nsteps) {
-                const int s2 = s + 2;
-                const int c2 = s2 / a.KT;
-                load_packed<FN, NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) bcur[fn] = bnext[fn];
-        }
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
         if (++t == a.KT) {
             t = 0;
-            if (c0 + kChunk < a.Cin_pad) stage_store_paired<XT>(tile, a, nrows, h_tile0, lane, xr);
+            if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);
             c0 += kChunk;
         }
+        __syncthreads();
     }
     if (!valid) return;
 #pragma unroll
@@ -480,9 +505,9 @@ PremixCfg pick_premix(const Geom &g) {
 bool paired_ok(const Geom &g) { return (g.W % 2) == 0; }
 
 template <typename K>
-void set_lds(K kern, size_t bytes) {
-    hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+hipError_t set_lds(K kern, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 template <int FM, int FN, int NW>
@@ -497,11 +522,11 @@ hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *w
     const long blocks = (long)g.B * a.n_ptiles * a.n_otiles;
     if (paired_ok(g)) {
         auto k = conv_premix_kernel<FM, FN, NW, true>;
-        set_lds(k, lds);
+        if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
         hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a);
     } else {
         auto k = conv_premix_kernel<FM, FN, NW, false>;
-        set_lds(k, lds);
+        if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
         hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a);
     }
     return hipGetLastError();
@@ -509,15 +534,12 @@ hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *w
 
 constexpr int kFusedFM = 13;  // positions per example <= 208
 constexpr int kFusedXT = 8;   // staging tasks per lane: 4 * rows * W/2 <= 512
-// Output-channel fragments per workgroup: 64 channels for up to 4 experts;
-// fewer as the packed words per step (8 * NP2 per fragment) grow, to stay
-// within the register file.
-constexpr int fused_fn(int np2) { return np2 <= 2 ? 4 : (np2 <= 4 ? 2 : 1); }
 
 int fused_tile_rows(const Geom &g) { return (g.Ho - 1) * g.stride + g.KH; }
 
 size_t fused_lds_bytes(const Geom &g) {
-    return 4 * (size_t)fused_tile_rows(g) * (g.W + 2 * g.pad) * kPosStride * sizeof(uint16_t);
+    const size_t tiles = 4 * (size_t)fused_tile_rows(g) * (g.W + 2 * g.pad) * kPosStride * sizeof(uint16_t);
+    return tiles + 2 * 4 * 4 * 64 * 16;  // + double-buffered B stage
 }
 
 template <int NP2>
@@ -526,12 +548,11 @@ hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *pac
     ConvArgs a = base_args(g);
     a.tile_rows = fused_tile_rows(g);
     a.n_btiles = ceil_div(g.B, 4);
-    constexpr int FN = fused_fn(NP2);
-    a.n_otiles = ceil_div(g.Cout, FN * 16);
+    a.n_otiles = ceil_div(g.Cout, 64);
     const size_t lds = fused_lds_bytes(g);
     const long blocks = (long)a.n_btiles * a.n_otiles;
-    auto k = conv_fused_kernel<kFusedFM, FN, NP2, kFusedXT>;
-    set_lds(k, lds);
+    auto k = conv_fused_kernel<kFusedFM, NP2, kFusedXT>;
+    if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
     return hipGetLastError();
 }
@@ -553,7 +574,7 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
 
 bool fused_conv_supported(const Geom &g) {
     const int rows = std::min(g.H, fused_tile_rows(g) - g.pad);
-    return g.bf16 && g.groups == 1 && g.n_pad <= 16 && g.P <= kFusedFM * 16 &&
+    return g.bf16 && g.groups == 1 && g.n_pad <= 8 && g.P <= kFusedFM * 16 &&
            g.W % 2 == 0 && 4 * rows * (g.W / 2) <= 64 * kFusedXT &&
            fused_lds_bytes(g) <= (size_t)kLdsBudget;
 }
@@ -566,10 +587,6 @@ hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *p
     case 2: return launch_fused_np<2>(g, x, pk, alpha, y, stream);
     case 3: return launch_fused_np<3>(g, x, pk, alpha, y, stream);
     case 4: return launch_fused_np<4>(g, x, pk, alpha, y, stream);
-    case 5: return launch_fused_np<5>(g, x, pk, alpha, y, stream);
-    case 6: return launch_fused_np<6>(g, x, pk, alpha, y, stream);
-    case 7: return launch_fused_np<7>(g, x, pk, alpha, y, stream);
-    case 8: return launch_fused_np<8>(g, x, pk, alpha, y, stream);
     default: return hipErrorInvalidValue;
     }
 }
