@@ -343,36 +343,40 @@ __device__ __forceinline__ u32x4_t mix_frag(const uint32_t (&w)[8 * NP2], const 
     return pk;
 }
 
-// Fused: a workgroup owns 4 examples and 64 output channels; 4 waves.
-//   - Mixing is split by output channels: wave w mixes the 16-channel
-//     fragment w for all 4 examples (the expert tile is read once per
-//     workgroup) and writes the 4 bf16 B fragments to a double-buffered LDS
-//     stage;
+// Fused: a workgroup owns 4 examples and 64 output channels; 4 waves, one
+// per SIMD. The convolution runs on v_mfma_f32_32x32x16_bf16 (32 positions x
+// 32 channels x 16 K per instruction), which keeps the matrix core busy from
+// a single wave per SIMD.
+//   - Mixing is split by fragments: per step (32 input channels of one tap)
+//     each example needs 4 B fragments (2 blocks of 32 output channels x 2
+//     halves of 16 input channels); wave w mixes fragment w for all 4
+//     examples, so the expert tile is read once per workgroup, and writes
+//     the bf16 fragments to a double-buffered LDS stage;
 //   - the MFMAs are split by examples: wave w convolves example w over all
-//     its positions (P <= FM*16) and all 64 channels, reading its 4 B
+//     its positions (P <= PB*32) and all 64 channels, reading its 4 B
 //     fragments from the stage and its A fragments from its own input tile.
 // Software pipeline over steps s = (chunk c, tap t), one barrier per step:
 // the MFMAs of step s run while the B fragments of step s+1 are mixed and
 // the expert words of step s+2 load; the next input chunk loads into
 // registers during a chunk and is written to the tile after its last tap.
-template <int FM, int NP2, int XT>
+template <int PB, int NP2, int XT>
 __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ packed,
                                                          const float *__restrict__ alpha,
                                                          uint16_t *__restrict__ y, ConvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    constexpr int FN = 4;
+    constexpr int CB = 2;  // 2 x 32 output channels
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int ot = logical / a.n_btiles;
     const int bt = logical - ot * a.n_btiles;
-    const int o0 = ot * FN * 16;
+    const int o0 = ot * CB * 32;
     const int tile_elems = a.tile_rows * a.ncols * kPosStride;
     uint16_t *tile = lds + wave * tile_elems;
     // B stage: [2 buffers][4 examples][4 fragments][64 lanes] x 16 bytes
     u32x4_t *bstage = reinterpret_cast<u32x4_t *>(lds + 4 * tile_elems);
-    auto bslot = [&](int buf, int e, int fn) { return bstage + ((buf * 4 + e) * FN + fn) * 64 + lane; };
+    auto bslot = [&](int buf, int e, int f) { return bstage + ((buf * 4 + e) * 4 + f) * 64 + lane; };
 
     // attentions of the workgroup's 4 examples as bf16 high/low pairs
     uint32_t ahi[4][NP2], alo[4][NP2];
@@ -393,22 +397,27 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
 
     zero_lds(tile, tile_elems, lane, 64);
 
-    int aoff[FM];
+    // A fragment of position block pb: lane -> position pb*32 + l32, 8 channels at 8*lh
+    int aoff[PB];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        const int p = min(fm * 16 + lr, a.P - 1);
+    for (int pb = 0; pb < PB; ++pb) {
+        const int p = min(pb * 32 + l32, a.P - 1);
         const int r = p / a.Wo;
         const int s = p - r * a.Wo;
-        aoff[fm] = ((r * a.stride) * a.ncols + s * a.stride) * kPosStride + 8 * lg;
+        aoff[pb] = ((r * a.stride) * a.ncols + s * a.stride) * kPosStride + 8 * lh;
     }
     const uint16_t *xb = x + (long)b * a.x_bstride;
-    const long prow = ((long)min(o0 + wave * 16 + lr, a.Cout - 1) * a.Cin_pad + 8 * lg) * NP2;
+    // fragment this wave mixes: channel block wave >> 1, K half wave & 1
+    const long prow =
+        ((long)min(o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh) * NP2;
 
-    f32x4_t acc[FM][FN];
+    f32x16_t acc[PB][CB];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < PB; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < CB; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     // input rows the tile holds (rows below the last output's reach are not needed)
     const int h_tile0 = -a.pad;
@@ -437,26 +446,43 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
             stage_load<XT>(xb + (long)(c0 + kChunk) * HW, a, c0 + kChunk, smap, xr);
         const int u = t / a.KW, v = t - u * a.KW;
         const int toff = (u * a.ncols + v) * kPosStride;
-        bf16x8_t bfr[FN];
+        bf16x8_t bfr[4];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) bfr[fn] = __builtin_bit_cast(bf16x8_t, *bslot(buf, wave, fn));
-        bf16x8_t afr[FM];
+        for (int f = 0; f < 4; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, *bslot(buf, wave, f));
+        bf16x8_t afr[PB][2];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-            afr[fm] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[fm] + toff);
-        if (s + 1 < nsteps) {
+        for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) *bslot(buf ^ 1, e, wave) = mix_frag<NP2>(w, ahi[e], alo[e]);
-            if (s + 2 < nsteps) {
-                const int c2 = (s + 2) / a.KT;
-                load_packed<NP2>(packed, a, s + 2 - c2 * a.KT, c2 * kChunk, prow, w);
-            }
+            for (int kh = 0; kh < 2; ++kh)
+                afr[pb][kh] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[pb] + toff + 16 * kh);
+        // Mix step s+1 and fetch step s+2 unconditionally (the last steps redo a
+        // valid step whose result is never read), so that the step body is one
+        // basic block the scheduler can interleave with the MFMAs.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *bslot(buf ^ 1, e, wave) = mix_frag<NP2>(w, ahi[e], alo[e]);
+        {
+            const int s2 = min(s + 2, nsteps - 1);
+            const int c2 = s2 / a.KT;
+            load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
         }
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+        for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+                    acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[pb][kh], bfr[cb * 2 + kh],
+                                                                          acc[pb][cb], 0, 0, 0);
+        // schedule: fragment reads first, then each MFMA followed by a group of
+        // mixing VALU instructions, then the stage writes and the expert loads
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * PB, 0);
+#pragma unroll
+        for (int i = 0; i < PB * CB * 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * NP2, 0);
         if (++t == a.KT) {
             t = 0;
             if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);
@@ -465,11 +491,17 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
         __syncthreads();
     }
     if (!valid) return;
+    // D of a 32x32 block: lane holds column l32 and rows 8j + 4*lh + (0..3), j = 0..3
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            store_frag(y, a, b, o0 + fn * 16 + lr, fm * 16 + 4 * lg, acc[fm][fn]);
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4_t d = {acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1], acc[pb][cb][4 * j + 2],
+                                   acc[pb][cb][4 * j + 3]};
+                store_frag(y, a, b, o0 + 32 * cb + l32, pb * 32 + 8 * j + 4 * lh, d);
+            }
 }
 
 ConvArgs base_args(const Geom &g) {
@@ -532,7 +564,7 @@ hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *w
     return hipGetLastError();
 }
 
-constexpr int kFusedFM = 13;  // positions per example <= 208
+constexpr int kFusedPB = 7;   // positions per example <= 224 (7 blocks of 32)
 constexpr int kFusedXT = 8;   // staging tasks per lane: 4 * rows * W/2 <= 512
 
 int fused_tile_rows(const Geom &g) { return (g.Ho - 1) * g.stride + g.KH; }
@@ -551,7 +583,7 @@ hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *pac
     a.n_otiles = ceil_div(g.Cout, 64);
     const size_t lds = fused_lds_bytes(g);
     const long blocks = (long)a.n_btiles * a.n_otiles;
-    auto k = conv_fused_kernel<kFusedFM, NP2, kFusedXT>;
+    auto k = conv_fused_kernel<kFusedPB, NP2, kFusedXT>;
     if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
     return hipGetLastError();
@@ -574,7 +606,7 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
 
 bool fused_conv_supported(const Geom &g) {
     const int rows = std::min(g.H, fused_tile_rows(g) - g.pad);
-    return g.bf16 && g.groups == 1 && g.n_pad <= 8 && g.P <= kFusedFM * 16 &&
+    return g.bf16 && g.groups == 1 && g.n_pad <= 8 && g.P <= kFusedPB * 32 &&
            g.W % 2 == 0 && 4 * rows * (g.W / 2) <= 64 * kFusedXT &&
            fused_lds_bytes(g) <= (size_t)kLdsBudget;
 }
