@@ -187,6 +187,7 @@ const char *dynconv_last_error(void) { return g_err; }
 size_t dynconv_route_workspace_bytes(const dynconv_desc_t *desc) {
     dynconv::Geom g;
     if (check_desc(desc, g, false) != DYNCONV_OK) return 0;
+    if (dynconv::route_single_kernel(g)) return 0;
     return round_up((size_t)g.B * g.Cin * sizeof(float), kWsAlign);
 }
 
@@ -206,7 +207,7 @@ dynconv_status_t dynconv_route(const dynconv_desc_t *desc, const void *x, const 
         return fail(DYNCONV_ERR_INVALID_ARG, "softmax temperature must be finite and > 0");
     if (g.n > 256) return fail(DYNCONV_ERR_UNSUPPORTED, "routing supports n <= 256 experts (got %d)", g.n);
     const size_t need = dynconv_route_workspace_bytes(desc);
-    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+    if (need > 0 && (workspace_bytes < need || !workspace || !aligned16(workspace)))
         return fail(DYNCONV_ERR_WORKSPACE, "route needs %zu bytes of 16-byte aligned workspace (got %zu)",
                     need, workspace_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);

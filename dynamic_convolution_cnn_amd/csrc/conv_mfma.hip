@@ -45,6 +45,10 @@
 namespace dynconv {
 namespace {
 
+#ifndef DYNCONV_SCHED_INTERLEAVE
+#define DYNCONV_SCHED_INTERLEAVE 0
+#endif
+
 constexpr int kPosStride = 40;  // bf16 per LDS position (32 channels + pad)
 constexpr int kChunk = 32;      // input channels per K chunk
 constexpr int kLdsBudget = 160 * 1024;
@@ -465,14 +469,17 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
             const int c2 = s2 / a.KT;
             load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
         }
+        // K half outermost: the 14 MFMAs between two updates of one
+        // accumulator keep the matrix pipeline full
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
+            for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+                for (int cb = 0; cb < CB; ++cb)
                     acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[pb][kh], bfr[cb * 2 + kh],
                                                                           acc[pb][cb], 0, 0, 0);
+#if DYNCONV_SCHED_INTERLEAVE
         // schedule: fragment reads first, then each MFMA followed by a group of
         // mixing VALU instructions, then the stage writes and the expert loads
         __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * PB, 0);
@@ -483,6 +490,7 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
         }
         __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 2 * NP2, 0);
+#endif
         if (++t == a.KT) {
             t = 0;
             if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);

@@ -24,6 +24,9 @@ struct Geom {
 // ---- routing -------------------------------------------------------------
 // gap[B*Cin] (float) = channel means of x; then alpha[B,n] from the FC and
 // the nonlinearity. `gap` is caller-provided scratch of B*Cin floats.
+// True when routing runs as one kernel (one workgroup per example) and
+// needs no `gap` scratch.
+bool route_single_kernel(const Geom &g);
 hipError_t launch_route(const Geom &g, const void *x, const float *fc_w,
                         const float *fc_b, int mode, float temperature,
                         float *gap, float *alpha, hipStream_t stream);

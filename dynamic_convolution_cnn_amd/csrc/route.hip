@@ -19,6 +19,8 @@ namespace dynconv {
 namespace {
 
 constexpr int kGapThreads = 256;
+// batches at least this large route with one workgroup per example
+constexpr int kRouteMinB = 128;
 
 // VEC elements per load (VEC * sizeof(T) bytes); LPR lanes per plane.
 template <typename T, int VEC, int LPR>
@@ -142,6 +144,132 @@ __global__ __launch_bounds__(256) void route_fc_kernel(const float *__restrict__
     }
 }
 
+// Single-kernel routing for batches that fill the chip: one workgroup per
+// example. Phase 1 streams the example's channel planes (LPR lanes per plane,
+// VEC-element loads, two planes per lane in flight) into channel means in
+// LDS; phase 2 computes the logits (one wave per expert, lanes over
+// channels, fixed-order reduction); phase 3 applies the nonlinearity. No
+// workspace and no second launch.
+constexpr int kRouteThreads = 512;
+constexpr int kRouteMaxC = 4096;
+template <typename T, int VEC, int LPR>
+__global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(
+    const T *__restrict__ x, const float *__restrict__ fc_w, const float *__restrict__ fc_b,
+    float *__restrict__ alpha, int C, int hw, int n, int mode, float temp) {
+    __shared__ float gsh[kRouteMaxC];
+    __shared__ float zsh[64 * kMaxJ];
+    constexpr int kGroups = kRouteThreads / LPR;  // planes per pass
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int grp = tid / LPR, lane_in = tid % LPR;
+    const int nvec = hw / VEC;
+    const T *xb = x + (long)b * C * hw;
+    for (int c0 = 0; c0 < C; c0 += 2 * kGroups) {
+        const int ca = c0 + grp, cb = c0 + kGroups + grp;
+        float sa = 0.f, sb = 0.f;
+        const T *pa = xb + (long)min(ca, C - 1) * hw;
+        const T *pb = xb + (long)min(cb, C - 1) * hw;
+        for (int i = lane_in; i < nvec; i += LPR) {
+            if constexpr (sizeof(T) == 2 && VEC == 8) {
+                const u32x4_t qa = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(pa) + i);
+                const u32x4_t qb = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(pb) + i);
+                sa += (bf16_lo(qa.x) + bf16_hi(qa.x)) + (bf16_lo(qa.y) + bf16_hi(qa.y)) +
+                      ((bf16_lo(qa.z) + bf16_hi(qa.z)) + (bf16_lo(qa.w) + bf16_hi(qa.w)));
+                sb += (bf16_lo(qb.x) + bf16_hi(qb.x)) + (bf16_lo(qb.y) + bf16_hi(qb.y)) +
+                      ((bf16_lo(qb.z) + bf16_hi(qb.z)) + (bf16_lo(qb.w) + bf16_hi(qb.w)));
+            } else if constexpr (sizeof(T) == 2 && VEC == 4) {
+                const u32x2_t qa = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(pa) + i);
+                const u32x2_t qb = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(pb) + i);
+                sa += (bf16_lo(qa.x) + bf16_hi(qa.x)) + (bf16_lo(qa.y) + bf16_hi(qa.y));
+                sb += (bf16_lo(qb.x) + bf16_hi(qb.x)) + (bf16_lo(qb.y) + bf16_hi(qb.y));
+            } else if constexpr (sizeof(T) == 4 && VEC == 4) {
+                const f32x4_t qa = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(pa) + i);
+                const f32x4_t qb = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(pb) + i);
+                sa += (qa[0] + qa[1]) + (qa[2] + qa[3]);
+                sb += (qb[0] + qb[1]) + (qb[2] + qb[3]);
+            } else {
+                static_assert(VEC == 1, "unsupported vector width");
+                sa += Elem<T>::to_f32(pa[i]);
+                sb += Elem<T>::to_f32(pb[i]);
+            }
+        }
+        sa = group_sum<LPR>(sa);
+        sb = group_sum<LPR>(sb);
+        if (lane_in == 0) {
+            if (ca < C) gsh[ca] = sa / (float)hw;
+            if (cb < C) gsh[cb] = sb / (float)hw;
+        }
+    }
+    __syncthreads();
+    const int wave = tid / 64, lane = tid % 64;
+    for (int i = wave; i < n; i += kRouteThreads / 64) {
+        float part = 0.f;
+        for (int c = lane; c < C; c += 64) part = fmaf(fc_w[(long)i * C + c], gsh[c], part);
+        part = wave_sum(part);
+        if (lane == 0) zsh[i] = part + (fc_b ? fc_b[i] : 0.f);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float z[kMaxJ];
+#pragma unroll
+    for (int j = 0; j < kMaxJ; ++j) z[j] = (lane + 64 * j < n) ? zsh[lane + 64 * j] : 0.f;
+    if (mode == 0) {
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+            const int i = lane + 64 * j;
+            if (i < n) {
+                float av;
+                if (z[j] >= 0.f) {
+                    av = 1.f / (1.f + expf(-z[j]));
+                } else {
+                    const float e = expf(z[j]);
+                    av = e / (1.f + e);
+                }
+                alpha[(long)b * n + i] = av;
+            }
+        }
+    } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j)
+            if (lane + 64 * j < n) m = fmaxf(m, z[j] / temp);
+        m = wave_max(m);
+        float e[kMaxJ];
+        float ssum = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+            e[j] = (lane + 64 * j < n) ? expf(z[j] / temp - m) : 0.f;
+            ssum += e[j];
+        }
+        ssum = wave_sum(ssum);
+#pragma unroll
+        for (int j = 0; j < kMaxJ; ++j) {
+            const int i = lane + 64 * j;
+            if (i < n) alpha[(long)b * n + i] = e[j] / ssum;
+        }
+    }
+}
+
+template <typename T, int VEC>
+hipError_t launch_route_fused_vec(const T *x, const float *fc_w, const float *fc_b, float *alpha,
+                                  int B, int C, int hw, int n, int mode, float temp,
+                                  hipStream_t s) {
+    const int nvec = hw / VEC;
+    int lpr = 8;
+    while (lpr < 64 && lpr * 4 < nvec) lpr *= 2;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(B), dim3(kRouteThreads), 0, s, x, fc_w, fc_b, alpha, C, hw,
+                           n, mode, temp);
+        return hipGetLastError();
+    };
+    switch (lpr) {
+    case 8: return go(route_fused_kernel<T, VEC, 8>);
+    case 16: return go(route_fused_kernel<T, VEC, 16>);
+    case 32: return go(route_fused_kernel<T, VEC, 32>);
+    default: return go(route_fused_kernel<T, VEC, 64>);
+    }
+}
+
 template <typename T, int VEC>
 hipError_t launch_gap_vec(const T *x, float *gap, long rows, int hw, hipStream_t s) {
     const int nvec = hw / VEC;
@@ -166,11 +294,25 @@ hipError_t launch_gap_vec(const T *x, float *gap, long rows, int hw, hipStream_t
 
 static_assert(kMaxJ * 64 >= 256, "route kernel covers n <= 256");
 
+bool route_single_kernel(const Geom &g) { return g.B >= kRouteMinB && g.Cin <= kRouteMaxC; }
+
 hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const float *fc_b,
                         int mode, float temperature, float *gap, float *alpha,
                         hipStream_t stream) {
     const long rows = (long)g.B * g.Cin;
     const int hw = g.H * g.W;
+    const float tp = mode == 1 ? temperature : 1.0f;
+    if (route_single_kernel(g)) {
+        if (g.bf16) {
+            const uint16_t *xb = static_cast<const uint16_t *>(x);
+            if (hw % 8 == 0) return launch_route_fused_vec<uint16_t, 8>(xb, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
+            if (hw % 4 == 0) return launch_route_fused_vec<uint16_t, 4>(xb, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
+            return launch_route_fused_vec<uint16_t, 1>(xb, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
+        }
+        const float *xf = static_cast<const float *>(x);
+        if (hw % 4 == 0) return launch_route_fused_vec<float, 4>(xf, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
+        return launch_route_fused_vec<float, 1>(xf, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
+    }
     hipError_t e;
     if (g.bf16) {
         const uint16_t *xb = static_cast<const uint16_t *>(x);

@@ -102,7 +102,9 @@ typedef struct {
  * Arguments: x [B,Cin,H,W] (dtype), fc_w [n,Cin] float32, fc_b [n] float32 or
  * NULL for no bias, temperature > 0 (ignored for sigmoid), alpha [B,n]
  * float32 (written). workspace: device memory of at least
- * dynconv_route_workspace_bytes(desc) bytes (may be NULL when that is 0);
+ * dynconv_route_workspace_bytes(desc) bytes (may be NULL when that is 0,
+ * which is the case for batches large enough to route with one workgroup
+ * per example);
  * its contents on entry do not matter and are clobbered. Only desc->B, Cin,
  * H, W, n and dtype are read. The result is deterministic: no atomics. */
 dynconv_status_t dynconv_route(const dynconv_desc_t *desc, const void *x,

@@ -112,6 +112,8 @@ def test_route_checks():
     d = good_desc()
     ws = bd.dynconv_route_workspace_bytes(d)
     assert ws >= 2 * 16 * 4
+    # large batches route with one workgroup per example and need no workspace
+    assert bd.dynconv_route_workspace_bytes(good_desc(B=256)) == 0
 
     def route(desc=d, x=FAKE, w=FAKE, b=FAKE, mode=0, t=1.0, a=FAKE, wsp=FAKE, wsb=ws):
         return L.dynconv_route(ctypes.byref(desc) if desc is not None else None, x, w, b, mode,
