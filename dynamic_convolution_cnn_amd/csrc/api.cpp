@@ -110,7 +110,7 @@ dynconv_status_t resolve_policy(const dynconv::Geom &g, int32_t policy, int32_t 
     if (policy == DYNCONV_POLICY_FUSED) {
         if (!fused_ok)
             return fail(DYNCONV_ERR_UNSUPPORTED,
-                        "fused path needs Ho*Wo <= 208 and the 4 example tiles in LDS (Ho*Wo=%d)", g.P);
+                        "fused path needs n <= 4, even W, Ho*Wo <= 256 and the 4 example tiles in LDS (Ho*Wo=%d)", g.P);
         out = policy;
         return DYNCONV_OK;
     }

@@ -241,15 +241,15 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // stage_load issues a lane's global loads into registers, stage_store writes
 // them to the tile. The per-task source and destination offsets do not
 // depend on the chunk and are computed once (StageMap). Paired layout only
-// (W even): a task is 2 neighbouring positions x 8 channels; lane owns tasks
-// lane, lane + 64, ...
+// (W even): a task is 2 neighbouring positions x 8 channels; of the NL lanes
+// staging one example, lane owns tasks lane, lane + NL, ...
 template <int XT>
 struct StageMap {
     int src[XT];  // element offset from the chunk's first channel plane
     int dst[XT];  // element offset in the tile; -1: no task
 };
 
-template <int XT>
+template <int XT, int NL>
 __device__ __forceinline__ void stage_map(const ConvArgs &a, int nrows, int h_tile0, int lane,
                                           StageMap<XT> &m) {
     const int HW = a.H * a.W;
@@ -258,7 +258,7 @@ __device__ __forceinline__ void stage_map(const ConvArgs &a, int nrows, int h_ti
     const int ntasks = 4 * per_g;
 #pragma unroll
     for (int k = 0; k < XT; ++k) {
-        const int task = lane + 64 * k;
+        const int task = lane + NL * k;
         const int g = task / per_g;
         const int rem = task - g * per_g;
         const int row = rem / pairs;
@@ -347,24 +347,26 @@ __device__ __forceinline__ u32x4_t mix_frag(const uint32_t (&w)[8 * NP2], const 
     return pk;
 }
 
-// Fused: a workgroup owns 4 examples and 64 output channels; 4 waves, one
-// per SIMD. The convolution runs on v_mfma_f32_32x32x16_bf16 (32 positions x
-// 32 channels x 16 K per instruction), which keeps the matrix core busy from
-// a single wave per SIMD.
-//   - Mixing is split by fragments: per step (32 input channels of one tap)
-//     each example needs 4 B fragments (2 blocks of 32 output channels x 2
-//     halves of 16 input channels); wave w mixes fragment w for all 4
-//     examples, so the expert tile is read once per workgroup, and writes
-//     the bf16 fragments to a double-buffered LDS stage;
-//   - the MFMAs are split by examples: wave w convolves example w over all
-//     its positions (P <= PB*32) and all 64 channels, reading its 4 B
-//     fragments from the stage and its A fragments from its own input tile.
+// Fused: a workgroup owns 4 examples and 64 output channels; 8 waves, two
+// per SIMD, so that one wave's mixing and memory work overlaps the other
+// wave's MFMAs. The convolution runs on v_mfma_f32_32x32x16_bf16 (32
+// positions x 32 channels x 16 K per instruction).
+//   - MFMAs: waves w and w+4 share example e = w & 3; wave w < 4 takes the
+//     first PBW blocks of 32 positions, wave w + 4 the rest, all 64 channels;
+//     A fragments come from the example's input tile, B fragments from the
+//     stage below.
+//   - Mixing: per step (32 input channels of one tap) each example needs 4 B
+//     fragments (2 blocks of 32 output channels x 2 halves of 16 input
+//     channels). Wave w mixes fragment w & 3 for examples 2(w >> 2) and
+//     2(w >> 2) + 1, and writes the bf16 fragments to a double-buffered LDS
+//     stage, so the expert tile is read once per pair of waves.
+//   - Staging: the two waves of an example stage its input chunk together.
 // Software pipeline over steps s = (chunk c, tap t), one barrier per step:
 // the MFMAs of step s run while the B fragments of step s+1 are mixed and
 // the expert words of step s+2 load; the next input chunk loads into
 // registers during a chunk and is written to the tile after its last tap.
-template <int PB, int NP2, int XT>
-__global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restrict__ x,
+template <int PBW, int NP2, int XT>
+__global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ packed,
                                                          const float *__restrict__ alpha,
                                                          uint16_t *__restrict__ y, ConvArgs a) {
@@ -372,52 +374,57 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
     constexpr int CB = 2;  // 2 x 32 output channels
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const int ex = wave & 3, half = wave >> 2;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int ot = logical / a.n_btiles;
     const int bt = logical - ot * a.n_btiles;
     const int o0 = ot * CB * 32;
     const int tile_elems = a.tile_rows * a.ncols * kPosStride;
-    uint16_t *tile = lds + wave * tile_elems;
+    uint16_t *tile = lds + ex * tile_elems;
     // B stage: [2 buffers][4 examples][4 fragments][64 lanes] x 16 bytes
     u32x4_t *bstage = reinterpret_cast<u32x4_t *>(lds + 4 * tile_elems);
     auto bslot = [&](int buf, int e, int f) { return bstage + ((buf * 4 + e) * 4 + f) * 64 + lane; };
 
-    // attentions of the workgroup's 4 examples as bf16 high/low pairs
-    uint32_t ahi[4][NP2], alo[4][NP2];
+    // mixing role: fragment mf for examples 2*half and 2*half + 1
+    const int mf = wave & 3;
+    uint32_t ahi[2][NP2], alo[2][NP2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int be = min(bt * 4 + e, a.B - 1);
+    for (int k = 0; k < 2; ++k) {
+        const int be = min(bt * 4 + 2 * half + k, a.B - 1);
 #pragma unroll
         for (int p = 0; p < NP2; ++p) {
             const float a0 = 2 * p < a.n ? alpha[(long)be * a.n + 2 * p] : 0.f;
             const float a1 = 2 * p + 1 < a.n ? alpha[(long)be * a.n + 2 * p + 1] : 0.f;
-            ahi[e][p] = pack_bf16x2(a0, a1);
-            alo[e][p] = pack_bf16x2(a0 - bf16_lo(ahi[e][p]), a1 - bf16_hi(ahi[e][p]));
+            ahi[k][p] = pack_bf16x2(a0, a1);
+            alo[k][p] = pack_bf16x2(a0 - bf16_lo(ahi[k][p]), a1 - bf16_hi(ahi[k][p]));
         }
     }
-    const int b_raw = bt * 4 + wave;
+    const long prow =
+        ((long)min(o0 + 32 * (mf >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (mf & 1) + 8 * lh) * NP2;
+
+    // convolution role: example ex, position blocks [pb0, pb0 + npb)
+    const int b_raw = bt * 4 + ex;
     const bool valid = b_raw < a.B;
     const int b = valid ? b_raw : a.B - 1;
+    const int pbt = ceil_div(a.P, 32);
+    const int pb0 = half * PBW;
+    const int npb = min(PBW, pbt - pb0);
 
-    zero_lds(tile, tile_elems, lane, 64);
+    zero_lds(tile, tile_elems, half * 64 + lane, 128);
 
-    // A fragment of position block pb: lane -> position pb*32 + l32, 8 channels at 8*lh
-    int aoff[PB];
+    int aoff[PBW];
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) {
-        const int p = min(pb * 32 + l32, a.P - 1);
+    for (int pb = 0; pb < PBW; ++pb) {
+        const int p = min((pb0 + pb) * 32 + l32, a.P - 1);
         const int r = p / a.Wo;
         const int s = p - r * a.Wo;
         aoff[pb] = ((r * a.stride) * a.ncols + s * a.stride) * kPosStride + 8 * lh;
     }
     const uint16_t *xb = x + (long)b * a.x_bstride;
-    // fragment this wave mixes: channel block wave >> 1, K half wave & 1
-    const long prow =
-        ((long)min(o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh) * NP2;
 
-    f32x16_t acc[PB][CB];
+    f32x16_t acc[PBW][CB];
 #pragma unroll
-    for (int i = 0; i < PB; ++i)
+    for (int i = 0; i < PBW; ++i)
 #pragma unroll
         for (int j = 0; j < CB; ++j)
 #pragma unroll
@@ -431,15 +438,16 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
     const int HW = a.H * a.W;
 
     StageMap<XT> smap;
-    stage_map<XT>(a, nrows, h_tile0, lane, smap);
+    stage_map<XT, 128>(a, nrows, h_tile0, half * 64 + lane, smap);
     uint32_t xr[XT][8];
+    __syncthreads();  // tile zeroed by both waves of the example
     stage_load<XT>(xb, a, 0, smap, xr);
     stage_store<XT>(tile, smap, xr);
 
     uint32_t w[8 * NP2];
     load_packed<NP2>(packed, a, 0, 0, prow, w);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *bslot(0, e, wave) = mix_frag<NP2>(w, ahi[e], alo[e]);
+    for (int k = 0; k < 2; ++k) *bslot(0, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
     if (nsteps > 1) load_packed<NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
     __syncthreads();
 
@@ -452,45 +460,34 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
         const int toff = (u * a.ncols + v) * kPosStride;
         bf16x8_t bfr[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, *bslot(buf, wave, f));
-        bf16x8_t afr[PB][2];
+        for (int f = 0; f < 4; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, *bslot(buf, ex, f));
+        // K half outermost: the MFMAs between two updates of one accumulator
+        // keep the matrix pipeline full
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb)
+        for (int kh = 0; kh < 2; ++kh) {
+            bf16x8_t afr[PBW];
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-                afr[pb][kh] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[pb] + toff + 16 * kh);
-        // Mix step s+1 and fetch step s+2 unconditionally (the last steps redo a
-        // valid step whose result is never read), so that the step body is one
-        // basic block the scheduler can interleave with the MFMAs.
+            for (int pb = 0; pb < PBW; ++pb)
+                afr[pb] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[pb] + toff + 16 * kh);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) *bslot(buf ^ 1, e, wave) = mix_frag<NP2>(w, ahi[e], alo[e]);
+            for (int pb = 0; pb < PBW; ++pb) {
+                if (pb < npb) {
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[pb], bfr[cb * 2 + kh],
+                                                                              acc[pb][cb], 0, 0, 0);
+                }
+            }
+        }
+        // mix step s+1 and fetch step s+2 (the last steps redo a valid step
+        // whose result is never read)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) *bslot(buf ^ 1, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
         {
             const int s2 = min(s + 2, nsteps - 1);
             const int c2 = s2 / a.KT;
             load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
         }
-        // K half outermost: the 14 MFMAs between two updates of one
-        // accumulator keep the matrix pipeline full
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[pb][kh], bfr[cb * 2 + kh],
-                                                                          acc[pb][cb], 0, 0, 0);
-#if DYNCONV_SCHED_INTERLEAVE
-        // schedule: fragment reads first, then each MFMA followed by a group of
-        // mixing VALU instructions, then the stage writes and the expert loads
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * PB, 0);
-#pragma unroll
-        for (int i = 0; i < PB * CB * 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2 * NP2, 0);
-#endif
         if (++t == a.KT) {
             t = 0;
             if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);
@@ -501,15 +498,17 @@ __global__ __launch_bounds__(256) void conv_fused_kernel(const uint16_t *__restr
     if (!valid) return;
     // D of a 32x32 block: lane holds column l32 and rows 8j + 4*lh + (0..3), j = 0..3
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb)
+    for (int pb = 0; pb < PBW; ++pb) {
+        if (pb >= npb) break;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f32x4_t d = {acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1], acc[pb][cb][4 * j + 2],
                                    acc[pb][cb][4 * j + 3]};
-                store_frag(y, a, b, o0 + 32 * cb + l32, pb * 32 + 8 * j + 4 * lh, d);
+                store_frag(y, a, b, o0 + 32 * cb + l32, (pb0 + pb) * 32 + 8 * j + 4 * lh, d);
             }
+    }
 }
 
 ConvArgs base_args(const Geom &g) {
@@ -572,8 +571,8 @@ hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *w
     return hipGetLastError();
 }
 
-constexpr int kFusedPB = 7;   // positions per example <= 224 (7 blocks of 32)
-constexpr int kFusedXT = 8;   // staging tasks per lane: 4 * rows * W/2 <= 512
+constexpr int kFusedPBW = 4;  // position blocks of 32 per wave: 2 waves cover <= 256 positions
+constexpr int kFusedXT = 4;   // staging tasks per lane: 4 * rows * W/2 <= 512 over 128 lanes
 
 int fused_tile_rows(const Geom &g) { return (g.Ho - 1) * g.stride + g.KH; }
 
@@ -591,9 +590,9 @@ hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *pac
     a.n_otiles = ceil_div(g.Cout, 64);
     const size_t lds = fused_lds_bytes(g);
     const long blocks = (long)a.n_btiles * a.n_otiles;
-    auto k = conv_fused_kernel<kFusedPB, NP2, kFusedXT>;
+    auto k = conv_fused_kernel<kFusedPBW, NP2, kFusedXT>;
     if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), lds, stream, x, packed, alpha, y, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(512), lds, stream, x, packed, alpha, y, a);
     return hipGetLastError();
 }
 
@@ -614,8 +613,8 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
 
 bool fused_conv_supported(const Geom &g) {
     const int rows = std::min(g.H, fused_tile_rows(g) - g.pad);
-    return g.bf16 && g.groups == 1 && g.n_pad <= 8 && g.P <= kFusedPB * 32 &&
-           g.W % 2 == 0 && 4 * rows * (g.W / 2) <= 64 * kFusedXT &&
+    return g.bf16 && g.groups == 1 && g.n_pad <= 4 && g.P <= 2 * kFusedPBW * 32 &&
+           g.W % 2 == 0 && 4 * rows * (g.W / 2) <= 128 * kFusedXT &&
            fused_lds_bytes(g) <= (size_t)kLdsBudget;
 }
 
@@ -625,8 +624,6 @@ hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *p
     switch (g.n_pad / 2) {
     case 1: return launch_fused_np<1>(g, x, pk, alpha, y, stream);
     case 2: return launch_fused_np<2>(g, x, pk, alpha, y, stream);
-    case 3: return launch_fused_np<3>(g, x, pk, alpha, y, stream);
-    case 4: return launch_fused_np<4>(g, x, pk, alpha, y, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -89,8 +89,9 @@ def test_forward_unsupported_layers():
     assert fwd(good_desc(Cin=16, Cout=32, groups=16)) == bd.DYNCONV_ERR_UNSUPPORTED
     # float32 has no fused path
     assert fwd(good_desc(dtype=bd.DYNCONV_F32), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
-    # fused path covers at most 208 output positions
+    # fused path covers at most 256 output positions and 4 experts
     assert fwd(good_desc(H=32, W=32), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert fwd(good_desc(n=5), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
     # bf16 groups == 1 supports up to 16 experts
     assert fwd(good_desc(n=17)) == bd.DYNCONV_ERR_UNSUPPORTED
 
