@@ -293,6 +293,33 @@ __device__ __forceinline__ void stage_load(const uint16_t *__restrict__ xc, cons
     }
 }
 
+// The loads of stage_load spread over the KT taps of a chunk: at tap t,
+// the tasks k with floor(k * KT / XT) == t.
+template <int XT>
+__device__ __forceinline__ void stage_load_part(const uint16_t *__restrict__ xc, const ConvArgs &a,
+                                                int c0, const StageMap<XT> &m, uint32_t (&r)[XT][8],
+                                                int t, int KT) {
+    const int HW2 = (a.H * a.W) >> 1;
+    const bool tail = c0 + kChunk > a.Cin;
+#pragma unroll
+    for (int k = 0; k < XT; ++k) {
+        if ((k * KT) / XT != t) continue;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(xc + m.src[k]);
+        if (!tail) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[k][j] = src[(long)j * HW2];
+        } else {
+            const int cb = c0 + (m.dst[k] >= 0 ? m.dst[k] % kPosStride : 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int jj = min(j, max(a.Cin - 1 - cb, 0));
+                const uint32_t v = src[(long)jj * HW2];
+                r[k][j] = cb + j < a.Cin ? v : 0u;
+            }
+        }
+    }
+}
+
 template <int XT>
 __device__ __forceinline__ void stage_store(uint16_t *__restrict__ tile, const StageMap<XT> &m,
                                             const uint32_t (&r)[XT][8]) {
@@ -437,12 +464,16 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
     const int nsteps = nchunks * a.KT;
     const int HW = a.H * a.W;
 
-    StageMap<XT> smap;
-    stage_map<XT, 128>(a, nrows, h_tile0, half * 64 + lane, smap);
+    // staging tasks of this lane (the two waves of an example share them)
+    const int slane = half * 64 + lane;
     uint32_t xr[XT][8];
     __syncthreads();  // tile zeroed by both waves of the example
-    stage_load<XT>(xb, a, 0, smap, xr);
-    stage_store<XT>(tile, smap, xr);
+    {
+        StageMap<XT> smap;
+        stage_map<XT, 128>(a, nrows, h_tile0, slane, smap);
+        stage_load<XT>(xb, a, 0, smap, xr);
+        stage_store<XT>(tile, smap, xr);
+    }
 
     uint32_t w[8 * NP2];
     load_packed<NP2>(packed, a, 0, 0, prow, w);
@@ -451,13 +482,11 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
     if (nsteps > 1) load_packed<NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
     __syncthreads();
 
-    int t = 0, c0 = 0;
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        if (t == 0 && c0 + kChunk < a.Cin_pad)
-            stage_load<XT>(xb + (long)(c0 + kChunk) * HW, a, c0 + kChunk, smap, xr);
-        const int u = t / a.KW, v = t - u * a.KW;
-        const int toff = (u * a.ncols + v) * kPosStride;
+    // The two waves on a SIMD (w and w + 4) run each step in opposite order
+    // (MFMAs then mixing, or mixing then MFMAs), so that the matrix core and
+    // the vector ALU work on different waves at the same time even though a
+    // barrier aligns the waves at every step boundary.
+    auto mfma_step = [&](int buf, int toff) {
         bf16x8_t bfr[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, *bslot(buf, ex, f));
@@ -465,32 +494,55 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
         // keep the matrix pipeline full
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-            bf16x8_t afr[PBW];
-#pragma unroll
-            for (int pb = 0; pb < PBW; ++pb)
-                afr[pb] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[pb] + toff + 16 * kh);
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb) {
                 if (pb < npb) {
+                    const bf16x8_t afr =
+                        *reinterpret_cast<const bf16x8_t *>(tile + aoff[pb] + toff + 16 * kh);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
-                        acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[pb], bfr[cb * 2 + kh],
+                        acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[cb * 2 + kh],
                                                                               acc[pb][cb], 0, 0, 0);
                 }
             }
         }
-        // mix step s+1 and fetch step s+2 (the last steps redo a valid step
-        // whose result is never read)
+    };
+    // mix step s+1 and fetch step s+2 (the last steps redo a valid step whose
+    // result is never read)
+    auto mix_step = [&](int buf, int s) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) *bslot(buf ^ 1, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
-        {
-            const int s2 = min(s + 2, nsteps - 1);
-            const int c2 = s2 / a.KT;
-            load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
+        const int s2 = min(s + 2, nsteps - 1);
+        const int c2 = s2 / a.KT;
+        load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
+    };
+
+    int t = 0, c0 = 0;
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        // the next input chunk's loads go out a few at a time, so that no
+        // expert load queues behind all of them
+        if (c0 + kChunk < a.Cin_pad) {
+            StageMap<XT> smap;
+            stage_map<XT, 128>(a, nrows, h_tile0, slane, smap);
+            stage_load_part<XT>(xb + (long)(c0 + kChunk) * HW, a, c0 + kChunk, smap, xr, t, a.KT);
+        }
+        const int u = t / a.KW, v = t - u * a.KW;
+        const int toff = (u * a.ncols + v) * kPosStride;
+        if (half == 0) {
+            mfma_step(buf, toff);
+            mix_step(buf, s);
+        } else {
+            mix_step(buf, s);
+            mfma_step(buf, toff);
         }
         if (++t == a.KT) {
             t = 0;
-            if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);
+            if (c0 + kChunk < a.Cin_pad) {
+                StageMap<XT> smap;
+                stage_map<XT, 128>(a, nrows, h_tile0, slane, smap);
+                stage_store<XT>(tile, smap, xr);
+            }
             c0 += kChunk;
         }
         __syncthreads();
