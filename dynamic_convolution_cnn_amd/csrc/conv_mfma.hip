@@ -236,6 +236,23 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Each dword shifted by v lanes within its 16-lane row (lane i takes lane
+// i + v; lanes past the row end read 0): v_mov_b32_dpp row_shl:v.
+__device__ __forceinline__ uint32_t dpp_shl_1(uint32_t x, int v) {
+    switch (v) {
+    case 1: return __builtin_amdgcn_mov_dpp(x, 0x101, 0xf, 0xf, true);
+    case 2: return __builtin_amdgcn_mov_dpp(x, 0x102, 0xf, 0xf, true);
+    case 3: return __builtin_amdgcn_mov_dpp(x, 0x103, 0xf, 0xf, true);
+    case 4: return __builtin_amdgcn_mov_dpp(x, 0x104, 0xf, 0xf, true);
+    case 5: return __builtin_amdgcn_mov_dpp(x, 0x105, 0xf, 0xf, true);
+    case 6: return __builtin_amdgcn_mov_dpp(x, 0x106, 0xf, 0xf, true);
+    default: return __builtin_amdgcn_mov_dpp(x, 0x107, 0xf, 0xf, true);
+    }
+}
+__device__ __forceinline__ u32x4_t dpp_shl(u32x4_t x, int v) {
+    return u32x4_t{dpp_shl_1(x.x, v), dpp_shl_1(x.y, v), dpp_shl_1(x.z, v), dpp_shl_1(x.w, v)};
+}
+
 // Input staging of the fused kernel, split in two phases so that the loads
 // of the next chunk are in flight while the current chunk computes:
 // stage_load issues a lane's global loads into registers, stage_store writes
@@ -282,33 +299,6 @@ __device__ __forceinline__ void stage_load(const uint16_t *__restrict__ xc, cons
             for (int j = 0; j < 8; ++j) r[k][j] = src[(long)j * HW2];
         } else {
             // channel of word j is c0 + 8g + j; 8g is the tile offset modulo kPosStride
-            const int cb = c0 + (m.dst[k] >= 0 ? m.dst[k] % kPosStride : 0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int jj = min(j, max(a.Cin - 1 - cb, 0));
-                const uint32_t v = src[(long)jj * HW2];
-                r[k][j] = cb + j < a.Cin ? v : 0u;
-            }
-        }
-    }
-}
-
-// The loads of stage_load spread over the KT taps of a chunk: at tap t,
-// the tasks k with floor(k * KT / XT) == t.
-template <int XT>
-__device__ __forceinline__ void stage_load_part(const uint16_t *__restrict__ xc, const ConvArgs &a,
-                                                int c0, const StageMap<XT> &m, uint32_t (&r)[XT][8],
-                                                int t, int KT) {
-    const int HW2 = (a.H * a.W) >> 1;
-    const bool tail = c0 + kChunk > a.Cin;
-#pragma unroll
-    for (int k = 0; k < XT; ++k) {
-        if ((k * KT) / XT != t) continue;
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(xc + m.src[k]);
-        if (!tail) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) r[k][j] = src[(long)j * HW2];
-        } else {
             const int cb = c0 + (m.dst[k] >= 0 ? m.dst[k] % kPosStride : 0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -464,16 +454,12 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
     const int nsteps = nchunks * a.KT;
     const int HW = a.H * a.W;
 
-    // staging tasks of this lane (the two waves of an example share them)
-    const int slane = half * 64 + lane;
+    StageMap<XT> smap;
+    stage_map<XT, 128>(a, nrows, h_tile0, half * 64 + lane, smap);
     uint32_t xr[XT][8];
     __syncthreads();  // tile zeroed by both waves of the example
-    {
-        StageMap<XT> smap;
-        stage_map<XT, 128>(a, nrows, h_tile0, slane, smap);
-        stage_load<XT>(xb, a, 0, smap, xr);
-        stage_store<XT>(tile, smap, xr);
-    }
+    stage_load<XT>(xb, a, 0, smap, xr);
+    stage_store<XT>(tile, smap, xr);
 
     uint32_t w[8 * NP2];
     load_packed<NP2>(packed, a, 0, 0, prow, w);
@@ -482,11 +468,13 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
     if (nsteps > 1) load_packed<NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
     __syncthreads();
 
-    // The two waves on a SIMD (w and w + 4) run each step in opposite order
-    // (MFMAs then mixing, or mixing then MFMAs), so that the matrix core and
-    // the vector ALU work on different waves at the same time even though a
-    // barrier aligns the waves at every step boundary.
-    auto mfma_step = [&](int buf, int toff) {
+    int t = 0, c0 = 0;
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        if (t == 0 && c0 + kChunk < a.Cin_pad)
+            stage_load<XT>(xb + (long)(c0 + kChunk) * HW, a, c0 + kChunk, smap, xr);
+        const int u = t / a.KW, v = t - u * a.KW;
+        const int toff = (u * a.ncols + v) * kPosStride;
         bf16x8_t bfr[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, *bslot(buf, ex, f));
@@ -494,55 +482,32 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
         // keep the matrix pipeline full
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
+            bf16x8_t afr[PBW];
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb)
+                afr[pb] = *reinterpret_cast<const bf16x8_t *>(tile + aoff[pb] + toff + 16 * kh);
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb) {
                 if (pb < npb) {
-                    const bf16x8_t afr =
-                        *reinterpret_cast<const bf16x8_t *>(tile + aoff[pb] + toff + 16 * kh);
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
-                        acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[cb * 2 + kh],
+                        acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[pb], bfr[cb * 2 + kh],
                                                                               acc[pb][cb], 0, 0, 0);
                 }
             }
         }
-    };
-    // mix step s+1 and fetch step s+2 (the last steps redo a valid step whose
-    // result is never read)
-    auto mix_step = [&](int buf, int s) {
+        // mix step s+1 and fetch step s+2 (the last steps redo a valid step
+        // whose result is never read)
 #pragma unroll
         for (int k = 0; k < 2; ++k) *bslot(buf ^ 1, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
-        const int s2 = min(s + 2, nsteps - 1);
-        const int c2 = s2 / a.KT;
-        load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
-    };
-
-    int t = 0, c0 = 0;
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        // the next input chunk's loads go out a few at a time, so that no
-        // expert load queues behind all of them
-        if (c0 + kChunk < a.Cin_pad) {
-            StageMap<XT> smap;
-            stage_map<XT, 128>(a, nrows, h_tile0, slane, smap);
-            stage_load_part<XT>(xb + (long)(c0 + kChunk) * HW, a, c0 + kChunk, smap, xr, t, a.KT);
-        }
-        const int u = t / a.KW, v = t - u * a.KW;
-        const int toff = (u * a.ncols + v) * kPosStride;
-        if (half == 0) {
-            mfma_step(buf, toff);
-            mix_step(buf, s);
-        } else {
-            mix_step(buf, s);
-            mfma_step(buf, toff);
+        {
+            const int s2 = min(s + 2, nsteps - 1);
+            const int c2 = s2 / a.KT;
+            load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
         }
         if (++t == a.KT) {
             t = 0;
-            if (c0 + kChunk < a.Cin_pad) {
-                StageMap<XT> smap;
-                stage_map<XT, 128>(a, nrows, h_tile0, slane, smap);
-                stage_store<XT>(tile, smap, xr);
-            }
+            if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);
             c0 += kChunk;
         }
         __syncthreads();
@@ -560,6 +525,259 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
                                    acc[pb][cb][4 * j + 3]};
                 store_frag(y, a, b, o0 + 32 * cb + l32, (pb0 + pb) * 32 + 8 * j + 4 * lh, d);
             }
+    }
+}
+
+// Fused, stride-1 layers on small images (W + 2*pad <= 16, Ho <= 16): the
+// ResNet-50-shaped 14x14 case. Workgroup plan as conv_fused_kernel (4
+// examples x 64 channels, 8 waves, cooperative mixing through an LDS
+// stage), with three changes that cut LDS traffic and registers:
+//   - output rows are padded to 16 positions, so a 32-position A fragment is
+//     two output rows, one per 16-lane DPP row; for column tap v the
+//     fragment is the tap-0 fragment shifted by v lanes within each row
+//     (v_mov_b32_dpp row_shl:v), so each kernel row costs one LDS read per
+//     fragment instead of kw. Junk columns (>= Wo) are computed and dropped;
+//   - the input tile uses a 64-byte position stride (32 channels) with the
+//     16-byte channel groups XOR-swizzled by position, which keeps the
+//     8-lane read phases conflict free, and is double buffered: the next
+//     chunk is staged one task per step into the other buffer through a
+//     handful of short-lived registers, its loads issued after the expert
+//     loads so that the in-order vmcnt never queues expert data behind them;
+//   - the epilogue transposes the output through LDS so that each lane
+//     stores 4 consecutive positions of one channel plane.
+__device__ __forceinline__ int swz(int q, int g) {
+    return q * 32 + ((g ^ ((q >> 1) & 3)) << 3);
+}
+
+template <int NP2, int XT, int KW>
+__global__ __launch_bounds__(512) void conv_fused_row16_kernel(const uint16_t *__restrict__ x,
+                                                               const uint32_t *__restrict__ packed,
+                                                               const float *__restrict__ alpha,
+                                                               uint16_t *__restrict__ y, ConvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    constexpr int CB = 2;   // 2 x 32 output channels
+    constexpr int PBW = 4;  // blocks of 2 padded rows per wave
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const int ex = wave & 3, half = wave >> 2;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int ot = logical / a.n_btiles;
+    const int bt = logical - ot * a.n_btiles;
+    const int o0 = ot * CB * 32;
+    const int tpos = a.tile_rows * a.ncols;     // positions per tile
+    const int tile_elems = tpos * 32;
+    uint16_t *tiles = lds + ex * 2 * tile_elems;  // [2 buffers] for this example
+    u32x4_t *bstage = reinterpret_cast<u32x4_t *>(lds + 8 * tile_elems);
+    auto bslot = [&](int buf, int e, int f) { return bstage + ((buf * 4 + e) * 4 + f) * 64 + lane; };
+
+    const int mf = wave & 3;
+    uint32_t ahi[2][NP2], alo[2][NP2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int be = min(bt * 4 + 2 * half + k, a.B - 1);
+#pragma unroll
+        for (int p = 0; p < NP2; ++p) {
+            const float a0 = 2 * p < a.n ? alpha[(long)be * a.n + 2 * p] : 0.f;
+            const float a1 = 2 * p + 1 < a.n ? alpha[(long)be * a.n + 2 * p + 1] : 0.f;
+            ahi[k][p] = pack_bf16x2(a0, a1);
+            alo[k][p] = pack_bf16x2(a0 - bf16_lo(ahi[k][p]), a1 - bf16_hi(ahi[k][p]));
+        }
+    }
+    const long prow =
+        ((long)min(o0 + 32 * (mf >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (mf & 1) + 8 * lh) * NP2;
+
+    const int b_raw = bt * 4 + ex;
+    const bool valid = b_raw < a.B;
+    const int b = valid ? b_raw : a.B - 1;
+    const int pbt = (a.Ho + 1) / 2;
+    const int pb0 = half * PBW;
+    const int npb = min(PBW, pbt - pb0);
+    const int slane = half * 64 + lane;  // staging lane among the example's two waves
+
+    zero_lds(tiles, 2 * tile_elems, slane, 128);
+
+    // A fragment of block pb, kernel row 0, column tap 0: lane -> padded
+    // position (row 2*pb + l32/16, column l32 % 16)
+    int aq[PBW];
+#pragma unroll
+    for (int pb = 0; pb < PBW; ++pb) {
+        const int r = min(2 * (pb0 + pb) + (l32 >> 4), a.Ho - 1);
+        const int c = min(l32 & 15, a.ncols - 1);
+        aq[pb] = r * a.ncols + c;
+    }
+    const uint16_t *xb = x + (long)b * a.x_bstride;
+    const int HW = a.H * a.W, HW2 = HW >> 1;
+    const int h_tile0 = -a.pad;
+    const int nrows = min(a.H, h_tile0 + a.tile_rows);
+    const int pairs = a.W >> 1;
+    const int per_g = nrows * pairs;
+    const int ntasks = 4 * per_g;
+
+    // one staging task: 2 neighbouring positions x 8 channels of chunk c0
+    auto task_load = [&](int k, int cc, uint32_t (&r)[8]) {
+        const int task = slane + 128 * k;
+        const int tt = min(task, ntasks - 1);
+        const int g = tt / per_g;
+        const int rem = tt - g * per_g;
+        const int row = rem / pairs;
+        const int pr = rem - row * pairs;
+        const int cb = cc + 8 * g;
+        const uint32_t *src =
+            reinterpret_cast<const uint32_t *>(xb + (long)cb * HW + row * a.W + 2 * pr);
+        const int last = a.Cin - 1 - cb;  // highest valid channel offset in this group
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t v = src[(long)min(j, max(last, 0)) * HW2];
+            r[j] = j <= last ? v : 0u;
+        }
+    };
+    auto task_store = [&](int k, uint16_t *tile, const uint32_t (&r)[8]) {
+        const int task = slane + 128 * k;
+        if (task >= ntasks) return;
+        const int g = task / per_g;
+        const int rem = task - g * per_g;
+        const int row = rem / pairs;
+        const int pr = rem - row * pairs;
+        const int q = (row - h_tile0) * a.ncols + 2 * pr + a.pad;
+        u32x4_t o0v, o1v;
+        o0v.x = lo_pair(r[0], r[1]); o0v.y = lo_pair(r[2], r[3]);
+        o0v.z = lo_pair(r[4], r[5]); o0v.w = lo_pair(r[6], r[7]);
+        o1v.x = hi_pair(r[0], r[1]); o1v.y = hi_pair(r[2], r[3]);
+        o1v.z = hi_pair(r[4], r[5]); o1v.w = hi_pair(r[6], r[7]);
+        *reinterpret_cast<u32x4_t *>(tile + swz(q, g)) = o0v;
+        *reinterpret_cast<u32x4_t *>(tile + swz(q + 1, g)) = o1v;
+    };
+
+    f32x16_t acc[PBW][CB];
+#pragma unroll
+    for (int i = 0; i < PBW; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    const int nchunks = a.Cin_pad / kChunk;
+    const int nsteps = nchunks * a.KT;
+
+    __syncthreads();  // tiles zeroed by both waves of the example
+#pragma unroll
+    for (int k = 0; k < XT; ++k) {
+        uint32_t r[8];
+        task_load(k, 0, r);
+        task_store(k, tiles, r);
+    }
+    uint32_t w[8 * NP2];
+    load_packed<NP2>(packed, a, 0, 0, prow, w);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) *bslot(0, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
+    if (nsteps > 1) load_packed<NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
+    __syncthreads();
+
+    int s = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        const uint16_t *cur = tiles + (c & 1) * tile_elems;
+        uint16_t *nxt = tiles + ((c + 1) & 1) * tile_elems;
+        const bool more = c + 1 < nchunks;
+        const int cn = (c + 1) * kChunk;
+        int i = 0;  // step within the chunk
+        for (int u = 0; u < a.KH; ++u) {
+            u32x4_t a0f[PBW][2];
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+                    a0f[pb][kh] = *reinterpret_cast<const u32x4_t *>(cur + swz(aq[pb] + u * a.ncols, 2 * kh + lh));
+#pragma unroll
+            for (int v = 0; v < KW; ++v, ++s, ++i) {
+                const int buf = s & 1;
+                // one staging task of the next chunk per step: loaded here,
+                // stored into the other tile buffer at the end of the step
+                uint32_t sr[8];
+                const bool stage_now = more && i < XT;
+                if (stage_now) task_load(i, cn, sr);
+                bf16x8_t bfr[4];
+#pragma unroll
+                for (int f = 0; f < 4; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, *bslot(buf, ex, f));
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+                    for (int pb = 0; pb < PBW; ++pb) {
+                        if (pb < npb) {
+                            const bf16x8_t afr =
+                                __builtin_bit_cast(bf16x8_t, v == 0 ? a0f[pb][kh] : dpp_shl(a0f[pb][kh], v));
+#pragma unroll
+                            for (int cb = 0; cb < CB; ++cb)
+                                acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    afr, bfr[cb * 2 + kh], acc[pb][cb], 0, 0, 0);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    *bslot(buf ^ 1, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
+                {
+                    const int s2 = min(s + 2, nsteps - 1);
+                    const int c2 = s2 / a.KT;
+                    load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
+                }
+                if (stage_now) task_store(i, nxt, sr);
+                if (more && i + 1 == a.KT) {
+                    // tasks the chunk's steps did not reach (chunks of fewer than XT steps)
+                    for (int k = i + 1; k < XT; ++k) {
+                        uint32_t r[8];
+                        task_load(k, cn, r);
+                        task_store(k, nxt, r);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+
+    // Epilogue through LDS, one 32-channel block at a time: each wave writes
+    // its D values as [channel][position of its rows], then stores 4
+    // consecutive positions of a channel plane per lane.
+    const int r_lo = 2 * pb0;                       // first output row of this wave
+    const int nr = max(0, min(a.Ho, r_lo + 2 * PBW) - r_lo);
+    const int span = nr * a.Wo;                     // positions this wave owns
+    const int pstride = (2 * PBW * 16) | 1;         // odd stride (in bf16 pairs) per channel
+    uint16_t *ebuf = lds + wave * 32 * 2 * pstride;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+        for (int pb = 0; pb < PBW; ++pb) {
+            if (pb < npb) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rl = 2 * pb + (j >> 1);
+                    const int cc = 8 * (j & 1) + 4 * lh;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (cc + q < a.Wo && r_lo + rl < a.Ho)
+                            ebuf[l32 * 2 * pstride + rl * a.Wo + cc + q] = f32_to_bf16(acc[pb][cb][4 * j + q]);
+                }
+            }
+        }
+        __syncthreads();
+        if (valid) {
+            const int chunks = (span + 3) / 4;
+            for (int ii = lane; ii < 32 * chunks; ii += 64) {
+                const int ch = ii / chunks, k4 = (ii - ch * chunks) * 4;
+                const int o = o0 + 32 * cb + ch;
+                if (o >= a.Cout) continue;
+                const long yi = ((long)b * a.Cout + o) * a.P + r_lo * a.Wo + k4;
+                const uint16_t *src = ebuf + ch * 2 * pstride + k4;
+                if (k4 + 3 < span && (yi & 3) == 0) {
+                    u32x2_t vv;
+                    vv.x = (uint32_t)src[0] | ((uint32_t)src[1] << 16);
+                    vv.y = (uint32_t)src[2] | ((uint32_t)src[3] << 16);
+                    *reinterpret_cast<u32x2_t *>(y + yi) = vv;
+                } else {
+                    for (int q = 0; q < 4 && k4 + q < span; ++q) y[yi + q] = src[q];
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -633,6 +851,21 @@ size_t fused_lds_bytes(const Geom &g) {
     return tiles + 2 * 4 * 4 * 64 * 16;  // + double-buffered B stage
 }
 
+size_t row16_lds_bytes(const Geom &g);
+
+bool row16_ok(const Geom &g) {
+    return g.stride == 1 && g.W + 2 * g.pad <= 16 && g.Ho <= 16 &&
+           (g.KW == 1 || g.KW == 3) && row16_lds_bytes(g) <= (size_t)kLdsBudget &&
+           4 * std::min(g.H, fused_tile_rows(g) - g.pad) * (g.W / 2) <= 128 * kFusedXT;
+}
+
+size_t row16_lds_bytes(const Geom &g) {
+    const size_t tiles = 8 * (size_t)fused_tile_rows(g) * (g.W + 2 * g.pad) * 32 * sizeof(uint16_t);
+    const size_t main = tiles + 2 * 4 * 4 * 64 * 16;
+    const size_t epi = 8 * (size_t)32 * 2 * ((2 * 4 * 16) | 1) * sizeof(uint16_t);
+    return main > epi ? main : epi;
+}
+
 template <int NP2>
 hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *packed,
                            const float *alpha, uint16_t *y, hipStream_t stream) {
@@ -640,8 +873,21 @@ hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *pac
     a.tile_rows = fused_tile_rows(g);
     a.n_btiles = ceil_div(g.B, 4);
     a.n_otiles = ceil_div(g.Cout, 64);
-    const size_t lds = fused_lds_bytes(g);
     const long blocks = (long)a.n_btiles * a.n_otiles;
+    if (row16_ok(g)) {
+        const size_t lds = row16_lds_bytes(g);
+        auto go = [&](auto k) {
+            if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
+            hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(512), lds, stream, x, packed, alpha, y, a);
+            return hipGetLastError();
+        };
+        switch (g.KW) {
+        case 1: return go(conv_fused_row16_kernel<NP2, kFusedXT, 1>);
+        case 3: return go(conv_fused_row16_kernel<NP2, kFusedXT, 3>);
+        default: break;  // other widths take the general fused kernel
+        }
+    }
+    const size_t lds = fused_lds_bytes(g);
     auto k = conv_fused_kernel<kFusedPBW, NP2, kFusedXT>;
     if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(512), lds, stream, x, packed, alpha, y, a);

@@ -236,6 +236,8 @@ RAGGED = [
     (6, 40, 100, 16, 16, (3, 3), 1, 1, 3),   # 256 positions, channel and Cout tails
     (3, 256, 64, 10, 12, (5, 5), 1, 2, 2),   # 5x5 on a non-square image
     (5, 32, 32, 20, 20, (3, 3), 2, 1, 4),    # stride 2
+    (3, 48, 40, 13, 14, (3, 3), 1, 1, 3),    # 16-wide padded rows, odd Ho, tails
+    (7, 64, 64, 6, 6, (3, 3), 1, 1, 4),      # small image: fewer rows than blocks
 ]
 
 
