@@ -68,4 +68,19 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Workgroup barrier for LDS traffic only. __syncthreads() also waits for
+// every outstanding global load of the wave (vmcnt(0)), which would drain
+// the prefetches a software pipeline keeps in flight across its per-step
+// barriers. Here each wave waits only for its own LDS operations
+// (lgkmcnt(0); s_waitcnt encoding with vmcnt and expcnt at their maxima),
+// then meets the others at s_barrier. The empty asm statements keep the
+// compiler from moving memory accesses across the barrier. Global memory
+// written before the barrier is NOT made visible by it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace dynconv

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
     StageMap<XT> smap;
     stage_map<XT, 128>(a, nrows, h_tile0, half * 64 + lane, smap);
     uint32_t xr[XT][8];
-    __syncthreads();  // tile zeroed by both waves of the example
+    lds_barrier();  // tile zeroed by both waves of the example
     stage_load<XT>(xb, a, 0, smap, xr);
     stage_store<XT>(tile, smap, xr);
 
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
 #pragma unroll
     for (int k = 0; k < 2; ++k) *bslot(0, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
     if (nsteps > 1) load_packed<NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
-    __syncthreads();
+    lds_barrier();
 
     int t = 0, c0 = 0;
     for (int s = 0; s < nsteps; ++s) {
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
             if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);
             c0 += kChunk;
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (!valid) return;
     // D of a 32x32 block: lane holds column l32 and rows 8j + 4*lh + (0..3), j = 0..3
@@ -528,256 +528,351 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
     }
 }
 
-// Fused, stride-1 layers on small images (W + 2*pad <= 16, Ho <= 16): the
-// ResNet-50-shaped 14x14 case. Workgroup plan as conv_fused_kernel (4
-// examples x 64 channels, 8 waves, cooperative mixing through an LDS
-// stage), with three changes that cut LDS traffic and registers:
-//   - output rows are padded to 16 positions, so a 32-position A fragment is
-//     two output rows, one per 16-lane DPP row; for column tap v the
-//     fragment is the tap-0 fragment shifted by v lanes within each row
-//     (v_mov_b32_dpp row_shl:v), so each kernel row costs one LDS read per
-//     fragment instead of kw. Junk columns (>= Wo) are computed and dropped;
-//   - the input tile uses a 64-byte position stride (32 channels) with the
-//     16-byte channel groups XOR-swizzled by position, which keeps the
-//     8-lane read phases conflict free, and is double buffered: the next
-//     chunk is staged one task per step into the other buffer through a
-//     handful of short-lived registers, its loads issued after the expert
-//     loads so that the in-order vmcnt never queues expert data behind them;
-//   - the epilogue transposes the output through LDS so that each lane
-//     stores 4 consecutive positions of one channel plane.
+// Fused, stride-1 layers on small images (W + 2*pad <= 16, Ho <= 14, input
+// plane <= 256 positions): the ResNet-50-shaped 14x14 case. A workgroup owns
+// 4 examples and 64 output channels with 4 waves, one per SIMD, so each wave
+// has the whole register file: 224 accumulators in AGPRs plus prefetch.
+//   - Mixing on the matrix cores: v_mfma_f32_4x4x4_16b_bf16 computes 16
+//     independent 4x4x4 products; with the 4 examples' attention rows as A
+//     (the same in every block) and one weight's 4 expert values per lane as
+//     B, lane l receives the 4 examples' mixed values of its own weight. Wave
+//     w mixes B fragment w (32 output channels x 16 input channels) of each
+//     step for all 4 examples with 8 such products per attention part (high
+//     and low bf16 halves, summed in fp32) and writes it to a double-buffered
+//     LDS stage; the expert tile is read once per workgroup.
+//   - Convolution: wave w convolves example w over all its positions and all
+//     64 channels on v_mfma_f32_32x32x16_bf16. Output rows are padded to 16
+//     positions, so a 32-position A fragment is two output rows, one per
+//     16-lane DPP row; for column tap v the fragment is the tap-0 fragment
+//     shifted by v lanes (v_mov_b32_dpp row_shl:v): one LDS read per
+//     fragment and kernel row instead of kw. Junk columns are dropped.
+//   - Input tile: 64-byte position stride with the 16-byte channel groups
+//     XOR-swizzled by position (conflict-free 8-lane read phases).
+//   - 3x3 taps only: the 9 steps of a chunk (tap x 32 input channels) are
+//     fully unrolled, so every prefetch slot and every staging decision is a
+//     compile-time constant and the step has no branches.
+//   - Exchange without exposed latency: step s mixes B_{s+2} into the stage
+//     buffer that B_s occupied and reads B_{s+1} into registers, so the
+//     fragments a step multiplies were read a whole step earlier; one
+//     barrier per step publishes the new buffer.
+//   - Prefetch in registers: the expert words of step s + 3 load during step
+//     s. The next chunk's raw NCHW bytes load 2 KB per step in steps 0..6
+//     and reach the wave's LDS raw buffer two steps later; after the chunk's
+//     last tap the wave transposes the raw chunk into its tile. All loads
+//     are ordinary vector loads issued in a fixed order (expert words, then
+//     raw bytes), so the compiler's wait counts stay exact and no wait
+//     covers a younger load.
+//   - The epilogue stores each lane's 4 consecutive output columns straight
+//     to y.
+constexpr int kRow16MaxPos = 256;  // tile positions (16 x 16) and input plane positions
+constexpr int kRow16RawBytes = 14 * 1024;  // raw chunk bytes the 3x3 schedule moves (7 steps x 2 KB)
+__shared__ __attribute__((aligned(16))) u32x4_t s_tiles[4 * kRow16MaxPos * 4];
+__shared__ __attribute__((aligned(16))) u32x4_t s_raw[4 * kChunk * kRow16MaxPos / 8];
+__shared__ __attribute__((aligned(16))) u32x4_t s_bstage[2 * 4 * 4 * 64];
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int swz(int q, int g) {
     return q * 32 + ((g ^ ((q >> 1) & 3)) << 3);
 }
 
-template <int NP2, int XT, int KW>
-__global__ __launch_bounds__(512) void conv_fused_row16_kernel(const uint16_t *__restrict__ x,
+// Attention row of example (lane & 3) as a 4x4x4 A operand: experts 0..3 as
+// bf16, high part (rounded) and low part (the rounding remainder).
+__device__ __forceinline__ void alpha_rows(const float *__restrict__ alpha, int be, int n,
+                                           s16x4_t &hi, s16x4_t &lo) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float v = k < n ? alpha[(long)be * n + k] : 0.f;
+        const uint16_t h = f32_to_bf16(v);
+        hi[k] = (short)h;
+        lo[k] = (short)f32_to_bf16(v - bf16_to_f32(h));
+    }
+}
+
+// Mixed B fragment words for the 4 examples: out[e] = 8 bf16 (channels
+// j = 0..7 of this lane's fragment column) of sum_k alpha[e][k] E_k.
+template <int NP2>
+__device__ __forceinline__ void mix4_frag(const uint32_t (&w)[8 * NP2], s16x4_t ahi, s16x4_t alo,
+                                          u32x4_t (&out)[4]) {
+    f32x4_t d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        u32x2_t e2;
+        e2.x = w[j * NP2];
+        e2.y = NP2 == 2 ? w[j * NP2 + 1] : 0u;
+        const s16x4_t ev = __builtin_bit_cast(s16x4_t, e2);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        d[j] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi, ev, z, 0, 0, 0);
+        d[j] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo, ev, d[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        out[e].x = pack_bf16x2(d[0][e], d[1][e]);
+        out[e].y = pack_bf16x2(d[2][e], d[3][e]);
+        out[e].z = pack_bf16x2(d[4][e], d[5][e]);
+        out[e].w = pack_bf16x2(d[6][e], d[7][e]);
+    }
+}
+
+template <int NP2>
+__global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *__restrict__ x,
                                                                const uint32_t *__restrict__ packed,
                                                                const float *__restrict__ alpha,
                                                                uint16_t *__restrict__ y, ConvArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    constexpr int CB = 2;   // 2 x 32 output channels
-    constexpr int PBW = 4;  // blocks of 2 padded rows per wave
+    constexpr int CB = 2;  // 2 x 32 output channels
+    constexpr int PB = 7;  // blocks of 2 padded rows: Ho <= 14
+    constexpr int K = 3;   // 3 x 3 taps: a chunk is 9 steps, fully unrolled
+    constexpr int KT = K * K;
+    constexpr int RL = 2;  // raw pieces load in step i and reach LDS in step i + RL
+    constexpr int RSTEPS = KT - RL;  // steps that load raw pieces
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
-    const int ex = wave & 3, half = wave >> 2;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int ot = logical / a.n_btiles;
     const int bt = logical - ot * a.n_btiles;
     const int o0 = ot * CB * 32;
-    const int tpos = a.tile_rows * a.ncols;     // positions per tile
-    const int tile_elems = tpos * 32;
-    uint16_t *tiles = lds + ex * 2 * tile_elems;  // [2 buffers] for this example
-    u32x4_t *bstage = reinterpret_cast<u32x4_t *>(lds + 8 * tile_elems);
-    auto bslot = [&](int buf, int e, int f) { return bstage + ((buf * 4 + e) * 4 + f) * 64 + lane; };
+    uint16_t *tile = reinterpret_cast<uint16_t *>(s_tiles + wave * kRow16MaxPos * 4);
+    u32x4_t *raw = s_raw + wave * (kChunk * kRow16MaxPos / 8);
+    auto bslot = [&](int buf, int e, int f) { return s_bstage + ((buf * 4 + e) * 4 + f) * 64 + lane; };
 
-    const int mf = wave & 3;
-    uint32_t ahi[2][NP2], alo[2][NP2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int be = min(bt * 4 + 2 * half + k, a.B - 1);
-#pragma unroll
-        for (int p = 0; p < NP2; ++p) {
-            const float a0 = 2 * p < a.n ? alpha[(long)be * a.n + 2 * p] : 0.f;
-            const float a1 = 2 * p + 1 < a.n ? alpha[(long)be * a.n + 2 * p + 1] : 0.f;
-            ahi[k][p] = pack_bf16x2(a0, a1);
-            alo[k][p] = pack_bf16x2(a0 - bf16_lo(ahi[k][p]), a1 - bf16_hi(ahi[k][p]));
-        }
-    }
+    // mixing role: fragment `wave` (channel block wave >> 1, K half wave & 1), all 4 examples
+    s16x4_t ahi, alo;
+    alpha_rows(alpha, min(bt * 4 + (lane & 3), a.B - 1), a.n, ahi, alo);
     const long prow =
-        ((long)min(o0 + 32 * (mf >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (mf & 1) + 8 * lh) * NP2;
+        ((long)min(o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh) * NP2;
 
-    const int b_raw = bt * 4 + ex;
+    // convolution role: example `wave`
+    const int b_raw = bt * 4 + wave;
     const bool valid = b_raw < a.B;
     const int b = valid ? b_raw : a.B - 1;
-    const int pbt = (a.Ho + 1) / 2;
-    const int pb0 = half * PBW;
-    const int npb = min(PBW, pbt - pb0);
-    const int slane = half * 64 + lane;  // staging lane among the example's two waves
+    zero_lds(tile, kRow16MaxPos * 32, lane, 64);
 
-    zero_lds(tiles, 2 * tile_elems, slane, 128);
-
-    // A fragment of block pb, kernel row 0, column tap 0: lane -> padded
-    // position (row 2*pb + l32/16, column l32 % 16)
-    int aq[PBW];
+    int aq[PB];
 #pragma unroll
-    for (int pb = 0; pb < PBW; ++pb) {
-        const int r = min(2 * (pb0 + pb) + (l32 >> 4), a.Ho - 1);
+    for (int pb = 0; pb < PB; ++pb) {
+        const int r = min(2 * pb + (l32 >> 4), a.Ho - 1);
         const int c = min(l32 & 15, a.ncols - 1);
         aq[pb] = r * a.ncols + c;
     }
     const uint16_t *xb = x + (long)b * a.x_bstride;
-    const int HW = a.H * a.W, HW2 = HW >> 1;
-    const int h_tile0 = -a.pad;
-    const int nrows = min(a.H, h_tile0 + a.tile_rows);
+    const int HW = a.H * a.W;
+    const int nrows = min(a.H, a.tile_rows - a.pad);  // input rows the tile holds
     const int pairs = a.W >> 1;
     const int per_g = nrows * pairs;
     const int ntasks = 4 * per_g;
 
-    // one staging task: 2 neighbouring positions x 8 channels of chunk c0
-    auto task_load = [&](int k, int cc, uint32_t (&r)[8]) {
-        const int task = slane + 128 * k;
-        const int tt = min(task, ntasks - 1);
-        const int g = tt / per_g;
-        const int rem = tt - g * per_g;
-        const int row = rem / pairs;
-        const int pr = rem - row * pairs;
-        const int cb = cc + 8 * g;
-        const uint32_t *src =
-            reinterpret_cast<const uint32_t *>(xb + (long)cb * HW + row * a.W + 2 * pr);
-        const int last = a.Cin - 1 - cb;  // highest valid channel offset in this group
+    // Raw copy of input channels [cc, cc + 32) (fewer at the tail): the
+    // chunk's bytes in NCHW order (16-byte aligned: Cin * H * W is a
+    // multiple of 8), in 1 KB pieces; a lane moves bytes [16 lane, 16 lane +
+    // 16) of a piece. Loads past the chunk's end re-read its last 16 bytes
+    // (discarded); stores past it are skipped.
+    auto raw_bytes = [&](int cc) { return min(kChunk, a.Cin - cc) * HW * 2; };
+    auto raw_load = [&](int cc, int j, u32x4_t &r) {
+        const char *src = reinterpret_cast<const char *>(xb + (long)cc * HW);
+        r = *reinterpret_cast<const u32x4_t *>(src + min(j * 1024 + lane * 16, raw_bytes(cc) - 16));
+    };
+    auto raw_store = [&](int cc, int j, const u32x4_t &r) {
+        const int off = j * 1024 + lane * 16;
+        if (off < raw_bytes(cc)) *reinterpret_cast<u32x4_t *>(reinterpret_cast<char *>(raw) + off) = r;
+    };
+    // raw chunk -> tile: task = 2 neighbouring positions x 8 channels
+    // (task + 0.5) / d rounded down is exact in float for task < 2^12, d <= 2^8
+    const float inv_per_g = 1.f / (float)per_g, inv_pairs = 1.f / (float)pairs;
+    auto raw_to_tile = [&](int cc) {
+        const int nch = min(kChunk, a.Cin - cc);
+        const uint32_t *rw = reinterpret_cast<const uint32_t *>(raw);
+        for (int task = lane; task < ntasks; task += 64) {
+            const int g = (int)(((float)task + 0.5f) * inv_per_g);
+            const int rem = task - g * per_g;
+            const int row = (int)(((float)rem + 0.5f) * inv_pairs);
+            const int pr = rem - row * pairs;
+            const int wofs = (row * a.W + 2 * pr) >> 1;
+            uint32_t r[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t v = src[(long)min(j, max(last, 0)) * HW2];
-            r[j] = j <= last ? v : 0u;
+            for (int j = 0; j < 8; ++j)
+                r[j] = (8 * g + j < nch) ? rw[(8 * g + j) * (HW >> 1) + wofs] : 0u;
+            const int q = (row + a.pad) * a.ncols + 2 * pr + a.pad;
+            u32x4_t o0v, o1v;
+            o0v.x = lo_pair(r[0], r[1]); o0v.y = lo_pair(r[2], r[3]);
+            o0v.z = lo_pair(r[4], r[5]); o0v.w = lo_pair(r[6], r[7]);
+            o1v.x = hi_pair(r[0], r[1]); o1v.y = hi_pair(r[2], r[3]);
+            o1v.z = hi_pair(r[4], r[5]); o1v.w = hi_pair(r[6], r[7]);
+            *reinterpret_cast<u32x4_t *>(tile + swz(q, g)) = o0v;
+            *reinterpret_cast<u32x4_t *>(tile + swz(q + 1, g)) = o1v;
         }
     };
-    auto task_store = [&](int k, uint16_t *tile, const uint32_t (&r)[8]) {
-        const int task = slane + 128 * k;
-        if (task >= ntasks) return;
-        const int g = task / per_g;
-        const int rem = task - g * per_g;
-        const int row = rem / pairs;
-        const int pr = rem - row * pairs;
-        const int q = (row - h_tile0) * a.ncols + 2 * pr + a.pad;
-        u32x4_t o0v, o1v;
-        o0v.x = lo_pair(r[0], r[1]); o0v.y = lo_pair(r[2], r[3]);
-        o0v.z = lo_pair(r[4], r[5]); o0v.w = lo_pair(r[6], r[7]);
-        o1v.x = hi_pair(r[0], r[1]); o1v.y = hi_pair(r[2], r[3]);
-        o1v.z = hi_pair(r[4], r[5]); o1v.w = hi_pair(r[6], r[7]);
-        *reinterpret_cast<u32x4_t *>(tile + swz(q, g)) = o0v;
-        *reinterpret_cast<u32x4_t *>(tile + swz(q + 1, g)) = o1v;
-    };
 
-    f32x16_t acc[PBW][CB];
+    f32x16_t acc[PB][CB];
 #pragma unroll
-    for (int i = 0; i < PBW; ++i)
+    for (int i = 0; i < PB; ++i)
 #pragma unroll
         for (int j = 0; j < CB; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     const int nchunks = a.Cin_pad / kChunk;
-    const int nsteps = nchunks * a.KT;
 
-    __syncthreads();  // tiles zeroed by both waves of the example
+    // chunk 0 straight into the tile (2 pieces per step cover <= 14 KB):
+    // all loads first, so that their latencies overlap
+    {
+        u32x4_t r0[2 * RSTEPS];
 #pragma unroll
-    for (int k = 0; k < XT; ++k) {
-        uint32_t r[8];
-        task_load(k, 0, r);
-        task_store(k, tiles, r);
+        for (int j = 0; j < 2 * RSTEPS; ++j) raw_load(0, j, r0[j]);
+#pragma unroll
+        for (int j = 0; j < 2 * RSTEPS; ++j) raw_store(0, j, r0[j]);
     }
-    uint32_t w[8 * NP2];
-    load_packed<NP2>(packed, a, 0, 0, prow, w);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) *bslot(0, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
-    if (nsteps > 1) load_packed<NP2>(packed, a, 1 % a.KT, (1 / a.KT) * kChunk, prow, w);
-    __syncthreads();
+    raw_to_tile(0);
 
-    int s = 0;
-    for (int c = 0; c < nchunks; ++c) {
-        const uint16_t *cur = tiles + (c & 1) * tile_elems;
-        uint16_t *nxt = tiles + ((c + 1) & 1) * tile_elems;
-        const bool more = c + 1 < nchunks;
-        const int cn = (c + 1) * kChunk;
-        int i = 0;  // step within the chunk
-        for (int u = 0; u < a.KH; ++u) {
-            u32x4_t a0f[PBW][2];
+    // expert words of (tap t, chunk starting at channel cc) into w
+    auto words = [&](int t, int cc, uint32_t (&w)[8 * NP2]) { load_packed<NP2>(packed, a, t, cc, prow, w); };
+    auto mix_to = [&](const uint32_t (&w)[8 * NP2], int buf) {
+        u32x4_t m[4];
+        mix4_frag<NP2>(w, ahi, alo, m);
 #pragma unroll
-            for (int pb = 0; pb < PBW; ++pb)
+        for (int e = 0; e < 4; ++e) *bslot(buf, e, wave) = m[e];
+    };
+    // Step s (over chunks and taps) convolves with B_s, held in registers.
+    // During step s the wave reads B_{s+1} from stage buffer (s+1) & 1 and
+    // mixes B_{s+2} into buffer s & 1 (B_s's buffer, whose reads all ended
+    // before the barrier closing step s - 1); the barrier closing step s
+    // publishes B_{s+2}. The expert words of step s' sit in ring slot s' % 3
+    // (9 steps per chunk keep the slot compile-time): those of step s + 5
+    // load in step s, three steps before their mixing.
+    const int nsteps = nchunks * KT;
+    auto step_words = [&](int st, uint32_t (&w)[8 * NP2]) {
+        st = min(st, nsteps - 1);
+        const int c = st / KT;
+        words(st - c * KT, c * kChunk, w);
+    };
+    constexpr int WR = 3;
+    uint32_t w[WR][8 * NP2];
+    u32x4_t rb[RL][2];  // raw pieces in flight, slot = (step within chunk) % RL
+    bf16x8_t bcur[4], bnext[4];
+    {
+        uint32_t w0[8 * NP2];
+        step_words(0, w0);
+        mix_to(w0, 0);
+        step_words(1, w0);
+        mix_to(w0, 1);
+#pragma unroll
+        for (int st = 2; st < 2 + WR; ++st) step_words(st, w[st % WR]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bcur[f] = __builtin_bit_cast(bf16x8_t, *bslot(0, wave, f));
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int cn = min(c + 1, nchunks - 1) * kChunk;  // last chunk: harmless re-reads
+        const bool more = c + 1 < nchunks;
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            u32x4_t a0f[PB][2];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
-                    a0f[pb][kh] = *reinterpret_cast<const u32x4_t *>(cur + swz(aq[pb] + u * a.ncols, 2 * kh + lh));
+                    a0f[pb][kh] = *reinterpret_cast<const u32x4_t *>(tile + swz(aq[pb] + u * a.ncols, 2 * kh + lh));
 #pragma unroll
-            for (int v = 0; v < KW; ++v, ++s, ++i) {
-                const int buf = s & 1;
-                // one staging task of the next chunk per step: loaded here,
-                // stored into the other tile buffer at the end of the step
-                uint32_t sr[8];
-                const bool stage_now = more && i < XT;
-                if (stage_now) task_load(i, cn, sr);
-                bf16x8_t bfr[4];
+            for (int v = 0; v < K; ++v) {
+                const int i = u * K + v;       // step within the chunk (compile-time)
+                const int par = (c + i) & 1;   // parity of the global step 9 c + i
 #pragma unroll
-                for (int f = 0; f < 4; ++f) bfr[f] = __builtin_bit_cast(bf16x8_t, *bslot(buf, ex, f));
+                for (int f = 0; f < 4; ++f) bnext[f] = __builtin_bit_cast(bf16x8_t, *bslot(par ^ 1, wave, f));
+                // All PB blocks are computed (rows past Ho are clamped duplicates,
+                // dropped in the epilogue), so the MFMA stream has no branches.
+                // The mixing sits between the two K halves, so that its
+                // matrix work queues behind the first half and its register
+                // and LDS work issues while the second half runs.
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
+                    if (kh == 1) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        mix_to(w[(i + 2) % WR], par);  // B of step 9 c + i + 2
+                    }
 #pragma unroll
-                    for (int pb = 0; pb < PBW; ++pb) {
-                        if (pb < npb) {
-                            const bf16x8_t afr =
-                                __builtin_bit_cast(bf16x8_t, v == 0 ? a0f[pb][kh] : dpp_shl(a0f[pb][kh], v));
+                    for (int pb = 0; pb < PB; ++pb) {
+                        const bf16x8_t afr =
+                            __builtin_bit_cast(bf16x8_t, v == 0 ? a0f[pb][kh] : dpp_shl(a0f[pb][kh], v));
 #pragma unroll
-                            for (int cb = 0; cb < CB; ++cb)
-                                acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                    afr, bfr[cb * 2 + kh], acc[pb][cb], 0, 0, 0);
-                        }
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                afr, bcur[cb * 2 + kh], acc[pb][cb], 0, 0, 0);
                     }
                 }
+                step_words(c * KT + i + 5, w[(i + 2) % WR]);  // slot (i + 5) % 3 == (i + 2) % 3
+                // Raw pieces loaded RL steps ago reach LDS, then this step's
+                // pieces load. Issued after the expert words, so waiting for
+                // the raw pieces never waits for younger expert words.
+                if (i >= RL) {
+                    raw_store(cn, 2 * (i - RL), rb[i % RL][0]);
+                    raw_store(cn, 2 * (i - RL) + 1, rb[i % RL][1]);
+                }
+                if (i < RSTEPS) {
+                    raw_load(cn, 2 * i, rb[i % RL][0]);
+                    raw_load(cn, 2 * i + 1, rb[i % RL][1]);
+                }
+                if (i == KT - 1 && more) raw_to_tile(cn);
+                lds_barrier();
 #pragma unroll
-                for (int k = 0; k < 2; ++k)
-                    *bslot(buf ^ 1, 2 * half + k, mf) = mix_frag<NP2>(w, ahi[k], alo[k]);
-                {
-                    const int s2 = min(s + 2, nsteps - 1);
-                    const int c2 = s2 / a.KT;
-                    load_packed<NP2>(packed, a, s2 - c2 * a.KT, c2 * kChunk, prow, w);
-                }
-                if (stage_now) task_store(i, nxt, sr);
-                if (more && i + 1 == a.KT) {
-                    // tasks the chunk's steps did not reach (chunks of fewer than XT steps)
-                    for (int k = i + 1; k < XT; ++k) {
-                        uint32_t r[8];
-                        task_load(k, cn, r);
-                        task_store(k, nxt, r);
-                    }
-                }
-                __syncthreads();
+                for (int f = 0; f < 4; ++f) bcur[f] = bnext[f];
             }
         }
     }
 
-    // Epilogue through LDS, one 32-channel block at a time: each wave writes
-    // its D values as [channel][position of its rows], then stores 4
-    // consecutive positions of a channel plane per lane.
-    const int r_lo = 2 * pb0;                       // first output row of this wave
-    const int nr = max(0, min(a.Ho, r_lo + 2 * PBW) - r_lo);
-    const int span = nr * a.Wo;                     // positions this wave owns
-    const int pstride = (2 * PBW * 16) | 1;         // odd stride (in bf16 pairs) per channel
-    uint16_t *ebuf = lds + wave * 32 * 2 * pstride;
+    // Epilogue through LDS (this wave's raw buffer), one 32-channel block
+    // at a time. D of a 32x32 block holds, per lane, output channel
+    // o0 + 32 cb + l32 and positions 8 j + 4 lh + (0..3): 4 consecutive
+    // columns of padded row 2 pb + (j >> 1). They go to ebuf[channel][row *
+    // Wo + col] as two 2-element words (a group starting at or past Wo is
+    // written at Wo). Junk columns past Wo land on the next row's first
+    // columns and are overwritten by that row's own words, which come later
+    // in the same wave's program order; the last row's spill (at most 4
+    // elements) lands in the channel's padding. Then each lane copies 4 (or
+    // 2, when P is not a multiple of 4) consecutive positions of a channel
+    // plane to y with one store.
+    uint16_t *ebuf = reinterpret_cast<uint16_t *>(raw);
+    const int pitch = a.P + 4;  // bf16 per channel: plane + room for the last row's spill
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
+        uint32_t *ech = reinterpret_cast<uint32_t *>(ebuf + l32 * pitch);
 #pragma unroll
-        for (int pb = 0; pb < PBW; ++pb) {
-            if (pb < npb) {
+        for (int pb = 0; pb < PB; ++pb) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rl = 2 * pb + (j >> 1);
-                    const int cc = 8 * (j & 1) + 4 * lh;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (cc + q < a.Wo && r_lo + rl < a.Ho)
-                            ebuf[l32 * 2 * pstride + rl * a.Wo + cc + q] = f32_to_bf16(acc[pb][cb][4 * j + q]);
+            for (int j = 0; j < 4; ++j) {
+                const int r = min(2 * pb + (j >> 1), a.Ho - 1);  // rows past Ho rewrite the last row
+                const int col = 8 * (j & 1) + 4 * lh;
+                const f32x16_t &d = acc[pb][cb];
+                const int e0 = r * a.Wo + min(col, a.Wo);   // even: Wo even, col even
+                const bool keep = 2 * pb + (j >> 1) < a.Ho;
+                if (keep) {
+                    ech[e0 >> 1] = pack_bf16x2(d[4 * j], d[4 * j + 1]);
+                    ech[(e0 >> 1) + 1] = pack_bf16x2(d[4 * j + 2], d[4 * j + 3]);
                 }
             }
         }
-        __syncthreads();
-        if (valid) {
-            const int chunks = (span + 3) / 4;
-            for (int ii = lane; ii < 32 * chunks; ii += 64) {
-                const int ch = ii / chunks, k4 = (ii - ch * chunks) * 4;
+        // the wave reads only what it wrote: LDS order within a wave suffices
+        if (valid && (a.P & 3) == 0) {
+            const int quads = a.P >> 2;
+            for (int ii = lane; ii < 32 * quads; ii += 64) {
+                const int ch = ii / quads, k4 = (ii - ch * quads) * 4;
                 const int o = o0 + 32 * cb + ch;
                 if (o >= a.Cout) continue;
-                const long yi = ((long)b * a.Cout + o) * a.P + r_lo * a.Wo + k4;
-                const uint16_t *src = ebuf + ch * 2 * pstride + k4;
-                if (k4 + 3 < span && (yi & 3) == 0) {
-                    u32x2_t vv;
-                    vv.x = (uint32_t)src[0] | ((uint32_t)src[1] << 16);
-                    vv.y = (uint32_t)src[2] | ((uint32_t)src[3] << 16);
-                    *reinterpret_cast<u32x2_t *>(y + yi) = vv;
-                } else {
-                    for (int q = 0; q < 4 && k4 + q < span; ++q) y[yi + q] = src[q];
-                }
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(ebuf + ch * pitch + k4);
+                u32x2_t vv;
+                vv.x = src[0];
+                vv.y = src[1];
+                *reinterpret_cast<u32x2_t *>(y + ((long)b * a.Cout + o) * a.P + k4) = vv;
+            }
+        } else if (valid) {
+            const int twos = a.P >> 1;  // P is even (Wo even)
+            for (int ii = lane; ii < 32 * twos; ii += 64) {
+                const int ch = ii / twos, k2 = (ii - ch * twos) * 2;
+                const int o = o0 + 32 * cb + ch;
+                if (o >= a.Cout) continue;
+                *reinterpret_cast<uint32_t *>(y + ((long)b * a.Cout + o) * a.P + k2) =
+                    *reinterpret_cast<const uint32_t *>(ebuf + ch * pitch + k2);
             }
         }
-        __syncthreads();
     }
 }
 
@@ -851,19 +946,16 @@ size_t fused_lds_bytes(const Geom &g) {
     return tiles + 2 * 4 * 4 * 64 * 16;  // + double-buffered B stage
 }
 
-size_t row16_lds_bytes(const Geom &g);
-
+// Static LDS of the row-16 kernel: 4 tiles of 16 x 16 positions, 4 raw
+// buffers of 16 KB (a chunk may use 14 KB: 7 loading steps x 2 KB) and the
+// double-buffered B stage. Conditions: 3x3 taps at stride 1, padded rows of
+// at most 16 positions, at most 14 output rows, W even (so output pieces of
+// 2 elements are 4-byte aligned) and 16-byte aligned channel chunks.
 bool row16_ok(const Geom &g) {
-    return g.stride == 1 && g.W + 2 * g.pad <= 16 && g.Ho <= 16 &&
-           (g.KW == 1 || g.KW == 3) && row16_lds_bytes(g) <= (size_t)kLdsBudget &&
-           4 * std::min(g.H, fused_tile_rows(g) - g.pad) * (g.W / 2) <= 128 * kFusedXT;
-}
-
-size_t row16_lds_bytes(const Geom &g) {
-    const size_t tiles = 8 * (size_t)fused_tile_rows(g) * (g.W + 2 * g.pad) * 32 * sizeof(uint16_t);
-    const size_t main = tiles + 2 * 4 * 4 * 64 * 16;
-    const size_t epi = 8 * (size_t)32 * 2 * ((2 * 4 * 16) | 1) * sizeof(uint16_t);
-    return main > epi ? main : epi;
+    const int tile_pos = fused_tile_rows(g) * (g.W + 2 * g.pad);
+    return g.stride == 1 && g.KH == 3 && g.KW == 3 && g.W + 2 * g.pad <= 16 && g.Ho <= 14 &&
+           g.W % 2 == 0 && ((long)g.Cin * g.H * g.W) % 8 == 0 && tile_pos <= kRow16MaxPos &&
+           g.H * g.W * kChunk * 2 <= kRow16RawBytes;
 }
 
 template <int NP2>
@@ -875,17 +967,9 @@ hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *pac
     a.n_otiles = ceil_div(g.Cout, 64);
     const long blocks = (long)a.n_btiles * a.n_otiles;
     if (row16_ok(g)) {
-        const size_t lds = row16_lds_bytes(g);
-        auto go = [&](auto k) {
-            if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
-            hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(512), lds, stream, x, packed, alpha, y, a);
-            return hipGetLastError();
-        };
-        switch (g.KW) {
-        case 1: return go(conv_fused_row16_kernel<NP2, kFusedXT, 1>);
-        case 3: return go(conv_fused_row16_kernel<NP2, kFusedXT, 3>);
-        default: break;  // other widths take the general fused kernel
-        }
+        hipLaunchKernelGGL(conv_fused_row16_kernel<NP2>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                           packed, alpha, y, a);
+        return hipGetLastError();
     }
     const size_t lds = fused_lds_bytes(g);
     auto k = conv_fused_kernel<kFusedPBW, NP2, kFusedXT>;
