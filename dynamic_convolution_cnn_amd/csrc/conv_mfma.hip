@@ -712,16 +712,12 @@ __global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *_
 
     const int nchunks = a.Cin_pad / kChunk;
 
-    // chunk 0 straight into the tile (2 pieces per step cover <= 14 KB):
-    // all loads first, so that their latencies overlap
-    {
-        u32x4_t r0[2 * RSTEPS];
+    // chunk 0's raw bytes (2 pieces per step cover <= 14 KB): all loads
+    // first, so that their latencies overlap with each other and with the
+    // first mixings; stored and transposed after those
+    u32x4_t r0[2 * RSTEPS];
 #pragma unroll
-        for (int j = 0; j < 2 * RSTEPS; ++j) raw_load(0, j, r0[j]);
-#pragma unroll
-        for (int j = 0; j < 2 * RSTEPS; ++j) raw_store(0, j, r0[j]);
-    }
-    raw_to_tile(0);
+    for (int j = 0; j < 2 * RSTEPS; ++j) raw_load(0, j, r0[j]);
 
     // expert words of (tap t, chunk starting at channel cc) into w
     auto words = [&](int t, int cc, uint32_t (&w)[8 * NP2]) { load_packed<NP2>(packed, a, t, cc, prow, w); };
@@ -757,6 +753,9 @@ __global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *_
 #pragma unroll
         for (int st = 2; st < 2 + WR; ++st) step_words(st, w[st % WR]);
     }
+#pragma unroll
+    for (int j = 0; j < 2 * RSTEPS; ++j) raw_store(0, j, r0[j]);
+    raw_to_tile(0);
     lds_barrier();
 #pragma unroll
     for (int f = 0; f < 4; ++f) bcur[f] = __builtin_bit_cast(bf16x8_t, *bslot(0, wave, f));
@@ -822,55 +821,40 @@ __global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *_
     // Epilogue through LDS (this wave's raw buffer), one 32-channel block
     // at a time. D of a 32x32 block holds, per lane, output channel
     // o0 + 32 cb + l32 and positions 8 j + 4 lh + (0..3): 4 consecutive
-    // columns of padded row 2 pb + (j >> 1). They go to ebuf[channel][row *
-    // Wo + col] as two 2-element words (a group starting at or past Wo is
-    // written at Wo). Junk columns past Wo land on the next row's first
-    // columns and are overwritten by that row's own words, which come later
-    // in the same wave's program order; the last row's spill (at most 4
-    // elements) lands in the channel's padding. Then each lane copies 4 (or
-    // 2, when P is not a multiple of 4) consecutive positions of a channel
-    // plane to y with one store.
+    // columns of padded row 2 pb + (j >> 1). The valid ones go to
+    // ebuf[channel][row * Wo + col] as 2-element words (Wo is even, so a
+    // group holds 0, 2 or 4 valid columns). The block's 32 channel planes
+    // are then one dense run, as are its planes in y, so the copy out is a
+    // straight 16-byte-per-lane copy (4 bytes when unaligned).
     uint16_t *ebuf = reinterpret_cast<uint16_t *>(raw);
-    const int pitch = a.P + 4;  // bf16 per channel: plane + room for the last row's spill
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        uint32_t *ech = reinterpret_cast<uint32_t *>(ebuf + l32 * pitch);
+        uint32_t *ech = reinterpret_cast<uint32_t *>(ebuf + l32 * a.P);
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = min(2 * pb + (j >> 1), a.Ho - 1);  // rows past Ho rewrite the last row
+                const int r = 2 * pb + (j >> 1);
                 const int col = 8 * (j & 1) + 4 * lh;
                 const f32x16_t &d = acc[pb][cb];
-                const int e0 = r * a.Wo + min(col, a.Wo);   // even: Wo even, col even
-                const bool keep = 2 * pb + (j >> 1) < a.Ho;
-                if (keep) {
-                    ech[e0 >> 1] = pack_bf16x2(d[4 * j], d[4 * j + 1]);
-                    ech[(e0 >> 1) + 1] = pack_bf16x2(d[4 * j + 2], d[4 * j + 3]);
-                }
+                const int e2 = (r * a.Wo + col) >> 1;  // word index (row * Wo + col is even)
+                if (r < a.Ho && col < a.Wo) ech[e2] = pack_bf16x2(d[4 * j], d[4 * j + 1]);
+                if (r < a.Ho && col + 2 < a.Wo) ech[e2 + 1] = pack_bf16x2(d[4 * j + 2], d[4 * j + 3]);
             }
         }
         // the wave reads only what it wrote: LDS order within a wave suffices
-        if (valid && (a.P & 3) == 0) {
-            const int quads = a.P >> 2;
-            for (int ii = lane; ii < 32 * quads; ii += 64) {
-                const int ch = ii / quads, k4 = (ii - ch * quads) * 4;
-                const int o = o0 + 32 * cb + ch;
-                if (o >= a.Cout) continue;
-                const uint32_t *src = reinterpret_cast<const uint32_t *>(ebuf + ch * pitch + k4);
-                u32x2_t vv;
-                vv.x = src[0];
-                vv.y = src[1];
-                *reinterpret_cast<u32x2_t *>(y + ((long)b * a.Cout + o) * a.P + k4) = vv;
-            }
-        } else if (valid) {
-            const int twos = a.P >> 1;  // P is even (Wo even)
-            for (int ii = lane; ii < 32 * twos; ii += 64) {
-                const int ch = ii / twos, k2 = (ii - ch * twos) * 2;
-                const int o = o0 + 32 * cb + ch;
-                if (o >= a.Cout) continue;
-                *reinterpret_cast<uint32_t *>(y + ((long)b * a.Cout + o) * a.P + k2) =
-                    *reinterpret_cast<const uint32_t *>(ebuf + ch * pitch + k2);
+        const int och = min(32, a.Cout - (o0 + 32 * cb));  // channels of this block that exist
+        if (valid && och > 0) {
+            const int bytes = och * a.P * 2;
+            char *dst = reinterpret_cast<char *>(y + ((long)b * a.Cout + o0 + 32 * cb) * a.P);
+            const char *src = reinterpret_cast<const char *>(ebuf);
+            if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (bytes & 15) == 0) {
+#pragma unroll 4
+                for (int off = lane * 16; off < bytes; off += 1024)
+                    *reinterpret_cast<u32x4_t *>(dst + off) = *reinterpret_cast<const u32x4_t *>(src + off);
+            } else {
+                for (int off = lane * 4; off < bytes; off += 256)
+                    *reinterpret_cast<uint32_t *>(dst + off) = *reinterpret_cast<const uint32_t *>(src + off);
             }
         }
     }
