@@ -35,10 +35,14 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 ROTATE_BYTES = 640 << 20        # rotating input/output sets larger than L2 + MALL
 
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE on the headline workload, scaled by the plain-copy calibration. Valid only
-# for the kernel source it was taken on (sha256 of the file below); otherwise null.
+# WRITE_SIZE on the headline workload (KiB per dispatch), each scaled by what the same
+# counter reads for a plain 256 MiB device copy (bench.py --calib-copy): FETCH_SIZE read
+# 131085 KiB for 262144 KiB moved (x 2.000), WRITE_SIZE 262144 KiB (x 1.000). Valid only
+# for the kernel source it was taken on (sha256 prefix of the file below); otherwise null.
 TRAFFIC = {
-    "resnet50_3x3": None,
+    "resnet50_3x3": {"source_sha": "9ff072401b62af08",
+                     "fetch_kib": 56329.2, "write_kib": 27648.0,
+                     "fetch_scale": 262144 / 131085, "write_scale": 1.0},
 }
 KERNEL_SOURCE = os.path.join(ROOT, "dynamic_convolution_cnn_amd", "csrc", "conv_mfma.hip")
 
@@ -81,19 +85,28 @@ def to_dev(a, dtype):
     return torch.from_numpy(a).cuda()
 
 
+CPU_SAMPLE_SECONDS = 10.0  # bounded CPU sample: whole batches until this much time has passed
+
+
 def cpu_baseline(w, d):
-    """The oracle (route + mix + conv in fp64) on one full batch, on the host's cores."""
+    """The oracle (route + mix + conv in fp64) on whole batches of the same
+    workload, repeated until CPU_SAMPLE_SECONDS have passed, on the host's cores."""
     import oracle
     t0 = time.perf_counter()
-    alpha, _, _ = oracle.route(d["x"], d["fc_w"], d["fc_b"], w.route_mode, w.temperature)
-    h = d["x"]
-    for L, e in zip(w.layers, d["experts"]):
-        h = oracle.forward(h, e, alpha, L.stride, L.pad, L.groups)
-    dt = time.perf_counter() - t0
-    return {"value": round(w.B / dt, 3), "unit": "images/s", "cores": oracle.threads(),
+    batches = 0
+    while True:
+        alpha, _, _ = oracle.route(d["x"], d["fc_w"], d["fc_b"], w.route_mode, w.temperature)
+        h = d["x"]
+        for L, e in zip(w.layers, d["experts"]):
+            h = oracle.forward(h, e, alpha, L.stride, L.pad, L.groups)
+        batches += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_SAMPLE_SECONDS:
+            break
+    return {"value": round(batches * w.B / dt, 3), "unit": "images/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"one full batch of {w.B} examples of {w.key} (route + mix + conv, "
-                      f"float64 direct loops), {dt:.2f} s"}
+            "sample": f"{batches} full batches of {w.B} examples of {w.key} (route + mix + conv, "
+                      f"float64 direct loops), {dt:.1f} s"}
 
 
 def main():
@@ -194,7 +207,7 @@ def main():
     traffic = None
     t = TRAFFIC.get(w.key)
     if t and t.get("source_sha") == source_sha():
-        traffic = t["bytes_per_launch"]
+        traffic = round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
     pol_name = {bd.DYNCONV_POLICY_FUSED: "fused", bd.DYNCONV_POLICY_PREMIX: "premix"}
     out = {
         "metric": METRIC,
