@@ -20,7 +20,7 @@ namespace {
 
 constexpr int kGapThreads = 256;
 // batches at least this large route with one workgroup per example
-constexpr int kRouteMinB = 128;
+constexpr int kRouteMinB = 64;
 
 // VEC elements per load (VEC * sizeof(T) bytes); LPR lanes per plane.
 template <typename T, int VEC, int LPR>
@@ -144,61 +144,72 @@ __global__ __launch_bounds__(256) void route_fc_kernel(const float *__restrict__
     }
 }
 
-// Single-kernel routing for batches that fill the chip: one workgroup per
-// example. Phase 1 streams the example's channel planes (LPR lanes per plane,
-// VEC-element loads, two planes per lane in flight) into channel means in
-// LDS; phase 2 computes the logits (one wave per expert, lanes over
-// channels, fixed-order reduction); phase 3 applies the nonlinearity. No
-// workspace and no second launch.
-constexpr int kRouteThreads = 512;
+// Single-kernel routing for batches of at least kRouteMinB examples: one
+// workgroup of 1024 threads per example. Phase 1 reduces the example's
+// channel planes into channel means in LDS: LPR lanes per plane, and every
+// lane issues all of its (at most kRouteMaxK) vector loads of a plane before
+// it adds any, so a CU keeps about 128 KB of loads in flight and a few dozen
+// workgroups already saturate HBM. Phase 2 computes the logits (one wave per
+// expert, lanes over channels, fixed-order reduction); phase 3 applies the
+// nonlinearity. No workspace, no atomics, one launch.
+constexpr int kRouteThreads = 1024;
 constexpr int kRouteMaxC = 4096;
+constexpr int kRouteMaxK = 16;  // vector loads per lane and plane
+// One load of VEC elements and its float sum (split so that a lane can issue
+// all of its loads before the first sum).
+template <typename T, int VEC> struct VecLoad;
+template <> struct VecLoad<uint16_t, 8> {
+    using V = u32x4_t;
+    static __device__ __forceinline__ float sum(V q) {
+        return (bf16_lo(q.x) + bf16_hi(q.x)) + (bf16_lo(q.y) + bf16_hi(q.y)) +
+               ((bf16_lo(q.z) + bf16_hi(q.z)) + (bf16_lo(q.w) + bf16_hi(q.w)));
+    }
+};
+template <> struct VecLoad<uint16_t, 4> {
+    using V = u32x2_t;
+    static __device__ __forceinline__ float sum(V q) {
+        return (bf16_lo(q.x) + bf16_hi(q.x)) + (bf16_lo(q.y) + bf16_hi(q.y));
+    }
+};
+template <> struct VecLoad<uint16_t, 1> {
+    using V = uint16_t;
+    static __device__ __forceinline__ float sum(V q) { return bf16_to_f32(q); }
+};
+template <> struct VecLoad<float, 4> {
+    using V = f32x4_t;
+    static __device__ __forceinline__ float sum(V q) { return (q[0] + q[1]) + (q[2] + q[3]); }
+};
+template <> struct VecLoad<float, 1> {
+    using V = float;
+    static __device__ __forceinline__ float sum(V q) { return q; }
+};
 template <typename T, int VEC, int LPR>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(
     const T *__restrict__ x, const float *__restrict__ fc_w, const float *__restrict__ fc_b,
     float *__restrict__ alpha, int C, int hw, int n, int mode, float temp) {
     __shared__ float gsh[kRouteMaxC];
     __shared__ float zsh[64 * kMaxJ];
-    constexpr int kGroups = kRouteThreads / LPR;  // planes per pass
+    constexpr int kPlanes = kRouteThreads / LPR;  // planes per pass
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int grp = tid / LPR, lane_in = tid % LPR;
-    const int nvec = hw / VEC;
+    const int nvec = hw / VEC;  // at most LPR * kRouteMaxK
     const T *xb = x + (long)b * C * hw;
-    for (int c0 = 0; c0 < C; c0 += 2 * kGroups) {
-        const int ca = c0 + grp, cb = c0 + kGroups + grp;
-        float sa = 0.f, sb = 0.f;
-        const T *pa = xb + (long)min(ca, C - 1) * hw;
-        const T *pb = xb + (long)min(cb, C - 1) * hw;
-        for (int i = lane_in; i < nvec; i += LPR) {
-            if constexpr (sizeof(T) == 2 && VEC == 8) {
-                const u32x4_t qa = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(pa) + i);
-                const u32x4_t qb = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(pb) + i);
-                sa += (bf16_lo(qa.x) + bf16_hi(qa.x)) + (bf16_lo(qa.y) + bf16_hi(qa.y)) +
-                      ((bf16_lo(qa.z) + bf16_hi(qa.z)) + (bf16_lo(qa.w) + bf16_hi(qa.w)));
-                sb += (bf16_lo(qb.x) + bf16_hi(qb.x)) + (bf16_lo(qb.y) + bf16_hi(qb.y)) +
-                      ((bf16_lo(qb.z) + bf16_hi(qb.z)) + (bf16_lo(qb.w) + bf16_hi(qb.w)));
-            } else if constexpr (sizeof(T) == 2 && VEC == 4) {
-                const u32x2_t qa = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(pa) + i);
-                const u32x2_t qb = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(pb) + i);
-                sa += (bf16_lo(qa.x) + bf16_hi(qa.x)) + (bf16_lo(qa.y) + bf16_hi(qa.y));
-                sb += (bf16_lo(qb.x) + bf16_hi(qb.x)) + (bf16_lo(qb.y) + bf16_hi(qb.y));
-            } else if constexpr (sizeof(T) == 4 && VEC == 4) {
-                const f32x4_t qa = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(pa) + i);
-                const f32x4_t qb = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(pb) + i);
-                sa += (qa[0] + qa[1]) + (qa[2] + qa[3]);
-                sb += (qb[0] + qb[1]) + (qb[2] + qb[3]);
-            } else {
-                static_assert(VEC == 1, "unsupported vector width");
-                sa += Elem<T>::to_f32(pa[i]);
-                sb += Elem<T>::to_f32(pb[i]);
-            }
-        }
-        sa = group_sum<LPR>(sa);
-        sb = group_sum<LPR>(sb);
-        if (lane_in == 0) {
-            if (ca < C) gsh[ca] = sa / (float)hw;
-            if (cb < C) gsh[cb] = sb / (float)hw;
-        }
+    for (int c0 = 0; c0 < C; c0 += kPlanes) {
+        const int c = c0 + grp;
+        const T *p = xb + (long)min(c, C - 1) * hw;
+        // unconditional loads at clamped indices (no branch between them, so
+        // all are in flight at once); lanes past the plane's end add 0
+        using L = VecLoad<T, VEC>;
+        const typename L::V *pv = reinterpret_cast<const typename L::V *>(p);
+        typename L::V q[kRouteMaxK];
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK; ++k) q[k] = pv[min(lane_in + LPR * k, nvec - 1)];
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK; ++k) s += lane_in + LPR * k < nvec ? L::sum(q[k]) : 0.f;
+        s = group_sum<LPR>(s);
+        if (lane_in == 0 && c < C) gsh[c] = s / (float)hw;
     }
     __syncthreads();
     const int wave = tid / 64, lane = tid % 64;
@@ -255,14 +266,18 @@ hipError_t launch_route_fused_vec(const T *x, const float *fc_w, const float *fc
                                   int B, int C, int hw, int n, int mode, float temp,
                                   hipStream_t s) {
     const int nvec = hw / VEC;
-    int lpr = 8;
-    while (lpr < 64 && lpr * 4 < nvec) lpr *= 2;
+    // fewest lanes per plane that keep a lane's loads within kRouteMaxK
+    int lpr = 1;
+    while (lpr * kRouteMaxK < nvec) lpr *= 2;
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(B), dim3(kRouteThreads), 0, s, x, fc_w, fc_b, alpha, C, hw,
                            n, mode, temp);
         return hipGetLastError();
     };
     switch (lpr) {
+    case 1: return go(route_fused_kernel<T, VEC, 1>);
+    case 2: return go(route_fused_kernel<T, VEC, 2>);
+    case 4: return go(route_fused_kernel<T, VEC, 4>);
     case 8: return go(route_fused_kernel<T, VEC, 8>);
     case 16: return go(route_fused_kernel<T, VEC, 16>);
     case 32: return go(route_fused_kernel<T, VEC, 32>);
@@ -294,7 +309,10 @@ hipError_t launch_gap_vec(const T *x, float *gap, long rows, int hw, hipStream_t
 
 static_assert(kMaxJ * 64 >= 256, "route kernel covers n <= 256");
 
-bool route_single_kernel(const Geom &g) { return g.B >= kRouteMinB && g.Cin <= kRouteMaxC; }
+bool route_single_kernel(const Geom &g) {
+    // planes up to 64 lanes x kRouteMaxK vectors (bf16: 8192 elements with 16-byte loads)
+    return g.B >= kRouteMinB && g.Cin <= kRouteMaxC && g.H * g.W <= 64 * kRouteMaxK;
+}
 
 hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const float *fc_b,
                         int mode, float temperature, float *gap, float *alpha,

@@ -237,6 +237,7 @@ RAGGED = [
     (3, 256, 64, 10, 12, (5, 5), 1, 2, 2),   # 5x5 on a non-square image
     (5, 32, 32, 20, 20, (3, 3), 2, 1, 4),    # stride 2
     (3, 48, 40, 13, 14, (3, 3), 1, 1, 3),    # 16-wide padded rows, odd Ho, tails
+    (2, 256, 24, 6, 6, (3, 3), 1, 1, 16),    # expert slab too big for the LDS packing path
     (7, 64, 64, 6, 6, (3, 3), 1, 1, 4),      # small image: fewer rows than blocks
 ]
 
