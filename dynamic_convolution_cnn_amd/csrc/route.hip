@@ -183,41 +183,45 @@ template <> struct VecLoad<float, 1> {
     using V = float;
     static __device__ __forceinline__ float sum(V q) { return q; }
 };
-template <typename T, int VEC, int LPR>
-__global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(
-    const T *__restrict__ x, const float *__restrict__ fc_w, const float *__restrict__ fc_b,
-    float *__restrict__ alpha, int C, int hw, int n, int mode, float temp) {
-    __shared__ float gsh[kRouteMaxC];
-    __shared__ float zsh[64 * kMaxJ];
-    constexpr int kPlanes = kRouteThreads / LPR;  // planes per pass
-    const int b = blockIdx.x;
+// Phases 2 and 3 of the single-kernel router, after the channel means of
+// example b are in gsh (and a barrier): logits by one wave per expert (lanes
+// over channels, fixed-order reduction), then the nonlinearity in wave 0.
+// The weights of a wave's first expert for channels lane + 64 k (k < kFcPre)
+// are loaded before the pooling starts, so their latency hides under it.
+constexpr int kFcPre = 8;
+struct FcPre {
+    float w[kFcPre];
+    float bias;
+};
+__device__ __forceinline__ FcPre route_prefetch_fc(const float *__restrict__ fc_w,
+                                                   const float *__restrict__ fc_b, int C, int n) {
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    FcPre f;
+    const int i = min(wave, n - 1);
+#pragma unroll
+    for (int k = 0; k < kFcPre; ++k) f.w[k] = fc_w[(long)i * C + min(lane + 64 * k, C - 1)];
+    f.bias = fc_b ? fc_b[i] : 0.f;
+    return f;
+}
+__device__ __forceinline__ void route_finish(const float *gsh, float *zsh, const float *__restrict__ fc_w,
+                                             const float *__restrict__ fc_b, float *__restrict__ alpha,
+                                             int b, int C, int n, int mode, float temp, const FcPre &pre) {
     const int tid = threadIdx.x;
-    const int grp = tid / LPR, lane_in = tid % LPR;
-    const int nvec = hw / VEC;  // at most LPR * kRouteMaxK
-    const T *xb = x + (long)b * C * hw;
-    for (int c0 = 0; c0 < C; c0 += kPlanes) {
-        const int c = c0 + grp;
-        const T *p = xb + (long)min(c, C - 1) * hw;
-        // unconditional loads at clamped indices (no branch between them, so
-        // all are in flight at once); lanes past the plane's end add 0
-        using L = VecLoad<T, VEC>;
-        const typename L::V *pv = reinterpret_cast<const typename L::V *>(p);
-        typename L::V q[kRouteMaxK];
-#pragma unroll
-        for (int k = 0; k < kRouteMaxK; ++k) q[k] = pv[min(lane_in + LPR * k, nvec - 1)];
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < kRouteMaxK; ++k) s += lane_in + LPR * k < nvec ? L::sum(q[k]) : 0.f;
-        s = group_sum<LPR>(s);
-        if (lane_in == 0 && c < C) gsh[c] = s / (float)hw;
-    }
-    __syncthreads();
     const int wave = tid / 64, lane = tid % 64;
     for (int i = wave; i < n; i += kRouteThreads / 64) {
         float part = 0.f;
-        for (int c = lane; c < C; c += 64) part = fmaf(fc_w[(long)i * C + c], gsh[c], part);
+        int c0 = 0;
+        if (i == wave) {  // first expert of this wave: prefetched weights
+#pragma unroll
+            for (int k = 0; k < kFcPre; ++k) {
+                const int c = lane + 64 * k;
+                if (c < C) part = fmaf(pre.w[k], gsh[c], part);
+            }
+            c0 = 64 * kFcPre;
+        }
+        for (int c = c0 + lane; c < C; c += 64) part = fmaf(fc_w[(long)i * C + c], gsh[c], part);
         part = wave_sum(part);
-        if (lane == 0) zsh[i] = part + (fc_b ? fc_b[i] : 0.f);
+        if (lane == 0) zsh[i] = part + (i == wave ? pre.bias : (fc_b ? fc_b[i] : 0.f));
     }
     __syncthreads();
     if (wave != 0) return;
@@ -259,6 +263,39 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(
             if (i < n) alpha[(long)b * n + i] = e[j] / ssum;
         }
     }
+}
+
+template <typename T, int VEC, int LPR>
+__global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(
+    const T *__restrict__ x, const float *__restrict__ fc_w, const float *__restrict__ fc_b,
+    float *__restrict__ alpha, int C, int hw, int n, int mode, float temp) {
+    __shared__ float gsh[kRouteMaxC];
+    __shared__ float zsh[64 * kMaxJ];
+    constexpr int kPlanes = kRouteThreads / LPR;  // planes per pass
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int grp = tid / LPR, lane_in = tid % LPR;
+    const int nvec = hw / VEC;  // at most LPR * kRouteMaxK
+    const T *xb = x + (long)b * C * hw;
+    const FcPre pre = route_prefetch_fc(fc_w, fc_b, C, n);
+    for (int c0 = 0; c0 < C; c0 += kPlanes) {
+        const int c = c0 + grp;
+        const T *p = xb + (long)min(c, C - 1) * hw;
+        // unconditional loads at clamped indices (no branch between them, so
+        // all are in flight at once); lanes past the plane's end add 0
+        using L = VecLoad<T, VEC>;
+        const typename L::V *pv = reinterpret_cast<const typename L::V *>(p);
+        typename L::V q[kRouteMaxK];
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK; ++k) q[k] = pv[min(lane_in + LPR * k, nvec - 1)];
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK; ++k) s += lane_in + LPR * k < nvec ? L::sum(q[k]) : 0.f;
+        s = group_sum<LPR>(s);
+        if (lane_in == 0 && c < C) gsh[c] = s / (float)hw;
+    }
+    __syncthreads();
+    route_finish(gsh, zsh, fc_w, fc_b, alpha, b, C, n, mode, temp, pre);
 }
 
 template <typename T, int VEC>

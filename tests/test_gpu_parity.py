@@ -82,7 +82,7 @@ def test_route_full_size(key):
 
 @pytest.mark.parametrize("shape", [(3, 5, 7, 9, 6), (2, 3, 1, 1, 300 // 2), (5, 33, 13, 11, 256),
                                    (1, 8, 56, 56, 17), (130, 7, 5, 3, 9), (128, 33, 8, 8, 40),
-                                   (200, 3, 14, 14, 256)])
+                                   (200, 3, 14, 14, 256), (70, 6, 2, 6, 5), (64, 130, 14, 14, 3)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_route_ragged(shape, dtype, mode):
