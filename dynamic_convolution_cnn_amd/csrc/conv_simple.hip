@@ -12,6 +12,8 @@
 //   other mixed kernel; the zero-padded input plane is staged in LDS as
 //   float; each thread computes a strip of outputs along a row, so input
 //   values are reused from registers across the strip.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -108,6 +110,147 @@ __global__ __launch_bounds__(256) void depthwise_kernel(
     }
 }
 
+// Depthwise for square K x K taps (K = 3, 5, 7) and stride ST (1, 2): one
+// wave per (example, channel) plane, 4 planes per workgroup.
+//   - The zero-padded plane goes to the wave's LDS region as float, row pitch
+//     a multiple of 4 floats and wide enough for the last strip's window;
+//     16-byte loads when the plane is 16-byte aligned.
+//   - Lanes 0..K*K-1 mix the plane's taps (sum_i alpha_bi E_i[c], rounded to
+//     the storage type), which every lane then keeps in registers.
+//   - A lane computes DW_S consecutive outputs of a row: per kernel row it
+//     reads the (DW_S - 1) * ST + K input values once into registers and
+//     does DW_S * K multiply-adds from them.
+constexpr int kDwS = 8;          // outputs per lane task along a row
+constexpr int kDwPlanes = 4;     // planes (waves) per workgroup
+constexpr int kDwPlaneFloats = 3840;  // LDS floats per plane at most (4 planes + taps < 64 KB)
+
+__host__ __device__ constexpr int dw_win(int K, int ST) { return (kDwS - 1) * ST + K; }
+
+template <typename T, int K, int ST>
+__global__ __launch_bounds__(64 * kDwPlanes) void depthwise_strip_kernel(
+    const T *__restrict__ x, const T *__restrict__ experts, const float *__restrict__ alpha,
+    const T *__restrict__ wmixed, T *__restrict__ y, int B, int C, int H, int W, int pad, int Ho,
+    int Wo, int n, int pitch) {
+    constexpr int KT = K * K;
+    constexpr int WIN = dw_win(K, ST);
+    extern __shared__ __attribute__((aligned(16))) float planes[];  // kDwPlanes x plane_floats
+    __shared__ float taps_sh[kDwPlanes][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long nplanes = (long)B * C;
+    const long bc_raw = (long)blockIdx.x * kDwPlanes + wave;
+    const bool valid = bc_raw < nplanes;
+    const long bc = valid ? bc_raw : nplanes - 1;
+    const int b = (int)(bc / C), c = (int)(bc - (long)b * C);
+    const int Hp = (Ho - 1) * ST + K;  // padded rows read
+    float *pl = planes + wave * Hp * pitch;  // Hp * pitch is a multiple of 4
+
+    const T *xp = x + bc * H * W;
+    const int hw = H * W;
+    constexpr int VE = 16 / sizeof(T);  // elements per 16-byte load
+    constexpr int kPre = 4;             // 16-byte loads per lane issued before the taps
+    const bool vec = (reinterpret_cast<uintptr_t>(xp) & 15) == 0 && hw % VE == 0;
+    const int nv = hw / VE;
+    u32x4_t pre[kPre];
+    if (vec) {
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) pre[k] = reinterpret_cast<const u32x4_t *>(xp)[min(lane + 64 * k, nv - 1)];
+    }
+    // taps: expert values and attentions load 8 at a time (clamped indices,
+    // no branches), so their latencies overlap with each other and the plane's
+    if (lane < KT) {
+        float wv;
+        if (wmixed) {
+            wv = Elem<T>::to_f32(wmixed[bc * KT + lane]);
+        } else {
+            float sm = 0.f;
+            for (int i0 = 0; i0 < n; i0 += 8) {
+                float ev[8], av[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int i = min(i0 + k, n - 1);
+                    ev[k] = Elem<T>::to_f32(experts[((long)i * C + c) * KT + lane]);
+                    av[k] = alpha[(long)b * n + i];
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (i0 + k < n) sm = fmaf(av[k], ev[k], sm);
+            }
+            wv = Elem<T>::to_f32(Elem<T>::from_f32(sm));  // as the materialised kernel would hold it
+        }
+        taps_sh[wave][lane] = wv;
+    }
+    // zero the padded plane, then the interior
+    for (int i = lane; i < Hp * pitch; i += 64) pl[i] = 0.f;
+    auto put = [&](int v, const u32x4_t &q) {
+        float f[VE];
+        if constexpr (sizeof(T) == 2) {
+            f[0] = bf16_lo(q.x); f[1] = bf16_hi(q.x); f[2] = bf16_lo(q.y); f[3] = bf16_hi(q.y);
+            f[4] = bf16_lo(q.z); f[5] = bf16_hi(q.z); f[6] = bf16_lo(q.w); f[7] = bf16_hi(q.w);
+        } else {
+            f[0] = __uint_as_float(q.x); f[1] = __uint_as_float(q.y);
+            f[2] = __uint_as_float(q.z); f[3] = __uint_as_float(q.w);
+        }
+        int h = (v * VE) / W, w = v * VE - h * W;
+#pragma unroll
+        for (int j = 0; j < VE; ++j) {
+            if (h + pad < Hp) pl[(h + pad) * pitch + w + pad] = f[j];
+            if (++w == W) { w = 0; ++h; }
+        }
+    };
+    if (vec) {
+#pragma unroll
+        for (int k = 0; k < kPre; ++k)
+            if (lane + 64 * k < nv) put(lane + 64 * k, pre[k]);
+        for (int v = lane + 64 * kPre; v < nv; v += 64) put(v, reinterpret_cast<const u32x4_t *>(xp)[v]);
+    } else {
+        for (int i = lane; i < hw; i += 64) {
+            const int h = i / W, w = i - h * W;
+            if (h + pad < Hp) pl[(h + pad) * pitch + w + pad] = Elem<T>::to_f32(xp[i]);
+        }
+    }
+    __syncthreads();
+    float tap[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) tap[t] = taps_sh[wave][t];
+
+    const int strips = (Wo + kDwS - 1) / kDwS;
+    T *yp = y + bc * Ho * Wo;
+    for (int task = lane; task < Ho * strips; task += 64) {
+        const int r = task / strips;
+        const int s0 = (task - r * strips) * kDwS;
+        float acc[kDwS];
+#pragma unroll
+        for (int j = 0; j < kDwS; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            const float *row = pl + (r * ST + u) * pitch + s0 * ST;
+            float win[WIN];
+            if constexpr (ST == 1) {
+                // 16-byte aligned: s0 is a multiple of 8 and the pitch of 4
+#pragma unroll
+                for (int q = 0; q < WIN / 4; ++q) {
+                    const f32x4_t v4 = reinterpret_cast<const f32x4_t *>(row)[q];
+                    win[4 * q] = v4[0]; win[4 * q + 1] = v4[1]; win[4 * q + 2] = v4[2]; win[4 * q + 3] = v4[3];
+                }
+#pragma unroll
+                for (int q = (WIN / 4) * 4; q < WIN; ++q) win[q] = row[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < WIN; ++q) win[q] = row[q];
+            }
+#pragma unroll
+            for (int j = 0; j < kDwS; ++j)
+#pragma unroll
+                for (int v = 0; v < K; ++v) acc[j] = fmaf(tap[u * K + v], win[j * ST + v], acc[j]);
+        }
+        if (valid) {
+#pragma unroll
+            for (int j = 0; j < kDwS; ++j)
+                if (s0 + j < Wo) yp[r * Wo + s0 + j] = Elem<T>::from_f32(acc[j]);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_conv_direct_f32(const Geom &g, const float *x, const float *wmixed, float *y,
@@ -128,9 +271,56 @@ bool depthwise_supported(const Geom &g) {
            dw_lds_bytes(g) <= 64 * 1024;
 }
 
+// row pitch (floats) of the strip kernel's plane: the last strip's window
+// stays inside, rounded up to a multiple of 4
+static int dw_pitch(const Geom &g) {
+    const int strips = (g.Wo + kDwS - 1) / kDwS;
+    const int need = (strips * kDwS - 1) * g.stride + g.KW;
+    return (std::max(need, g.W + 2 * g.pad) + 3) / 4 * 4;
+}
+
+static bool dw_strip_ok(const Geom &g) {
+    const int Hp = (g.Ho - 1) * g.stride + g.KH;
+    return g.KH == g.KW && (g.KH == 3 || g.KH == 5 || g.KH == 7) && (g.stride == 1 || g.stride == 2) &&
+           (long)Hp * dw_pitch(g) <= kDwPlaneFloats;
+}
+
+template <typename T>
+static hipError_t launch_dw_strip(const Geom &g, const T *x, const T *experts, const float *alpha,
+                                  const T *wmixed, T *y, hipStream_t stream) {
+    const long planes = (long)g.B * g.Cin;
+    const dim3 grid((unsigned)((planes + kDwPlanes - 1) / kDwPlanes));
+    const int pitch = dw_pitch(g);
+    const size_t lds = (size_t)kDwPlanes * ((g.Ho - 1) * g.stride + g.KH) * pitch * sizeof(float);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(64 * kDwPlanes), lds, stream, x, experts, alpha, wmixed, y,
+                           g.B, g.Cin, g.H, g.W, g.pad, g.Ho, g.Wo, g.n, pitch);
+        return hipGetLastError();
+    };
+    const int key = g.KH * 10 + g.stride;
+    switch (key) {
+    case 31: return go(depthwise_strip_kernel<T, 3, 1>);
+    case 32: return go(depthwise_strip_kernel<T, 3, 2>);
+    case 51: return go(depthwise_strip_kernel<T, 5, 1>);
+    case 52: return go(depthwise_strip_kernel<T, 5, 2>);
+    case 71: return go(depthwise_strip_kernel<T, 7, 1>);
+    default: return go(depthwise_strip_kernel<T, 7, 2>);
+    }
+}
+
 hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
                                  const float *alpha, const void *wmixed, void *y,
                                  hipStream_t stream) {
+    if (dw_strip_ok(g)) {
+        if (g.bf16)
+            return launch_dw_strip<uint16_t>(g, static_cast<const uint16_t *>(x),
+                                             static_cast<const uint16_t *>(experts), alpha,
+                                             static_cast<const uint16_t *>(wmixed),
+                                             static_cast<uint16_t *>(y), stream);
+        return launch_dw_strip<float>(g, static_cast<const float *>(x), static_cast<const float *>(experts),
+                                      alpha, static_cast<const float *>(wmixed), static_cast<float *>(y),
+                                      stream);
+    }
     const size_t lds = dw_lds_bytes(g);
     const dim3 grid((unsigned)((long)g.B * g.Cin));
     if (g.bf16) {
