@@ -4,7 +4,9 @@
 One step = the whole path over one batch of synthetic input already resident
 in HBM: routing (GAP -> FC -> sigmoid/softmax), packing of the expert bank,
 and the per-example convolution with mixed kernels (fused into the MFMA
-convolution for the ResNet-50-shaped layer). Default workload: the
+convolution for the ResNet-50-shaped layer). Each step is one replay of a HIP
+graph that holds all of its launches; per-kernel times come from HIP events
+around eager launches of the same kernels. Default workload: the
 ResNet-50-shaped 3x3 layer, B=256, 256->256 channels, 14x14, n=4 experts,
 bf16 storage with float32 accumulation.
 
@@ -185,18 +187,37 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, events around route / pack / first conv in every step
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # One HIP graph per rotating set holds a whole step (route, pack, forward of
+    # every layer), so the timed loop measures the GPU, not Python launch cost.
+    graphs = []
+    for s in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(s)
+        graphs.append(g)
+    for i in range(max(args.warmup, 2)):
+        graphs[i % R].replay()
     torch.cuda.synchronize()
+
+    # timed region: exactly K steps (graph replays)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        graphs[i % R].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    route_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    pack_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    conv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    # per-kernel times: eager steps with HIP events on the launch stream around
+    # route / pack / first conv (the same kernels the graphs replay)
+    nk = min(args.steps, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nk)]
+    torch.cuda.synchronize()
+    for i in range(nk):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / nk
+    pack_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / nk
+    conv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / nk
 
     L0 = w.layers[0]
     conv_flops0 = 2 * w.B * L0.macs_per_example()

@@ -351,3 +351,48 @@ def test_packed_api_matches_forward(key, B):
         y2 = bd.dynconv_forward(x, ed, alpha, L.stride, L.pad, L.groups, policy=pol)
         torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("key,B", [("resnet50_3x3", 8), ("many_expert_softmax", 4)])
+def test_graph_replay_matches_eager(key, B):
+    """A HIP graph holding route + pack + forward (as the benchmark replays it)
+    gives bitwise the eager results on every replay, with other eager work and
+    host synchronisations between the replays."""
+    w = inputs.WORKLOADS[key]
+    d = inputs.make_inputs(w, B=B)
+    L, e = w.layers[0], d["experts"][0]
+    x, ed = to_dev(d["x"], "bf16"), to_dev(e, "bf16")
+    fw, fb = to_dev(d["fc_w"], "f32"), to_dev(d["fc_b"], "f32")
+    desc = bd.layer_desc(x, ed, L.stride, L.pad, L.groups)
+    pol = bd.dynconv_forward_policy(desc)
+    alpha = torch.empty((B, w.n), dtype=torch.float32, device="cuda")
+    packed = torch.empty(bd.dynconv_packed_experts_bytes(desc), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(bd.dynconv_forward_packed_workspace_bytes(desc, pol), 16), dtype=torch.uint8,
+                     device="cuda")
+    rws = torch.empty(max(bd.dynconv_route_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
+    y = torch.empty((B, L.Cout, L.Ho, L.Wo), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        bd.dynconv_route(x, fw, fb, w.route_mode, w.temperature, alpha=alpha, workspace=rws)
+        bd.dynconv_pack_experts(desc, ed, packed)
+        bd.dynconv_forward_packed(desc, x, packed, alpha, policy=pol, y=y, workspace=ws)
+
+    say("graph replay", key, "policy", pol)
+    step()
+    torch.cuda.synchronize()
+    a_ref, y_ref = alpha.clone(), y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    x2 = torch.flip(x, dims=[0]).contiguous()
+    for r in range(3):
+        alpha.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(alpha, a_ref), f"replay {r}: alpha differs"
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), f"replay {r}: y differs"
+        # unrelated eager work between replays
+        bd.dynconv_forward(x2, ed, a_ref, L.stride, L.pad, L.groups)
+        torch.cuda.synchronize()
