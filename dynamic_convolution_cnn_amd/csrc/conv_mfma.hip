@@ -614,43 +614,91 @@ __device__ __forceinline__ void mix4_frag(const uint32_t (&w)[8 * NP2], s16x4_t 
     }
 }
 
+// Expert words of one (tap, chunk) step for half of this lane's fragment
+// column: channels r = 4 h .. 4 h + 3 of the lane's 8 (prow includes 4 h) x
+// NP2 expert pairs, NP2 16-byte loads.
 template <int NP2>
-__global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *__restrict__ x,
-                                                               const uint32_t *__restrict__ packed,
-                                                               const float *__restrict__ alpha,
-                                                               uint16_t *__restrict__ y, ConvArgs a) {
+__device__ __forceinline__ void load_packed_half(const uint32_t *__restrict__ packed, const ConvArgs &a,
+                                                 int t, int c0, long prow, uint32_t (&w)[4 * NP2]) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+        packed + ((long)t * a.Cout * a.Cin_pad + c0) * NP2 + prow);
+#pragma unroll
+    for (int q = 0; q < NP2; ++q) {
+        const u32x4_t v4 = src[q];
+        w[4 * q + 0] = v4.x; w[4 * q + 1] = v4.y;
+        w[4 * q + 2] = v4.z; w[4 * q + 3] = v4.w;
+    }
+}
+
+// Half a B fragment for the 4 examples: out[e] = 4 bf16 (channels 4 h ..
+// 4 h + 3 of the lane's column) of sum_k alpha[e][k] E_k, on
+// v_mfma_f32_4x4x4_16b_bf16 (high and low attention parts summed in fp32).
+template <int NP2>
+__device__ __forceinline__ void mix4_half(const uint32_t (&w)[4 * NP2], s16x4_t ahi, s16x4_t alo,
+                                          u32x2_t (&out)[4]) {
+    f32x4_t d[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u32x2_t e2;
+        e2.x = w[j * NP2];
+        e2.y = NP2 == 2 ? w[j * NP2 + 1] : 0u;
+        const s16x4_t ev = __builtin_bit_cast(s16x4_t, e2);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        d[j] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi, ev, z, 0, 0, 0);
+        d[j] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo, ev, d[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        out[e].x = pack_bf16x2(d[0][e], d[1][e]);
+        out[e].y = pack_bf16x2(d[2][e], d[3][e]);
+    }
+}
+
+// 8 waves, two per SIMD: waves w and w + 4 (same SIMD) convolve example
+// e = w & 3, wave w over position blocks 0..3 and wave w + 4 over blocks
+// 4..6 (7 blocks of 32 positions = two padded rows each), both over all 64
+// channels, so one A fragment feeds two MFMAs. The two waves of a SIMD share
+// its matrix core: one wave's LDS round trips, waits and barrier skew overlap
+// the other's MFMAs. Wave w also mixes half h = w & 1 of B fragment w >> 1
+// for all 4 examples, and stages and transposes the 16 input channels
+// [16 hs, 16 hs + 16), hs = w >> 2, of its example's next chunk, so its raw
+// bytes and tile granules are its own.
+template <int NP2, int PBW>
+__device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const uint32_t *__restrict__ packed,
+                                           const float *__restrict__ alpha, uint16_t *__restrict__ y,
+                                           const ConvArgs &a, int pb0) {
     constexpr int CB = 2;  // 2 x 32 output channels
-    constexpr int PB = 7;  // blocks of 2 padded rows: Ho <= 14
     constexpr int K = 3;   // 3 x 3 taps: a chunk is 9 steps, fully unrolled
     constexpr int KT = K * K;
     constexpr int RL = 2;  // raw pieces load in step i and reach LDS in step i + RL
-    constexpr int RSTEPS = KT - RL;  // steps that load raw pieces
+    constexpr int RSTEPS = KT - RL;  // steps that load a raw piece (one 1 KB piece each)
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int ot = logical / a.n_btiles;
     const int bt = logical - ot * a.n_btiles;
     const int o0 = ot * CB * 32;
-    uint16_t *tile = reinterpret_cast<uint16_t *>(s_tiles + wave * kRow16MaxPos * 4);
-    u32x4_t *raw = s_raw + wave * (kChunk * kRow16MaxPos / 8);
-    auto bslot = [&](int buf, int e, int f) { return s_bstage + ((buf * 4 + e) * 4 + f) * 64 + lane; };
-
-    // mixing role: fragment `wave` (channel block wave >> 1, K half wave & 1), all 4 examples
+    // convolution role
+    const int e = wave & 3, hs = wave >> 2;
+    uint16_t *tile = reinterpret_cast<uint16_t *>(s_tiles + e * kRow16MaxPos * 4);
+    char *raw = reinterpret_cast<char *>(s_raw + e * (kChunk * kRow16MaxPos / 8));
+    auto bslot = [&](int buf, int ex, int f) { return s_bstage + ((buf * 4 + ex) * 4 + f) * 64 + lane; };
+    // mixing role: fragment mf = (channel block mf >> 1, K half mf & 1), half mh
+    const int mf = wave >> 1, mh = wave & 1;
     s16x4_t ahi, alo;
     alpha_rows(alpha, min(bt * 4 + (lane & 3), a.B - 1), a.n, ahi, alo);
-    const long prow =
-        ((long)min(o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh) * NP2;
+    const long prow = ((long)min(o0 + 32 * (mf >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (mf & 1) +
+                       8 * lh + 4 * mh) * NP2;
 
-    // convolution role: example `wave`
-    const int b_raw = bt * 4 + wave;
+    const int b_raw = bt * 4 + e;
     const bool valid = b_raw < a.B;
     const int b = valid ? b_raw : a.B - 1;
-    zero_lds(tile, kRow16MaxPos * 32, lane, 64);
+    zero_lds(tile, kRow16MaxPos * 32, lane + 64 * hs, 128);  // the example's two waves
 
-    int aq[PB];
+    int aq[PBW];
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) {
-        const int r = min(2 * pb + (l32 >> 4), a.Ho - 1);
+    for (int pb = 0; pb < PBW; ++pb) {
+        const int r = min(2 * (pb0 + pb) + (l32 >> 4), a.Ho - 1);
         const int c = min(l32 & 15, a.ncols - 1);
         aq[pb] = r * a.ncols + c;
     }
@@ -659,31 +707,35 @@ __global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *_
     const int nrows = min(a.H, a.tile_rows - a.pad);  // input rows the tile holds
     const int pairs = a.W >> 1;
     const int per_g = nrows * pairs;
-    const int ntasks = 4 * per_g;
 
-    // Raw copy of input channels [cc, cc + 32) (fewer at the tail): the
-    // chunk's bytes in NCHW order (16-byte aligned: Cin * H * W is a
-    // multiple of 8), in 1 KB pieces; a lane moves bytes [16 lane, 16 lane +
-    // 16) of a piece. Loads past the chunk's end re-read its last 16 bytes
-    // (discarded); stores past it are skipped.
-    auto raw_bytes = [&](int cc) { return min(kChunk, a.Cin - cc) * HW * 2; };
+    // This wave's raw half of input channels [cc + 16 hs, cc + 16 hs + 16)
+    // (fewer or none at the tail): NCHW bytes, 16-byte aligned, in 1 KB
+    // pieces at byte 32 hs HW of the example's raw buffer. Loads past the
+    // half's end re-read a valid 16 bytes (discarded); stores past it are
+    // skipped.
+    const int hbase = 16 * hs * HW * 2;
+    auto half_bytes = [&](int cc) { return max(0, min(16, a.Cin - cc - 16 * hs)) * HW * 2; };
     auto raw_load = [&](int cc, int j, u32x4_t &r) {
-        const char *src = reinterpret_cast<const char *>(xb + (long)cc * HW);
-        r = *reinterpret_cast<const u32x4_t *>(src + min(j * 1024 + lane * 16, raw_bytes(cc) - 16));
+        const int nb = half_bytes(cc);
+        const char *src = nb > 0 ? reinterpret_cast<const char *>(xb + (long)(cc + 16 * hs) * HW)
+                                 : reinterpret_cast<const char *>(xb);
+        r = *reinterpret_cast<const u32x4_t *>(src + max(0, min(j * 1024 + lane * 16, nb - 16)));
     };
     auto raw_store = [&](int cc, int j, const u32x4_t &r) {
         const int off = j * 1024 + lane * 16;
-        if (off < raw_bytes(cc)) *reinterpret_cast<u32x4_t *>(reinterpret_cast<char *>(raw) + off) = r;
+        if (off < half_bytes(cc)) *reinterpret_cast<u32x4_t *>(raw + hbase + off) = r;
     };
-    // raw chunk -> tile: task = 2 neighbouring positions x 8 channels
+    // raw chunk -> tile for channel groups g = 2 hs, 2 hs + 1: task = 2
+    // neighbouring positions x 8 channels
     // (task + 0.5) / d rounded down is exact in float for task < 2^12, d <= 2^8
     const float inv_per_g = 1.f / (float)per_g, inv_pairs = 1.f / (float)pairs;
     auto raw_to_tile = [&](int cc) {
         const int nch = min(kChunk, a.Cin - cc);
         const uint32_t *rw = reinterpret_cast<const uint32_t *>(raw);
-        for (int task = lane; task < ntasks; task += 64) {
-            const int g = (int)(((float)task + 0.5f) * inv_per_g);
-            const int rem = task - g * per_g;
+        for (int task = lane; task < 2 * per_g; task += 64) {
+            const int gl = (int)(((float)task + 0.5f) * inv_per_g);
+            const int g = 2 * hs + gl;
+            const int rem = task - gl * per_g;
             const int row = (int)(((float)rem + 0.5f) * inv_pairs);
             const int pr = rem - row * pairs;
             const int wofs = (row * a.W + 2 * pr) >> 1;
@@ -702,72 +754,58 @@ __global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *_
         }
     };
 
-    f32x16_t acc[PB][CB];
+    f32x16_t acc[PBW][CB];
 #pragma unroll
-    for (int i = 0; i < PB; ++i)
+    for (int i = 0; i < PBW; ++i)
 #pragma unroll
         for (int j = 0; j < CB; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     const int nchunks = a.Cin_pad / kChunk;
-
-    // chunk 0's raw bytes (2 pieces per step cover <= 14 KB): all loads
-    // first, so that their latencies overlap with each other and with the
-    // first mixings; stored and transposed after those
-    u32x4_t r0[2 * RSTEPS];
-#pragma unroll
-    for (int j = 0; j < 2 * RSTEPS; ++j) raw_load(0, j, r0[j]);
-
-    // expert words of (tap t, chunk starting at channel cc) into w
-    auto words = [&](int t, int cc, uint32_t (&w)[8 * NP2]) { load_packed<NP2>(packed, a, t, cc, prow, w); };
-    auto mix_to = [&](const uint32_t (&w)[8 * NP2], int buf) {
-        u32x4_t m[4];
-        mix4_frag<NP2>(w, ahi, alo, m);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) *bslot(buf, e, wave) = m[e];
-    };
-    // Step s (over chunks and taps) convolves with B_s, held in registers.
-    // During step s the wave reads B_{s+1} from stage buffer (s+1) & 1 and
-    // mixes B_{s+2} into buffer s & 1 (B_s's buffer, whose reads all ended
-    // before the barrier closing step s - 1); the barrier closing step s
-    // publishes B_{s+2}. The expert words of step s' sit in ring slot s' % 3
-    // (9 steps per chunk keep the slot compile-time): those of step s + 5
-    // load in step s, three steps before their mixing.
     const int nsteps = nchunks * KT;
-    auto step_words = [&](int st, uint32_t (&w)[8 * NP2]) {
+
+    // chunk 0's raw half: loads first, so that their latencies overlap with
+    // each other and with the first mixings
+    u32x4_t r0[RSTEPS];
+#pragma unroll
+    for (int j = 0; j < RSTEPS; ++j) raw_load(0, j, r0[j]);
+
+    auto words = [&](int st, uint32_t (&w)[4 * NP2]) {
         st = min(st, nsteps - 1);
         const int c = st / KT;
-        words(st - c * KT, c * kChunk, w);
+        load_packed_half<NP2>(packed, a, st - c * KT, c * kChunk, prow, w);
     };
-    constexpr int WR = 3;
-    uint32_t w[WR][8 * NP2];
-    u32x4_t rb[RL][2];  // raw pieces in flight, slot = (step within chunk) % RL
-    bf16x8_t bcur[4], bnext[4];
-    {
-        uint32_t w0[8 * NP2];
-        step_words(0, w0);
-        mix_to(w0, 0);
-        step_words(1, w0);
-        mix_to(w0, 1);
+    auto mix_to = [&](const uint32_t (&w)[4 * NP2], int buf) {
+        u32x2_t m[4];
+        mix4_half<NP2>(w, ahi, alo, m);
 #pragma unroll
-        for (int st = 2; st < 2 + WR; ++st) step_words(st, w[st % WR]);
-    }
+        for (int ex = 0; ex < 4; ++ex) reinterpret_cast<u32x2_t *>(bslot(buf, ex, mf))[mh] = m[ex];
+    };
+    // Step s reads B_s from stage buffer s & 1 after the barrier that
+    // published it and mixes its half of B_{s+1} into buffer (s+1) & 1, whose
+    // reads (of B_{s-1}) all ended before that barrier; the barrier closing
+    // step s publishes B_{s+1}. The words a mixing uses were loaded right
+    // after the previous mixing, one step earlier.
+    uint32_t w[4 * NP2];
+    u32x4_t rb[RL];  // raw piece in flight, slot = (step within chunk) % RL
+    words(0, w);
+    mix_to(w, 0);
+    words(1, w);
+    lds_barrier();  // tile zeroed, B_0 staged
 #pragma unroll
-    for (int j = 0; j < 2 * RSTEPS; ++j) raw_store(0, j, r0[j]);
+    for (int j = 0; j < RSTEPS; ++j) raw_store(0, j, r0[j]);
     raw_to_tile(0);
-    lds_barrier();
-#pragma unroll
-    for (int f = 0; f < 4; ++f) bcur[f] = __builtin_bit_cast(bf16x8_t, *bslot(0, wave, f));
+    lds_barrier();  // both halves of every tile in place
 
     for (int c = 0; c < nchunks; ++c) {
         const int cn = min(c + 1, nchunks - 1) * kChunk;  // last chunk: harmless re-reads
         const bool more = c + 1 < nchunks;
 #pragma unroll
         for (int u = 0; u < K; ++u) {
-            u32x4_t a0f[PB][2];
+            u32x4_t a0f[PBW][2];
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
+            for (int pb = 0; pb < PBW; ++pb)
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh)
                     a0f[pb][kh] = *reinterpret_cast<const u32x4_t *>(tile + swz(aq[pb] + u * a.ncols, 2 * kh + lh));
@@ -775,21 +813,21 @@ __global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *_
             for (int v = 0; v < K; ++v) {
                 const int i = u * K + v;       // step within the chunk (compile-time)
                 const int par = (c + i) & 1;   // parity of the global step 9 c + i
+                bf16x8_t bcur[4];
 #pragma unroll
-                for (int f = 0; f < 4; ++f) bnext[f] = __builtin_bit_cast(bf16x8_t, *bslot(par ^ 1, wave, f));
-                // All PB blocks are computed (rows past Ho are clamped duplicates,
+                for (int f = 0; f < 4; ++f) bcur[f] = __builtin_bit_cast(bf16x8_t, *bslot(par, e, f));
+                // All blocks are computed (rows past Ho are clamped duplicates,
                 // dropped in the epilogue), so the MFMA stream has no branches.
-                // The mixing sits between the two K halves, so that its
-                // matrix work queues behind the first half and its register
-                // and LDS work issues while the second half runs.
+                // The mixing sits between the two K halves.
 #pragma unroll
                 for (int kh = 0; kh < 2; ++kh) {
                     if (kh == 1) {
                         __builtin_amdgcn_sched_barrier(0);
-                        mix_to(w[(i + 2) % WR], par);  // B of step 9 c + i + 2
+                        mix_to(w, par ^ 1);            // B of step 9 c + i + 1
+                        words(c * KT + i + 2, w);      // for the next step's mixing
                     }
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) {
+                    for (int pb = 0; pb < PBW; ++pb) {
                         const bf16x8_t afr =
                             __builtin_bit_cast(bf16x8_t, v == 0 ? a0f[pb][kh] : dpp_shl(a0f[pb][kh], v));
 #pragma unroll
@@ -798,66 +836,69 @@ __global__ __launch_bounds__(256) void conv_fused_row16_kernel(const uint16_t *_
                                 afr, bcur[cb * 2 + kh], acc[pb][cb], 0, 0, 0);
                     }
                 }
-                step_words(c * KT + i + 5, w[(i + 2) % WR]);  // slot (i + 5) % 3 == (i + 2) % 3
-                // Raw pieces loaded RL steps ago reach LDS, then this step's
-                // pieces load. Issued after the expert words, so waiting for
-                // the raw pieces never waits for younger expert words.
-                if (i >= RL) {
-                    raw_store(cn, 2 * (i - RL), rb[i % RL][0]);
-                    raw_store(cn, 2 * (i - RL) + 1, rb[i % RL][1]);
-                }
-                if (i < RSTEPS) {
-                    raw_load(cn, 2 * i, rb[i % RL][0]);
-                    raw_load(cn, 2 * i + 1, rb[i % RL][1]);
-                }
+                // Raw piece loaded RL steps ago reaches LDS, then this step's
+                // piece loads (after the expert words, so waiting for the raw
+                // piece never waits for younger expert words).
+                if (i >= RL) raw_store(cn, i - RL, rb[i % RL]);
+                if (i < RSTEPS) raw_load(cn, i, rb[i % RL]);
                 if (i == KT - 1 && more) raw_to_tile(cn);
                 lds_barrier();
-#pragma unroll
-                for (int f = 0; f < 4; ++f) bcur[f] = bnext[f];
             }
         }
     }
 
-    // Epilogue through LDS (this wave's raw buffer), one 32-channel block
-    // at a time. D of a 32x32 block holds, per lane, output channel
-    // o0 + 32 cb + l32 and positions 8 j + 4 lh + (0..3): 4 consecutive
-    // columns of padded row 2 pb + (j >> 1). The valid ones go to
-    // ebuf[channel][row * Wo + col] as 2-element words (Wo is even, so a
-    // group holds 0, 2 or 4 valid columns). The block's 32 channel planes
-    // are then one dense run, as are its planes in y, so the copy out is a
-    // straight 16-byte-per-lane copy (4 bytes when unaligned).
-    uint16_t *ebuf = reinterpret_cast<uint16_t *>(raw);
+    // Epilogue through LDS: channel block 0 goes to the example's raw buffer,
+    // block 1 to its tile (no wave reads either any more). D holds, per lane,
+    // channel o0 + 32 cb + l32 and positions 8 j + 4 lh + (0..3): 4
+    // consecutive columns of padded row 2 pb + (j >> 1). The valid ones go
+    // to ebuf[channel][row * Wo + col] as 2-element words (Wo is even, so a
+    // group holds 0, 2 or 4 valid columns). After a barrier (the example's
+    // two waves fill the same planes) each block's 32 channel planes are one
+    // dense run, as in y; wave hs copies block hs out with 16-byte (or
+    // 4-byte) stores.
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
+        uint16_t *ebuf = cb == 0 ? reinterpret_cast<uint16_t *>(raw) : tile;
         uint32_t *ech = reinterpret_cast<uint32_t *>(ebuf + l32 * a.P);
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) {
+        for (int pb = 0; pb < PBW; ++pb) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 2 * pb + (j >> 1);
+                const int r = 2 * (pb0 + pb) + (j >> 1);
                 const int col = 8 * (j & 1) + 4 * lh;
-                const f32x16_t &d = acc[pb][cb];
                 const int e2 = (r * a.Wo + col) >> 1;  // word index (row * Wo + col is even)
-                if (r < a.Ho && col < a.Wo) ech[e2] = pack_bf16x2(d[4 * j], d[4 * j + 1]);
-                if (r < a.Ho && col + 2 < a.Wo) ech[e2 + 1] = pack_bf16x2(d[4 * j + 2], d[4 * j + 3]);
-            }
-        }
-        // the wave reads only what it wrote: LDS order within a wave suffices
-        const int och = min(32, a.Cout - (o0 + 32 * cb));  // channels of this block that exist
-        if (valid && och > 0) {
-            const int bytes = och * a.P * 2;
-            char *dst = reinterpret_cast<char *>(y + ((long)b * a.Cout + o0 + 32 * cb) * a.P);
-            const char *src = reinterpret_cast<const char *>(ebuf);
-            if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (bytes & 15) == 0) {
-#pragma unroll 4
-                for (int off = lane * 16; off < bytes; off += 1024)
-                    *reinterpret_cast<u32x4_t *>(dst + off) = *reinterpret_cast<const u32x4_t *>(src + off);
-            } else {
-                for (int off = lane * 4; off < bytes; off += 256)
-                    *reinterpret_cast<uint32_t *>(dst + off) = *reinterpret_cast<const uint32_t *>(src + off);
+                if (r < a.Ho && col < a.Wo) ech[e2] = pack_bf16x2(acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1]);
+                if (r < a.Ho && col + 2 < a.Wo)
+                    ech[e2 + 1] = pack_bf16x2(acc[pb][cb][4 * j + 2], acc[pb][cb][4 * j + 3]);
             }
         }
     }
+    lds_barrier();
+    const int cbo = hs;  // block this wave copies out
+    const int och = min(32, a.Cout - (o0 + 32 * cbo));  // channels of this block that exist
+    if (valid && och > 0) {
+        const int bytes = och * a.P * 2;
+        char *dst = reinterpret_cast<char *>(y + ((long)b * a.Cout + o0 + 32 * cbo) * a.P);
+        const char *src = cbo == 0 ? raw : reinterpret_cast<const char *>(tile);
+        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (bytes & 15) == 0) {
+#pragma unroll 4
+            for (int off = lane * 16; off < bytes; off += 1024)
+                *reinterpret_cast<u32x4_t *>(dst + off) = *reinterpret_cast<const u32x4_t *>(src + off);
+        } else {
+            for (int off = lane * 4; off < bytes; off += 256)
+                *reinterpret_cast<uint32_t *>(dst + off) = *reinterpret_cast<const uint32_t *>(src + off);
+        }
+    }
+}
+
+template <int NP2>
+__global__ __launch_bounds__(512) void conv_fused_row16_kernel(const uint16_t *__restrict__ x,
+                                                               const uint32_t *__restrict__ packed,
+                                                               const float *__restrict__ alpha,
+                                                               uint16_t *__restrict__ y, ConvArgs a) {
+    // waves 0..3: position blocks 0..3; waves 4..7: blocks 4..6
+    if ((threadIdx.x >> 6) < 4) row16_wave<NP2, 4>(x, packed, alpha, y, a, 0);
+    else row16_wave<NP2, 3>(x, packed, alpha, y, a, 4);
 }
 
 ConvArgs base_args(const Geom &g) {
@@ -939,7 +980,7 @@ bool row16_ok(const Geom &g) {
     const int tile_pos = fused_tile_rows(g) * (g.W + 2 * g.pad);
     return g.stride == 1 && g.KH == 3 && g.KW == 3 && g.W + 2 * g.pad <= 16 && g.Ho <= 14 &&
            g.W % 2 == 0 && ((long)g.Cin * g.H * g.W) % 8 == 0 && tile_pos <= kRow16MaxPos &&
-           g.H * g.W * kChunk * 2 <= kRow16RawBytes;
+           g.H * g.W * kChunk * 2 <= kRow16RawBytes && (g.Cin % 16 == 0 || (g.H * g.W) % 8 == 0);
 }
 
 template <int NP2>
@@ -951,7 +992,7 @@ hipError_t launch_fused_np(const Geom &g, const uint16_t *x, const uint32_t *pac
     a.n_otiles = ceil_div(g.Cout, 64);
     const long blocks = (long)a.n_btiles * a.n_otiles;
     if (row16_ok(g)) {
-        hipLaunchKernelGGL(conv_fused_row16_kernel<NP2>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+        hipLaunchKernelGGL(conv_fused_row16_kernel<NP2>, dim3((unsigned)blocks), dim3(512), 0, stream, x,
                            packed, alpha, y, a);
         return hipGetLastError();
     }
