@@ -725,14 +725,14 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
         const int off = j * 1024 + lane * 16;
         if (off < half_bytes(cc)) *reinterpret_cast<u32x4_t *>(raw + hbase + off) = r;
     };
-    // raw chunk -> tile for channel groups g = 2 hs, 2 hs + 1: task = 2
-    // neighbouring positions x 8 channels
+    // raw chunk -> tile for channel groups g = 2 hs + gl, gl in [gl0, gl1):
+    // task = 2 neighbouring positions x 8 channels
     // (task + 0.5) / d rounded down is exact in float for task < 2^12, d <= 2^8
     const float inv_per_g = 1.f / (float)per_g, inv_pairs = 1.f / (float)pairs;
-    auto raw_to_tile = [&](int cc) {
+    auto raw_to_tile = [&](int cc, int gl0, int gl1) {
         const int nch = min(kChunk, a.Cin - cc);
         const uint32_t *rw = reinterpret_cast<const uint32_t *>(raw);
-        for (int task = lane; task < 2 * per_g; task += 64) {
+        for (int task = gl0 * per_g + lane; task < gl1 * per_g; task += 64) {
             const int gl = (int)(((float)task + 0.5f) * inv_per_g);
             const int g = 2 * hs + gl;
             const int rem = task - gl * per_g;
@@ -795,7 +795,7 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     lds_barrier();  // tile zeroed, B_0 staged
 #pragma unroll
     for (int j = 0; j < RSTEPS; ++j) raw_store(0, j, r0[j]);
-    raw_to_tile(0);
+    raw_to_tile(0, 0, 2);
     lds_barrier();  // both halves of every tile in place
 
     for (int c = 0; c < nchunks; ++c) {
@@ -841,7 +841,12 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
                 // piece never waits for younger expert words).
                 if (i >= RL) raw_store(cn, i - RL, rb[i % RL]);
                 if (i < RSTEPS) raw_load(cn, i, rb[i % RL]);
-                if (i == KT - 1 && more) raw_to_tile(cn);
+                // The tile's last reads of this chunk (row 2's fragments) came
+                // before the barrier closing step 6, so steps 7 and 8 may
+                // overwrite it: group 2 hs in step 7 (its raw bytes arrived by
+                // step 5), group 2 hs + 1 in step 8 after its last piece.
+                if (i == KT - 2 && more) raw_to_tile(cn, 0, 1);
+                if (i == KT - 1 && more) raw_to_tile(cn, 1, 2);
                 lds_barrier();
             }
         }
