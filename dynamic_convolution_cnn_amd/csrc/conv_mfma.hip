@@ -782,13 +782,18 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
 #pragma unroll
         for (int ex = 0; ex < 4; ++ex) reinterpret_cast<u32x2_t *>(bslot(buf, ex, mf))[mh] = m[ex];
     };
-    // Step s reads B_s from stage buffer s & 1 after the barrier that
-    // published it and mixes its half of B_{s+1} into buffer (s+1) & 1, whose
-    // reads (of B_{s-1}) all ended before that barrier; the barrier closing
-    // step s publishes B_{s+1}. The words a mixing uses were loaded right
-    // after the previous mixing, one step earlier.
+    // One barrier per step, between its two K halves, so that no MFMA waits
+    // for it: step s
+    //   reads B_s's K-half-1 fragments from stage buffer s & 1,
+    //   runs the K-half-0 MFMAs (fragments read during step s - 1),
+    //   mixes its half of B_{s+1} into buffer (s+1) & 1 (B_{s-1}'s, whose last
+    //   reads came before the previous barrier) and does the raw staging,
+    //   meets the barrier, which publishes B_{s+1},
+    //   reads B_{s+1}'s K-half-0 fragments while the K-half-1 MFMAs run.
+    // The words a mixing uses were loaded right after the previous mixing.
     uint32_t w[4 * NP2];
     u32x4_t rb[RL];  // raw piece in flight, slot = (step within chunk) % RL
+    bf16x8_t bk0[2];  // K-half-0 fragments (channel blocks 0, 1) of the coming step
     words(0, w);
     mix_to(w, 0);
     words(1, w);
@@ -797,6 +802,8 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     for (int j = 0; j < RSTEPS; ++j) raw_store(0, j, r0[j]);
     raw_to_tile(0, 0, 2);
     lds_barrier();  // both halves of every tile in place
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) bk0[cb] = __builtin_bit_cast(bf16x8_t, *bslot(0, e, 2 * cb));
 
     for (int c = 0; c < nchunks; ++c) {
         const int cn = min(c + 1, nchunks - 1) * kChunk;  // last chunk: harmless re-reads
@@ -813,41 +820,42 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
             for (int v = 0; v < K; ++v) {
                 const int i = u * K + v;       // step within the chunk (compile-time)
                 const int par = (c + i) & 1;   // parity of the global step 9 c + i
-                bf16x8_t bcur[4];
+                bf16x8_t bk1[2];
 #pragma unroll
-                for (int f = 0; f < 4; ++f) bcur[f] = __builtin_bit_cast(bf16x8_t, *bslot(par, e, f));
+                for (int cb = 0; cb < 2; ++cb)
+                    bk1[cb] = __builtin_bit_cast(bf16x8_t, *bslot(par, e, 2 * cb + 1));
                 // All blocks are computed (rows past Ho are clamped duplicates,
                 // dropped in the epilogue), so the MFMA stream has no branches.
-                // The mixing sits between the two K halves.
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    if (kh == 1) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        mix_to(w, par ^ 1);            // B of step 9 c + i + 1
-                        words(c * KT + i + 2, w);      // for the next step's mixing
-                    }
+                auto mfma_half = [&](int kh, const bf16x8_t (&bf)[2]) {
 #pragma unroll
                     for (int pb = 0; pb < PBW; ++pb) {
                         const bf16x8_t afr =
                             __builtin_bit_cast(bf16x8_t, v == 0 ? a0f[pb][kh] : dpp_shl(a0f[pb][kh], v));
 #pragma unroll
-                        for (int cb = 0; cb < CB; ++cb)
-                            acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                afr, bcur[cb * 2 + kh], acc[pb][cb], 0, 0, 0);
+                        for (int cb = 0; cb < 2; ++cb)
+                            acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bf[cb], acc[pb][cb], 0, 0, 0);
                     }
-                }
+                };
+                mfma_half(0, bk0);
+                mix_to(w, par ^ 1);            // B of step 9 c + i + 1
+                words(c * KT + i + 2, w);      // for the next step's mixing
                 // Raw piece loaded RL steps ago reaches LDS, then this step's
                 // piece loads (after the expert words, so waiting for the raw
-                // piece never waits for younger expert words).
+                // piece never waits for younger expert words). The tile's last
+                // reads of this chunk (row 2's fragments, step 6) came before
+                // step 6's barrier, so steps 7 and 8 may overwrite it: group
+                // 2 hs in step 7 (its raw bytes arrived by step 5), group
+                // 2 hs + 1 in step 8 after its last piece; both before the
+                // barrier that precedes the next chunk's first tile reads.
                 if (i >= RL) raw_store(cn, i - RL, rb[i % RL]);
                 if (i < RSTEPS) raw_load(cn, i, rb[i % RL]);
-                // The tile's last reads of this chunk (row 2's fragments) came
-                // before the barrier closing step 6, so steps 7 and 8 may
-                // overwrite it: group 2 hs in step 7 (its raw bytes arrived by
-                // step 5), group 2 hs + 1 in step 8 after its last piece.
                 if (i == KT - 2 && more) raw_to_tile(cn, 0, 1);
                 if (i == KT - 1 && more) raw_to_tile(cn, 1, 2);
                 lds_barrier();
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    bk0[cb] = __builtin_bit_cast(bf16x8_t, *bslot(par ^ 1, e, 2 * cb));
+                mfma_half(1, bk1);
             }
         }
     }
