@@ -219,7 +219,29 @@ def main():
     pack_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / nk
     conv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / nk
 
+    # standalone mixing (dynconv_mix: every W_b to memory in the natural
+    # layout) of the first layer, timed alone with events: an HBM stream of
+    # n |W| bytes in and B |W| bytes out
     L0 = w.layers[0]
+    mixed = torch.empty((w.B,) + tuple(experts[0].shape[1:]), dtype=experts[0].dtype, device=dev)
+    nm = 20  # launches per graph replay (a graph, so that launch cost stays out)
+    for _ in range(3):
+        bd.dynconv_mix(alphas[0], experts[0], L0.groups, mixed=mixed)
+    gm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gm):
+        for _ in range(nm):
+            bd.dynconv_mix(alphas[0], experts[0], L0.groups, mixed=mixed)
+    gm.replay()
+    torch.cuda.synchronize()
+    mev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    mev[0].record(stream)
+    gm.replay()
+    mev[1].record(stream)
+    torch.cuda.synchronize()
+    mix_ms = mev[0].elapsed_time(mev[1]) / nm
+    mix_bytes = (w.n + w.B) * experts[0][0].numel() * esz + w.B * w.n * 4
+    del mixed
+
     conv_flops0 = 2 * w.B * L0.macs_per_example()
     flops_all = w.conv_flops()
     images_s = w.B / (ms_per_step * 1e-3)
@@ -255,6 +277,9 @@ def main():
                        "conv_layer0": round(conv_ms * 1e3, 2)},
         "route_hbm": {"GB/s": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
                       "frac": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
+        "mix_hbm": {"us": round(mix_ms * 1e3, 2), "MB": round(mix_bytes / 1e6, 2),
+                    "GB/s": round(mix_bytes / (mix_ms * 1e-3) / 1e9, 1),
+                    "frac": round(mix_bytes / (mix_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
         "roofline": {"kernel": "conv layer 0 (" + pol_name.get(pols[0], "") + ")",
                      "bound": "mfma", "achieved": round(conv_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -110,6 +110,45 @@ __global__ __launch_bounds__(kMixThreads) void mix_natural_kernel(
         if (j < nb) Vec8<T>::store(mixed + (long)(b0 + j) * wsize + v * 8, acc[j]);
 }
 
+// Vector path for n <= kMixMaxN: all of a thread's expert vectors load at
+// once (clamped indices, no branches, so their latencies overlap); experts
+// past n get attention 0. Then expert by expert: widen, and accumulate into
+// the kMixBT examples (attentions are uniform across the workgroup).
+constexpr int kMixMaxN = 8;  // above this the accumulate is VALU-bound; chunked kernel
+template <typename T, int NMAX>
+__global__ __launch_bounds__(kMixThreads) void mix_natural_all_kernel(
+    const float *__restrict__ alpha, const T *__restrict__ experts, T *__restrict__ mixed,
+    int B, int n, long wsize) {
+    const long nvec = wsize / 8;
+    const long v = min((long)blockIdx.x * kMixThreads + threadIdx.x, nvec - 1);
+    const bool active = (long)blockIdx.x * kMixThreads + threadIdx.x < nvec;
+    const int b0 = blockIdx.y * kMixBT;
+    const int nb = min(kMixBT, B - b0);
+    Vec8<T> q[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) q[i].load(experts + (long)min(i, n - 1) * wsize + v * 8);
+    float acc[kMixBT][8];
+#pragma unroll
+    for (int j = 0; j < kMixBT; ++j)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[j][k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        float e[8];
+        q[i].widen(e);
+#pragma unroll
+        for (int j = 0; j < kMixBT; ++j) {
+            const float aj = (i < n && j < nb) ? alpha[(long)(b0 + j) * n + min(i, n - 1)] : 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[j][k] = fmaf(aj, e[k], acc[j][k]);
+        }
+    }
+    if (!active) return;
+#pragma unroll
+    for (int j = 0; j < kMixBT; ++j)
+        if (j < nb) Vec8<T>::store(mixed + (long)(b0 + j) * wsize + v * 8, acc[j]);
+}
+
 // Scalar path for any wsize: one element per thread, all examples.
 template <typename T>
 __global__ __launch_bounds__(kMixThreads) void mix_scalar_kernel(
@@ -216,6 +255,21 @@ hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha, con
         const long nvec = wsize / 8;
         dim3 grid((unsigned)((nvec + kMixThreads - 1) / kMixThreads),
                   (unsigned)((g.B + kMixBT - 1) / kMixBT));
+        if (g.n <= kMixMaxN) {
+            auto go = [&](auto kb, auto kf) {
+                if (g.bf16)
+                    hipLaunchKernelGGL(kb, grid, dim3(kMixThreads), 0, stream, alpha,
+                                       static_cast<const uint16_t *>(experts),
+                                       static_cast<uint16_t *>(mixed), g.B, g.n, wsize);
+                else
+                    hipLaunchKernelGGL(kf, grid, dim3(kMixThreads), 0, stream, alpha,
+                                       static_cast<const float *>(experts), static_cast<float *>(mixed),
+                                       g.B, g.n, wsize);
+                return hipGetLastError();
+            };
+            if (g.n <= 4) return go(mix_natural_all_kernel<uint16_t, 4>, mix_natural_all_kernel<float, 4>);
+            return go(mix_natural_all_kernel<uint16_t, 8>, mix_natural_all_kernel<float, 8>);
+        }
         if (g.bf16)
             hipLaunchKernelGGL(mix_natural_kernel<uint16_t>, grid, dim3(kMixThreads), 0, stream,
                                alpha, static_cast<const uint16_t *>(experts),

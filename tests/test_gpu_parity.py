@@ -148,6 +148,23 @@ def test_mix_one_hot_is_bitwise(dtype):
         np.testing.assert_array_equal(got[b], e[b % n])
 
 
+@pytest.mark.parametrize("n", [5, 7, 9, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mix_vector_expert_counts(n, dtype):
+    """Vector path (kernel size a multiple of 8) for expert counts below and
+    above the single-pass limit, with a batch that is not a multiple of 8."""
+    B = 11
+    rng = np.random.default_rng(13 + n)
+    e = rng.standard_normal((n, 16, 8, 3, 3), dtype=np.float32)
+    if dtype == "bf16":
+        e = inputs.bf16_round(e)
+    alpha = rng.uniform(-1, 1, (B, n)).astype(np.float32)
+    say("mix vector", n, dtype)
+    m = bd.dynconv_mix(to_dev(alpha, "f32"), to_dev(e, dtype))
+    torch.cuda.synchronize()
+    check(from_dev(m), oracle.mix(alpha, e), TOL[dtype], f"mix n={n}")
+
+
 @pytest.mark.parametrize("wshape", [(5, 3, 3, 3), (7, 1, 5, 5), (3, 2, 1, 1)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_mix_ragged(wshape, dtype):
