@@ -564,10 +564,10 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
 //     covers a younger load.
 //   - The epilogue stores each lane's 4 consecutive output columns straight
 //     to y.
-constexpr int kRow16MaxPos = 256;  // tile positions (16 x 16) and input plane positions
-constexpr int kRow16RawBytes = 14 * 1024;  // raw chunk bytes the 3x3 schedule moves (7 steps x 2 KB)
-__shared__ __attribute__((aligned(16))) u32x4_t s_tiles[4 * kRow16MaxPos * 4];
-__shared__ __attribute__((aligned(16))) u32x4_t s_raw[4 * kChunk * kRow16MaxPos / 8];
+constexpr int kRow16MaxPos = 256;  // tile positions (16 x 16)
+constexpr int kRow16Slots = 7;     // staging slots per chunk (loads in steps 0..6)
+// Two tiles per example (chunk parity), then the double-buffered B stage.
+__shared__ __attribute__((aligned(16))) u32x4_t s_tiles[2 * 4 * kRow16MaxPos * 4];
 __shared__ __attribute__((aligned(16))) u32x4_t s_bstage[2 * 4 * 4 * 64];
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -660,9 +660,8 @@ __device__ __forceinline__ void mix4_half(const uint32_t (&w)[4 * NP2], s16x4_t 
 // channels, so one A fragment feeds two MFMAs. The two waves of a SIMD share
 // its matrix core: one wave's LDS round trips, waits and barrier skew overlap
 // the other's MFMAs. Wave w also mixes half h = w & 1 of B fragment w >> 1
-// for all 4 examples, and stages and transposes the 16 input channels
-// [16 hs, 16 hs + 16), hs = w >> 2, of its example's next chunk, so its raw
-// bytes and tile granules are its own.
+// for all 4 examples, and stages the 16 input channels [16 hs, 16 hs + 16),
+// hs = w >> 2, of its example's next chunk into the example's other tile.
 template <int NP2, int PBW>
 __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const uint32_t *__restrict__ packed,
                                            const float *__restrict__ alpha, uint16_t *__restrict__ y,
@@ -670,18 +669,18 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     constexpr int CB = 2;  // 2 x 32 output channels
     constexpr int K = 3;   // 3 x 3 taps: a chunk is 9 steps, fully unrolled
     constexpr int KT = K * K;
-    constexpr int RL = 2;  // raw pieces load in step i and reach LDS in step i + RL
-    constexpr int RSTEPS = KT - RL;  // steps that load a raw piece (one 1 KB piece each)
+    constexpr int RL = 2;  // a staging slot loads in step i and reaches the tile in step i + RL
+    static_assert(kRow16Slots + RL <= KT, "staging must end by the chunk's last step");
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int ot = logical / a.n_btiles;
     const int bt = logical - ot * a.n_btiles;
     const int o0 = ot * CB * 32;
     // convolution role
     const int e = wave & 3, hs = wave >> 2;
-    uint16_t *tile = reinterpret_cast<uint16_t *>(s_tiles + e * kRow16MaxPos * 4);
-    char *raw = reinterpret_cast<char *>(s_raw + e * (kChunk * kRow16MaxPos / 8));
+    auto tile_of = [&](int par) { return reinterpret_cast<uint16_t *>(s_tiles + (par * 4 + e) * kRow16MaxPos * 4); };
     auto bslot = [&](int buf, int ex, int f) { return s_bstage + ((buf * 4 + ex) * 4 + f) * 64 + lane; };
     // mixing role: fragment mf = (channel block mf >> 1, K half mf & 1), half mh
     const int mf = wave >> 1, mh = wave & 1;
@@ -693,7 +692,9 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     const int b_raw = bt * 4 + e;
     const bool valid = b_raw < a.B;
     const int b = valid ? b_raw : a.B - 1;
-    zero_lds(tile, kRow16MaxPos * 32, lane + 64 * hs, 128);  // the example's two waves
+    // both tiles (their padding stays zero: staging writes interior positions only)
+    zero_lds(tile_of(0), kRow16MaxPos * 32, lane + 64 * hs, 128);
+    zero_lds(tile_of(1), kRow16MaxPos * 32, lane + 64 * hs, 128);
 
     int aq[PBW];
 #pragma unroll
@@ -704,54 +705,53 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     }
     const uint16_t *xb = x + (long)b * a.x_bstride;
     const int HW = a.H * a.W;
-    const int nrows = min(a.H, a.tile_rows - a.pad);  // input rows the tile holds
+    const int plane = HW * 2;  // bytes per input channel plane
     const int pairs = a.W >> 1;
-    const int per_g = nrows * pairs;
+    const int per_g = min(a.H, a.tile_rows - a.pad) * pairs;  // position pairs the tile holds per channel
+    const int nhalf = 4 * per_g;                               // half-tasks of this wave per chunk
 
-    // This wave's raw half of input channels [cc + 16 hs, cc + 16 hs + 16)
-    // (fewer or none at the tail): NCHW bytes, 16-byte aligned, in 1 KB
-    // pieces at byte 32 hs HW of the example's raw buffer. Loads past the
-    // half's end re-read a valid 16 bytes (discarded); stores past it are
-    // skipped.
-    const int hbase = 16 * hs * HW * 2;
-    auto half_bytes = [&](int cc) { return max(0, min(16, a.Cin - cc - 16 * hs)) * HW * 2; };
-    auto raw_load = [&](int cc, int j, u32x4_t &r) {
-        const int nb = half_bytes(cc);
-        const char *src = nb > 0 ? reinterpret_cast<const char *>(xb + (long)(cc + 16 * hs) * HW)
-                                 : reinterpret_cast<const char *>(xb);
-        r = *reinterpret_cast<const u32x4_t *>(src + max(0, min(j * 1024 + lane * 16, nb - 16)));
+    // Staging of this wave's 16 input channels [cc + 16 hs, cc + 16 hs + 16)
+    // of a chunk, as half-tasks of 2 neighbouring positions x 4 channels:
+    // 4 dword loads (one per channel, both positions) and, transposed in
+    // registers, two 8-byte tile writes (half a 16-byte channel granule per
+    // position). Half-task t = 64 s + lane is in slot s; lanes past the last
+    // one repeat it (same bytes to the same place). Channels past Cin are
+    // beyond the buffer's extent and read as zeros.
+    // (The descriptor must live in scalar registers: its fields are passed
+    // through readfirstlane, which they equal on every lane anyway.)
+    auto rsrc_of = [&](int cc) {
+        const int c0 = min(cc + 16 * hs, a.Cin - 1);
+        const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(16, a.Cin - cc - 16 * hs)) * plane);
+        const uint64_t p = reinterpret_cast<uint64_t>(xb + (long)c0 * HW);
+        const uint64_t ps = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
+        return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ps), 0, nbytes, 0x00020000);
     };
-    auto raw_store = [&](int cc, int j, const u32x4_t &r) {
-        const int off = j * 1024 + lane * 16;
-        if (off < half_bytes(cc)) *reinterpret_cast<u32x4_t *>(raw + hbase + off) = r;
-    };
-    // raw chunk -> tile for channel groups g = 2 hs + gl, gl in [gl0, gl1):
-    // task = 2 neighbouring positions x 8 channels
-    // (task + 0.5) / d rounded down is exact in float for task < 2^12, d <= 2^8
+    // (t + 0.5) / d rounded down is exact in float for t < 2^12, d <= 2^8
     const float inv_per_g = 1.f / (float)per_g, inv_pairs = 1.f / (float)pairs;
-    auto raw_to_tile = [&](int cc, int gl0, int gl1) {
-        const int nch = min(kChunk, a.Cin - cc);
-        const uint32_t *rw = reinterpret_cast<const uint32_t *>(raw);
-        for (int task = gl0 * per_g + lane; task < gl1 * per_g; task += 64) {
-            const int gl = (int)(((float)task + 0.5f) * inv_per_g);
-            const int g = 2 * hs + gl;
-            const int rem = task - gl * per_g;
-            const int row = (int)(((float)rem + 0.5f) * inv_pairs);
-            const int pr = rem - row * pairs;
-            const int wofs = (row * a.W + 2 * pr) >> 1;
-            uint32_t r[8];
+    auto split = [&](int s, int ln, int &quad, int &rem) {
+        const int t = min(64 * s + ln, nhalf - 1);
+        quad = (int)(((float)t + 0.5f) * inv_per_g);
+        rem = t - quad * per_g;
+    };
+    auto stage_load = [&](__amdgpu_buffer_rsrc_t rs, int s, int ln, uint32_t (&r)[4]) {
+        int quad, rem;
+        split(s, ln, quad, rem);
+        const int vo = 4 * quad * plane + 4 * rem;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                r[j] = (8 * g + j < nch) ? rw[(8 * g + j) * (HW >> 1) + wofs] : 0u;
-            const int q = (row + a.pad) * a.ncols + 2 * pr + a.pad;
-            u32x4_t o0v, o1v;
-            o0v.x = lo_pair(r[0], r[1]); o0v.y = lo_pair(r[2], r[3]);
-            o0v.z = lo_pair(r[4], r[5]); o0v.w = lo_pair(r[6], r[7]);
-            o1v.x = hi_pair(r[0], r[1]); o1v.y = hi_pair(r[2], r[3]);
-            o1v.z = hi_pair(r[4], r[5]); o1v.w = hi_pair(r[6], r[7]);
-            *reinterpret_cast<u32x4_t *>(tile + swz(q, g)) = o0v;
-            *reinterpret_cast<u32x4_t *>(tile + swz(q + 1, g)) = o1v;
-        }
+        for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + j * plane, 0, 0);
+    };
+    auto stage_store = [&](uint16_t *t, int s, int ln, const uint32_t (&r)[4]) {
+        int quad, rem;
+        split(s, ln, quad, rem);
+        const int row = (int)(((float)rem + 0.5f) * inv_pairs);
+        const int q = (row + a.pad) * a.ncols + 2 * (rem - row * pairs) + a.pad;
+        const int g = 2 * hs + (quad >> 1), ho = 4 * (quad & 1);
+        u32x2_t p0, p1;
+        p0.x = lo_pair(r[0], r[1]); p0.y = lo_pair(r[2], r[3]);
+        p1.x = hi_pair(r[0], r[1]); p1.y = hi_pair(r[2], r[3]);
+        *reinterpret_cast<u32x2_t *>(t + swz(q, g) + ho) = p0;
+        *reinterpret_cast<u32x2_t *>(t + swz(q + 1, g) + ho) = p1;
     };
 
     f32x16_t acc[PBW][CB];
@@ -765,11 +765,14 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     const int nchunks = a.Cin_pad / kChunk;
     const int nsteps = nchunks * KT;
 
-    // chunk 0's raw half: loads first, so that their latencies overlap with
-    // each other and with the first mixings
-    u32x4_t r0[RSTEPS];
+    // chunk 0: loads first, so that their latencies overlap with each other
+    // and with the first mixings
+    uint32_t r0[kRow16Slots][4];
+    {
+        const auto rs = rsrc_of(0);
 #pragma unroll
-    for (int j = 0; j < RSTEPS; ++j) raw_load(0, j, r0[j]);
+        for (int s = 0; s < kRow16Slots; ++s) stage_load(rs, s, lane, r0[s]);
+    }
 
     auto words = [&](int st, uint32_t (&w)[4 * NP2]) {
         st = min(st, nsteps - 1);
@@ -787,29 +790,38 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     //   reads B_s's K-half-1 fragments from stage buffer s & 1,
     //   runs the K-half-0 MFMAs (fragments read during step s - 1),
     //   mixes its half of B_{s+1} into buffer (s+1) & 1 (B_{s-1}'s, whose last
-    //   reads came before the previous barrier) and does the raw staging,
+    //   reads came before the previous barrier) and does its staging slot,
     //   meets the barrier, which publishes B_{s+1},
     //   reads B_{s+1}'s K-half-0 fragments while the K-half-1 MFMAs run.
     // The words a mixing uses were loaded right after the previous mixing.
     uint32_t w[4 * NP2];
-    u32x4_t rb[RL];  // raw piece in flight, slot = (step within chunk) % RL
-    bf16x8_t bk0[2];  // K-half-0 fragments (channel blocks 0, 1) of the coming step
+    uint32_t rb[RL][4];  // staging slot in flight, ring index = (step within chunk) % RL
+    bf16x8_t bk0[2];     // K-half-0 fragments (channel blocks 0, 1) of the coming step
     words(0, w);
     mix_to(w, 0);
     words(1, w);
-    lds_barrier();  // tile zeroed, B_0 staged
+    lds_barrier();  // tiles zeroed, B_0 staged
 #pragma unroll
-    for (int j = 0; j < RSTEPS; ++j) raw_store(0, j, r0[j]);
-    raw_to_tile(0, 0, 2);
-    lds_barrier();  // both halves of every tile in place
+    for (int s = 0; s < kRow16Slots; ++s) stage_store(tile_of(0), s, lane, r0[s]);
+    lds_barrier();  // chunk 0 in tile 0
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) bk0[cb] = __builtin_bit_cast(bf16x8_t, *bslot(0, e, 2 * cb));
 
     for (int c = 0; c < nchunks; ++c) {
-        const int cn = min(c + 1, nchunks - 1) * kChunk;  // last chunk: harmless re-reads
-        const bool more = c + 1 < nchunks;
+        const uint16_t *tile = tile_of(c & 1);
+        uint16_t *tnext = tile_of((c + 1) & 1);  // chunk c - 1's, whose last reads preceded this chunk
+        // the last chunk stages a harmless copy of itself into the idle tile
+        const auto rs = rsrc_of(min(c + 1, nchunks - 1) * kChunk);
+        // Lane index kept opaque per chunk: the staging addresses are
+        // recomputed where used rather than held across the whole loop.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int u = 0; u < K; ++u) {
+            // Positions kept opaque per kernel row, like the lane above: the
+            // swizzled fragment addresses are computed next to their reads.
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) asm volatile("" : "+v"(aq[pb]));
             u32x4_t a0f[PBW][2];
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb)
@@ -839,18 +851,13 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
                 mfma_half(0, bk0);
                 mix_to(w, par ^ 1);            // B of step 9 c + i + 1
                 words(c * KT + i + 2, w);      // for the next step's mixing
-                // Raw piece loaded RL steps ago reaches LDS, then this step's
-                // piece loads (after the expert words, so waiting for the raw
-                // piece never waits for younger expert words). The tile's last
-                // reads of this chunk (row 2's fragments, step 6) came before
-                // step 6's barrier, so steps 7 and 8 may overwrite it: group
-                // 2 hs in step 7 (its raw bytes arrived by step 5), group
-                // 2 hs + 1 in step 8 after its last piece; both before the
-                // barrier that precedes the next chunk's first tile reads.
-                if (i >= RL) raw_store(cn, i - RL, rb[i % RL]);
-                if (i < RSTEPS) raw_load(cn, i, rb[i % RL]);
-                if (i == KT - 2 && more) raw_to_tile(cn, 0, 1);
-                if (i == KT - 1 && more) raw_to_tile(cn, 1, 2);
+                // The slot loaded RL steps ago goes to the next chunk's tile,
+                // then this step's slot loads (after the expert words, so
+                // waiting for a slot never waits for younger expert words).
+                // Every tile write precedes the barrier of step 8, after
+                // which the next chunk's first fragments are read.
+                if (i >= RL) stage_store(tnext, i - RL, ln, rb[i % RL]);
+                if (i < kRow16Slots) stage_load(rs, i, ln, rb[i % RL]);
                 lds_barrier();
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
@@ -860,18 +867,18 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
         }
     }
 
-    // Epilogue through LDS: channel block 0 goes to the example's raw buffer,
-    // block 1 to its tile (no wave reads either any more). D holds, per lane,
-    // channel o0 + 32 cb + l32 and positions 8 j + 4 lh + (0..3): 4
-    // consecutive columns of padded row 2 pb + (j >> 1). The valid ones go
-    // to ebuf[channel][row * Wo + col] as 2-element words (Wo is even, so a
+    // Epilogue through LDS: channel block cb goes to the example's tile
+    // cb (no wave reads either any more). D holds, per lane, channel o0 +
+    // 32 cb + l32 and positions 8 j + 4 lh + (0..3): 4 consecutive columns
+    // of padded row 2 pb + (j >> 1). The valid ones go to
+    // ebuf[channel][row * Wo + col] as 2-element words (Wo is even, so a
     // group holds 0, 2 or 4 valid columns). After a barrier (the example's
     // two waves fill the same planes) each block's 32 channel planes are one
     // dense run, as in y; wave hs copies block hs out with 16-byte (or
     // 4-byte) stores.
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        uint16_t *ebuf = cb == 0 ? reinterpret_cast<uint16_t *>(raw) : tile;
+        uint16_t *ebuf = tile_of(cb);
         uint32_t *ech = reinterpret_cast<uint32_t *>(ebuf + l32 * a.P);
 #pragma unroll
         for (int pb = 0; pb < PBW; ++pb) {
@@ -892,7 +899,7 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     if (valid && och > 0) {
         const int bytes = och * a.P * 2;
         char *dst = reinterpret_cast<char *>(y + ((long)b * a.Cout + o0 + 32 * cbo) * a.P);
-        const char *src = cbo == 0 ? raw : reinterpret_cast<const char *>(tile);
+        const char *src = reinterpret_cast<const char *>(tile_of(cbo));
         if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (bytes & 15) == 0) {
 #pragma unroll 4
             for (int off = lane * 16; off < bytes; off += 1024)
@@ -984,16 +991,17 @@ size_t fused_lds_bytes(const Geom &g) {
     return tiles + 2 * 4 * 4 * 64 * 16;  // + double-buffered B stage
 }
 
-// Static LDS of the row-16 kernel: 4 tiles of 16 x 16 positions, 4 raw
-// buffers of 16 KB (a chunk may use 14 KB: 7 loading steps x 2 KB) and the
-// double-buffered B stage. Conditions: 3x3 taps at stride 1, padded rows of
-// at most 16 positions, at most 14 output rows, W even (so output pieces of
-// 2 elements are 4-byte aligned) and 16-byte aligned channel chunks.
+// Static LDS of the row-16 kernel: 2 x 4 tiles of 16 x 16 positions (chunk
+// parity x example) and the double-buffered B stage. Conditions: 3x3 taps
+// at stride 1, padded rows of at most 16 positions, at most 14 output rows,
+// W even (position pairs are 4-byte words of a channel plane, and output
+// pieces of 2 elements are 4-byte aligned) and at most 7 x 64 half-tasks
+// (2 positions x 4 channels) per wave and chunk.
 bool row16_ok(const Geom &g) {
     const int tile_pos = fused_tile_rows(g) * (g.W + 2 * g.pad);
+    const int per_g = std::min(g.H, fused_tile_rows(g) - g.pad) * (g.W / 2);
     return g.stride == 1 && g.KH == 3 && g.KW == 3 && g.W + 2 * g.pad <= 16 && g.Ho <= 14 &&
-           g.W % 2 == 0 && ((long)g.Cin * g.H * g.W) % 8 == 0 && tile_pos <= kRow16MaxPos &&
-           g.H * g.W * kChunk * 2 <= kRow16RawBytes && (g.Cin % 16 == 0 || (g.H * g.W) % 8 == 0);
+           g.W % 2 == 0 && tile_pos <= kRow16MaxPos && 4 * per_g <= kRow16Slots * 64;
 }
 
 template <int NP2>
