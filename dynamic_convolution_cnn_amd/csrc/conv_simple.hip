@@ -13,6 +13,7 @@
 //   float; each thread computes a strip of outputs along a row, so input
 //   values are reused from registers across the strip.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -251,6 +252,300 @@ __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_strip_kernel(
     }
 }
 
+// Depthwise for bf16 planes with square K x K taps (K = 3, 5, 7), stride ST
+// (1, 2) and W even, products on v_dot2_f32_bf16 (two bf16 products summed
+// in fp32 per instruction). Shared by the two kernels below:
+//   - The zero-padded plane sits in the wave's LDS region as bf16: row pitch
+//     a multiple of 8 elements, wide enough for the last strip's window,
+//     interior at column pad. Rows arrive as 4-element pieces (8 bytes) when
+//     W % 4 == 0, else as 2-element words.
+//   - The mixed taps (sum_i alpha_bi E_i[c], rounded to bf16 like every other
+//     mixed kernel) are kept as bf16 pairs: row u, columns 2q and 2q + 1;
+//     past an odd K the pair ends in 0.
+//   - A lane task is 8 consecutive outputs of a row. Per kernel row it reads
+//     the window with 16-byte LDS reads; output j and tap pair q take input
+//     elements j*ST + 2q and j*ST + 2q + 1: a window word when j*ST is even,
+//     else a word assembled from two neighbours (alignbit).
+constexpr int kDw2S = 8;              // outputs per lane task along a row
+constexpr int kDw2PlaneBytes = 8192;  // LDS bytes per plane at most
+constexpr int kDw2Pre = 4;            // plane pieces per lane held in registers
+
+__host__ __device__ constexpr int dw2_pairs(int K) { return (K + 1) / 2; }
+__host__ __device__ constexpr int dw2_words(int K, int ST) { return ((kDw2S - 1) * ST + 2 * dw2_pairs(K) + 1) / 2; }
+
+// One plane's pieces: first kDw2Pre per lane (clamped indices, no branches
+// between the loads).
+__device__ __forceinline__ void dw2_fetch(const uint16_t *__restrict__ xp, int lane, int npc, bool q4,
+                                          u32x2_t (&pc)[kDw2Pre]) {
+#pragma unroll
+    for (int k = 0; k < kDw2Pre; ++k) {
+        const int p = min(lane + 64 * k, npc - 1);
+        if (q4) {
+            pc[k] = reinterpret_cast<const u32x2_t *>(xp)[p];
+        } else {
+            pc[k].x = reinterpret_cast<const uint32_t *>(xp)[p];
+            pc[k].y = 0u;
+        }
+    }
+}
+
+// Writes piece p (pe elements at element p * pe of the plane) into the padded
+// LDS plane; rows below the last one read (stride 2) are skipped.
+__device__ __forceinline__ void dw2_put(uint32_t *pl, int p, u32x2_t v, int pe, bool q4, float invW, int W,
+                                        int pad, int pitch, int Hp) {
+    const int e = p * pe;
+    // (e + 0.5) / W rounded down is exact in float for e < 2^12, W <= 2^8
+    const int h = (int)(((float)e + 0.5f) * invW);
+    if (h + pad >= Hp) return;
+    const int off = (h + pad) * pitch + (e - h * W) + pad;  // element offset
+    if ((pad & 1) == 0) {
+        pl[off >> 1] = v.x;
+        if (q4) pl[(off >> 1) + 1] = v.y;
+    } else {
+        uint16_t *pl16 = reinterpret_cast<uint16_t *>(pl);
+        pl16[off] = (uint16_t)v.x;
+        pl16[off + 1] = (uint16_t)(v.x >> 16);
+        if (q4) {
+            pl16[off + 2] = (uint16_t)v.y;
+            pl16[off + 3] = (uint16_t)(v.y >> 16);
+        }
+    }
+}
+
+// 8 outputs of row r from column s0 of the staged plane.
+template <int K, int ST>
+__device__ __forceinline__ void dw2_task(const uint32_t *pl, int pw, const uint32_t (&tp)[K][dw2_pairs(K)], int r,
+                                         int s0, float (&acc)[kDw2S]) {
+    constexpr int KP = dw2_pairs(K);
+    constexpr int NQ = (dw2_words(K, ST) + 3) / 4;  // 16-byte window reads per kernel row
+#pragma unroll
+    for (int j = 0; j < kDw2S; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+        // window start: element s0 * ST of padded row r * ST + u (16-byte aligned)
+        const u32x4_t *row = reinterpret_cast<const u32x4_t *>(pl + (r * ST + u) * pw + ((s0 * ST) >> 1));
+        uint32_t wd[4 * NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const u32x4_t v4 = row[q];
+            wd[4 * q] = v4.x; wd[4 * q + 1] = v4.y; wd[4 * q + 2] = v4.z; wd[4 * q + 3] = v4.w;
+        }
+#pragma unroll
+        for (int j = 0; j < kDw2S; ++j)
+#pragma unroll
+            for (int q = 0; q < KP; ++q) {
+                const int e0 = j * ST + 2 * q;
+                const uint32_t pr = (e0 & 1) == 0 ? wd[e0 >> 1]
+                                                  : __builtin_amdgcn_alignbit(wd[(e0 >> 1) + 1], wd[e0 >> 1], 16);
+                acc[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, tp[u][q]),
+                                                         __builtin_bit_cast(bf16x2_t, pr), acc[j], false);
+            }
+    }
+}
+
+// Stores a task's outputs (8-byte stores when Wo % 4 == 0).
+__device__ __forceinline__ void dw2_store(uint16_t *dst, int s0, int Wo, bool st8, const float (&acc)[kDw2S]) {
+    if (st8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (s0 + 4 * h + 4 <= Wo) {
+                u32x2_t o;
+                o.x = pack_bf16x2(acc[4 * h], acc[4 * h + 1]);
+                o.y = pack_bf16x2(acc[4 * h + 2], acc[4 * h + 3]);
+                reinterpret_cast<u32x2_t *>(dst)[h] = o;
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kDw2S; ++j)
+            if (s0 + j < Wo) dst[j] = f32_to_bf16(acc[j]);
+    }
+}
+
+// Plane-per-wave form (any n, or taps already mixed in wmixed): wave w of
+// workgroup g takes plane 4 g + w. Lanes 0..2*K*KP-1 mix the plane's taps.
+template <int K, int ST>
+__global__ __launch_bounds__(64 * kDwPlanes) void depthwise_dot2_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ experts, const float *__restrict__ alpha,
+    const uint16_t *__restrict__ wmixed, uint16_t *__restrict__ y, int B, int C, int H, int W, int pad,
+    int Ho, int Wo, int n, int pitch) {
+    constexpr int KT = K * K;
+    constexpr int KP = dw2_pairs(K);
+    extern __shared__ __attribute__((aligned(16))) uint32_t dwl[];  // kDwPlanes planes
+    __shared__ uint32_t taps_sh[kDwPlanes][K * KP];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long nplanes = (long)B * C;
+    const long bc_raw = (long)blockIdx.x * kDwPlanes + wave;
+    const bool valid = bc_raw < nplanes;
+    const long bc = valid ? bc_raw : nplanes - 1;
+    const int b = (int)(bc / C), c = (int)(bc - (long)b * C);
+    const int Hp = (Ho - 1) * ST + K;  // padded rows read
+    const int pw = pitch >> 1;         // words per padded row (a multiple of 4)
+    uint32_t *pl = dwl + wave * Hp * pw;
+    const uint16_t *xp = x + bc * H * W;
+    const int hw = H * W;
+    const bool q4 = (W & 3) == 0;
+    const int pe = q4 ? 4 : 2;  // elements per piece
+    const int npc = hw / pe;
+    const float invW = 1.f / (float)W;
+
+    u32x2_t pre[kDw2Pre];
+    dw2_fetch(xp, lane, npc, q4, pre);
+    // taps: element (u, v) of the pair table, v < 2 KP; expert values and
+    // attentions load 8 at a time
+    if (lane < K * 2 * KP) {
+        const int u = lane / (2 * KP), v = lane - u * (2 * KP);
+        uint16_t tv = 0;
+        if (v < K) {
+            const int t = u * K + v;
+            if (wmixed) {
+                tv = wmixed[bc * KT + t];
+            } else {
+                float sm = 0.f;
+                for (int i0 = 0; i0 < n; i0 += 8) {
+                    float ev[8], av[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int i = min(i0 + k, n - 1);
+                        ev[k] = bf16_to_f32(experts[((long)i * C + c) * KT + t]);
+                        av[k] = alpha[(long)b * n + i];
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (i0 + k < n) sm = fmaf(av[k], ev[k], sm);
+                }
+                tv = f32_to_bf16(sm);
+            }
+        }
+        reinterpret_cast<uint16_t *>(taps_sh[wave])[lane] = tv;
+    }
+    // zero the padded plane, then write the interior (LDS operations of a
+    // wave complete in order; the empty asm statements keep the compiler
+    // from reordering them)
+    for (int i = lane; i < Hp * pw / 4; i += 64) reinterpret_cast<u32x4_t *>(pl)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < kDw2Pre; ++k)
+        if (lane + 64 * k < npc) dw2_put(pl, lane + 64 * k, pre[k], pe, q4, invW, W, pad, pitch, Hp);
+    for (int p = lane + 64 * kDw2Pre; p < npc; p += 64) {
+        u32x2_t v;
+        if (q4) {
+            v = reinterpret_cast<const u32x2_t *>(xp)[p];
+        } else {
+            v.x = reinterpret_cast<const uint32_t *>(xp)[p];
+            v.y = 0u;
+        }
+        dw2_put(pl, p, v, pe, q4, invW, W, pad, pitch, Hp);
+    }
+    asm volatile("" ::: "memory");
+    uint32_t tp[K][KP];
+#pragma unroll
+    for (int u = 0; u < K; ++u)
+#pragma unroll
+        for (int q = 0; q < KP; ++q) tp[u][q] = taps_sh[wave][u * KP + q];
+
+    const int strips = (Wo + kDw2S - 1) / kDw2S;
+    const float inv_Ho = 1.f / (float)Ho;
+    uint16_t *yp = y + bc * Ho * Wo;
+    const bool st8 = (Wo & 3) == 0;
+    for (int task = lane; task < Ho * strips; task += 64) {
+        // strip-major: neighbouring lanes take neighbouring rows of one strip
+        const int sidx = (int)(((float)task + 0.5f) * inv_Ho);
+        const int r = task - sidx * Ho, s0 = sidx * kDw2S;
+        float acc[kDw2S];
+        dw2_task<K, ST>(pl, pw, tp, r, s0, acc);
+        if (valid) dw2_store(yp + r * Wo + s0, s0, Wo, st8, acc);
+    }
+}
+
+// Channel-major form for n <= 8: workgroup (c, g) takes channel c of
+// examples [16 g, 16 g + 16); wave w takes the examples 16 g + 4 w + k
+// (k < 4) one after the other. The channel's expert values of the lane's tap
+// load once per wave; each example's attentions are 8 unconditional loads of
+// one address per wave; the next example's plane loads before the current
+// one mixes, stages and computes.
+constexpr int kDwChanPB = 4;  // examples (planes) per wave
+template <int K, int ST>
+__global__ __launch_bounds__(64 * kDwPlanes) void depthwise_chan_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ experts, const float *__restrict__ alpha,
+    uint16_t *__restrict__ y, int B, int C, int H, int W, int pad, int Ho, int Wo, int n, int pitch) {
+    constexpr int KT = K * K;
+    constexpr int KP = dw2_pairs(K);
+    extern __shared__ __attribute__((aligned(16))) uint32_t dwl[];
+    __shared__ uint32_t taps_sh[kDwPlanes][K * KP];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int c = blockIdx.x % C;
+    const int b0 = (blockIdx.x / C) * (kDwPlanes * kDwChanPB) + wave * kDwChanPB;
+    const int Hp = (Ho - 1) * ST + K;
+    const int pw = pitch >> 1;
+    uint32_t *pl = dwl + wave * Hp * pw;
+    const int hw = H * W;
+    const bool q4 = (W & 3) == 0;
+    const int pe = q4 ? 4 : 2;
+    const int npc = hw / pe;
+    const float invW = 1.f / (float)W;
+    const int tl = lane < K * 2 * KP ? lane : 0;  // tap-table element of this lane
+    const int tu = tl / (2 * KP), tv = tl - tu * (2 * KP);
+    const bool tap_lane = lane < K * 2 * KP && tv < K;
+    const int tt = tu * K + min(tv, K - 1);
+    float ev[8];  // this channel's expert values of the lane's tap, 0 past n
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ev[i] = i < n ? bf16_to_f32(experts[((long)min(i, n - 1) * C + c) * KT + tt]) : 0.f;
+    for (int i = lane; i < Hp * pw / 4; i += 64) reinterpret_cast<u32x4_t *>(pl)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    const int strips = (Wo + kDw2S - 1) / kDw2S;
+    const float inv_Ho = 1.f / (float)Ho;
+    const bool st8 = (Wo & 3) == 0;
+    u32x2_t cur[kDw2Pre];
+    dw2_fetch(x + ((long)min(b0, B - 1) * C + c) * hw, lane, npc, q4, cur);
+    for (int k = 0; k < kDwChanPB; ++k) {
+        const int b = b0 + k;
+        if (b >= B) break;
+        u32x2_t nxt[kDw2Pre];
+        dw2_fetch(x + ((long)min(b + 1, B - 1) * C + c) * hw, lane, npc, q4, nxt);
+        {
+            float av[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) av[i] = alpha[(long)b * n + min(i, n - 1)];
+            float sm = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm = fmaf(av[i], ev[i], sm);
+            if (lane < K * 2 * KP)
+                reinterpret_cast<uint16_t *>(taps_sh[wave])[lane] = tap_lane ? f32_to_bf16(sm) : (uint16_t)0;
+        }
+        asm volatile("" ::: "memory");
+        const uint16_t *xp = x + ((long)b * C + c) * hw;
+#pragma unroll
+        for (int q = 0; q < kDw2Pre; ++q)
+            if (lane + 64 * q < npc) dw2_put(pl, lane + 64 * q, cur[q], pe, q4, invW, W, pad, pitch, Hp);
+        for (int p = lane + 64 * kDw2Pre; p < npc; p += 64) {
+            u32x2_t v;
+            if (q4) {
+                v = reinterpret_cast<const u32x2_t *>(xp)[p];
+            } else {
+                v.x = reinterpret_cast<const uint32_t *>(xp)[p];
+                v.y = 0u;
+            }
+            dw2_put(pl, p, v, pe, q4, invW, W, pad, pitch, Hp);
+        }
+        asm volatile("" ::: "memory");
+        uint32_t tp[K][KP];
+#pragma unroll
+        for (int u = 0; u < K; ++u)
+#pragma unroll
+            for (int q = 0; q < KP; ++q) tp[u][q] = taps_sh[wave][u * KP + q];
+        uint16_t *yp = y + ((long)b * C + c) * Ho * Wo;
+        for (int task = lane; task < Ho * strips; task += 64) {
+            const int sidx = (int)(((float)task + 0.5f) * inv_Ho);
+            const int r = task - sidx * Ho, s0 = sidx * kDw2S;
+            float acc[kDw2S];
+            dw2_task<K, ST>(pl, pw, tp, r, s0, acc);
+            dw2_store(yp + r * Wo + s0, s0, Wo, st8, acc);
+        }
+        asm volatile("" ::: "memory");  // this plane's last LDS reads before the next plane's writes
+#pragma unroll
+        for (int q = 0; q < kDw2Pre; ++q) cur[q] = nxt[q];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_conv_direct_f32(const Geom &g, const float *x, const float *wmixed, float *y,
@@ -308,9 +603,66 @@ static hipError_t launch_dw_strip(const Geom &g, const T *x, const T *experts, c
     }
 }
 
+static int dw2_pitch(const Geom &g) {
+    const int strips = (g.Wo + kDw2S - 1) / kDw2S;
+    const int words = dw2_words(g.KW, g.stride);
+    const int need = (strips - 1) * kDw2S * g.stride + 8 * ((words + 3) / 4);
+    return (std::max(need, g.W + 2 * g.pad) + 7) / 8 * 8;
+}
+
+// bf16 planes for the dot2 kernels: square 3/5/7 taps, stride 1 or 2, W even
+// (2-element words), planes of at most 4096 elements and rows of at most 256
+// (exact float index splits), padded plane within kDw2PlaneBytes.
+static bool dw2_ok(const Geom &g) {
+    const int Hp = (g.Ho - 1) * g.stride + g.KH;
+    return g.bf16 && g.KH == g.KW && (g.KH == 3 || g.KH == 5 || g.KH == 7) && (g.stride == 1 || g.stride == 2) &&
+           g.W % 2 == 0 && g.H * g.W <= 4096 && g.W <= 256 && g.Ho <= 256 &&
+           g.Ho * ((g.Wo + kDw2S - 1) / kDw2S) < 4096 &&
+           (long)Hp * dw2_pitch(g) * 2 <= kDw2PlaneBytes;
+}
+
+template <typename F>
+static hipError_t dw2_dispatch(const Geom &g, F &&go) {
+    switch (g.KH * 10 + g.stride) {
+    case 31: return go(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    case 32: return go(std::integral_constant<int, 3>{}, std::integral_constant<int, 2>{});
+    case 51: return go(std::integral_constant<int, 5>{}, std::integral_constant<int, 1>{});
+    case 52: return go(std::integral_constant<int, 5>{}, std::integral_constant<int, 2>{});
+    case 71: return go(std::integral_constant<int, 7>{}, std::integral_constant<int, 1>{});
+    default: return go(std::integral_constant<int, 7>{}, std::integral_constant<int, 2>{});
+    }
+}
+
+static hipError_t launch_dw2(const Geom &g, const uint16_t *x, const uint16_t *experts, const float *alpha,
+                             const uint16_t *wmixed, uint16_t *y, hipStream_t stream) {
+    const int pitch = dw2_pitch(g);
+    const size_t lds = (size_t)kDwPlanes * ((g.Ho - 1) * g.stride + g.KH) * pitch * sizeof(uint16_t);
+    if (!wmixed && g.n <= 8) {
+        const int per_wg = kDwPlanes * kDwChanPB;
+        const dim3 grid((unsigned)((long)g.Cin * ((g.B + per_wg - 1) / per_wg)));
+        return dw2_dispatch(g, [&](auto k, auto st) {
+            hipLaunchKernelGGL((depthwise_chan_kernel<decltype(k)::value, decltype(st)::value>), grid,
+                               dim3(64 * kDwPlanes), lds, stream, x, experts, alpha, y, g.B, g.Cin, g.H, g.W,
+                               g.pad, g.Ho, g.Wo, g.n, pitch);
+            return hipGetLastError();
+        });
+    }
+    const long planes = (long)g.B * g.Cin;
+    const dim3 grid((unsigned)((planes + kDwPlanes - 1) / kDwPlanes));
+    return dw2_dispatch(g, [&](auto k, auto st) {
+        hipLaunchKernelGGL((depthwise_dot2_kernel<decltype(k)::value, decltype(st)::value>), grid,
+                           dim3(64 * kDwPlanes), lds, stream, x, experts, alpha, wmixed, y, g.B, g.Cin, g.H,
+                           g.W, g.pad, g.Ho, g.Wo, g.n, pitch);
+        return hipGetLastError();
+    });
+}
+
 hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
                                  const float *alpha, const void *wmixed, void *y,
                                  hipStream_t stream) {
+    if (dw2_ok(g))
+        return launch_dw2(g, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(experts), alpha,
+                          static_cast<const uint16_t *>(wmixed), static_cast<uint16_t *>(y), stream);
     if (dw_strip_ok(g)) {
         if (g.bf16)
             return launch_dw_strip<uint16_t>(g, static_cast<const uint16_t *>(x),

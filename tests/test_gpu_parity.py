@@ -297,7 +297,12 @@ def test_forward_ragged_f32(case):
 
 
 DW = [(3, 16, 9, 11, 5, 1, 2, 4), (2, 24, 28, 28, 3, 2, 1, 3), (4, 8, 7, 7, 7, 1, 3, 9),
-      (1, 5, 1, 1, 3, 1, 1, 2)]
+      (1, 5, 1, 1, 3, 1, 1, 2),
+      # even W (bf16 dot2 kernels): 2-element rows, n > 8, stride 2 with odd pad,
+      # batch not a multiple of 16, a plane past the lanes' prefetched pieces, pad 0
+      (3, 12, 10, 10, 5, 1, 2, 4), (2, 8, 14, 14, 3, 1, 1, 12), (2, 10, 16, 16, 5, 2, 2, 5),
+      (2, 6, 12, 12, 7, 1, 3, 8), (5, 7, 28, 28, 5, 1, 2, 8), (1, 2, 56, 56, 3, 1, 1, 4),
+      (2, 4, 12, 12, 3, 2, 0, 4), (17, 3, 8, 8, 7, 2, 3, 2)]
 
 
 @pytest.mark.parametrize("case", DW)
