@@ -7,6 +7,8 @@
 //   reads its 8 elements of every expert once (16-32 byte loads), widens
 //   them to float once, and writes BT mixed vectors, so the expert bank is
 //   read once per batch tile while the B mixed kernels stream out.
+// mix_mfma_kernel: the stand-alone mix of bf16 banks with more than 8
+//   experts, as a small-K product on the matrix cores (see the kernel).
 // pack_experts_kernel: the expert bank in the layout the MFMA convolution
 //   reads, packed[t][o][cp][ip]: tap-major, channels contiguous and padded
 //   to the 32-wide K chunk, expert pairs sharing one 32-bit word so that a
@@ -247,6 +249,132 @@ __global__ __launch_bounds__(256) void premix_kernel(const float *__restrict__ a
     }
 }
 
+// Stand-alone mix on the matrix cores for bf16 banks with more experts
+// (kMixMaxN < n <= 16 kMixMfmaMaxG): W_b[w] = sum_i alpha[b,i] E_i[w] is the
+// product [examples x experts] . [experts x weights], computed with
+// v_mfma_f32_32x32x16_bf16. A workgroup stages the bank's slice of kMixMW
+// weights (all experts, zeros past n and past wsize) in LDS with 16-byte
+// copies in the natural layout; wave w takes weights [64 w, 64 w + 64) of it
+// as two B fragments per 16 experts, gathered per weight from the LDS rows.
+// The attentions of 32 examples are an A fragment split into three bf16
+// parts (high, middle, low: 24 bits, as a float32 significand), so the three
+// exact products summed in fp32 match a float32 mix before its one bf16
+// rounding. Workgroup (t, c) takes weight tile t and the 32 examples of
+// chunk c; the 32 x kMixMW results go through LDS as bf16 rows and leave as
+// 16-byte stores along each W_b row.
+constexpr int kMixMW = 256;       // weights per workgroup (4 waves x 64)
+constexpr int kMixMfmaMaxG = 4;   // expert groups of 16: n <= 64
+constexpr int kMixOutPitch = kMixMW + 8;  // bf16 per staged output row (rows 4 apart on other banks)
+constexpr int kMixEx = 32;                // examples per workgroup
+
+template <int NKG>
+__global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__ alpha,
+                                                       const uint16_t *__restrict__ experts,
+                                                       uint16_t *__restrict__ mixed, int B, int n, long wsize) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_e[NKG * 16][kMixMW];
+    __shared__ __attribute__((aligned(16))) uint16_t s_o[kMixEx][kMixOutPitch];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const long w0 = (long)blockIdx.x * kMixMW;
+    // stage: clamped unconditional loads first, then masked LDS stores
+    constexpr int kRowVec = kMixMW / 8;            // 16-byte vectors per row
+    constexpr int kIt = NKG * 16 * kRowVec / 256;  // expert vectors per thread
+    u32x4_t q[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int v = tid + 256 * it;
+        const int k = v / kRowVec, c = v - k * kRowVec;
+        const long w = min(w0 + 8 * c, wsize - 8);
+        q[it] = *reinterpret_cast<const u32x4_t *>(experts + (long)min(k, n - 1) * wsize + w);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int v = tid + 256 * it;
+        const int k = v / kRowVec, c = v - k * kRowVec;
+        const bool in = k < n && w0 + 8 * c < wsize;
+        *reinterpret_cast<u32x4_t *>(&s_e[k][8 * c]) = in ? q[it] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    // B fragments: experts 16 g + 8 lh + (0..7), weight 64 wave + 32 nt + l32
+    bf16x8_t ef[2][NKG];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int g = 0; g < NKG; ++g) {
+            const int wl = 64 * wave + 32 * nt + l32;
+            const int k0 = 16 * g + 8 * lh;
+            u32x4_t v;
+            v.x = (uint32_t)s_e[k0 + 0][wl] | ((uint32_t)s_e[k0 + 1][wl] << 16);
+            v.y = (uint32_t)s_e[k0 + 2][wl] | ((uint32_t)s_e[k0 + 3][wl] << 16);
+            v.z = (uint32_t)s_e[k0 + 4][wl] | ((uint32_t)s_e[k0 + 5][wl] << 16);
+            v.w = (uint32_t)s_e[k0 + 6][wl] | ((uint32_t)s_e[k0 + 7][wl] << 16);
+            ef[nt][g] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    {
+        const int bc0 = blockIdx.y * kMixEx;
+        // A fragments: example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
+        bf16x8_t ap[3][1][NKG];
+#pragma unroll
+        for (int mt = 0; mt < 1; ++mt) {
+            const int b = bc0 + 32 * mt + l32;
+            const float *ab = alpha + (long)min(b, B - 1) * n;
+#pragma unroll
+            for (int g = 0; g < NKG; ++g) {
+                uint32_t pw[3][4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    uint16_t p2[3][2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int k = 16 * g + 8 * lh + 2 * jj + e;
+                        const float a = ab[min(k, n - 1)];
+                        float r = (k < n && b < B) ? a : 0.f;
+#pragma unroll
+                        for (int part = 0; part < 3; ++part) {
+                            p2[part][e] = f32_to_bf16(r);
+                            r -= bf16_to_f32(p2[part][e]);  // exact
+                        }
+                    }
+#pragma unroll
+                    for (int part = 0; part < 3; ++part)
+                        pw[part][jj] = (uint32_t)p2[part][0] | ((uint32_t)p2[part][1] << 16);
+                }
+#pragma unroll
+                for (int part = 0; part < 3; ++part)
+                    ap[part][mt][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[part][0], pw[part][1], pw[part][2], pw[part][3]});
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 1; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x16_t acc;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+                for (int g = 0; g < NKG; ++g)
+#pragma unroll
+                    for (int part = 2; part >= 0; --part)  // small parts first
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[part][mt][g], ef[nt][g], acc, 0, 0, 0);
+                // D(lane, 4 j + r) = example 32 mt + 8 j + 4 lh + r, weight 64 wave + 32 nt + l32
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s_o[32 * mt + 8 * (i >> 2) + 4 * lh + (i & 3)][64 * wave + 32 * nt + l32] = f32_to_bf16(acc[i]);
+            }
+        __syncthreads();
+        // rows out: kMixEx examples x kRowVec vectors
+#pragma unroll
+        for (int it = 0; it < kMixEx * kRowVec / 256; ++it) {
+            const int v = tid + 256 * it;
+            const int r = v / kRowVec, c = v - r * kRowVec;
+            const int b = bc0 + r;
+            const long w = w0 + 8 * c;
+            if (b < B && w < wsize)
+                *reinterpret_cast<u32x4_t *>(mixed + (long)b * wsize + w) =
+                    *reinterpret_cast<const u32x4_t *>(&s_o[r][8 * c]);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha, const void *experts,
@@ -269,6 +397,19 @@ hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha, con
             };
             if (g.n <= 4) return go(mix_natural_all_kernel<uint16_t, 4>, mix_natural_all_kernel<float, 4>);
             return go(mix_natural_all_kernel<uint16_t, 8>, mix_natural_all_kernel<float, 8>);
+        }
+        if (g.bf16 && g.n <= 16 * kMixMfmaMaxG) {
+            const dim3 mgrid((unsigned)((wsize + kMixMW - 1) / kMixMW), (unsigned)((g.B + kMixEx - 1) / kMixEx));
+            auto go = [&](auto kern) {
+                hipLaunchKernelGGL(kern, mgrid, dim3(256), 0, stream, alpha,
+                                   static_cast<const uint16_t *>(experts), static_cast<uint16_t *>(mixed), g.B,
+                                   g.n, wsize);
+                return hipGetLastError();
+            };
+            if (g.n <= 16) return go(mix_mfma_kernel<1>);
+            if (g.n <= 32) return go(mix_mfma_kernel<2>);
+            if (g.n <= 48) return go(mix_mfma_kernel<3>);
+            return go(mix_mfma_kernel<4>);
         }
         if (g.bf16)
             hipLaunchKernelGGL(mix_natural_kernel<uint16_t>, grid, dim3(kMixThreads), 0, stream,

@@ -148,12 +148,14 @@ def test_mix_one_hot_is_bitwise(dtype):
         np.testing.assert_array_equal(got[b], e[b % n])
 
 
-@pytest.mark.parametrize("n", [5, 7, 9, 16])
+@pytest.mark.parametrize("n,B", [(5, 11), (7, 11), (9, 11), (12, 11), (16, 11), (17, 11), (33, 11), (48, 11),
+                                 (64, 11), (20, 70), (16, 129)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_mix_vector_expert_counts(n, dtype):
-    """Vector path (kernel size a multiple of 8) for expert counts below and
-    above the single-pass limit, with a batch that is not a multiple of 8."""
-    B = 11
+def test_mix_vector_expert_counts(n, B, dtype):
+    """Vector path (kernel size a multiple of 8, not of the 256-weight matrix
+    tile) for expert counts below and above the single-pass limit and across
+    the matrix-core groups of 16, with batches that are not multiples of 8 or
+    span several 64-example chunks."""
     rng = np.random.default_rng(13 + n)
     e = rng.standard_normal((n, 16, 8, 3, 3), dtype=np.float32)
     if dtype == "bf16":
