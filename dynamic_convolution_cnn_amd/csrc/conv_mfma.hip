@@ -941,6 +941,224 @@ __global__ __launch_bounds__(512) void conv_fused_row16_kernel(const uint16_t *_
     else row16_wave<NP2, 3>(x, packed, alpha, y, a, 4);
 }
 
+// ---- premix 3x3 convolution on 32x32x16 MFMA -------------------------------
+// Stride-1 3x3 layers with W_b in memory (wt[b][t][o][cp]) and images too
+// wide for the row-16 kernel. A workgroup of 4 waves owns example b, 64
+// output channels and kPmMT consecutive output positions (row-major).
+//   - Input tile: the padded input rows the tile's outputs read, 64-byte
+//     positions whose 16-byte channel granules are XOR-swizzled by position
+//     (swz), two buffers: the current chunk of 32 input channels and the next.
+//   - A fragment (32 positions x 16 channels): each lane reads the granule of
+//     its own output position shifted by the tap, tile position q + u * ncols
+//     + v; the next step's fragments are read during the current step.
+//   - B fragments (16 channels x 32 output channels): wave w loads fragment
+//     w of each step (output-channel block w >> 1, K half w & 1) three steps
+//     ahead into a register ring, writes it to a double-buffered LDS stage one
+//     step ahead, and one barrier per step publishes it; every wave then
+//     reads the step's four fragments from the stage.
+//   - Staging of the next chunk as in the row-16 kernel: dword buffer loads
+//     of position pairs (channels past Cin read as zeros), a register
+//     transpose, 8-byte tile writes two steps later; slots in steps 0..6.
+//   - Epilogue through LDS: the accumulators go into the idle tiles as 64
+//     channel rows of kPmMT positions, then out along y's rows with 16-byte
+//     stores.
+constexpr int kPmPB = 2;                 // position blocks of 32 per wave
+constexpr int kPmMT = 4 * kPmPB * 32;    // positions per workgroup
+constexpr int kPmMaxPos = 512;           // tile positions per buffer
+constexpr int kPmSlots = 7;              // staging slots per chunk (steps 0..6)
+constexpr int kPmOutPitch = kPmMT + 8;   // bf16 per staged output row
+__shared__ __attribute__((aligned(16))) u32x4_t s_pm[2 * kPmMaxPos * 4];  // 2 x 32 KB
+__shared__ __attribute__((aligned(16))) u32x4_t s_pmb[2 * 4 * 64];        // 2 x 4 B fragments
+static_assert(64 * kPmOutPitch * 2 <= 2 * kPmMaxPos * 64, "epilogue rows fit in the tiles");
+
+__global__ __launch_bounds__(256) void conv_pm3_kernel(const uint16_t *__restrict__ x,
+                                                       const uint16_t *__restrict__ wt,
+                                                       uint16_t *__restrict__ y, ConvArgs a) {
+    constexpr int KT = 9, CB = 2, RL = 2;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_b = a.n_ptiles * a.n_otiles;
+    const int b = logical / per_b;
+    const int rem = logical - b * per_b;
+    const int pt = rem / a.n_otiles, ot = rem - pt * a.n_otiles;
+    const int p0 = pt * kPmMT, o0 = ot * 64;
+    const int r_first = p0 / a.Wo;
+    const int h_tile0 = r_first - a.pad;  // input row of tile row 0
+    const int h_lo = max(0, h_tile0), h_hi = min(a.H, h_tile0 + a.tile_rows);
+    auto tile_of = [&](int par) { return reinterpret_cast<uint16_t *>(s_pm + par * kPmMaxPos * 4); };
+    zero_lds(tile_of(0), 2 * kPmMaxPos * 32, tid, 256);
+
+    int aq[kPmPB];  // tile position of the lane's output in each block (tap 0)
+#pragma unroll
+    for (int pb = 0; pb < kPmPB; ++pb) {
+        const int p = min(p0 + 32 * (wave * kPmPB + pb) + l32, a.P - 1);
+        const int r = p / a.Wo, s = p - r * a.Wo;
+        aq[pb] = (r - r_first) * a.ncols + s;
+    }
+    const uint16_t *wb = wt + (long)b * KT * a.Cout * a.Cin_pad;
+    long wrow[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wrow[cb] = (long)min(o0 + 32 * cb + l32, a.Cout - 1) * a.Cin_pad + 8 * lh;
+    // this wave's fragment of step 9 c + t (clamped to the last step)
+    const int nsteps = (a.Cin_pad / kChunk) * KT;
+    const long wfrag = wrow[wave >> 1] + 16 * (wave & 1);
+    auto load_b = [&](int st) {
+        st = min(st, nsteps - 1);
+        const int c = st / KT, t = st - c * KT;
+        return *reinterpret_cast<const u32x4_t *>(wb + (long)t * a.Cout * a.Cin_pad + c * kChunk + wfrag);
+    };
+    auto bslot = [&](int buf, int f) { return s_pmb + (buf * 4 + f) * 64 + lane; };
+    auto read_b = [&](int buf, bf16x8_t (&bw)[CB][2]) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) bw[cb][kh] = __builtin_bit_cast(bf16x8_t, *bslot(buf, 2 * cb + kh));
+    };
+    auto read_a = [&](const uint16_t *tile, int t, u32x4_t (&af)[kPmPB][2]) {
+        const int u = t / 3, v = t - 3 * (t / 3);
+#pragma unroll
+        for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+                af[pb][kh] = *reinterpret_cast<const u32x4_t *>(tile + swz(aq[pb] + u * a.ncols + v, 2 * kh + lh));
+    };
+
+    // staging: half-task t = 256 slot + tid is channel quad t & 7 of position
+    // pair t >> 3 of the staged rows [h_lo, h_hi); pairs past the last
+    // repeat it (same bytes to the same place)
+    const uint16_t *xb = x + (long)b * a.x_bstride;
+    const int HW = a.H * a.W, plane = HW * 2, pairs = a.W >> 1;
+    const int npairs = max(1, (h_hi - h_lo) * pairs);
+    const float inv_pairs = 1.f / (float)pairs;
+    auto rsrc_of = [&](int cc) {
+        const int c0 = min(cc, a.Cin - 1);
+        const int nb = max(0, min(kChunk, a.Cin - cc)) * plane - h_lo * a.W * 2;
+        const int nbytes = __builtin_amdgcn_readfirstlane(max(0, nb));
+        const uint64_t p = reinterpret_cast<uint64_t>(xb + (long)c0 * HW + (long)h_lo * a.W);
+        const uint64_t ps = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
+        return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ps), 0, nbytes, 0x00020000);
+    };
+    auto pair_of = [&](int s, int ln) { return min((256 * s + ln) >> 3, npairs - 1); };
+    auto stage_load = [&](__amdgpu_buffer_rsrc_t rs, int s, int ln, uint32_t (&r)[4]) {
+        const int vo = 4 * (ln & 7) * plane + 4 * pair_of(s, ln);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + j * plane, 0, 0);
+    };
+    auto stage_store = [&](uint16_t *t, int s, int ln, const uint32_t (&r)[4]) {
+        const int pg = pair_of(s, ln), quad = ln & 7;
+        const int row = (int)(((float)pg + 0.5f) * inv_pairs);
+        const int q = (h_lo - h_tile0 + row) * a.ncols + 2 * (pg - row * pairs) + a.pad;
+        const int g = quad >> 1, ho = 4 * (quad & 1);
+        const int sel = (quad ^ pg) & 1;
+        const uint32_t bs0 = 0x05040100u + (uint32_t)sel * 0x02020202u;
+        const uint32_t bs1 = 0x07060302u - (uint32_t)sel * 0x02020202u;
+        u32x2_t q0, q1;
+        q0.x = __builtin_amdgcn_perm(r[1], r[0], bs0); q0.y = __builtin_amdgcn_perm(r[3], r[2], bs0);
+        q1.x = __builtin_amdgcn_perm(r[1], r[0], bs1); q1.y = __builtin_amdgcn_perm(r[3], r[2], bs1);
+        *reinterpret_cast<u32x2_t *>(t + swz(q + sel, g) + ho) = q0;
+        *reinterpret_cast<u32x2_t *>(t + swz(q + 1 - sel, g) + ho) = q1;
+    };
+
+    f32x16_t acc[kPmPB][CB];
+#pragma unroll
+    for (int i = 0; i < kPmPB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    const int nchunks = a.Cin_pad / kChunk;
+
+    // chunk 0
+    {
+        const auto rs = rsrc_of(0);
+        uint32_t r0[kPmSlots][4];
+#pragma unroll
+        for (int s = 0; s < kPmSlots; ++s) stage_load(rs, s, tid, r0[s]);
+        lds_barrier();  // tiles zeroed
+#pragma unroll
+        for (int s = 0; s < kPmSlots; ++s) stage_store(tile_of(0), s, tid, r0[s]);
+    }
+    // B ring: slot k holds this wave's fragment of a step s with s % 3 == k
+    u32x4_t wring[3];
+    wring[0] = load_b(0);
+    wring[1] = load_b(1);
+    wring[2] = load_b(2);
+    *bslot(0, wave) = wring[0];
+    wring[0] = load_b(3);
+    lds_barrier();  // chunk 0 in tile 0, B_0 staged
+    bf16x8_t bw[CB][2];
+    read_b(0, bw);
+    u32x4_t af[kPmPB][2];
+    read_a(tile_of(0), 0, af);
+
+    for (int c = 0; c < nchunks; ++c) {
+        const uint16_t *tile = tile_of(c & 1);
+        uint16_t *tnext = tile_of((c + 1) & 1);  // chunk c - 1's, whose last reads preceded the last barrier
+        const auto rs = rsrc_of(min(c + 1, nchunks - 1) * kChunk);
+        int ln = tid;
+        asm volatile("" : "+v"(ln));
+        uint32_t rb[RL][4];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            // step s = 9 c + t; the ring slot of step s + 1 is (t + 1) % 3
+            const int nbuf = (c + t + 1) & 1;  // stage buffer of B_{s+1}
+            u32x4_t an[kPmPB][2];
+            if (t + 1 < KT) read_a(tile, t + 1, an);
+#pragma unroll
+            for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, af[pb][kh]);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bw[cb][kh], acc[pb][cb], 0, 0, 0);
+                }
+            // B_{s+1} to the stage (buffer nbuf held B_{s-1}, read before the
+            // previous barrier), then B_{s+4} into the freed ring slot
+            *bslot(nbuf, wave) = wring[(t + 1) % 3];
+            wring[(t + 1) % 3] = load_b(9 * c + t + 4);
+            if (t >= RL && t - RL < kPmSlots) stage_store(tnext, t - RL, ln, rb[t % RL]);
+            if (t < kPmSlots) stage_load(rs, t, ln, rb[t % RL]);
+            lds_barrier();  // B_{s+1} published; at the chunk's end also the next tile
+            if (t + 1 == KT) read_a(tnext, 0, an);
+            read_b(nbuf, bw);
+#pragma unroll
+            for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) af[pb][kh] = an[pb][kh];
+        }
+    }
+    // epilogue: D(lane, 4 j + q) = channel o0 + 32 cb + l32, position
+    // 32 (wave kPmPB + pb) + 8 j + 4 lh + q of the tile
+    lds_barrier();  // last A reads of every wave done
+    uint16_t *s_out = tile_of(0);
+#pragma unroll
+    for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u32x2_t o;
+                o.x = pack_bf16x2(acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1]);
+                o.y = pack_bf16x2(acc[pb][cb][4 * j + 2], acc[pb][cb][4 * j + 3]);
+                const int pos = 32 * (wave * kPmPB + pb) + 8 * j + 4 * lh;
+                *reinterpret_cast<u32x2_t *>(s_out + (32 * cb + l32) * kPmOutPitch + pos) = o;
+            }
+    lds_barrier();
+    const int npos = min(kPmMT, a.P - p0);
+    constexpr int kRowVec = kPmMT / 8;
+    for (int v = tid; v < 64 * kRowVec; v += 256) {
+        const int ch = v / kRowVec, cv = v - ch * kRowVec;
+        const int o = o0 + ch;
+        if (o < a.Cout && 8 * cv < npos)
+            *reinterpret_cast<u32x4_t *>(y + ((long)b * a.Cout + o) * a.P + p0 + 8 * cv) =
+                *reinterpret_cast<const u32x4_t *>(s_out + ch * kPmOutPitch + 8 * cv);
+    }
+}
+
 ConvArgs base_args(const Geom &g) {
     ConvArgs a{};
     a.B = g.B; a.Cin = g.Cin; a.H = g.H; a.W = g.W; a.Cout = g.Cout;
@@ -1051,8 +1269,27 @@ bool premix_conv_supported(const Geom &g) {
            premix_lds_bytes(g, pick_premix(g)) <= (size_t)kLdsBudget;
 }
 
+// The 32x32x16 premix kernel: bf16 3x3 stride-1 layers with W even (position
+// pairs), P % 8 == 0 (16-byte output rows), a tile of at most kPmMaxPos
+// padded positions and at most kPmSlots x 256 staging half-tasks per chunk.
+static bool pm3_ok(const Geom &g) {
+    if (!(g.bf16 && g.groups == 1 && g.KH == 3 && g.KW == 3 && g.stride == 1 && g.W % 2 == 0 && g.P % 8 == 0))
+        return false;
+    const int tr = tile_rows_for(g, kPmMT);
+    return tr * (g.W + 2 * g.pad) <= kPmMaxPos && tr * (g.W / 2) * 8 <= kPmSlots * 256;
+}
+
 hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
                               hipStream_t stream) {
+    if (pm3_ok(g)) {
+        ConvArgs a = base_args(g);
+        a.tile_rows = tile_rows_for(g, kPmMT);
+        a.n_ptiles = ceil_div(g.P, kPmMT);
+        a.n_otiles = ceil_div(g.Cout, 64);
+        const long blocks = (long)g.B * a.n_ptiles * a.n_otiles;
+        hipLaunchKernelGGL(conv_pm3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+        return hipGetLastError();
+    }
     const PremixCfg c = pick_premix(g);
     if (c.FM == kPremixLarge.FM)
         return launch_premix_cfg<kPremixLarge.FM, kPremixLarge.FN, kPremixLarge.NW>(g, x, wt, y, stream);
