@@ -14,7 +14,9 @@
 //   to the 32-wide K chunk, expert pairs sharing one 32-bit word so that a
 //   bf16 dot2 instruction mixes two experts at once.
 // premix_kernel: mixed kernels in the convolution's layout wt[b][t][o][cp],
-//   computed from the packed bank with bf16 dot2 instructions.
+//   computed from the packed bank with bf16 dot2 instructions;
+//   premix_mfma_kernel the same on the matrix cores when the padded expert
+//   count is a multiple of 8.
 //
 // Precision: natural mixing sums in float32 in expert order and rounds
 // once. The dot2 mixes split each float32 attention into a bf16 high part
@@ -375,6 +377,92 @@ __global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__
     }
 }
 
+// Premix on the matrix cores for banks whose padded expert count is a
+// multiple of 8: as mix_mfma_kernel, but the experts of each weight come
+// straight from the packed bank (8 consecutive experts = 16 bytes of a
+// weight's record, no LDS transpose) and the mixed kernels are written in
+// the convolution's layout wt[b][t][o][cp], which has the packed bank's
+// weight order.
+template <int NKG>
+__global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restrict__ alpha,
+                                                          const uint16_t *__restrict__ packed,
+                                                          uint16_t *__restrict__ wt, int B, int n, int n_pad,
+                                                          long wsize) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_o[kMixEx][kMixOutPitch];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const long w0 = (long)blockIdx.x * kMixMW;
+    const int bc0 = blockIdx.y * kMixEx;
+    // B fragments: experts 16 g + 8 lh + (0..7) of weight w0 + 64 wave + 32 nt + l32
+    bf16x8_t ef[2][NKG];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const long w = min(w0 + 64 * wave + 32 * nt + l32, wsize - 1);
+#pragma unroll
+        for (int g = 0; g < NKG; ++g) {
+            const int k0 = 16 * g + 8 * lh;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(packed + w * n_pad + min(k0, n_pad - 8));
+            ef[nt][g] = __builtin_bit_cast(bf16x8_t, k0 < n_pad ? v : u32x4_t{0u, 0u, 0u, 0u});
+        }
+    }
+    // A fragments: example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
+    bf16x8_t ap[3][NKG];
+    {
+        const int b = bc0 + l32;
+        const float *ab = alpha + (long)min(b, B - 1) * n;
+#pragma unroll
+        for (int g = 0; g < NKG; ++g) {
+            uint32_t pw[3][4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                uint16_t p2[3][2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k = 16 * g + 8 * lh + 2 * jj + e;
+                    const float a = ab[min(k, n - 1)];
+                    float r = (k < n && b < B) ? a : 0.f;
+#pragma unroll
+                    for (int part = 0; part < 3; ++part) {
+                        p2[part][e] = f32_to_bf16(r);
+                        r -= bf16_to_f32(p2[part][e]);  // exact
+                    }
+                }
+#pragma unroll
+                for (int part = 0; part < 3; ++part)
+                    pw[part][jj] = (uint32_t)p2[part][0] | ((uint32_t)p2[part][1] << 16);
+            }
+#pragma unroll
+            for (int part = 0; part < 3; ++part)
+                ap[part][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[part][0], pw[part][1], pw[part][2], pw[part][3]});
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        f32x16_t acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int g = 0; g < NKG; ++g)
+#pragma unroll
+            for (int part = 2; part >= 0; --part)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[part][g], ef[nt][g], acc, 0, 0, 0);
+        // D(lane, 4 j + r) = example 8 j + 4 lh + r, weight 64 wave + 32 nt + l32
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            s_o[8 * (i >> 2) + 4 * lh + (i & 3)][64 * wave + 32 * nt + l32] = f32_to_bf16(acc[i]);
+    }
+    __syncthreads();
+    constexpr int kRowVec = kMixMW / 8;
+#pragma unroll
+    for (int it = 0; it < kMixEx * kRowVec / 256; ++it) {
+        const int v = tid + 256 * it;
+        const int r = v / kRowVec, c = v - r * kRowVec;
+        const int b = bc0 + r;
+        const long w = w0 + 8 * c;
+        if (b < B && w < wsize)
+            *reinterpret_cast<u32x4_t *>(wt + (long)b * wsize + w) = *reinterpret_cast<const u32x4_t *>(&s_o[r][8 * c]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha, const void *experts,
@@ -455,6 +543,20 @@ size_t premixed_bytes(const Geom &g) {
 hipError_t launch_premix(const Geom &g, const float *alpha, const uint16_t *packed,
                          uint16_t *wt, hipStream_t stream) {
     const long nvec = (long)g.KT * g.Cout * g.Cin_pad / 8;
+    // matrix-core premix when the padded expert records are 16-byte multiples
+    if (g.n_pad % 8 == 0 && g.n_pad <= 16 * kMixMfmaMaxG) {
+        const long wsize = nvec * 8;
+        const dim3 mgrid((unsigned)((wsize + kMixMW - 1) / kMixMW), (unsigned)((g.B + kMixEx - 1) / kMixEx));
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, mgrid, dim3(256), 0, stream, alpha, packed, wt, g.B, g.n, g.n_pad, wsize);
+            return hipGetLastError();
+        };
+        const int nkg = (g.n_pad + 15) / 16;
+        if (nkg == 1) return go(premix_mfma_kernel<1>);
+        if (nkg == 2) return go(premix_mfma_kernel<2>);
+        if (nkg == 3) return go(premix_mfma_kernel<3>);
+        return go(premix_mfma_kernel<4>);
+    }
     dim3 grid((unsigned)((nvec + 255) / 256), (unsigned)((g.B + kPremixBT - 1) / kPremixBT));
     const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
     switch (g.n_pad / 2) {
