@@ -1159,6 +1159,147 @@ __global__ __launch_bounds__(256) void conv_pm3_kernel(const uint16_t *__restric
     }
 }
 
+// ---- premix 1x1 convolution on 32x32x16 MFMA -------------------------------
+// Stride-1 1x1 layers without padding (the MBConv expand and project
+// layers, HBM-bound): a workgroup of 4 waves owns example b, 64 output
+// channels and kPmMT consecutive positions. Per chunk of 32 input channels,
+// the x slice (half-tasks of 2 positions x 4 channels: dword buffer loads,
+// register transpose, 8-byte writes into a swizzled [position][channel]
+// tile) and the W_b slice (one 16-byte fragment piece per thread) of the
+// next chunk load at the start of the chunk and go to the other LDS buffer at
+// its end; one barrier per chunk. Outputs leave through LDS as 16-byte row
+// stores.
+constexpr int kPm1Tile = kPmMT * 32;  // bf16 per x tile buffer (256 positions x 32 channels)
+constexpr int kPm1LdsBytes = 64 * kPmOutPitch * 2 > 2 * kPm1Tile * 2 ? 64 * kPmOutPitch * 2 : 2 * kPm1Tile * 2;
+__shared__ __attribute__((aligned(16))) u32x4_t s_pm1x[kPm1LdsBytes / 16];  // 2 x 16 KB tiles, or the epilogue rows
+__shared__ __attribute__((aligned(16))) u32x4_t s_pm1w[2 * 4 * 64];        // 2 x 4 fragments
+
+__global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restrict__ x,
+                                                       const uint16_t *__restrict__ wt,
+                                                       uint16_t *__restrict__ y, ConvArgs a) {
+    constexpr int CB = 2;
+    constexpr int kHalf = kPmMT / 2 * 8 / 256;  // half-tasks per thread per chunk (4)
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_b = a.n_ptiles * a.n_otiles;
+    const int b = logical / per_b;
+    const int rem = logical - b * per_b;
+    const int pt = rem / a.n_otiles, ot = rem - pt * a.n_otiles;
+    const int p0 = pt * kPmMT, o0 = ot * 64;
+    auto xtile = [&](int par) { return reinterpret_cast<uint16_t *>(s_pm1x + par * (kPm1Tile / 8)); };
+    auto wslot = [&](int par, int f) { return s_pm1w + (par * 4 + f) * 64; };
+    const int nchunks = a.Cin_pad / kChunk;
+    const uint16_t *xb = x + (long)b * a.x_bstride;
+    const int plane = a.P * 2;  // bytes per channel plane (H W = P)
+    // x: half-task t = 256 k + tid is channel quad t & 7 of position pair t >> 3
+    auto rsrc_of = [&](int cc) {
+        const int c0 = min(cc, a.Cin - 1);
+        const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(kChunk, a.Cin - cc)) * plane - p0 * 2);
+        const uint64_t p = reinterpret_cast<uint64_t>(xb + (long)c0 * a.P + p0);
+        const uint64_t ps = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
+        return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ps), 0, max(0, nbytes), 0x00020000);
+    };
+    // W: thread tid holds lane tid & 63 of fragment f = tid >> 6 (block f >> 1, K half f & 1)
+    const uint16_t *wb = wt + (long)b * a.Cout * a.Cin_pad;
+    const long wrow = (long)min(o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh;
+    struct Stage {
+        uint32_t r[kHalf][4];
+        u32x4_t w;
+    };
+    auto load = [&](int c, Stage &st) {
+        const auto rs = rsrc_of(c * kChunk);
+#pragma unroll
+        for (int k = 0; k < kHalf; ++k) {
+            const int t = 256 * k + tid;
+            const int vo = 4 * (t & 7) * plane + 4 * (t >> 3);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st.r[k][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + j * plane, 0, 0);
+        }
+        st.w = *reinterpret_cast<const u32x4_t *>(wb + wrow + c * kChunk);
+    };
+    auto store = [&](int par, const Stage &st) {
+        uint16_t *t16 = xtile(par);
+#pragma unroll
+        for (int k = 0; k < kHalf; ++k) {
+            const int t = 256 * k + tid;
+            const int quad = t & 7, pg = t >> 3;
+            const int q = 2 * pg, g = quad >> 1, ho = 4 * (quad & 1);
+            const int sel = (quad ^ pg) & 1;
+            const uint32_t bs0 = 0x05040100u + (uint32_t)sel * 0x02020202u;
+            const uint32_t bs1 = 0x07060302u - (uint32_t)sel * 0x02020202u;
+            u32x2_t q0, q1;
+            q0.x = __builtin_amdgcn_perm(st.r[k][1], st.r[k][0], bs0); q0.y = __builtin_amdgcn_perm(st.r[k][3], st.r[k][2], bs0);
+            q1.x = __builtin_amdgcn_perm(st.r[k][1], st.r[k][0], bs1); q1.y = __builtin_amdgcn_perm(st.r[k][3], st.r[k][2], bs1);
+            *reinterpret_cast<u32x2_t *>(t16 + swz(q + sel, g) + ho) = q0;
+            *reinterpret_cast<u32x2_t *>(t16 + swz(q + 1 - sel, g) + ho) = q1;
+        }
+        wslot(par, wave)[lane] = st.w;
+    };
+    f32x16_t acc[kPmPB][CB];
+#pragma unroll
+    for (int i = 0; i < kPmPB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    Stage st;
+    load(0, st);
+    store(0, st);
+    lds_barrier();
+    for (int c = 0; c < nchunks; ++c) {
+        const int par = c & 1;
+        if (c + 1 < nchunks) load(c + 1, st);
+        const uint16_t *t16 = xtile(par);
+        bf16x8_t bw[CB][2];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) bw[cb][kh] = __builtin_bit_cast(bf16x8_t, wslot(par, 2 * cb + kh)[lane]);
+#pragma unroll
+        for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const int q = 32 * (wave * kPmPB + pb) + l32;
+                const bf16x8_t afr =
+                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(t16 + swz(q, 2 * kh + lh)));
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bw[cb][kh], acc[pb][cb], 0, 0, 0);
+            }
+        // the other buffer was last read in chunk c - 1, before the previous barrier
+        if (c + 1 < nchunks) store(par ^ 1, st);
+        lds_barrier();
+    }
+    // epilogue (as the 3x3 kernel): D(lane, 4 j + q) = channel o0 + 32 cb + l32,
+    // position 32 (wave kPmPB + pb) + 8 j + 4 lh + q
+    uint16_t *s_out = reinterpret_cast<uint16_t *>(s_pm1x);
+#pragma unroll
+    for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u32x2_t o;
+                o.x = pack_bf16x2(acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1]);
+                o.y = pack_bf16x2(acc[pb][cb][4 * j + 2], acc[pb][cb][4 * j + 3]);
+                const int pos = 32 * (wave * kPmPB + pb) + 8 * j + 4 * lh;
+                *reinterpret_cast<u32x2_t *>(s_out + (32 * cb + l32) * kPmOutPitch + pos) = o;
+            }
+    lds_barrier();
+    const int npos = min(kPmMT, a.P - p0);
+    constexpr int kRowVec = kPmMT / 8;
+    for (int v = tid; v < 64 * kRowVec; v += 256) {
+        const int ch = v / kRowVec, cv = v - ch * kRowVec;
+        const int o = o0 + ch;
+        if (o < a.Cout && 8 * cv < npos)
+            *reinterpret_cast<u32x4_t *>(y + ((long)b * a.Cout + o) * a.P + p0 + 8 * cv) =
+                *reinterpret_cast<const u32x4_t *>(s_out + ch * kPmOutPitch + 8 * cv);
+    }
+}
+
 ConvArgs base_args(const Geom &g) {
     ConvArgs a{};
     a.B = g.B; a.Cin = g.Cin; a.H = g.H; a.W = g.W; a.Cout = g.Cout;
@@ -1279,8 +1420,22 @@ static bool pm3_ok(const Geom &g) {
     return tr * (g.W + 2 * g.pad) <= kPmMaxPos && tr * (g.W / 2) * 8 <= kPmSlots * 256;
 }
 
+// The 1x1 premix kernel: bf16 1x1 stride-1 layers without padding, P even
+// and P % 8 == 0 (position pairs, 16-byte output rows).
+static bool pm1_ok(const Geom &g) {
+    return g.bf16 && g.groups == 1 && g.KH == 1 && g.KW == 1 && g.stride == 1 && g.pad == 0 && g.P % 8 == 0;
+}
+
 hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
                               hipStream_t stream) {
+    if (pm1_ok(g)) {
+        ConvArgs a = base_args(g);
+        a.n_ptiles = ceil_div(g.P, kPmMT);
+        a.n_otiles = ceil_div(g.Cout, 64);
+        const long blocks = (long)g.B * a.n_ptiles * a.n_otiles;
+        hipLaunchKernelGGL(conv_pm1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+        return hipGetLastError();
+    }
     if (pm3_ok(g)) {
         ConvArgs a = base_args(g);
         a.tile_rows = tile_rows_for(g, kPmMT);

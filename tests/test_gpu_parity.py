@@ -258,6 +258,8 @@ RAGGED = [
     (3, 48, 40, 13, 14, (3, 3), 1, 1, 3),    # 16-wide padded rows, odd Ho, tails
     (2, 256, 24, 6, 6, (3, 3), 1, 1, 16),    # expert slab too big for the LDS packing path
     (7, 64, 64, 6, 6, (3, 3), 1, 1, 4),      # small image: fewer rows than blocks
+    (3, 40, 72, 24, 20, (1, 1), 1, 0, 8),    # 1x1: two chunks (tail), two channel tiles, partial position tile
+    (2, 48, 64, 30, 56, (3, 3), 1, 1, 2),    # wide rows: several 256-position tiles spanning rows
 ]
 
 
