@@ -42,8 +42,8 @@ ROTATE_BYTES = 640 << 20        # rotating input/output sets larger than L2 + MA
 # 131085 KiB for 262144 KiB moved (x 2.000), WRITE_SIZE 262144 KiB (x 1.000). Valid only
 # for the kernel source it was taken on (sha256 prefix of the file below); otherwise null.
 TRAFFIC = {
-    "resnet50_3x3": {"source_sha": "e1bd152eeef32d7d",
-                     "fetch_kib": 55812.3, "write_kib": 26624.0,
+    "resnet50_3x3": {"source_sha": "a4aaeb034773ecf9",
+                     "fetch_kib": 55048.4, "write_kib": 25088.0,
                      "fetch_scale": 262144 / 131085, "write_scale": 1.0},
 }
 KERNEL_SOURCE = os.path.join(ROOT, "dynamic_convolution_cnn_amd", "csrc", "conv_mfma.hip")
