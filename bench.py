@@ -4,9 +4,10 @@
 One step = the whole path over one batch of synthetic input already resident
 in HBM: routing (GAP -> FC -> sigmoid/softmax), packing of the expert bank,
 and the per-example convolution with mixed kernels (fused into the MFMA
-convolution for the ResNet-50-shaped layer). Each step is one replay of a HIP
-graph that holds all of its launches; per-kernel times come from HIP events
-around eager launches of the same kernels. Default workload: the
+convolution for the ResNet-50-shaped layer). The timed steps run as replays of
+HIP graphs that hold 10 whole steps each, so that one launch gap falls on ten
+steps; per-kernel times come from HIP events around eager launches of the
+same kernels. Default workload: the
 ResNet-50-shaped 3x3 layer, B=256, 256->256 channels, 14x14, n=4 experts,
 bf16 storage with float32 accumulation.
 
@@ -35,6 +36,7 @@ METRIC = "dynamic-conv images/s + TFLOP/s (% bf16 MFMA peak), ResNet-50 3x3 laye
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 ROTATE_BYTES = 640 << 20        # rotating input/output sets larger than L2 + MALL
+GRAPH_STEPS = 10                # steps per HIP graph replay in the timed loop
 
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE on the headline workload (KiB per dispatch), each scaled by what the same
@@ -159,50 +161,63 @@ def main():
 
     def step(i, ev=None):
         s = i % R
+        cur = torch.cuda.current_stream()  # the capture stream inside a graph
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].record(cur)
         bd.dynconv_route(xs[s], fc_w, fc_b, w.route_mode, w.temperature, alpha=alphas[s],
                          workspace=route_ws)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record(cur)
         h = xs[s]
         for li, desc in enumerate(descs):
             if packed[li] is not None:
                 bd.dynconv_pack_experts(desc, experts[li], packed[li])
                 if ev is not None and li == 0:
-                    ev[2].record(stream)
+                    ev[2].record(cur)
                 bd.dynconv_forward_packed(desc, h, packed[li], alphas[s], policy=pols[li],
                                           y=outs[li][s], workspace=ws[li])
             else:
                 if ev is not None and li == 0:
-                    ev[2].record(stream)
+                    ev[2].record(cur)
                 bd.dynconv_forward(h, experts[li], alphas[s], w.layers[li].stride,
                                    w.layers[li].pad, w.layers[li].groups, policy=pols[li],
                                    y=outs[li][s], workspace=ws[li])
             if ev is not None and li == 0:
-                ev[3].record(stream)
+                ev[3].record(cur)
             h = outs[li][s]
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # One HIP graph per rotating set holds a whole step (route, pack, forward of
-    # every layer), so the timed loop measures the GPU, not Python launch cost.
-    graphs = []
-    for s in range(R):
+    # HIP graphs hold whole steps (route, pack, forward of every layer), so the
+    # timed loop measures the GPU, not Python launch cost: graph g holds the G
+    # steps over rotating sets g, g + 1, ..., g + G - 1 (mod R), and a few
+    # one-step graphs make up the remainder, so that exactly K steps run.
+    G = GRAPH_STEPS
+
+    def capture(first, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(s)
-        graphs.append(g)
-    for i in range(max(args.warmup, 2)):
-        graphs[i % R].replay()
+            for j in range(count):
+                step(first + j)
+        return g
+
+    multi = [capture(s, G) for s in range(R)]
+    single = [capture(s, 1) for s in range(R)]
+    plan, i = [], 0
+    while i + G <= args.steps:
+        plan.append(multi[i % R]); i += G
+    while i < args.steps:
+        plan.append(single[i % R]); i += 1
+    for g in multi[:2] + single[:2]:
+        g.replay()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps (graph replays)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % R].replay()
+    for g in plan:
+        g.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
