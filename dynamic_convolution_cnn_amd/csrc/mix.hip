@@ -168,30 +168,52 @@ __global__ __launch_bounds__(kMixThreads) void mix_scalar_kernel(
     }
 }
 
-// One 32-bit output word (an expert pair) per thread.
-// experts[i][o][c][t] (c < cpg = Cin for groups == 1) -> packed[t][o][cp][ip]
+// One (tap, output channel, input channel) triple per thread: it loads the
+// n experts' values of that weight together and writes its NP2 expert-pair
+// words as one vector store, next to those of the neighbouring threads
+// (neighbouring input channels). NP2 = 0: any pair count, one word at a time.
+// experts[i][o][c][t] (c < Cin, groups == 1) -> packed[t][o][cp][ip]
+template <int NP2>
 __global__ __launch_bounds__(256) void pack_experts_kernel(const uint16_t *__restrict__ e,
                                                            uint32_t *__restrict__ packed,
                                                            int n, int Cout, int Cin, int KT,
                                                            int Cin_pad, int np2) {
-    const long total = (long)KT * Cout * Cin_pad * np2;
-    const long d = (long)blockIdx.x * 256 + threadIdx.x;
-    if (d >= total) return;
-    const int p = (int)(d % np2);
-    long r = d / np2;
-    const int c = (int)(r % Cin_pad);
-    r /= Cin_pad;
-    const int o = (int)(r % Cout);
-    const int t = (int)(r / Cout);
-    uint32_t lo = 0, hi = 0;
-    if (c < Cin) {
-        const long wsize = (long)Cout * Cin * KT;
-        const long off = ((long)o * Cin + c) * KT + t;
-        const int i0 = 2 * p, i1 = 2 * p + 1;
-        if (i0 < n) lo = e[(long)i0 * wsize + off];
-        if (i1 < n) hi = e[(long)i1 * wsize + off];
+    const long d = (long)blockIdx.x * 256 + threadIdx.x;  // (t Cout + o) Cin_pad + cp
+    if (d >= (long)KT * Cout * Cin_pad) return;
+    const int c = (int)(d % Cin_pad);
+    const long r = d / Cin_pad;
+    const int o = (int)(r % Cout), t = (int)(r / Cout);
+    const bool cv = c < Cin;
+    const long wsize = (long)Cout * Cin * KT;
+    const uint16_t *src = e + ((long)o * Cin + min(c, Cin - 1)) * KT + t;
+    if constexpr (NP2 > 0) {
+        uint32_t v[2 * NP2];
+#pragma unroll
+        for (int i = 0; i < 2 * NP2; ++i) v[i] = cv && i < n ? src[(long)i * wsize] : 0u;
+        uint32_t w[NP2];
+#pragma unroll
+        for (int p = 0; p < NP2; ++p) w[p] = v[2 * p] | (v[2 * p + 1] << 16);
+        uint32_t *dst = packed + d * NP2;
+        if constexpr (NP2 % 4 == 0) {
+#pragma unroll
+            for (int p = 0; p < NP2; p += 4)
+                *reinterpret_cast<u32x4_t *>(dst + p) = u32x4_t{w[p], w[p + 1], w[p + 2], w[p + 3]};
+        } else if constexpr (NP2 % 2 == 0) {
+#pragma unroll
+            for (int p = 0; p < NP2; p += 2) *reinterpret_cast<u32x2_t *>(dst + p) = u32x2_t{w[p], w[p + 1]};
+        } else {
+#pragma unroll
+            for (int p = 0; p < NP2; ++p) dst[p] = w[p];
+        }
+    } else {
+        uint32_t *dst = packed + d * np2;
+        for (int p = 0; p < np2; ++p) {
+            const int i0 = 2 * p, i1 = 2 * p + 1;
+            const uint32_t lo = cv && i0 < n ? src[(long)i0 * wsize] : 0u;
+            const uint32_t hi = cv && i1 < n ? src[(long)i1 * wsize] : 0u;
+            dst[p] = lo | (hi << 16);
+        }
     }
-    packed[d] = lo | (hi << 16);
 }
 
 __device__ __forceinline__ void split_alpha(float a0, float a1, uint32_t &hi, uint32_t &lo) {
@@ -529,10 +551,24 @@ size_t packed_experts_bytes(const Geom &g) {
 hipError_t launch_pack_experts(const Geom &g, const uint16_t *experts, uint16_t *packed,
                                hipStream_t stream) {
     const int np2 = g.n_pad / 2;
-    const long total = (long)g.KT * g.Cout * g.Cin_pad * np2;
-    hipLaunchKernelGGL(pack_experts_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, experts, reinterpret_cast<uint32_t *>(packed), g.n, g.Cout,
-                       g.Cin, g.KT, g.Cin_pad, np2);
+    const long total = (long)g.KT * g.Cout * g.Cin_pad;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    uint32_t *dst = reinterpret_cast<uint32_t *>(packed);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, experts, dst, g.n, g.Cout, g.Cin, g.KT,
+                           g.Cin_pad, np2);
+    };
+    switch (np2) {
+    case 1: go(pack_experts_kernel<1>); break;
+    case 2: go(pack_experts_kernel<2>); break;
+    case 3: go(pack_experts_kernel<3>); break;
+    case 4: go(pack_experts_kernel<4>); break;
+    case 5: go(pack_experts_kernel<5>); break;
+    case 6: go(pack_experts_kernel<6>); break;
+    case 7: go(pack_experts_kernel<7>); break;
+    case 8: go(pack_experts_kernel<8>); break;
+    default: go(pack_experts_kernel<0>); break;
+    }
     return hipGetLastError();
 }
 
