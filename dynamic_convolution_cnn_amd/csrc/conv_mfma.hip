@@ -1163,22 +1163,31 @@ __global__ __launch_bounds__(256) void conv_pm3_kernel(const uint16_t *__restric
 // Stride-1 1x1 layers without padding (the MBConv expand and project
 // layers, HBM-bound): a workgroup of 4 waves owns example b, 64 output
 // channels and kPmMT consecutive positions. Per chunk of 32 input channels,
-// the x slice (half-tasks of 2 positions x 4 channels: dword buffer loads,
-// register transpose, 8-byte writes into a swizzled [position][channel]
-// tile) and the W_b slice (one 16-byte fragment piece per thread) of the
-// next chunk load at the start of the chunk and go to the other LDS buffer at
-// its end; one barrier per chunk. Outputs leave through LDS as 16-byte row
-// stores.
-constexpr int kPm1Tile = kPmMT * 32;  // bf16 per x tile buffer (256 positions x 32 channels)
+// the x slice is read with 16-byte loads along the positions (32 lanes
+// cover 512 contiguous bytes of one channel plane) into a [channel][position]
+// LDS tile, and the transpose to MFMA A fragments (8 channels of one
+// position per lane) happens in the 2-byte LDS reads. The W_b slice is one
+// 16-byte fragment piece per thread. Both load at the start of the previous
+// chunk and go to the other LDS buffer at its end; one barrier per chunk.
+// Outputs leave through LDS as 16-byte row stores.
+constexpr int kPm1Tile = kPmMT * 32;  // bf16 per x tile buffer (32 channels x 256 positions)
 constexpr int kPm1LdsBytes = 64 * kPmOutPitch * 2 > 2 * kPm1Tile * 2 ? 64 * kPmOutPitch * 2 : 2 * kPm1Tile * 2;
 __shared__ __attribute__((aligned(16))) u32x4_t s_pm1x[kPm1LdsBytes / 16];  // 2 x 16 KB tiles, or the epilogue rows
 __shared__ __attribute__((aligned(16))) u32x4_t s_pm1w[2 * 4 * 64];        // 2 x 4 fragments
+
+// byte offset of position q of channel row c in a [32][256] tile: the
+// 16-byte pieces of rows 8..15 and 24..31 are XOR-swapped by 4 pieces, so
+// that the two half-waves of a fragment read (rows 8 apart) use different
+// banks
+__device__ __forceinline__ int pm1_off(int c, int q) {
+    return c * (kPmMT * 2) + ((((q >> 3) ^ (((c >> 3) & 1) << 2))) << 4) + ((q & 7) << 1);
+}
 
 __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restrict__ x,
                                                        const uint16_t *__restrict__ wt,
                                                        uint16_t *__restrict__ y, ConvArgs a) {
     constexpr int CB = 2;
-    constexpr int kHalf = kPmMT / 2 * 8 / 256;  // half-tasks per thread per chunk (4)
+    constexpr int kLoads = 32 * kPmMT * 2 / 16 / 256;  // 16-byte x loads per thread per chunk (4)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
@@ -1188,12 +1197,13 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
     const int rem = logical - b * per_b;
     const int pt = rem / a.n_otiles, ot = rem - pt * a.n_otiles;
     const int p0 = pt * kPmMT, o0 = ot * 64;
-    auto xtile = [&](int par) { return reinterpret_cast<uint16_t *>(s_pm1x + par * (kPm1Tile / 8)); };
+    auto xtile = [&](int par) { return reinterpret_cast<char *>(s_pm1x + par * (kPm1Tile / 8)); };
     auto wslot = [&](int par, int f) { return s_pm1w + (par * 4 + f) * 64; };
     const int nchunks = a.Cin_pad / kChunk;
     const uint16_t *xb = x + (long)b * a.x_bstride;
     const int plane = a.P * 2;  // bytes per channel plane (H W = P)
-    // x: half-task t = 256 k + tid is channel quad t & 7 of position pair t >> 3
+    // x: load u = 256 k + tid is piece u & 31 (8 positions) of channel row u >> 5;
+    // rows past Cin and positions past the example's last plane read as zeros
     auto rsrc_of = [&](int cc) {
         const int c0 = min(cc, a.Cin - 1);
         const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(kChunk, a.Cin - cc)) * plane - p0 * 2);
@@ -1206,37 +1216,42 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
     const uint16_t *wb = wt + (long)b * a.Cout * a.Cin_pad;
     const long wrow = (long)min(o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh;
     struct Stage {
-        uint32_t r[kHalf][4];
+        u32x4_t r[kLoads];
         u32x4_t w;
     };
+    // pieces at positions past the plane's end take an offset beyond the
+    // buffer's extent: zeros, with no memory traffic
+    const int npos = min(kPmMT, a.P - p0);
+    int xoff[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const int u = 256 * k + tid;
+        xoff[k] = 8 * (u & 31) < npos ? (u >> 5) * plane + ((u & 31) << 4) : 0x7ffffff0;
+    }
     auto load = [&](int c, Stage &st) {
         const auto rs = rsrc_of(c * kChunk);
 #pragma unroll
-        for (int k = 0; k < kHalf; ++k) {
-            const int t = 256 * k + tid;
-            const int vo = 4 * (t & 7) * plane + 4 * (t >> 3);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) st.r[k][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + j * plane, 0, 0);
-        }
+        for (int k = 0; k < kLoads; ++k) st.r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff[k], 0, 0);
         st.w = *reinterpret_cast<const u32x4_t *>(wb + wrow + c * kChunk);
     };
     auto store = [&](int par, const Stage &st) {
-        uint16_t *t16 = xtile(par);
+        char *t = xtile(par);
 #pragma unroll
-        for (int k = 0; k < kHalf; ++k) {
-            const int t = 256 * k + tid;
-            const int quad = t & 7, pg = t >> 3;
-            const int q = 2 * pg, g = quad >> 1, ho = 4 * (quad & 1);
-            const int sel = (quad ^ pg) & 1;
-            const uint32_t bs0 = 0x05040100u + (uint32_t)sel * 0x02020202u;
-            const uint32_t bs1 = 0x07060302u - (uint32_t)sel * 0x02020202u;
-            u32x2_t q0, q1;
-            q0.x = __builtin_amdgcn_perm(st.r[k][1], st.r[k][0], bs0); q0.y = __builtin_amdgcn_perm(st.r[k][3], st.r[k][2], bs0);
-            q1.x = __builtin_amdgcn_perm(st.r[k][1], st.r[k][0], bs1); q1.y = __builtin_amdgcn_perm(st.r[k][3], st.r[k][2], bs1);
-            *reinterpret_cast<u32x2_t *>(t16 + swz(q + sel, g) + ho) = q0;
-            *reinterpret_cast<u32x2_t *>(t16 + swz(q + 1 - sel, g) + ho) = q1;
+        for (int k = 0; k < kLoads; ++k) {
+            const int u = 256 * k + tid;
+            *reinterpret_cast<u32x4_t *>(t + pm1_off(u >> 5, (u & 31) << 3)) = st.r[k];
         }
         wslot(par, wave)[lane] = st.w;
+    };
+    // A fragment: position q, channels 8 g .. 8 g + 7 of the chunk
+    auto afrag = [&](const char *t, int q, int g) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = *reinterpret_cast<const uint16_t *>(t + pm1_off(8 * g + i, q));
+        u32x4_t v;
+        v.x = h[0] | (h[1] << 16); v.y = h[2] | (h[3] << 16);
+        v.z = h[4] | (h[5] << 16); v.w = h[6] | (h[7] << 16);
+        return __builtin_bit_cast(bf16x8_t, v);
     };
     f32x16_t acc[kPmPB][CB];
 #pragma unroll
@@ -1245,14 +1260,8 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
         for (int j = 0; j < CB; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-    Stage st;
-    load(0, st);
-    store(0, st);
-    lds_barrier();
-    for (int c = 0; c < nchunks; ++c) {
-        const int par = c & 1;
-        if (c + 1 < nchunks) load(c + 1, st);
-        const uint16_t *t16 = xtile(par);
+    auto compute = [&](int par) {
+        const char *t = xtile(par);
         bf16x8_t bw[CB][2];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -1262,14 +1271,20 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
         for (int pb = 0; pb < kPmPB; ++pb)
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-                const int q = 32 * (wave * kPmPB + pb) + l32;
-                const bf16x8_t afr =
-                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(t16 + swz(q, 2 * kh + lh)));
+                const bf16x8_t afr = afrag(t, 32 * (wave * kPmPB + pb) + l32, 2 * kh + lh);
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
                     acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bw[cb][kh], acc[pb][cb], 0, 0, 0);
             }
-        // the other buffer was last read in chunk c - 1, before the previous barrier
+    };
+    Stage st;
+    load(0, st);
+    store(0, st);
+    lds_barrier();
+    for (int c = 0; c < nchunks; ++c) {
+        const int par = c & 1;
+        if (c + 1 < nchunks) load(c + 1, st);
+        compute(par);
         if (c + 1 < nchunks) store(par ^ 1, st);
         lds_barrier();
     }
@@ -1289,7 +1304,6 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
                 *reinterpret_cast<u32x2_t *>(s_out + (32 * cb + l32) * kPmOutPitch + pos) = o;
             }
     lds_barrier();
-    const int npos = min(kPmMT, a.P - p0);
     constexpr int kRowVec = kPmMT / 8;
     for (int v = tid; v < 64 * kRowVec; v += 256) {
         const int ch = v / kRowVec, cv = v - ch * kRowVec;
