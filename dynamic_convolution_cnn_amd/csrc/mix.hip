@@ -279,14 +279,17 @@ __global__ __launch_bounds__(256) void premix_kernel(const float *__restrict__ a
 // v_mfma_f32_32x32x16_bf16. A workgroup stages the bank's slice of kMixMW
 // weights (all experts, zeros past n and past wsize) in LDS with 16-byte
 // copies in the natural layout; wave w takes weights [64 w, 64 w + 64) of it
-// as two B fragments per 16 experts, gathered per weight from the LDS rows.
-// The attentions of 32 examples are an A fragment split into three bf16
-// parts (high, middle, low: 24 bits, as a float32 significand), so the three
-// exact products summed in fp32 match a float32 mix before its one bf16
-// rounding. Workgroup (t, c) takes weight tile t and the 32 examples of
-// chunk c; the 32 x kMixMW results go through LDS as bf16 rows and leave as
-// 16-byte stores along each W_b row.
+// as two [32 weights x 16 experts] operands per 16 experts, gathered per
+// weight from the LDS rows. The attentions of 32 examples, [16 experts x 32
+// examples], are split into three bf16 parts (high, middle, low: 24 bits, as
+// a float32 significand), so the three exact products summed in fp32 match a
+// float32 mix before its one bf16 rounding. With the weights as the result's
+// rows, a lane holds 4 consecutive weights of one example's W_b row.
+// Workgroup (t, c) takes weight tile t and the 32 examples of chunk c; the
+// 32 x kMixMW results go through LDS as bf16 rows and leave as 16-byte
+// stores along each W_b row.
 constexpr int kMixMW = 256;       // weights per workgroup (4 waves x 64)
+typedef short s16x4_lds_t __attribute__((ext_vector_type(4)));
 constexpr int kMixMfmaMaxG = 4;   // expert groups of 16: n <= 64
 constexpr int kMixOutPitch = kMixMW + 8;  // bf16 per staged output row (rows 4 apart on other banks)
 constexpr int kMixEx = 32;                // examples per workgroup
@@ -299,6 +302,18 @@ __global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__
     __shared__ __attribute__((aligned(16))) uint16_t s_o[kMixEx][kMixOutPitch];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const long w0 = (long)blockIdx.x * kMixMW;
+    const int bc0 = blockIdx.y * kMixEx;
+    // the attentions of this lane's A-fragment row (example bc0 + l32,
+    // experts 16 g + 8 lh + (0..7)) load first, so that their latency
+    // overlaps with that of the expert slice
+    float av[NKG][8];
+    {
+        const float *ab = alpha + (long)min(bc0 + l32, B - 1) * n;
+#pragma unroll
+        for (int g = 0; g < NKG; ++g)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) av[g][q] = ab[min(16 * g + 8 * lh + q, n - 1)];
+    }
     // stage: clamped unconditional loads first, then masked LDS stores
     constexpr int kRowVec = kMixMW / 8;            // 16-byte vectors per row
     constexpr int kIt = NKG * 16 * kRowVec / 256;  // expert vectors per thread
@@ -318,29 +333,37 @@ __global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__
         *reinterpret_cast<u32x4_t *>(&s_e[k][8 * c]) = in ? q[it] : u32x4_t{0u, 0u, 0u, 0u};
     }
     __syncthreads();
-    // B fragments: experts 16 g + 8 lh + (0..7), weight 64 wave + 32 nt + l32
+    // expert operands (A: rows = weights): experts 16 g + 8 lh + (0..7), weight 64 wave + 32 nt + l32
+    // Each half of an operand is one LDS transpose read (ds_read_b64_tr_b16):
+    // within a group of 16 lanes, lane i receives element i & 3 of the 8 bytes
+    // that lanes 4 j + (i >> 2) (j = 0..3) address, as its element j. Lane
+    // s = 4 j + r of the group addresses expert row k0 + 4 h + j at weights
+    // wg + 4 r .. wg + 4 r + 3, so lane i gets experts k0 + 4 h + (0..3) of
+    // weight wg + i.
     bf16x8_t ef[2][NKG];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int g = 0; g < NKG; ++g) {
-            const int wl = 64 * wave + 32 * nt + l32;
-            const int k0 = 16 * g + 8 * lh;
-            u32x4_t v;
-            v.x = (uint32_t)s_e[k0 + 0][wl] | ((uint32_t)s_e[k0 + 1][wl] << 16);
-            v.y = (uint32_t)s_e[k0 + 2][wl] | ((uint32_t)s_e[k0 + 3][wl] << 16);
-            v.z = (uint32_t)s_e[k0 + 4][wl] | ((uint32_t)s_e[k0 + 5][wl] << 16);
-            v.w = (uint32_t)s_e[k0 + 6][wl] | ((uint32_t)s_e[k0 + 7][wl] << 16);
-            ef[nt][g] = __builtin_bit_cast(bf16x8_t, v);
-        }
     {
-        const int bc0 = blockIdx.y * kMixEx;
-        // A fragments: example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
+        const int si = lane & 15;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int g = 0; g < NKG; ++g) {
+                const int wg = 64 * wave + 32 * nt + 16 * ((lane >> 4) & 1);
+                const int k0 = 16 * g + 8 * lh;
+                s16x4_lds_t h[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4_lds_t *)(&s_e[k0 + 4 * hh + (si >> 2)][wg + 4 * (si & 3)]));
+                const u32x2_t lo = __builtin_bit_cast(u32x2_t, h[0]), hi = __builtin_bit_cast(u32x2_t, h[1]);
+                ef[nt][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+            }
+    }
+    {
+        // attention operands (B: columns = examples): example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
         bf16x8_t ap[3][1][NKG];
 #pragma unroll
         for (int mt = 0; mt < 1; ++mt) {
             const int b = bc0 + 32 * mt + l32;
-            const float *ab = alpha + (long)min(b, B - 1) * n;
 #pragma unroll
             for (int g = 0; g < NKG; ++g) {
                 uint32_t pw[3][4];
@@ -350,8 +373,7 @@ __global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int k = 16 * g + 8 * lh + 2 * jj + e;
-                        const float a = ab[min(k, n - 1)];
-                        float r = (k < n && b < B) ? a : 0.f;
+                        float r = (k < n && b < B) ? av[g][2 * jj + e] : 0.f;
 #pragma unroll
                         for (int part = 0; part < 3; ++part) {
                             p2[part][e] = f32_to_bf16(r);
@@ -378,11 +400,14 @@ __global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__
                 for (int g = 0; g < NKG; ++g)
 #pragma unroll
                     for (int part = 2; part >= 0; --part)  // small parts first
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[part][mt][g], ef[nt][g], acc, 0, 0, 0);
-                // D(lane, 4 j + r) = example 32 mt + 8 j + 4 lh + r, weight 64 wave + 32 nt + l32
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[nt][g], ap[part][mt][g], acc, 0, 0, 0);
+                // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
+                // example 32 mt + l32, so a lane's 4 registers of group j are
+                // 4 consecutive weights of one W_b row (one 8-byte LDS write)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s_o[32 * mt + 8 * (i >> 2) + 4 * lh + (i & 3)][64 * wave + 32 * nt + l32] = f32_to_bf16(acc[i]);
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<u32x2_t *>(&s_o[32 * mt + l32][64 * wave + 32 * nt + 8 * j + 4 * lh]) =
+                        u32x2_t{pack_bf16x2(acc[4 * j], acc[4 * j + 1]), pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3])};
             }
         __syncthreads();
         // rows out: kMixEx examples x kRowVec vectors
@@ -414,7 +439,7 @@ __global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restric
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const long w0 = (long)blockIdx.x * kMixMW;
     const int bc0 = blockIdx.y * kMixEx;
-    // B fragments: experts 16 g + 8 lh + (0..7) of weight w0 + 64 wave + 32 nt + l32
+    // expert operands (A: rows = weights): experts 16 g + 8 lh + (0..7) of weight w0 + 64 wave + 32 nt + l32
     bf16x8_t ef[2][NKG];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -426,7 +451,7 @@ __global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restric
             ef[nt][g] = __builtin_bit_cast(bf16x8_t, k0 < n_pad ? v : u32x4_t{0u, 0u, 0u, 0u});
         }
     }
-    // A fragments: example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
+    // attention operands (B: columns = examples): example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
     bf16x8_t ap[3][NKG];
     {
         const int b = bc0 + l32;
@@ -466,11 +491,13 @@ __global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restric
         for (int g = 0; g < NKG; ++g)
 #pragma unroll
             for (int part = 2; part >= 0; --part)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[part][g], ef[nt][g], acc, 0, 0, 0);
-        // D(lane, 4 j + r) = example 8 j + 4 lh + r, weight 64 wave + 32 nt + l32
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[nt][g], ap[part][g], acc, 0, 0, 0);
+        // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
+        // example l32 (one 8-byte LDS write per group j)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            s_o[8 * (i >> 2) + 4 * lh + (i & 3)][64 * wave + 32 * nt + l32] = f32_to_bf16(acc[i]);
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<u32x2_t *>(&s_o[l32][64 * wave + 32 * nt + 8 * j + 4 * lh]) =
+                u32x2_t{pack_bf16x2(acc[4 * j], acc[4 * j + 1]), pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3])};
     }
     __syncthreads();
     constexpr int kRowVec = kMixMW / 8;
