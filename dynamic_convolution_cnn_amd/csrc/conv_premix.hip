@@ -380,6 +380,8 @@ __global__ __launch_bounds__(256) void conv_pm3_kernel(const uint16_t *__restric
 // 16-byte fragment piece per thread. Both load at the start of the previous
 // chunk and go to the other LDS buffer at its end; one barrier per chunk.
 // Outputs leave through LDS as 16-byte row stores.
+constexpr int kPm1Resident = 3;       // workgroups per CU (LDS: 3 x 41 KB)
+constexpr int kCUs = 256;             // compute units of the MI355X
 constexpr int kPm1Tile = kPmMT * 32;  // bf16 per x tile buffer (32 channels x 256 positions)
 constexpr int kPm1LdsBytes = 64 * kPmOutPitch * 2 > 2 * kPm1Tile * 2 ? 64 * kPmOutPitch * 2 : 2 * kPm1Tile * 2;
 __shared__ __attribute__((aligned(16))) u32x4_t s_pm1x[kPm1LdsBytes / 16];  // 2 x 16 KB tiles, or the epilogue rows
@@ -401,48 +403,60 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int per_b = a.n_ptiles * a.n_otiles;
-    const int b = logical / per_b;
-    const int rem = logical - b * per_b;
-    const int pt = rem / a.n_otiles, ot = rem - pt * a.n_otiles;
-    const int p0 = pt * kPmMT, o0 = ot * 64;
     auto xtile = [&](int par) { return reinterpret_cast<char *>(s_pm1x + par * (kPm1Tile / 8)); };
     auto wslot = [&](int par, int f) { return s_pm1w + (par * 4 + f) * 64; };
     const int nchunks = a.Cin_pad / kChunk;
-    const uint16_t *xb = x + (long)b * a.x_bstride;
     const int plane = a.P * 2;  // bytes per channel plane (H W = P)
-    // x: load u = 256 k + tid is piece u & 31 (8 positions) of channel row u >> 5;
-    // rows past Cin and positions past the example's last plane read as zeros
-    auto rsrc_of = [&](int cc) {
-        const int c0 = min(cc, a.Cin - 1);
-        const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(kChunk, a.Cin - cc)) * plane - p0 * 2);
-        const uint64_t p = reinterpret_cast<uint64_t>(xb + (long)c0 * a.P + p0);
-        const uint64_t ps = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
-                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
-        return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ps), 0, max(0, nbytes), 0x00020000);
+    // Persistent workgroups: tiles (example b, position tile pt, channel tile
+    // ot) in that order are cut into 8 contiguous ranges, one per XCD
+    // (workgroup i runs on XCD i % 8; the grid is a multiple of 8), so the
+    // channel tiles of one position tile share an L2. Workgroup i walks its
+    // XCD's range with stride gridDim.x / 8.
+    const int per_b = a.n_ptiles * a.n_otiles;
+    const int ntiles = a.B * per_b;
+    const int xcd = blockIdx.x & 7, g8 = gridDim.x >> 3;
+    const int hi = (int)((long)ntiles * (xcd + 1) / 8);
+    const int first = (int)((long)ntiles * xcd / 8) + (blockIdx.x >> 3);
+    if (first >= hi) return;
+    struct Tile {
+        int b, p0, o0, npos;
     };
-    // W: thread tid holds lane tid & 63 of fragment f = tid >> 6 (block f >> 1, K half f & 1)
-    const uint16_t *wb = wt + (long)b * a.Cout * a.Cin_pad;
-    const long wrow = (long)min(o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh;
+    auto tile_at = [&](int t) {
+        Tile ti;
+        ti.b = t / per_b;
+        const int rem = t - ti.b * per_b;
+        const int pt = rem / a.n_otiles;
+        ti.p0 = pt * kPmMT;
+        ti.o0 = (rem - pt * a.n_otiles) * 64;
+        ti.npos = min(kPmMT, a.P - ti.p0);
+        return ti;
+    };
     struct Stage {
         u32x4_t r[kLoads];
         u32x4_t w;
     };
+    // Chunk c of tile ti. x: load u = 256 k + tid is piece u & 31 (8
+    // positions) of channel row u >> 5; rows past Cin read as zeros, and
     // pieces at positions past the plane's end take an offset beyond the
-    // buffer's extent: zeros, with no memory traffic
-    const int npos = min(kPmMT, a.P - p0);
-    int xoff[kLoads];
+    // buffer's extent (zeros, with no memory traffic). W: thread tid holds
+    // lane tid & 63 of fragment f = tid >> 6 (block f >> 1, K half f & 1).
+    // (The descriptor's fields go through readfirstlane: scalar registers.)
+    auto load = [&](const Tile &ti, int c, Stage &st) {
+        const int cc = c * kChunk;
+        const int c0 = min(cc, a.Cin - 1);
+        const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(kChunk, a.Cin - cc)) * plane - ti.p0 * 2);
+        const uint64_t p = reinterpret_cast<uint64_t>(x + (long)ti.b * a.x_bstride + (long)c0 * a.P + ti.p0);
+        const uint64_t ps = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ps), 0, max(0, nbytes), 0x00020000);
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        const int u = 256 * k + tid;
-        xoff[k] = 8 * (u & 31) < npos ? (u >> 5) * plane + ((u & 31) << 4) : 0x7ffffff0;
-    }
-    auto load = [&](int c, Stage &st) {
-        const auto rs = rsrc_of(c * kChunk);
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) st.r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff[k], 0, 0);
-        st.w = *reinterpret_cast<const u32x4_t *>(wb + wrow + c * kChunk);
+        for (int k = 0; k < kLoads; ++k) {
+            const int u = 256 * k + tid;
+            const int off = 8 * (u & 31) < ti.npos ? (u >> 5) * plane + ((u & 31) << 4) : 0x7ffffff0;
+            st.r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        }
+        const long wrow = (long)min(ti.o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh;
+        st.w = *reinterpret_cast<const u32x4_t *>(wt + (long)ti.b * a.Cout * a.Cin_pad + wrow + cc);
     };
     auto store = [&](int par, const Stage &st) {
         char *t = xtile(par);
@@ -464,12 +478,6 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
         return __builtin_bit_cast(bf16x8_t, v);
     };
     f32x16_t acc[kPmPB][CB];
-#pragma unroll
-    for (int i = 0; i < kPmPB; ++i)
-#pragma unroll
-        for (int j = 0; j < CB; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
     auto compute = [&](int par) {
         const char *t = xtile(par);
         bf16x8_t bw[CB][2];
@@ -487,40 +495,61 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
                     acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bw[cb][kh], acc[pb][cb], 0, 0, 0);
             }
     };
+    uint16_t *s_out = reinterpret_cast<uint16_t *>(s_pm1x);  // epilogue rows (over the x tiles)
+    int t = first;
+    Tile ti = tile_at(t);
     Stage st;
-    load(0, st);
-    store(0, st);
-    lds_barrier();
-    for (int c = 0; c < nchunks; ++c) {
-        const int par = c & 1;
-        if (c + 1 < nchunks) load(c + 1, st);
-        compute(par);
-        if (c + 1 < nchunks) store(par ^ 1, st);
+    load(ti, 0, st);
+    while (true) {
+        // chunk 0 of this tile: loaded during the previous tile's last chunk
+        // and epilogue (whose LDS reads ended before the last barrier)
+        store(0, st);
         lds_barrier();
-    }
-    // epilogue (as the 3x3 kernel): D(lane, 4 j + q) = channel o0 + 32 cb + l32,
-    // position 32 (wave kPmPB + pb) + 8 j + 4 lh + q
-    uint16_t *s_out = reinterpret_cast<uint16_t *>(s_pm1x);
 #pragma unroll
-    for (int pb = 0; pb < kPmPB; ++pb)
+        for (int i = 0; i < kPmPB; ++i)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+            for (int j = 0; j < CB; ++j)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x2_t o;
-                o.x = pack_bf16x2(acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1]);
-                o.y = pack_bf16x2(acc[pb][cb][4 * j + 2], acc[pb][cb][4 * j + 3]);
-                const int pos = 32 * (wave * kPmPB + pb) + 8 * j + 4 * lh;
-                *reinterpret_cast<u32x2_t *>(s_out + (32 * cb + l32) * kPmOutPitch + pos) = o;
-            }
-    lds_barrier();
-    constexpr int kRowVec = kPmMT / 8;
-    for (int v = tid; v < 64 * kRowVec; v += 256) {
-        const int ch = v / kRowVec, cv = v - ch * kRowVec;
-        const int o = o0 + ch;
-        if (o < a.Cout && 8 * cv < npos)
-            *reinterpret_cast<u32x4_t *>(y + ((long)b * a.Cout + o) * a.P + p0 + 8 * cv) =
-                *reinterpret_cast<const u32x4_t *>(s_out + ch * kPmOutPitch + 8 * cv);
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        const int tn = t + g8;
+        const bool more = tn < hi;
+        const Tile tin = tile_at(more ? tn : t);
+        for (int c = 0; c < nchunks; ++c) {
+            const int par = c & 1;
+            if (c + 1 < nchunks) load(ti, c + 1, st);
+            else if (more) load(tin, 0, st);
+            compute(par);
+            // the other buffer was last read in chunk c - 1, before the previous barrier
+            if (c + 1 < nchunks) store(par ^ 1, st);
+            lds_barrier();
+        }
+        // epilogue (as the 3x3 kernel): D(lane, 4 j + q) = channel o0 + 32 cb + l32,
+        // position 32 (wave kPmPB + pb) + 8 j + 4 lh + q
+#pragma unroll
+        for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x2_t o;
+                    o.x = pack_bf16x2(acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1]);
+                    o.y = pack_bf16x2(acc[pb][cb][4 * j + 2], acc[pb][cb][4 * j + 3]);
+                    const int pos = 32 * (wave * kPmPB + pb) + 8 * j + 4 * lh;
+                    *reinterpret_cast<u32x2_t *>(s_out + (32 * cb + l32) * kPmOutPitch + pos) = o;
+                }
+        lds_barrier();
+        constexpr int kRowVec = kPmMT / 8;
+        for (int v = tid; v < 64 * kRowVec; v += 256) {
+            const int ch = v / kRowVec, cv = v - ch * kRowVec;
+            const int o = ti.o0 + ch;
+            if (o < a.Cout && 8 * cv < ti.npos)
+                *reinterpret_cast<u32x4_t *>(y + ((long)ti.b * a.Cout + o) * a.P + ti.p0 + 8 * cv) =
+                    *reinterpret_cast<const u32x4_t *>(s_out + ch * kPmOutPitch + 8 * cv);
+        }
+        if (!more) break;
+        lds_barrier();  // the epilogue's LDS reads end before the next chunk 0 lands there
+        t = tn;
+        ti = tin;
     }
 }
 
@@ -597,7 +626,10 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
         ConvArgs a = base_args(g);
         a.n_ptiles = ceil_div(g.P, kPmMT);
         a.n_otiles = ceil_div(g.Cout, 64);
-        const long blocks = (long)g.B * a.n_ptiles * a.n_otiles;
+        // persistent: at most kPm1Resident workgroups per CU, a multiple of 8
+        const long tiles = (long)g.B * a.n_ptiles * a.n_otiles;
+        const long blocks = std::min(ceil_div((int)std::min(tiles, (long)INT32_MAX - 8), 8) * 8L,
+                                     (long)kCUs * kPm1Resident);
         hipLaunchKernelGGL(conv_pm1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
         return hipGetLastError();
     }
