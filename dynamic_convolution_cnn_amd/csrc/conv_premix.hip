@@ -553,6 +553,146 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
     }
 }
 
+// ---- 1x1 convolution with few input channels (Cin <= 64) ----------------
+// The MBConv expand layers write many more bytes than they read. A
+// workgroup owns one example's kPmMT positions and all output channels: its
+// x slice (NCH <= 2 chunks) loads once into a [channel][position] LDS tile
+// (the layout and reads of conv_pm1_kernel), then it walks the 64-channel
+// output tiles, loading the next tile's W_b slice while it multiplies, and
+// sends each tile out through a 32-channel LDS stage in two passes, so that
+// one tile's output stores overlap the next tile's work.
+constexpr int kPm1xOutPitch = kPmMT + 8;  // bf16 per staged output row
+template <int NCH>
+__global__ __launch_bounds__(256) void conv_pm1x_kernel(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ wt,
+                                                        uint16_t *__restrict__ y, ConvArgs a) {
+    constexpr int CB = 2;
+    constexpr int kLoads = 32 * kPmMT * 2 / 16 / 256;  // 16-byte x loads per thread per chunk (4)
+    __shared__ __attribute__((aligned(16))) u32x4_t s_x[NCH * kPm1Tile / 8];     // NCH x 16 KB
+    __shared__ __attribute__((aligned(16))) u32x4_t s_w[2 * NCH * 4 * 64];       // 2 x NCH x 4 fragments
+    __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * kPm1xOutPitch];    // one 32-channel block
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = logical / a.n_ptiles, pt = logical - b * a.n_ptiles;
+    const int p0 = pt * kPmMT, npos = min(kPmMT, a.P - p0);
+    const int plane = a.P * 2;  // bytes per channel plane
+    auto xtile = [&](int c) { return reinterpret_cast<char *>(s_x + c * (kPm1Tile / 8)); };
+    auto wslot = [&](int buf, int c, int f) { return s_w + ((buf * NCH + c) * 4 + f) * 64; };
+    const uint16_t *wb = wt + (long)b * a.Cout * a.Cin_pad;
+    // W_b piece of output tile ot, chunk c: lane tid & 63 of fragment f = tid >> 6
+    auto wload = [&](int ot, int c) {
+        const long row = (long)min(64 * ot + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad;
+        return *reinterpret_cast<const u32x4_t *>(wb + row + c * kChunk + 16 * (wave & 1) + 8 * lh);
+    };
+    // x: as conv_pm1_kernel (rows past Cin and positions past the plane read as zeros)
+    {
+        u32x4_t r[NCH][kLoads];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int cc = c * kChunk;
+            const int c0 = min(cc, a.Cin - 1);
+            const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(kChunk, a.Cin - cc)) * plane - p0 * 2);
+            const uint64_t p = reinterpret_cast<uint64_t>(x + (long)b * a.x_bstride + (long)c0 * a.P + p0);
+            const uint64_t ps = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p) |
+                                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32);
+            const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ps), 0, max(0, nbytes), 0x00020000);
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k) {
+                const int u = 256 * k + tid;
+                const int off = 8 * (u & 31) < npos ? (u >> 5) * plane + ((u & 31) << 4) : 0x7ffffff0;
+                r[c][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            }
+        }
+        u32x4_t w0[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) w0[c] = wload(0, c);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+            for (int k = 0; k < kLoads; ++k) {
+                const int u = 256 * k + tid;
+                *reinterpret_cast<u32x4_t *>(xtile(c) + pm1_off(u >> 5, (u & 31) << 3)) = r[c][k];
+            }
+            wslot(0, c, wave)[lane] = w0[c];
+        }
+    }
+    lds_barrier();
+    auto afrag = [&](const char *t, int q, int g) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = *reinterpret_cast<const uint16_t *>(t + pm1_off(8 * g + i, q));
+        u32x4_t v;
+        v.x = h[0] | (h[1] << 16); v.y = h[2] | (h[3] << 16);
+        v.z = h[4] | (h[5] << 16); v.w = h[6] | (h[7] << 16);
+        return __builtin_bit_cast(bf16x8_t, v);
+    };
+    for (int ot = 0; ot < a.n_otiles; ++ot) {
+        const int buf = ot & 1;
+        const bool more = ot + 1 < a.n_otiles;
+        u32x4_t wn[NCH];
+        if (more)
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) wn[c] = wload(ot + 1, c);
+        f32x16_t acc[kPmPB][CB];
+#pragma unroll
+        for (int i = 0; i < kPmPB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const char *t = xtile(c);
+            bf16x8_t bw[CB][2];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+                    bw[cb][kh] = __builtin_bit_cast(bf16x8_t, wslot(buf, c, 2 * cb + kh)[lane]);
+#pragma unroll
+            for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const bf16x8_t afr = afrag(t, 32 * (wave * kPmPB + pb) + l32, 2 * kh + lh);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[pb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bw[cb][kh], acc[pb][cb], 0, 0, 0);
+                }
+        }
+        // the next tile's W_b goes to the other buffer, last read during tile ot - 1
+        if (more)
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) wslot(buf ^ 1, c, wave)[lane] = wn[c];
+        // epilogue, one 32-channel block per pass: D(lane, 4 j + q) = channel
+        // 64 ot + 32 cb + l32, position 32 (wave kPmPB + pb) + 8 j + 4 lh + q
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x2_t o;
+                    o.x = pack_bf16x2(acc[pb][cb][4 * j], acc[pb][cb][4 * j + 1]);
+                    o.y = pack_bf16x2(acc[pb][cb][4 * j + 2], acc[pb][cb][4 * j + 3]);
+                    const int pos = 32 * (wave * kPmPB + pb) + 8 * j + 4 * lh;
+                    *reinterpret_cast<u32x2_t *>(s_o + l32 * kPm1xOutPitch + pos) = o;
+                }
+            lds_barrier();
+            constexpr int kRowVec = kPmMT / 8;
+            for (int v = tid; v < 32 * kRowVec; v += 256) {
+                const int ch = v / kRowVec, cv = v - ch * kRowVec;
+                const int o = 64 * ot + 32 * cb + ch;
+                if (o < a.Cout && 8 * cv < npos)
+                    *reinterpret_cast<u32x4_t *>(y + ((long)b * a.Cout + o) * a.P + p0 + 8 * cv) =
+                        *reinterpret_cast<const u32x4_t *>(s_o + ch * kPm1xOutPitch + 8 * cv);
+            }
+            lds_barrier();  // the stage is read before the next pass writes it
+        }
+    }
+}
+
 // Premix tile shapes: (FM, FN, NW) -> MT = NW*FM*16 positions, NT = FN*16 channels.
 struct PremixCfg { int FM, FN, NW; };
 constexpr PremixCfg kPremixLarge{7, 4, 7};  // MT 784, NT 64
@@ -622,6 +762,17 @@ static bool pm1_ok(const Geom &g) {
 
 hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
                               hipStream_t stream) {
+    if (pm1_ok(g) && g.Cin <= 2 * kChunk) {
+        ConvArgs a = base_args(g);
+        a.n_ptiles = ceil_div(g.P, kPmMT);
+        a.n_otiles = ceil_div(g.Cout, 64);
+        const long blocks = (long)g.B * a.n_ptiles;
+        if (g.Cin <= kChunk)
+            hipLaunchKernelGGL(conv_pm1x_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+        else
+            hipLaunchKernelGGL(conv_pm1x_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+        return hipGetLastError();
+    }
     if (pm1_ok(g)) {
         ConvArgs a = base_args(g);
         a.n_ptiles = ceil_div(g.P, kPmMT);
