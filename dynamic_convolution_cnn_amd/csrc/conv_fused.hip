@@ -290,7 +290,12 @@ __global__ __launch_bounds__(512) void conv_fused_kernel(const uint16_t *__restr
         }
         if (++t == a.KT) {
             t = 0;
-            if (c0 + kChunk < a.Cin_pad) stage_store<XT>(tile, smap, xr);
+            if (c0 + kChunk < a.Cin_pad) {
+                // the example's other wave may still read this chunk's tile
+                // for the current step: meet it before overwriting the tile
+                lds_barrier();
+                stage_store<XT>(tile, smap, xr);
+            }
             c0 += kChunk;
         }
         lds_barrier();

@@ -260,6 +260,9 @@ RAGGED = [
     (7, 64, 64, 6, 6, (3, 3), 1, 1, 4),      # small image: fewer rows than blocks
     (3, 40, 72, 24, 20, (1, 1), 1, 0, 8),    # 1x1: two chunks (tail), two channel tiles, partial position tile
     (2, 48, 64, 30, 56, (3, 3), 1, 1, 2),    # wide rows: several 256-position tiles spanning rows
+    (2, 64, 130, 18, 16, (1, 1), 1, 0, 4),   # 1x1, Cin <= 64: three output tiles (tail 2), position tail 32
+    (3, 20, 33, 10, 8, (1, 1), 1, 0, 3),     # 1x1, one partial chunk, odd Cout
+    (3, 96, 40, 12, 12, (1, 1), 1, 0, 2),    # 1x1, three chunks (odd count) on the persistent path
 ]
 
 
