@@ -298,6 +298,14 @@ def main():
     images_s = w.B / (ms_per_step * 1e-3)
     route_bytes = w.B * L0.Cin * L0.H * L0.W * esz + w.B * w.n * 4
     conv_tflops = conv_flops0 / (conv_ms * 1e-3) / 1e12
+    # algorithmic bytes of the first layer's forward: x and y once, the expert
+    # bank once, and W_b written and read again when the policy materialises it
+    wsize0 = experts[0][0].numel()
+    conv_bytes0 = (w.B * (L0.Cin * L0.H * L0.W + L0.Cout * L0.Ho * L0.Wo) + w.n * wsize0) * esz
+    if pols[0] == bd.DYNCONV_POLICY_PREMIX:
+        conv_bytes0 += 2 * w.B * wsize0 * esz
+    conv_gbs = conv_bytes0 / (conv_ms * 1e-3) / 1e9
+    hbm_bound = conv_gbs / PEAK_HBM_GBS > conv_tflops / PEAK_BF16_TFLOPS
     traffic = None
     t = TRAFFIC.get(w.key)
     if t and t.get("source_sha") == source_sha():
@@ -332,10 +340,15 @@ def main():
         "mix_hbm": {"us": round(mix_ms * 1e3, 2), "MB": round(mix_bytes / 1e6, 2),
                     "GB/s": round(mix_bytes / (mix_ms * 1e-3) / 1e9, 1),
                     "frac": round(mix_bytes / (mix_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
-        "roofline": {"kernel": "conv layer 0 (" + pol_name.get(pols[0], "") + ")",
-                     "bound": "mfma", "achieved": round(conv_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "roofline": ({"kernel": "conv layer 0 (" + pol_name.get(pols[0], "") + ")",
+                      "bound": "hbm", "achieved": round(conv_gbs, 1),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(conv_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+                     if hbm_bound else
+                     {"kernel": "conv layer 0 (" + pol_name.get(pols[0], "") + ")",
+                      "bound": "mfma", "achieved": round(conv_tflops, 2),
+                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d)
