@@ -20,6 +20,10 @@ cites the passage of the pages it follows:
 * convolution - one ordinary convolution per example with its own kernel:
   "specialized convolutional kernels for each example" (CondConv:
   Conditionally Parameterized Convolutions, abstract).
+* input and output attention - FMDConv's per-channel scales of the layer's
+  input and output (FMDConv: Fast multi-attention dynamic convolution,
+  abstract, which names them without a formula; the reading is stated at
+  ``forward_attn``). Each head is a route (GAP -> FC -> sigmoid) of its own.
 
 Parity pins live in ``tests/test_oracle_pins.py``.
 """
@@ -72,8 +76,9 @@ def _load():
     lib.oracle_conv.argtypes = [i32] * 10 + [P, P, P]
     lib.oracle_forward.argtypes = [i32] * 11 + [P, P, P, P]
     lib.oracle_forward_points.argtypes = [i32] * 11 + [P, P, P, i64, P, P]
+    lib.oracle_forward_attn.argtypes = [i32] * 11 + [P, P, P, P, P, P]
     for f in (lib.oracle_gap, lib.oracle_route, lib.oracle_mix, lib.oracle_conv,
-              lib.oracle_forward, lib.oracle_forward_points):
+              lib.oracle_forward, lib.oracle_forward_points, lib.oracle_forward_attn):
         f.restype = i32
     _lib = lib
     return lib
@@ -198,3 +203,32 @@ def forward_points(x, experts, alpha, idx, stride: int = 1, pad: int = 0,
                                        idx.shape[0], _ptr(idx), _ptr(out))
     _check(rc, "forward_points")
     return out
+
+
+def forward_attn(x, experts, alpha, a_in=None, a_out=None, stride: int = 1, pad: int = 0,
+                 groups: int = 1) -> np.ndarray:
+    """The layer with FMDConv's input and output attentions (FMDConv: Fast
+    multi-attention dynamic convolution, abstract). Reading: a_in[b, c]
+    scales input channel c of example b before the convolution, a_out[b, o]
+    scales output channel o after it; None means all ones:
+    y[b,o] = a_out[b,o] * conv(a_in[b,:] * x[b], W_b)[o]."""
+    x = _f32(x)
+    experts = _f32(experts)
+    alpha = _f64(alpha)
+    B, Cin, H, W = x.shape
+    n, Cout, cpg, kh, kw = experts.shape
+    assert alpha.shape == (B, n) and cpg * groups == Cin
+    ai = None if a_in is None else _f64(a_in)
+    ao = None if a_out is None else _f64(a_out)
+    if ai is not None:
+        assert ai.shape == (B, Cin)
+    if ao is not None:
+        assert ao.shape == (B, Cout)
+    Ho, Wo = out_size(H, kh, stride, pad), out_size(W, kw, stride, pad)
+    y = np.empty((B, Cout, Ho, Wo), np.float64)
+    rc = _load().oracle_forward_attn(B, Cin, H, W, Cout, kh, kw, stride, pad, groups, n,
+                                     _ptr(x), _ptr(experts), _ptr(alpha),
+                                     None if ai is None else _ptr(ai),
+                                     None if ao is None else _ptr(ao), _ptr(y))
+    _check(rc, "forward_attn")
+    return y

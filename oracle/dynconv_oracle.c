@@ -318,3 +318,64 @@ int oracle_forward_points(int B, int Cin, int H, int W, int Cout, int kh,
     }
     return ORACLE_OK;
 }
+
+/*
+ * The layer with FMDConv's input and output attentions (FMDConv: Fast
+ * multi-attention dynamic convolution, abstract: input attention, kernel
+ * attention and output attention). The page gives no formula; the reading
+ * taken: the input attention scales each input channel of the example before
+ * the convolution, the output attention scales each output channel after it,
+ * and the kernel attention is alpha as above:
+ *   y[b,o,r,s] = a_out[b,o] * sum_{c,u,v} W_b[o,c,u,v] * a_in[b,gc] * x[b,gc,h,w],
+ *   gc = (o / (Cout/groups)) * (Cin/groups) + c, h = r*stride - pad + u,
+ *   w = s*stride - pad + v (zero outside the image).
+ * a_in [B, Cin] and a_out [B, Cout] may be NULL (all ones).
+ */
+int oracle_forward_attn(int B, int Cin, int H, int W, int Cout, int kh, int kw,
+                        int stride, int pad, int groups, int n, const float *x,
+                        const float *experts, const double *alpha,
+                        const double *a_in, const double *a_out, double *y)
+{
+    if (B < 0 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 ||
+        stride < 1 || pad < 0 || groups < 1 || n < 1 || !x || !experts ||
+        !alpha || !y)
+        return ORACLE_BAD_ARG;
+    if (Cin % groups || Cout % groups) return ORACLE_BAD_ARG;
+    int Ho = out_size(H, kh, stride, pad), Wo = out_size(W, kw, stride, pad);
+    if (Ho < 1 || Wo < 1) return ORACLE_BAD_ARG;
+    int cpg = Cin / groups, opg = Cout / groups;
+    long per_o = (long)cpg * kh * kw;
+    long wsz = (long)Cout * per_o;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b) {
+        for (int o = 0; o < Cout; ++o) {
+            int g = o / opg;
+            double so = a_out ? a_out[(long)b * Cout + o] : 1.0;
+            for (int r = 0; r < Ho; ++r) {
+                for (int s = 0; s < Wo; ++s) {
+                    double acc = 0.0;
+                    for (int c = 0; c < cpg; ++c) {
+                        int gc = g * cpg + c;
+                        double si = a_in ? a_in[(long)b * Cin + gc] : 1.0;
+                        const float *xp = x + (((long)b * Cin + gc) * H) * W;
+                        for (int u = 0; u < kh; ++u) {
+                            int h = r * stride - pad + u;
+                            if (h < 0 || h >= H) continue;
+                            for (int v = 0; v < kw; ++v) {
+                                int w = s * stride - pad + v;
+                                if (w < 0 || w >= W) continue;
+                                long e = (long)o * per_o + ((long)c * kh + u) * kw + v;
+                                double wv = 0.0;
+                                for (int i = 0; i < n; ++i)
+                                    wv += alpha[(long)b * n + i] * (double)experts[(long)i * wsz + e];
+                                acc += wv * (si * (double)xp[(long)h * W + w]);
+                            }
+                        }
+                    }
+                    y[(((long)b * Cout + o) * Ho + r) * Wo + s] = so * acc;
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}

@@ -270,3 +270,71 @@ def test_invalid_arguments_rejected():
         oracle.forward(x, e, np.ones((1, 2)), stride=1, pad=-1)
     with pytest.raises(ValueError):
         oracle.route(x, np.ones((2, 3), np.float32), None, oracle.SOFTMAX, 0.0)
+
+
+# ------------------------------------------------ FMDConv input / output attention
+ATTN_CASES = [
+    # B, Cin, Cout, H, W, k, stride, pad, groups, n
+    (2, 6, 5, 7, 6, 3, 1, 1, 1, 3),
+    (3, 4, 4, 6, 6, 5, 2, 2, 4, 2),   # depthwise
+    (2, 8, 3, 5, 5, 1, 1, 0, 1, 1),   # 1x1
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_attention_of_ones_is_the_plain_layer(case):
+    B, Cin, Cout, H, W, k, st, p, g, n = case
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+    e = rng.standard_normal((n, Cout, Cin // g, k, k)).astype(np.float32)
+    alpha = rng.uniform(0, 1, (B, n))
+    ones_in, ones_out = np.ones((B, Cin)), np.ones((B, Cout))
+    ref = oracle.forward(x, e, alpha, st, p, g)
+    np.testing.assert_allclose(oracle.forward_attn(x, e, alpha, ones_in, ones_out, st, p, g), ref,
+                               rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.forward_attn(x, e, alpha, None, None, st, p, g), ref,
+                               rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_output_attention_scales_output_channels(case):
+    """a_out[b, o] multiplies output channel o of example b (and nothing else)."""
+    B, Cin, Cout, H, W, k, st, p, g, n = case
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+    e = rng.standard_normal((n, Cout, Cin // g, k, k)).astype(np.float32)
+    alpha = rng.uniform(0, 1, (B, n))
+    a_out = rng.uniform(0.1, 1.0, (B, Cout))
+    got = oracle.forward_attn(x, e, alpha, None, a_out, st, p, g)
+    ref = oracle.forward(x, e, alpha, st, p, g) * a_out[:, :, None, None]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_input_attention_scales_input_channels(case):
+    """a_in[b, c] acts as a scale of input channel c of example b: the layer of
+    the scaled input (power-of-two scales, so x * a_in is exact in float32)."""
+    B, Cin, Cout, H, W, k, st, p, g, n = case
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+    e = rng.standard_normal((n, Cout, Cin // g, k, k)).astype(np.float32)
+    alpha = rng.uniform(0, 1, (B, n))
+    a_in = 2.0 ** rng.integers(-3, 2, (B, Cin))   # 1/8 .. 2: exact scaling
+    got = oracle.forward_attn(x, e, alpha, a_in, None, st, p, g)
+    xs = (x.astype(np.float64) * a_in[:, :, None, None]).astype(np.float32)
+    np.testing.assert_allclose(got, oracle.forward(xs, e, alpha, st, p, g), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_layer_matches_torch_conv2d():
+    """One expert with attention 1: a_out * conv2d(a_in * x, E_0) in float64 torch."""
+    rng = np.random.default_rng(34)
+    for (B, Cin, Cout, H, W, k, st, p, g, _) in ATTN_CASES:
+        x = rng.standard_normal((B, Cin, H, W)).astype(np.float32)
+        e = rng.standard_normal((1, Cout, Cin // g, k, k)).astype(np.float32)
+        a_in = rng.uniform(0.1, 1.0, (B, Cin))
+        a_out = rng.uniform(0.1, 1.0, (B, Cout))
+        got = oracle.forward_attn(x, e, np.ones((B, 1)), a_in, a_out, st, p, g)
+        xt = torch.from_numpy(x.astype(np.float64)) * torch.from_numpy(a_in)[:, :, None, None]
+        ref = F.conv2d(xt, torch.from_numpy(e[0].astype(np.float64)), stride=st, padding=p, groups=g)
+        ref = (ref * torch.from_numpy(a_out)[:, :, None, None]).numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
