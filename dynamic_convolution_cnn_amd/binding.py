@@ -41,6 +41,8 @@ EXPORTED = (
     "dynconv_forward_workspace_bytes", "dynconv_forward_policy", "dynconv_status_string",
     "dynconv_last_error", "dynconv_abi_version", "dynconv_packed_experts_bytes",
     "dynconv_pack_experts", "dynconv_forward_packed", "dynconv_forward_packed_workspace_bytes",
+    "dynconv_route_attn", "dynconv_route_attn_workspace_bytes", "dynconv_forward_attn",
+    "dynconv_forward_attn_workspace_bytes",
 )
 
 
@@ -98,6 +100,14 @@ def lib():
     L.dynconv_forward_packed.restype = i32
     L.dynconv_forward_packed_workspace_bytes.argtypes = [D, i32]
     L.dynconv_forward_packed_workspace_bytes.restype = sz
+    L.dynconv_route_attn.argtypes = [D, P, P, P, i32, f32, P, P, P, P, P, P, P, P, sz, P]
+    L.dynconv_route_attn.restype = i32
+    L.dynconv_route_attn_workspace_bytes.argtypes = [D]
+    L.dynconv_route_attn_workspace_bytes.restype = sz
+    L.dynconv_forward_attn.argtypes = [D, i32, P, P, P, P, P, P, P, sz, P]
+    L.dynconv_forward_attn.restype = i32
+    L.dynconv_forward_attn_workspace_bytes.argtypes = [D, i32]
+    L.dynconv_forward_attn_workspace_bytes.restype = sz
     _lib = L
     return L
 
@@ -226,6 +236,53 @@ def dynconv_forward(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
     _check(lib().dynconv_forward(ctypes.byref(desc), int(policy), _ptr(x), _ptr(experts),
                                  _ptr(alpha), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "dynconv_forward")
+    return y
+
+
+def dynconv_route_attn_workspace_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_route_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def dynconv_route_attn(x: torch.Tensor, Cout: int, fc_w: torch.Tensor, fc_b: Optional[torch.Tensor],
+                       fc_w_in: torch.Tensor, fc_b_in: Optional[torch.Tensor], fc_w_out: torch.Tensor,
+                       fc_b_out: Optional[torch.Tensor], mode: int = DYNCONV_SIGMOID,
+                       temperature: float = 1.0, workspace: Optional[torch.Tensor] = None,
+                       stream=None):
+    """FMDConv's three attentions from one pooling of x: (alpha [B, n], a_in [B, Cin],
+    a_out [B, Cout]), float32."""
+    B, Cin, H, W = x.shape
+    n = fc_w.shape[0]
+    desc = make_desc(B, Cin, H, W, Cout, 1, 1, 1, 0, 1, n, _dtype_code(x))
+    alpha = torch.empty((B, n), dtype=torch.float32, device=x.device)
+    a_in = torch.empty((B, Cin), dtype=torch.float32, device=x.device)
+    a_out = torch.empty((B, Cout), dtype=torch.float32, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_route_attn_workspace_bytes(desc), x.device, workspace)
+    _check(lib().dynconv_route_attn(ctypes.byref(desc), _ptr(x), _ptr(fc_w), _ptr(fc_b), int(mode),
+                                    float(temperature), _ptr(fc_w_in), _ptr(fc_b_in), _ptr(fc_w_out),
+                                    _ptr(fc_b_out), _ptr(alpha), _ptr(a_in), _ptr(a_out), _ptr(ws),
+                                    ws_bytes, _stream(stream)), "dynconv_route_attn")
+    return alpha, a_in, a_out
+
+
+def dynconv_forward_attn_workspace_bytes(desc: dynconv_desc_t, policy: int = DYNCONV_POLICY_AUTO) -> int:
+    return int(lib().dynconv_forward_attn_workspace_bytes(ctypes.byref(desc), int(policy)))
+
+
+def dynconv_forward_attn(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
+                         a_in: Optional[torch.Tensor], a_out: Optional[torch.Tensor],
+                         stride: int = 1, pad: int = 0, groups: int = 1,
+                         policy: int = DYNCONV_POLICY_AUTO, y: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[b, o] = a_out[b, o] * conv(a_in[b, :] x[b], sum_i alpha[b, i] experts[i])[o]."""
+    desc = layer_desc(x, experts, stride, pad, groups)
+    Ho = (desc.H + 2 * pad - desc.kh) // stride + 1
+    Wo = (desc.W + 2 * pad - desc.kw) // stride + 1
+    if y is None:
+        y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_forward_attn_workspace_bytes(desc, policy), x.device, workspace)
+    _check(lib().dynconv_forward_attn(ctypes.byref(desc), int(policy), _ptr(x), _ptr(experts),
+                                      _ptr(alpha), _ptr(a_in), _ptr(a_out), _ptr(y), _ptr(ws), ws_bytes,
+                                      _stream(stream)), "dynconv_forward_attn")
     return y
 
 

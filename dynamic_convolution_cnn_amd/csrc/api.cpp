@@ -37,6 +37,8 @@ constexpr size_t kWsAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+int d_cout(const dynconv_desc_t *d) { return d->Cout; }
+
 // Shape checks shared by every entry point. On success fills `g`.
 dynconv_status_t check_desc(const dynconv_desc_t *d, dynconv::Geom &g, bool need_conv) {
     if (!d) return fail(DYNCONV_ERR_INVALID_ARG, "desc is NULL");
@@ -152,17 +154,73 @@ bool packable(const dynconv::Geom &g) { return g.bf16 && g.groups == 1 && g.n_pa
 // premixed kernels for the PREMIX policy.
 dynconv_status_t forward_from_packed(const dynconv::Geom &g, int32_t p, const void *x,
                                      const uint16_t *packed, const float *alpha, void *y,
-                                     char *ws, hipStream_t st) {
+                                     char *ws, hipStream_t st, dynconv::ChanAttn att = {}) {
     if (p == DYNCONV_POLICY_FUSED)
         return hip_status(dynconv::launch_conv_fused(g, static_cast<const uint16_t *>(x), packed,
                                                      alpha, static_cast<uint16_t *>(y), st),
                           "fused convolution launch");
     uint16_t *wt = reinterpret_cast<uint16_t *>(ws);
-    hipError_t e = dynconv::launch_premix(g, alpha, packed, wt, st);
+    hipError_t e = dynconv::launch_premix(g, alpha, packed, wt, st, att);
     if (e != hipSuccess) return hip_status(e, "premix launch");
     return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
-                                                  static_cast<uint16_t *>(y), st),
+                                                  static_cast<uint16_t *>(y), st, att),
                       "convolution launch");
+}
+
+// The forward of dynconv_forward and dynconv_forward_attn. With channel
+// attentions the fused policy is not available (AUTO resolves to PREMIX for
+// groups == 1 layers).
+dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const void *x,
+                              const void *experts, const float *alpha, void *y, void *workspace,
+                              size_t workspace_bytes, void *stream, dynconv::ChanAttn att) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !experts || !alpha || !y)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, experts, alpha and y must not be NULL");
+    if (!aligned16(x) || !aligned16(experts) || !aligned16(alpha) || !aligned16(y) ||
+        (att.in && !aligned16(att.in)) || (att.out && !aligned16(att.out)))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const bool attn = att.in || att.out;
+    int32_t p;
+    if (attn && !depthwise(g) && g.bf16) {
+        if (policy == DYNCONV_POLICY_FUSED)
+            return fail(DYNCONV_ERR_UNSUPPORTED, "channel attentions run on the PREMIX policy (groups == 1)");
+        s = resolve_policy(g, DYNCONV_POLICY_PREMIX, p);
+    } else {
+        s = resolve_policy(g, policy, p);
+    }
+    if (s != DYNCONV_OK) return s;
+    const size_t need = forward_ws(g, p);
+    if (need > 0 && (workspace_bytes < need || !workspace || !aligned16(workspace)))
+        return fail(DYNCONV_ERR_WORKSPACE, "forward needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    hipError_t e;
+    if (depthwise(g)) {
+        const void *wm = nullptr;
+        if (p == DYNCONV_POLICY_PREMIX) {
+            e = dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, ws, st);
+            if (e != hipSuccess) return hip_status(e, "dynconv_forward mix launch");
+            wm = ws;
+        }
+        return hip_status(dynconv::launch_conv_depthwise(g, x, experts, alpha, wm, y, st, att),
+                          "dynconv_forward depthwise launch");
+    }
+    if (!g.bf16) {
+        e = dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, ws, st);
+        if (e != hipSuccess) return hip_status(e, "dynconv_forward mix launch");
+        return hip_status(dynconv::launch_conv_direct_f32(g, static_cast<const float *>(x),
+                                                          reinterpret_cast<const float *>(ws),
+                                                          static_cast<float *>(y), st, att),
+                          "dynconv_forward conv launch");
+    }
+    uint16_t *packed = reinterpret_cast<uint16_t *>(ws);
+    e = dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), packed, st);
+    if (e != hipSuccess) return hip_status(e, "dynconv_forward pack launch");
+    return forward_from_packed(g, p, x, packed, alpha, y,
+                               ws + round_up(dynconv::packed_experts_bytes(g), kWsAlign), st, att);
 }
 
 }  // namespace
@@ -249,46 +307,68 @@ size_t dynconv_forward_workspace_bytes(const dynconv_desc_t *desc, int32_t polic
 dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy, const void *x,
                                  const void *experts, const float *alpha, void *y,
                                  void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(desc, policy, x, experts, alpha, y, workspace, workspace_bytes, stream, {});
+}
+
+size_t dynconv_forward_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t policy) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK) return 0;
+    int32_t p;
+    const int32_t want = (!depthwise(g) && g.bf16) ? DYNCONV_POLICY_PREMIX : policy;
+    if (policy == DYNCONV_POLICY_FUSED && !depthwise(g) && g.bf16) return 0;
+    if (resolve_policy(g, want, p) != DYNCONV_OK) return 0;
+    return forward_ws(g, p);
+}
+
+dynconv_status_t dynconv_forward_attn(const dynconv_desc_t *desc, int32_t policy, const void *x,
+                                      const void *experts, const float *alpha, const float *a_in,
+                                      const float *a_out, void *y, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    dynconv::ChanAttn att;
+    att.in = a_in;
+    att.out = a_out;
+    return forward_impl(desc, policy, x, experts, alpha, y, workspace, workspace_bytes, stream, att);
+}
+
+size_t dynconv_route_attn_workspace_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK) return 0;
+    return round_up((size_t)g.B * g.Cin * sizeof(float), kWsAlign);
+}
+
+dynconv_status_t dynconv_route_attn(const dynconv_desc_t *desc, const void *x, const float *fc_w,
+                                    const float *fc_b, int32_t mode, float temperature,
+                                    const float *fc_w_in, const float *fc_b_in, const float *fc_w_out,
+                                    const float *fc_b_out, float *alpha, float *a_in, float *a_out,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
     dynconv::Geom g;
     dynconv_status_t s = check_desc(desc, g, true);
     if (s != DYNCONV_OK) return s;
-    if (!x || !experts || !alpha || !y)
-        return fail(DYNCONV_ERR_INVALID_ARG, "x, experts, alpha and y must not be NULL");
-    if (!aligned16(x) || !aligned16(experts) || !aligned16(alpha) || !aligned16(y))
-        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    int32_t p;
-    s = resolve_policy(g, policy, p);
-    if (s != DYNCONV_OK) return s;
-    const size_t need = forward_ws(g, p);
-    if (need > 0 && (workspace_bytes < need || !workspace || !aligned16(workspace)))
-        return fail(DYNCONV_ERR_WORKSPACE, "forward needs %zu bytes of 16-byte aligned workspace (got %zu)",
+    if (!x || !fc_w || !fc_w_in || !fc_w_out || !alpha || !a_in || !a_out)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, the three FC weights and the three outputs must not be NULL");
+    const void *ptrs[] = {x, fc_w, fc_b, fc_w_in, fc_b_in, fc_w_out, fc_b_out, alpha, a_in, a_out};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (mode != DYNCONV_SIGMOID && mode != DYNCONV_SOFTMAX)
+        return fail(DYNCONV_ERR_INVALID_ARG, "mode %d is not a dynconv_route_mode_t", mode);
+    if (mode == DYNCONV_SOFTMAX && !(temperature > 0.f && std::isfinite(temperature)))
+        return fail(DYNCONV_ERR_INVALID_ARG, "softmax temperature must be finite and > 0");
+    if (g.n > 256 || g.Cin > 256 || d_cout(desc) > 256)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "attention routing supports n, Cin and Cout <= 256 (got %d, %d, %d)",
+                    g.n, g.Cin, d_cout(desc));
+    const size_t need = dynconv_route_attn_workspace_bytes(desc);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE, "attention routing needs %zu bytes of 16-byte aligned workspace (got %zu)",
                     need, workspace_bytes);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *ws = static_cast<char *>(workspace);
-    hipError_t e;
-    if (depthwise(g)) {
-        const void *wm = nullptr;
-        if (p == DYNCONV_POLICY_PREMIX) {
-            e = dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, ws, st);
-            if (e != hipSuccess) return hip_status(e, "dynconv_forward mix launch");
-            wm = ws;
-        }
-        return hip_status(dynconv::launch_conv_depthwise(g, x, experts, alpha, wm, y, st),
-                          "dynconv_forward depthwise launch");
-    }
-    if (!g.bf16) {
-        e = dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, ws, st);
-        if (e != hipSuccess) return hip_status(e, "dynconv_forward mix launch");
-        return hip_status(dynconv::launch_conv_direct_f32(g, static_cast<const float *>(x),
-                                                          reinterpret_cast<const float *>(ws),
-                                                          static_cast<float *>(y), st),
-                          "dynconv_forward conv launch");
-    }
-    uint16_t *packed = reinterpret_cast<uint16_t *>(ws);
-    e = dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), packed, st);
-    if (e != hipSuccess) return hip_status(e, "dynconv_forward pack launch");
-    return forward_from_packed(g, p, x, packed, alpha, y,
-                               ws + round_up(dynconv::packed_experts_bytes(g), kWsAlign), st);
+    const float *ws_[3] = {fc_w, fc_w_in, fc_w_out};
+    const float *bs_[3] = {fc_b, fc_b_in, fc_b_out};
+    const int nout[3] = {g.n, g.Cin, d_cout(desc)};
+    const int modes[3] = {mode, DYNCONV_SIGMOID, DYNCONV_SIGMOID};
+    float *outs[3] = {alpha, a_in, a_out};
+    return hip_status(dynconv::launch_route_heads(g, x, 3, ws_, bs_, nout, modes, temperature,
+                                                  static_cast<float *>(workspace), outs,
+                                                  static_cast<hipStream_t>(stream)),
+                      "dynconv_route_attn launch");
 }
 
 size_t dynconv_packed_experts_bytes(const dynconv_desc_t *desc) {

@@ -84,7 +84,7 @@ template <int FM, int FN, int NW, bool PAIRED>
 __global__ __launch_bounds__(NW * 64) void conv_premix_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ wt,
                                                               uint16_t *__restrict__ y,
-                                                              ConvArgs a) {
+                                                              ConvArgs a, const float *__restrict__ a_out) {
     extern __shared__ __attribute__((aligned(16))) uint16_t tile[];
     constexpr int MT = NW * FM * 16;
     constexpr int NT = FN * 16;
@@ -144,6 +144,15 @@ __global__ __launch_bounds__(NW * 64) void conv_premix_kernel(const uint16_t *__
             }
         }
     }
+    if (a_out)  // output attention: a scale of output channel o0 + 16 fn + lr
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const float so = a_out[(long)b * a.Cout + min(o0 + fn * 16 + lr, a.Cout - 1)];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[fm][fn][q] *= so;
+        }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -183,7 +192,8 @@ static_assert(64 * kPmOutPitch * 2 <= 2 * kPmMaxPos * 64, "epilogue rows fit in 
 
 __global__ __launch_bounds__(256) void conv_pm3_kernel(const uint16_t *__restrict__ x,
                                                        const uint16_t *__restrict__ wt,
-                                                       uint16_t *__restrict__ y, ConvArgs a) {
+                                                       uint16_t *__restrict__ y, ConvArgs a,
+                                                       const float *__restrict__ a_out) {
     constexpr int KT = 9, CB = 2, RL = 2;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -344,6 +354,15 @@ __global__ __launch_bounds__(256) void conv_pm3_kernel(const uint16_t *__restric
     // epilogue: D(lane, 4 j + q) = channel o0 + 32 cb + l32, position
     // 32 (wave kPmPB + pb) + 8 j + 4 lh + q of the tile
     lds_barrier();  // last A reads of every wave done
+    if (a_out)  // output attention: a scale of output channel o0 + 32 cb + l32
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const float so = a_out[(long)b * a.Cout + min(o0 + 32 * cb + l32, a.Cout - 1)];
+#pragma unroll
+            for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[pb][cb][q] *= so;
+        }
     uint16_t *s_out = tile_of(0);
 #pragma unroll
     for (int pb = 0; pb < kPmPB; ++pb)
@@ -397,7 +416,8 @@ __device__ __forceinline__ int pm1_off(int c, int q) {
 
 __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restrict__ x,
                                                        const uint16_t *__restrict__ wt,
-                                                       uint16_t *__restrict__ y, ConvArgs a) {
+                                                       uint16_t *__restrict__ y, ConvArgs a,
+                                                       const float *__restrict__ a_out) {
     constexpr int CB = 2;
     constexpr int kLoads = 32 * kPmMT * 2 / 16 / 256;  // 16-byte x loads per thread per chunk (4)
     const int tid = threadIdx.x;
@@ -525,6 +545,15 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
         }
         // epilogue (as the 3x3 kernel): D(lane, 4 j + q) = channel o0 + 32 cb + l32,
         // position 32 (wave kPmPB + pb) + 8 j + 4 lh + q
+        if (a_out)  // output attention
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const float so = a_out[(long)ti.b * a.Cout + min(ti.o0 + 32 * cb + l32, a.Cout - 1)];
+#pragma unroll
+                for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[pb][cb][q] *= so;
+            }
 #pragma unroll
         for (int pb = 0; pb < kPmPB; ++pb)
 #pragma unroll
@@ -565,7 +594,8 @@ constexpr int kPm1xOutPitch = kPmMT + 8;  // bf16 per staged output row
 template <int NCH>
 __global__ __launch_bounds__(256) void conv_pm1x_kernel(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ wt,
-                                                        uint16_t *__restrict__ y, ConvArgs a) {
+                                                        uint16_t *__restrict__ y, ConvArgs a,
+                                                        const float *__restrict__ a_out) {
     constexpr int CB = 2;
     constexpr int kLoads = 32 * kPmMT * 2 / 16 / 256;  // 16-byte x loads per thread per chunk (4)
     __shared__ __attribute__((aligned(16))) u32x4_t s_x[NCH * kPm1Tile / 8];     // NCH x 16 KB
@@ -667,6 +697,15 @@ __global__ __launch_bounds__(256) void conv_pm1x_kernel(const uint16_t *__restri
             for (int c = 0; c < NCH; ++c) wslot(buf ^ 1, c, wave)[lane] = wn[c];
         // epilogue, one 32-channel block per pass: D(lane, 4 j + q) = channel
         // 64 ot + 32 cb + l32, position 32 (wave kPmPB + pb) + 8 j + 4 lh + q
+        if (a_out)  // output attention
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const float so = a_out[(long)b * a.Cout + min(64 * ot + 32 * cb + l32, a.Cout - 1)];
+#pragma unroll
+                for (int pb = 0; pb < kPmPB; ++pb)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) acc[pb][cb][q] *= so;
+            }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -717,7 +756,7 @@ bool paired_ok(const Geom &g) { return (g.W % 2) == 0; }
 
 template <int FM, int FN, int NW>
 hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
-                             hipStream_t stream) {
+                             hipStream_t stream, const float *a_out) {
     ConvArgs a = base_args(g);
     constexpr int MT = NW * FM * 16, NT = FN * 16;
     a.tile_rows = tile_rows_for(g, MT);
@@ -728,11 +767,11 @@ hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *w
     if (paired_ok(g)) {
         auto k = conv_premix_kernel<FM, FN, NW, true>;
         if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a);
+        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a, a_out);
     } else {
         auto k = conv_premix_kernel<FM, FN, NW, false>;
         if (hipError_t e = set_lds(k, lds); e != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a);
+        hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, x, wt, y, a, a_out);
     }
     return hipGetLastError();
 }
@@ -761,16 +800,16 @@ static bool pm1_ok(const Geom &g) {
 }
 
 hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
-                              hipStream_t stream) {
+                              hipStream_t stream, ChanAttn att) {
     if (pm1_ok(g) && g.Cin <= 2 * kChunk) {
         ConvArgs a = base_args(g);
         a.n_ptiles = ceil_div(g.P, kPmMT);
         a.n_otiles = ceil_div(g.Cout, 64);
         const long blocks = (long)g.B * a.n_ptiles;
         if (g.Cin <= kChunk)
-            hipLaunchKernelGGL(conv_pm1x_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+            hipLaunchKernelGGL(conv_pm1x_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
         else
-            hipLaunchKernelGGL(conv_pm1x_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+            hipLaunchKernelGGL(conv_pm1x_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
         return hipGetLastError();
     }
     if (pm1_ok(g)) {
@@ -781,7 +820,7 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
         const long tiles = (long)g.B * a.n_ptiles * a.n_otiles;
         const long blocks = std::min(ceil_div((int)std::min(tiles, (long)INT32_MAX - 8), 8) * 8L,
                                      (long)kCUs * kPm1Resident);
-        hipLaunchKernelGGL(conv_pm1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+        hipLaunchKernelGGL(conv_pm1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
         return hipGetLastError();
     }
     if (pm3_ok(g)) {
@@ -790,13 +829,13 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
         a.n_ptiles = ceil_div(g.P, kPmMT);
         a.n_otiles = ceil_div(g.Cout, 64);
         const long blocks = (long)g.B * a.n_ptiles * a.n_otiles;
-        hipLaunchKernelGGL(conv_pm3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a);
+        hipLaunchKernelGGL(conv_pm3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
         return hipGetLastError();
     }
     const PremixCfg c = pick_premix(g);
     if (c.FM == kPremixLarge.FM)
-        return launch_premix_cfg<kPremixLarge.FM, kPremixLarge.FN, kPremixLarge.NW>(g, x, wt, y, stream);
-    return launch_premix_cfg<kPremixSmall.FM, kPremixSmall.FN, kPremixSmall.NW>(g, x, wt, y, stream);
+        return launch_premix_cfg<kPremixLarge.FM, kPremixLarge.FN, kPremixLarge.NW>(g, x, wt, y, stream, att.out);
+    return launch_premix_cfg<kPremixSmall.FM, kPremixSmall.FN, kPremixSmall.NW>(g, x, wt, y, stream, att.out);
 }
 
 }  // namespace dynconv

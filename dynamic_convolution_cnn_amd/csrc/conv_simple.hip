@@ -23,7 +23,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void conv_direct_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ w, float *__restrict__ y, int B,
-    int Cin, int H, int W, int Cout, int KH, int KW, int stride, int pad, int Ho, int Wo) {
+    int Cin, int H, int W, int Cout, int KH, int KW, int stride, int pad, int Ho, int Wo,
+    const float *__restrict__ a_in, const float *__restrict__ a_out) {
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     const long total = (long)B * Cout * Ho * Wo;
     if (idx >= total) return;
@@ -39,17 +40,18 @@ __global__ __launch_bounds__(256) void conv_direct_f32_kernel(
     for (int c = 0; c < Cin; ++c) {
         const float *xc = xb + (long)c * H * W;
         const float *wc = wo + (long)c * KH * KW;
+        const float si = a_in ? a_in[(long)b * Cin + c] : 1.f;  // input attention
         for (int u = 0; u < KH; ++u) {
             const int h = r * stride - pad + u;
             if (h < 0 || h >= H) continue;
             for (int v = 0; v < KW; ++v) {
                 const int ww = s * stride - pad + v;
                 if (ww < 0 || ww >= W) continue;
-                acc = fmaf(wc[u * KW + v], xc[h * W + ww], acc);
+                acc = fmaf(wc[u * KW + v], si * xc[h * W + ww], acc);
             }
         }
     }
-    y[idx] = acc;
+    y[idx] = a_out ? a_out[(long)b * Cout + o] * acc : acc;  // output attention
 }
 
 constexpr int kDwMaxTaps = 64;
@@ -59,7 +61,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void depthwise_kernel(
     const T *__restrict__ x, const T *__restrict__ experts, const float *__restrict__ alpha,
     const T *__restrict__ wmixed, T *__restrict__ y, int B, int C, int H, int W, int KH, int KW,
-    int stride, int pad, int Ho, int Wo, int n) {
+    int stride, int pad, int Ho, int Wo, int n, const float *__restrict__ a_in,
+    const float *__restrict__ a_out) {
     extern __shared__ __attribute__((aligned(16))) float plane[];
     __shared__ float taps[kDwMaxTaps];
     const int bc = blockIdx.x;
@@ -75,10 +78,12 @@ __global__ __launch_bounds__(256) void depthwise_kernel(
             for (int i = 0; i < n; ++i)
                 s = fmaf(alpha[(long)b * n + i],
                          Elem<T>::to_f32(experts[((long)i * C + c) * KT + threadIdx.x]), s);
-            // mixed kernel in the storage type, as the materialised path would hold it
-            wv = Elem<T>::to_f32(Elem<T>::from_f32(s));
+            wv = s;
         }
-        taps[threadIdx.x] = wv;
+        // channel attentions of a depthwise plane scale its taps; the tap is
+        // held in the storage type, as a materialised kernel would be
+        const float sc = (a_in ? a_in[(long)b * C + c] : 1.f) * (a_out ? a_out[(long)b * C + c] : 1.f);
+        taps[threadIdx.x] = Elem<T>::to_f32(Elem<T>::from_f32(wv * sc));
     }
     const T *xp = x + (long)bc * H * W;
     for (int i = threadIdx.x; i < Hp * Wp; i += 256) {
@@ -131,7 +136,7 @@ template <typename T, int K, int ST>
 __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_strip_kernel(
     const T *__restrict__ x, const T *__restrict__ experts, const float *__restrict__ alpha,
     const T *__restrict__ wmixed, T *__restrict__ y, int B, int C, int H, int W, int pad, int Ho,
-    int Wo, int n, int pitch) {
+    int Wo, int n, int pitch, const float *__restrict__ a_in, const float *__restrict__ a_out) {
     constexpr int KT = K * K;
     constexpr int WIN = dw_win(K, ST);
     extern __shared__ __attribute__((aligned(16))) float planes[];  // kDwPlanes x plane_floats
@@ -176,9 +181,12 @@ __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_strip_kernel(
                 for (int k = 0; k < 8; ++k)
                     if (i0 + k < n) sm = fmaf(av[k], ev[k], sm);
             }
-            wv = Elem<T>::to_f32(Elem<T>::from_f32(sm));  // as the materialised kernel would hold it
+            wv = sm;
         }
-        taps_sh[wave][lane] = wv;
+        // channel attentions of a depthwise plane scale its taps; the tap is
+        // held in the storage type, as a materialised kernel would be
+        const float sc = (a_in ? a_in[(long)b * C + c] : 1.f) * (a_out ? a_out[(long)b * C + c] : 1.f);
+        taps_sh[wave][lane] = Elem<T>::to_f32(Elem<T>::from_f32(wv * sc));
     }
     // zero the padded plane, then the interior
     for (int i = lane; i < Hp * pitch; i += 64) pl[i] = 0.f;
@@ -367,7 +375,7 @@ template <int K, int ST>
 __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_dot2_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ experts, const float *__restrict__ alpha,
     const uint16_t *__restrict__ wmixed, uint16_t *__restrict__ y, int B, int C, int H, int W, int pad,
-    int Ho, int Wo, int n, int pitch) {
+    int Ho, int Wo, int n, int pitch, const float *__restrict__ a_in, const float *__restrict__ a_out) {
     constexpr int KT = K * K;
     constexpr int KP = dw2_pairs(K);
     extern __shared__ __attribute__((aligned(16))) uint32_t dwl[];  // kDwPlanes planes
@@ -397,8 +405,9 @@ __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_dot2_kernel(
         uint16_t tv = 0;
         if (v < K) {
             const int t = u * K + v;
+            float tf;
             if (wmixed) {
-                tv = wmixed[bc * KT + t];
+                tf = bf16_to_f32(wmixed[bc * KT + t]);
             } else {
                 float sm = 0.f;
                 for (int i0 = 0; i0 < n; i0 += 8) {
@@ -413,8 +422,10 @@ __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_dot2_kernel(
                     for (int k = 0; k < 8; ++k)
                         if (i0 + k < n) sm = fmaf(av[k], ev[k], sm);
                 }
-                tv = f32_to_bf16(sm);
+                tf = sm;
             }
+            // channel attentions of a depthwise plane scale its taps (one bf16 rounding)
+            tv = f32_to_bf16(tf * (a_in ? a_in[(long)b * C + c] : 1.f) * (a_out ? a_out[(long)b * C + c] : 1.f));
         }
         reinterpret_cast<uint16_t *>(taps_sh[wave])[lane] = tv;
     }
@@ -467,7 +478,8 @@ constexpr int kDwChanPB = 4;  // examples (planes) per wave
 template <int K, int ST>
 __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_chan_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ experts, const float *__restrict__ alpha,
-    uint16_t *__restrict__ y, int B, int C, int H, int W, int pad, int Ho, int Wo, int n, int pitch) {
+    uint16_t *__restrict__ y, int B, int C, int H, int W, int pad, int Ho, int Wo, int n, int pitch,
+    const float *__restrict__ a_in, const float *__restrict__ a_out) {
     constexpr int KT = K * K;
     constexpr int KP = dw2_pairs(K);
     extern __shared__ __attribute__((aligned(16))) uint32_t dwl[];
@@ -508,8 +520,11 @@ __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_chan_kernel(
             float sm = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) sm = fmaf(av[i], ev[i], sm);
+            // channel attentions of a depthwise plane scale its taps (one bf16 rounding)
+            const uint16_t tv =
+                f32_to_bf16(sm * (a_in ? a_in[(long)b * C + c] : 1.f) * (a_out ? a_out[(long)b * C + c] : 1.f));
             if (lane < K * 2 * KP)
-                reinterpret_cast<uint16_t *>(taps_sh[wave])[lane] = tap_lane ? f32_to_bf16(sm) : (uint16_t)0;
+                reinterpret_cast<uint16_t *>(taps_sh[wave])[lane] = tap_lane ? tv : (uint16_t)0;
         }
         asm volatile("" ::: "memory");
         const uint16_t *xp = x + ((long)b * C + c) * hw;
@@ -549,11 +564,11 @@ __global__ __launch_bounds__(64 * kDwPlanes) void depthwise_chan_kernel(
 }  // namespace
 
 hipError_t launch_conv_direct_f32(const Geom &g, const float *x, const float *wmixed, float *y,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, ChanAttn att) {
     const long total = (long)g.B * g.Cout * g.Ho * g.Wo;
     hipLaunchKernelGGL(conv_direct_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
                        0, stream, x, wmixed, y, g.B, g.Cin, g.H, g.W, g.Cout, g.KH, g.KW,
-                       g.stride, g.pad, g.Ho, g.Wo);
+                       g.stride, g.pad, g.Ho, g.Wo, att.in, att.out);
     return hipGetLastError();
 }
 
@@ -582,14 +597,14 @@ static bool dw_strip_ok(const Geom &g) {
 
 template <typename T>
 static hipError_t launch_dw_strip(const Geom &g, const T *x, const T *experts, const float *alpha,
-                                  const T *wmixed, T *y, hipStream_t stream) {
+                                  const T *wmixed, T *y, hipStream_t stream, ChanAttn att) {
     const long planes = (long)g.B * g.Cin;
     const dim3 grid((unsigned)((planes + kDwPlanes - 1) / kDwPlanes));
     const int pitch = dw_pitch(g);
     const size_t lds = (size_t)kDwPlanes * ((g.Ho - 1) * g.stride + g.KH) * pitch * sizeof(float);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(64 * kDwPlanes), lds, stream, x, experts, alpha, wmixed, y,
-                           g.B, g.Cin, g.H, g.W, g.pad, g.Ho, g.Wo, g.n, pitch);
+                           g.B, g.Cin, g.H, g.W, g.pad, g.Ho, g.Wo, g.n, pitch, att.in, att.out);
         return hipGetLastError();
     };
     const int key = g.KH * 10 + g.stride;
@@ -634,7 +649,7 @@ static hipError_t dw2_dispatch(const Geom &g, F &&go) {
 }
 
 static hipError_t launch_dw2(const Geom &g, const uint16_t *x, const uint16_t *experts, const float *alpha,
-                             const uint16_t *wmixed, uint16_t *y, hipStream_t stream) {
+                             const uint16_t *wmixed, uint16_t *y, hipStream_t stream, ChanAttn att) {
     const int pitch = dw2_pitch(g);
     const size_t lds = (size_t)kDwPlanes * ((g.Ho - 1) * g.stride + g.KH) * pitch * sizeof(uint16_t);
     if (!wmixed && g.n <= 8) {
@@ -643,7 +658,7 @@ static hipError_t launch_dw2(const Geom &g, const uint16_t *x, const uint16_t *e
         return dw2_dispatch(g, [&](auto k, auto st) {
             hipLaunchKernelGGL((depthwise_chan_kernel<decltype(k)::value, decltype(st)::value>), grid,
                                dim3(64 * kDwPlanes), lds, stream, x, experts, alpha, y, g.B, g.Cin, g.H, g.W,
-                               g.pad, g.Ho, g.Wo, g.n, pitch);
+                               g.pad, g.Ho, g.Wo, g.n, pitch, att.in, att.out);
             return hipGetLastError();
         });
     }
@@ -652,26 +667,26 @@ static hipError_t launch_dw2(const Geom &g, const uint16_t *x, const uint16_t *e
     return dw2_dispatch(g, [&](auto k, auto st) {
         hipLaunchKernelGGL((depthwise_dot2_kernel<decltype(k)::value, decltype(st)::value>), grid,
                            dim3(64 * kDwPlanes), lds, stream, x, experts, alpha, wmixed, y, g.B, g.Cin, g.H,
-                           g.W, g.pad, g.Ho, g.Wo, g.n, pitch);
+                           g.W, g.pad, g.Ho, g.Wo, g.n, pitch, att.in, att.out);
         return hipGetLastError();
     });
 }
 
 hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
                                  const float *alpha, const void *wmixed, void *y,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, ChanAttn att) {
     if (dw2_ok(g))
         return launch_dw2(g, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(experts), alpha,
-                          static_cast<const uint16_t *>(wmixed), static_cast<uint16_t *>(y), stream);
+                          static_cast<const uint16_t *>(wmixed), static_cast<uint16_t *>(y), stream, att);
     if (dw_strip_ok(g)) {
         if (g.bf16)
             return launch_dw_strip<uint16_t>(g, static_cast<const uint16_t *>(x),
                                              static_cast<const uint16_t *>(experts), alpha,
                                              static_cast<const uint16_t *>(wmixed),
-                                             static_cast<uint16_t *>(y), stream);
+                                             static_cast<uint16_t *>(y), stream, att);
         return launch_dw_strip<float>(g, static_cast<const float *>(x), static_cast<const float *>(experts),
                                       alpha, static_cast<const float *>(wmixed), static_cast<float *>(y),
-                                      stream);
+                                      stream, att);
     }
     const size_t lds = dw_lds_bytes(g);
     const dim3 grid((unsigned)((long)g.B * g.Cin));
@@ -680,12 +695,12 @@ hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *exper
                            static_cast<const uint16_t *>(x),
                            static_cast<const uint16_t *>(experts), alpha,
                            static_cast<const uint16_t *>(wmixed), static_cast<uint16_t *>(y),
-                           g.B, g.Cin, g.H, g.W, g.KH, g.KW, g.stride, g.pad, g.Ho, g.Wo, g.n);
+                           g.B, g.Cin, g.H, g.W, g.KH, g.KW, g.stride, g.pad, g.Ho, g.Wo, g.n, att.in, att.out);
     } else {
         hipLaunchKernelGGL(depthwise_kernel<float>, grid, dim3(256), lds, stream,
                            static_cast<const float *>(x), static_cast<const float *>(experts),
                            alpha, static_cast<const float *>(wmixed), static_cast<float *>(y),
-                           g.B, g.Cin, g.H, g.W, g.KH, g.KW, g.stride, g.pad, g.Ho, g.Wo, g.n);
+                           g.B, g.Cin, g.H, g.W, g.KH, g.KW, g.stride, g.pad, g.Ho, g.Wo, g.n, att.in, att.out);
     }
     return hipGetLastError();
 }

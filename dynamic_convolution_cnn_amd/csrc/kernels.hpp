@@ -21,6 +21,15 @@ struct Geom {
     bool bf16;    // element type of x, experts, mixed kernels and y
 };
 
+// FMDConv's channel attentions (FMDConv: Fast multi-attention dynamic
+// convolution, abstract): in[b * Cin + c] scales input channel c of example
+// b before the convolution, out[b * Cout + o] scales output channel o after
+// it (float32). Either may be null: all ones.
+struct ChanAttn {
+    const float *in = nullptr;
+    const float *out = nullptr;
+};
+
 // ---- routing -------------------------------------------------------------
 // gap[B*Cin] (float) = channel means of x; then alpha[B,n] from the FC and
 // the nonlinearity. `gap` is caller-provided scratch of B*Cin floats.
@@ -30,6 +39,12 @@ bool route_single_kernel(const Geom &g);
 hipError_t launch_route(const Geom &g, const void *x, const float *fc_w,
                         const float *fc_b, int mode, float temperature,
                         float *gap, float *alpha, hipStream_t stream);
+// GAP into `gap` (B*Cin floats), then nout[h] logits per example for each of
+// `heads` FC heads (fc_w[h]: [nout[h]][Cin], fc_b[h] or null), each through
+// its own nonlinearity mode[h] into out[h] [B][nout[h]]. nout[h] <= 256.
+hipError_t launch_route_heads(const Geom &g, const void *x, int heads, const float *const *fc_w,
+                              const float *const *fc_b, const int *nout, const int *mode,
+                              float temperature, float *gap, float *const *out, hipStream_t stream);
 
 // ---- mixing --------------------------------------------------------------
 // mixed[b, e] = sum_i alpha[b, i] * experts[i, e], natural layout, wsize
@@ -47,14 +62,16 @@ hipError_t launch_pack_experts(const Geom &g, const uint16_t *experts,
 // Mixed kernels in the convolution's layout wt[b][t][o][cp] (bf16) from
 // the packed bank.
 size_t premixed_bytes(const Geom &g);
+// att.in scales the mixed kernels' input channels (att.out is not used).
 hipError_t launch_premix(const Geom &g, const float *alpha, const uint16_t *packed,
-                         uint16_t *wt, hipStream_t stream);
+                         uint16_t *wt, hipStream_t stream, ChanAttn att = {});
 
 // ---- convolution -----------------------------------------------------------
 // Implicit-GEMM bf16 MFMA convolution with mixed kernels read from `wt`.
 bool premix_conv_supported(const Geom &g);
+// att.out scales the output channels (att.in is not used: it is folded into wt).
 hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt,
-                              uint16_t *y, hipStream_t stream);
+                              uint16_t *y, hipStream_t stream, ChanAttn att = {});
 
 // Implicit-GEMM bf16 MFMA convolution that mixes each kernel tile from the
 // packed bank in registers (no mixed kernel in memory).
@@ -65,14 +82,15 @@ hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *p
 // Direct float32 convolution (groups == 1) with mixed kernels in natural
 // layout [B][Cout][Cin][KH][KW].
 hipError_t launch_conv_direct_f32(const Geom &g, const float *x, const float *wmixed,
-                                  float *y, hipStream_t stream);
+                                  float *y, hipStream_t stream, ChanAttn att = {});
 
 // Depthwise convolution (groups == Cin == Cout). With `wmixed` == nullptr
 // each plane's taps are mixed in the kernel from experts and alpha;
 // otherwise they are read from wmixed [B][C][KH][KW].
 bool depthwise_supported(const Geom &g);
+// With attentions, each plane's taps are scaled by in[b,c] * out[b,c].
 hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
                                  const float *alpha, const void *wmixed, void *y,
-                                 hipStream_t stream);
+                                 hipStream_t stream, ChanAttn att = {});
 
 }  // namespace dynconv

@@ -233,9 +233,11 @@ template <int NP2>
 __global__ __launch_bounds__(256) void premix_kernel(const float *__restrict__ alpha,
                                                      const uint32_t *__restrict__ packed,
                                                      uint16_t *__restrict__ wt, int B, int n,
-                                                     long nvec /* KT*Cout*Cin_pad/8 */) {
+                                                     long nvec /* KT*Cout*Cin_pad/8 */,
+                                                     const float *__restrict__ a_in, int Cin, int Cin_pad) {
     const long v = (long)blockIdx.x * 256 + threadIdx.x;
     if (v >= nvec) return;
+    const int cp = (int)((v * 8) % Cin_pad);  // first input channel of this vector
     const int b0 = blockIdx.y * kPremixBT;
     // 8 channels x NP2 words, contiguous
     uint32_t w[8][NP2];
@@ -269,6 +271,9 @@ __global__ __launch_bounds__(256) void premix_kernel(const float *__restrict__ a
             for (int p = 0; p < NP2; ++p) s = dot2(w[c][p], alo[p], s);
             f[c] = s;
         }
+        if (a_in)  // input attention: a scale of the mixed kernel's input channel
+#pragma unroll
+            for (int c = 0; c < 8; ++c) f[c] *= a_in[(long)b * Cin + min(cp + c, Cin - 1)];
         Vec8<uint16_t>::store(wt + ((long)b * nvec + v) * 8, f);
     }
 }
@@ -434,7 +439,8 @@ template <int NKG>
 __global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restrict__ alpha,
                                                           const uint16_t *__restrict__ packed,
                                                           uint16_t *__restrict__ wt, int B, int n, int n_pad,
-                                                          long wsize) {
+                                                          long wsize, const float *__restrict__ a_in, int Cin,
+                                                          int Cin_pad) {
     __shared__ __attribute__((aligned(16))) uint16_t s_o[kMixEx][kMixOutPitch];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const long w0 = (long)blockIdx.x * kMixMW;
@@ -494,6 +500,14 @@ __global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restric
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[nt][g], ap[part][g], acc, 0, 0, 0);
         // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
         // example l32 (one 8-byte LDS write per group j)
+        if (a_in) {
+            // input attention: weight w's input channel is w % Cin_pad (a
+            // 32-aligned weight block holds 32 consecutive channels)
+            const int cb = (int)((w0 + 64 * wave + 32 * nt) % Cin_pad);
+            const float *ai = a_in + (long)min(bc0 + l32, B - 1) * Cin;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] *= ai[min(cb + 8 * (i >> 2) + 4 * lh + (i & 3), Cin - 1)];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             *reinterpret_cast<u32x2_t *>(&s_o[l32][64 * wave + 32 * nt + 8 * j + 4 * lh]) =
@@ -604,14 +618,15 @@ size_t premixed_bytes(const Geom &g) {
 }
 
 hipError_t launch_premix(const Geom &g, const float *alpha, const uint16_t *packed,
-                         uint16_t *wt, hipStream_t stream) {
+                         uint16_t *wt, hipStream_t stream, ChanAttn att) {
     const long nvec = (long)g.KT * g.Cout * g.Cin_pad / 8;
     // matrix-core premix when the padded expert records are 16-byte multiples
     if (g.n_pad % 8 == 0 && g.n_pad <= 16 * kMixMfmaMaxG) {
         const long wsize = nvec * 8;
         const dim3 mgrid((unsigned)((wsize + kMixMW - 1) / kMixMW), (unsigned)((g.B + kMixEx - 1) / kMixEx));
         auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, mgrid, dim3(256), 0, stream, alpha, packed, wt, g.B, g.n, g.n_pad, wsize);
+            hipLaunchKernelGGL(kern, mgrid, dim3(256), 0, stream, alpha, packed, wt, g.B, g.n, g.n_pad, wsize,
+                               att.in, g.Cin, g.Cin_pad);
             return hipGetLastError();
         };
         const int nkg = (g.n_pad + 15) / 16;
@@ -623,14 +638,14 @@ hipError_t launch_premix(const Geom &g, const float *alpha, const uint16_t *pack
     dim3 grid((unsigned)((nvec + 255) / 256), (unsigned)((g.B + kPremixBT - 1) / kPremixBT));
     const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
     switch (g.n_pad / 2) {
-    case 1: hipLaunchKernelGGL(premix_kernel<1>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
-    case 2: hipLaunchKernelGGL(premix_kernel<2>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
-    case 3: hipLaunchKernelGGL(premix_kernel<3>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
-    case 4: hipLaunchKernelGGL(premix_kernel<4>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
-    case 5: hipLaunchKernelGGL(premix_kernel<5>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
-    case 6: hipLaunchKernelGGL(premix_kernel<6>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
-    case 7: hipLaunchKernelGGL(premix_kernel<7>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
-    case 8: hipLaunchKernelGGL(premix_kernel<8>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec); break;
+    case 1: hipLaunchKernelGGL(premix_kernel<1>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
+    case 2: hipLaunchKernelGGL(premix_kernel<2>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
+    case 3: hipLaunchKernelGGL(premix_kernel<3>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
+    case 4: hipLaunchKernelGGL(premix_kernel<4>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
+    case 5: hipLaunchKernelGGL(premix_kernel<5>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
+    case 6: hipLaunchKernelGGL(premix_kernel<6>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
+    case 7: hipLaunchKernelGGL(premix_kernel<7>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
+    case 8: hipLaunchKernelGGL(premix_kernel<8>, grid, dim3(256), 0, stream, alpha, pk, wt, g.B, g.n, nvec, att.in, g.Cin, g.Cin_pad); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

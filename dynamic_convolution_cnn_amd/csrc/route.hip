@@ -386,4 +386,31 @@ hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const f
     return hipGetLastError();
 }
 
+hipError_t launch_route_heads(const Geom &g, const void *x, int heads, const float *const *fc_w,
+                              const float *const *fc_b, const int *nout, const int *mode,
+                              float temperature, float *gap, float *const *out, hipStream_t stream) {
+    const long rows = (long)g.B * g.Cin;
+    const int hw = g.H * g.W;
+    hipError_t e;
+    if (g.bf16) {
+        const uint16_t *xb = static_cast<const uint16_t *>(x);
+        if (hw % 8 == 0) e = launch_gap_vec<uint16_t, 8>(xb, gap, rows, hw, stream);
+        else if (hw % 4 == 0) e = launch_gap_vec<uint16_t, 4>(xb, gap, rows, hw, stream);
+        else e = launch_gap_vec<uint16_t, 1>(xb, gap, rows, hw, stream);
+    } else {
+        const float *xf = static_cast<const float *>(x);
+        if (hw % 4 == 0) e = launch_gap_vec<float, 4>(xf, gap, rows, hw, stream);
+        else e = launch_gap_vec<float, 1>(xf, gap, rows, hw, stream);
+    }
+    if (e != hipSuccess) return e;
+    // one FC + nonlinearity per head, all from the same channel means
+    for (int h = 0; h < heads; ++h) {
+        const float temp = mode[h] == 1 ? temperature : 1.0f;
+        hipLaunchKernelGGL(route_fc_kernel, dim3((g.B + 3) / 4), dim3(256), 0, stream, gap, fc_w[h],
+                           fc_b[h], out[h], g.B, g.Cin, nout[h], mode[h], temp);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace dynconv

@@ -164,6 +164,49 @@ dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t poli
                                         size_t workspace_bytes, void *stream);
 size_t dynconv_forward_packed_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
 
+/* FMDConv's multi-attention layer (FMDConv: Fast multi-attention dynamic
+ * convolution via speed-accuracy trade-off, abstract: input attention,
+ * temperature-degraded kernel attention and output attention). The page
+ * gives no formulas; the reading implemented: each attention is a head of
+ * its own on the layer input's global average pool (an FC with bias), the
+ * kernel attention with `mode` (softmax(z/T) for the temperature form), the
+ * input and output attentions with a sigmoid; the input attention scales the
+ * example's input channels before the convolution and the output attention
+ * its output channels after it:
+ *   y[b,o] = a_out[b,o] * conv(a_in[b,:] * x[b], sum_i alpha[b,i] E_i)[o].
+ *
+ * dynconv_route_attn: the three heads from one pooling of x [B,Cin,H,W]
+ * (dtype). fc_w [n,Cin], fc_w_in [Cin,Cin], fc_w_out [Cout,Cin] float32,
+ * row-major; the biases fc_b [n], fc_b_in [Cin], fc_b_out [Cout] may be NULL.
+ * Writes alpha [B,n], a_in [B,Cin], a_out [B,Cout] (float32). n, Cin and Cout
+ * <= 256 (DYNCONV_ERR_UNSUPPORTED otherwise). workspace: at least
+ * dynconv_route_attn_workspace_bytes(desc) bytes (the B*Cin channel means;
+ * clobbered). Reads desc->B, Cin, H, W, Cout, n, dtype (and checks the rest
+ * of the layer description as dynconv_forward does). */
+dynconv_status_t dynconv_route_attn(const dynconv_desc_t *desc, const void *x,
+                                    const float *fc_w, const float *fc_b, int32_t mode,
+                                    float temperature, const float *fc_w_in, const float *fc_b_in,
+                                    const float *fc_w_out, const float *fc_b_out, float *alpha,
+                                    float *a_in, float *a_out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+size_t dynconv_route_attn_workspace_bytes(const dynconv_desc_t *desc);
+
+/* dynconv_forward with the channel attentions a_in [B,Cin] and a_out
+ * [B,Cout] (float32; either may be NULL, meaning all ones). bf16 layers with
+ * groups == 1 run on DYNCONV_POLICY_PREMIX (AUTO resolves to it; FUSED
+ * returns DYNCONV_ERR_UNSUPPORTED): the input attention scales the premixed
+ * kernels' input channels before their bf16 rounding and the output
+ * attention scales the accumulators before the bf16 output. Depthwise layers
+ * scale each plane's taps by a_in[b,c] * a_out[b,c] before their rounding to
+ * the storage type; float32 layers scale the input values and the sums.
+ * workspace: at least dynconv_forward_attn_workspace_bytes(desc, policy)
+ * bytes. Other arguments, errors and determinism as dynconv_forward. */
+dynconv_status_t dynconv_forward_attn(const dynconv_desc_t *desc, int32_t policy, const void *x,
+                                      const void *experts, const float *alpha, const float *a_in,
+                                      const float *a_out, void *y, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+size_t dynconv_forward_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
+
 /* The policy DYNCONV_POLICY_AUTO resolves to for this layer
  * (DYNCONV_POLICY_PREMIX or DYNCONV_POLICY_FUSED), or -1 for an invalid or
  * unsupported descriptor. */

@@ -188,3 +188,54 @@ def test_pack_and_forward_packed_checks():
     assert fp(ctypes.byref(d), bd.DYNCONV_POLICY_PREMIX, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
               None) == bd.DYNCONV_ERR_WORKSPACE
     assert bd.dynconv_forward_packed_workspace_bytes(d, bd.DYNCONV_POLICY_FUSED) == 0
+
+
+def test_route_attn_checks():
+    L = _lib()
+    d = good_desc()
+    ws = bd.dynconv_route_attn_workspace_bytes(d)
+    assert ws >= d.B * d.Cin * 4  # the channel means, also for large batches
+    assert bd.dynconv_route_attn_workspace_bytes(good_desc(B=256)) >= 256 * d.Cin * 4
+
+    def route(desc=d, x=FAKE, w=FAKE, b=FAKE, mode=0, t=1.0, wi=FAKE, bi=FAKE, wo=FAKE, bo=FAKE,
+              a=FAKE, ai=FAKE, ao=FAKE, wsp=FAKE, wsb=ws):
+        return L.dynconv_route_attn(ctypes.byref(desc) if desc is not None else None, x, w, b, mode,
+                                    t, wi, bi, wo, bo, a, ai, ao, wsp, wsb, None)
+
+    assert route(desc=None) == bd.DYNCONV_ERR_INVALID_ARG
+    for kw in ("x", "w", "wi", "wo", "a", "ai", "ao"):
+        assert route(**{kw: None}) == bd.DYNCONV_ERR_INVALID_ARG, kw
+        assert route(**{kw: MISALIGNED}) == bd.DYNCONV_ERR_INVALID_ARG, kw
+    for kw in ("b", "bi", "bo"):
+        assert route(**{kw: MISALIGNED}) == bd.DYNCONV_ERR_INVALID_ARG, kw
+    assert route(mode=2) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(mode=1, t=0.0) == bd.DYNCONV_ERR_INVALID_ARG
+    assert route(wsb=ws - 1) == bd.DYNCONV_ERR_WORKSPACE
+    assert route(wsp=None) == bd.DYNCONV_ERR_WORKSPACE
+    assert route(desc=good_desc(Cin=288, Cout=16)) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert route(desc=good_desc(Cout=300)) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert route(desc=good_desc(n=257)) == bd.DYNCONV_ERR_UNSUPPORTED
+
+
+def test_forward_attn_checks():
+    L = _lib()
+    d = good_desc()
+
+    def fwd_attn(desc=d, policy=bd.DYNCONV_POLICY_AUTO, x=FAKE, e=FAKE, a=FAKE, ai=FAKE, ao=FAKE, y=FAKE,
+                 wsp=FAKE, wsb=None):
+        if wsb is None:
+            wsb = bd.dynconv_forward_attn_workspace_bytes(desc, policy)
+        return L.dynconv_forward_attn(ctypes.byref(desc), policy, x, e, a, ai, ao, y, wsp, wsb, None)
+
+    # bf16 groups == 1: the attentions run on the PREMIX policy
+    assert bd.dynconv_forward_attn_workspace_bytes(d) == bd.dynconv_forward_workspace_bytes(
+        d, bd.DYNCONV_POLICY_PREMIX)
+    assert bd.dynconv_forward_attn_workspace_bytes(d, bd.DYNCONV_POLICY_FUSED) == 0
+    assert fwd_attn(policy=bd.DYNCONV_POLICY_FUSED, wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert fwd_attn(ai=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fwd_attn(ao=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fwd_attn(x=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fwd_attn(wsb=bd.dynconv_forward_attn_workspace_bytes(d) - 1) == bd.DYNCONV_ERR_WORKSPACE
+    # depthwise layers keep in-kernel mixing (no workspace)
+    dw = good_desc(Cin=8, Cout=8, groups=8, kh=5, kw=5, pad=2)
+    assert bd.dynconv_forward_attn_workspace_bytes(dw) == 0
