@@ -108,8 +108,14 @@ def cpu_baseline(w, d):
     while True:
         alpha, _, _ = oracle.route(d["x"], d["fc_w"], d["fc_b"], w.route_mode, w.temperature)
         h = d["x"]
-        for L, e in zip(w.layers, d["experts"]):
-            h = oracle.forward(h, e, alpha, L.stride, L.pad, L.groups)
+        if w.attention:
+            a_in, _, _ = oracle.route(d["x"], d["fc_w_in"], d["fc_b_in"], oracle.SIGMOID)
+            a_out, _, _ = oracle.route(d["x"], d["fc_w_out"], d["fc_b_out"], oracle.SIGMOID)
+            L = w.layers[0]
+            h = oracle.forward_attn(h, d["experts"][0], alpha, a_in, a_out, L.stride, L.pad, L.groups)
+        else:
+            for L, e in zip(w.layers, d["experts"]):
+                h = oracle.forward(h, e, alpha, L.stride, L.pad, L.groups)
         batches += 1
         dt = time.perf_counter() - t0
         if dt >= CPU_SAMPLE_SECONDS:
@@ -153,6 +159,15 @@ def main():
     for L, e in zip(w.layers, experts):
         desc = bd.make_desc(w.B, L.Cin, L.H, L.W, L.Cout, L.k, L.k, L.stride, L.pad, L.groups, w.n,
                             bd.DYNCONV_BF16 if w.dtype == "bf16" else bd.DYNCONV_F32)
+        if w.attention:  # channel attentions: the forward packs its bank itself (PREMIX policy)
+            descs.append(desc)
+            pols.append(bd.DYNCONV_POLICY_PREMIX if L.groups == 1 else bd.dynconv_forward_policy(desc))
+            packed.append(None)
+            nb = bd.dynconv_forward_attn_workspace_bytes(desc, pols[-1])
+            ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
+            outs.append([torch.empty((w.B, L.Cout, L.Ho, L.Wo), dtype=x0.dtype, device=dev)
+                         for _ in range(R)])
+            continue
         pol = bd.dynconv_forward_policy(desc)
         pk = bd.dynconv_packed_experts_bytes(desc)
         packed.append(torch.empty(pk, dtype=torch.uint8, device=dev) if pk else None)
@@ -165,30 +180,50 @@ def main():
         pols.append(pol)
     alphas = [torch.empty((w.B, w.n), dtype=torch.float32, device=dev) for _ in range(R)]
     route_ws = torch.empty(bd.dynconv_route_workspace_bytes(descs[0]), dtype=torch.uint8, device=dev)
+    if w.attention:
+        L0 = w.layers[0]
+        heads = [to_dev(d[k], "f32") for k in ("fc_w_in", "fc_b_in", "fc_w_out", "fc_b_out")]
+        a_ins = [torch.empty((w.B, L0.Cin), dtype=torch.float32, device=dev) for _ in range(R)]
+        a_outs = [torch.empty((w.B, L0.Cout), dtype=torch.float32, device=dev) for _ in range(R)]
+        route_ws = torch.empty(bd.dynconv_route_attn_workspace_bytes(descs[0]), dtype=torch.uint8,
+                               device=dev)
+
+    def route(s):
+        if w.attention:
+            bd.dynconv_route_attn(xs[s], w.layers[0].Cout, fc_w, fc_b, *heads, mode=w.route_mode,
+                                  temperature=w.temperature, alpha=alphas[s], a_in=a_ins[s],
+                                  a_out=a_outs[s], workspace=route_ws)
+        else:
+            bd.dynconv_route(xs[s], fc_w, fc_b, w.route_mode, w.temperature, alpha=alphas[s],
+                             workspace=route_ws)
+
+    def forward(li, h, s):
+        L = w.layers[li]
+        if w.attention:
+            bd.dynconv_forward_attn(h, experts[li], alphas[s], a_ins[s], a_outs[s], L.stride, L.pad,
+                                    L.groups, policy=pols[li], y=outs[li][s], workspace=ws[li])
+        elif packed[li] is not None:
+            bd.dynconv_forward_packed(descs[li], h, packed[li], alphas[s], policy=pols[li],
+                                      y=outs[li][s], workspace=ws[li])
+        else:
+            bd.dynconv_forward(h, experts[li], alphas[s], L.stride, L.pad, L.groups, policy=pols[li],
+                               y=outs[li][s], workspace=ws[li])
 
     def step(i, ev=None):
         s = i % R
         cur = torch.cuda.current_stream()  # the capture stream inside a graph
         if ev is not None:
             ev[0].record(cur)
-        bd.dynconv_route(xs[s], fc_w, fc_b, w.route_mode, w.temperature, alpha=alphas[s],
-                         workspace=route_ws)
+        route(s)
         if ev is not None:
             ev[1].record(cur)
         h = xs[s]
         for li, desc in enumerate(descs):
             if packed[li] is not None:
                 bd.dynconv_pack_experts(desc, experts[li], packed[li])
-                if ev is not None and li == 0:
-                    ev[2].record(cur)
-                bd.dynconv_forward_packed(desc, h, packed[li], alphas[s], policy=pols[li],
-                                          y=outs[li][s], workspace=ws[li])
-            else:
-                if ev is not None and li == 0:
-                    ev[2].record(cur)
-                bd.dynconv_forward(h, experts[li], alphas[s], w.layers[li].stride,
-                                   w.layers[li].pad, w.layers[li].groups, policy=pols[li],
-                                   y=outs[li][s], workspace=ws[li])
+            if ev is not None and li == 0:
+                ev[2].record(cur)
+            forward(li, h, s)
             if ev is not None and li == 0:
                 ev[3].record(cur)
             h = outs[li][s]
@@ -236,14 +271,7 @@ def main():
     h0 = [xs[s] for s in range(R)]
 
     def fwd0(i):
-        s = i % R
-        if packed[0] is not None:
-            bd.dynconv_forward_packed(descs[0], h0[s], packed[0], alphas[s], policy=pols[0],
-                                      y=outs[0][s], workspace=ws[0])
-        else:
-            L = w.layers[0]
-            bd.dynconv_forward(h0[s], experts[0], alphas[s], L.stride, L.pad, L.groups,
-                               policy=pols[0], y=outs[0][s], workspace=ws[0])
+        forward(0, h0[i % R], i % R)
 
     NC = 2 if args.profile else 20
     gc = capture(0, G, fwd0)
@@ -329,6 +357,7 @@ def main():
                                    pad=L.pad, groups=L.groups) for L in w.layers],
                    "routing": "softmax(z/T)" if w.route_mode else "sigmoid",
                    "policy": [pol_name.get(p, str(p)) for p in pols],
+                   "attention": w.attention,
                    "rotating_sets": R},
         "tflops_step": round(flops_all / (ms_per_step * 1e-3) / 1e12, 2),
         "pct_bf16_peak_step": round(100 * flops_all / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),

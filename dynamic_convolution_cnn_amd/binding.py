@@ -246,16 +246,20 @@ def dynconv_route_attn_workspace_bytes(desc: dynconv_desc_t) -> int:
 def dynconv_route_attn(x: torch.Tensor, Cout: int, fc_w: torch.Tensor, fc_b: Optional[torch.Tensor],
                        fc_w_in: torch.Tensor, fc_b_in: Optional[torch.Tensor], fc_w_out: torch.Tensor,
                        fc_b_out: Optional[torch.Tensor], mode: int = DYNCONV_SIGMOID,
-                       temperature: float = 1.0, workspace: Optional[torch.Tensor] = None,
-                       stream=None):
+                       temperature: float = 1.0, alpha: Optional[torch.Tensor] = None,
+                       a_in: Optional[torch.Tensor] = None, a_out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
     """FMDConv's three attentions from one pooling of x: (alpha [B, n], a_in [B, Cin],
     a_out [B, Cout]), float32."""
     B, Cin, H, W = x.shape
     n = fc_w.shape[0]
     desc = make_desc(B, Cin, H, W, Cout, 1, 1, 1, 0, 1, n, _dtype_code(x))
-    alpha = torch.empty((B, n), dtype=torch.float32, device=x.device)
-    a_in = torch.empty((B, Cin), dtype=torch.float32, device=x.device)
-    a_out = torch.empty((B, Cout), dtype=torch.float32, device=x.device)
+    if alpha is None:
+        alpha = torch.empty((B, n), dtype=torch.float32, device=x.device)
+    if a_in is None:
+        a_in = torch.empty((B, Cin), dtype=torch.float32, device=x.device)
+    if a_out is None:
+        a_out = torch.empty((B, Cout), dtype=torch.float32, device=x.device)
     ws, ws_bytes = _workspace(dynconv_route_attn_workspace_bytes(desc), x.device, workspace)
     _check(lib().dynconv_route_attn(ctypes.byref(desc), _ptr(x), _ptr(fc_w), _ptr(fc_b), int(mode),
                                     float(temperature), _ptr(fc_w_in), _ptr(fc_b_in), _ptr(fc_w_out),

@@ -342,6 +342,73 @@ hipError_t launch_gap_vec(const T *x, float *gap, long rows, int hw, hipStream_t
     }
 }
 
+
+// Several FC heads on the channel means, for FMDConv's kernel, input and
+// output attentions. Workgroup (b, j): chunk j of the heads' logits of
+// example b. A head with the softmax (its normalisation spans all its
+// logits) is one chunk of up to 256 logits; a sigmoid head is cut into
+// chunks of 64. Wave w computes the chunk's logits w, w + 4, ..., four at a
+// time with the lanes over channels (coalesced rows of fc_w) and a fixed
+// butterfly per logit; the nonlinearity runs after a barrier.
+constexpr int kHeadsMax = 3;
+struct RouteHeads {
+    const float *w[kHeadsMax];
+    const float *b[kHeadsMax];
+    float *out[kHeadsMax];
+    int n[kHeadsMax], mode[kHeadsMax], first[kHeadsMax + 1];  // first chunk of each head
+    int heads;
+};
+__global__ __launch_bounds__(256) void route_heads_kernel(const float *__restrict__ gap, RouteHeads hp,
+                                                          int C, float temp) {
+    __shared__ float z[256];
+    const int b = blockIdx.x, j = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int h = 0;
+    while (h + 1 < hp.heads && j >= hp.first[h + 1]) ++h;
+    const int n = hp.n[h], mode = hp.mode[h];
+    const int per = mode == 1 ? n : 64;
+    const int i0 = (j - hp.first[h]) * per, cnt = min(per, n - i0);
+    const float *gb = gap + (long)b * C;
+    const float *W = hp.w[h];
+    for (int q = wave * 4; q < cnt; q += 16) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int c = lane; c < C; c += 64) {
+            const float gc = gb[c];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                part[k] = fmaf(W[(long)(i0 + min(q + k, cnt - 1)) * C + c], gc, part[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float t = wave_sum(part[k]);
+            if (lane == 0 && q + k < cnt) z[q + k] = t + (hp.b[h] ? hp.b[h][i0 + q + k] : 0.f);
+        }
+    }
+    __syncthreads();
+    float *out = hp.out[h] + (long)b * n + i0;
+    if (mode == 0) {
+        for (int i = tid; i < cnt; i += 256) {
+            const float v = z[i];
+            float a;
+            if (v >= 0.f) {
+                a = 1.f / (1.f + expf(-v));
+            } else {
+                const float e = expf(v);
+                a = e / (1.f + e);
+            }
+            out[i] = a;
+        }
+    } else if (wave == 0) {
+        float m = -INFINITY;
+        for (int i = lane; i < cnt; i += 64) m = fmaxf(m, z[i] / temp);
+        m = wave_max(m);
+        float s = 0.f;
+        for (int i = lane; i < cnt; i += 64) s += expf(z[i] / temp - m);
+        s = wave_sum(s);
+        for (int i = lane; i < cnt; i += 64) out[i] = expf(z[i] / temp - m) / s;
+    }
+}
+
 }  // namespace
 
 static_assert(kMaxJ * 64 >= 256, "route kernel covers n <= 256");
@@ -389,6 +456,7 @@ hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const f
 hipError_t launch_route_heads(const Geom &g, const void *x, int heads, const float *const *fc_w,
                               const float *const *fc_b, const int *nout, const int *mode,
                               float temperature, float *gap, float *const *out, hipStream_t stream) {
+    if (heads < 1 || heads > kHeadsMax) return hipErrorInvalidValue;
     const long rows = (long)g.B * g.Cin;
     const int hw = g.H * g.W;
     hipError_t e;
@@ -403,14 +471,24 @@ hipError_t launch_route_heads(const Geom &g, const void *x, int heads, const flo
         else e = launch_gap_vec<float, 1>(xf, gap, rows, hw, stream);
     }
     if (e != hipSuccess) return e;
-    // one FC + nonlinearity per head, all from the same channel means
+    // all heads from the same channel means, in one launch
+    RouteHeads hp{};
+    hp.heads = heads;
+    int chunks = 0;
     for (int h = 0; h < heads; ++h) {
-        const float temp = mode[h] == 1 ? temperature : 1.0f;
-        hipLaunchKernelGGL(route_fc_kernel, dim3((g.B + 3) / 4), dim3(256), 0, stream, gap, fc_w[h],
-                           fc_b[h], out[h], g.B, g.Cin, nout[h], mode[h], temp);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (nout[h] < 1 || nout[h] > 256) return hipErrorInvalidValue;
+        hp.w[h] = fc_w[h];
+        hp.b[h] = fc_b[h];
+        hp.out[h] = out[h];
+        hp.n[h] = nout[h];
+        hp.mode[h] = mode[h];
+        hp.first[h] = chunks;
+        chunks += mode[h] == 1 ? 1 : ceil_div(nout[h], 64);
     }
-    return hipSuccess;
+    hp.first[heads] = chunks;
+    hipLaunchKernelGGL(route_heads_kernel, dim3((unsigned)g.B, (unsigned)chunks), dim3(256), 0, stream, gap,
+                       hp, g.Cin, temperature);
+    return hipGetLastError();
 }
 
 }  // namespace dynconv

@@ -80,6 +80,7 @@ class Workload:
     temperature: float = 1.0
     x_relu: bool = False
     fc_std: Optional[float] = 0.1
+    attention: bool = False     # FMDConv input and output attention heads as well
 
     @property
     def route_layer(self) -> Layer:
@@ -121,6 +122,14 @@ WORKLOADS: Dict[str, Workload] = {
         title="many-expert 3x3, B=64, 128->128, 28x28, n=16, softmax(z/4), bf16",
         B=64, n=16, dtype="bf16", route_mode=SOFTMAX, temperature=4.0, fc_std=None,
         layers=(Layer(128, 128, 28, 28, 3, 1, 1),)),
+    # FMDConv's multi-attention layer (input, temperature-scaled kernel and
+    # output attention) on the ResNet-18-shaped 3x3 layer; not one of the
+    # five configurations of the method's hot path
+    "fmdconv_resnet18_3x3": Workload(
+        key="fmdconv_resnet18_3x3",
+        title="FMDConv multi-attention on the ResNet-18-shaped 3x3, B=32, 64->64, 56x56, n=4, softmax(z/4), bf16",
+        B=32, n=4, dtype="bf16", route_mode=SOFTMAX, temperature=4.0, attention=True,
+        layers=(Layer(64, 64, 56, 56, 3, 1, 1),)),
 }
 
 # The order the workloads are listed in: the tiny parity case first, the
@@ -177,8 +186,16 @@ def make_inputs(w: Workload, seed: int = 0, B: Optional[int] = None) -> dict:
         banks.append(_store(e, w.dtype))
     fc_w = rng.standard_normal((w.n, L0.Cin), dtype=np.float32) * np.float32(w.fc_std_value())
     fc_b = np.zeros((w.n,), np.float32)
-    return {"x": _store(x, w.dtype), "experts": banks, "fc_w": fc_w.astype(np.float32),
-            "fc_b": fc_b}
+    out = {"x": _store(x, w.dtype), "experts": banks, "fc_w": fc_w.astype(np.float32), "fc_b": fc_b}
+    if w.attention:
+        # input and output attention heads (FC on the same pooled input), drawn
+        # after everything else so the other draws match a plain workload's
+        Cout = w.layers[-1].Cout
+        for name, m in (("in", L0.Cin), ("out", Cout)):
+            out[f"fc_w_{name}"] = (rng.standard_normal((m, L0.Cin), dtype=np.float32) *
+                                   np.float32(w.fc_std_value())).astype(np.float32)
+            out[f"fc_b_{name}"] = np.zeros((m,), np.float32)
+    return out
 
 
 def layer_input(L: Layer, B: int, dtype: str, seed: int) -> np.ndarray:
