@@ -47,8 +47,8 @@ GRAPH_STEPS = 10                # steps per HIP graph replay in the timed loop
 # for the kernel source it was taken on (sha256 prefix over the files the dominant kernel
 # is compiled from, listed below); otherwise null.
 TRAFFIC = {
-    "resnet50_3x3": {"source_sha": "5bbe5565e16d6a3f",
-                     "fetch_kib": 55057.9, "write_kib": 25088.0,
+    "resnet50_3x3": {"source_sha": "df7b9a8901e9d51d",
+                     "fetch_kib": 55057.8, "write_kib": 25088.0,
                      "fetch_scale": 262144 / 131085, "write_scale": 1.0},
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "dynamic_convolution_cnn_amd", "csrc", f)
