@@ -24,6 +24,10 @@ cites the passage of the pages it follows:
   input and output (FMDConv: Fast multi-attention dynamic convolution,
   abstract, which names them without a formula; the reading is stated at
   ``forward_attn``). Each head is a route (GAP -> FC -> sigmoid) of its own.
+* gradients - the pages train these layers end to end ("learn specialized
+  convolutional kernels", CondConv abstract; "learns a linear mixture",
+  KernelWarehouse abstract) but print no backward pass. ``backward`` and
+  ``route_backward`` write out the derivative of the forward definition.
 
 Parity pins live in ``tests/test_oracle_pins.py``.
 """
@@ -77,8 +81,10 @@ def _load():
     lib.oracle_forward.argtypes = [i32] * 11 + [P, P, P, P]
     lib.oracle_forward_points.argtypes = [i32] * 11 + [P, P, P, i64, P, P]
     lib.oracle_forward_attn.argtypes = [i32] * 11 + [P, P, P, P, P, P]
+    lib.oracle_backward.argtypes = [i32] * 11 + [P, P, P, P, P, P, P]
     for f in (lib.oracle_gap, lib.oracle_route, lib.oracle_mix, lib.oracle_conv,
-              lib.oracle_forward, lib.oracle_forward_points, lib.oracle_forward_attn):
+              lib.oracle_forward, lib.oracle_forward_points, lib.oracle_forward_attn,
+              lib.oracle_backward):
         f.restype = i32
     _lib = lib
     return lib
@@ -232,3 +238,62 @@ def forward_attn(x, experts, alpha, a_in=None, a_out=None, stride: int = 1, pad:
                                      None if ao is None else _ptr(ao), _ptr(y))
     _check(rc, "forward_attn")
     return y
+
+
+def backward(x, experts, alpha, dy, stride: int = 1, pad: int = 0, groups: int = 1,
+             want=("dx", "dalpha", "dexperts")):
+    """Gradients of the layer (``forward``) for the output gradient dy.
+
+    Returns (dx [B,Cin,H,W], dalpha [B,n], dexperts [n,Cout,Cin/g,kh,kw]) in
+    float64; an entry not named in ``want`` is None. Definitions (the
+    derivative of the forward, written out in ``dynconv_oracle.c``):
+    dW_b = sum_{r,s} dy * shifted x;  dalpha[b,i] = <dW_b, E_i>;
+    dE_i = sum_b alpha[b,i] dW_b;  dx = the adjoint of the convolution
+    with W_b applied to dy."""
+    x = _f32(x)
+    experts = _f32(experts)
+    alpha = _f64(alpha)
+    dy = _f32(dy)
+    B, Cin, H, W = x.shape
+    n, Cout, cpg, kh, kw = experts.shape
+    assert alpha.shape == (B, n) and cpg * groups == Cin
+    Ho, Wo = out_size(H, kh, stride, pad), out_size(W, kw, stride, pad)
+    assert dy.shape == (B, Cout, Ho, Wo)
+    dx = np.empty(x.shape, np.float64) if "dx" in want else None
+    da = np.empty((B, n), np.float64) if "dalpha" in want else None
+    de = np.empty(experts.shape, np.float64) if "dexperts" in want else None
+    rc = _load().oracle_backward(B, Cin, H, W, Cout, kh, kw, stride, pad, groups, n,
+                                 _ptr(x), _ptr(experts), _ptr(alpha), _ptr(dy),
+                                 None if dx is None else _ptr(dx),
+                                 None if da is None else _ptr(da),
+                                 None if de is None else _ptr(de))
+    _check(rc, "backward")
+    return dx, da, de
+
+
+def route_backward(x, fc_w, fc_b, dalpha, mode: int = SIGMOID, temperature: float = 1.0):
+    """Gradients of the routing (``route``: GAP -> FC(+bias) -> sigmoid or
+    softmax(z/T)) for the attention gradient dalpha[B, n].
+
+    The derivative of each routing step, in reverse order:
+    sigmoid: dz = dalpha * alpha * (1 - alpha);
+    softmax(z/T): dz_j = alpha_j * (dalpha_j - sum_k alpha_k dalpha_k) / T;
+    dfc_w = dz^T gap, dfc_b = sum_b dz, dgap = dz fc_w, and every position
+    of channel c receives dgap[b, c] / (H W).
+    Returns (dfc_w [n,Cin], dfc_b [n], dgap [B,Cin], dx [B,Cin,H,W]) in float64.
+    """
+    alpha, g, _ = route(x, fc_w, fc_b, mode, temperature)
+    da = _f64(dalpha)
+    assert da.shape == alpha.shape
+    if mode == SIGMOID:
+        dz = da * alpha * (1.0 - alpha)
+    else:
+        inner = np.sum(alpha * da, axis=1, keepdims=True)
+        dz = alpha * (da - inner) / float(temperature)
+    fw = _f64(fc_w)
+    dfc_w = dz.T @ g
+    dfc_b = dz.sum(axis=0)
+    dgap = dz @ fw
+    B, C, H, W = np.shape(x)
+    dx = np.broadcast_to((dgap / float(H * W))[:, :, None, None], (B, C, H, W)).copy()
+    return dfc_w, dfc_b, dgap, dx

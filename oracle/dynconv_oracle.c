@@ -28,7 +28,9 @@
  *
  * Parity is pinned by the not-gpu tests (torch conv2d in float64 for the
  * single-expert case, one-hot selection, brute-force linearity, routing
- * closed forms and a hand-worked example); see the test suite.
+ * closed forms and a hand-worked example); the gradients by torch autograd
+ * in float64, unit-impulse brute force and Euler's identity for the
+ * bilinear layer; see the test suite.
  */
 #include <math.h>
 #include <stddef.h>
@@ -377,5 +379,102 @@ int oracle_forward_attn(int B, int Cin, int H, int W, int Cout, int kh, int kw,
             }
         }
     }
+    return ORACLE_OK;
+}
+
+/*
+ * Gradients of the layer (mix, then per-example convolution) for a given
+ * output gradient dy. The pages train these layers ("learn specialized
+ * convolutional kernels for each example", CondConv abstract; "learns a
+ * linear mixture of n static kernels weighted with their input-dependent
+ * attentions", KernelWarehouse abstract) but print no backward pass; what
+ * follows is the derivative of the forward definition above, term by term.
+ * With W_b = sum_i alpha[b,i] E_i and y = conv(x_b, W_b):
+ *   dW_b[o,c,u,v] = sum_{r,s} dy[b,o,r,s] * x[b, gc, r*st - p + u, s*st - p + v]
+ *   dalpha[b,i]   = sum_e dW_b[e] * E_i[e]
+ *   dE_i[e]       = sum_b alpha[b,i] * dW_b[e]
+ *   dx[b,gc,h,w]  = sum over (o, r, s, u, v) with h = r*st - p + u and
+ *                   w = s*st - p + v of W_b[o,c,u,v] * dy[b,o,r,s]
+ * (gc = (o / (Cout/groups)) * (Cin/groups) + c; positions outside the image
+ * take no part). dx, dalpha and dexperts may each be NULL (not computed).
+ * dy: [B,Cout,Ho,Wo]; dx: [B,Cin,H,W]; dalpha: [B,n]; dexperts: [n, wsize].
+ */
+int oracle_backward(int B, int Cin, int H, int W, int Cout, int kh, int kw,
+                    int stride, int pad, int groups, int n, const float *x,
+                    const float *experts, const double *alpha, const float *dy,
+                    double *dx, double *dalpha, double *dexperts)
+{
+    if (B < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 ||
+        stride < 1 || pad < 0 || groups < 1 || n < 1 || !x || !experts ||
+        !alpha || !dy)
+        return ORACLE_BAD_ARG;
+    if (Cin % groups || Cout % groups) return ORACLE_BAD_ARG;
+    int Ho = out_size(H, kh, stride, pad), Wo = out_size(W, kw, stride, pad);
+    if (Ho < 1 || Wo < 1) return ORACLE_BAD_ARG;
+    int cpg = Cin / groups, opg = Cout / groups;
+    long per_o = (long)cpg * kh * kw;
+    long wsz = (long)Cout * per_o;
+    /* dW_b for every example, then the two contractions over it */
+    double *dwb = (double *)calloc((size_t)B * wsz, sizeof(double));
+    double *wb = (double *)malloc(sizeof(double) * (size_t)B * wsz);
+    if (!dwb || !wb) { free(dwb); free(wb); return ORACLE_BAD_ARG; }
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < B; ++b) {
+        double *w = wb + (long)b * wsz;
+        for (long e = 0; e < wsz; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i)
+                acc += alpha[(long)b * n + i] * (double)experts[(long)i * wsz + e];
+            w[e] = acc;
+        }
+        double *dw = dwb + (long)b * wsz;
+        double *dxb = dx ? dx + (long)b * Cin * H * W : NULL;
+        if (dxb)
+            for (long j = 0; j < (long)Cin * H * W; ++j) dxb[j] = 0.0;
+        for (int o = 0; o < Cout; ++o) {
+            int g = o / opg;
+            for (int r = 0; r < Ho; ++r) {
+                for (int s = 0; s < Wo; ++s) {
+                    double d = (double)dy[(((long)b * Cout + o) * Ho + r) * Wo + s];
+                    for (int c = 0; c < cpg; ++c) {
+                        long xoff = (((long)b * Cin + (long)g * cpg + c) * H) * W;
+                        for (int u = 0; u < kh; ++u) {
+                            int h = r * stride - pad + u;
+                            if (h < 0 || h >= H) continue;
+                            for (int v = 0; v < kw; ++v) {
+                                int ww = s * stride - pad + v;
+                                if (ww < 0 || ww >= W) continue;
+                                long e = (long)o * per_o + ((long)c * kh + u) * kw + v;
+                                dw[e] += d * (double)x[xoff + (long)h * W + ww];
+                                if (dxb)
+                                    dxb[xoff - (long)b * Cin * H * W + (long)h * W + ww] += w[e] * d;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (dalpha) {
+            for (int i = 0; i < n; ++i) {
+                double acc = 0.0;
+                for (long e = 0; e < wsz; ++e)
+                    acc += dw[e] * (double)experts[(long)i * wsz + e];
+                dalpha[(long)b * n + i] = acc;
+            }
+        }
+    }
+    if (dexperts) {
+#pragma omp parallel for schedule(static)
+        for (long e = 0; e < wsz; ++e) {
+            for (int i = 0; i < n; ++i) {
+                double acc = 0.0;
+                for (int b = 0; b < B; ++b)
+                    acc += alpha[(long)b * n + i] * dwb[(long)b * wsz + e];
+                dexperts[(long)i * wsz + e] = acc;
+            }
+        }
+    }
+    free(dwb);
+    free(wb);
     return ORACLE_OK;
 }
