@@ -42,7 +42,10 @@ EXPORTED = (
     "dynconv_last_error", "dynconv_abi_version", "dynconv_packed_experts_bytes",
     "dynconv_pack_experts", "dynconv_forward_packed", "dynconv_forward_packed_workspace_bytes",
     "dynconv_route_attn", "dynconv_route_attn_workspace_bytes", "dynconv_forward_attn",
-    "dynconv_forward_attn_workspace_bytes",
+    "dynconv_forward_attn_workspace_bytes", "dynconv_backward_data",
+    "dynconv_backward_data_workspace_bytes", "dynconv_backward_weights",
+    "dynconv_backward_weights_workspace_bytes", "dynconv_route_backward",
+    "dynconv_route_backward_workspace_bytes",
 )
 
 
@@ -108,6 +111,18 @@ def lib():
     L.dynconv_forward_attn.restype = i32
     L.dynconv_forward_attn_workspace_bytes.argtypes = [D, i32]
     L.dynconv_forward_attn_workspace_bytes.restype = sz
+    L.dynconv_backward_data.argtypes = [D, i32, P, P, P, P, P, sz, P]
+    L.dynconv_backward_data.restype = i32
+    L.dynconv_backward_data_workspace_bytes.argtypes = [D, i32]
+    L.dynconv_backward_data_workspace_bytes.restype = sz
+    L.dynconv_backward_weights.argtypes = [D, P, P, P, P, P, P, P, sz, P]
+    L.dynconv_backward_weights.restype = i32
+    L.dynconv_backward_weights_workspace_bytes.argtypes = [D]
+    L.dynconv_backward_weights_workspace_bytes.restype = sz
+    L.dynconv_route_backward.argtypes = [D, P, P, i32, f32, P, P, P, P, P, P, sz, P]
+    L.dynconv_route_backward.restype = i32
+    L.dynconv_route_backward_workspace_bytes.argtypes = [D]
+    L.dynconv_route_backward_workspace_bytes.restype = sz
     _lib = L
     return L
 
@@ -326,3 +341,73 @@ def dynconv_forward_packed(desc: dynconv_desc_t, x: torch.Tensor, packed: torch.
                                         _ptr(alpha), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "dynconv_forward_packed")
     return y
+
+
+def dynconv_backward_data_workspace_bytes(desc: dynconv_desc_t, policy: int = DYNCONV_POLICY_AUTO) -> int:
+    return int(lib().dynconv_backward_data_workspace_bytes(ctypes.byref(desc), int(policy)))
+
+
+def dynconv_backward_data(dy: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor, H: int, W: int,
+                          stride: int = 1, pad: int = 0, groups: int = 1,
+                          policy: int = DYNCONV_POLICY_AUTO, dx: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Input gradient dx [B, Cin, H, W] of the layer for the output gradient dy."""
+    B = dy.shape[0]
+    n, Cout, cpg, kh, kw = experts.shape
+    desc = make_desc(B, cpg * groups, H, W, Cout, kh, kw, stride, pad, groups, n, _dtype_code(dy))
+    if dx is None:
+        dx = torch.empty((B, cpg * groups, H, W), dtype=dy.dtype, device=dy.device)
+    ws, ws_bytes = _workspace(dynconv_backward_data_workspace_bytes(desc, policy), dy.device, workspace)
+    _check(lib().dynconv_backward_data(ctypes.byref(desc), int(policy), _ptr(dy), _ptr(experts),
+                                       _ptr(alpha), _ptr(dx), _ptr(ws), ws_bytes, _stream(stream)),
+           "dynconv_backward_data")
+    return dx
+
+
+def dynconv_backward_weights_workspace_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_backward_weights_workspace_bytes(ctypes.byref(desc)))
+
+
+def dynconv_backward_weights(x: torch.Tensor, dy: torch.Tensor, experts: torch.Tensor,
+                             alpha: torch.Tensor, stride: int = 1, pad: int = 0, groups: int = 1,
+                             dalpha: Optional[torch.Tensor] = None,
+                             dexperts: Optional[torch.Tensor] = None, want=("dalpha", "dexperts"),
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """(dalpha [B, n], dexperts [n, Cout, Cin/g, kh, kw]), float32; an entry not in
+    ``want`` (and not given) is None."""
+    desc = layer_desc(x, experts, stride, pad, groups)
+    if dalpha is None and "dalpha" in want:
+        dalpha = torch.empty((desc.B, desc.n), dtype=torch.float32, device=x.device)
+    if dexperts is None and "dexperts" in want:
+        dexperts = torch.empty(tuple(experts.shape), dtype=torch.float32, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_backward_weights_workspace_bytes(desc), x.device, workspace)
+    _check(lib().dynconv_backward_weights(ctypes.byref(desc), _ptr(x), _ptr(dy), _ptr(experts),
+                                          _ptr(alpha), _ptr(dalpha), _ptr(dexperts), _ptr(ws), ws_bytes,
+                                          _stream(stream)), "dynconv_backward_weights")
+    return dalpha, dexperts
+
+
+def dynconv_route_backward_workspace_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_route_backward_workspace_bytes(ctypes.byref(desc)))
+
+
+def dynconv_route_backward(x: torch.Tensor, fc_w: torch.Tensor, alpha: torch.Tensor,
+                           dalpha: torch.Tensor, mode: int = DYNCONV_SIGMOID,
+                           temperature: float = 1.0, dx: Optional[torch.Tensor] = None,
+                           dfc_w: Optional[torch.Tensor] = None, dfc_b: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """(dfc_w [n, Cin], dfc_b [n]) of the routing; when dx is given, the pooling's
+    share dgap / (H W) is added to it in place."""
+    B, Cin, H, W = x.shape
+    n = fc_w.shape[0]
+    desc = make_desc(B, Cin, H, W, n=n, dtype=_dtype_code(x))
+    if dfc_w is None:
+        dfc_w = torch.empty((n, Cin), dtype=torch.float32, device=x.device)
+    if dfc_b is None:
+        dfc_b = torch.empty((n,), dtype=torch.float32, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_route_backward_workspace_bytes(desc), x.device, workspace)
+    _check(lib().dynconv_route_backward(ctypes.byref(desc), _ptr(x), _ptr(fc_w), int(mode),
+                                        float(temperature), _ptr(alpha), _ptr(dalpha), _ptr(dfc_w),
+                                        _ptr(dfc_b), _ptr(dx), _ptr(ws), ws_bytes, _stream(stream)),
+           "dynconv_route_backward")
+    return dfc_w, dfc_b

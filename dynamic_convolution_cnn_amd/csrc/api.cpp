@@ -223,6 +223,39 @@ dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const 
                                ws + round_up(dynconv::packed_experts_bytes(g), kWsAlign), st, att);
 }
 
+// The input gradient of a stride-1 layer is the forward layer applied to
+// dy with the transposed, flipped bank and padding k - 1 - p: `t` is that
+// layer's descriptor (input dy [B,Cout,Ho,Wo], output dx [B,Cin,H,W]).
+dynconv_status_t backward_data_desc(const dynconv_desc_t *desc, dynconv::Geom &g, dynconv_desc_t &t) {
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (g.stride != 1)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "backward_data: only stride 1 is implemented (got %d)", g.stride);
+    if (g.KH != g.KW)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "backward_data: square kernels only (got %dx%d)", g.KH, g.KW);
+    if (g.pad > g.KH - 1)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "backward_data: pad %d exceeds kernel size - 1", g.pad);
+    t = *desc;
+    t.Cin = desc->Cout;
+    t.Cout = desc->Cin;
+    t.H = g.Ho;
+    t.W = g.Wo;
+    t.pad = g.KH - 1 - g.pad;
+    dynconv::Geom gt;
+    return check_desc(&t, gt, true);
+}
+
+size_t flipped_bytes(const dynconv::Geom &g) {
+    return round_up((size_t)g.n * kernel_elems(g) * esize(g), kWsAlign);
+}
+
+size_t backward_weights_ws(const dynconv::Geom &g) { return round_up(dynconv::wgrad_bytes(g), kWsAlign); }
+
+size_t route_backward_ws(const dynconv::Geom &g) {
+    return 2 * round_up((size_t)g.B * g.Cin * sizeof(float), kWsAlign) +
+           round_up((size_t)g.B * g.n * sizeof(float), kWsAlign);
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,6 +459,115 @@ dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t poli
                     need, workspace_bytes);
     return forward_from_packed(g, p, x, static_cast<const uint16_t *>(packed), alpha, y,
                                static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+}
+
+size_t dynconv_backward_data_workspace_bytes(const dynconv_desc_t *desc, int32_t policy) {
+    dynconv::Geom g;
+    dynconv_desc_t t;
+    if (backward_data_desc(desc, g, t) != DYNCONV_OK) return 0;
+    const size_t fw = dynconv_forward_workspace_bytes(&t, policy);
+    dynconv::Geom gt;
+    int32_t p;
+    if (check_desc(&t, gt, true) != DYNCONV_OK || resolve_policy(gt, policy, p) != DYNCONV_OK) return 0;
+    return flipped_bytes(g) + fw;
+}
+
+dynconv_status_t dynconv_backward_data(const dynconv_desc_t *desc, int32_t policy, const void *dy,
+                                       const void *experts, const float *alpha, void *dx, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    dynconv::Geom g;
+    dynconv_desc_t t;
+    dynconv_status_t s = backward_data_desc(desc, g, t);
+    if (s != DYNCONV_OK) return s;
+    if (!dy || !experts || !alpha || !dx)
+        return fail(DYNCONV_ERR_INVALID_ARG, "dy, experts, alpha and dx must not be NULL");
+    if (!aligned16(dy) || !aligned16(experts) || !aligned16(alpha) || !aligned16(dx))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    dynconv::Geom gt;
+    int32_t p;
+    s = check_desc(&t, gt, true);
+    if (s != DYNCONV_OK) return s;
+    s = resolve_policy(gt, policy, p);
+    if (s != DYNCONV_OK) return s;
+    const size_t flip = flipped_bytes(g);
+    const size_t need = flip + forward_ws(gt, p);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE, "backward_data needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    s = hip_status(dynconv::launch_flip_experts(g, experts, ws, st), "backward_data flip launch");
+    if (s != DYNCONV_OK) return s;
+    return forward_impl(&t, policy, dy, ws, alpha, dx, ws + flip, workspace_bytes - flip, stream, {});
+}
+
+size_t dynconv_backward_weights_workspace_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK) return 0;
+    return backward_weights_ws(g);
+}
+
+dynconv_status_t dynconv_backward_weights(const dynconv_desc_t *desc, const void *x, const void *dy,
+                                          const void *experts, const float *alpha, float *dalpha,
+                                          float *dexperts, void *workspace, size_t workspace_bytes,
+                                          void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !dy || !experts || !alpha)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, dy, experts and alpha must not be NULL");
+    if (!dalpha && !dexperts)
+        return fail(DYNCONV_ERR_INVALID_ARG, "dalpha and dexperts are both NULL: nothing to compute");
+    const void *ptrs[] = {x, dy, experts, alpha, dalpha, dexperts};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (g.B > 65535) return fail(DYNCONV_ERR_UNSUPPORTED, "backward_weights supports B <= 65535 (got %d)", g.B);
+    if (depthwise(g) && !dynconv::wgrad_dw_supported(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "depthwise backward_weights supports up to 64 kernel taps");
+    const size_t need = backward_weights_ws(g);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE, "backward_weights needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    return hip_status(dynconv::launch_backward_weights(g, x, dy, experts, alpha, static_cast<float *>(workspace),
+                                                       dalpha, dexperts, static_cast<hipStream_t>(stream)),
+                      "dynconv_backward_weights launch");
+}
+
+size_t dynconv_route_backward_workspace_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, false) != DYNCONV_OK) return 0;
+    return route_backward_ws(g);
+}
+
+dynconv_status_t dynconv_route_backward(const dynconv_desc_t *desc, const void *x, const float *fc_w,
+                                        int32_t mode, float temperature, const float *alpha,
+                                        const float *dalpha, float *dfc_w, float *dfc_b, void *dx,
+                                        void *workspace, size_t workspace_bytes, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, false);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !fc_w || !alpha || !dalpha || !dfc_w)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, fc_w, alpha, dalpha and dfc_w must not be NULL");
+    const void *ptrs[] = {x, fc_w, alpha, dalpha, dfc_w, dfc_b, dx};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (mode != DYNCONV_SIGMOID && mode != DYNCONV_SOFTMAX)
+        return fail(DYNCONV_ERR_INVALID_ARG, "mode %d is not a dynconv_route_mode_t", mode);
+    if (mode == DYNCONV_SOFTMAX && !(temperature > 0.f && std::isfinite(temperature)))
+        return fail(DYNCONV_ERR_INVALID_ARG, "softmax temperature must be finite and > 0");
+    if (g.n > 256) return fail(DYNCONV_ERR_UNSUPPORTED, "routing supports n <= 256 experts (got %d)", g.n);
+    const size_t need = route_backward_ws(g);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE, "route_backward needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    char *ws = static_cast<char *>(workspace);
+    const size_t bc = round_up((size_t)g.B * g.Cin * sizeof(float), kWsAlign);
+    float *gap = reinterpret_cast<float *>(ws);
+    float *dgap = reinterpret_cast<float *>(ws + bc);
+    float *dz = reinterpret_cast<float *>(ws + 2 * bc);
+    return hip_status(dynconv::launch_route_backward(g, x, fc_w, mode, temperature, alpha, dalpha, gap, dz, dgap,
+                                                     dfc_w, dfc_b, dx, static_cast<hipStream_t>(stream)),
+                      "dynconv_route_backward launch");
 }
 
 }  // extern "C"

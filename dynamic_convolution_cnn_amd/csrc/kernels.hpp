@@ -39,6 +39,8 @@ bool route_single_kernel(const Geom &g);
 hipError_t launch_route(const Geom &g, const void *x, const float *fc_w,
                         const float *fc_b, int mode, float temperature,
                         float *gap, float *alpha, hipStream_t stream);
+// Channel means of x into gap[B*Cin] (float).
+hipError_t launch_gap(const Geom &g, const void *x, float *gap, hipStream_t stream);
 // GAP into `gap` (B*Cin floats), then nout[h] logits per example for each of
 // `heads` FC heads (fc_w[h]: [nout[h]][Cin], fc_b[h] or null), each through
 // its own nonlinearity mode[h] into out[h] [B][nout[h]]. nout[h] <= 256.
@@ -92,5 +94,30 @@ bool depthwise_supported(const Geom &g);
 hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
                                  const float *alpha, const void *wmixed, void *y,
                                  hipStream_t stream, ChanAttn att = {});
+
+// ---- gradients ---------------------------------------------------------------
+// Bank transposed in its channels and flipped in its taps: for groups == 1
+// flipped[i][c][o][u][v] = experts[i][o][c][KH-1-u][KW-1-v]; depthwise
+// flipped[i][c][0][u][v] = experts[i][c][0][KH-1-u][KW-1-v]. Element type
+// per g.bf16. The forward layer with this bank and padding k - 1 - p,
+// applied to dy, is the input gradient of a stride-1 layer.
+hipError_t launch_flip_experts(const Geom &g, const void *experts, void *flipped, hipStream_t stream);
+
+// Per-example kernel gradients dW_b (float32, [B][Cout][Cin/g][KH][KW]) of
+// x and dy (element type per g.bf16), then dalpha[B][n] = <dW_b, E_i> and
+// dexperts[n][...] = sum_b alpha[b][i] dW_b (either output may be null).
+size_t wgrad_bytes(const Geom &g);
+bool wgrad_dw_supported(const Geom &g);
+hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy, const void *experts,
+                                   const float *alpha, float *dwb, float *dalpha, float *dexperts,
+                                   hipStream_t stream);
+
+// Routing gradient: gap (B*Cin), dz (B*n) and dgap (B*Cin) are scratch;
+// dfc_w[n][Cin], dfc_b[n] (may be null) are written; when dx is not null,
+// dgap[b][c] / (H W) is added to every position of dx[b][c] (one rounding
+// to the element type). mode 0 = sigmoid, 1 = softmax(z / temperature).
+hipError_t launch_route_backward(const Geom &g, const void *x, const float *fc_w, int mode, float temperature,
+                                 const float *alpha, const float *dalpha, float *gap, float *dz, float *dgap,
+                                 float *dfc_w, float *dfc_b, void *dx, hipStream_t stream);
 
 }  // namespace dynconv

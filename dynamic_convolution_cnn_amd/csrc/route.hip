@@ -453,23 +453,25 @@ hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const f
     return hipGetLastError();
 }
 
+hipError_t launch_gap(const Geom &g, const void *x, float *gap, hipStream_t stream) {
+    const long rows = (long)g.B * g.Cin;
+    const int hw = g.H * g.W;
+    if (g.bf16) {
+        const uint16_t *xb = static_cast<const uint16_t *>(x);
+        if (hw % 8 == 0) return launch_gap_vec<uint16_t, 8>(xb, gap, rows, hw, stream);
+        if (hw % 4 == 0) return launch_gap_vec<uint16_t, 4>(xb, gap, rows, hw, stream);
+        return launch_gap_vec<uint16_t, 1>(xb, gap, rows, hw, stream);
+    }
+    const float *xf = static_cast<const float *>(x);
+    if (hw % 4 == 0) return launch_gap_vec<float, 4>(xf, gap, rows, hw, stream);
+    return launch_gap_vec<float, 1>(xf, gap, rows, hw, stream);
+}
+
 hipError_t launch_route_heads(const Geom &g, const void *x, int heads, const float *const *fc_w,
                               const float *const *fc_b, const int *nout, const int *mode,
                               float temperature, float *gap, float *const *out, hipStream_t stream) {
     if (heads < 1 || heads > kHeadsMax) return hipErrorInvalidValue;
-    const long rows = (long)g.B * g.Cin;
-    const int hw = g.H * g.W;
-    hipError_t e;
-    if (g.bf16) {
-        const uint16_t *xb = static_cast<const uint16_t *>(x);
-        if (hw % 8 == 0) e = launch_gap_vec<uint16_t, 8>(xb, gap, rows, hw, stream);
-        else if (hw % 4 == 0) e = launch_gap_vec<uint16_t, 4>(xb, gap, rows, hw, stream);
-        else e = launch_gap_vec<uint16_t, 1>(xb, gap, rows, hw, stream);
-    } else {
-        const float *xf = static_cast<const float *>(x);
-        if (hw % 4 == 0) e = launch_gap_vec<float, 4>(xf, gap, rows, hw, stream);
-        else e = launch_gap_vec<float, 1>(xf, gap, rows, hw, stream);
-    }
+    hipError_t e = launch_gap(g, x, gap, stream);
     if (e != hipSuccess) return e;
     // all heads from the same channel means, in one launch
     RouteHeads hp{};

@@ -207,6 +207,70 @@ dynconv_status_t dynconv_forward_attn(const dynconv_desc_t *desc, int32_t policy
                                       size_t workspace_bytes, void *stream);
 size_t dynconv_forward_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
 
+/* ---- gradients ------------------------------------------------------------
+ * The pages train dynamic convolutions end to end ("learn specialized
+ * convolutional kernels for each example", CondConv: Conditionally
+ * Parameterized Convolutions, abstract; "learns a linear mixture of n static
+ * kernels weighted with their input-dependent attentions", KernelWarehouse:
+ * Rethinking the Design of Dynamic Convolution, abstract) but print no
+ * backward pass. These entry points compute the derivative of the forward
+ * definition above for a given output gradient dy [B,Cout,Ho,Wo] (same
+ * element type as x). Calls are asynchronous on `stream`, validate every
+ * argument before any launch (nothing is launched or written on failure)
+ * and run in a fixed order (deterministic). */
+
+/* Input gradient of the layer:
+ *   dx[b] = the transposed convolution of dy[b] with W_b = sum_i alpha[b,i] E_i,
+ * i.e. dx[b,c,h,w] = sum of W_b[o,c',u,v] * dy[b,o,r,s] over the (o, r, s,
+ * u, v) whose forward output read x[b,c,h,w]. Computed as the forward layer
+ * (any policy of dynconv_forward; AUTO picks as for that layer) applied to dy
+ * with the bank transposed in its channels, flipped in its taps, and padding
+ * k - 1 - pad. dy: [B,Cout,Ho,Wo]; experts, alpha as dynconv_forward; dx:
+ * [B,Cin,H,W], written (not accumulated), in the layer's element type with
+ * one rounding. Supported: stride 1, kh == kw, pad <= kh - 1, groups 1 or
+ * depthwise (else DYNCONV_ERR_UNSUPPORTED). workspace: at least
+ * dynconv_backward_data_workspace_bytes(desc, policy) bytes (the flipped
+ * bank, then the forward's workspace); 0 if the descriptor is invalid. */
+dynconv_status_t dynconv_backward_data(const dynconv_desc_t *desc, int32_t policy, const void *dy,
+                                       const void *experts, const float *alpha, void *dx,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+size_t dynconv_backward_data_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
+
+/* Gradients of the attentions and of the expert bank:
+ *   dW_b[o,c',u,v] = sum_{r,s} dy[b,o,r,s] * x[b, gc, r*stride-pad+u, s*stride-pad+v]
+ *   dalpha[b,i]    = sum_e dW_b[e] * E_i[e]          (float32 [B,n])
+ *   dexperts[i,e]  = sum_b alpha[b,i] * dW_b[e]      (float32 [n,Cout,Cin/g,kh,kw])
+ * x outside the image counts as 0. dW_b is formed in float32 from the stored
+ * x and dy (bf16 products are exact in float32) and kept in the workspace:
+ * at least dynconv_backward_weights_workspace_bytes(desc) bytes, i.e.
+ * B * Cout * (Cin/g) * kh * kw floats. dalpha or dexperts may be NULL (not
+ * computed), not both. Any stride and padding; groups 1 or depthwise (at
+ * most 64 taps); B <= 65535. Both outputs are written, not accumulated. */
+dynconv_status_t dynconv_backward_weights(const dynconv_desc_t *desc, const void *x, const void *dy,
+                                          const void *experts, const float *alpha, float *dalpha,
+                                          float *dexperts, void *workspace, size_t workspace_bytes,
+                                          void *stream);
+size_t dynconv_backward_weights_workspace_bytes(const dynconv_desc_t *desc);
+
+/* Gradient of the routing (dynconv_route) for the attention gradient dalpha:
+ *   sigmoid:      dz = dalpha * alpha * (1 - alpha)
+ *   softmax(z/T): dz_i = alpha_i * (dalpha_i - sum_k alpha_k dalpha_k) / T
+ *   dfc_w[i,c] = sum_b dz[b,i] * gap[b,c],  dfc_b[i] = sum_b dz[b,i]
+ *   dgap[b,c]  = sum_i dz[b,i] * fc_w[i,c]
+ * alpha [B,n] must be dynconv_route's output for the same x, fc_w, fc_b,
+ * mode and temperature; gap is recomputed from x. dfc_w [n,Cin] and dfc_b
+ * [n] (may be NULL) are written (float32). When dx [B,Cin,H,W] (layer
+ * element type) is not NULL, dgap[b,c] / (H*W) is ADDED to every position of
+ * dx[b,c] in float32 and rounded once to the element type: pass the input
+ * gradient from dynconv_backward_data to get the whole input gradient.
+ * Only B, Cin, H, W, n and dtype of desc are read; n <= 256. workspace: at
+ * least dynconv_route_backward_workspace_bytes(desc) bytes. */
+dynconv_status_t dynconv_route_backward(const dynconv_desc_t *desc, const void *x, const float *fc_w,
+                                        int32_t mode, float temperature, const float *alpha,
+                                        const float *dalpha, float *dfc_w, float *dfc_b, void *dx,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+size_t dynconv_route_backward_workspace_bytes(const dynconv_desc_t *desc);
+
 /* The policy DYNCONV_POLICY_AUTO resolves to for this layer
  * (DYNCONV_POLICY_PREMIX or DYNCONV_POLICY_FUSED), or -1 for an invalid or
  * unsupported descriptor. */

@@ -239,3 +239,77 @@ def test_forward_attn_checks():
     # depthwise layers keep in-kernel mixing (no workspace)
     dw = good_desc(Cin=8, Cout=8, groups=8, kh=5, kw=5, pad=2)
     assert bd.dynconv_forward_attn_workspace_bytes(dw) == 0
+
+
+def test_backward_data_checks():
+    L = _lib()
+    d = good_desc()
+
+    def bwd(desc=d, policy=bd.DYNCONV_POLICY_AUTO, dy=FAKE, e=FAKE, a=FAKE, dx=FAKE, wsp=FAKE, wsb=None):
+        if wsb is None:
+            wsb = bd.dynconv_backward_data_workspace_bytes(desc, policy)
+        return L.dynconv_backward_data(ctypes.byref(desc), policy, dy, e, a, dx, wsp, wsb, None)
+
+    # the flipped bank, then the forward workspace of the transposed layer
+    t = good_desc()   # 16 -> 16, 8x8, pad 1 is its own transpose
+    flip = (4 * 16 * 16 * 9 * 2 + 255) // 256 * 256
+    for p in (bd.DYNCONV_POLICY_AUTO, bd.DYNCONV_POLICY_PREMIX):
+        assert bd.dynconv_backward_data_workspace_bytes(d, p) == flip + bd.dynconv_forward_workspace_bytes(t, p)
+    assert bwd(dy=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bwd(dx=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bwd(wsb=bd.dynconv_backward_data_workspace_bytes(d) - 1) == bd.DYNCONV_ERR_WORKSPACE
+    assert bwd(wsp=None) == bd.DYNCONV_ERR_WORKSPACE
+    for bad in (good_desc(stride=2), good_desc(kh=3, kw=1, pad=0), good_desc(kh=3, kw=3, pad=3, H=4, W=4)):
+        assert bd.dynconv_backward_data_workspace_bytes(bad) == 0
+        assert bwd(desc=bad, wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert bwd(desc=good_desc(groups=2), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert bwd(policy=7, wsb=1 << 30) == bd.DYNCONV_ERR_INVALID_ARG
+    # 1x1 with Cin != Cout transposes the channels: 40 -> 240 runs as 240 -> 40
+    e1 = good_desc(Cin=40, Cout=240, kh=1, kw=1, pad=0, n=8)
+    t1 = good_desc(Cin=240, Cout=40, kh=1, kw=1, pad=0, n=8)
+    assert bd.dynconv_backward_data_workspace_bytes(e1) == (8 * 240 * 40 * 2 + 255) // 256 * 256 + \
+        bd.dynconv_forward_workspace_bytes(t1)
+
+
+def test_backward_weights_checks():
+    L = _lib()
+    d = good_desc()
+
+    def bwd(desc=d, x=FAKE, dy=FAKE, e=FAKE, a=FAKE, da=FAKE, de=FAKE, wsp=FAKE, wsb=None):
+        if wsb is None:
+            wsb = bd.dynconv_backward_weights_workspace_bytes(desc)
+        return L.dynconv_backward_weights(ctypes.byref(desc), x, dy, e, a, da, de, wsp, wsb, None)
+
+    # dW_b in float32
+    assert bd.dynconv_backward_weights_workspace_bytes(d) == (2 * 16 * 16 * 9 * 4 + 255) // 256 * 256
+    assert bwd(x=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bwd(da=None, de=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bwd(de=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bwd(wsb=bd.dynconv_backward_weights_workspace_bytes(d) - 1) == bd.DYNCONV_ERR_WORKSPACE
+    assert bwd(desc=good_desc(groups=2), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    big_dw = good_desc(Cin=8, Cout=8, groups=8, kh=9, kw=9, pad=4, H=16, W=16)
+    assert bwd(desc=big_dw, wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert bwd(desc=good_desc(B=70000, H=1, W=1, kh=1, kw=1, pad=0), wsb=1 << 40) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert bd.dynconv_backward_weights_workspace_bytes(good_desc(stride=0)) == 0
+
+
+def test_route_backward_checks():
+    L = _lib()
+    d = good_desc()
+
+    def rb(desc=d, x=FAKE, w=FAKE, mode=bd.DYNCONV_SIGMOID, t=1.0, a=FAKE, da=FAKE, dw=FAKE, db=FAKE,
+           dx=FAKE, wsp=FAKE, wsb=None):
+        if wsb is None:
+            wsb = bd.dynconv_route_backward_workspace_bytes(desc)
+        return L.dynconv_route_backward(ctypes.byref(desc), x, w, mode, t, a, da, dw, db, dx, wsp, wsb, None)
+
+    # gap and dgap [B, Cin], dz [B, n]
+    assert bd.dynconv_route_backward_workspace_bytes(d) == 2 * 256 + 256
+    assert rb(da=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert rb(dw=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert rb(dx=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert rb(mode=5) == bd.DYNCONV_ERR_INVALID_ARG
+    assert rb(mode=bd.DYNCONV_SOFTMAX, t=0.0) == bd.DYNCONV_ERR_INVALID_ARG
+    assert rb(mode=bd.DYNCONV_SOFTMAX, t=float("inf")) == bd.DYNCONV_ERR_INVALID_ARG
+    assert rb(desc=good_desc(n=300), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert rb(wsb=bd.dynconv_route_backward_workspace_bytes(d) - 1) == bd.DYNCONV_ERR_WORKSPACE
