@@ -17,8 +17,11 @@
 // its channels and flipped in its taps (flip_experts_kernel) and padding
 // k - 1 - p. The kernel gradient is a GEMM per example (M = output
 // channels, N = kernel columns (c, u, v), reduction over output positions)
-// on the matrix cores; dW_b goes to an fp32 workspace and two contraction
-// kernels reduce it to dalpha and dE.
+// on the matrix cores (depthwise: per-plane tap sums on the VALU); dW_b goes
+// to an fp32 workspace, and one pass over it (contract_kernel) yields dE
+// and per-chunk partial sums of dalpha, which a small kernel reduces.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,197 +49,339 @@ __global__ __launch_bounds__(256) void flip_experts_kernel(const T *__restrict__
 }
 
 // ---- kernel gradient per example (groups == 1) ------------------------------
-// Workgroup (tile, b): a 64 x 64 block of dW_b (output channels o0.., kernel
-// columns K0.., K = c * KT + t) reduced over the example's output positions
-// in chunks of 32. Both operands are staged position-contiguous in LDS:
+// Workgroup (tile, b): a 128 x 64 block of dW_b (output channels o0..,
+// kernel columns K0.., K = c * KT + t) reduced over the example's output
+// positions in chunks of 64. Both operands are staged position-contiguous in
+// LDS:
 //   A[o][p] = dy[b, o, p],   B[K][p] = x[b, c, r*st - pad + u, s*st - pad + v]
 // (zero outside the image, past P, Cout or Kdim), so a lane's MFMA fragment
-// (8 consecutive positions of one row) is one 16-byte LDS read. Four waves
-// each own a 32 x 32 quarter of the block.
+// (8 consecutive positions of one row) is one 16-byte LDS read. Wave w owns
+// output rows 64 (w & 1) .. + 63 (two 32-row blocks) and kernel columns
+// 32 (w >> 1) .. + 31. The next chunk's global loads are issued before the
+// current chunk's MFMAs, so their latency hides behind the matrix work.
 struct WgArgs {
     int B, Cin, H, W, Cout, KW, stride, pad, Wo, P, KT, Kdim, n_ktiles;
+    int dy_vec;  // P % 4 == 0: rows of dy are read with 8- or 16-byte loads
 };
 
 template <typename T> struct WgPitch;
-template <> struct WgPitch<uint16_t> { static constexpr int v = 40; };  // 80-byte LDS rows
-template <> struct WgPitch<float> { static constexpr int v = 36; };     // 144-byte LDS rows
+template <> struct WgPitch<uint16_t> { static constexpr int v = 72; };  // 144-byte LDS rows (64 positions + pad)
+template <> struct WgPitch<float> { static constexpr int v = 68; };     // 272-byte LDS rows
 
-template <typename T>
-__device__ __forceinline__ void lds_store8(T *dst, const T (&v)[8]);
-template <>
-__device__ __forceinline__ void lds_store8<uint16_t>(uint16_t *dst, const uint16_t (&v)[8]) {
-    u32x4_t w;
-    w.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-    w.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-    w.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-    w.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-    *reinterpret_cast<u32x4_t *>(dst) = w;
-}
-template <>
-__device__ __forceinline__ void lds_store8<float>(float *dst, const float (&v)[8]) {
-    f32x4_t a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
-    reinterpret_cast<f32x4_t *>(dst)[0] = a;
-    reinterpret_cast<f32x4_t *>(dst)[1] = b;
-}
+// 8 consecutive elements of one staged row, in registers.
+template <typename T> struct Row8;
+template <> struct Row8<uint16_t> {
+    u32x4_t v;
+    __device__ __forceinline__ void zero() { v = u32x4_t{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ void set(int j, uint16_t h) {
+        const uint32_t m = (j & 1) ? 0xffff0000u : 0x0000ffffu;
+        const uint32_t w = (j & 1) ? ((uint32_t)h << 16) : (uint32_t)h;
+        v[j >> 1] = (v[j >> 1] & ~m) | w;
+    }
+    __device__ __forceinline__ void load_vec(const uint16_t *p) {  // 8-byte aligned
+        const u32x2_t a = *reinterpret_cast<const u32x2_t *>(p);
+        const u32x2_t b = *reinterpret_cast<const u32x2_t *>(p + 4);
+        v = u32x4_t{a.x, a.y, b.x, b.y};
+    }
+    __device__ __forceinline__ void store(uint16_t *dst) const { *reinterpret_cast<u32x4_t *>(dst) = v; }
+};
+template <> struct Row8<float> {
+    f32x4_t v0, v1;
+    __device__ __forceinline__ void zero() { v0 = f32x4_t{0.f, 0.f, 0.f, 0.f}; v1 = v0; }
+    __device__ __forceinline__ void set(int j, float f) {
+        if (j < 4) v0[j] = f;
+        else v1[j - 4] = f;
+    }
+    __device__ __forceinline__ void load_vec(const float *p) {  // 16-byte aligned
+        v0 = reinterpret_cast<const f32x4_t *>(p)[0];
+        v1 = reinterpret_cast<const f32x4_t *>(p)[1];
+    }
+    __device__ __forceinline__ void store(float *dst) const {
+        reinterpret_cast<f32x4_t *>(dst)[0] = v0;
+        reinterpret_cast<f32x4_t *>(dst)[1] = v1;
+    }
+};
 
 template <typename T>
 __global__ __launch_bounds__(256) void wgrad_kernel(const T *__restrict__ x, const T *__restrict__ dy,
                                                     float *__restrict__ dw, WgArgs a) {
     constexpr int PITCH = WgPitch<T>::v;
-    __shared__ __attribute__((aligned(16))) T s_a[64 * PITCH];
+    __shared__ __attribute__((aligned(16))) T s_a[128 * PITCH];
     __shared__ __attribute__((aligned(16))) T s_b[64 * PITCH];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
-    const int mh = wave & 1, nh = wave >> 1;
+    const int mq = wave & 1, nh = wave >> 1;
     const int b = blockIdx.y;
     const int ot = blockIdx.x / a.n_ktiles, kt = blockIdx.x - ot * a.n_ktiles;
-    const int o0 = ot * 64, K0 = kt * 64;
-    // staging role: row `row` of both tiles, positions 8 * seg .. + 7 of the chunk
+    const int o0 = ot * 128, K0 = kt * 64;
+    // staging roles: dy rows `row` and `row + 64`, im2col row `row`;
+    // positions 8 * seg .. + 7 and 32 + 8 * seg .. + 7 of the chunk
     const int row = tid >> 2, seg = tid & 3;
-    const int o = o0 + row;
-    const bool o_ok = o < a.Cout;
-    const T *dyrow = dy + ((long)b * a.Cout + (o_ok ? o : 0)) * a.P;
+    const T *dyrow[2];
+    bool o_ok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int o = o0 + row + 64 * h;
+        o_ok[h] = o < a.Cout;
+        dyrow[h] = dy + ((long)b * a.Cout + (o_ok[h] ? o : 0)) * a.P;
+    }
     const int K = K0 + row;
     const bool k_ok = K < a.Kdim;
     const int kc = k_ok ? K / a.KT : 0;
     const int kt_ = k_ok ? K - kc * a.KT : 0;
     const int ku = kt_ / a.KW, kv = kt_ - ku * a.KW;
     const T *xplane = x + ((long)b * a.Cin + kc) * a.H * a.W;
-    f32x16_t acc = {};
-    for (int p0 = 0; p0 < a.P; p0 += 32) {
-        T av[8], bv[8];
-        const int p = p0 + 8 * seg;
-        int r = p / a.Wo, s = p - r * a.Wo;
+    Row8<T> ra[2][2], rb[2];
+    auto load = [&](int p0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool pin = p + j < a.P;
-            av[j] = (o_ok && pin) ? dyrow[p + j] : T(0);
-            const int h = r * a.stride - a.pad + ku, w = s * a.stride - a.pad + kv;
-            const bool xin = k_ok && pin && h >= 0 && h < a.H && w >= 0 && w < a.W;
-            bv[j] = xin ? xplane[(long)h * a.W + w] : T(0);
-            if (++s == a.Wo) { s = 0; ++r; }
+        for (int half = 0; half < 2; ++half) {
+            const int p = p0 + 32 * half + 8 * seg;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (a.dy_vec && o_ok[h] && p + 8 <= a.P) {
+                    ra[half][h].load_vec(dyrow[h] + p);
+                } else {
+                    ra[half][h].zero();
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (o_ok[h] && p + j < a.P) ra[half][h].set(j, dyrow[h][p + j]);
+                }
+            }
+            rb[half].zero();
+            int r = p / a.Wo, s = p - r * a.Wo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int hh = r * a.stride - a.pad + ku, ww = s * a.stride - a.pad + kv;
+                if (k_ok && p + j < a.P && hh >= 0 && hh < a.H && ww >= 0 && ww < a.W)
+                    rb[half].set(j, xplane[(long)hh * a.W + ww]);
+                if (++s == a.Wo) { s = 0; ++r; }
+            }
         }
+    };
+    f32x16_t acc[2] = {};
+    load(0);
+    for (int p0 = 0; p0 < a.P; p0 += 64) {
         __syncthreads();  // the previous chunk's fragment reads are done
-        lds_store8<T>(s_a + row * PITCH + 8 * seg, av);
-        lds_store8<T>(s_b + row * PITCH + 8 * seg, bv);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            ra[half][0].store(s_a + row * PITCH + 32 * half + 8 * seg);
+            ra[half][1].store(s_a + (row + 64) * PITCH + 32 * half + 8 * seg);
+            rb[half].store(s_b + row * PITCH + 32 * half + 8 * seg);
+        }
         __syncthreads();
-        const T *pa = s_a + (32 * mh + l32) * PITCH;
+        if (p0 + 64 < a.P) load(p0 + 64);
         const T *pb = s_b + (32 * nh + l32) * PITCH;
+        const T *pa0 = s_a + (64 * mq + l32) * PITCH;
+        const T *pa1 = pa0 + 32 * PITCH;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t af = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(pa + 16 * ks + 8 * lh));
-                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(pb + 16 * ks + 8 * lh));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = 16 * ks + 8 * lh;
+                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(pb + off));
+                const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(pa0 + off));
+                const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(pa1 + off));
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bf, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bf, acc[1], 0, 0, 0);
             }
         } else {
 #pragma unroll
-            for (int ks = 0; ks < 16; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[2 * ks + lh], pb[2 * ks + lh], acc, 0, 0, 0);
+            for (int ks = 0; ks < 32; ++ks) {
+                const float bf = pb[2 * ks + lh];
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa0[2 * ks + lh], bf, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa1[2 * ks + lh], bf, acc[1], 0, 0, 0);
+            }
         }
     }
-    // D(lane, 4j + q) = row 8j + 4 lh + q, column l32 of the wave's quarter
+    // D(lane, 4j + q) = row 8j + 4 lh + q, column l32 of a 32 x 32 block
     const int KK = K0 + 32 * nh + l32;
     if (KK >= a.Kdim) return;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int oo = o0 + 32 * mh + 8 * j + 4 * lh + q;
-            if (oo < a.Cout) dw[((long)b * a.Cout + oo) * a.Kdim + KK] = acc[4 * j + q];
-        }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int oo = o0 + 64 * mq + 32 * mb + 8 * j + 4 * lh + q;
+                if (oo < a.Cout) dw[((long)b * a.Cout + oo) * a.Kdim + KK] = acc[mb][4 * j + q];
+            }
 }
 
 // ---- kernel gradient per example, depthwise --------------------------------
 // Workgroup (c, b): dW_b[c][t] = sum_p dy[b,c,p] * x[b,c, shifted by tap t].
-// Each thread sums its positions for every tap, then the block reduces.
+// The example's input plane, with its zero border, and its dy plane are
+// staged in LDS as float32 (tile row i, column j <-> x row i - pad, column
+// j - pad). Thread (t, g) with t < K*K sums tap t over the positions
+// g, g + G, ... (G = 256 / (K*K) groups), reading LDS only; then the G
+// partial sums of each tap are added in LDS in a fixed order.
+template <typename T, int K>
+__global__ __launch_bounds__(256) void wgrad_dw_kernel(const T *__restrict__ x, const T *__restrict__ dy,
+                                                       float *__restrict__ dw, WgArgs a, int Hp, int Wp) {
+    constexpr int KK = K * K;
+    constexpr int G = 256 / KK;
+    extern __shared__ float s_dyn[];
+    float *s_x = s_dyn;                 // Hp * Wp
+    float *s_d = s_dyn + Hp * Wp;       // P
+    __shared__ float s_part[256];
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const T *xp = x + ((long)b * a.Cin + c) * a.H * a.W;
+    const T *dp = dy + ((long)b * a.Cin + c) * a.P;
+    for (int i = tid; i < Hp * Wp; i += 256) {
+        const int ii = i / Wp;
+        const int hh = ii - a.pad, ww = i - ii * Wp - a.pad;
+        s_x[i] = (hh >= 0 && hh < a.H && ww >= 0 && ww < a.W) ? Elem<T>::to_f32(xp[(long)hh * a.W + ww]) : 0.f;
+    }
+    for (int i = tid; i < a.P; i += 256) s_d[i] = Elem<T>::to_f32(dp[i]);
+    __syncthreads();
+    const int t = tid % KK, g = tid / KK;
+    float part = 0.f;
+    if (g < G) {
+        const int u = t / K, v = t - u * K;
+        int r = g / a.Wo, s = g - r * a.Wo;
+        const int dr = G / a.Wo, ds = G - dr * a.Wo;  // position step G as (rows, columns)
+        for (int p = g; p < a.P; p += G) {
+            part += s_d[p] * s_x[(r * a.stride + u) * Wp + s * a.stride + v];
+            r += dr;
+            s += ds;
+            if (s >= a.Wo) { s -= a.Wo; ++r; }
+        }
+    }
+    s_part[tid] = part;
+    __syncthreads();
+    if (tid < KK) {
+        float sum = 0.f;
+        for (int j = 0; j < G; ++j) sum += s_part[j * KK + tid];
+        dw[((long)b * a.Cin + c) * KK + tid] = sum;
+    }
+}
+
+// Any other depthwise kernel size (up to 64 taps), bounds-checked global reads.
 constexpr int kDwTaps = 64;
 template <typename T>
-__global__ __launch_bounds__(256) void wgrad_dw_kernel(const T *__restrict__ x, const T *__restrict__ dy,
-                                                       float *__restrict__ dw, WgArgs a) {
+__global__ __launch_bounds__(256) void wgrad_dw_any_kernel(const T *__restrict__ x, const T *__restrict__ dy,
+                                                           float *__restrict__ dw, WgArgs a) {
     __shared__ float s_red[4][kDwTaps];
     const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const T *xp = x + ((long)b * a.Cin + c) * a.H * a.W;
     const T *dp = dy + ((long)b * a.Cin + c) * a.P;
-    float part[kDwTaps];
-#pragma unroll
-    for (int t = 0; t < kDwTaps; ++t) part[t] = 0.f;
-    for (int p = tid; p < a.P; p += 256) {
-        const int r = p / a.Wo, s = p - r * a.Wo;
-        const float d = Elem<T>::to_f32(dp[p]);
-#pragma unroll
-        for (int t = 0; t < kDwTaps; ++t) {
-            if (t < a.KT) {
-                const int u = t / a.KW, v = t - u * a.KW;
-                const int h = r * a.stride - a.pad + u, w = s * a.stride - a.pad + v;
-                if (h >= 0 && h < a.H && w >= 0 && w < a.W) part[t] += d * Elem<T>::to_f32(xp[(long)h * a.W + w]);
-            }
-        }
-    }
     const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-    for (int t = 0; t < kDwTaps; ++t) {
-        if (t < a.KT) {
-            const float v = wave_sum(part[t]);
-            if (lane == 0) s_red[wave][t] = v;
+    for (int t = 0; t < a.KT; ++t) {
+        const int u = t / a.KW, v = t - u * a.KW;
+        float part = 0.f;
+        for (int p = tid; p < a.P; p += 256) {
+            const int r = p / a.Wo, s = p - r * a.Wo;
+            const int hh = r * a.stride - a.pad + u, ww = s * a.stride - a.pad + v;
+            if (hh >= 0 && hh < a.H && ww >= 0 && ww < a.W)
+                part += Elem<T>::to_f32(dp[p]) * Elem<T>::to_f32(xp[(long)hh * a.W + ww]);
         }
+        part = wave_sum(part);
+        if (lane == 0) s_red[wave][t] = part;
     }
     __syncthreads();
     if (tid < a.KT)
         dw[((long)b * a.Cin + c) * a.KT + tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
 }
 
-// ---- contractions of dW_b -----------------------------------------------------
-// dalpha[b][i] = sum_e dW_b[e] * E_i[e]: workgroup per example, up to 8
-// experts per pass over dW_b.
-template <typename T>
-__global__ __launch_bounds__(256) void dalpha_kernel(const float *__restrict__ dw, const T *__restrict__ e,
-                                                     float *__restrict__ dalpha, long wsize, int n) {
-    __shared__ float s_red[4][8];
-    const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const float *d = dw + (long)b * wsize;
-    for (int i0 = 0; i0 < n; i0 += 8) {
-        float acc[8];
+// ---- contraction of dW_b into dalpha and dE ---------------------------------------
+// One pass over dW_b [B][wsize] for NE experts i0 .. i0 + NE - 1. Workgroup
+// (ch, bg) owns elements ch * 256 * VEC .. (VEC per thread) and the examples
+// bg * bpg .. + bpg - 1:
+//   dEp[bg][i][e]   = sum_{b in group} alpha[b][i] * dW_b[e]
+//   dpart[b][i][ch] = sum_{e in chunk} dW_b[e] * E_i[e]
+// With one example group dEp is dE itself; otherwise dE_reduce_kernel adds
+// the groups, and dalpha_reduce_kernel adds the chunks of dpart. The
+// workgroup's slice of the bank stays in registers; dW_b rows are loaded
+// kCtU examples ahead.
+constexpr int kCtB = 16;  // examples per LDS round of partial sums
+constexpr int kCtU = 4;   // examples whose dW_b rows are in flight together
+template <typename T, int NE, int VEC>
+__global__ __launch_bounds__(256) void contract_kernel(const float *__restrict__ dw, const T *__restrict__ ex,
+                                                       const float *__restrict__ alpha, float *__restrict__ dep,
+                                                       float *__restrict__ dpart, long wsize, int B, int bpg, int n,
+                                                       int i0, int nch) {
+    __shared__ float s_red[4][kCtB][NE];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const long e0 = ((long)blockIdx.x * 256 + tid) * VEC;
+    const bool in = e0 < wsize;  // VEC == 4 only when wsize % 4 == 0
+    const int bbeg = blockIdx.y * bpg, bend = min(B, bbeg + bpg);
+    float ev[NE][VEC], acc[NE][VEC];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-        for (long j = tid; j < wsize; j += 256) {
-            const float v = d[j];
+    for (int k = 0; k < NE; ++k)
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (i0 + k < n) acc[k] += v * Elem<T>::to_f32(e[(long)(i0 + k) * wsize + j]);
+        for (int j = 0; j < VEC; ++j) {
+            ev[k][j] = (in && i0 + k < n) ? Elem<T>::to_f32(ex[(long)(i0 + k) * wsize + e0 + j]) : 0.f;
+            acc[k][j] = 0.f;
         }
+    for (int b0 = bbeg; b0 < bend; b0 += kCtB) {
+        const int nb = min(kCtB, bend - b0);
+        for (int u0 = 0; u0 < nb; u0 += kCtU) {
+            float d[kCtU][VEC];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float v = wave_sum(acc[k]);
-            if (lane == 0) s_red[wave][k] = v;
+            for (int uu = 0; uu < kCtU; ++uu) {
+                const int b = b0 + u0 + uu;
+                const bool ok = in && u0 + uu < nb;
+                if constexpr (VEC == 4) {
+                    const f32x4_t v = ok ? *reinterpret_cast<const f32x4_t *>(dw + (long)b * wsize + e0)
+                                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    d[uu][0] = v[0]; d[uu][1] = v[1]; d[uu][2] = v[2]; d[uu][3] = v[3];
+                } else {
+                    d[uu][0] = ok ? dw[(long)b * wsize + e0] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int uu = 0; uu < kCtU; ++uu) {
+                if (u0 + uu >= nb) break;
+                const int b = b0 + u0 + uu;
+#pragma unroll
+                for (int k = 0; k < NE; ++k) {
+                    const float al = i0 + k < n ? alpha[(long)b * n + i0 + k] : 0.f;
+                    float part = 0.f;
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) {
+                        acc[k][j] += al * d[uu][j];
+                        part += d[uu][j] * ev[k][j];
+                    }
+                    part = wave_sum(part);
+                    if (lane == 0) s_red[wave][u0 + uu][k] = part;
+                }
+            }
         }
         __syncthreads();
-        if (tid < 8 && i0 + tid < n)
-            dalpha[(long)b * n + i0 + tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
+        if (tid < nb * NE) {
+            const int bb = tid / NE, k = tid - bb * NE;
+            if (i0 + k < n)
+                dpart[((long)(b0 + bb) * n + i0 + k) * nch + blockIdx.x] =
+                    (s_red[0][bb][k] + s_red[1][bb][k]) + (s_red[2][bb][k] + s_red[3][bb][k]);
+        }
         __syncthreads();
     }
+    if (!in || dep == nullptr) return;
+    float *out = dep + (long)blockIdx.y * n * wsize;
+#pragma unroll
+    for (int k = 0; k < NE; ++k)
+        if (i0 + k < n)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) out[(long)(i0 + k) * wsize + e0 + j] = acc[k][j];
 }
 
-// dE[i][e] = sum_b alpha[b][i] * dW_b[e]: thread per element e, up to 8
-// experts per pass; every example's dW_b is read once per pass.
-__global__ __launch_bounds__(256) void dexperts_kernel(const float *__restrict__ dw, const float *__restrict__ alpha,
-                                                       float *__restrict__ de, long wsize, int B, int n) {
+// dE[j] = sum over example groups of dEp[g][j] (j over n * wsize), in group order.
+__global__ __launch_bounds__(256) void dE_reduce_kernel(const float *__restrict__ dep, float *__restrict__ de,
+                                                        long total, int groups) {
     const long j = (long)blockIdx.x * 256 + threadIdx.x;
-    if (j >= wsize) return;
-    for (int i0 = 0; i0 < n; i0 += 8) {
-        float acc[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-        for (int b = 0; b < B; ++b) {
-            const float v = dw[(long)b * wsize + j];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (i0 + k < n) acc[k] += alpha[(long)b * n + i0 + k] * v;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (i0 + k < n) de[(long)(i0 + k) * wsize + j] = acc[k];
-    }
+    if (j >= total) return;
+    float s = 0.f;
+    for (int g = 0; g < groups; ++g) s += dep[(long)g * total + j];
+    de[j] = s;
+}
+
+// dalpha[b][i] = sum over chunks of dpart[b][i][ch], in chunk order.
+__global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float *__restrict__ dpart,
+                                                            float *__restrict__ dalpha, int total, int nch) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const float *p = dpart + (long)idx * nch;
+    float s = 0.f;
+    for (int c = 0; c < nch; ++c) s += p[c];
+    dalpha[idx] = s;
 }
 
 // ---- routing gradient -----------------------------------------------------------
@@ -323,7 +468,64 @@ hipError_t launch_flip_experts(const Geom &g, const void *experts, void *flipped
     return hipGetLastError();
 }
 
-size_t wgrad_bytes(const Geom &g) { return (size_t)g.B * g.Cout * g.cpg * g.KT * sizeof(float); }
+namespace {
+long bank_elems(const Geom &g) { return (long)g.Cout * g.cpg * g.KT; }
+int contract_vec(const Geom &g) { return bank_elems(g) % 4 == 0 ? 4 : 1; }
+int contract_chunks(const Geom &g) { return (int)((bank_elems(g) + 256L * contract_vec(g) - 1) / (256L * contract_vec(g))); }
+// Examples per contraction workgroup: enough example groups that the grid
+// has about 1024 workgroups, with at least 8 examples per group.
+int contract_bpg(const Geom &g) {
+    const int want = std::max(1, std::min(ceil_div(1024, contract_chunks(g)), ceil_div(g.B, 8)));
+    return ceil_div(g.B, want);
+}
+int contract_groups(const Geom &g) { return ceil_div(g.B, contract_bpg(g)); }
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+size_t dwb_bytes(const Geom &g) { return align256((size_t)g.B * bank_elems(g) * sizeof(float)); }
+size_t dpart_bytes(const Geom &g) { return align256((size_t)g.B * g.n * contract_chunks(g) * sizeof(float)); }
+size_t dep_bytes(const Geom &g) {
+    return contract_groups(g) > 1 ? align256((size_t)contract_groups(g) * g.n * bank_elems(g) * sizeof(float)) : 0;
+}
+bool dw_lds_plane(const Geom &g, int &Hp, int &Wp) {
+    if (g.KH != g.KW || (g.KH != 3 && g.KH != 5)) return false;
+    Hp = (g.Ho - 1) * g.stride + g.KH;
+    Wp = (g.Wo - 1) * g.stride + g.KW;
+    return ((long)Hp * Wp + g.P) * 4 <= 64 * 1024;
+}
+
+template <typename T, int NE>
+hipError_t launch_contract_t(const Geom &g, const float *dwb, const void *experts, const float *alpha, float *dep,
+                             float *dpart, int i0, hipStream_t stream) {
+    const long wsize = bank_elems(g);
+    const int nch = contract_chunks(g);
+    const dim3 grid((unsigned)nch, (unsigned)contract_groups(g));
+    if (contract_vec(g) == 4)
+        hipLaunchKernelGGL((contract_kernel<T, NE, 4>), grid, dim3(256), 0, stream, dwb,
+                           static_cast<const T *>(experts), alpha, dep, dpart, wsize, g.B, contract_bpg(g), g.n, i0,
+                           nch);
+    else
+        hipLaunchKernelGGL((contract_kernel<T, NE, 1>), grid, dim3(256), 0, stream, dwb,
+                           static_cast<const T *>(experts), alpha, dep, dpart, wsize, g.B, contract_bpg(g), g.n, i0,
+                           nch);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_contract(const Geom &g, const float *dwb, const void *experts, const float *alpha, float *dep,
+                           float *dpart, hipStream_t stream) {
+    for (int i0 = 0; i0 < g.n; i0 += 8) {
+        const int left = g.n - i0;
+        hipError_t e;
+        if (left >= 5) e = launch_contract_t<T, 8>(g, dwb, experts, alpha, dep, dpart, i0, stream);
+        else if (left >= 3) e = launch_contract_t<T, 4>(g, dwb, experts, alpha, dep, dpart, i0, stream);
+        else if (left == 2) e = launch_contract_t<T, 2>(g, dwb, experts, alpha, dep, dpart, i0, stream);
+        else e = launch_contract_t<T, 1>(g, dwb, experts, alpha, dep, dpart, i0, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+}  // namespace
+
+size_t wgrad_bytes(const Geom &g) { return dwb_bytes(g) + dpart_bytes(g) + dep_bytes(g); }
 
 bool wgrad_dw_supported(const Geom &g) { return g.KT <= kDwTaps; }
 
@@ -335,8 +537,9 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
     a.stride = g.stride; a.pad = g.pad; a.Wo = g.Wo; a.P = g.P; a.KT = g.KT;
     a.Kdim = g.cpg * g.KT;
     a.n_ktiles = ceil_div(a.Kdim, 64);
+    a.dy_vec = g.P % 4 == 0;
     if (g.groups == 1) {
-        const dim3 grid((unsigned)(ceil_div(g.Cout, 64) * a.n_ktiles), (unsigned)g.B);
+        const dim3 grid((unsigned)(ceil_div(g.Cout, 128) * a.n_ktiles), (unsigned)g.B);
         if (g.bf16)
             hipLaunchKernelGGL(wgrad_kernel<uint16_t>, grid, dim3(256), 0, stream,
                                static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dy), dwb, a);
@@ -345,32 +548,52 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
                                static_cast<const float *>(dy), dwb, a);
     } else {
         const dim3 grid((unsigned)g.Cin, (unsigned)g.B);
-        if (g.bf16)
-            hipLaunchKernelGGL(wgrad_dw_kernel<uint16_t>, grid, dim3(256), 0, stream,
+        int Hp = 0, Wp = 0;
+        if (dw_lds_plane(g, Hp, Wp)) {
+            const size_t lds = ((size_t)Hp * Wp + g.P) * sizeof(float);
+            if (g.bf16 && g.KH == 3)
+                hipLaunchKernelGGL((wgrad_dw_kernel<uint16_t, 3>), grid, dim3(256), lds, stream,
+                                   static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dy), dwb, a, Hp, Wp);
+            else if (g.bf16)
+                hipLaunchKernelGGL((wgrad_dw_kernel<uint16_t, 5>), grid, dim3(256), lds, stream,
+                                   static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dy), dwb, a, Hp, Wp);
+            else if (g.KH == 3)
+                hipLaunchKernelGGL((wgrad_dw_kernel<float, 3>), grid, dim3(256), lds, stream,
+                                   static_cast<const float *>(x), static_cast<const float *>(dy), dwb, a, Hp, Wp);
+            else
+                hipLaunchKernelGGL((wgrad_dw_kernel<float, 5>), grid, dim3(256), lds, stream,
+                                   static_cast<const float *>(x), static_cast<const float *>(dy), dwb, a, Hp, Wp);
+        } else if (g.bf16) {
+            hipLaunchKernelGGL(wgrad_dw_any_kernel<uint16_t>, grid, dim3(256), 0, stream,
                                static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dy), dwb, a);
-        else
-            hipLaunchKernelGGL(wgrad_dw_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float *>(x),
+        } else {
+            hipLaunchKernelGGL(wgrad_dw_any_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float *>(x),
                                static_cast<const float *>(dy), dwb, a);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long wsize = (long)g.Cout * g.cpg * g.KT;
-    if (dalpha) {
-        if (g.bf16)
-            hipLaunchKernelGGL(dalpha_kernel<uint16_t>, dim3((unsigned)g.B), dim3(256), 0, stream, dwb,
-                               static_cast<const uint16_t *>(experts), dalpha, wsize, g.n);
-        else
-            hipLaunchKernelGGL(dalpha_kernel<float>, dim3((unsigned)g.B), dim3(256), 0, stream, dwb,
-                               static_cast<const float *>(experts), dalpha, wsize, g.n);
+    // scratch: dW_b | dalpha partial sums | dE per example group
+    char *base = reinterpret_cast<char *>(dwb);
+    float *dpart = reinterpret_cast<float *>(base + dwb_bytes(g));
+    const int groups = contract_groups(g);
+    float *dep = groups > 1 ? reinterpret_cast<float *>(base + dwb_bytes(g) + dpart_bytes(g)) : dexperts;
+    if (!dexperts) dep = nullptr;
+    e = g.bf16 ? launch_contract<uint16_t>(g, dwb, experts, alpha, dep, dpart, stream)
+               : launch_contract<float>(g, dwb, experts, alpha, dep, dpart, stream);
+    if (e != hipSuccess) return e;
+    if (dexperts && groups > 1) {
+        const long total = (long)g.n * bank_elems(g);
+        hipLaunchKernelGGL(dE_reduce_kernel, dim3(blocks_for(total)), dim3(256), 0, stream, dep, dexperts, total,
+                           groups);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (dexperts) {
-        hipLaunchKernelGGL(dexperts_kernel, dim3(blocks_for(wsize)), dim3(256), 0, stream, dwb, alpha, dexperts,
-                           wsize, g.B, g.n);
-        e = hipGetLastError();
-    }
-    return e;
+    if (!dalpha) return hipSuccess;
+    const int total = g.B * g.n;
+    hipLaunchKernelGGL(dalpha_reduce_kernel, dim3(blocks_for(total)), dim3(256), 0, stream, dpart, dalpha, total,
+                       contract_chunks(g));
+    return hipGetLastError();
 }
 
 hipError_t launch_route_backward(const Geom &g, const void *x, const float *fc_w, int mode, float temperature,

@@ -241,9 +241,11 @@ size_t dynconv_backward_data_workspace_bytes(const dynconv_desc_t *desc, int32_t
  *   dalpha[b,i]    = sum_e dW_b[e] * E_i[e]          (float32 [B,n])
  *   dexperts[i,e]  = sum_b alpha[b,i] * dW_b[e]      (float32 [n,Cout,Cin/g,kh,kw])
  * x outside the image counts as 0. dW_b is formed in float32 from the stored
- * x and dy (bf16 products are exact in float32) and kept in the workspace:
- * at least dynconv_backward_weights_workspace_bytes(desc) bytes, i.e.
- * B * Cout * (Cin/g) * kh * kw floats. dalpha or dexperts may be NULL (not
+ * x and dy (bf16 products are exact in float32) and kept in the workspace,
+ * followed by partial sums of dalpha and, for larger batches, of dexperts
+ * per group of examples: at least dynconv_backward_weights_workspace_bytes(desc)
+ * bytes (B * Cout * (Cin/g) * kh * kw floats and the partial sums, each
+ * piece rounded up to 256 bytes). dalpha or dexperts may be NULL (not
  * computed), not both. Any stride and padding; groups 1 or depthwise (at
  * most 64 taps); B <= 65535. Both outputs are written, not accumulated. */
 dynconv_status_t dynconv_backward_weights(const dynconv_desc_t *desc, const void *x, const void *dy,

@@ -280,8 +280,12 @@ def test_backward_weights_checks():
             wsb = bd.dynconv_backward_weights_workspace_bytes(desc)
         return L.dynconv_backward_weights(ctypes.byref(desc), x, dy, e, a, da, de, wsp, wsb, None)
 
-    # dW_b in float32
-    assert bd.dynconv_backward_weights_workspace_bytes(d) == (2 * 16 * 16 * 9 * 4 + 255) // 256 * 256
+    # dW_b in float32, then B * n partial sums of dalpha per 1024-element chunk of the bank
+    r256 = lambda v: (v + 255) // 256 * 256
+    wsize = 16 * 16 * 9
+    assert bd.dynconv_backward_weights_workspace_bytes(d) == r256(2 * wsize * 4) + r256(2 * 4 * 3 * 4)
+    odd = good_desc(Cin=3, Cout=3, n=2)   # wsize 81: one element per thread, 256-element chunks
+    assert bd.dynconv_backward_weights_workspace_bytes(odd) == r256(2 * 81 * 4) + r256(2 * 2 * 1 * 4)
     assert bwd(x=None) == bd.DYNCONV_ERR_INVALID_ARG
     assert bwd(da=None, de=None) == bd.DYNCONV_ERR_INVALID_ARG
     assert bwd(de=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG

@@ -59,6 +59,10 @@ BWD_CASES = [
     (2, 8, 8, 9, 7, 3, 1, 1, 8, 3, "f32"),          # depthwise float32, odd W
     (2, 12, 20, 9, 9, 3, 1, 1, 1, 3, "f32"),        # float32 groups == 1
     (2, 16, 16, 8, 8, 3, 1, 1, 1, 4, "f32"),        # the tiny float32 layer
+    (2, 3, 3, 7, 7, 3, 1, 1, 1, 11, "bf16"),        # odd bank size (scalar contraction), 8 + 3 experts
+    (2, 32, 160, 8, 8, 3, 1, 1, 1, 16, "bf16"),     # 16 experts, two 128-channel output tiles
+    (3, 16, 16, 11, 9, 3, 2, 1, 16, 5, "bf16"),     # depthwise 3x3, stride 2 (data gradient declines)
+    (2, 8, 8, 12, 12, 7, 1, 3, 8, 3, "bf16"),       # depthwise 7x7 (bounds-checked kernel)
 ]
 
 
@@ -68,11 +72,17 @@ def test_backward_matches_oracle(case):
     x, e, a, dy = _layer_inputs(case, seed=100 + Cin + Cout)
     say("backward", case)
     xd, ed, ad, dyd = to_dev(x, dtype), to_dev(e, dtype), to_dev(a, "f32"), to_dev(dy, dtype)
-    dx = bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
+    dx = None
+    if st == 1:
+        dx = bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
+    else:
+        with pytest.raises(bd.DynconvError):
+            bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
     da, de = bd.dynconv_backward_weights(xd, dyd, ed, ad, st, p, g)
     torch.cuda.synchronize()
     rx, ra, re = oracle.backward(x, e, a, dy, st, p, g)
-    check(from_dev(dx), rx, TOL[dtype], f"dx {case}")
+    if dx is not None:
+        check(from_dev(dx), rx, TOL[dtype], f"dx {case}")
     check(from_dev(da), ra, GRAD_TOL[dtype], f"dalpha {case}")
     check(from_dev(de), re, GRAD_TOL[dtype], f"dexperts {case}")
 
