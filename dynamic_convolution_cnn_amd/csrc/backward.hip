@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void flip_experts_kernel(const T *__restrict__
 // ---- kernel gradient per example (groups == 1) ------------------------------
 // Workgroup (tile, b): a 128 x 64 block of dW_b (output channels o0..,
 // kernel columns K0.., K = c * KT + t) reduced over the example's output
-// positions in chunks of 64. Both operands are staged position-contiguous in
+// positions in chunks of 32. Both operands are staged position-contiguous in
 // LDS:
 //   A[o][p] = dy[b, o, p],   B[K][p] = x[b, c, r*st - pad + u, s*st - pad + v]
 // (zero outside the image, past P, Cout or Kdim), so a lane's MFMA fragment
@@ -60,13 +60,13 @@ __global__ __launch_bounds__(256) void flip_experts_kernel(const T *__restrict__
 // 32 (w >> 1) .. + 31. The next chunk's global loads are issued before the
 // current chunk's MFMAs, so their latency hides behind the matrix work.
 struct WgArgs {
-    int B, Cin, H, W, Cout, KW, stride, pad, Wo, P, KT, Kdim, n_ktiles;
+    int B, Cin, H, W, Cout, KW, stride, pad, Ho, Wo, P, KT, Kdim, n_ktiles;
     int dy_vec;  // P % 4 == 0: rows of dy are read with 8- or 16-byte loads
 };
 
 template <typename T> struct WgPitch;
-template <> struct WgPitch<uint16_t> { static constexpr int v = 72; };  // 144-byte LDS rows (64 positions + pad)
-template <> struct WgPitch<float> { static constexpr int v = 68; };     // 272-byte LDS rows
+template <> struct WgPitch<uint16_t> { static constexpr int v = 40; };  // 80-byte LDS rows (32 positions + pad)
+template <> struct WgPitch<float> { static constexpr int v = 36; };     // 144-byte LDS rows
 
 // 8 consecutive elements of one staged row, in registers.
 template <typename T> struct Row8;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const T *__restrict__ x, con
     const int ot = blockIdx.x / a.n_ktiles, kt = blockIdx.x - ot * a.n_ktiles;
     const int o0 = ot * 128, K0 = kt * 64;
     // staging roles: dy rows `row` and `row + 64`, im2col row `row`;
-    // positions 8 * seg .. + 7 and 32 + 8 * seg .. + 7 of the chunk
+    // positions 8 * seg .. + 7 of the chunk
     const int row = tid >> 2, seg = tid & 3;
     const T *dyrow[2];
     bool o_ok[2];
@@ -131,51 +131,45 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const T *__restrict__ x, con
     const int kt_ = k_ok ? K - kc * a.KT : 0;
     const int ku = kt_ / a.KW, kv = kt_ - ku * a.KW;
     const T *xplane = x + ((long)b * a.Cin + kc) * a.H * a.W;
-    Row8<T> ra[2][2], rb[2];
+    Row8<T> ra[2], rb;
     auto load = [&](int p0) {
+        const int p = p0 + 8 * seg;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int p = p0 + 32 * half + 8 * seg;
+        for (int h = 0; h < 2; ++h) {
+            if (a.dy_vec && o_ok[h] && p + 8 <= a.P) {
+                ra[h].load_vec(dyrow[h] + p);
+            } else {
+                ra[h].zero();
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if (a.dy_vec && o_ok[h] && p + 8 <= a.P) {
-                    ra[half][h].load_vec(dyrow[h] + p);
-                } else {
-                    ra[half][h].zero();
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (o_ok[h] && p + j < a.P) ra[half][h].set(j, dyrow[h][p + j]);
-                }
+                for (int j = 0; j < 8; ++j)
+                    if (o_ok[h] && p + j < a.P) ra[h].set(j, dyrow[h][p + j]);
             }
-            rb[half].zero();
-            int r = p / a.Wo, s = p - r * a.Wo;
+        }
+        rb.zero();
+        int r = p / a.Wo, s = p - r * a.Wo;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int hh = r * a.stride - a.pad + ku, ww = s * a.stride - a.pad + kv;
-                if (k_ok && p + j < a.P && hh >= 0 && hh < a.H && ww >= 0 && ww < a.W)
-                    rb[half].set(j, xplane[(long)hh * a.W + ww]);
-                if (++s == a.Wo) { s = 0; ++r; }
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int hh = r * a.stride - a.pad + ku, ww = s * a.stride - a.pad + kv;
+            if (k_ok && p + j < a.P && hh >= 0 && hh < a.H && ww >= 0 && ww < a.W)
+                rb.set(j, xplane[(long)hh * a.W + ww]);
+            if (++s == a.Wo) { s = 0; ++r; }
         }
     };
     f32x16_t acc[2] = {};
     load(0);
-    for (int p0 = 0; p0 < a.P; p0 += 64) {
+    for (int p0 = 0; p0 < a.P; p0 += 32) {
         __syncthreads();  // the previous chunk's fragment reads are done
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            ra[half][0].store(s_a + row * PITCH + 32 * half + 8 * seg);
-            ra[half][1].store(s_a + (row + 64) * PITCH + 32 * half + 8 * seg);
-            rb[half].store(s_b + row * PITCH + 32 * half + 8 * seg);
-        }
+        ra[0].store(s_a + row * PITCH + 8 * seg);
+        ra[1].store(s_a + (row + 64) * PITCH + 8 * seg);
+        rb.store(s_b + row * PITCH + 8 * seg);
         __syncthreads();
-        if (p0 + 64 < a.P) load(p0 + 64);
+        if (p0 + 32 < a.P) load(p0 + 32);
         const T *pb = s_b + (32 * nh + l32) * PITCH;
         const T *pa0 = s_a + (64 * mq + l32) * PITCH;
         const T *pa1 = pa0 + 32 * PITCH;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < 2; ++ks) {
                 const int off = 16 * ks + 8 * lh;
                 const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(pb + off));
                 const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(pa0 + off));
@@ -185,7 +179,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const T *__restrict__ x, con
             }
         } else {
 #pragma unroll
-            for (int ks = 0; ks < 32; ++ks) {
+            for (int ks = 0; ks < 16; ++ks) {
                 const float bf = pb[2 * ks + lh];
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa0[2 * ks + lh], bf, acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa1[2 * ks + lh], bf, acc[1], 0, 0, 0);
@@ -207,21 +201,23 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const T *__restrict__ x, con
 }
 
 // ---- kernel gradient per example, depthwise --------------------------------
-// Workgroup (c, b): dW_b[c][t] = sum_p dy[b,c,p] * x[b,c, shifted by tap t].
+// Workgroup (c, b): dW_b[c][u][v] = sum_{r,s} dy[b,c,r,s] * x[b,c, r*st-pad+u, s*st-pad+v].
 // The example's input plane, with its zero border, and its dy plane are
 // staged in LDS as float32 (tile row i, column j <-> x row i - pad, column
-// j - pad). Thread (t, g) with t < K*K sums tap t over the positions
-// g, g + G, ... (G = 256 / (K*K) groups), reading LDS only; then the G
-// partial sums of each tap are added in LDS in a fixed order.
+// j - pad). Thread (u, g) owns kernel row u and output rows g, g + G, ...
+// (G = 256 / K row groups): along each output row it slides a K-wide window
+// of the tile row r*st + u, so every multiply-add reads at most one new x
+// value, and keeps the K sums of kernel row u in registers. The G partial
+// sums of each tap are then added in LDS in a fixed order.
 template <typename T, int K>
 __global__ __launch_bounds__(256) void wgrad_dw_kernel(const T *__restrict__ x, const T *__restrict__ dy,
                                                        float *__restrict__ dw, WgArgs a, int Hp, int Wp) {
     constexpr int KK = K * K;
-    constexpr int G = 256 / KK;
+    constexpr int G = 256 / K;
     extern __shared__ float s_dyn[];
     float *s_x = s_dyn;                 // Hp * Wp
     float *s_d = s_dyn + Hp * Wp;       // P
-    __shared__ float s_part[256];
+    __shared__ float s_part[G * KK];
     const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const T *xp = x + ((long)b * a.Cin + c) * a.H * a.W;
     const T *dp = dy + ((long)b * a.Cin + c) * a.P;
@@ -232,20 +228,38 @@ __global__ __launch_bounds__(256) void wgrad_dw_kernel(const T *__restrict__ x, 
     }
     for (int i = tid; i < a.P; i += 256) s_d[i] = Elem<T>::to_f32(dp[i]);
     __syncthreads();
-    const int t = tid % KK, g = tid / KK;
-    float part = 0.f;
+    const int u = tid % K, g = tid / K;
+    float part[K];
+#pragma unroll
+    for (int v = 0; v < K; ++v) part[v] = 0.f;
     if (g < G) {
-        const int u = t / K, v = t - u * K;
-        int r = g / a.Wo, s = g - r * a.Wo;
-        const int dr = G / a.Wo, ds = G - dr * a.Wo;  // position step G as (rows, columns)
-        for (int p = g; p < a.P; p += G) {
-            part += s_d[p] * s_x[(r * a.stride + u) * Wp + s * a.stride + v];
-            r += dr;
-            s += ds;
-            if (s >= a.Wo) { s -= a.Wo; ++r; }
+        for (int r = g; r < a.Ho; r += G) {
+            const float *xr = s_x + (r * a.stride + u) * Wp;
+            const float *dr = s_d + r * a.Wo;
+            if (a.stride == 1) {
+                float w[K];
+#pragma unroll
+                for (int v = 0; v < K - 1; ++v) w[v] = xr[v];
+                for (int s = 0; s < a.Wo; ++s) {
+                    w[K - 1] = xr[s + K - 1];
+                    const float d = dr[s];
+#pragma unroll
+                    for (int v = 0; v < K; ++v) part[v] += d * w[v];
+#pragma unroll
+                    for (int v = 0; v < K - 1; ++v) w[v] = w[v + 1];
+                }
+            } else {
+                for (int s = 0; s < a.Wo; ++s) {
+                    const float d = dr[s];
+                    const float *xs = xr + s * a.stride;
+#pragma unroll
+                    for (int v = 0; v < K; ++v) part[v] += d * xs[v];
+                }
+            }
         }
+#pragma unroll
+        for (int v = 0; v < K; ++v) s_part[g * KK + u * K + v] = part[v];
     }
-    s_part[tid] = part;
     __syncthreads();
     if (tid < KK) {
         float sum = 0.f;
@@ -534,7 +548,7 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
                                    hipStream_t stream) {
     WgArgs a;
     a.B = g.B; a.Cin = g.Cin; a.H = g.H; a.W = g.W; a.Cout = g.Cout; a.KW = g.KW;
-    a.stride = g.stride; a.pad = g.pad; a.Wo = g.Wo; a.P = g.P; a.KT = g.KT;
+    a.stride = g.stride; a.pad = g.pad; a.Ho = g.Ho; a.Wo = g.Wo; a.P = g.P; a.KT = g.KT;
     a.Kdim = g.cpg * g.KT;
     a.n_ktiles = ceil_div(a.Kdim, 64);
     a.dy_vec = g.P % 4 == 0;

@@ -63,6 +63,7 @@ BWD_CASES = [
     (2, 32, 160, 8, 8, 3, 1, 1, 1, 16, "bf16"),     # 16 experts, two 128-channel output tiles
     (3, 16, 16, 11, 9, 3, 2, 1, 16, 5, "bf16"),     # depthwise 3x3, stride 2 (data gradient declines)
     (2, 8, 8, 12, 12, 7, 1, 3, 8, 3, "bf16"),       # depthwise 7x7 (bounds-checked kernel)
+    (2, 64, 64, 20, 20, 3, 1, 1, 1, 4, "bf16"),     # 3x3 kernel gradient in two row bands (12 + 8 rows)
 ]
 
 
