@@ -20,6 +20,7 @@ stream the kernels run on) and the CPU oracle timed on a bounded sample.
     python bench.py [--steps K] [--warmup W] [--workload KEY] [--no-cpu-baseline]
     python bench.py --profile       # short run for rocprofv3 (no CPU leg)
     python bench.py --calib-copy    # plain device copy of known size (counter calibration)
+    python bench.py --backward      # training step: forward + backward (single-layer workloads)
 """
 from __future__ import annotations
 
@@ -64,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true", help="few steps, no CPU leg")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="training step: forward, then the weight, input and routing gradients")
     return ap.parse_args()
 
 
@@ -134,6 +137,9 @@ def main():
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
+        return
+    if args.backward:
+        train_main(args)
         return
     import numpy as np
     import torch
@@ -381,6 +387,192 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_train(w, d, dy):
+    """The oracle's training step (route, forward, gradients of the layer and of
+    the routing, float64 direct loops) on sub-batches of the same workload until
+    CPU_SAMPLE_SECONDS have passed."""
+    import oracle
+    L = w.layers[0]
+    sub = min(w.B, 8)
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        lo = done % w.B
+        hi = min(lo + sub, w.B)
+        x = d["x"][lo:hi]
+        alpha, _, _ = oracle.route(x, d["fc_w"], d["fc_b"], w.route_mode, w.temperature)
+        oracle.forward(x, d["experts"][0], alpha, L.stride, L.pad, L.groups)
+        _, da, _ = oracle.backward(x, d["experts"][0], alpha, dy[lo:hi], L.stride, L.pad, L.groups)
+        oracle.route_backward(x, d["fc_w"], d["fc_b"], da, w.route_mode, w.temperature)
+        done += hi - lo
+        dt = time.perf_counter() - t0
+        if dt >= CPU_SAMPLE_SECONDS:
+            break
+    return {"value": round(done / dt, 3), "unit": "images/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} examples of {w.key} in sub-batches of {sub} (route, forward, dx, dalpha, "
+                      f"dE and routing gradients, float64 direct loops), {dt:.1f} s"}
+
+
+def train_main(args):
+    """Training step of a single-layer workload: route, forward, then
+    dynconv_backward_weights (dalpha, dE), dynconv_backward_data (dx) and
+    dynconv_route_backward (dfc_w, dfc_b, pooling share added to dx), with the
+    output gradient dy synthetic and resident like x."""
+    import numpy as np
+    import torch
+    from dynamic_convolution_cnn_amd import binding as bd
+    from dynamic_convolution_cnn_amd import inputs
+
+    if args.profile:
+        args.steps, args.warmup, args.no_cpu_baseline = min(args.steps, 10), min(args.warmup, 3), True
+    w = inputs.WORKLOADS[args.workload]
+    if len(w.layers) != 1 or w.attention:
+        print(f"bench.py --backward: {w.key} is not a single-layer workload without channel attentions",
+              file=sys.stderr)
+        sys.exit(2)
+    L = w.layers[0]
+    d = inputs.make_inputs(w, seed=0)
+    dy_host = inputs.bf16_round(np.random.default_rng(1).standard_normal((w.B, L.Cout, L.Ho, L.Wo),
+                                                                         dtype=np.float32))
+    if w.dtype != "bf16":
+        dy_host = np.random.default_rng(1).standard_normal((w.B, L.Cout, L.Ho, L.Wo), dtype=np.float32)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    e = to_dev(d["experts"][0], w.dtype)
+    fc_w, fc_b = to_dev(d["fc_w"], "f32"), to_dev(d["fc_b"], "f32")
+    x0, dy0 = to_dev(d["x"], w.dtype), to_dev(dy_host, w.dtype)
+    esz = 2 if w.dtype == "bf16" else 4
+    set_bytes = w.B * (2 * L.Cin * L.H * L.W + 2 * L.Cout * L.Ho * L.Wo) * esz
+    R = max(1, math.ceil(ROTATE_BYTES / set_bytes))
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    dys = [dy0] + [dy0.clone() for _ in range(R - 1)]
+    ys = [torch.empty((w.B, L.Cout, L.Ho, L.Wo), dtype=x0.dtype, device=dev) for _ in range(R)]
+    dxs = [torch.empty_like(x0) for _ in range(R)]
+    alphas = [torch.empty((w.B, w.n), dtype=torch.float32, device=dev) for _ in range(R)]
+    das = [torch.empty((w.B, w.n), dtype=torch.float32, device=dev) for _ in range(R)]
+    de = torch.empty(tuple(e.shape), dtype=torch.float32, device=dev)
+    dfw = torch.empty((w.n, L.Cin), dtype=torch.float32, device=dev)
+    dfb = torch.empty((w.n,), dtype=torch.float32, device=dev)
+    desc = bd.layer_desc(x0, e, L.stride, L.pad, L.groups)
+    pol = bd.dynconv_forward_policy(desc)
+    ws_f = torch.empty(max(16, bd.dynconv_forward_workspace_bytes(desc, pol)), dtype=torch.uint8, device=dev)
+    ws_w = torch.empty(max(16, bd.dynconv_backward_weights_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(16, bd.dynconv_backward_data_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+    rdesc = bd.make_desc(w.B, L.Cin, L.H, L.W, n=w.n, dtype=desc.dtype)
+    ws_r = torch.empty(max(16, bd.dynconv_route_workspace_bytes(rdesc)), dtype=torch.uint8, device=dev)
+    ws_rb = torch.empty(max(16, bd.dynconv_route_backward_workspace_bytes(rdesc)), dtype=torch.uint8, device=dev)
+
+    def bwd_weights(i):
+        s = i % R
+        bd.dynconv_backward_weights(xs[s], dys[s], e, alphas[s], L.stride, L.pad, L.groups, dalpha=das[s],
+                                    dexperts=de, workspace=ws_w)
+
+    def step(i, ev=None):
+        s = i % R
+        cur = torch.cuda.current_stream()
+        marks = []
+
+        def mark():
+            if ev is not None:
+                ev[len(marks)].record(cur)
+                marks.append(1)
+        mark()
+        bd.dynconv_route(xs[s], fc_w, fc_b, w.route_mode, w.temperature, alpha=alphas[s], workspace=ws_r)
+        mark()
+        bd.dynconv_forward(xs[s], e, alphas[s], L.stride, L.pad, L.groups, policy=pol, y=ys[s], workspace=ws_f)
+        mark()
+        bwd_weights(s)
+        mark()
+        bd.dynconv_backward_data(dys[s], e, alphas[s], L.H, L.W, L.stride, L.pad, L.groups, dx=dxs[s],
+                                 workspace=ws_d)
+        mark()
+        bd.dynconv_route_backward(xs[s], fc_w, alphas[s], das[s], w.route_mode, w.temperature, dx=dxs[s],
+                                  dfc_w=dfw, dfc_b=dfb, workspace=ws_rb)
+        mark()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    G = GRAPH_STEPS
+
+    def capture(first, count, fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(count):
+                fn(first + j)
+        return g
+
+    multi = [capture(s, G, step) for s in range(R)]
+    single = [capture(s, 1, step) for s in range(R)]
+    plan, i = [], 0
+    while i + G <= args.steps:
+        plan.append(multi[i % R]); i += G
+    while i < args.steps:
+        plan.append(single[i % R]); i += 1
+    multi[0].replay(); single[0].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in plan:
+        g.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the dominant call, dynconv_backward_weights, back to back on the launch stream
+    NC = 2 if args.profile else 10
+    gw = capture(0, G, bwd_weights)
+    gw.replay()
+    torch.cuda.synchronize()
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record(stream)
+    for _ in range(NC):
+        gw.replay()
+    cev[1].record(stream)
+    torch.cuda.synchronize()
+    bw_ms = cev[0].elapsed_time(cev[1]) / (NC * G)
+
+    # per-call times of eager steps, HIP events between the calls
+    nk = min(args.steps, 20)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nk)]
+    for i in range(nk):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    names = ["route", "forward", "backward_weights", "backward_data", "route_backward"]
+    per = {nm: round(sum(ev[k].elapsed_time(ev[k + 1]) for ev in evs) / nk * 1e3, 2) for k, nm in enumerate(names)}
+    per["backward_weights_back_to_back"] = round(bw_ms * 1e3, 2)
+
+    # the kernel-gradient GEMM's work: 2 B Cout Ho Wo (Cin/g) k^2 FLOP, the same as the forward's
+    gemm_flops = 2 * w.B * L.macs_per_example()
+    bw_tflops = gemm_flops / (bw_ms * 1e-3) / 1e12
+    step_flops = 3 * gemm_flops  # forward, kernel gradient and input gradient convolutions
+    out = {
+        "metric": METRIC,
+        "value": round(w.B / (ms_per_step * 1e-3), 1),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded numpy draws, shapes of the pages' networks; no dataset)",
+        "config": {"workload": w.key, "title": w.title, "B": w.B, "n": w.n, "pass": "forward+backward",
+                   "layers": [dict(Cin=L.Cin, Cout=L.Cout, H=L.H, W=L.W, k=L.k, stride=L.stride, pad=L.pad,
+                                   groups=L.groups)],
+                   "routing": "softmax(z/T)" if w.route_mode else "sigmoid", "rotating_sets": R},
+        "tflops_step": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "pct_bf16_peak_step": round(100 * step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernels_us": per,
+        "roofline": {"kernel": "dynconv_backward_weights (kernel-gradient GEMM; contraction of dW_b into dalpha, dE)",
+                     "bound": "mfma", "achieved": round(bw_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bw_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_train(w, d, dy_host)
     print(json.dumps(out), flush=True)
 
 

@@ -387,15 +387,17 @@ __global__ __launch_bounds__(256) void dE_reduce_kernel(const float *__restrict_
     de[j] = s;
 }
 
-// dalpha[b][i] = sum over chunks of dpart[b][i][ch], in chunk order.
+// dalpha[b][i] = sum over chunks of dpart[b][i][ch]: one wave per (b, i);
+// lane l adds chunks l, l + 64, ... in order, then a fixed-tree wave sum.
 __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float *__restrict__ dpart,
                                                             float *__restrict__ dalpha, int total, int nch) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (idx >= total) return;
     const float *p = dpart + (long)idx * nch;
     float s = 0.f;
-    for (int c = 0; c < nch; ++c) s += p[c];
-    dalpha[idx] = s;
+    for (int c = lane; c < nch; c += 64) s += p[c];
+    s = wave_sum(s);
+    if (lane == 0) dalpha[idx] = s;
 }
 
 // ---- routing gradient -----------------------------------------------------------
@@ -434,33 +436,50 @@ __global__ __launch_bounds__(256) void route_dz_kernel(const float *__restrict__
     }
 }
 
-// dfc_w[i][c] = sum_b dz[b][i] gap[b][c] (thread per (i, c)); the threads
-// of column c == 0 also write dfc_b[i] = sum_b dz[b][i].
+// dfc_w[i][c] = sum_b dz[b][i] gap[b][c] and dfc_b[i] = sum_b dz[b][i].
+// Workgroup (i, 32-channel chunk): thread (c, g) sums the examples
+// g, g + 8, ... of channel c; the 8 partial sums are added in LDS in group order.
 __global__ __launch_bounds__(256) void route_dfc_kernel(const float *__restrict__ dz, const float *__restrict__ gap,
                                                         float *__restrict__ dfc_w, float *__restrict__ dfc_b,
                                                         int B, int n, int C) {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)n * C) return;
-    const int i = (int)(idx / C), c = (int)(idx - (long)i * C);
+    __shared__ float s_w[8][32];
+    __shared__ float s_b[8][32];
+    const int i = blockIdx.x, cl = threadIdx.x & 31, gr = threadIdx.x >> 5;
+    const int c = blockIdx.y * 32 + cl;
     float acc = 0.f, accb = 0.f;
-    for (int b = 0; b < B; ++b) {
-        const float z = dz[(long)b * n + i];
-        acc += z * gap[(long)b * C + c];
-        accb += z;
+    if (c < C) {
+#pragma unroll 4
+        for (int b = gr; b < B; b += 8) {
+            const float z = dz[(long)b * n + i];
+            acc += z * gap[(long)b * C + c];
+            accb += z;
+        }
     }
-    dfc_w[idx] = acc;
-    if (c == 0 && dfc_b) dfc_b[i] = accb;
+    s_w[gr][cl] = acc;
+    s_b[gr][cl] = accb;
+    __syncthreads();
+    if (gr == 0 && c < C) {
+        float w = 0.f, wb = 0.f;
+        for (int k = 0; k < 8; ++k) {
+            w += s_w[k][cl];
+            wb += s_b[k][cl];
+        }
+        dfc_w[(long)i * C + c] = w;
+        if (c == 0 && dfc_b) dfc_b[i] = wb;
+    }
 }
 
 // dx[b][c][h][w] += dgap[b][c] / (H W): the pooling's share of the input
-// gradient, added in float32 and rounded once to the element type.
-template <typename T>
+// gradient, added in float32 and rounded once to the element type. VEC
+// consecutive elements per thread (VEC divides H W, so they share a plane).
+template <typename T, int VEC>
 __global__ __launch_bounds__(256) void add_pool_grad_kernel(T *__restrict__ dx, const float *__restrict__ dgap,
                                                             long total, int hw, float inv_hw) {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const long idx = ((long)blockIdx.x * 256 + threadIdx.x) * VEC;
     if (idx >= total) return;
-    const float v = Elem<T>::to_f32(dx[idx]) + dgap[idx / hw] * inv_hw;
-    dx[idx] = Elem<T>::from_f32(v);
+    const float add = dgap[idx / hw] * inv_hw;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) dx[idx + j] = Elem<T>::from_f32(Elem<T>::to_f32(dx[idx + j]) + add);
 }
 
 unsigned blocks_for(long total) { return (unsigned)((total + 255) / 256); }
@@ -605,8 +624,8 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
     }
     if (!dalpha) return hipSuccess;
     const int total = g.B * g.n;
-    hipLaunchKernelGGL(dalpha_reduce_kernel, dim3(blocks_for(total)), dim3(256), 0, stream, dpart, dalpha, total,
-                       contract_chunks(g));
+    hipLaunchKernelGGL(dalpha_reduce_kernel, dim3((unsigned)ceil_div(total, 4)), dim3(256), 0, stream, dpart, dalpha,
+                       total, contract_chunks(g));
     return hipGetLastError();
 }
 
@@ -619,19 +638,28 @@ hipError_t launch_route_backward(const Geom &g, const void *x, const float *fc_w
                        g.n, g.Cin, mode, mode == 1 ? 1.f / temperature : 1.f);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long nc = (long)g.n * g.Cin;
-    hipLaunchKernelGGL(route_dfc_kernel, dim3(blocks_for(nc)), dim3(256), 0, stream, dz, gap, dfc_w, dfc_b, g.B,
-                       g.n, g.Cin);
+    hipLaunchKernelGGL(route_dfc_kernel, dim3((unsigned)g.n, (unsigned)ceil_div(g.Cin, 32)), dim3(256), 0, stream,
+                       dz, gap, dfc_w, dfc_b, g.B, g.n, g.Cin);
     e = hipGetLastError();
     if (e != hipSuccess || !dx) return e;
     const long total = (long)g.B * g.Cin * g.H * g.W;
     const int hw = g.H * g.W;
-    if (g.bf16)
-        hipLaunchKernelGGL(add_pool_grad_kernel<uint16_t>, dim3(blocks_for(total)), dim3(256), 0, stream,
-                           static_cast<uint16_t *>(dx), dgap, total, hw, 1.f / (float)hw);
-    else
-        hipLaunchKernelGGL(add_pool_grad_kernel<float>, dim3(blocks_for(total)), dim3(256), 0, stream,
-                           static_cast<float *>(dx), dgap, total, hw, 1.f / (float)hw);
+    const float inv = 1.f / (float)hw;
+    if (hw % 8 == 0) {
+        const unsigned nb = blocks_for(total / 8);
+        if (g.bf16)
+            hipLaunchKernelGGL((add_pool_grad_kernel<uint16_t, 8>), dim3(nb), dim3(256), 0, stream,
+                               static_cast<uint16_t *>(dx), dgap, total, hw, inv);
+        else
+            hipLaunchKernelGGL((add_pool_grad_kernel<float, 8>), dim3(nb), dim3(256), 0, stream,
+                               static_cast<float *>(dx), dgap, total, hw, inv);
+    } else if (g.bf16) {
+        hipLaunchKernelGGL((add_pool_grad_kernel<uint16_t, 1>), dim3(blocks_for(total)), dim3(256), 0, stream,
+                           static_cast<uint16_t *>(dx), dgap, total, hw, inv);
+    } else {
+        hipLaunchKernelGGL((add_pool_grad_kernel<float, 1>), dim3(blocks_for(total)), dim3(256), 0, stream,
+                           static_cast<float *>(dx), dgap, total, hw, inv);
+    }
     return hipGetLastError();
 }
 
