@@ -345,17 +345,40 @@ __global__ __launch_bounds__(256) void contract_kernel(const float *__restrict__
             for (int uu = 0; uu < kCtU; ++uu) {
                 if (u0 + uu >= nb) break;
                 const int b = b0 + u0 + uu;
+                float part[NE];
 #pragma unroll
                 for (int k = 0; k < NE; ++k) {
                     const float al = i0 + k < n ? alpha[(long)b * n + i0 + k] : 0.f;
-                    float part = 0.f;
+                    part[k] = 0.f;
 #pragma unroll
                     for (int j = 0; j < VEC; ++j) {
                         acc[k][j] += al * d[uu][j];
-                        part += d[uu][j] * ev[k][j];
+                        part[k] += d[uu][j] * ev[k][j];
                     }
-                    part = wave_sum(part);
-                    if (lane == 0) s_red[wave][u0 + uu][k] = part;
+                }
+                // transpose-reduce: each halving step swaps half of the
+                // partials with the partner lane (xor m) and adds, so after
+                // log2(NE) steps lane L holds the partial of expert
+                // bitrev(L mod NE); xor steps over the other lane bits finish
+                // the sums in lanes 0 .. NE - 1 (fixed order: deterministic)
+#pragma unroll
+                for (int h = NE / 2, m = 1; h >= 1; h >>= 1, m <<= 1) {
+                    const bool up = (lane & m) != 0;
+#pragma unroll
+                    for (int j = 0; j < h; ++j) {
+                        const float send = up ? part[j] : part[j + h];
+                        const float keep = up ? part[j + h] : part[j];
+                        part[j] = keep + __shfl_xor(send, m, 64);
+                    }
+                }
+#pragma unroll
+                for (int m = NE; m < 64; m <<= 1) part[0] += __shfl_xor(part[0], m, 64);
+                if (lane < NE) {
+                    int k = 0;
+#pragma unroll
+                    for (int bit = 1, val = NE / 2; bit < NE; bit <<= 1, val >>= 1)
+                        if (lane & bit) k += val;
+                    s_red[wave][u0 + uu][k] = part[0];
                 }
             }
         }
