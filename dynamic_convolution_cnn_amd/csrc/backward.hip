@@ -676,6 +676,14 @@ hipError_t launch_route_backward(const Geom &g, const void *x, const float *fc_w
         else
             hipLaunchKernelGGL((add_pool_grad_kernel<float, 8>), dim3(nb), dim3(256), 0, stream,
                                static_cast<float *>(dx), dgap, total, hw, inv);
+    } else if (hw % 4 == 0) {
+        const unsigned nb = blocks_for(total / 4);
+        if (g.bf16)
+            hipLaunchKernelGGL((add_pool_grad_kernel<uint16_t, 4>), dim3(nb), dim3(256), 0, stream,
+                               static_cast<uint16_t *>(dx), dgap, total, hw, inv);
+        else
+            hipLaunchKernelGGL((add_pool_grad_kernel<float, 4>), dim3(nb), dim3(256), 0, stream,
+                               static_cast<float *>(dx), dgap, total, hw, inv);
     } else if (g.bf16) {
         hipLaunchKernelGGL((add_pool_grad_kernel<uint16_t, 1>), dim3(blocks_for(total)), dim3(256), 0, stream,
                            static_cast<uint16_t *>(dx), dgap, total, hw, inv);
