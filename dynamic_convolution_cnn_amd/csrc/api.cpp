@@ -86,6 +86,9 @@ dynconv_status_t check_desc(const dynconv_desc_t *d, dynconv::Geom &g, bool need
 long kernel_elems(const dynconv::Geom &g) { return (long)g.Cout * g.cpg * g.KT; }
 size_t esize(const dynconv::Geom &g) { return g.bf16 ? 2 : 4; }
 bool depthwise(const dynconv::Geom &g) { return g.groups != 1; }
+// bf16 groups == 1 layers with more than 16 experts mix on the matrix cores
+// from a bank in the convolution's weight order (KernelWarehouse's n > 100)
+bool wide(const dynconv::Geom &g) { return g.bf16 && g.groups == 1 && g.n_pad > 16; }
 
 // Resolve AUTO and check that the chosen path exists for this layer.
 dynconv_status_t resolve_policy(const dynconv::Geom &g, int32_t policy, int32_t &out) {
@@ -105,14 +108,15 @@ dynconv_status_t resolve_policy(const dynconv::Geom &g, int32_t policy, int32_t 
         out = DYNCONV_POLICY_PREMIX;
         return DYNCONV_OK;
     }
-    if (g.n_pad > 16)
-        return fail(DYNCONV_ERR_UNSUPPORTED, "bf16 layers with groups == 1 support n <= 16 experts (got %d)", g.n);
-    const bool fused_ok = dynconv::fused_conv_supported(g);
+    if (wide(g) && !dynconv::pack_wide_supported(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "more than 16 experts: one expert's Cin x kh x kw block must fit 64 KB");
+    const bool fused_ok = g.n_pad <= 16 && dynconv::fused_conv_supported(g);
     const bool premix_ok = dynconv::premix_conv_supported(g);
     if (policy == DYNCONV_POLICY_FUSED) {
         if (!fused_ok)
             return fail(DYNCONV_ERR_UNSUPPORTED,
-                        "fused path needs n <= 4, even W, Ho*Wo <= 256 and the 4 example tiles in LDS (Ho*Wo=%d)", g.P);
+                        "fused path needs n <= 4, even W, Ho*Wo <= 256 and the 4 example tiles in LDS (n=%d, Ho*Wo=%d)",
+                        g.n, g.P);
         out = policy;
         return DYNCONV_OK;
     }
@@ -137,6 +141,8 @@ size_t forward_ws(const dynconv::Geom &g, int32_t policy) {
     if (depthwise(g))
         return policy == DYNCONV_POLICY_PREMIX ? round_up((size_t)g.B * kernel_elems(g) * esize(g), kWsAlign) : 0;
     if (!g.bf16) return round_up((size_t)g.B * kernel_elems(g) * sizeof(float), kWsAlign);
+    if (wide(g))  // many experts: the bank in the conv's weight order, then W_b
+        return round_up(dynconv::wide_bank_bytes(g), kWsAlign) + round_up(dynconv::premixed_bytes(g), kWsAlign);
     size_t ws = round_up(dynconv::packed_experts_bytes(g), kWsAlign);
     if (policy == DYNCONV_POLICY_PREMIX) ws += round_up(dynconv::premixed_bytes(g), kWsAlign);
     return ws;
@@ -182,6 +188,8 @@ dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const 
         (att.in && !aligned16(att.in)) || (att.out && !aligned16(att.out)))
         return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
     const bool attn = att.in || att.out;
+    if (attn && wide(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "channel attentions support n <= 16 experts on bf16 groups == 1 layers");
     int32_t p;
     if (attn && !depthwise(g) && g.bf16) {
         if (policy == DYNCONV_POLICY_FUSED)
@@ -215,6 +223,17 @@ dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const 
                                                           reinterpret_cast<const float *>(ws),
                                                           static_cast<float *>(y), st, att),
                           "dynconv_forward conv launch");
+    }
+    if (wide(g)) {
+        uint16_t *bank = reinterpret_cast<uint16_t *>(ws);
+        uint16_t *wt = reinterpret_cast<uint16_t *>(ws + round_up(dynconv::wide_bank_bytes(g), kWsAlign));
+        e = dynconv::launch_pack_wide(g, static_cast<const uint16_t *>(experts), bank, st);
+        if (e != hipSuccess) return hip_status(e, "dynconv_forward wide pack launch");
+        e = dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st);
+        if (e != hipSuccess) return hip_status(e, "dynconv_forward wide mix launch");
+        return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
+                                                      static_cast<uint16_t *>(y), st),
+                          "convolution launch");
     }
     uint16_t *packed = reinterpret_cast<uint16_t *>(ws);
     e = dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), packed, st);
@@ -349,6 +368,7 @@ size_t dynconv_forward_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t 
     int32_t p;
     const int32_t want = (!depthwise(g) && g.bf16) ? DYNCONV_POLICY_PREMIX : policy;
     if (policy == DYNCONV_POLICY_FUSED && !depthwise(g) && g.bf16) return 0;
+    if (wide(g)) return 0;  // channel attentions: n <= 16 on bf16 groups == 1 layers
     if (resolve_policy(g, want, p) != DYNCONV_OK) return 0;
     return forward_ws(g, p);
 }

@@ -778,9 +778,10 @@ hipError_t launch_premix_cfg(const Geom &g, const uint16_t *x, const uint16_t *w
 
 }  // namespace
 
+// The convolution reads W_b only (any expert count: the mix that fills it
+// depends on n, this kernel does not).
 bool premix_conv_supported(const Geom &g) {
-    return g.bf16 && g.groups == 1 && g.n_pad <= 16 &&
-           premix_lds_bytes(g, pick_premix(g)) <= (size_t)kLdsBudget;
+    return g.bf16 && g.groups == 1 && premix_lds_bytes(g, pick_premix(g)) <= (size_t)kLdsBudget;
 }
 
 // The 32x32x16 premix kernel: bf16 3x3 stride-1 layers with W even (position

@@ -61,6 +61,18 @@ size_t packed_experts_bytes(const Geom &g);
 hipError_t launch_pack_experts(const Geom &g, const uint16_t *experts,
                                uint16_t *packed, hipStream_t stream);
 
+// Many experts (bf16): mixed[b][w] = sum_i alpha[b,i] bank[i][w] for a bank
+// of n rows of wsize weights (wsize a multiple of 8), on the matrix cores
+// with the experts as the reduction dimension; any n.
+bool mix_wide_supported(long wsize);
+hipError_t launch_mix_wide(const Geom &g, long wsize, const float *alpha, const uint16_t *experts, uint16_t *mixed,
+                           hipStream_t stream);
+// The natural bank in the convolution's weight order, wide[i][t][o][cp]
+// (bf16, zeros for cp >= Cin): the forward's bank for n > 16.
+size_t wide_bank_bytes(const Geom &g);
+bool pack_wide_supported(const Geom &g);  // one expert's Cin x KT block fits 64 KB of LDS
+hipError_t launch_pack_wide(const Geom &g, const uint16_t *experts, uint16_t *wide, hipStream_t stream);
+
 // Mixed kernels in the convolution's layout wt[b][t][o][cp] (bf16) from
 // the packed bank.
 size_t premixed_bytes(const Geom &g);

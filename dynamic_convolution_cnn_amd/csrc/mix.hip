@@ -549,6 +549,9 @@ hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha, con
             if (g.n <= 4) return go(mix_natural_all_kernel<uint16_t, 4>, mix_natural_all_kernel<float, 4>);
             return go(mix_natural_all_kernel<uint16_t, 8>, mix_natural_all_kernel<float, 8>);
         }
+        if (g.bf16 && g.n > 16 * kMixMfmaMaxG) return launch_mix_wide(g, wsize, alpha,
+                                                                      static_cast<const uint16_t *>(experts),
+                                                                      static_cast<uint16_t *>(mixed), stream);
         if (g.bf16 && g.n <= 16 * kMixMfmaMaxG) {
             const dim3 mgrid((unsigned)((wsize + kMixMW - 1) / kMixMW), (unsigned)((g.B + kMixEx - 1) / kMixEx));
             auto go = [&](auto kern) {

@@ -130,6 +130,13 @@ WORKLOADS: Dict[str, Workload] = {
         title="FMDConv multi-attention on the ResNet-18-shaped 3x3, B=32, 64->64, 56x56, n=4, softmax(z/4), bf16",
         B=32, n=4, dtype="bf16", route_mode=SOFTMAX, temperature=4.0, attention=True,
         layers=(Layer(64, 64, 56, 56, 3, 1, 1),)),
+    # KernelWarehouse's setting of more than 100 experts (n > 100) on the
+    # many-expert layer's shape; not one of the five configurations
+    "kernelwarehouse_n128": Workload(
+        key="kernelwarehouse_n128",
+        title="KernelWarehouse-scale bank: 3x3, B=64, 128->128, 28x28, n=128, softmax(z/4), bf16",
+        B=64, n=128, dtype="bf16", route_mode=SOFTMAX, temperature=4.0, fc_std=None,
+        layers=(Layer(128, 128, 28, 28, 3, 1, 1),)),
 }
 
 # The order the workloads are listed in: the tiny parity case first, the

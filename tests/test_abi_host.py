@@ -93,7 +93,8 @@ def test_forward_unsupported_layers():
     assert fwd(good_desc(H=32, W=32), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
     assert fwd(good_desc(n=5), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
     # bf16 groups == 1 supports up to 16 experts
-    assert fwd(good_desc(n=17)) == bd.DYNCONV_ERR_UNSUPPORTED
+    # more than 16 experts: PREMIX from the wide bank, no fused path
+    assert fwd(good_desc(n=17), policy=bd.DYNCONV_POLICY_FUSED) == bd.DYNCONV_ERR_UNSUPPORTED
 
 
 def test_forward_workspace_checks():
@@ -317,3 +318,25 @@ def test_route_backward_checks():
     assert rb(mode=bd.DYNCONV_SOFTMAX, t=float("inf")) == bd.DYNCONV_ERR_INVALID_ARG
     assert rb(desc=good_desc(n=300), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
     assert rb(wsb=bd.dynconv_route_backward_workspace_bytes(d) - 1) == bd.DYNCONV_ERR_WORKSPACE
+
+
+def test_many_expert_forward_checks():
+    """bf16 groups == 1 with n > 16: PREMIX from a bank in the conv's weight order."""
+    L = _lib()
+    r256 = lambda v: (v + 255) // 256 * 256
+    d = good_desc(Cin=40, Cout=72, n=128)
+    assert bd.dynconv_forward_policy(d) == bd.DYNCONV_POLICY_PREMIX
+    cin_pad = 64
+    want = r256(128 * 9 * 72 * cin_pad * 2) + r256(2 * 9 * 72 * cin_pad * 2)
+    assert bd.dynconv_forward_workspace_bytes(d) == want
+    assert bd.dynconv_forward_workspace_bytes(d, bd.DYNCONV_POLICY_FUSED) == 0
+    assert L.dynconv_forward(ctypes.byref(d), bd.DYNCONV_POLICY_FUSED, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                             None) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert L.dynconv_forward(ctypes.byref(d), bd.DYNCONV_POLICY_AUTO, FAKE, FAKE, FAKE, FAKE, FAKE, want - 1,
+                             None) == bd.DYNCONV_ERR_WORKSPACE
+    # channel attentions stay at n <= 16 on these layers
+    assert bd.dynconv_forward_attn_workspace_bytes(d) == 0
+    assert L.dynconv_forward_attn(ctypes.byref(d), bd.DYNCONV_POLICY_AUTO, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 30, None) == bd.DYNCONV_ERR_UNSUPPORTED
+    # the packed-bank entry points keep n <= 16
+    assert bd.dynconv_packed_experts_bytes(d) == 0

@@ -338,3 +338,25 @@ def test_attention_layer_matches_torch_conv2d():
         ref = F.conv2d(xt, torch.from_numpy(e[0].astype(np.float64)), stride=st, padding=p, groups=g)
         ref = (ref * torch.from_numpy(a_out)[:, :, None, None]).numpy()
         np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("n", [101, 128])
+def test_many_experts_one_hot_and_linearity(n):
+    """KernelWarehouse's n > 100 (KernelWarehouse, abstract): with one-hot
+    attentions the layer equals one expert's ordinary convolution (torch conv2d
+    in float64); and the layer is linear in the attentions across the whole bank."""
+    B, Cin, Cout, H, W = 2, 3, 4, 5, 6
+    x = _rand((B, Cin, H, W), 31)
+    e = _rand((n, Cout, Cin, 3, 3), 32)
+    for k in (0, n // 2, n - 1):
+        a = np.zeros((B, n))
+        a[:, k] = 1.0
+        y = oracle.forward(x, e, a, 1, 1, 1)
+        np.testing.assert_allclose(y, _torch_conv(x, e[k], 1, 1, 1), rtol=1e-12, atol=1e-12)
+    rng = np.random.default_rng(33)
+    a1, a2 = rng.random((B, n)), rng.random((B, n))
+    y12 = oracle.forward(x, e, a1 + a2, 1, 1, 1)
+    y1, y2 = oracle.forward(x, e, a1, 1, 1, 1), oracle.forward(x, e, a2, 1, 1, 1)
+    np.testing.assert_allclose(y12, y1 + y2, rtol=1e-11, atol=1e-11)
+    m = oracle.mix(a1, e)
+    np.testing.assert_allclose(oracle.mix(a1 + a2, e), m + oracle.mix(a2, e), rtol=1e-12, atol=1e-12)
