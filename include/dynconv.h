@@ -132,7 +132,12 @@ dynconv_status_t dynconv_mix(const dynconv_desc_t *desc, const float *alpha,
  * fused kernel does not cover). workspace: at least
  * dynconv_forward_workspace_bytes(desc, policy) bytes of device memory
  * (contents on entry do not matter; clobbered). Deterministic: two calls on
- * the same inputs give bitwise-equal y. */
+ * the same inputs give bitwise-equal y. bf16 layers with groups == 1 and
+ * more than 16 experts (KernelWarehouse abstract: n > 100) run on
+ * DYNCONV_POLICY_PREMIX only (FUSED returns DYNCONV_ERR_UNSUPPORTED): the
+ * bank is put in the convolution's weight order and mixed on the matrix
+ * cores with the experts as the reduction dimension; one expert's
+ * Cin * kh * kw bf16 values must fit 64 KB. */
 dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy,
                                  const void *x, const void *experts,
                                  const float *alpha, void *y, void *workspace,
@@ -140,7 +145,7 @@ dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy,
 size_t dynconv_forward_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
 
 /* Expert bank in the layout the bf16 MFMA convolution reads (bf16 layers with
- * groups == 1 only): packed[t][o][c'][i'] with t = kh*kw tap (row-major),
+ * groups == 1 and at most 16 experts only): packed[t][o][c'][i'] with t = kh*kw tap (row-major),
  * o = output channel, c' < Cin rounded up to 32 (zero beyond Cin), and
  * i' < n rounded up to even (zero beyond n), so that two experts' values of
  * one kernel element share a 32-bit word. A pure layout transform of the
@@ -193,8 +198,9 @@ size_t dynconv_route_attn_workspace_bytes(const dynconv_desc_t *desc);
 
 /* dynconv_forward with the channel attentions a_in [B,Cin] and a_out
  * [B,Cout] (float32; either may be NULL, meaning all ones). bf16 layers with
- * groups == 1 run on DYNCONV_POLICY_PREMIX (AUTO resolves to it; FUSED
- * returns DYNCONV_ERR_UNSUPPORTED): the input attention scales the premixed
+ * groups == 1 (at most 16 experts; more return DYNCONV_ERR_UNSUPPORTED) run
+ * on DYNCONV_POLICY_PREMIX (AUTO resolves to it; FUSED returns
+ * DYNCONV_ERR_UNSUPPORTED): the input attention scales the premixed
  * kernels' input channels before their bf16 rounding and the output
  * attention scales the accumulators before the bf16 output. Depthwise layers
  * scale each plane's taps by a_in[b,c] * a_out[b,c] before their rounding to
