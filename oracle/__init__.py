@@ -24,6 +24,12 @@ cites the passage of the pages it follows:
   input and output (FMDConv: Fast multi-attention dynamic convolution,
   abstract, which names them without a formula; the reading is stated at
   ``forward_attn``). Each head is a route (GAP -> FC -> sigmoid) of its own.
+* spatially sparse evaluation - "a small gating branch learns which spatial
+  positions should be evaluated" in a residual block, run with a
+  gather-scatter approach (Dynamic Convolutions: Exploiting Spatial Sparsity
+  for Faster Inference, abstract). ``forward_sparse`` takes the gate as a
+  given mask: the layer's output at the masked positions only, plus the
+  block's input when the block is residual.
 * gradients - the pages train these layers end to end ("learn specialized
   convolutional kernels", CondConv abstract; "learns a linear mixture",
   KernelWarehouse abstract) but print no backward pass. ``backward`` and
@@ -297,3 +303,24 @@ def route_backward(x, fc_w, fc_b, dalpha, mode: int = SIGMOID, temperature: floa
     B, C, H, W = np.shape(x)
     dx = np.broadcast_to((dgap / float(H * W))[:, :, None, None], (B, C, H, W)).copy()
     return dfc_w, dfc_b, dgap, dx
+
+
+def forward_sparse(x, experts, alpha, mask, stride: int = 1, pad: int = 0, groups: int = 1,
+                   residual: bool = False) -> np.ndarray:
+    """The layer evaluated at the positions a gate selects (Dynamic
+    Convolutions: Exploiting Spatial Sparsity for Faster Inference, abstract:
+    a gating branch chooses the spatial positions to evaluate, inside a
+    residual block). Reading: mask[b, r, s] (nonzero = evaluate) over the
+    output positions;
+        y[b, o, r, s] = (x[b, o, r, s] if residual else 0) + [mask[b, r, s] != 0] * layer(x)[b, o, r, s]
+    where layer is ``forward``. A residual block needs Cin == Cout and an
+    output the size of the input."""
+    y = forward(x, experts, alpha, stride, pad, groups)
+    m = (np.asarray(mask) != 0)
+    assert m.shape == (y.shape[0],) + y.shape[2:]
+    out = y * m[:, None, :, :]
+    if residual:
+        xv = _f32(x).astype(np.float64)
+        assert xv.shape == out.shape, "a residual block needs the output the size of the input"
+        out = out + xv
+    return out

@@ -360,3 +360,29 @@ def test_many_experts_one_hot_and_linearity(n):
     np.testing.assert_allclose(y12, y1 + y2, rtol=1e-11, atol=1e-11)
     m = oracle.mix(a1, e)
     np.testing.assert_allclose(oracle.mix(a1 + a2, e), m + oracle.mix(a2, e), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_sparse_evaluation_special_cases(residual):
+    """Gated evaluation (Dynamic Convolutions: Exploiting Spatial Sparsity for
+    Faster Inference, abstract): an all-ones gate is the dense layer (plus the
+    residual), an all-zero gate leaves only the residual; and each output is
+    either the dense layer's value at that position or the residual alone."""
+    B, C, H, W, n = 2, 4, 6, 5, 3
+    x = _rand((B, C, H, W), 41)
+    e = _rand((n, C, C, 3, 3), 42)
+    a = np.random.default_rng(43).random((B, n))
+    dense = _torch_conv(x[0:1], np.einsum("i,i...->...", a[0], e.astype(np.float64)), 1, 1, 1)
+    ones = np.ones((B, H, W), np.uint8)
+    zeros = np.zeros((B, H, W), np.uint8)
+    res = x.astype(np.float64) if residual else 0.0
+    y1 = oracle.forward_sparse(x, e, a, ones, 1, 1, 1, residual)
+    np.testing.assert_allclose(y1[0:1], dense + (res[0:1] if residual else 0.0), rtol=1e-12, atol=1e-12)
+    y0 = oracle.forward_sparse(x, e, a, zeros, 1, 1, 1, residual)
+    np.testing.assert_array_equal(y0, np.zeros_like(y0) + res)
+    m = (np.random.default_rng(44).random((B, H, W)) < 0.4).astype(np.uint8)
+    ym = oracle.forward_sparse(x, e, a, m, 1, 1, 1, residual)
+    full = oracle.forward(x, e, a, 1, 1, 1) + res
+    on = np.broadcast_to(m[:, None] != 0, ym.shape)
+    np.testing.assert_array_equal(ym[on], full[on])
+    np.testing.assert_array_equal(ym[~on], (np.zeros_like(ym) + res)[~on])
