@@ -111,7 +111,10 @@ def cpu_baseline(w, d):
     while True:
         alpha, _, _ = oracle.route(d["x"], d["fc_w"], d["fc_b"], w.route_mode, w.temperature)
         h = d["x"]
-        if w.attention:
+        if w.mask_density > 0:
+            L = w.layers[0]
+            h = oracle.forward_sparse(h, d["experts"][0], alpha, d["mask"], L.stride, L.pad, L.groups, True)
+        elif w.attention:
             a_in, _, _ = oracle.route(d["x"], d["fc_w_in"], d["fc_b_in"], oracle.SIGMOID)
             a_out, _, _ = oracle.route(d["x"], d["fc_w_out"], d["fc_b_out"], oracle.SIGMOID)
             L = w.layers[0]
@@ -165,6 +168,15 @@ def main():
     for L, e in zip(w.layers, experts):
         desc = bd.make_desc(w.B, L.Cin, L.H, L.W, L.Cout, L.k, L.k, L.stride, L.pad, L.groups, w.n,
                             bd.DYNCONV_BF16 if w.dtype == "bf16" else bd.DYNCONV_F32)
+        if w.mask_density > 0:  # gated residual layer: the sparse entry point mixes itself
+            descs.append(desc)
+            pols.append(bd.DYNCONV_POLICY_PREMIX)
+            packed.append(None)
+            nb = bd.dynconv_forward_sparse_workspace_bytes(desc)
+            ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
+            outs.append([torch.empty((w.B, L.Cout, L.Ho, L.Wo), dtype=x0.dtype, device=dev)
+                         for _ in range(R)])
+            continue
         if w.attention:  # channel attentions: the forward packs its bank itself (PREMIX policy)
             descs.append(desc)
             pols.append(bd.DYNCONV_POLICY_PREMIX if L.groups == 1 else bd.dynconv_forward_policy(desc))
@@ -203,9 +215,14 @@ def main():
             bd.dynconv_route(xs[s], fc_w, fc_b, w.route_mode, w.temperature, alpha=alphas[s],
                              workspace=route_ws)
 
+    mask_dev = torch.from_numpy(d["mask"]).to(dev) if w.mask_density > 0 else None
+
     def forward(li, h, s):
         L = w.layers[li]
-        if w.attention:
+        if w.mask_density > 0:
+            bd.dynconv_forward_sparse(h, experts[li], alphas[s], mask_dev, L.stride, L.pad, L.groups,
+                                      residual=True, y=outs[li][s], workspace=ws[li])
+        elif w.attention:
             bd.dynconv_forward_attn(h, experts[li], alphas[s], a_ins[s], a_outs[s], L.stride, L.pad,
                                     L.groups, policy=pols[li], y=outs[li][s], workspace=ws[li])
         elif packed[li] is not None:
@@ -327,8 +344,10 @@ def main():
     mix_bytes = (w.n + w.B) * experts[0][0].numel() * esz + w.B * w.n * 4
     del mixed
 
-    conv_flops0 = 2 * w.B * L0.macs_per_example()
-    flops_all = w.conv_flops()
+    # a gated layer computes only its active positions
+    active = float(d["mask"].mean()) if w.mask_density > 0 else 1.0
+    conv_flops0 = 2 * w.B * L0.macs_per_example() * active
+    flops_all = w.conv_flops() * active
     images_s = w.B / (ms_per_step * 1e-3)
     route_bytes = w.B * L0.Cin * L0.H * L0.W * esz + w.B * w.n * 4
     conv_tflops = conv_flops0 / (conv_ms * 1e-3) / 1e12
@@ -364,6 +383,7 @@ def main():
                    "routing": "softmax(z/T)" if w.route_mode else "sigmoid",
                    "policy": [pol_name.get(p, str(p)) for p in pols],
                    "attention": w.attention,
+                   "mask_density": w.mask_density,
                    "rotating_sets": R},
         "tflops_step": round(flops_all / (ms_per_step * 1e-3) / 1e12, 2),
         "pct_bf16_peak_step": round(100 * flops_all / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),

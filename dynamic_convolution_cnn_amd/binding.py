@@ -45,7 +45,8 @@ EXPORTED = (
     "dynconv_forward_attn_workspace_bytes", "dynconv_backward_data",
     "dynconv_backward_data_workspace_bytes", "dynconv_backward_weights",
     "dynconv_backward_weights_workspace_bytes", "dynconv_route_backward",
-    "dynconv_route_backward_workspace_bytes",
+    "dynconv_route_backward_workspace_bytes", "dynconv_forward_sparse",
+    "dynconv_forward_sparse_workspace_bytes",
 )
 
 
@@ -123,6 +124,10 @@ def lib():
     L.dynconv_route_backward.restype = i32
     L.dynconv_route_backward_workspace_bytes.argtypes = [D]
     L.dynconv_route_backward_workspace_bytes.restype = sz
+    L.dynconv_forward_sparse.argtypes = [D, P, P, P, P, i32, P, P, sz, P]
+    L.dynconv_forward_sparse.restype = i32
+    L.dynconv_forward_sparse_workspace_bytes.argtypes = [D]
+    L.dynconv_forward_sparse_workspace_bytes.restype = sz
     _lib = L
     return L
 
@@ -411,3 +416,24 @@ def dynconv_route_backward(x: torch.Tensor, fc_w: torch.Tensor, alpha: torch.Ten
                                         _ptr(dfc_b), _ptr(dx), _ptr(ws), ws_bytes, _stream(stream)),
            "dynconv_route_backward")
     return dfc_w, dfc_b
+
+
+def dynconv_forward_sparse_workspace_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_forward_sparse_workspace_bytes(ctypes.byref(desc)))
+
+
+def dynconv_forward_sparse(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor, mask: torch.Tensor,
+                           stride: int = 1, pad: int = 0, groups: int = 1, residual: bool = False,
+                           y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """y = (x if residual else 0) + mask * layer(x); mask [B, Ho, Wo] uint8 (nonzero = evaluate)."""
+    desc = layer_desc(x, experts, stride, pad, groups)
+    Ho = (desc.H + 2 * pad - desc.kh) // stride + 1
+    Wo = (desc.W + 2 * pad - desc.kw) // stride + 1
+    if y is None:
+        y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_forward_sparse_workspace_bytes(desc), x.device, workspace)
+    _check(lib().dynconv_forward_sparse(ctypes.byref(desc), _ptr(x), _ptr(experts), _ptr(alpha), _ptr(mask),
+                                        int(bool(residual)), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "dynconv_forward_sparse")
+    return y

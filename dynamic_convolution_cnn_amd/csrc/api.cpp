@@ -275,6 +275,29 @@ size_t route_backward_ws(const dynconv::Geom &g) {
            round_up((size_t)g.B * g.n * sizeof(float), kWsAlign);
 }
 
+// Workspace of dynconv_forward_sparse: W_b in the premix layout (through
+// the packed bank for n <= 16, the wide bank otherwise), then the compacted
+// active positions.
+size_t sparse_ws(const dynconv::Geom &g) {
+    const size_t bank = wide(g) ? dynconv::wide_bank_bytes(g) : dynconv::packed_experts_bytes(g);
+    return round_up(bank, kWsAlign) + round_up(dynconv::premixed_bytes(g), kWsAlign) +
+           round_up(dynconv::sparse_index_bytes(g), kWsAlign);
+}
+
+dynconv_status_t check_sparse(const dynconv_desc_t *desc, dynconv::Geom &g, int32_t residual) {
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!g.bf16 || g.groups != 1)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "gated evaluation supports bf16 layers with groups == 1");
+    if (wide(g) && !dynconv::pack_wide_supported(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "more than 16 experts: one expert's Cin x kh x kw block must fit 64 KB");
+    if (residual != 0 && residual != 1) return fail(DYNCONV_ERR_INVALID_ARG, "residual must be 0 or 1");
+    if (g.B > 65535) return fail(DYNCONV_ERR_UNSUPPORTED, "gated evaluation supports B <= 65535 (got %d)", g.B);
+    if (residual && (g.Cin != g.Cout || g.Ho != g.H || g.Wo != g.W))
+        return fail(DYNCONV_ERR_INVALID_ARG, "a residual block needs Cin == Cout and an output the size of the input");
+    return DYNCONV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -588,6 +611,52 @@ dynconv_status_t dynconv_route_backward(const dynconv_desc_t *desc, const void *
     return hip_status(dynconv::launch_route_backward(g, x, fc_w, mode, temperature, alpha, dalpha, gap, dz, dgap,
                                                      dfc_w, dfc_b, dx, static_cast<hipStream_t>(stream)),
                       "dynconv_route_backward launch");
+}
+
+size_t dynconv_forward_sparse_workspace_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_sparse(desc, g, 0) != DYNCONV_OK) return 0;
+    return sparse_ws(g);
+}
+
+dynconv_status_t dynconv_forward_sparse(const dynconv_desc_t *desc, const void *x, const void *experts,
+                                        const float *alpha, const uint8_t *mask, int32_t residual, void *y,
+                                        void *workspace, size_t workspace_bytes, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_sparse(desc, g, residual);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !experts || !alpha || !mask || !y)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, experts, alpha, mask and y must not be NULL");
+    const void *ptrs[] = {x, experts, alpha, mask, y};
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t xn = (uintptr_t)g.B * g.Cin * g.H * g.W * 2, yn = (uintptr_t)g.B * g.Cout * g.P * 2;
+    if (x0 < y0 + yn && y0 < x0 + xn) return fail(DYNCONV_ERR_INVALID_ARG, "y must not overlap x");
+    if (!dynconv::premix_conv_supported(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "the mixed kernels' layout does not fit this layer");
+    const size_t need = sparse_ws(g);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE, "forward_sparse needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                    need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const size_t bank_b = round_up(wide(g) ? dynconv::wide_bank_bytes(g) : dynconv::packed_experts_bytes(g), kWsAlign);
+    uint16_t *bank = reinterpret_cast<uint16_t *>(ws);
+    uint16_t *wt = reinterpret_cast<uint16_t *>(ws + bank_b);
+    int *idx = reinterpret_cast<int *>(ws + bank_b + round_up(dynconv::premixed_bytes(g), kWsAlign));
+    hipError_t e;
+    if (wide(g)) {
+        e = dynconv::launch_pack_wide(g, static_cast<const uint16_t *>(experts), bank, st);
+        if (e == hipSuccess) e = dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st);
+    } else {
+        e = dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), bank, st);
+        if (e == hipSuccess) e = dynconv::launch_premix(g, alpha, bank, wt, st);
+    }
+    if (e != hipSuccess) return hip_status(e, "dynconv_forward_sparse mix launch");
+    return hip_status(dynconv::launch_conv_sparse(g, static_cast<const uint16_t *>(x), wt, mask, residual, idx,
+                                                  static_cast<uint16_t *>(y), st),
+                      "dynconv_forward_sparse launch");
 }
 
 }  // extern "C"

@@ -107,6 +107,15 @@ hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *exper
                                  const float *alpha, const void *wmixed, void *y,
                                  hipStream_t stream, ChanAttn att = {});
 
+// ---- gated (spatially sparse) evaluation ----------------------------------
+// y = (residual ? x : 0) + [mask != 0] * conv(x, W_b) with W_b premixed in
+// wt[b][t][o][cp] (bf16, groups == 1); mask [B][Ho*Wo] uint8 over the output
+// positions; idx: sparse_index_bytes(g) of scratch (the compacted positions
+// and their counts). y must not overlap x.
+size_t sparse_index_bytes(const Geom &g);
+hipError_t launch_conv_sparse(const Geom &g, const uint16_t *x, const uint16_t *wt, const uint8_t *mask, int residual,
+                              int *idx, uint16_t *y, hipStream_t stream);
+
 // ---- gradients ---------------------------------------------------------------
 // Bank transposed in its channels and flipped in its taps: for groups == 1
 // flipped[i][c][o][u][v] = experts[i][o][c][KH-1-u][KW-1-v]; depthwise

@@ -81,6 +81,7 @@ class Workload:
     x_relu: bool = False
     fc_std: Optional[float] = 0.1
     attention: bool = False     # FMDConv input and output attention heads as well
+    mask_density: float = 0.0   # > 0: a gate evaluates this fraction of output positions (residual block)
 
     @property
     def route_layer(self) -> Layer:
@@ -129,6 +130,13 @@ WORKLOADS: Dict[str, Workload] = {
         key="fmdconv_resnet18_3x3",
         title="FMDConv multi-attention on the ResNet-18-shaped 3x3, B=32, 64->64, 56x56, n=4, softmax(z/4), bf16",
         B=32, n=4, dtype="bf16", route_mode=SOFTMAX, temperature=4.0, attention=True,
+        layers=(Layer(64, 64, 56, 56, 3, 1, 1),)),
+    # spatially sparse evaluation: a gate selects a quarter of the positions of
+    # a residual ResNet-18-shaped layer; not one of the five configurations
+    "sparse_resnet18_3x3": Workload(
+        key="sparse_resnet18_3x3",
+        title="gated residual 3x3, 25% of positions, B=32, 64->64, 56x56, n=4, bf16",
+        B=32, n=4, dtype="bf16", mask_density=0.25,
         layers=(Layer(64, 64, 56, 56, 3, 1, 1),)),
     # KernelWarehouse's setting of more than 100 experts (n > 100) on the
     # many-expert layer's shape; not one of the five configurations
@@ -202,6 +210,11 @@ def make_inputs(w: Workload, seed: int = 0, B: Optional[int] = None) -> dict:
             out[f"fc_w_{name}"] = (rng.standard_normal((m, L0.Cin), dtype=np.float32) *
                                    np.float32(w.fc_std_value())).astype(np.float32)
             out[f"fc_b_{name}"] = np.zeros((m,), np.float32)
+    if w.mask_density > 0:
+        # the gate: each output position of each example on with probability
+        # mask_density (drawn last, so the other draws match a dense workload's)
+        L = w.layers[0]
+        out["mask"] = (rng.random((Bn, L.Ho, L.Wo)) < w.mask_density).astype(np.uint8)
     return out
 
 

@@ -213,6 +213,27 @@ dynconv_status_t dynconv_forward_attn(const dynconv_desc_t *desc, int32_t policy
                                       size_t workspace_bytes, void *stream);
 size_t dynconv_forward_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
 
+/* The layer evaluated only where a gate says so (Dynamic Convolutions:
+ * Exploiting Spatial Sparsity for Faster Inference, abstract: a small gating
+ * branch picks the spatial positions a residual block evaluates; the work is
+ * done with a gather-scatter approach). The gate is an input here:
+ *   y[b,o,r,s] = (residual ? x[b,o,r,s] : 0) + [mask[b,r,s] != 0] * layer(x)[b,o,r,s]
+ * where layer is dynconv_forward's convolution with W_b = sum_i alpha[b,i] E_i.
+ * mask: [B,Ho,Wo] uint8 (nonzero = evaluate). residual: 0 or 1; 1 needs
+ * Cin == Cout and Ho == H, Wo == W. bf16 layers with groups == 1 (any n;
+ * more than 16 experts as dynconv_forward). The convolution runs only at the
+ * active positions: their im2col rows are gathered, multiplied on the matrix
+ * cores and scattered back; the other positions receive 0 or x. y
+ * [B,Cout,Ho,Wo] must not overlap x (DYNCONV_ERR_INVALID_ARG). workspace: at
+ * least dynconv_forward_sparse_workspace_bytes(desc) bytes (the mixed
+ * kernels and the compacted positions; 0 for an unsupported layer). y is
+ * rounded once to bf16 (the residual is added in float32 first);
+ * deterministic. */
+dynconv_status_t dynconv_forward_sparse(const dynconv_desc_t *desc, const void *x, const void *experts,
+                                        const float *alpha, const uint8_t *mask, int32_t residual, void *y,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+size_t dynconv_forward_sparse_workspace_bytes(const dynconv_desc_t *desc);
+
 /* ---- gradients ------------------------------------------------------------
  * The pages train dynamic convolutions end to end ("learn specialized
  * convolutional kernels for each example", CondConv: Conditionally

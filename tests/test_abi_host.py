@@ -340,3 +340,31 @@ def test_many_expert_forward_checks():
                                   1 << 30, None) == bd.DYNCONV_ERR_UNSUPPORTED
     # the packed-bank entry points keep n <= 16
     assert bd.dynconv_packed_experts_bytes(d) == 0
+
+
+
+def test_forward_sparse_checks():
+    L = _lib()
+    d = good_desc()
+    r256 = lambda v: (v + 255) // 256 * 256
+    X, Y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+
+    def fs(desc=d, x=X, e=FAKE, a=FAKE, m=FAKE, res=0, y=Y, wsp=FAKE, wsb=None):
+        if wsb is None:
+            wsb = bd.dynconv_forward_sparse_workspace_bytes(desc)
+        return L.dynconv_forward_sparse(ctypes.byref(desc), x, e, a, m, res, y, wsp, wsb, None)
+
+    # packed bank, W_b in the premix layout, then B*P positions and B counts
+    want = (r256(9 * 16 * 32 * 4 * 2) + r256(2 * 9 * 16 * 32 * 2) + r256((2 * 64 + 2) * 4))
+    assert bd.dynconv_forward_sparse_workspace_bytes(d) == want
+    assert fs(m=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fs(res=2) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fs(y=X) == bd.DYNCONV_ERR_INVALID_ARG                                   # y overlaps x
+    assert fs(y=ctypes.c_void_p(0x100000 + 1024)) == bd.DYNCONV_ERR_INVALID_ARG  # partial overlap (x is 2 KB)
+    assert fs(wsb=want - 1) == bd.DYNCONV_ERR_WORKSPACE
+    assert fs(desc=good_desc(dtype=bd.DYNCONV_F32), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert fs(desc=good_desc(Cin=16, Cout=16, groups=16), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    # a residual block needs Cin == Cout and the input's size
+    assert fs(desc=good_desc(Cout=32), res=1, wsb=1 << 30) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fs(desc=good_desc(stride=2), res=1, wsb=1 << 30) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bd.dynconv_forward_sparse_workspace_bytes(good_desc(groups=16, Cin=16, Cout=16)) == 0
