@@ -111,7 +111,7 @@ hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *exper
 // y = (residual ? x : 0) + [mask != 0] * conv(x, W_b) with W_b premixed in
 // wt[b][t][o][cp] (bf16, groups == 1); mask [B][Ho*Wo] uint8 over the output
 // positions; idx: sparse_index_bytes(g) of scratch (the compacted positions
-// and their counts). y must not overlap x.
+// and their counts, then a channel-innermost copy of x). y must not overlap x.
 size_t sparse_index_bytes(const Geom &g);
 hipError_t launch_conv_sparse(const Geom &g, const uint16_t *x, const uint16_t *wt, const uint8_t *mask, int residual,
                               int *idx, uint16_t *y, hipStream_t stream);

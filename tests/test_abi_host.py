@@ -355,7 +355,8 @@ def test_forward_sparse_checks():
         return L.dynconv_forward_sparse(ctypes.byref(desc), x, e, a, m, res, y, wsp, wsb, None)
 
     # packed bank, W_b in the premix layout, then B*P positions and B counts
-    want = (r256(9 * 16 * 32 * 4 * 2) + r256(2 * 9 * 16 * 32 * 2) + r256((2 * 64 + 2) * 4))
+    # ... followed by x channel-innermost with Cin padded to 32
+    want = (r256(9 * 16 * 32 * 4 * 2) + r256(2 * 9 * 16 * 32 * 2) + r256(r256((2 * 64 + 2) * 4) + 2 * 64 * 32 * 2))
     assert bd.dynconv_forward_sparse_workspace_bytes(d) == want
     assert fs(m=None) == bd.DYNCONV_ERR_INVALID_ARG
     assert fs(res=2) == bd.DYNCONV_ERR_INVALID_ARG
