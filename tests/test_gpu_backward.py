@@ -226,3 +226,60 @@ def test_backward_full_size_sampled():
     rhs = float(np.sum(a.astype(np.float64) * from_dev(da)))
     say(f"Euler: <dE, E> = {lhs:.6e}, <alpha, dalpha> = {rhs:.6e}")
     assert abs(lhs - rhs) <= 1e-4 * max(abs(rhs), 1e-30)
+
+
+@pytest.mark.parametrize("key,B", [("resnet50_3x3", 24), ("many_expert_softmax", 12)])
+def test_training_graph_replay_matches_eager(key, B):
+    """A HIP graph holding the training step's gradient calls (as bench.py
+    --backward replays them) gives bitwise the eager results on every replay,
+    with other eager work and host synchronisations between the replays."""
+    w = inputs.WORKLOADS[key]
+    d = inputs.make_inputs(w, B=B)
+    L, e = w.layers[0], d["experts"][0]
+    x, ed = to_dev(d["x"], "bf16"), to_dev(e, "bf16")
+    fw, fb = to_dev(d["fc_w"], "f32"), to_dev(d["fc_b"], "f32")
+    dy = to_dev(inputs.bf16_round(np.random.default_rng(4).standard_normal((B, L.Cout, L.Ho, L.Wo),
+                                                                           dtype=np.float32)), "bf16")
+    desc = bd.layer_desc(x, ed, L.stride, L.pad, L.groups)
+    rdesc = bd.make_desc(B, L.Cin, L.H, L.W, n=w.n, dtype=desc.dtype)
+    alpha = torch.empty((B, w.n), dtype=torch.float32, device="cuda")
+    da = torch.empty_like(alpha)
+    de = torch.empty(tuple(e.shape), dtype=torch.float32, device="cuda")
+    dfw = torch.empty((w.n, L.Cin), dtype=torch.float32, device="cuda")
+    dfb = torch.empty((w.n,), dtype=torch.float32, device="cuda")
+    dx = torch.empty_like(x)
+    ws_w = torch.empty(bd.dynconv_backward_weights_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(bd.dynconv_backward_data_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(max(16, bd.dynconv_route_workspace_bytes(rdesc)), dtype=torch.uint8, device="cuda")
+    ws_rb = torch.empty(bd.dynconv_route_backward_workspace_bytes(rdesc), dtype=torch.uint8, device="cuda")
+
+    def step():
+        bd.dynconv_route(x, fw, fb, w.route_mode, w.temperature, alpha=alpha, workspace=ws_r)
+        bd.dynconv_backward_weights(x, dy, ed, alpha, L.stride, L.pad, L.groups, dalpha=da, dexperts=de,
+                                    workspace=ws_w)
+        bd.dynconv_backward_data(dy, ed, alpha, L.H, L.W, L.stride, L.pad, L.groups, dx=dx, workspace=ws_d)
+        bd.dynconv_route_backward(x, fw, alpha, da, w.route_mode, w.temperature, dx=dx, dfc_w=dfw, dfc_b=dfb,
+                                  workspace=ws_rb)
+
+    say("training graph replay", key, B)
+    step()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in (alpha, da, de, dfw, dfb, dx)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    x2 = torch.flip(x, dims=[0]).contiguous()
+    for r in range(3):
+        for t in (alpha, da, de, dfw, dfb, dx):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, ref in zip(("alpha", "dalpha", "dE", "dfc_w", "dfc_b", "dx"),
+                                (alpha, da, de, dfw, dfb, dx), refs):
+            assert torch.equal(t.view(torch.int16) if t.dtype == torch.bfloat16 else t,
+                               ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref), \
+                f"replay {r}: {name} differs"
+        # unrelated eager work between replays
+        bd.dynconv_backward_weights(x2, dy, ed, refs[0], L.stride, L.pad, L.groups)
+        torch.cuda.synchronize()
