@@ -84,6 +84,10 @@ template <> struct Row8<uint16_t> {
         v = u32x4_t{a.x, a.y, b.x, b.y};
     }
     __device__ __forceinline__ void store(uint16_t *dst) const { *reinterpret_cast<u32x4_t *>(dst) = v; }
+    __device__ __forceinline__ void pack(const uint16_t (&h)[8]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (uint32_t)h[2 * j] | ((uint32_t)h[2 * j + 1] << 16);
+    }
 };
 template <> struct Row8<float> {
     f32x4_t v0, v1;
@@ -99,6 +103,10 @@ template <> struct Row8<float> {
     __device__ __forceinline__ void store(float *dst) const {
         reinterpret_cast<f32x4_t *>(dst)[0] = v0;
         reinterpret_cast<f32x4_t *>(dst)[1] = v1;
+    }
+    __device__ __forceinline__ void pack(const float (&h)[8]) {
+        v0 = f32x4_t{h[0], h[1], h[2], h[3]};
+        v1 = f32x4_t{h[4], h[5], h[6], h[7]};
     }
 };
 
@@ -131,6 +139,9 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const T *__restrict__ x, con
     const int kt_ = k_ok ? K - kc * a.KT : 0;
     const int ku = kt_ / a.KW, kv = kt_ - ku * a.KW;
     const T *xplane = x + ((long)b * a.Cin + kc) * a.H * a.W;
+    const int r_lo = max(0, ceil_div(a.pad - ku, a.stride)), r_hi = ceil_div(a.H + a.pad - ku, a.stride);
+    const int s_lo = max(0, ceil_div(a.pad - kv, a.stride)), s_hi = ceil_div(a.W + a.pad - kv, a.stride);
+    const long row_step = (long)a.stride * a.W - (long)a.Wo * a.stride;
     Row8<T> ra[2], rb;
     auto load = [&](int p0) {
         const int p = p0 + 8 * seg;
@@ -145,15 +156,20 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const T *__restrict__ x, con
                     if (o_ok[h] && p + j < a.P) ra[h].set(j, dyrow[h][p + j]);
             }
         }
-        rb.zero();
+        // the thread's tap is fixed: output row r reads inside the image for
+        // r in [r_lo, r_hi), column s for s in [s_lo, s_hi); the x address
+        // moves by the stride along a row and by row_step to the next row
+        T xv[8];
         int r = p / a.Wo, s = p - r * a.Wo;
+        long addr = (long)(r * a.stride - a.pad + ku) * a.W + (s * a.stride - a.pad + kv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int hh = r * a.stride - a.pad + ku, ww = s * a.stride - a.pad + kv;
-            if (k_ok && p + j < a.P && hh >= 0 && hh < a.H && ww >= 0 && ww < a.W)
-                rb.set(j, xplane[(long)hh * a.W + ww]);
-            if (++s == a.Wo) { s = 0; ++r; }
+            xv[j] = T(0);
+            if (k_ok && p + j < a.P && r >= r_lo && r < r_hi && s >= s_lo && s < s_hi) xv[j] = xplane[addr];
+            addr += a.stride;
+            if (++s == a.Wo) { s = 0; ++r; addr += row_step; }
         }
+        rb.pack(xv);
     };
     f32x16_t acc[2] = {};
     load(0);
