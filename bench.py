@@ -135,7 +135,7 @@ def cpu_baseline(w, d):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by example: see the design notes)", file=sys.stderr)
         sys.exit(2)
     if args.calib_copy:
