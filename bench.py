@@ -136,7 +136,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by example: see the design notes)", file=sys.stderr)
+              "(every step is independent per example, so several GPUs would each take a share of the batch)",
+              file=sys.stderr)
         sys.exit(2)
     if args.calib_copy:
         calib_copy()

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdynconv.so")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU forms are kept off (see DESIGN notes on gfx950 codegen).
+# Packed-fp32 VALU forms (v_pk_*_f32) are kept off for every device source.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
