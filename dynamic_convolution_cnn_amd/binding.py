@@ -150,7 +150,81 @@ def _dtype_code(t: torch.Tensor) -> int:
         return DYNCONV_BF16
     if t.dtype == torch.float32:
         return DYNCONV_F32
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise ValueError(f"unsupported dtype {t.dtype}: activations and experts are bfloat16 or float32")
+
+
+F32 = torch.float32
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype=None, optional: bool = False):
+    """Check one tensor argument against what the call will read or write:
+    its exact shape, its dtype and a dense layout. The C ABI takes raw
+    pointers and sizes from the descriptor, so a tensor that does not match
+    would be read or written out of bounds; mismatches raise ValueError
+    before the library is called."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor (got {type(t).__name__})")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(v) for v in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_bytes(t: Optional[torch.Tensor], name: str, nbytes: int):
+    """A byte buffer (packed bank, workspace): dense and at least nbytes long."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor (got {type(t).__name__})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, {nbytes} needed")
+
+
+def _same_gpu(**tensors):
+    """Every given tensor on one GPU (the device the call's pointers belong to)."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} is on {t.device}; the library takes device memory only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other arguments on {dev}")
+    return dev
+
+
+def _out_hw(H, W, kh, kw, stride, pad):
+    Ho = (H + 2 * pad - kh) // stride + 1
+    Wo = (W + 2 * pad - kw) // stride + 1
+    if Ho < 1 or Wo < 1:
+        raise ValueError(f"kernel {kh}x{kw} does not fit the padded {H}x{W} input")
+    return Ho, Wo
+
+
+def _layer_tensors(x, experts, groups):
+    """Shapes implied by x [B, Cin, H, W] and experts [n, Cout, Cin/groups, kh, kw]."""
+    if x.dim() != 4:
+        raise ValueError(f"x must be [B, Cin, H, W] (got {tuple(x.shape)})")
+    if experts.dim() != 5:
+        raise ValueError(f"experts must be [n, Cout, Cin/groups, kh, kw] (got {tuple(experts.shape)})")
+    B, Cin, H, W = x.shape
+    n, Cout, cpg, kh, kw = experts.shape
+    if groups < 1 or Cin % groups or cpg != Cin // groups:
+        raise ValueError(f"experts.shape[2] = {cpg} must be Cin / groups = {Cin} / {groups}")
+    if experts.dtype != x.dtype:
+        raise ValueError(f"experts dtype {experts.dtype} differs from x dtype {x.dtype}")
+    _dtype_code(x)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -173,6 +247,11 @@ def _check(status: int, where: str):
 
 
 def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+    if given is not None:
+        _need_bytes(given, "workspace", nbytes)
+        _same_gpu(workspace=given)
+        if given.device != device:
+            raise ValueError(f"workspace is on {given.device}, the call's tensors on {device}")
     if nbytes == 0:
         return given, 0
     if given is not None:
@@ -182,6 +261,7 @@ def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
 
 def layer_desc(x: torch.Tensor, experts: torch.Tensor, stride: int, pad: int,
                groups: int) -> dynconv_desc_t:
+    _layer_tensors(x, experts, groups)
     B, Cin, H, W = x.shape
     n, Cout, cpg, kh, kw = experts.shape
     return make_desc(B, Cin, H, W, Cout, kh, kw, stride, pad, groups, n, _dtype_code(x))
@@ -216,9 +296,15 @@ def dynconv_route(x: torch.Tensor, fc_w: torch.Tensor, fc_b: Optional[torch.Tens
                   alpha: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """alpha[B, n] (float32) from GAP -> FC(+bias) -> sigmoid | softmax(z / T)."""
+    if x.dim() != 4 or fc_w.dim() != 2:
+        raise ValueError("x must be [B, Cin, H, W] and fc_w [n, Cin]")
     B, Cin, H, W = x.shape
     n = fc_w.shape[0]
     desc = make_desc(B, Cin, H, W, n=n, dtype=_dtype_code(x))
+    _need(fc_w, "fc_w", (n, Cin), F32)
+    _need(fc_b, "fc_b", (n,), F32, optional=True)
+    _need(alpha, "alpha", (B, n), F32, optional=True)
+    _same_gpu(x=x, fc_w=fc_w, fc_b=fc_b, alpha=alpha)
     if alpha is None:
         alpha = torch.empty((B, n), dtype=torch.float32, device=x.device)
     ws, ws_bytes = _workspace(dynconv_route_workspace_bytes(desc), x.device, workspace)
@@ -231,10 +317,16 @@ def dynconv_route(x: torch.Tensor, fc_w: torch.Tensor, fc_b: Optional[torch.Tens
 def dynconv_mix(alpha: torch.Tensor, experts: torch.Tensor, groups: int = 1,
                 mixed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """mixed[b] = sum_i alpha[b, i] experts[i]; experts [n, Cout, Cin/g, kh, kw]."""
+    if alpha.dim() != 2 or experts.dim() != 5:
+        raise ValueError("alpha must be [B, n] and experts [n, Cout, Cin/groups, kh, kw]")
     B = alpha.shape[0]
     n, Cout, cpg, kh, kw = experts.shape
     # H = W = kh, kw-sized input keeps the descriptor valid; mixing reads only the kernel shape
     desc = make_desc(B, cpg * groups, kh, kw, Cout, kh, kw, 1, 0, groups, n, _dtype_code(experts))
+    _need(alpha, "alpha", (B, n), F32)
+    _need(experts, "experts", (n, Cout, cpg, kh, kw))
+    _need(mixed, "mixed", (B, Cout, cpg, kh, kw), experts.dtype, optional=True)
+    _same_gpu(alpha=alpha, experts=experts, mixed=mixed)
     if mixed is None:
         mixed = torch.empty((B, Cout, cpg, kh, kw), dtype=experts.dtype, device=experts.device)
     _check(lib().dynconv_mix(ctypes.byref(desc), _ptr(alpha), _ptr(experts), _ptr(mixed),
@@ -248,8 +340,12 @@ def dynconv_forward(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """y[b] = conv(x[b], sum_i alpha[b, i] experts[i]) for every example."""
     desc = layer_desc(x, experts, stride, pad, groups)
-    Ho = (desc.H + 2 * pad - desc.kh) // stride + 1
-    Wo = (desc.W + 2 * pad - desc.kw) // stride + 1
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, stride, pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W))
+    _need(experts, "experts", tuple(experts.shape))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(y, "y", (desc.B, desc.Cout, Ho, Wo), x.dtype, optional=True)
+    _same_gpu(x=x, experts=experts, alpha=alpha, y=y)
     if y is None:
         y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
     ws, ws_bytes = _workspace(dynconv_forward_workspace_bytes(desc, policy), x.device, workspace)
@@ -271,9 +367,22 @@ def dynconv_route_attn(x: torch.Tensor, Cout: int, fc_w: torch.Tensor, fc_b: Opt
                        workspace: Optional[torch.Tensor] = None, stream=None):
     """FMDConv's three attentions from one pooling of x: (alpha [B, n], a_in [B, Cin],
     a_out [B, Cout]), float32."""
+    if x.dim() != 4 or fc_w.dim() != 2:
+        raise ValueError("x must be [B, Cin, H, W] and fc_w [n, Cin]")
     B, Cin, H, W = x.shape
     n = fc_w.shape[0]
     desc = make_desc(B, Cin, H, W, Cout, 1, 1, 1, 0, 1, n, _dtype_code(x))
+    _need(fc_w, "fc_w", (n, Cin), F32)
+    _need(fc_b, "fc_b", (n,), F32, optional=True)
+    _need(fc_w_in, "fc_w_in", (Cin, Cin), F32)
+    _need(fc_b_in, "fc_b_in", (Cin,), F32, optional=True)
+    _need(fc_w_out, "fc_w_out", (Cout, Cin), F32)
+    _need(fc_b_out, "fc_b_out", (Cout,), F32, optional=True)
+    _need(alpha, "alpha", (B, n), F32, optional=True)
+    _need(a_in, "a_in", (B, Cin), F32, optional=True)
+    _need(a_out, "a_out", (B, Cout), F32, optional=True)
+    _same_gpu(x=x, fc_w=fc_w, fc_b=fc_b, fc_w_in=fc_w_in, fc_b_in=fc_b_in, fc_w_out=fc_w_out,
+              fc_b_out=fc_b_out, alpha=alpha, a_in=a_in, a_out=a_out)
     if alpha is None:
         alpha = torch.empty((B, n), dtype=torch.float32, device=x.device)
     if a_in is None:
@@ -299,8 +408,14 @@ def dynconv_forward_attn(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Te
                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """y[b, o] = a_out[b, o] * conv(a_in[b, :] x[b], sum_i alpha[b, i] experts[i])[o]."""
     desc = layer_desc(x, experts, stride, pad, groups)
-    Ho = (desc.H + 2 * pad - desc.kh) // stride + 1
-    Wo = (desc.W + 2 * pad - desc.kw) // stride + 1
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, stride, pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W))
+    _need(experts, "experts", tuple(experts.shape))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(a_in, "a_in", (desc.B, desc.Cin), F32, optional=True)
+    _need(a_out, "a_out", (desc.B, desc.Cout), F32, optional=True)
+    _need(y, "y", (desc.B, desc.Cout, Ho, Wo), x.dtype, optional=True)
+    _same_gpu(x=x, experts=experts, alpha=alpha, a_in=a_in, a_out=a_out, y=y)
     if y is None:
         y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
     ws, ws_bytes = _workspace(dynconv_forward_attn_workspace_bytes(desc, policy), x.device, workspace)
@@ -323,6 +438,10 @@ def dynconv_pack_experts(desc: dynconv_desc_t, experts: torch.Tensor,
                          packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """The expert bank in the layout the bf16 MFMA convolution reads (uint8 bytes)."""
     nbytes = dynconv_packed_experts_bytes(desc)
+    _need(experts, "experts", (desc.n, desc.Cout, desc.Cin // max(desc.groups, 1), desc.kh, desc.kw),
+          torch.bfloat16)
+    _need_bytes(packed, "packed", nbytes)
+    _same_gpu(experts=experts, packed=packed)
     if packed is None:
         packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=experts.device)
     _check(lib().dynconv_pack_experts(ctypes.byref(desc), _ptr(experts), _ptr(packed),
@@ -336,8 +455,12 @@ def dynconv_forward_packed(desc: dynconv_desc_t, x: torch.Tensor, packed: torch.
                            y: Optional[torch.Tensor] = None,
                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """dynconv_forward with a bank packed by dynconv_pack_experts."""
-    Ho = (desc.H + 2 * desc.pad - desc.kh) // desc.stride + 1
-    Wo = (desc.W + 2 * desc.pad - desc.kw) // desc.stride + 1
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, desc.stride, desc.pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W), torch.bfloat16)
+    _need_bytes(packed, "packed", dynconv_packed_experts_bytes(desc))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(y, "y", (desc.B, desc.Cout, Ho, Wo), torch.bfloat16, optional=True)
+    _same_gpu(x=x, packed=packed, alpha=alpha, y=y)
     if y is None:
         y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
     ws, ws_bytes = _workspace(dynconv_forward_packed_workspace_bytes(desc, policy), x.device,
@@ -357,9 +480,17 @@ def dynconv_backward_data(dy: torch.Tensor, experts: torch.Tensor, alpha: torch.
                           policy: int = DYNCONV_POLICY_AUTO, dx: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Input gradient dx [B, Cin, H, W] of the layer for the output gradient dy."""
+    if dy.dim() != 4 or experts.dim() != 5:
+        raise ValueError("dy must be [B, Cout, Ho, Wo] and experts [n, Cout, Cin/groups, kh, kw]")
     B = dy.shape[0]
     n, Cout, cpg, kh, kw = experts.shape
     desc = make_desc(B, cpg * groups, H, W, Cout, kh, kw, stride, pad, groups, n, _dtype_code(dy))
+    Ho, Wo = _out_hw(H, W, kh, kw, stride, pad)
+    _need(dy, "dy", (B, Cout, Ho, Wo))
+    _need(experts, "experts", (n, Cout, cpg, kh, kw), dy.dtype)
+    _need(alpha, "alpha", (B, n), F32)
+    _need(dx, "dx", (B, cpg * groups, H, W), dy.dtype, optional=True)
+    _same_gpu(dy=dy, experts=experts, alpha=alpha, dx=dx)
     if dx is None:
         dx = torch.empty((B, cpg * groups, H, W), dtype=dy.dtype, device=dy.device)
     ws, ws_bytes = _workspace(dynconv_backward_data_workspace_bytes(desc, policy), dy.device, workspace)
@@ -381,6 +512,14 @@ def dynconv_backward_weights(x: torch.Tensor, dy: torch.Tensor, experts: torch.T
     """(dalpha [B, n], dexperts [n, Cout, Cin/g, kh, kw]), float32; an entry not in
     ``want`` (and not given) is None."""
     desc = layer_desc(x, experts, stride, pad, groups)
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, stride, pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W))
+    _need(dy, "dy", (desc.B, desc.Cout, Ho, Wo), x.dtype)
+    _need(experts, "experts", tuple(experts.shape))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(dalpha, "dalpha", (desc.B, desc.n), F32, optional=True)
+    _need(dexperts, "dexperts", tuple(experts.shape), F32, optional=True)
+    _same_gpu(x=x, dy=dy, experts=experts, alpha=alpha, dalpha=dalpha, dexperts=dexperts)
     if dalpha is None and "dalpha" in want:
         dalpha = torch.empty((desc.B, desc.n), dtype=torch.float32, device=x.device)
     if dexperts is None and "dexperts" in want:
@@ -403,9 +542,18 @@ def dynconv_route_backward(x: torch.Tensor, fc_w: torch.Tensor, alpha: torch.Ten
                            workspace: Optional[torch.Tensor] = None, stream=None):
     """(dfc_w [n, Cin], dfc_b [n]) of the routing; when dx is given, the pooling's
     share dgap / (H W) is added to it in place."""
+    if x.dim() != 4 or fc_w.dim() != 2:
+        raise ValueError("x must be [B, Cin, H, W] and fc_w [n, Cin]")
     B, Cin, H, W = x.shape
     n = fc_w.shape[0]
     desc = make_desc(B, Cin, H, W, n=n, dtype=_dtype_code(x))
+    _need(fc_w, "fc_w", (n, Cin), F32)
+    _need(alpha, "alpha", (B, n), F32)
+    _need(dalpha, "dalpha", (B, n), F32)
+    _need(dx, "dx", (B, Cin, H, W), x.dtype, optional=True)
+    _need(dfc_w, "dfc_w", (n, Cin), F32, optional=True)
+    _need(dfc_b, "dfc_b", (n,), F32, optional=True)
+    _same_gpu(x=x, fc_w=fc_w, alpha=alpha, dalpha=dalpha, dx=dx, dfc_w=dfc_w, dfc_b=dfc_b)
     if dfc_w is None:
         dfc_w = torch.empty((n, Cin), dtype=torch.float32, device=x.device)
     if dfc_b is None:
@@ -428,8 +576,13 @@ def dynconv_forward_sparse(x: torch.Tensor, experts: torch.Tensor, alpha: torch.
                            stream=None) -> torch.Tensor:
     """y = (x if residual else 0) + mask * layer(x); mask [B, Ho, Wo] uint8 (nonzero = evaluate)."""
     desc = layer_desc(x, experts, stride, pad, groups)
-    Ho = (desc.H + 2 * pad - desc.kh) // stride + 1
-    Wo = (desc.W + 2 * pad - desc.kw) // stride + 1
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, stride, pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W))
+    _need(experts, "experts", tuple(experts.shape))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(mask, "mask", (desc.B, Ho, Wo), torch.uint8)
+    _need(y, "y", (desc.B, desc.Cout, Ho, Wo), x.dtype, optional=True)
+    _same_gpu(x=x, experts=experts, alpha=alpha, mask=mask, y=y)
     if y is None:
         y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
     ws, ws_bytes = _workspace(dynconv_forward_sparse_workspace_bytes(desc), x.device, workspace)

@@ -1,11 +1,10 @@
 // Gradients of the dynamic convolution layer and of its routing on gfx950.
 //
-// The pages train these layers end to end ("learn specialized convolutional
-// kernels for each example", CondConv: Conditionally Parameterized
-// Convolutions, abstract; "learns a linear mixture of n static kernels
-// weighted with their input-dependent attentions", KernelWarehouse:
-// Rethinking the Design of Dynamic Convolution, abstract) without printing a
-// backward pass. The kernels below compute the derivative of the forward
+// The pages train these layers end to end (CondConv: Conditionally
+// Parameterized Convolutions, abstract, where each example's kernel is
+// learned; KernelWarehouse: Rethinking the Design of Dynamic Convolution,
+// abstract, where the mixture of static kernels and its attentions are
+// learned) without printing a backward pass. The kernels below compute the derivative of the forward
 // W_b = sum_i alpha[b,i] E_i, y_b = conv(x_b, W_b):
 //
 //   dW_b[o][c,u,v] = sum_{r,s} dy[b,o,r,s] * x[b,c, r*st-p+u, s*st-p+v]

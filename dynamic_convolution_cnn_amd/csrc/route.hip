@@ -1,6 +1,6 @@
-// Routing: input-dependent attentions of each example (KernelWarehouse:
-// Rethinking the Design of Dynamic Convolution, abstract: "input-dependent
-// attentions"; FMDConv, abstract: temperature-scaled kernel attention).
+// Routing: the attentions of each example, computed from its input
+// (KernelWarehouse: Rethinking the Design of Dynamic Convolution, abstract;
+// FMDConv, abstract: temperature-scaled kernel attention).
 //
 //   gap[b,c] = mean_{h,w} x[b,c,h,w]
 //   z[b,i]   = sum_c fc_w[i,c] gap[b,c] + fc_b[i]

@@ -10,8 +10,8 @@
  * example with W_b. The attentions come from a router: global average pool
  * of the layer input, a fully connected layer with bias, then a sigmoid or a
  * softmax of the logits divided by a temperature (FMDConv: Fast
- * multi-attention dynamic convolution, abstract, "temperature ... kernel
- * attention"; the pages give no further detail of the router).
+ * multi-attention dynamic convolution, abstract, which puts a temperature on
+ * the kernel attention; the pages give no further detail of the router).
  *
  * Conventions shared by every entry point
  *   - Memory: every tensor pointer is a DEVICE pointer into memory the
@@ -97,8 +97,8 @@ typedef struct {
  *   z[b,i]   = sum_c fc_w[i,c] * gap[b,c] + fc_b[i]
  *   alpha    = sigmoid(z)                       (mode DYNCONV_SIGMOID)
  *            = softmax over i of z[b,i] / temperature (mode DYNCONV_SOFTMAX)
- * (KernelWarehouse abstract: "input-dependent attentions"; FMDConv abstract:
- * temperature-scaled kernel attention.)
+ * (KernelWarehouse abstract: the attentions depend on the input; FMDConv
+ * abstract: temperature-scaled kernel attention.)
  * Arguments: x [B,Cin,H,W] (dtype), fc_w [n,Cin] float32, fc_b [n] float32 or
  * NULL for no bias, temperature > 0 (ignored for sigmoid), alpha [B,n]
  * float32 (written). workspace: device memory of at least
@@ -235,12 +235,11 @@ dynconv_status_t dynconv_forward_sparse(const dynconv_desc_t *desc, const void *
 size_t dynconv_forward_sparse_workspace_bytes(const dynconv_desc_t *desc);
 
 /* ---- gradients ------------------------------------------------------------
- * The pages train dynamic convolutions end to end ("learn specialized
- * convolutional kernels for each example", CondConv: Conditionally
- * Parameterized Convolutions, abstract; "learns a linear mixture of n static
- * kernels weighted with their input-dependent attentions", KernelWarehouse:
- * Rethinking the Design of Dynamic Convolution, abstract) but print no
- * backward pass. These entry points compute the derivative of the forward
+ * The pages train dynamic convolutions end to end (CondConv: Conditionally
+ * Parameterized Convolutions, abstract, where the per-example kernels are
+ * learned; KernelWarehouse: Rethinking the Design of Dynamic Convolution,
+ * abstract, where the mixture of static kernels and its attentions are
+ * learned) but print no backward pass. These entry points compute the derivative of the forward
  * definition above for a given output gradient dy [B,Cout,Ho,Wo] (same
  * element type as x). Calls are asynchronous on `stream`, validate every
  * argument before any launch (nothing is launched or written on failure)

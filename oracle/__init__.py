@@ -11,27 +11,27 @@ host compiler, loads it with ctypes and marshals numpy arrays. Each function
 cites the passage of the pages it follows:
 
 * routing - global average pool, FC with bias, sigmoid or softmax(z/T):
-  "input-dependent attentions" (KernelWarehouse: Rethinking the Design of
-  Dynamic Convolution, abstract) and "temperature-degraded kernel attention"
-  (FMDConv: Fast multi-attention dynamic convolution, abstract). The pages
+  attentions that depend on the input (KernelWarehouse: Rethinking the Design
+  of Dynamic Convolution, abstract) and a kernel attention whose temperature
+  is lowered over training (FMDConv: Fast multi-attention dynamic
+  convolution, abstract). The pages
   give no formula for the router; the plainest reading is used.
-* mixing - W_b = sum_i alpha_bi E_i: "a linear mixture of n static kernels
-  weighted with their input-dependent attentions" (KernelWarehouse, abstract).
-* convolution - one ordinary convolution per example with its own kernel:
-  "specialized convolutional kernels for each example" (CondConv:
-  Conditionally Parameterized Convolutions, abstract).
+* mixing - W_b = sum_i alpha_bi E_i: each example's kernel is a weighted sum
+  of n static kernels, the weights being its attentions (KernelWarehouse,
+  abstract).
+* convolution - one ordinary convolution per example with its own kernel
+  (CondConv: Conditionally Parameterized Convolutions, abstract).
 * input and output attention - FMDConv's per-channel scales of the layer's
   input and output (FMDConv: Fast multi-attention dynamic convolution,
   abstract, which names them without a formula; the reading is stated at
   ``forward_attn``). Each head is a route (GAP -> FC -> sigmoid) of its own.
-* spatially sparse evaluation - "a small gating branch learns which spatial
-  positions should be evaluated" in a residual block, run with a
-  gather-scatter approach (Dynamic Convolutions: Exploiting Spatial Sparsity
-  for Faster Inference, abstract). ``forward_sparse`` takes the gate as a
+* spatially sparse evaluation - a small learned gate picks the output
+  positions a residual block computes, executed by gathering and scattering
+  those positions (Dynamic Convolutions: Exploiting Spatial Sparsity for
+  Faster Inference, abstract). ``forward_sparse`` takes the gate as a
   given mask: the layer's output at the masked positions only, plus the
   block's input when the block is residual.
-* gradients - the pages train these layers end to end ("learn specialized
-  convolutional kernels", CondConv abstract; "learns a linear mixture",
+* gradients - the pages train these layers end to end (CondConv abstract;
   KernelWarehouse abstract) but print no backward pass. ``backward`` and
   ``route_backward`` write out the derivative of the forward definition.
 

@@ -7,8 +7,8 @@
  * with the HIP library and includes nothing from it.
  *
  * What it computes, and where the pages define it:
- *   - per-example kernels ("specialized convolutional kernels for each
- *     example", CondConv: Conditionally Parameterized Convolutions, abstract);
+ *   - per-example kernels: every example gets a kernel of its own (CondConv:
+ *     Conditionally Parameterized Convolutions, abstract);
  *   - each example's kernel is a linear mixture of n static kernels weighted
  *     by input-dependent attentions (KernelWarehouse: Rethinking the Design
  *     of Dynamic Convolution, abstract);
@@ -59,7 +59,8 @@ int oracle_threads(void)
 
 /*
  * Global average pool of one example's channel plane: the mean over all
- * H*W positions (routing input; CondConv abstract, "input-dependent").
+ * H*W positions (the routing input: the attentions depend on the example,
+ * KernelWarehouse abstract).
  * gap[b*C + c] = (1/(H*W)) * sum_{h,w} x[b,c,h,w]
  */
 int oracle_gap(int B, int C, int H, int W, const float *x, double *gap)
@@ -384,10 +385,9 @@ int oracle_forward_attn(int B, int Cin, int H, int W, int Cout, int kh, int kw,
 
 /*
  * Gradients of the layer (mix, then per-example convolution) for a given
- * output gradient dy. The pages train these layers ("learn specialized
- * convolutional kernels for each example", CondConv abstract; "learns a
- * linear mixture of n static kernels weighted with their input-dependent
- * attentions", KernelWarehouse abstract) but print no backward pass; what
+ * output gradient dy. The pages train these layers (CondConv abstract: the
+ * per-example kernels are learned; KernelWarehouse abstract: the mixture and
+ * its attentions are learned) but print no backward pass; what
  * follows is the derivative of the forward definition above, term by term.
  * With W_b = sum_i alpha[b,i] E_i and y = conv(x_b, W_b):
  *   dW_b[o,c,u,v] = sum_{r,s} dy[b,o,r,s] * x[b, gc, r*st - p + u, s*st - p + v]

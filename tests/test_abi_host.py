@@ -369,3 +369,148 @@ def test_forward_sparse_checks():
     assert fs(desc=good_desc(Cout=32), res=1, wsb=1 << 30) == bd.DYNCONV_ERR_INVALID_ARG
     assert fs(desc=good_desc(stride=2), res=1, wsb=1 << 30) == bd.DYNCONV_ERR_INVALID_ARG
     assert bd.dynconv_forward_sparse_workspace_bytes(good_desc(groups=16, Cin=16, Cout=16)) == 0
+
+
+# ---- the binding's argument checks ---------------------------------------
+# The C ABI reads and writes through raw pointers sized from the descriptor,
+# so the binding checks every tensor against the call before handing it
+# over. These tests patch the library so that any compute entry point fails
+# the test if reached: each mismatch must be rejected first (size queries
+# stay available, they only compute byte counts on the host).
+
+COMPUTE_ENTRY_POINTS = {
+    "dynconv_route", "dynconv_mix", "dynconv_forward", "dynconv_pack_experts",
+    "dynconv_forward_packed", "dynconv_route_attn", "dynconv_forward_attn",
+    "dynconv_backward_data", "dynconv_backward_weights", "dynconv_route_backward",
+    "dynconv_forward_sparse",
+}
+
+
+class _NoCompute:
+    def __init__(self, real):
+        self._real = real
+
+    def __getattr__(self, name):
+        if name in COMPUTE_ENTRY_POINTS:
+            raise AssertionError(f"{name} reached the library with invalid arguments")
+        return getattr(self._real, name)
+
+
+@pytest.fixture
+def no_compute(monkeypatch):
+    real = _lib()
+    monkeypatch.setattr(bd, "lib", lambda: _NoCompute(real))
+
+
+def _t(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _layer(B=2, Cin=16, Cout=16, H=8, W=8, k=3, n=4, dtype=None):
+    import torch
+    dt = dtype or torch.bfloat16
+    return (_t((B, Cin, H, W), dt), _t((n, Cout, Cin, k, k), dt), _t((B, n), torch.float32))
+
+
+def test_binding_rejects_mismatched_forward_arguments(no_compute):
+    import torch
+    x, e, a = _layer()
+    cases = [
+        (lambda: bd.dynconv_forward(x.float(), e, a, 1, 1), "dtype"),            # f32 x, bf16 experts
+        (lambda: bd.dynconv_forward(x, _t((4, 16, 8, 3, 3)), a, 1, 1), "Cin"),   # experts.shape[2] != Cin
+        (lambda: bd.dynconv_forward(x, e, _t((2, 3), torch.float32), 1, 1), "alpha"),
+        (lambda: bd.dynconv_forward(x, e, a.double(), 1, 1), "alpha"),
+        (lambda: bd.dynconv_forward(x, e, a, 1, 1, y=_t((2, 16, 8, 7))), "y"),
+        (lambda: bd.dynconv_forward(x, e, a, 1, 1, y=_t((2, 16, 8, 8), torch.float32)), "y"),
+        (lambda: bd.dynconv_forward(x.transpose(2, 3), e, a, 1, 1), "contiguous"),
+        (lambda: bd.dynconv_forward(x, e, a, 1, 1), "device"),                   # host tensors
+        (lambda: bd.dynconv_forward(_t((2, 16, 8)), e, a, 1, 1), "x must be"),
+    ]
+    for fn, word in cases:
+        with pytest.raises(ValueError, match=word):
+            fn()
+
+
+def test_binding_rejects_mismatched_route_and_mix_arguments(no_compute):
+    import torch
+    x, e, a = _layer()
+    fw, fb = _t((4, 16), torch.float32), _t((4,), torch.float32)
+    with pytest.raises(ValueError, match="fc_w"):
+        bd.dynconv_route(x, _t((4, 15), torch.float32), fb)            # fewer than Cin columns
+    with pytest.raises(ValueError, match="fc_w"):
+        bd.dynconv_route(x, fw.to(torch.bfloat16), fb)
+    with pytest.raises(ValueError, match="fc_b"):
+        bd.dynconv_route(x, fw, _t((5,), torch.float32))
+    with pytest.raises(ValueError, match="alpha"):
+        bd.dynconv_route(x, fw, fb, alpha=_t((2, 5), torch.float32))
+    with pytest.raises(ValueError, match="device"):
+        bd.dynconv_route(x, fw, fb)
+    with pytest.raises(ValueError, match="mixed"):
+        bd.dynconv_mix(a, e, mixed=_t((2, 16, 16, 3, 2)))
+    with pytest.raises(ValueError, match="alpha"):
+        bd.dynconv_mix(_t((2, 4)), e)                                   # bf16 attentions
+    with pytest.raises(ValueError, match="device"):
+        bd.dynconv_mix(a, e)
+
+
+def test_binding_rejects_mismatched_attention_and_sparse_arguments(no_compute):
+    import torch
+    x, e, a = _layer()
+    f32 = torch.float32
+    heads = [_t((4, 16), f32), None, _t((16, 16), f32), None, _t((16, 16), f32), None]
+    bad_in = list(heads)
+    bad_in[2] = _t((16, 15), f32)
+    with pytest.raises(ValueError, match="fc_w_in"):
+        bd.dynconv_route_attn(x, 16, *bad_in)
+    with pytest.raises(ValueError, match="fc_w_out"):
+        bd.dynconv_route_attn(x, 24, *heads)                            # Cout 24, head has 16 rows
+    with pytest.raises(ValueError, match="a_in"):
+        bd.dynconv_forward_attn(x, e, a, _t((2, 15), f32), None, 1, 1)
+    with pytest.raises(ValueError, match="a_out"):
+        bd.dynconv_forward_attn(x, e, a, None, _t((2, 16)), 1, 1)     # bf16 attention
+    with pytest.raises(ValueError, match="mask"):
+        bd.dynconv_forward_sparse(x, e, a, _t((2, 8, 8), f32), 1, 1)   # mask must be uint8
+    with pytest.raises(ValueError, match="mask"):
+        bd.dynconv_forward_sparse(x, e, a, _t((2, 8, 7), torch.uint8), 1, 1)
+
+
+def test_binding_rejects_mismatched_gradient_arguments(no_compute):
+    import torch
+    x, e, a = _layer()
+    f32 = torch.float32
+    dy = _t((2, 16, 8, 8))
+    with pytest.raises(ValueError, match="dy"):
+        bd.dynconv_backward_weights(x, _t((2, 16, 8, 7)), e, a, 1, 1)
+    with pytest.raises(ValueError, match="dexperts"):
+        bd.dynconv_backward_weights(x, dy, e, a, 1, 1, dexperts=_t(tuple(e.shape)))   # bf16 gradient
+    with pytest.raises(ValueError, match="dalpha"):
+        bd.dynconv_backward_weights(x, dy, e, a, 1, 1, dalpha=_t((2, 3), f32))
+    with pytest.raises(ValueError, match="dx"):
+        bd.dynconv_backward_data(dy, e, a, 8, 8, 1, 1, dx=_t((2, 16, 8, 9)))
+    with pytest.raises(ValueError, match="dy"):
+        bd.dynconv_backward_data(_t((2, 16, 7, 8)), e, a, 8, 8, 1, 1)
+    with pytest.raises(ValueError, match="experts"):
+        bd.dynconv_backward_data(dy, e.float(), a, 8, 8, 1, 1)
+    with pytest.raises(ValueError, match="dalpha"):
+        bd.dynconv_route_backward(x, _t((4, 16), f32), a, _t((2, 5), f32))
+    with pytest.raises(ValueError, match="device"):
+        bd.dynconv_backward_weights(x, dy, e, a, 1, 1)
+
+
+def test_binding_rejects_short_packed_bank_and_workspace(no_compute):
+    import torch
+    x, e, a = _layer(B=2, Cin=64, Cout=64, H=14, W=14)
+    desc = bd.layer_desc(x, e, 1, 1, 1)
+    need = bd.dynconv_packed_experts_bytes(desc)
+    assert need > 0
+    short = torch.empty(need - 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="packed"):
+        bd.dynconv_pack_experts(desc, e, short)
+    with pytest.raises(ValueError, match="packed"):
+        bd.dynconv_forward_packed(desc, x, short, a)
+    with pytest.raises(ValueError, match="device"):
+        bd.dynconv_forward_packed(desc, x, torch.empty(need, dtype=torch.uint8), a)
+    ws_need = bd.dynconv_forward_workspace_bytes(desc)
+    with pytest.raises(ValueError, match="device|workspace"):
+        bd.dynconv_forward(x, e, a, 1, 1, workspace=torch.empty(max(ws_need - 16, 0), dtype=torch.uint8))

@@ -66,8 +66,22 @@ BWD_CASES = [
     (2, 64, 64, 20, 20, 3, 1, 1, 1, 4, "bf16"),     # 3x3 kernel gradient in two row bands (12 + 8 rows)
 ]
 
+# Batches of 9 or more examples split the contraction of dW_b into example
+# groups whose per-group dE partials are summed by a second pass; these cases
+# compare that sum element by element (2 and 3 groups, the 4- and 8-expert
+# contraction widths, float32 and depthwise banks, and the ResNet-18-shaped
+# layer at its full batch).
+MULTIGROUP_CASES = [
+    (12, 24, 32, 10, 10, 3, 1, 1, 1, 4, "bf16"),    # 2 groups of 6, 4-expert width
+    (24, 64, 64, 14, 14, 3, 1, 1, 1, 4, "bf16"),    # 3 groups of 8
+    (12, 16, 24, 9, 9, 3, 1, 1, 1, 11, "bf16"),     # 8 + 3 experts (both widths), 2 groups
+    (10, 12, 20, 9, 9, 3, 1, 1, 1, 3, "f32"),       # float32, 2 groups of 5
+    (12, 24, 24, 10, 10, 3, 1, 1, 24, 8, "bf16"),   # depthwise 3x3, 2 groups
+    (32, 64, 64, 56, 56, 3, 1, 1, 1, 4, "bf16"),    # ResNet-18-shaped layer, full batch, 4 groups
+]
 
-@pytest.mark.parametrize("case", BWD_CASES)
+
+@pytest.mark.parametrize("case", BWD_CASES + MULTIGROUP_CASES)
 def test_backward_matches_oracle(case):
     B, Cin, Cout, H, W, k, st, p, g, n, dtype = case
     x, e, a, dy = _layer_inputs(case, seed=100 + Cin + Cout)
@@ -192,10 +206,10 @@ def test_training_step_chain(dtype):
     ra, _, _ = oracle.route(x, fw, fb, oracle.SIGMOID)
     rx, rda, rde = oracle.backward(x, e, ra, dy, 1, p, 1)
     rfw, rfb, _, rdx = oracle.route_backward(x, fw, fb, rda, oracle.SIGMOID)
-    check(from_dev(da), rda, GRAD_TOL[dtype] * 10, f"chain dalpha {dtype}")
-    check(from_dev(de), rde, GRAD_TOL[dtype] * 10, f"chain dexperts {dtype}")
-    check(from_dev(dfw), rfw, GRAD_TOL[dtype] * 10, f"chain dfc_w {dtype}")
-    check(from_dev(dfb), rfb, GRAD_TOL[dtype] * 10, f"chain dfc_b {dtype}")
+    check(from_dev(da), rda, GRAD_TOL[dtype], f"chain dalpha {dtype}")
+    check(from_dev(de), rde, GRAD_TOL[dtype], f"chain dexperts {dtype}")
+    check(from_dev(dfw), rfw, GRAD_TOL[dtype], f"chain dfc_w {dtype}")
+    check(from_dev(dfb), rfb, GRAD_TOL[dtype], f"chain dfc_b {dtype}")
     check(from_dev(dx), rx + rdx, TOL[dtype], f"chain dx {dtype}")
 
 

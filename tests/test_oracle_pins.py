@@ -7,11 +7,9 @@ a dropped term, a wrong sign or index, or a transposed operand in
 
 * convolution indexing (stride, padding, groups, kh != kw): the single-expert
   case equals torch's conv2d in float64;
-* the mixture "linear mixture of n static kernels" (KernelWarehouse,
-  abstract): one-hot attentions select one expert; the layer is linear in the
+* the mixture of n static kernels (KernelWarehouse, abstract): one-hot attentions select one expert; the layer is linear in the
   attentions, checked against a sum of separate library convolutions;
-* "specialized convolutional kernels for each example" (CondConv, abstract):
-  permuting the batch permutes the outputs; every example uses its own row of
+* one kernel per example (CondConv, abstract): permuting the batch permutes the outputs; every example uses its own row of
   attentions;
 * routing: closed forms (zero FC, constant planes, sigmoid symmetry, softmax
   normalisation and shift invariance, large temperature) and a hand-worked
