@@ -47,16 +47,16 @@ GRAPH_STEPS = 10                # steps per HIP graph replay in the timed loop
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE on the headline workload (KiB per dispatch), each scaled by what the same
 # counter reads for a plain 256 MiB device copy (bench.py --calib-copy): FETCH_SIZE read
-# 131085 KiB for 262144 KiB moved (x 2.000), WRITE_SIZE 262144 KiB (x 1.000). Valid only
+# 131085.4 KiB for 262144 KiB moved (x 2.000), WRITE_SIZE 262144 KiB (x 1.000). Valid only
 # for the kernel source it was taken on (sha256 prefix over the files the dominant kernel
 # is compiled from, listed below); otherwise null.
 TRAFFIC = {
-    "resnet50_3x3": {"source_sha": "df7b9a8901e9d51d",
-                     "fetch_kib": 55057.8, "write_kib": 25088.0,
-                     "fetch_scale": 262144 / 131085, "write_scale": 1.0},
+    "resnet50_3x3": {"source_sha": "0a54c8e6c19cb5d8",
+                     "fetch_kib": 31917.2, "write_kib": 25088.0,
+                     "fetch_scale": 262144 / 131085.4, "write_scale": 1.0},
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "dynamic_convolution_cnn_amd", "csrc", f)
-                  for f in ("conv_fused.hip", "conv_common.hpp", "common.hpp")]
+                  for f in ("conv_fused_wave.hip", "conv_common.hpp", "common.hpp")]
 
 
 def parse():

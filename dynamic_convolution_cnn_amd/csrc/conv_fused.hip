@@ -777,6 +777,7 @@ bool fused_conv_supported(const Geom &g) {
 
 hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *packed,
                              const float *alpha, uint16_t *y, hipStream_t stream) {
+    if (fused_wave_ok(g)) return launch_conv_fused_wave(g, x, packed, alpha, y, stream);
     const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
     switch (g.n_pad / 2) {
     case 1: return launch_fused_np<1>(g, x, pk, alpha, y, stream);

@@ -1,0 +1,441 @@
+// Fused mixing + 3x3 convolution for small images (rows of at most 14
+// outputs, at most 14 output rows): the ResNet-50-shaped layer, 256 -> 256
+// channels at 14x14. W_b = sum_i alpha_bi E_i (KernelWarehouse: Rethinking
+// the Design of Dynamic Convolution, abstract) is formed inside the GEMM and
+// never reaches memory; the convolution with it is one ordinary convolution
+// per example (CondConv: Conditionally Parameterized Convolutions, abstract).
+//
+// Work split. A workgroup owns 4 examples and 64 output channels with 4
+// waves, one per SIMD. Wave e owns example e: all 64 channels and all output
+// positions (7 blocks of 32 positions = two output rows padded to 16), 14
+// accumulator tiles of 32x32 fp32 in AGPRs. Each MFMA
+// (v_mfma_f32_32x32x16_bf16) takes 32 positions x 16 input channels of one
+// tap as A and 16 input channels x 32 output channels of W_b as B.
+//
+// Input tile. Each wave stages its own example's input, 16 channels at a
+// time, into a private LDS tile of 16 x 16 positions (tile row = input row
+// + 1, tile column = input column; padding rows and the columns past the
+// image stay zero) after one zero guard position. Positions are 48 bytes
+// apart (32 bytes of channels and 16 of padding), so the 16-byte reads of
+// any 16 consecutive positions fall on distinct banks. Staging needs no
+// workgroup barrier. Tap (u, v) of output position (r, c) is tile position
+// (r + u) * 16 + c + v - 1 + 1: a constant offset from the tap (0, 1)
+// address, so each tap's A fragment is one 16-byte read per lane with an
+// immediate offset; the left neighbour of column 0 is the zero column 15 of
+// the row above (or the guard).
+//
+// Mixing on the matrix cores. v_mfma_f32_4x4x4_16b_bf16 computes 16
+// independent 4x4x4 products: with the 4 examples' attention rows as A and
+// one weight's 4 expert values per lane as B (from the packed bank,
+// packed[t][o][c][i]), lane l receives the 4 examples' mixed values of its
+// weight. Attentions are split in a bf16 high part and the rounding
+// remainder (two products accumulated in fp32); the sum is rounded once to
+// bf16. Every lane of the workgroup mixes 4 input channels of one output
+// channel for the three taps of a kernel row, so the workgroup forms all of
+// a group's B fragments for all 4 examples and each expert word is read once
+// per workgroup. The fragments pass to their waves through a double-buffered
+// LDS stage.
+//
+// Schedule. The K loop runs over groups g = (16-channel chunk, kernel row
+// u): 3 taps x 14 MFMAs per wave. During group g a wave mixes group g + 1
+// from expert words loaded during group g - 1 and loads the words of group
+// g + 2. One workgroup barrier per group, placed after the second tap's
+// MFMAs: it publishes group g + 1's fragments, which are then read (with
+// the next row's A fragments) while the third tap's MFMAs run. The next
+// chunk's input loads during the chunk's first two groups and reaches the
+// other tile during its last two.
+//
+// Epilogue. Each wave writes its valid outputs into LDS as 64 dense channel
+// planes (its part of y is one contiguous run) and copies them to y with
+// 16-byte stores.
+#include "conv_common.hpp"
+
+namespace dynconv {
+namespace {
+
+constexpr int kWvChunk = 16;                       // input channels per chunk
+constexpr int kWvPosBytes = 48;                    // 16 channels x 2 bytes + 16 bytes of padding
+constexpr int kWvTileBytes = 12800;                // guard + 16 x 16 positions (+ overreach of junk lanes)
+constexpr int kWvNPB = 7;                          // position blocks of 32
+constexpr int kWvStageBytes = 2 * 3 * 2 * 4 * 1024;  // [buf][tap][tile][example] x 1 KB
+constexpr int kWvLdsBytes = 4 * 2 * kWvTileBytes + kWvStageBytes;  // 148 KB
+constexpr int kWvRounds = 7;                       // staging rounds of 64 tasks per chunk
+static_assert((1 + 16 * 16 + 1) * kWvPosBytes <= kWvTileBytes, "tile holds the guard and every read");
+
+__shared__ __attribute__((aligned(16))) u32x4_t s_wv[kWvLdsBytes / 16];
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Byte offset in a tile of tile position q (the guard is position -1).
+__device__ __forceinline__ int wv_pos(int q) { return (q + 1) * kWvPosBytes; }
+
+template <int NP2>
+struct WvWords {
+    uint32_t w[3][4 * NP2];  // [tap v][channel j * NP2 + expert pair]
+};
+
+// 64-bit pointer as a buffer descriptor of nbytes (reads past it return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wv_rsrc(const void *p, int nbytes) {
+    const uint64_t q = reinterpret_cast<uint64_t>(p);
+    const uint64_t qs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)q) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(q >> 32)) << 32);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(qs), 0,
+                                             __builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
+}
+
+template <int NP2>
+__global__ __launch_bounds__(256) void conv_fused_wave_kernel(const uint16_t *__restrict__ x,
+                                                              const uint32_t *__restrict__ packed,
+                                                              const float *__restrict__ alpha,
+                                                              uint16_t *__restrict__ y, ConvArgs a) {
+    char *lds = reinterpret_cast<char *>(s_wv);
+    const int tid = threadIdx.x;
+    const int e = __builtin_amdgcn_readfirstlane(tid >> 6);  // example of this wave
+    const int lane = tid & 63;
+    // XCD k holds logical tiles [32k, 32k + 32): 8 example quads x all 4
+    // channel tiles, so an example's input and a channel tile's expert slice
+    // are both fetched once per XCD.
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int ot = logical % a.n_otiles;
+    const int bt = logical / a.n_otiles;
+    const int o0 = ot * 64;
+    const int b_raw = bt * 4 + e;
+    const bool valid = b_raw < a.B;
+    const int b = valid ? b_raw : a.B - 1;
+
+    auto tile = [&](int ex, int buf) { return lds + (ex * 2 + buf) * kWvTileBytes; };
+    auto stage = [&](int buf, int v, int n, int ex) {
+        return lds + 4 * 2 * kWvTileBytes + (((buf * 3 + v) * 2 + n) * 4 + ex) * 1024;
+    };
+
+    // ---- mixing role: output channel o0 + om; channel pairs mp and 4 + mp
+    // (channels 2 mp, 2 mp + 1 and 8 + 2 mp, 9 + 2 mp) of each chunk
+    const int om = tid >> 2, mp = tid & 3;
+    s16x4_t ahi, alo;
+    {
+        const int be = min(bt * 4 + (lane & 3), a.B - 1);
+        const bool live = bt * 4 + (lane & 3) < a.B;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float v = (k < a.n && live) ? alpha[(long)be * a.n + k] : 0.f;
+            const uint16_t h = f32_to_bf16(v);
+            ahi[k] = (short)h;
+            alo[k] = (short)f32_to_bf16(v - bf16_to_f32(h));
+        }
+    }
+    // Expert words: the bank as a buffer (groups past the last read zeros);
+    // lane offset for output channel o0 + om, channel pair mp of chunk 0, and
+    // one scalar offset per tap.
+    const int tap_bytes = a.Cout * a.Cin_pad * NP2 * 4;
+    const auto bank = wv_rsrc(packed, 9 * tap_bytes);
+    const int wlane = (min(o0 + om, a.Cout - 1) * a.Cin_pad + 2 * mp) * NP2 * 4;
+    const int nchunks = a.Cin_pad / kWvChunk;
+    auto load_words = [&](int c, int u, WvWords<NP2> &wd) {
+        const int vo = wlane + c * (kWvChunk * NP2 * 4);
+#pragma unroll
+        for (int v = 0; v < 3; ++v) {
+            const int so = __builtin_amdgcn_readfirstlane((3 * u + v) * tap_bytes);
+            // channels 2 mp, 2 mp + 1 (words 0 .. 2 NP2 - 1), then 8 channels on
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t t[4];
+                if constexpr (NP2 == 2) {
+                    const u32x4_t v4 = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bank, vo + h * 8 * NP2 * 4, so, 0));
+                    t[0] = v4.x; t[1] = v4.y; t[2] = v4.z; t[3] = v4.w;
+                } else {
+                    const u32x2_t v2 = __builtin_bit_cast(
+                        u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(bank, vo + h * 8 * NP2 * 4, so, 0));
+                    t[0] = v2.x; t[1] = v2.y;
+                }
+#pragma unroll
+                for (int q = 0; q < 2 * NP2; ++q) wd.w[v][2 * NP2 * h + q] = t[q];
+            }
+        }
+    };
+    // Consumer lanes of the mixed words: output channel om & 31 of tile
+    // om >> 5 holds channels 0..7 of the chunk in lane om & 31 and channels
+    // 8..15 in lane 32 + (om & 31); channel pair mp is its 4 bytes at 4 mp.
+    // One stage write of a wave thus covers 16 whole consumer lanes: 256
+    // contiguous bytes.
+    const int moff = (om & 31) * 16 + mp * 4;
+    const int mtile = om >> 5;
+    // Mixing of channels j0, j0 + 1 (of this lane's four) of one tap: the
+    // high-part products, then the low-part products accumulated onto them.
+    auto mix_hi = [&](const uint32_t (&w)[4 * NP2], f32x4_t (&d)[4], int j0) {
+#pragma unroll
+        for (int j = j0; j < j0 + 2; ++j) {
+            u32x2_t e2;
+            e2.x = w[j * NP2];
+            e2.y = NP2 == 2 ? w[j * NP2 + 1] : 0u;
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            d[j] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi, __builtin_bit_cast(s16x4_t, e2), z, 0, 0, 0);
+        }
+    };
+    auto mix_lo = [&](const uint32_t (&w)[4 * NP2], f32x4_t (&d)[4], int j0) {
+#pragma unroll
+        for (int j = j0; j < j0 + 2; ++j) {
+            u32x2_t e2;
+            e2.x = w[j * NP2];
+            e2.y = NP2 == 2 ? w[j * NP2 + 1] : 0u;
+            d[j] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo, __builtin_bit_cast(s16x4_t, e2), d[j], 0, 0, 0);
+        }
+    };
+    // Channels j0, j0 + 1 of one tap: products, then one 4-byte stage write
+    // per example.
+    auto mix_pair = [&](const uint32_t (&w)[4 * NP2], int buf, int v, int j0) {
+        f32x4_t d[4];
+        mix_hi(w, d, j0);
+        mix_lo(w, d, j0);
+#pragma unroll
+        for (int ex = 0; ex < 4; ++ex)
+            *reinterpret_cast<uint32_t *>(stage(buf, v, mtile, ex) + moff + (j0 >> 1) * 512) =
+                pack_bf16x2(d[j0][ex], d[j0 + 1][ex]);
+    };
+    auto mix_tap = [&](const uint32_t (&w)[4 * NP2], int buf, int v) {
+        mix_pair(w, buf, v, 0);
+        mix_pair(w, buf, v, 2);
+    };
+
+    // ---- convolution role
+    // zero both tiles of this example (guard, padding rows and columns)
+    {
+        u32x4_t z = {0u, 0u, 0u, 0u};
+        u32x4_t *t0 = reinterpret_cast<u32x4_t *>(tile(e, 0));
+        for (int i = lane; i < 2 * kWvTileBytes / 16; i += 64) t0[i] = z;
+    }
+    const uint16_t *xb = x + (long)b * a.x_bstride;
+    const int HW = a.H * a.W;
+    const int plane = HW * 2;  // bytes per input channel plane
+    const int pairs = a.W >> 1;
+    const int per_g = a.H * pairs;  // position pairs per channel
+    const int ntasks = 4 * per_g;   // (position pair, channel quad) tasks per chunk
+    // Buffer descriptor of chunk c's 16 channel planes; channels past Cin
+    // are beyond its extent and read as zeros.
+    auto rsrc_of = [&](int c) {
+        const int c0 = min(c * kWvChunk, a.Cin - 1);
+        return wv_rsrc(xb + (long)c0 * HW, max(0, min(kWvChunk, a.Cin - c * kWvChunk)) * plane);
+    };
+    // Staging task k: channel quad k / per_g, row r, column pair kp: 4 dword
+    // loads (one per channel, both positions) and two 8-byte tile writes.
+    // Lane takes tasks lane + 64 i (the last repeats: same bytes, same place).
+    // Source and destination offsets do not depend on the chunk: computed
+    // once, packed as source | destination << 16 (both below 2^16).
+    uint32_t stask[kWvRounds];
+#pragma unroll
+    for (int i = 0; i < kWvRounds; ++i) {
+        const int k = min(i * 64 + lane, ntasks - 1);
+        const int g4 = k / per_g, rem = k - g4 * per_g;
+        const int row = rem / pairs, kp = rem - row * pairs;
+        const int vo = 4 * g4 * plane + 4 * rem;  // channel 4 g4, row r, columns 2 kp, 2 kp + 1
+        const int dst = wv_pos((row + 1) * 16 + 2 * kp) + 8 * g4;  // position + 1 is 48 bytes further
+        stask[i] = (uint32_t)vo | ((uint32_t)dst << 16);
+    }
+    auto st_load = [&](__amdgpu_buffer_rsrc_t rs, int round, uint32_t (&r)[4]) {
+        const int vo = (int)(stask[round] & 0xffffu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + j * plane, 0, 0);
+    };
+    auto st_store = [&](char *t, int round, const uint32_t (&r)[4]) {
+        const int dst = (int)(stask[round] >> 16);
+        u32x2_t p0, p1;
+        p0.x = __builtin_amdgcn_perm(r[1], r[0], 0x05040100u); p0.y = __builtin_amdgcn_perm(r[3], r[2], 0x05040100u);
+        p1.x = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u); p1.y = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
+        *reinterpret_cast<u32x2_t *>(t + dst) = p0;
+        *reinterpret_cast<u32x2_t *>(t + dst + kWvPosBytes) = p1;
+    };
+
+    // A fragments: block pb, lane: output row 2 pb + (lane & 31) / 16, column
+    // lane & 15, channel half lane / 32; tap (u, v) adds (16 u + v - 1)
+    // positions to the output position's own tile position (row + 1, col).
+    const int aoff = wv_pos((((lane & 31) >> 4) + 1) * 16 + (lane & 15)) + 16 * (lane >> 5);
+    auto read_tap = [&](const char *t, int u, int v, u32x4_t (&f)[kWvNPB]) {
+        const char *tb = t + aoff + (16 * (u - 1) + v - 1) * kWvPosBytes;
+#pragma unroll
+        for (int pb = 0; pb < kWvNPB; ++pb)
+            f[pb] = *reinterpret_cast<const u32x4_t *>(tb + pb * 32 * kWvPosBytes);
+    };
+    auto read_b = [&](int buf, bf16x8_t (&bf)[3][2]) {
+#pragma unroll
+        for (int v = 0; v < 3; ++v)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                bf[v][n] = *reinterpret_cast<const bf16x8_t *>(stage(buf, v, n, e) + lane * 16);
+    };
+
+    f32x16_t acc[kWvNPB][2];
+#pragma unroll
+    for (int i = 0; i < kWvNPB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+
+    // One tap's 14 MFMAs in 7 slots (block pb, both channel tiles). After
+    // slot k, the work item k of the tap runs; scheduling barriers keep that
+    // order, so the mixing chain's dependent steps sit two or more MFMA pairs
+    // apart and the matrix core never waits on them.
+    auto mfma_pb = [&](const u32x4_t (&af)[kWvNPB], const bf16x8_t (&bf)[2], int pb) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, af[pb]);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+            acc[pb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bf[n], acc[pb][n], 0, 0, 0);
+    };
+
+    // ---- prologue: chunk 0 staged, chunk 1's input in flight, group 0
+    // mixed into stage buffer 0, words of group 1 in flight
+    uint32_t sr[kWvRounds][4];  // the next chunk's input, loaded a chunk ahead of its tile writes
+    {
+        const auto rs0 = rsrc_of(0);
+#pragma unroll
+        for (int i = 0; i < kWvRounds; ++i) st_load(rs0, i, sr[i]);
+        WvWords<NP2> w0;
+        load_words(0, 0, w0);
+        // the tile zeroing by this wave precedes the staging writes in LDS order
+#pragma unroll
+        for (int i = 0; i < kWvRounds; ++i) st_store(tile(e, 0), i, sr[i]);
+        const auto rs1 = rsrc_of(min(1, nchunks - 1));
+#pragma unroll
+        for (int i = 0; i < kWvRounds; ++i) st_load(rs1, i, sr[i]);
+#pragma unroll
+        for (int v = 0; v < 3; ++v) mix_tap(w0.w[v], 0, v);
+    }
+    WvWords<NP2> wn;  // words of group g + 1
+    load_words(0, 1, wn);
+    lds_barrier();  // stage buffer 0 complete
+    bf16x8_t bcur[3][2];
+    read_b(0, bcur);
+    u32x4_t acur[kWvNPB];
+    read_tap(tile(e, 0), 0, 0, acur);
+
+    for (int c = 0; c < nchunks; ++c) {
+        const char *tcur = tile(e, c & 1);
+        char *tnext = tile(e, (c + 1) & 1);
+        const auto rs2 = rsrc_of(min(c + 2, nchunks - 1));
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int g = 3 * c + u;
+            const int buf = g & 1;
+            const int nb = buf ^ 1;
+            // the next chunk's input goes to its tile (written during groups 0
+            // and 1; the last chunk rewrites a copy of itself into the idle
+            // tile), and the chunk after it starts loading into the same
+            // registers
+            if (u == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st_store(tnext, i, sr[i]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st_load(rs2, i, sr[i]);
+            }
+            if (u == 1) {
+#pragma unroll
+                for (int i = 4; i < kWvRounds; ++i) st_store(tnext, i, sr[i]);
+#pragma unroll
+                for (int i = 4; i < kWvRounds; ++i) st_load(rs2, i, sr[i]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // tap 0 (left column) with half of group g + 1's mixing
+            u32x4_t anx[kWvNPB];
+            read_tap(tcur, u, 1, anx);
+            __builtin_amdgcn_sched_barrier(0);  // reads for the next tap go out first
+#pragma unroll
+            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb(acur, bcur[0], pb);
+            mix_pair(wn.w[0], nb, 0, 0);
+            mix_pair(wn.w[0], nb, 0, 2);
+            mix_pair(wn.w[1], nb, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // tap 1 (centre) with the rest; then the words of group g + 2
+            // load into the same registers
+            read_tap(tcur, u, 2, acur);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb(anx, bcur[1], pb);
+            mix_pair(wn.w[1], nb, 1, 2);
+            mix_pair(wn.w[2], nb, 2, 0);
+            mix_pair(wn.w[2], nb, 2, 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (u == 0) load_words(c, 2, wn);
+            else load_words(c + 1, u - 1, wn);
+            // the group's B fragments are in registers (read after the
+            // previous barrier), so the stage buffer g + 1 writes into is free
+            lds_barrier();
+            bf16x8_t bnext[3][2];
+            read_b(nb, bnext);
+            // tap 2 (right column); the next group's first fragments load
+            read_tap(u < 2 ? tcur : tnext, u < 2 ? u + 1 : 0, 0, anx);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb(acur, bcur[2], pb);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int v = 0; v < 3; ++v)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) bcur[v][n] = bnext[v][n];
+#pragma unroll
+            for (int pb = 0; pb < kWvNPB; ++pb) acur[pb] = anx[pb];
+        }
+    }
+
+    // ---- epilogue: dense channel planes in LDS, then 16-byte copies
+    lds_barrier();  // every wave is done with the tiles and the stage
+    const int P = a.P;
+    const int ah = lane >> 5;
+    char *ebuf = lds + e * (64 * P * 2);
+    uint32_t *ew = reinterpret_cast<uint32_t *>(ebuf);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int ch = 32 * n + (lane & 31);
+#pragma unroll
+        for (int pb = 0; pb < kWvNPB; ++pb) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 2 * pb + (j >> 1);
+                const int col = 8 * (j & 1) + 4 * ah;
+                const int w2 = (ch * P + r * a.Wo + col) >> 1;  // P and Wo even: word aligned
+                if (r < a.Ho && col < a.Wo) ew[w2] = pack_bf16x2(acc[pb][n][4 * j], acc[pb][n][4 * j + 1]);
+                if (r < a.Ho && col + 2 < a.Wo)
+                    ew[w2 + 1] = pack_bf16x2(acc[pb][n][4 * j + 2], acc[pb][n][4 * j + 3]);
+            }
+        }
+    }
+    const int och = min(64, a.Cout - o0);
+    if (valid && och > 0) {
+        const int bytes = och * P * 2;
+        char *dst = reinterpret_cast<char *>(y + ((long)b * a.Cout + o0) * P);
+        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (bytes & 15) == 0) {
+            for (int off = lane * 16; off < bytes; off += 1024)
+                *reinterpret_cast<u32x4_t *>(dst + off) = *reinterpret_cast<const u32x4_t *>(ebuf + off);
+        } else {
+            for (int off = lane * 4; off < bytes; off += 256)
+                *reinterpret_cast<uint32_t *>(dst + off) = *reinterpret_cast<const uint32_t *>(ebuf + off);
+        }
+    }
+}
+
+}  // namespace
+
+// 3x3, stride 1, padding 1, at most 14 x 14 outputs (7 blocks of two rows
+// padded to 16), 3 or 4 experts (two expert-pair words per weight), even W (position pairs are 4-byte words of a channel
+// plane), the staging tasks of a chunk within 7 rounds of 64 lanes, and the
+// four examples' output planes within the LDS.
+bool fused_wave_ok(const Geom &g) {
+    return g.stride == 1 && g.KH == 3 && g.KW == 3 && g.pad == 1 && g.H <= 14 && g.W <= 14 &&
+           g.W % 2 == 0 && g.H * (g.W / 2) * 4 <= kWvRounds * 64 && 4 * 64 * g.P * 2 <= kWvLdsBytes &&
+           16 * g.H * g.W * 2 < (1 << 16) && 9L * g.Cout * g.Cin_pad * (g.n_pad / 2) * 4 < (1L << 31) &&
+           g.n_pad == 4 && g.Cin_pad % kWvChunk == 0;
+}
+
+hipError_t launch_conv_fused_wave(const Geom &g, const uint16_t *x, const uint16_t *packed, const float *alpha,
+                                  uint16_t *y, hipStream_t stream) {
+    ConvArgs a = base_args(g);
+    a.tile_rows = 16;
+    a.n_btiles = ceil_div(g.B, 4);
+    a.n_otiles = ceil_div(g.Cout, 64);
+    const long blocks = (long)a.n_btiles * a.n_otiles;
+    const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
+    hipLaunchKernelGGL(conv_fused_wave_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, x, pk, alpha, y, a);
+    return hipGetLastError();
+}
+
+}  // namespace dynconv

@@ -263,6 +263,11 @@ RAGGED = [
     (2, 64, 130, 18, 16, (1, 1), 1, 0, 4),   # 1x1, Cin <= 64: three output tiles (tail 2), position tail 32
     (3, 20, 33, 10, 8, (1, 1), 1, 0, 3),     # 1x1, one partial chunk, odd Cout
     (3, 96, 40, 12, 12, (1, 1), 1, 0, 2),    # 1x1, three chunks (odd count) on the persistent path
+    # 3x3 pad-1 layers up to 14x14 with n <= 4 (the fused path's one-wave-per-example kernel)
+    (1, 20, 70, 14, 12, (3, 3), 1, 1, 2),    # one example, 16-channel chunk tail, Cout tail, two experts
+    (6, 256, 256, 14, 14, (3, 3), 1, 1, 1),  # one expert
+    (9, 32, 64, 14, 14, (3, 3), 1, 1, 4),    # 9 examples: a quad with one live example
+    (4, 16, 64, 2, 2, (3, 3), 1, 1, 3),      # 2x2 image
 ]
 
 
