@@ -46,7 +46,7 @@ EXPORTED = (
     "dynconv_backward_data_workspace_bytes", "dynconv_backward_weights",
     "dynconv_backward_weights_workspace_bytes", "dynconv_route_backward",
     "dynconv_route_backward_workspace_bytes", "dynconv_forward_sparse",
-    "dynconv_forward_sparse_workspace_bytes",
+    "dynconv_forward_sparse_workspace_bytes", "dynconv_forward_noalloc",
 )
 
 
@@ -128,6 +128,8 @@ def lib():
     L.dynconv_forward_sparse.restype = i32
     L.dynconv_forward_sparse_workspace_bytes.argtypes = [D]
     L.dynconv_forward_sparse_workspace_bytes.restype = sz
+    L.dynconv_forward_noalloc.argtypes = [D, i32, P, P, P, P, P]
+    L.dynconv_forward_noalloc.restype = i32
     _lib = L
     return L
 
@@ -352,6 +354,29 @@ def dynconv_forward(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
     _check(lib().dynconv_forward(ctypes.byref(desc), int(policy), _ptr(x), _ptr(experts),
                                  _ptr(alpha), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "dynconv_forward")
+    return y
+
+
+DYNCONV_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def dynconv_forward_noalloc(x: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
+                            stride: int = 1, pad: int = 0, groups: int = 1,
+                            policy: int = DYNCONV_POLICY_AUTO, y: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """dynconv_forward with the library's fixed per-GPU scratch as workspace (no
+    device allocation in the call; pass y to keep the call allocation-free)."""
+    desc = layer_desc(x, experts, stride, pad, groups)
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, stride, pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W))
+    _need(experts, "experts", tuple(experts.shape))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(y, "y", (desc.B, desc.Cout, Ho, Wo), x.dtype, optional=True)
+    _same_gpu(x=x, experts=experts, alpha=alpha, y=y)
+    if y is None:
+        y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    _check(lib().dynconv_forward_noalloc(ctypes.byref(desc), int(policy), _ptr(x), _ptr(experts),
+                                         _ptr(alpha), _ptr(y), _stream(stream)), "dynconv_forward_noalloc")
     return y
 
 

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -298,6 +299,40 @@ dynconv_status_t check_sparse(const dynconv_desc_t *desc, dynconv::Geom &g, int3
     return DYNCONV_OK;
 }
 
+// ---- workspace of the no-allocation forward --------------------------------
+// A fixed device array per GPU (each GPU holds its own copy from the first
+// use until the process ends). In host code `scratch` only names the symbol:
+// its device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = DYNCONV_NOALLOC_MAX_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+dynconv_status_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DYNCONV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DYNCONV_ERR_UNSUPPORTED, "device %d: the no-allocation forward supports devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(DYNCONV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DYNCONV_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -383,6 +418,32 @@ dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy, con
                                  const void *experts, const float *alpha, void *y,
                                  void *workspace, size_t workspace_bytes, void *stream) {
     return forward_impl(desc, policy, x, experts, alpha, y, workspace, workspace_bytes, stream, {});
+}
+
+dynconv_status_t dynconv_forward_noalloc(const dynconv_desc_t *desc, int32_t policy, const void *x,
+                                         const void *experts, const float *alpha, void *y, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !experts || !alpha || !y)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, experts, alpha and y must not be NULL");
+    if (!aligned16(x) || !aligned16(experts) || !aligned16(alpha) || !aligned16(y))
+        return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    int32_t p;
+    s = resolve_policy(g, policy, p);
+    if (s != DYNCONV_OK) return s;
+    const size_t need = forward_ws(g, p);
+    if (need > kScratchBytes)
+        return fail(DYNCONV_ERR_UNSUPPORTED,
+                    "this layer needs %zu bytes of workspace; the no-allocation forward holds %zu (use dynconv_forward "
+                    "with a caller-provided workspace)",
+                    need, kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        s = scratch_address(&ws);
+        if (s != DYNCONV_OK) return s;
+    }
+    return forward_impl(desc, policy, x, experts, alpha, y, ws, need, stream, {});
 }
 
 size_t dynconv_forward_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t policy) {

@@ -169,6 +169,24 @@ dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t poli
                                         size_t workspace_bytes, void *stream);
 size_t dynconv_forward_packed_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
 
+/* dynconv_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The library keeps one fixed scratch array
+ * of DYNCONV_NOALLOC_MAX_BYTES per GPU (held from the first call on that GPU
+ * until the process ends) and uses it as the workspace; the call itself
+ * allocates and frees nothing. The caller still owns x, experts, alpha and y
+ * (as dynconv_forward); the call runs on the current device, which must be
+ * the one `stream` belongs to. Layers whose workspace
+ * (dynconv_forward_workspace_bytes(desc, policy)) exceeds the array return
+ * DYNCONV_ERR_UNSUPPORTED before anything is enqueued. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and must be serialised by the caller; calls on
+ * one stream are ordered and safe. Nothing in the array needs to start at
+ * zero. Results are bitwise those of dynconv_forward with the same policy. */
+#define DYNCONV_NOALLOC_MAX_BYTES (64ull << 20)
+dynconv_status_t dynconv_forward_noalloc(const dynconv_desc_t *desc, int32_t policy, const void *x,
+                                         const void *experts, const float *alpha, void *y, void *stream);
+
 /* FMDConv's multi-attention layer (FMDConv: Fast multi-attention dynamic
  * convolution via speed-accuracy trade-off, abstract: input attention,
  * temperature-degraded kernel attention and output attention). The page
