@@ -824,6 +824,7 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
         hipLaunchKernelGGL(conv_pm1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
         return hipGetLastError();
     }
+    if (pm3w_ok(g)) return launch_conv_pm3w(g, x, wt, y, stream, att.out);
     if (pm3_ok(g)) {
         ConvArgs a = base_args(g);
         a.tile_rows = tile_rows_for(g, kPmMT);

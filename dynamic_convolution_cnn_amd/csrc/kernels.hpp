@@ -87,6 +87,12 @@ bool premix_conv_supported(const Geom &g);
 hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *wt,
                               uint16_t *y, hipStream_t stream, ChanAttn att = {});
 
+// 3x3 stride-1 pad-1 premix convolution with 4x2 / 2x4 wave tiles
+// (conv_pm3w.hip); launch_conv_premix dispatches to it.
+bool pm3w_ok(const Geom &g);
+hipError_t launch_conv_pm3w(const Geom &g, const uint16_t *x, const uint16_t *wt, uint16_t *y,
+                            hipStream_t stream, const float *a_out);
+
 // Implicit-GEMM bf16 MFMA convolution that mixes each kernel tile from the
 // packed bank in registers (no mixed kernel in memory).
 bool fused_conv_supported(const Geom &g);
