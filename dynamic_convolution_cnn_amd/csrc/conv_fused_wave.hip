@@ -18,11 +18,12 @@
 // image stay zero) after one zero guard position. Positions are 48 bytes
 // apart (32 bytes of channels and 16 of padding), so the 16-byte reads of
 // any 16 consecutive positions fall on distinct banks. Staging needs no
-// workgroup barrier. Tap (u, v) of output position (r, c) is tile position
-// (r + u) * 16 + c + v - 1 + 1: a constant offset from the tap (0, 1)
-// address, so each tap's A fragment is one 16-byte read per lane with an
-// immediate offset; the left neighbour of column 0 is the zero column 15 of
-// the row above (or the guard).
+// workgroup barrier. Tap (u, v) of output position (r, c) is tile column
+// c + v - 1 of tile row r + u. Only the centre tap (v = 1) of each kernel row
+// is read from LDS (one 16-byte read per lane and position block); a lane
+// holds one column of a 16-lane row, so the left and right taps are the same
+// registers moved one lane within the row (DPP), with a zero entering at the
+// row ends.
 //
 // Mixing on the matrix cores. v_mfma_f32_4x4x4_16b_bf16 computes 16
 // independent 4x4x4 products: with the 4 examples' attention rows as A and
@@ -41,7 +42,7 @@
 // from expert words loaded during group g - 1 and loads the words of group
 // g + 2. One workgroup barrier per group, placed after the second tap's
 // MFMAs: it publishes group g + 1's fragments, which are then read (with
-// the next row's A fragments) while the third tap's MFMAs run. The next
+// the next row's centre fragments) while the third tap's MFMAs run. The next
 // chunk's input loads during the chunk's first two groups and reaches the
 // other tile during its last two.
 //
@@ -68,6 +69,26 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // Byte offset in a tile of tile position q (the guard is position -1).
 __device__ __forceinline__ int wv_pos(int q) { return (q + 1) * kWvPosBytes; }
+
+// Lanes 16 k .. 16 k + 15 of an A fragment hold the 16 columns of one tile
+// row. The left and right taps of a position are the centre taps of its
+// left and right neighbours: the centre fragment read from lane l - 1
+// (v_mov_b32_dpp row_shr:1) or lane l + 1 (row_shl:1) of the same row of 16
+// lanes. A lane whose source is outside its row receives 0: on the left that
+// is the zero padding column; on the right the lane is column 15, past every
+// output column.
+__device__ __forceinline__ u32x4_t left_neighbour(u32x4_t x) {
+    return u32x4_t{(uint32_t)__builtin_amdgcn_mov_dpp((int)x.x, 0x111, 0xf, 0xf, true),
+                   (uint32_t)__builtin_amdgcn_mov_dpp((int)x.y, 0x111, 0xf, 0xf, true),
+                   (uint32_t)__builtin_amdgcn_mov_dpp((int)x.z, 0x111, 0xf, 0xf, true),
+                   (uint32_t)__builtin_amdgcn_mov_dpp((int)x.w, 0x111, 0xf, 0xf, true)};
+}
+__device__ __forceinline__ u32x4_t right_neighbour(u32x4_t x) {
+    return u32x4_t{(uint32_t)__builtin_amdgcn_mov_dpp((int)x.x, 0x101, 0xf, 0xf, true),
+                   (uint32_t)__builtin_amdgcn_mov_dpp((int)x.y, 0x101, 0xf, 0xf, true),
+                   (uint32_t)__builtin_amdgcn_mov_dpp((int)x.z, 0x101, 0xf, 0xf, true),
+                   (uint32_t)__builtin_amdgcn_mov_dpp((int)x.w, 0x101, 0xf, 0xf, true)};
+}
 
 template <int NP2>
 struct WvWords {
@@ -272,12 +293,9 @@ __global__ __launch_bounds__(256) void conv_fused_wave_kernel(const uint16_t *__
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
 
-    // One tap's 14 MFMAs in 7 slots (block pb, both channel tiles). After
-    // slot k, the work item k of the tap runs; scheduling barriers keep that
-    // order, so the mixing chain's dependent steps sit two or more MFMA pairs
-    // apart and the matrix core never waits on them.
-    auto mfma_pb = [&](const u32x4_t (&af)[kWvNPB], const bf16x8_t (&bf)[2], int pb) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, af[pb]);
+    // Block pb of one tap: its A fragment against both channel tiles.
+    auto mfma_pb_frag = [&](const u32x4_t af, const bf16x8_t (&bf)[2], int pb) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, af);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             acc[pb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bf[n], acc[pb][n], 0, 0, 0);
@@ -306,8 +324,8 @@ __global__ __launch_bounds__(256) void conv_fused_wave_kernel(const uint16_t *__
     lds_barrier();  // stage buffer 0 complete
     bf16x8_t bcur[3][2];
     read_b(0, bcur);
-    u32x4_t acur[kWvNPB];
-    read_tap(tile(e, 0), 0, 0, acur);
+    u32x4_t acur[kWvNPB];  // centre-column fragments of the current group
+    read_tap(tile(e, 0), 0, 1, acur);
 
     for (int c = 0; c < nchunks; ++c) {
         const char *tcur = tile(e, c & 1);
@@ -335,22 +353,18 @@ __global__ __launch_bounds__(256) void conv_fused_wave_kernel(const uint16_t *__
                 for (int i = 4; i < kWvRounds; ++i) st_load(rs2, i, sr[i]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            // tap 0 (left column) with half of group g + 1's mixing
-            u32x4_t anx[kWvNPB];
-            read_tap(tcur, u, 1, anx);
-            __builtin_amdgcn_sched_barrier(0);  // reads for the next tap go out first
+            // tap 0 (left column: the centre fragments one lane down) with
+            // half of group g + 1's mixing
 #pragma unroll
-            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb(acur, bcur[0], pb);
+            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb_frag(left_neighbour(acur[pb]), bcur[0], pb);
             mix_pair(wn.w[0], nb, 0, 0);
             mix_pair(wn.w[0], nb, 0, 2);
             mix_pair(wn.w[1], nb, 1, 0);
             __builtin_amdgcn_sched_barrier(0);
             // tap 1 (centre) with the rest; then the words of group g + 2
             // load into the same registers
-            read_tap(tcur, u, 2, acur);
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb(anx, bcur[1], pb);
+            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb_frag(acur[pb], bcur[1], pb);
             mix_pair(wn.w[1], nb, 1, 2);
             mix_pair(wn.w[2], nb, 2, 0);
             mix_pair(wn.w[2], nb, 2, 2);
@@ -362,11 +376,19 @@ __global__ __launch_bounds__(256) void conv_fused_wave_kernel(const uint16_t *__
             lds_barrier();
             bf16x8_t bnext[3][2];
             read_b(nb, bnext);
-            // tap 2 (right column); the next group's first fragments load
-            read_tap(u < 2 ? tcur : tnext, u < 2 ? u + 1 : 0, 0, anx);
+            // tap 2 (right column: the centre fragments one lane up); the
+            // next group's centre fragments load
+            u32x4_t anx[kWvNPB];
+            read_tap(u < 2 ? tcur : tnext, u < 2 ? u + 1 : 0, 1, anx);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb(acur, bcur[2], pb);
+            for (int pb = 0; pb < kWvNPB; ++pb) mfma_pb_frag(right_neighbour(acur[pb]), bcur[2], pb);
+            // each block's 4 lane moves just ahead of its 2 MFMAs
+#pragma unroll
+            for (int pb = 0; pb < kWvNPB; ++pb) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int v = 0; v < 3; ++v)
