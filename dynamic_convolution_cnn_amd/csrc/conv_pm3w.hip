@@ -5,13 +5,17 @@
 // for the fused small-image kernels (the ResNet-18-shaped 56x56 layer and the
 // many-expert 28x28 layer).
 //
-// Work split. A workgroup of 4 waves (one per SIMD) owns example b, NT =
-// 32 NCB output channels and MT = 4 * 32 NPB consecutive output positions
-// (row-major); wave w owns position blocks w NPB .. w NPB + NPB - 1 (32
-// positions each) over all NT channels: NPB x NCB accumulator tiles of
+// Work split. A workgroup of 4 waves owns example b, NT = 32 NCB output
+// channels and MT = 4 * 32 NPB consecutive output positions (row-major);
+// wave w owns position blocks w NPB .. w NPB + NPB - 1 (32 positions each)
+// over all NT channels: NPB x NCB accumulator tiles of
 // v_mfma_f32_32x32x16_bf16 (positions x channels). An A fragment feeds NCB
 // MFMAs and a B fragment NPB, so a step reads (NPB + NCB) KB of LDS per
-// NPB NCB MFMAs (half of what 2x2 tiles read).
+// NPB NCB MFMAs. Launched with 2 x 2 tiles: 256 positions x 64 channels,
+// whose LDS (at most 80 KB at the 56x56 and 28x28 layers) lets two
+// workgroups share a CU, so each SIMD runs two waves and the grid covers
+// the 56x56 planes with 6 % padding instead of 14 %. Larger per-wave tiles
+// read less LDS per MFMA but leave one workgroup per CU; measured slower.
 //
 // K loop. Chunks of 16 input channels; within a chunk, 9 steps (taps), one
 // MFMA K of 16 each. Per chunk two LDS buffers are filled for the next chunk
@@ -314,7 +318,7 @@ struct Pm3wShape {
     int npb, ncb;
 };
 
-Pm3wShape pm3w_shape(const Geom &g) { return g.Cout <= 64 ? Pm3wShape{4, 2} : Pm3wShape{2, 4}; }
+Pm3wShape pm3w_shape(const Geom &) { return Pm3wShape{2, 2}; }
 
 int pm3w_tile_rows(const Geom &g, int MT) {
     int rows_out = (MT - 1) / g.Wo + 2;
@@ -377,24 +381,22 @@ hipError_t launch_conv_pm3w(const Geom &g, const uint16_t *x, const uint16_t *wt
                             const float *a_out) {
     const Pm3wShape sh = pm3w_shape(g);
     const int xr = pm3w_rounds(g);
-    if (sh.npb == 4) {
+    auto go = [&](auto npb_c, auto ncb_c) {
+        constexpr int NPB = decltype(npb_c)::value, NCB = decltype(ncb_c)::value;
         switch (xr) {
-        case 1: return launch_pm3w_t<4, 2, 1>(g, x, wt, y, stream, a_out);
-        case 2: return launch_pm3w_t<4, 2, 2>(g, x, wt, y, stream, a_out);
-        case 3: return launch_pm3w_t<4, 2, 3>(g, x, wt, y, stream, a_out);
-        case 4: return launch_pm3w_t<4, 2, 4>(g, x, wt, y, stream, a_out);
-        case 5: return launch_pm3w_t<4, 2, 5>(g, x, wt, y, stream, a_out);
-        default: return launch_pm3w_t<4, 2, 6>(g, x, wt, y, stream, a_out);
+        case 1: return launch_pm3w_t<NPB, NCB, 1>(g, x, wt, y, stream, a_out);
+        case 2: return launch_pm3w_t<NPB, NCB, 2>(g, x, wt, y, stream, a_out);
+        case 3: return launch_pm3w_t<NPB, NCB, 3>(g, x, wt, y, stream, a_out);
+        case 4: return launch_pm3w_t<NPB, NCB, 4>(g, x, wt, y, stream, a_out);
+        case 5: return launch_pm3w_t<NPB, NCB, 5>(g, x, wt, y, stream, a_out);
+        default: return launch_pm3w_t<NPB, NCB, 6>(g, x, wt, y, stream, a_out);
         }
-    }
-    switch (xr) {
-    case 1: return launch_pm3w_t<2, 4, 1>(g, x, wt, y, stream, a_out);
-    case 2: return launch_pm3w_t<2, 4, 2>(g, x, wt, y, stream, a_out);
-    case 3: return launch_pm3w_t<2, 4, 3>(g, x, wt, y, stream, a_out);
-    case 4: return launch_pm3w_t<2, 4, 4>(g, x, wt, y, stream, a_out);
-    case 5: return launch_pm3w_t<2, 4, 5>(g, x, wt, y, stream, a_out);
-    default: return launch_pm3w_t<2, 4, 6>(g, x, wt, y, stream, a_out);
-    }
+    };
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    if (sh.npb == 4) return go(I4{}, I2{});
+    if (sh.ncb == 4) return go(I2{}, I4{});
+    return go(I2{}, I2{});
 }
 
 }  // namespace dynconv
