@@ -290,9 +290,11 @@ __global__ __launch_bounds__(256) void premix_kernel(const float *__restrict__ a
 // a float32 significand), so the three exact products summed in fp32 match a
 // float32 mix before its one bf16 rounding. With the weights as the result's
 // rows, a lane holds 4 consecutive weights of one example's W_b row.
-// Workgroup (t, c) takes weight tile t and the 32 examples of chunk c; the
-// 32 x kMixMW results go through LDS as bf16 rows and leave as 16-byte
-// stores along each W_b row.
+// Workgroup (i, c) takes the 32 examples of chunk c and weight tiles
+// i, i + gridDim.x, ... in turn (about two each): the 32 x kMixMW results of
+// a tile go through LDS as bf16 rows and leave as 16-byte stores along each
+// W_b row while the next tile's expert slice is in flight, so the bank's
+// reads overlap the (four times larger) W_b writes.
 constexpr int kMixMW = 256;       // weights per workgroup (4 waves x 64)
 typedef short s16x4_lds_t __attribute__((ext_vector_type(4)));
 constexpr int kMixMfmaMaxG = 4;   // expert groups of 16: n <= 64
@@ -302,119 +304,121 @@ constexpr int kMixEx = 32;                // examples per workgroup
 template <int NKG>
 __global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__ alpha,
                                                        const uint16_t *__restrict__ experts,
-                                                       uint16_t *__restrict__ mixed, int B, int n, long wsize) {
+                                                       uint16_t *__restrict__ mixed, int B, int n, long wsize,
+                                                       int ntiles) {
     __shared__ __attribute__((aligned(16))) uint16_t s_e[NKG * 16][kMixMW];
     __shared__ __attribute__((aligned(16))) uint16_t s_o[kMixEx][kMixOutPitch];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
-    const long w0 = (long)blockIdx.x * kMixMW;
     const int bc0 = blockIdx.y * kMixEx;
-    // the attentions of this lane's A-fragment row (example bc0 + l32,
-    // experts 16 g + 8 lh + (0..7)) load first, so that their latency
-    // overlaps with that of the expert slice
-    float av[NKG][8];
-    {
-        const float *ab = alpha + (long)min(bc0 + l32, B - 1) * n;
-#pragma unroll
-        for (int g = 0; g < NKG; ++g)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) av[g][q] = ab[min(16 * g + 8 * lh + q, n - 1)];
-    }
-    // stage: clamped unconditional loads first, then masked LDS stores
+    // Expert slice of weight tile t: clamped unconditional loads (the
+    // masking happens at the LDS store).
     constexpr int kRowVec = kMixMW / 8;            // 16-byte vectors per row
     constexpr int kIt = NKG * 16 * kRowVec / 256;  // expert vectors per thread
+    auto load_tile = [&](int t, u32x4_t (&q)[kIt]) {
+        const long w0 = (long)t * kMixMW;
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int v = tid + 256 * it;
+            const int k = v / kRowVec, c = v - k * kRowVec;
+            const long w = min(w0 + 8 * c, wsize - 8);
+            q[it] = *reinterpret_cast<const u32x4_t *>(experts + (long)min(k, n - 1) * wsize + w);
+        }
+    };
+    // the first tile's slice loads first, so that its latency overlaps the
+    // attention split below
     u32x4_t q[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-        const int v = tid + 256 * it;
-        const int k = v / kRowVec, c = v - k * kRowVec;
-        const long w = min(w0 + 8 * c, wsize - 8);
-        q[it] = *reinterpret_cast<const u32x4_t *>(experts + (long)min(k, n - 1) * wsize + w);
-    }
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-        const int v = tid + 256 * it;
-        const int k = v / kRowVec, c = v - k * kRowVec;
-        const bool in = k < n && w0 + 8 * c < wsize;
-        *reinterpret_cast<u32x4_t *>(&s_e[k][8 * c]) = in ? q[it] : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-    // expert operands (A: rows = weights): experts 16 g + 8 lh + (0..7), weight 64 wave + 32 nt + l32
-    // Each half of an operand is one LDS transpose read (ds_read_b64_tr_b16):
-    // within a group of 16 lanes, lane i receives element i & 3 of the 8 bytes
-    // that lanes 4 j + (i >> 2) (j = 0..3) address, as its element j. Lane
-    // s = 4 j + r of the group addresses expert row k0 + 4 h + j at weights
-    // wg + 4 r .. wg + 4 r + 3, so lane i gets experts k0 + 4 h + (0..3) of
-    // weight wg + i.
-    bf16x8_t ef[2][NKG];
+    load_tile(blockIdx.x, q);
+    // attention operands (B: columns = examples): example bc0 + l32, experts
+    // 16 g + 8 lh + (0..7), three parts; the same for every tile
+    bf16x8_t ap[3][NKG];
     {
-        const int si = lane & 15;
+        const int b = bc0 + l32;
+        const float *ab = alpha + (long)min(b, B - 1) * n;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int g = 0; g < NKG; ++g) {
+            uint32_t pw[3][4];
 #pragma unroll
-            for (int g = 0; g < NKG; ++g) {
-                const int wg = 64 * wave + 32 * nt + 16 * ((lane >> 4) & 1);
-                const int k0 = 16 * g + 8 * lh;
-                s16x4_lds_t h[2];
+            for (int jj = 0; jj < 4; ++jj) {
+                uint16_t p2[3][2];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4_lds_t *)(&s_e[k0 + 4 * hh + (si >> 2)][wg + 4 * (si & 3)]));
-                const u32x2_t lo = __builtin_bit_cast(u32x2_t, h[0]), hi = __builtin_bit_cast(u32x2_t, h[1]);
-                ef[nt][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-            }
-    }
-    {
-        // attention operands (B: columns = examples): example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
-        bf16x8_t ap[3][1][NKG];
+                for (int e = 0; e < 2; ++e) {
+                    const int k = 16 * g + 8 * lh + 2 * jj + e;
+                    const float a = ab[min(k, n - 1)];
+                    float r = (k < n && b < B) ? a : 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 1; ++mt) {
-            const int b = bc0 + 32 * mt + l32;
-#pragma unroll
-            for (int g = 0; g < NKG; ++g) {
-                uint32_t pw[3][4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    uint16_t p2[3][2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int k = 16 * g + 8 * lh + 2 * jj + e;
-                        float r = (k < n && b < B) ? av[g][2 * jj + e] : 0.f;
-#pragma unroll
-                        for (int part = 0; part < 3; ++part) {
-                            p2[part][e] = f32_to_bf16(r);
-                            r -= bf16_to_f32(p2[part][e]);  // exact
-                        }
+                    for (int part = 0; part < 3; ++part) {
+                        p2[part][e] = f32_to_bf16(r);
+                        r -= bf16_to_f32(p2[part][e]);  // exact
                     }
-#pragma unroll
-                    for (int part = 0; part < 3; ++part)
-                        pw[part][jj] = (uint32_t)p2[part][0] | ((uint32_t)p2[part][1] << 16);
                 }
 #pragma unroll
                 for (int part = 0; part < 3; ++part)
-                    ap[part][mt][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[part][0], pw[part][1], pw[part][2], pw[part][3]});
+                    pw[part][jj] = (uint32_t)p2[part][0] | ((uint32_t)p2[part][1] << 16);
             }
+#pragma unroll
+            for (int part = 0; part < 3; ++part)
+                ap[part][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[part][0], pw[part][1], pw[part][2], pw[part][3]});
+        }
+    }
+    // one tile from the register set qc, the next tile loading into qn
+    auto tile_body = [&](int t, const u32x4_t (&qc)[kIt], u32x4_t (&qn)[kIt]) {
+        const long w0 = (long)t * kMixMW;
+        // stage (masked); the previous tile's operand reads and output
+        // copies finished before its second barrier
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int v = tid + 256 * it;
+            const int k = v / kRowVec, c = v - k * kRowVec;
+            const bool in = k < n && w0 + 8 * c < wsize;
+            *reinterpret_cast<u32x4_t *>(&s_e[k][8 * c]) = in ? qc[it] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        lds_barrier();
+        // the next tile's slice loads during this tile's products and stores
+        load_tile(min(t + (int)gridDim.x, ntiles - 1), qn);
+        // expert operands (A: rows = weights): experts 16 g + 8 lh + (0..7), weight 64 wave + 32 nt + l32
+        // Each half of an operand is one LDS transpose read (ds_read_b64_tr_b16):
+        // within a group of 16 lanes, lane i receives element i & 3 of the 8 bytes
+        // that lanes 4 j + (i >> 2) (j = 0..3) address, as its element j. Lane
+        // s = 4 j + r of the group addresses expert row k0 + 4 h + j at weights
+        // wg + 4 r .. wg + 4 r + 3, so lane i gets experts k0 + 4 h + (0..3) of
+        // weight wg + i.
+        bf16x8_t ef[2][NKG];
+        {
+            const int si = lane & 15;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int g = 0; g < NKG; ++g) {
+                    const int wg = 64 * wave + 32 * nt + 16 * ((lane >> 4) & 1);
+                    const int k0 = 16 * g + 8 * lh;
+                    s16x4_lds_t h[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4_lds_t *)(&s_e[k0 + 4 * hh + (si >> 2)][wg + 4 * (si & 3)]));
+                    const u32x2_t lo = __builtin_bit_cast(u32x2_t, h[0]), hi = __builtin_bit_cast(u32x2_t, h[1]);
+                    ef[nt][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+                }
         }
 #pragma unroll
-        for (int mt = 0; mt < 1; ++mt)
+        for (int nt = 0; nt < 2; ++nt) {
+            f32x16_t acc;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x16_t acc;
+            for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+            for (int g = 0; g < NKG; ++g)
 #pragma unroll
-                for (int g = 0; g < NKG; ++g)
+                for (int part = 2; part >= 0; --part)  // small parts first
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[nt][g], ap[part][g], acc, 0, 0, 0);
+            // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
+            // example l32, so a lane's 4 registers of group j are 4
+            // consecutive weights of one W_b row (one 8-byte LDS write)
 #pragma unroll
-                    for (int part = 2; part >= 0; --part)  // small parts first
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[nt][g], ap[part][mt][g], acc, 0, 0, 0);
-                // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
-                // example 32 mt + l32, so a lane's 4 registers of group j are
-                // 4 consecutive weights of one W_b row (one 8-byte LDS write)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<u32x2_t *>(&s_o[32 * mt + l32][64 * wave + 32 * nt + 8 * j + 4 * lh]) =
-                        u32x2_t{pack_bf16x2(acc[4 * j], acc[4 * j + 1]), pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3])};
-            }
-        __syncthreads();
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2_t *>(&s_o[l32][64 * wave + 32 * nt + 8 * j + 4 * lh]) =
+                    u32x2_t{pack_bf16x2(acc[4 * j], acc[4 * j + 1]), pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3])};
+        }
+        lds_barrier();
         // rows out: kMixEx examples x kRowVec vectors
 #pragma unroll
         for (int it = 0; it < kMixEx * kRowVec / 256; ++it) {
@@ -426,37 +430,48 @@ __global__ __launch_bounds__(256) void mix_mfma_kernel(const float *__restrict__
                 *reinterpret_cast<u32x4_t *>(mixed + (long)b * wsize + w) =
                     *reinterpret_cast<const u32x4_t *>(&s_o[r][8 * c]);
         }
+    };
+    // two register sets in turn, so that each waits for its loads only where
+    // it is stored
+    u32x4_t q1[kIt];
+    for (int t = blockIdx.x; t < ntiles; t += 2 * gridDim.x) {
+        tile_body(t, q, q1);
+        if (t + (int)gridDim.x < ntiles) tile_body(t + gridDim.x, q1, q);
     }
 }
 
 // Premix on the matrix cores for banks whose padded expert count is a
-// multiple of 8: as mix_mfma_kernel, but the experts of each weight come
-// straight from the packed bank (8 consecutive experts = 16 bytes of a
-// weight's record, no LDS transpose) and the mixed kernels are written in
-// the convolution's layout wt[b][t][o][cp], which has the packed bank's
-// weight order.
+// multiple of 8: as mix_mfma_kernel (persistent over weight tiles, the next
+// tile's expert records in flight during the current tile's stores), but the
+// experts of each weight come straight from the packed bank (8 consecutive
+// experts = 16 bytes of a weight's record, no LDS transpose) and the mixed
+// kernels are written in the convolution's layout wt[b][t][o][cp], which has
+// the packed bank's weight order.
 template <int NKG>
 __global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restrict__ alpha,
                                                           const uint16_t *__restrict__ packed,
                                                           uint16_t *__restrict__ wt, int B, int n, int n_pad,
                                                           long wsize, const float *__restrict__ a_in, int Cin,
-                                                          int Cin_pad) {
+                                                          int Cin_pad, int ntiles) {
     __shared__ __attribute__((aligned(16))) uint16_t s_o[kMixEx][kMixOutPitch];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
-    const long w0 = (long)blockIdx.x * kMixMW;
     const int bc0 = blockIdx.y * kMixEx;
-    // expert operands (A: rows = weights): experts 16 g + 8 lh + (0..7) of weight w0 + 64 wave + 32 nt + l32
-    bf16x8_t ef[2][NKG];
+    // expert operands of weight tile t (A: rows = weights): experts
+    // 16 g + 8 lh + (0..7) of weight 256 t + 64 wave + 32 nt + l32
+    // (raw records; experts past n_pad are masked where the operands are used,
+    // so that a wave waits for these loads only there)
+    auto load_tile = [&](int t, u32x4_t (&ef)[2][NKG]) {
+        const long w0 = (long)t * kMixMW;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const long w = min(w0 + 64 * wave + 32 * nt + l32, wsize - 1);
+        for (int nt = 0; nt < 2; ++nt) {
+            const long w = min(w0 + 64 * wave + 32 * nt + l32, wsize - 1);
 #pragma unroll
-        for (int g = 0; g < NKG; ++g) {
-            const int k0 = 16 * g + 8 * lh;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(packed + w * n_pad + min(k0, n_pad - 8));
-            ef[nt][g] = __builtin_bit_cast(bf16x8_t, k0 < n_pad ? v : u32x4_t{0u, 0u, 0u, 0u});
+            for (int g = 0; g < NKG; ++g)
+                ef[nt][g] = *reinterpret_cast<const u32x4_t *>(packed + w * n_pad + min(16 * g + 8 * lh, n_pad - 8));
         }
-    }
+    };
+    u32x4_t ef[2][NKG];
+    load_tile(blockIdx.x, ef);
     // attention operands (B: columns = examples): example bc0 + l32, experts 16 g + 8 lh + (0..7), three parts
     bf16x8_t ap[3][NKG];
     {
@@ -488,42 +503,71 @@ __global__ __launch_bounds__(256) void premix_mfma_kernel(const float *__restric
                 ap[part][g] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[part][0], pw[part][1], pw[part][2], pw[part][3]});
         }
     }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        f32x16_t acc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-        for (int g = 0; g < NKG; ++g)
-#pragma unroll
-            for (int part = 2; part >= 0; --part)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[nt][g], ap[part][g], acc, 0, 0, 0);
-        // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
-        // example l32 (one 8-byte LDS write per group j)
-        if (a_in) {
-            // input attention: weight w's input channel is w % Cin_pad (a
-            // 32-aligned weight block holds 32 consecutive channels)
-            const int cb = (int)((w0 + 64 * wave + 32 * nt) % Cin_pad);
-            const float *ai = a_in + (long)min(bc0 + l32, B - 1) * Cin;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] *= ai[min(cb + 8 * (i >> 2) + 4 * lh + (i & 3), Cin - 1)];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x2_t *>(&s_o[l32][64 * wave + 32 * nt + 8 * j + 4 * lh]) =
-                u32x2_t{pack_bf16x2(acc[4 * j], acc[4 * j + 1]), pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3])};
-    }
-    __syncthreads();
     constexpr int kRowVec = kMixMW / 8;
+    // one tile from the operands efc, the next tile loading into efn
+    auto tile_body = [&](int t, const u32x4_t (&efc)[2][NKG], u32x4_t (&efn)[2][NKG]) {
+        const long w0 = (long)t * kMixMW;
+        f32x16_t acc[2];
 #pragma unroll
-    for (int it = 0; it < kMixEx * kRowVec / 256; ++it) {
-        const int v = tid + 256 * it;
-        const int r = v / kRowVec, c = v - r * kRowVec;
-        const int b = bc0 + r;
-        const long w = w0 + 8 * c;
-        if (b < B && w < wsize)
-            *reinterpret_cast<u32x4_t *>(wt + (long)b * wsize + w) = *reinterpret_cast<const u32x4_t *>(&s_o[r][8 * c]);
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[nt][i] = 0.f;
+#pragma unroll
+            for (int g = 0; g < NKG; ++g)
+#pragma unroll
+                for (int part = 2; part >= 0; --part)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, 16 * g + 8 * lh < n_pad ? efc[nt][g] : u32x4_t{0u, 0u, 0u, 0u}),
+                        ap[part][g], acc[nt], 0, 0, 0);
+        }
+        // the next tile's expert records load during this tile's stores
+        load_tile(min(t + (int)gridDim.x, ntiles - 1), efn);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
+            // example l32 (one 8-byte LDS write per group j)
+            if (a_in) {
+                // input attention: weight w's input channel is w % Cin_pad (a
+                // 32-aligned weight block holds 32 consecutive channels)
+                const int cb = (int)((w0 + 64 * wave + 32 * nt) % Cin_pad);
+                const float *ai = a_in + (long)min(bc0 + l32, B - 1) * Cin;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[nt][i] *= ai[min(cb + 8 * (i >> 2) + 4 * lh + (i & 3), Cin - 1)];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2_t *>(&s_o[l32][64 * wave + 32 * nt + 8 * j + 4 * lh]) =
+                    u32x2_t{pack_bf16x2(acc[nt][4 * j], acc[nt][4 * j + 1]),
+                            pack_bf16x2(acc[nt][4 * j + 2], acc[nt][4 * j + 3])};
+        }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < kMixEx * kRowVec / 256; ++it) {
+            const int v = tid + 256 * it;
+            const int r = v / kRowVec, c = v - r * kRowVec;
+            const int b = bc0 + r;
+            const long w = w0 + 8 * c;
+            if (b < B && w < wsize)
+                *reinterpret_cast<u32x4_t *>(wt + (long)b * wsize + w) = *reinterpret_cast<const u32x4_t *>(&s_o[r][8 * c]);
+        }
+        // the copies read s_o before the next tile writes it
+        lds_barrier();
+    };
+    u32x4_t ef1[2][NKG];
+    for (int t = blockIdx.x; t < ntiles; t += 2 * gridDim.x) {
+        tile_body(t, ef, ef1);
+        if (t + (int)gridDim.x < ntiles) tile_body(t + gridDim.x, ef1, ef);
     }
+}
+
+// Workgroups per example chunk for the persistent matrix-core mixes: about
+// kMixWorkers in all (two or three per CU), each taking the same number of
+// weight tiles.
+constexpr int kMixWorkers = 640;
+int mix_workers(int ntiles, int B) {
+    const long chunks = (B + kMixEx - 1) / kMixEx;
+    const long per = std::max(1L, ((long)ntiles * chunks + kMixWorkers - 1) / kMixWorkers);
+    return (int)((ntiles + per - 1) / per);
 }
 
 }  // namespace
@@ -553,11 +597,12 @@ hipError_t launch_mix_natural(const Geom &g, long wsize, const float *alpha, con
                                                                       static_cast<const uint16_t *>(experts),
                                                                       static_cast<uint16_t *>(mixed), stream);
         if (g.bf16 && g.n <= 16 * kMixMfmaMaxG) {
-            const dim3 mgrid((unsigned)((wsize + kMixMW - 1) / kMixMW), (unsigned)((g.B + kMixEx - 1) / kMixEx));
+            const int ntiles = (int)((wsize + kMixMW - 1) / kMixMW);
+            const dim3 mgrid((unsigned)mix_workers(ntiles, g.B), (unsigned)((g.B + kMixEx - 1) / kMixEx));
             auto go = [&](auto kern) {
                 hipLaunchKernelGGL(kern, mgrid, dim3(256), 0, stream, alpha,
                                    static_cast<const uint16_t *>(experts), static_cast<uint16_t *>(mixed), g.B,
-                                   g.n, wsize);
+                                   g.n, wsize, ntiles);
                 return hipGetLastError();
             };
             if (g.n <= 16) return go(mix_mfma_kernel<1>);
@@ -626,10 +671,11 @@ hipError_t launch_premix(const Geom &g, const float *alpha, const uint16_t *pack
     // matrix-core premix when the padded expert records are 16-byte multiples
     if (g.n_pad % 8 == 0 && g.n_pad <= 16 * kMixMfmaMaxG) {
         const long wsize = nvec * 8;
-        const dim3 mgrid((unsigned)((wsize + kMixMW - 1) / kMixMW), (unsigned)((g.B + kMixEx - 1) / kMixEx));
+        const int ntiles = (int)((wsize + kMixMW - 1) / kMixMW);
+        const dim3 mgrid((unsigned)mix_workers(ntiles, g.B), (unsigned)((g.B + kMixEx - 1) / kMixEx));
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, mgrid, dim3(256), 0, stream, alpha, packed, wt, g.B, g.n, g.n_pad, wsize,
-                               att.in, g.Cin, g.Cin_pad);
+                               att.in, g.Cin, g.Cin_pad, ntiles);
             return hipGetLastError();
         };
         const int nkg = (g.n_pad + 15) / 16;
