@@ -246,16 +246,23 @@ dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const 
 // The input gradient of a stride-1 layer is the forward layer applied to
 // dy with the transposed, flipped bank and padding k - 1 - p: `t` is that
 // layer's descriptor (input dy [B,Cout,Ho,Wo], output dx [B,Cin,H,W]).
+// The data gradient runs as the forward layer on the transposed, flipped bank
+// when that layer exists (stride 1, square kernel, padding below the kernel
+// size); otherwise W_b is mixed into the workspace and a direct transposed
+// convolution gathers each dx element.
+bool backward_data_via_forward(const dynconv::Geom &g) {
+    return g.stride == 1 && g.KH == g.KW && g.pad <= g.KH - 1;
+}
+
+size_t backward_data_direct_ws(const dynconv::Geom &g) {
+    return round_up((size_t)g.B * kernel_elems(g) * esize(g), kWsAlign);
+}
+
 dynconv_status_t backward_data_desc(const dynconv_desc_t *desc, dynconv::Geom &g, dynconv_desc_t &t) {
     dynconv_status_t s = check_desc(desc, g, true);
     if (s != DYNCONV_OK) return s;
-    if (g.stride != 1)
-        return fail(DYNCONV_ERR_UNSUPPORTED, "backward_data: only stride 1 is implemented (got %d)", g.stride);
-    if (g.KH != g.KW)
-        return fail(DYNCONV_ERR_UNSUPPORTED, "backward_data: square kernels only (got %dx%d)", g.KH, g.KW);
-    if (g.pad > g.KH - 1)
-        return fail(DYNCONV_ERR_UNSUPPORTED, "backward_data: pad %d exceeds kernel size - 1", g.pad);
     t = *desc;
+    if (!backward_data_via_forward(g)) return DYNCONV_OK;
     t.Cin = desc->Cout;
     t.Cout = desc->Cin;
     t.H = g.Ho;
@@ -569,6 +576,11 @@ size_t dynconv_backward_data_workspace_bytes(const dynconv_desc_t *desc, int32_t
     dynconv::Geom g;
     dynconv_desc_t t;
     if (backward_data_desc(desc, g, t) != DYNCONV_OK) return 0;
+    if (!backward_data_via_forward(g)) {
+        const bool known = policy == DYNCONV_POLICY_AUTO || policy == DYNCONV_POLICY_PREMIX ||
+                           policy == DYNCONV_POLICY_FUSED;
+        return known ? backward_data_direct_ws(g) : 0;
+    }
     const size_t fw = dynconv_forward_workspace_bytes(&t, policy);
     dynconv::Geom gt;
     int32_t p;
@@ -587,6 +599,19 @@ dynconv_status_t dynconv_backward_data(const dynconv_desc_t *desc, int32_t polic
         return fail(DYNCONV_ERR_INVALID_ARG, "dy, experts, alpha and dx must not be NULL");
     if (!aligned16(dy) || !aligned16(experts) || !aligned16(alpha) || !aligned16(dx))
         return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (!backward_data_via_forward(g)) {
+        if (policy != DYNCONV_POLICY_AUTO && policy != DYNCONV_POLICY_PREMIX && policy != DYNCONV_POLICY_FUSED)
+            return fail(DYNCONV_ERR_INVALID_ARG, "policy %d is not a dynconv_policy_t", policy);
+        const size_t need = backward_data_direct_ws(g);
+        if (workspace_bytes < need || !workspace || !aligned16(workspace))
+            return fail(DYNCONV_ERR_WORKSPACE, "backward_data needs %zu bytes of 16-byte aligned workspace (got %zu)",
+                        need, workspace_bytes);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        s = hip_status(dynconv::launch_mix_natural(g, kernel_elems(g), alpha, experts, workspace, st),
+                       "backward_data mix launch");
+        if (s != DYNCONV_OK) return s;
+        return hip_status(dynconv::launch_dgrad_direct(g, dy, workspace, dx, st), "backward_data launch");
+    }
     dynconv::Geom gt;
     int32_t p;
     s = check_desc(&t, gt, true);

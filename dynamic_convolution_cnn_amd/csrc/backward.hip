@@ -709,4 +709,70 @@ hipError_t launch_route_backward(const Geom &g, const void *x, const float *fc_w
     return hipGetLastError();
 }
 
+namespace {
+
+// Input gradient for the layers the forward machinery does not transpose
+// (stride above 1, kh != kw, or padding of k or more): dx[b,c,h,w] is the sum
+// of W_b[o,c',u,v] * dy[b,o,r,s] over the output positions (r, s) and taps
+// (u, v) with r * stride + u - pad = h and s * stride + v - pad = w, o over
+// the output channels of c's group (c' = c within its group). W_b is mixed
+// into the workspace first (the layer's element type, one rounding, as the
+// forward uses it); products accumulate in fp32 and dx is rounded once. One
+// thread per dx element, positions fastest, so a wave reads one W_b row per
+// (o, u, v) (a broadcast) and neighbouring dy elements.
+struct DgradArgs {
+    int B, Cin, H, W, Cout, KH, KW, stride, pad, groups, Ho, Wo;
+};
+template <typename T>
+__global__ __launch_bounds__(256) void dgrad_direct_kernel(const T *__restrict__ dy, const T *__restrict__ wb,
+                                                           T *__restrict__ dx, DgradArgs a) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const long total = (long)a.B * a.Cin * a.H * a.W;
+    if (idx >= total) return;
+    const int w = (int)(idx % a.W);
+    long t = idx / a.W;
+    const int h = (int)(t % a.H);
+    t /= a.H;
+    const int c = (int)(t % a.Cin);
+    const int b = (int)(t / a.Cin);
+    const int cpg_in = a.Cin / a.groups, cpg_out = a.Cout / a.groups;
+    const int grp = c / cpg_in, ci = c - grp * cpg_in;
+    float acc = 0.f;
+    for (int oo = 0; oo < cpg_out; ++oo) {
+        const int o = grp * cpg_out + oo;
+        const T *wp = wb + (((long)b * a.Cout + o) * cpg_in + ci) * a.KH * a.KW;
+        const T *dp = dy + ((long)b * a.Cout + o) * a.Ho * a.Wo;
+        for (int u = 0; u < a.KH; ++u) {
+            const int th = h + a.pad - u;
+            if (th < 0 || th % a.stride != 0) continue;
+            const int r = th / a.stride;
+            if (r >= a.Ho) continue;
+            for (int v = 0; v < a.KW; ++v) {
+                const int tw = w + a.pad - v;
+                if (tw < 0 || tw % a.stride != 0) continue;
+                const int s = tw / a.stride;
+                if (s >= a.Wo) continue;
+                acc = fmaf(Elem<T>::to_f32(wp[u * a.KW + v]), Elem<T>::to_f32(dp[(long)r * a.Wo + s]), acc);
+            }
+        }
+    }
+    dx[idx] = Elem<T>::from_f32(acc);
+}
+
+}  // namespace
+
+hipError_t launch_dgrad_direct(const Geom &g, const void *dy, const void *wb, void *dx, hipStream_t stream) {
+    DgradArgs a{g.B, g.Cin, g.H, g.W, g.Cout, g.KH, g.KW, g.stride, g.pad, g.groups, g.Ho, g.Wo};
+    const long total = (long)g.B * g.Cin * g.H * g.W;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (g.bf16)
+        hipLaunchKernelGGL(dgrad_direct_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint16_t *>(dy), static_cast<const uint16_t *>(wb),
+                           static_cast<uint16_t *>(dx), a);
+    else
+        hipLaunchKernelGGL(dgrad_direct_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float *>(dy),
+                           static_cast<const float *>(wb), static_cast<float *>(dx), a);
+    return hipGetLastError();
+}
+
 }  // namespace dynconv

@@ -134,6 +134,10 @@ hipError_t launch_conv_sparse(const Geom &g, const uint16_t *x, const uint16_t *
 // per g.bf16. The forward layer with this bank and padding k - 1 - p,
 // applied to dy, is the input gradient of a stride-1 layer.
 hipError_t launch_flip_experts(const Geom &g, const void *experts, void *flipped, hipStream_t stream);
+// Input gradient dx [B][Cin][H][W] from dy [B][Cout][Ho][Wo] and the mixed
+// kernels W_b [B][Cout][Cin/g][KH][KW] (element type per g.bf16), any stride,
+// padding and kernel shape; groups 1 or depthwise.
+hipError_t launch_dgrad_direct(const Geom &g, const void *dy, const void *wb, void *dx, hipStream_t stream);
 
 // Per-example kernel gradients dW_b (float32, [B][Cout][Cin/g][KH][KW]) of
 // x and dy (element type per g.bf16), then dalpha[B][n] = <dW_b, E_i> and

@@ -266,15 +266,19 @@ size_t dynconv_forward_sparse_workspace_bytes(const dynconv_desc_t *desc);
 /* Input gradient of the layer:
  *   dx[b] = the transposed convolution of dy[b] with W_b = sum_i alpha[b,i] E_i,
  * i.e. dx[b,c,h,w] = sum of W_b[o,c',u,v] * dy[b,o,r,s] over the (o, r, s,
- * u, v) whose forward output read x[b,c,h,w]. Computed as the forward layer
- * (any policy of dynconv_forward; AUTO picks as for that layer) applied to dy
- * with the bank transposed in its channels, flipped in its taps, and padding
- * k - 1 - pad. dy: [B,Cout,Ho,Wo]; experts, alpha as dynconv_forward; dx:
- * [B,Cin,H,W], written (not accumulated), in the layer's element type with
- * one rounding. Supported: stride 1, kh == kw, pad <= kh - 1, groups 1 or
- * depthwise (else DYNCONV_ERR_UNSUPPORTED). workspace: at least
- * dynconv_backward_data_workspace_bytes(desc, policy) bytes (the flipped
- * bank, then the forward's workspace); 0 if the descriptor is invalid. */
+ * u, v) whose forward output read x[b,c,h,w]. For stride 1, kh == kw and
+ * pad <= kh - 1 it is computed as the forward layer (any policy of
+ * dynconv_forward; AUTO picks as for that layer) applied to dy with the bank
+ * transposed in its channels, flipped in its taps, and padding k - 1 - pad;
+ * workspace: the flipped bank, then the forward's workspace. Any other
+ * stride, padding or kernel shape mixes W_b into the workspace (as
+ * dynconv_mix: B * Cout * (Cin/g) * kh * kw elements of the layer's type) and
+ * gathers each dx element directly; the policy is then only checked. dy:
+ * [B,Cout,Ho,Wo]; experts, alpha as dynconv_forward; dx: [B,Cin,H,W],
+ * written (not accumulated), in the layer's element type with one rounding.
+ * Groups 1 or depthwise (else DYNCONV_ERR_UNSUPPORTED). workspace: at least
+ * dynconv_backward_data_workspace_bytes(desc, policy) bytes; 0 if the
+ * descriptor is invalid. */
 dynconv_status_t dynconv_backward_data(const dynconv_desc_t *desc, int32_t policy, const void *dy,
                                        const void *experts, const float *alpha, void *dx,
                                        void *workspace, size_t workspace_bytes, void *stream);

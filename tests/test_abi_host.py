@@ -260,9 +260,17 @@ def test_backward_data_checks():
     assert bwd(dx=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
     assert bwd(wsb=bd.dynconv_backward_data_workspace_bytes(d) - 1) == bd.DYNCONV_ERR_WORKSPACE
     assert bwd(wsp=None) == bd.DYNCONV_ERR_WORKSPACE
-    for bad in (good_desc(stride=2), good_desc(kh=3, kw=1, pad=0), good_desc(kh=3, kw=3, pad=3, H=4, W=4)):
-        assert bd.dynconv_backward_data_workspace_bytes(bad) == 0
-        assert bwd(desc=bad, wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    # shapes the forward cannot transpose mix W_b into the workspace and run the direct kernel
+    for gen, taps in ((good_desc(stride=2), 9), (good_desc(kh=3, kw=1, pad=0), 3),
+                      (good_desc(kh=3, kw=3, pad=3, H=4, W=4), 9)):
+        need = (2 * 16 * 16 * taps * 2 + 255) // 256 * 256
+        for p in (bd.DYNCONV_POLICY_AUTO, bd.DYNCONV_POLICY_PREMIX, bd.DYNCONV_POLICY_FUSED):
+            assert bd.dynconv_backward_data_workspace_bytes(gen, p) == need
+        assert bd.dynconv_backward_data_workspace_bytes(gen, 7) == 0
+        assert bwd(desc=gen, wsb=need - 1) == bd.DYNCONV_ERR_WORKSPACE
+        assert bwd(desc=gen, wsp=None, wsb=need) == bd.DYNCONV_ERR_WORKSPACE
+        assert bwd(desc=gen, policy=7, wsb=need) == bd.DYNCONV_ERR_INVALID_ARG
+        assert bwd(desc=gen, dy=None, wsb=need) == bd.DYNCONV_ERR_INVALID_ARG
     assert bwd(desc=good_desc(groups=2), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
     assert bwd(policy=7, wsb=1 << 30) == bd.DYNCONV_ERR_INVALID_ARG
     # 1x1 with Cin != Cout transposes the channels: 40 -> 240 runs as 240 -> 40

@@ -61,7 +61,11 @@ BWD_CASES = [
     (2, 16, 16, 8, 8, 3, 1, 1, 1, 4, "f32"),        # the tiny float32 layer
     (2, 3, 3, 7, 7, 3, 1, 1, 1, 11, "bf16"),        # odd bank size (scalar contraction), 8 + 3 experts
     (2, 32, 160, 8, 8, 3, 1, 1, 1, 16, "bf16"),     # 16 experts, two 128-channel output tiles
-    (3, 16, 16, 11, 9, 3, 2, 1, 16, 5, "bf16"),     # depthwise 3x3, stride 2 (data gradient declines)
+    (3, 16, 16, 11, 9, 3, 2, 1, 16, 5, "bf16"),     # depthwise 3x3, stride 2 (direct data gradient)
+    (2, 16, 24, 15, 15, 3, 2, 1, 1, 2, "bf16"),     # stride 2, odd size (direct data gradient)
+    (2, 12, 20, 11, 9, 3, 2, 1, 1, 3, "f32"),       # float32 stride 2
+    (2, 8, 12, 6, 7, 3, 1, 3, 1, 4, "bf16"),        # padding 3 with a 3x3 kernel (direct data gradient)
+    (2, 10, 10, 12, 12, 5, 3, 2, 10, 4, "bf16"),    # depthwise 5x5, stride 3
     (2, 8, 8, 12, 12, 7, 1, 3, 8, 3, "bf16"),       # depthwise 7x7 (bounds-checked kernel)
     (2, 64, 64, 20, 20, 3, 1, 1, 1, 4, "bf16"),     # 3x3 kernel gradient in two row bands (12 + 8 rows)
 ]
@@ -87,17 +91,11 @@ def test_backward_matches_oracle(case):
     x, e, a, dy = _layer_inputs(case, seed=100 + Cin + Cout)
     say("backward", case)
     xd, ed, ad, dyd = to_dev(x, dtype), to_dev(e, dtype), to_dev(a, "f32"), to_dev(dy, dtype)
-    dx = None
-    if st == 1:
-        dx = bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
-    else:
-        with pytest.raises(bd.DynconvError):
-            bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
+    dx = bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
     da, de = bd.dynconv_backward_weights(xd, dyd, ed, ad, st, p, g)
     torch.cuda.synchronize()
     rx, ra, re = oracle.backward(x, e, a, dy, st, p, g)
-    if dx is not None:
-        check(from_dev(dx), rx, TOL[dtype], f"dx {case}")
+    check(from_dev(dx), rx, TOL[dtype], f"dx {case}")
     check(from_dev(da), ra, GRAD_TOL[dtype], f"dalpha {case}")
     check(from_dev(de), re, GRAD_TOL[dtype], f"dexperts {case}")
 
@@ -129,8 +127,33 @@ def test_backward_weights_stride2_and_partial_outputs():
     check(from_dev(da), ra, GRAD_TOL[dtype], "dalpha stride 2")
     check(from_dev(de), re, GRAD_TOL[dtype], "dexperts stride 2")
     assert torch.equal(da, da_only)
-    with pytest.raises(bd.DynconvError):
-        bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
+    dx = bd.dynconv_backward_data(dyd, ed, ad, H, W, st, p, g)
+    torch.cuda.synchronize()
+    rx, _, _ = oracle.backward(x, e, a, dy, st, p, g, want=("dx",))
+    check(from_dev(dx), rx, TOL[dtype], "dx stride 2")
+
+
+@pytest.mark.parametrize("shape", [
+    # B, Cin, Cout, H, W, kh, kw, stride, pad, groups, n, dtype
+    (2, 12, 16, 9, 10, 3, 1, 1, 0, 1, 4, "bf16"),     # 3x1 kernel
+    (2, 12, 16, 9, 10, 1, 5, 2, 2, 1, 3, "bf16"),     # 1x5 kernel, stride 2
+    (2, 6, 6, 7, 8, 3, 5, 2, 1, 6, 5, "f32"),         # depthwise 3x5, stride 2, float32
+])
+def test_backward_data_general_shapes(shape):
+    """Kernels that are not square (and strides above 1) take the direct data gradient."""
+    B, Cin, Cout, H, W, kh, kw, st, p, g, n, dtype = shape
+    rng = np.random.default_rng(300 + kh * 10 + kw)
+    Ho, Wo = oracle.out_size(H, kh, st, p), oracle.out_size(W, kw, st, p)
+    x = _round(rng.standard_normal((B, Cin, H, W), dtype=np.float32), dtype)
+    e = _round((rng.standard_normal((n, Cout, Cin // g, kh, kw)) * np.sqrt(2.0 / (Cin // g * kh * kw)))
+               .astype(np.float32), dtype)
+    a = (rng.random((B, n)) * 0.9 + 0.05).astype(np.float32)
+    dy = _round(rng.standard_normal((B, Cout, Ho, Wo), dtype=np.float32), dtype)
+    say("backward_data general", shape)
+    dx = bd.dynconv_backward_data(to_dev(dy, dtype), to_dev(e, dtype), to_dev(a, "f32"), H, W, st, p, g)
+    torch.cuda.synchronize()
+    rx, _, _ = oracle.backward(x, e, a, dy, st, p, g, want=("dx",))
+    check(from_dev(dx), rx, TOL[dtype], f"dx {shape}")
 
 
 def test_backward_deterministic():
