@@ -155,7 +155,14 @@ dynconv_status_t hip_status(hipError_t e, const char *what) {
     return ok();
 }
 
-bool packable(const dynconv::Geom &g) { return g.bf16 && g.groups == 1 && g.n_pad <= 16; }
+// bf16 layers with groups == 1 keep a packed bank: [t][o][c'][i'] for at most
+// 16 experts, the wide layout [i][t][o][c'] for more.
+bool packable(const dynconv::Geom &g) {
+    return g.bf16 && g.groups == 1 && (g.n_pad <= 16 || dynconv::pack_wide_supported(g));
+}
+size_t packed_bank_bytes(const dynconv::Geom &g) {
+    return wide(g) ? dynconv::wide_bank_bytes(g) : dynconv::packed_experts_bytes(g);
+}
 
 // bf16, groups == 1: the convolution from a packed bank. `ws` holds the
 // premixed kernels for the PREMIX policy.
@@ -518,7 +525,7 @@ dynconv_status_t dynconv_route_attn(const dynconv_desc_t *desc, const void *x, c
 size_t dynconv_packed_experts_bytes(const dynconv_desc_t *desc) {
     dynconv::Geom g;
     if (check_desc(desc, g, true) != DYNCONV_OK || !packable(g)) return 0;
-    return dynconv::packed_experts_bytes(g);
+    return packed_bank_bytes(g);
 }
 
 dynconv_status_t dynconv_pack_experts(const dynconv_desc_t *desc, const void *experts,
@@ -527,16 +534,22 @@ dynconv_status_t dynconv_pack_experts(const dynconv_desc_t *desc, const void *ex
     dynconv_status_t s = check_desc(desc, g, true);
     if (s != DYNCONV_OK) return s;
     if (!packable(g))
-        return fail(DYNCONV_ERR_UNSUPPORTED, "packing applies to bf16 layers with groups == 1 and n <= 16");
+        return fail(DYNCONV_ERR_UNSUPPORTED,
+                    "packing applies to bf16 layers with groups == 1 (more than 16 experts: one expert's Cin x kh x "
+                    "kw block must fit 64 KB)");
     if (!experts || !packed) return fail(DYNCONV_ERR_INVALID_ARG, "experts and packed must not be NULL");
     if (!aligned16(experts) || !aligned16(packed))
         return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    if (packed_bytes < dynconv::packed_experts_bytes(g))
+    if (packed_bytes < packed_bank_bytes(g))
         return fail(DYNCONV_ERR_INVALID_ARG, "packed holds %zu bytes, %zu needed", packed_bytes,
-                    dynconv::packed_experts_bytes(g));
+                    packed_bank_bytes(g));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (wide(g))
+        return hip_status(dynconv::launch_pack_wide(g, static_cast<const uint16_t *>(experts),
+                                                    static_cast<uint16_t *>(packed), st),
+                          "dynconv_pack_experts launch");
     return hip_status(dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts),
-                                                   static_cast<uint16_t *>(packed),
-                                                   static_cast<hipStream_t>(stream)),
+                                                   static_cast<uint16_t *>(packed), st),
                       "dynconv_pack_experts launch");
 }
 
@@ -545,7 +558,7 @@ size_t dynconv_forward_packed_workspace_bytes(const dynconv_desc_t *desc, int32_
     if (check_desc(desc, g, true) != DYNCONV_OK || !packable(g)) return 0;
     int32_t p;
     if (resolve_policy(g, policy, p) != DYNCONV_OK) return 0;
-    return p == DYNCONV_POLICY_PREMIX ? round_up(dynconv::premixed_bytes(g), kWsAlign) : 0;
+    return p == DYNCONV_POLICY_PREMIX || wide(g) ? round_up(dynconv::premixed_bytes(g), kWsAlign) : 0;
 }
 
 dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t policy,
@@ -560,16 +573,28 @@ dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t poli
     if (!aligned16(x) || !aligned16(packed) || !aligned16(alpha) || !aligned16(y))
         return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
     if (!packable(g))
-        return fail(DYNCONV_ERR_UNSUPPORTED, "packed experts apply to bf16 layers with groups == 1 and n <= 16");
+        return fail(DYNCONV_ERR_UNSUPPORTED, "packed experts apply to bf16 layers with groups == 1");
     int32_t p;
     s = resolve_policy(g, policy, p);
     if (s != DYNCONV_OK) return s;
-    const size_t need = p == DYNCONV_POLICY_PREMIX ? round_up(dynconv::premixed_bytes(g), kWsAlign) : 0;
+    const size_t need =
+        p == DYNCONV_POLICY_PREMIX || wide(g) ? round_up(dynconv::premixed_bytes(g), kWsAlign) : 0;
     if (need > 0 && (workspace_bytes < need || !workspace || !aligned16(workspace)))
         return fail(DYNCONV_ERR_WORKSPACE, "forward_packed needs %zu bytes of 16-byte aligned workspace (got %zu)",
                     need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (wide(g)) {
+        // many experts: W_b from the wide bank on the matrix cores, then the premix convolution
+        uint16_t *wt = static_cast<uint16_t *>(workspace);
+        hipError_t e = dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha,
+                                                static_cast<const uint16_t *>(packed), wt, st);
+        if (e != hipSuccess) return hip_status(e, "dynconv_forward_packed wide mix launch");
+        return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
+                                                      static_cast<uint16_t *>(y), st),
+                          "dynconv_forward_packed convolution launch");
+    }
     return forward_from_packed(g, p, x, static_cast<const uint16_t *>(packed), alpha, y,
-                               static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+                               static_cast<char *>(workspace), st);
 }
 
 size_t dynconv_backward_data_workspace_bytes(const dynconv_desc_t *desc, int32_t policy) {

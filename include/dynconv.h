@@ -144,11 +144,15 @@ dynconv_status_t dynconv_forward(const dynconv_desc_t *desc, int32_t policy,
                                  size_t workspace_bytes, void *stream);
 size_t dynconv_forward_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
 
-/* Expert bank in the layout the bf16 MFMA convolution reads (bf16 layers with
- * groups == 1 and at most 16 experts only): packed[t][o][c'][i'] with t = kh*kw tap (row-major),
- * o = output channel, c' < Cin rounded up to 32 (zero beyond Cin), and
- * i' < n rounded up to even (zero beyond n), so that two experts' values of
- * one kernel element share a 32-bit word. A pure layout transform of the
+/* Expert bank in the layout the bf16 MFMA path reads (bf16 layers with
+ * groups == 1): for at most 16 experts packed[t][o][c'][i'] with t = kh*kw
+ * tap (row-major), o = output channel, c' < Cin rounded up to 32 (zero beyond
+ * Cin), and i' < n rounded up to even (zero beyond n), so that two experts'
+ * values of one kernel element share a 32-bit word; for more experts (the
+ * many-expert layers of KernelWarehouse: Rethinking the Design of Dynamic
+ * Convolution, abstract) packed[i][t][o][c'], the weight order the matrix-core
+ * mix over the expert dimension reads (one expert's Cin x kh x kw block must
+ * fit 64 KB, else DYNCONV_ERR_UNSUPPORTED). A pure layout transform of the
  * static experts: a bank can be packed once and then reused by
  * dynconv_forward_packed for every batch. dynconv_forward packs internally on
  * every call. experts [n,Cout,Cin,kh,kw] bf16; packed: device memory of at
@@ -161,8 +165,8 @@ dynconv_status_t dynconv_pack_experts(const dynconv_desc_t *desc, const void *ex
 /* dynconv_forward with an expert bank already packed by dynconv_pack_experts
  * (bf16, groups == 1). Same arguments, policies and results as
  * dynconv_forward; the workspace holds only what the policy needs besides
- * the packed bank (the premixed kernels for DYNCONV_POLICY_PREMIX, nothing
- * for DYNCONV_POLICY_FUSED). */
+ * the packed bank (the premixed kernels for DYNCONV_POLICY_PREMIX and for
+ * banks of more than 16 experts, nothing for DYNCONV_POLICY_FUSED). */
 dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t policy,
                                         const void *x, const void *packed,
                                         const float *alpha, void *y, void *workspace,

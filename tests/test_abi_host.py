@@ -346,8 +346,22 @@ def test_many_expert_forward_checks():
     assert bd.dynconv_forward_attn_workspace_bytes(d) == 0
     assert L.dynconv_forward_attn(ctypes.byref(d), bd.DYNCONV_POLICY_AUTO, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                   1 << 30, None) == bd.DYNCONV_ERR_UNSUPPORTED
-    # the packed-bank entry points keep n <= 16
-    assert bd.dynconv_packed_experts_bytes(d) == 0
+    # the packed-bank entry points keep the bank in that order once: [n][t][o][c'] bf16
+    bank = 128 * 9 * 72 * cin_pad * 2
+    assert bd.dynconv_packed_experts_bytes(d) == bank
+    assert L.dynconv_pack_experts(ctypes.byref(d), FAKE, FAKE, bank - 1, None) == bd.DYNCONV_ERR_INVALID_ARG
+    # the packed forward needs only W_b in its workspace, under AUTO and PREMIX
+    for pol in (bd.DYNCONV_POLICY_AUTO, bd.DYNCONV_POLICY_PREMIX):
+        assert bd.dynconv_forward_packed_workspace_bytes(d, pol) == r256(2 * 9 * 72 * cin_pad * 2)
+    assert bd.dynconv_forward_packed_workspace_bytes(d, bd.DYNCONV_POLICY_FUSED) == 0
+    fp = L.dynconv_forward_packed
+    assert fp(ctypes.byref(d), bd.DYNCONV_POLICY_AUTO, FAKE, FAKE, FAKE, FAKE, FAKE, r256(2 * 9 * 72 * cin_pad * 2) - 1,
+              None) == bd.DYNCONV_ERR_WORKSPACE
+    assert fp(ctypes.byref(d), bd.DYNCONV_POLICY_FUSED, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+              None) == bd.DYNCONV_ERR_UNSUPPORTED
+    # an expert block past 64 KB cannot be packed
+    big = good_desc(Cin=4000, Cout=8, n=20)
+    assert bd.dynconv_packed_experts_bytes(big) == 0
 
 
 

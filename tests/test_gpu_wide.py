@@ -71,6 +71,29 @@ def test_forward_many_experts(case):
                            policy=bd.DYNCONV_POLICY_FUSED)
 
 
+@pytest.mark.parametrize("case", WIDE_FWD[:3])
+def test_forward_packed_many_experts(case):
+    """A bank of more than 16 experts packed once ([n][t][o][c']) and reused: the same result, bit for bit, as
+    dynconv_forward, which packs on every call."""
+    B, Cin, Cout, H, W, k, p, n = case
+    rng = np.random.default_rng(90 + n)
+    x = inputs.bf16_round(rng.standard_normal((B, Cin, H, W), dtype=np.float32))
+    e = inputs.bf16_round((rng.standard_normal((n, Cout, Cin, k, k)) * np.sqrt(2.0 / (Cin * k * k)))
+                          .astype(np.float32))
+    a = (rng.random((B, n)) / n * 4).astype(np.float32)
+    desc = bd.make_desc(B, Cin, H, W, Cout, k, k, 1, p, 1, n, bd.DYNCONV_BF16)
+    say("forward packed wide", case)
+    xd, ed, ad = to_dev(x, "bf16"), to_dev(e, "bf16"), to_dev(a, "f32")
+    pk = torch.empty(bd.dynconv_packed_experts_bytes(desc), dtype=torch.uint8, device=xd.device)
+    bd.dynconv_pack_experts(desc, ed, pk)
+    y1 = bd.dynconv_forward_packed(desc, xd, pk, ad)
+    y2 = bd.dynconv_forward_packed(desc, xd, pk, ad)   # the bank is reused, not consumed
+    y0 = bd.dynconv_forward(xd, ed, ad, 1, p, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0) and torch.equal(y2, y0)
+    check(from_dev(y1), oracle.forward(x, e, a, 1, p, 1), TOL["bf16"], f"forward packed n={n} {case}")
+
+
 def test_route_and_layer_at_kernelwarehouse_scale():
     """The n = 128 workload's routing (softmax(z/4)) and layer, on sampled examples."""
     w = inputs.WORKLOADS["kernelwarehouse_n128"]
