@@ -51,8 +51,8 @@ GRAPH_STEPS = 10                # steps per HIP graph replay in the timed loop
 # for the kernel source it was taken on (sha256 prefix over the files the dominant kernel
 # is compiled from, listed below); otherwise null.
 TRAFFIC = {
-    "resnet50_3x3": {"source_sha": "ea064e70743521a7",
-                     "fetch_kib": 32314.7, "write_kib": 25088.0,
+    "resnet50_3x3": {"source_sha": "79207e4add6e4901",
+                     "fetch_kib": 32312.8, "write_kib": 25088.0,
                      "fetch_scale": 262144 / 131085.4, "write_scale": 1.0},
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "dynamic_convolution_cnn_amd", "csrc", f)

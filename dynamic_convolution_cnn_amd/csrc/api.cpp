@@ -171,7 +171,7 @@ dynconv_status_t forward_from_packed(const dynconv::Geom &g, int32_t p, const vo
                                      char *ws, hipStream_t st, dynconv::ChanAttn att = {}) {
     if (p == DYNCONV_POLICY_FUSED)
         return hip_status(dynconv::launch_conv_fused(g, static_cast<const uint16_t *>(x), packed,
-                                                     alpha, static_cast<uint16_t *>(y), st),
+                                                     alpha, static_cast<uint16_t *>(y), st, att),
                           "fused convolution launch");
     uint16_t *wt = reinterpret_cast<uint16_t *>(ws);
     hipError_t e = dynconv::launch_premix(g, alpha, packed, wt, st, att);
@@ -181,9 +181,22 @@ dynconv_status_t forward_from_packed(const dynconv::Geom &g, int32_t p, const vo
                       "convolution launch");
 }
 
-// The forward of dynconv_forward and dynconv_forward_attn. With channel
-// attentions the fused policy is not available (AUTO resolves to PREMIX for
-// groups == 1 layers).
+// Policy of a bf16 groups == 1 layer with channel attentions: the fused path
+// where the small-image 3x3 kernel takes them, else PREMIX (AUTO resolves as
+// for the plain layer, then falls back to PREMIX).
+dynconv_status_t resolve_attn_policy(const dynconv::Geom &g, int32_t policy, int32_t &out) {
+    if (policy == DYNCONV_POLICY_FUSED && !dynconv::fused_wave_attn_ok(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED,
+                    "channel attentions on the fused path need the 3x3 pad-1 small-image kernel (n <= 4, up to "
+                    "14x14, Cin <= 768)");
+    dynconv_status_t s = resolve_policy(g, policy, out);
+    if (s != DYNCONV_OK) return s;
+    if (out == DYNCONV_POLICY_FUSED && !dynconv::fused_wave_attn_ok(g))
+        return resolve_policy(g, DYNCONV_POLICY_PREMIX, out);
+    return DYNCONV_OK;
+}
+
+// The forward of dynconv_forward and dynconv_forward_attn.
 dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const void *x,
                               const void *experts, const float *alpha, void *y, void *workspace,
                               size_t workspace_bytes, void *stream, dynconv::ChanAttn att) {
@@ -200,9 +213,7 @@ dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const 
         return fail(DYNCONV_ERR_UNSUPPORTED, "channel attentions support n <= 16 experts on bf16 groups == 1 layers");
     int32_t p;
     if (attn && !depthwise(g) && g.bf16) {
-        if (policy == DYNCONV_POLICY_FUSED)
-            return fail(DYNCONV_ERR_UNSUPPORTED, "channel attentions run on the PREMIX policy (groups == 1)");
-        s = resolve_policy(g, DYNCONV_POLICY_PREMIX, p);
+        s = resolve_attn_policy(g, policy, p);
     } else {
         s = resolve_policy(g, policy, p);
     }
@@ -464,10 +475,12 @@ size_t dynconv_forward_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t 
     dynconv::Geom g;
     if (check_desc(desc, g, true) != DYNCONV_OK) return 0;
     int32_t p;
-    const int32_t want = (!depthwise(g) && g.bf16) ? DYNCONV_POLICY_PREMIX : policy;
-    if (policy == DYNCONV_POLICY_FUSED && !depthwise(g) && g.bf16) return 0;
     if (wide(g)) return 0;  // channel attentions: n <= 16 on bf16 groups == 1 layers
-    if (resolve_policy(g, want, p) != DYNCONV_OK) return 0;
+    if (!depthwise(g) && g.bf16) {
+        if (resolve_attn_policy(g, policy, p) != DYNCONV_OK) return 0;
+    } else if (resolve_policy(g, policy, p) != DYNCONV_OK) {
+        return 0;
+    }
     return forward_ws(g, p);
 }
 

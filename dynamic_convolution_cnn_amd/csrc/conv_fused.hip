@@ -776,7 +776,11 @@ bool fused_conv_supported(const Geom &g) {
 }
 
 hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *packed,
-                             const float *alpha, uint16_t *y, hipStream_t stream) {
+                             const float *alpha, uint16_t *y, hipStream_t stream, ChanAttn att) {
+    // channel attentions: the 3x3 small-image kernel only
+    if (att.in || att.out)
+        return fused_wave_attn_ok(g) ? launch_conv_fused_wave(g, x, packed, alpha, y, stream, att)
+                                     : hipErrorInvalidValue;
     if (fused_wave_ok(g)) return launch_conv_fused_wave(g, x, packed, alpha, y, stream);
     const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
     switch (g.n_pad / 2) {

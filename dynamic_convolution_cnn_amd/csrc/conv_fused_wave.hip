@@ -67,6 +67,7 @@ constexpr int kWvLdsBytes = 4 * 2 * kWvTileBytes + kWvStageBytes;  // 148 KB
 constexpr int kWvRounds = 4;                       // staging rounds of 128 tasks (two waves) per chunk
 constexpr int kWvThreads = 512;
 static_assert((1 + 16 * 16 + 1) * kWvPosBytes <= kWvTileBytes, "tile holds the guard and every read");
+constexpr int kWvAinMax = 768;  // input channels (padded) whose attentions fit beside the tiles and the stage
 
 __shared__ __attribute__((aligned(16))) u32x4_t s_wv[kWvLdsBytes / 16];
 
@@ -105,10 +106,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wv_rsrc(const void *p, int nby
 }
 
 // 4 experts: each weight is two words (expert pairs) of the packed bank.
+// ATT: FMDConv's channel attentions (either pointer may be null): a_in[b,c]
+// scales every mixed weight of input channel c before its rounding, a_out[b,o]
+// scales the fp32 accumulators of output channel o before theirs.
+template <bool ATT>
 __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint16_t *__restrict__ x,
                                                                      const uint32_t *__restrict__ packed,
                                                                      const float *__restrict__ alpha,
-                                                                     uint16_t *__restrict__ y, ConvArgs a) {
+                                                                     uint16_t *__restrict__ y, ConvArgs a,
+                                                                     const float *__restrict__ a_in,
+                                                                     const float *__restrict__ a_out) {
     char *lds = reinterpret_cast<char *>(s_wv);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -130,6 +137,17 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
     auto stage = [&](int buf, int v, int n, int ex) {
         return lds + 4 * 2 * kWvTileBytes + (((buf * 3 + v) * 2 + n) * 4 + ex) * 1024;
     };
+    // input attentions of the 4 examples, zero past Cin (visible to the mixing
+    // after the prologue's first barrier)
+    __shared__ __attribute__((aligned(16))) float s_ain[ATT ? 4 * kWvAinMax : 1];
+    if constexpr (ATT) {
+        if (a_in)
+            for (int i = tid; i < 4 * a.Cin_pad; i += kWvThreads) {
+                const int ex = i / a.Cin_pad, c = i - ex * a.Cin_pad;
+                const int bb = bt * 4 + ex;
+                s_ain[i] = (c < a.Cin && bb < a.B) ? a_in[(long)bb * a.Cin + c] : 0.f;
+            }
+    }
 
     // ---- mixing role: output channel o0 + om, channels 8 kh + 2 mp and
     // 8 kh + 2 mp + 1 of each chunk
@@ -171,9 +189,10 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
     // contiguous bytes.
     const int moff = ((om & 31) + 32 * kh) * 16 + mp * 4;
     const int mtile = om >> 5;
-    // One tap: the high-part products of both channels, the low-part
-    // products accumulated onto them, one 4-byte stage write per example.
-    auto mix_tap = [&](const u32x4_t wv, int buf, int v) {
+    // One tap of chunk cm: the high-part products of both channels, the
+    // low-part products accumulated onto them (times the input attentions),
+    // one 4-byte stage write per example.
+    auto mix_tap = [&](const u32x4_t wv, int buf, int v, int cm) {
         u32x2_t e0, e1;
         e0.x = wv.x; e0.y = wv.y;
         e1.x = wv.z; e1.y = wv.w;
@@ -182,6 +201,17 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
         f32x4_t d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ahi, __builtin_bit_cast(s16x4_t, e1), z, 0, 0, 0);
         d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo, __builtin_bit_cast(s16x4_t, e0), d0, 0, 0, 0);
         d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo, __builtin_bit_cast(s16x4_t, e1), d1, 0, 0, 0);
+        if constexpr (ATT) {
+            if (a_in) {
+                const int ch = cm * kWvChunk + 8 * kh + 2 * mp;
+#pragma unroll
+                for (int ex = 0; ex < 4; ++ex) {
+                    const f32x2_t ai = *reinterpret_cast<const f32x2_t *>(&s_ain[ex * a.Cin_pad + ch]);
+                    d0[ex] *= ai[0];
+                    d1[ex] *= ai[1];
+                }
+            }
+        }
 #pragma unroll
         for (int ex = 0; ex < 4; ++ex)
             *reinterpret_cast<uint32_t *>(stage(buf, v, mtile, ex) + moff) = pack_bf16x2(d0[ex], d1[ex]);
@@ -291,7 +321,7 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
             for (int i = 0; i < kWvRounds; ++i) st_load(rs1, i, sr[i]);
             load_words(0, 1, wq[1]);
 #pragma unroll
-            for (int v = 0; v < 3; ++v) mix_tap(wq[0][v], 0, v);
+            for (int v = 0; v < 3; ++v) mix_tap(wq[0][v], 0, v, 0);
         }
         load_words(0, 2, wq[0]);
         lds_barrier();  // stage buffer 0 and tile 0 complete
@@ -326,14 +356,15 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
                 // with the mixing of group g + 1's tap 0
 #pragma unroll
                 for (int pb = 0; pb < NPB; ++pb) mfma_pb(left_neighbour(acur[pb]), bcur[0], pb);
-                mix_tap(wn[0], nb, 0);
+                const int cm = u < 2 ? c : c + 1;  // chunk of group g + 1
+                mix_tap(wn[0], nb, 0, cm);
                 __builtin_amdgcn_sched_barrier(0);
                 // tap 1 (centre) with the rest; then the words of group g + 3
                 // load into the buffer just used
 #pragma unroll
                 for (int pb = 0; pb < NPB; ++pb) mfma_pb(acur[pb], bcur[1], pb);
-                mix_tap(wn[1], nb, 1);
-                mix_tap(wn[2], nb, 2);
+                mix_tap(wn[1], nb, 1, cm);
+                mix_tap(wn[2], nb, 2, cm);
                 __builtin_amdgcn_sched_barrier(0);
                 // group g + 3 is (chunk c + 1, row u)
                 load_words(c + 1, u, wn);
@@ -388,6 +419,15 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int ch = 32 * n + (lane & 31);
+            if constexpr (ATT) {
+                if (a_out) {
+                    const float ao = a_out[(long)b * a.Cout + min(o0 + ch, a.Cout - 1)];
+#pragma unroll
+                    for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) acc[pb][n][q] *= ao;
+                }
+            }
 #pragma unroll
             for (int pb = 0; pb < NPB; ++pb) {
                 if (!owns(pb, n)) continue;
@@ -439,16 +479,24 @@ bool fused_wave_ok(const Geom &g) {
            g.Cin_pad % kWvChunk == 0;
 }
 
+bool fused_wave_attn_ok(const Geom &g) { return fused_wave_ok(g) && g.Cin_pad <= kWvAinMax; }
+
 hipError_t launch_conv_fused_wave(const Geom &g, const uint16_t *x, const uint16_t *packed, const float *alpha,
-                                  uint16_t *y, hipStream_t stream) {
+                                  uint16_t *y, hipStream_t stream, ChanAttn att) {
     ConvArgs a = base_args(g);
     a.tile_rows = 16;
     a.n_btiles = ceil_div(g.B, 4);
     a.n_otiles = ceil_div(g.Cout, 64);
     const long blocks = (long)a.n_btiles * a.n_otiles;
     const uint32_t *pk = reinterpret_cast<const uint32_t *>(packed);
-    hipLaunchKernelGGL(conv_fused_wave_kernel, dim3((unsigned)blocks), dim3(kWvThreads), 0, stream, x, pk, alpha, y,
-                       a);
+    if (att.in || att.out) {
+        if (!fused_wave_attn_ok(g)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(conv_fused_wave_kernel<true>, dim3((unsigned)blocks), dim3(kWvThreads), 0, stream, x, pk,
+                           alpha, y, a, att.in, att.out);
+    } else {
+        hipLaunchKernelGGL(conv_fused_wave_kernel<false>, dim3((unsigned)blocks), dim3(kWvThreads), 0, stream, x, pk,
+                           alpha, y, a, nullptr, nullptr);
+    }
     return hipGetLastError();
 }
 

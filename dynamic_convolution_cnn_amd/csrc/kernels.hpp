@@ -97,12 +97,14 @@ hipError_t launch_conv_pm3w(const Geom &g, const uint16_t *x, const uint16_t *wt
 // packed bank in registers (no mixed kernel in memory).
 bool fused_conv_supported(const Geom &g);
 hipError_t launch_conv_fused(const Geom &g, const uint16_t *x, const uint16_t *packed,
-                             const float *alpha, uint16_t *y, hipStream_t stream);
+                             const float *alpha, uint16_t *y, hipStream_t stream, ChanAttn att = {});
 // The 3x3 pad-1 case up to 14 x 14 outputs with one wave per example
 // (conv_fused_wave.hip); launch_conv_fused dispatches to it.
 bool fused_wave_ok(const Geom &g);
+// ... and with channel attentions (the input attentions of 4 examples in LDS)
+bool fused_wave_attn_ok(const Geom &g);
 hipError_t launch_conv_fused_wave(const Geom &g, const uint16_t *x, const uint16_t *packed,
-                                  const float *alpha, uint16_t *y, hipStream_t stream);
+                                  const float *alpha, uint16_t *y, hipStream_t stream, ChanAttn att = {});
 
 // Direct float32 convolution (groups == 1) with mixed kernels in natural
 // layout [B][Cout][Cin][KH][KW].

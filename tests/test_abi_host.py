@@ -228,11 +228,18 @@ def test_forward_attn_checks():
             wsb = bd.dynconv_forward_attn_workspace_bytes(desc, policy)
         return L.dynconv_forward_attn(ctypes.byref(desc), policy, x, e, a, ai, ao, y, wsp, wsb, None)
 
-    # bf16 groups == 1: the attentions run on the PREMIX policy
-    assert bd.dynconv_forward_attn_workspace_bytes(d) == bd.dynconv_forward_workspace_bytes(
-        d, bd.DYNCONV_POLICY_PREMIX)
-    assert bd.dynconv_forward_attn_workspace_bytes(d, bd.DYNCONV_POLICY_FUSED) == 0
-    assert fwd_attn(policy=bd.DYNCONV_POLICY_FUSED, wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    # bf16 groups == 1 that the small-image 3x3 fused kernel takes: the attentions follow the plain layer's policy
+    assert bd.dynconv_forward_policy(d) == bd.DYNCONV_POLICY_FUSED
+    for pol in (bd.DYNCONV_POLICY_AUTO, bd.DYNCONV_POLICY_FUSED, bd.DYNCONV_POLICY_PREMIX):
+        assert bd.dynconv_forward_attn_workspace_bytes(d, pol) == bd.dynconv_forward_workspace_bytes(d, pol)
+    # other bf16 groups == 1 layers: FUSED is refused with attentions and AUTO premixes
+    big = good_desc(H=16, W=16)
+    assert bd.dynconv_forward_attn_workspace_bytes(big) == bd.dynconv_forward_workspace_bytes(
+        big, bd.DYNCONV_POLICY_PREMIX)
+    assert bd.dynconv_forward_attn_workspace_bytes(big, bd.DYNCONV_POLICY_FUSED) == 0
+    assert fwd_attn(desc=big, policy=bd.DYNCONV_POLICY_FUSED, wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert fwd_attn(desc=good_desc(Cin=800), policy=bd.DYNCONV_POLICY_FUSED,
+                    wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED  # input attentions past the LDS budget
     assert fwd_attn(ai=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
     assert fwd_attn(ao=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
     assert fwd_attn(x=None) == bd.DYNCONV_ERR_INVALID_ARG

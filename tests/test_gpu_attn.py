@@ -107,6 +107,39 @@ def test_forward_attn_depthwise_premixed_taps(case):
     _forward_case(case, "both", bd.DYNCONV_POLICY_PREMIX)
 
 
+# Layers the small-image 3x3 fused kernel takes: the attentions ride the fused path (a_in scales the mixed
+# weights before their rounding, a_out the accumulators); ragged example quads and channel tiles.
+FUSED_ATTN_CASES = [
+    (6, 64, 96, 14, 14, 3, 1, 1, 1, 4, "bf16"),     # ResNet-50-shaped layer, 1.5 example quads, 1.5 channel tiles
+    (5, 40, 64, 10, 12, 3, 1, 1, 1, 3, "bf16"),     # 3 experts, Cin padded 40 -> 64, H != W
+]
+
+
+@pytest.mark.parametrize("which", ["both", "in", "out"])
+@pytest.mark.parametrize("policy", [bd.DYNCONV_POLICY_FUSED, bd.DYNCONV_POLICY_AUTO])
+@pytest.mark.parametrize("case", FUSED_ATTN_CASES)
+def test_forward_attn_fused(case, policy, which):
+    _forward_case(case, which, policy)
+
+
+@pytest.mark.parametrize("case", FUSED_ATTN_CASES)
+def test_fused_attention_of_ones_is_bitwise_the_plain_fused_layer(case):
+    B, Cin, Cout, H, W, k, st, p, g, n, dtype = case
+    rng = np.random.default_rng(11)
+    x = inputs.bf16_round(rng.standard_normal((B, Cin, H, W), dtype=np.float32))
+    e = inputs.bf16_round(rng.standard_normal((n, Cout, Cin, k, k), dtype=np.float32))
+    alpha = rng.uniform(-1, 1, (B, n)).astype(np.float32)
+    xd, ed, ad = to_dev(x, dtype), to_dev(e, dtype), to_dev(alpha, "f32")
+    ones_in = torch.ones((B, Cin), dtype=torch.float32, device="cuda")
+    ones_out = torch.ones((B, Cout), dtype=torch.float32, device="cuda")
+    say("fused attention of ones", case)
+    pol = bd.DYNCONV_POLICY_FUSED
+    y1 = bd.dynconv_forward_attn(xd, ed, ad, ones_in, ones_out, st, p, g, policy=pol)
+    y0 = bd.dynconv_forward(xd, ed, ad, st, p, g, policy=pol)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
 @pytest.mark.parametrize("case", [FWD_CASES[0], FWD_CASES[1], FWD_CASES[2], FWD_CASES[6]])
 def test_attention_of_ones_is_bitwise_the_plain_layer(case):
     """a_in = a_out = 1 gives exactly dynconv_forward's result on the same policy."""
