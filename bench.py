@@ -51,7 +51,7 @@ GRAPH_STEPS = 10                # steps per HIP graph replay in the timed loop
 # for the kernel source it was taken on (sha256 prefix over the files the dominant kernel
 # is compiled from, listed below); otherwise null.
 TRAFFIC = {
-    "resnet50_3x3": {"source_sha": "79207e4add6e4901",
+    "resnet50_3x3": {"source_sha": "97a3c8fc8b79f574",
                      "fetch_kib": 32312.8, "write_kib": 25088.0,
                      "fetch_scale": 262144 / 131085.4, "write_scale": 1.0},
 }
@@ -183,7 +183,7 @@ def main():
             continue
         if w.attention:  # channel attentions: the forward packs its bank itself (PREMIX policy)
             descs.append(desc)
-            pols.append(bd.DYNCONV_POLICY_PREMIX if L.groups == 1 else bd.dynconv_forward_policy(desc))
+            pols.append(bd.dynconv_forward_policy(desc))  # the attentions follow the plain layer's policy
             packed.append(None)
             nb = bd.dynconv_forward_attn_workspace_bytes(desc, pols[-1])
             ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))

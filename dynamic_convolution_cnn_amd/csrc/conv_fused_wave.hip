@@ -189,10 +189,23 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
     // contiguous bytes.
     const int moff = ((om & 31) + 32 * kh) * 16 + mp * 4;
     const int mtile = om >> 5;
-    // One tap of chunk cm: the high-part products of both channels, the
-    // low-part products accumulated onto them (times the input attentions),
-    // one 4-byte stage write per example.
-    auto mix_tap = [&](const u32x4_t wv, int buf, int v, int cm) {
+    // The input attentions of the lane's two channels of chunk cm for the 4
+    // examples (ones without input attentions).
+    auto read_ain = [&](int cm, f32x2_t (&ai)[4]) {
+#pragma unroll
+        for (int ex = 0; ex < 4; ++ex) ai[ex] = f32x2_t{1.f, 1.f};
+        if constexpr (ATT) {
+            if (a_in) {
+                const int ch = cm * kWvChunk + 8 * kh + 2 * mp;
+#pragma unroll
+                for (int ex = 0; ex < 4; ++ex) ai[ex] = *reinterpret_cast<const f32x2_t *>(&s_ain[ex * a.Cin_pad + ch]);
+            }
+        }
+    };
+    // One tap: the high-part products of both channels, the low-part products
+    // accumulated onto them (times the input attentions ai), one 4-byte stage
+    // write per example.
+    auto mix_tap = [&](const u32x4_t wv, int buf, int v, const f32x2_t (&ai)[4]) {
         u32x2_t e0, e1;
         e0.x = wv.x; e0.y = wv.y;
         e1.x = wv.z; e1.y = wv.w;
@@ -202,14 +215,10 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
         d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo, __builtin_bit_cast(s16x4_t, e0), d0, 0, 0, 0);
         d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(alo, __builtin_bit_cast(s16x4_t, e1), d1, 0, 0, 0);
         if constexpr (ATT) {
-            if (a_in) {
-                const int ch = cm * kWvChunk + 8 * kh + 2 * mp;
 #pragma unroll
-                for (int ex = 0; ex < 4; ++ex) {
-                    const f32x2_t ai = *reinterpret_cast<const f32x2_t *>(&s_ain[ex * a.Cin_pad + ch]);
-                    d0[ex] *= ai[0];
-                    d1[ex] *= ai[1];
-                }
+            for (int ex = 0; ex < 4; ++ex) {
+                d0[ex] *= ai[ex][0];
+                d1[ex] *= ai[ex][1];
             }
         }
 #pragma unroll
@@ -320,8 +329,12 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
 #pragma unroll
             for (int i = 0; i < kWvRounds; ++i) st_load(rs1, i, sr[i]);
             load_words(0, 1, wq[1]);
+            {
+                f32x2_t ai0[4];
+                read_ain(0, ai0);
 #pragma unroll
-            for (int v = 0; v < 3; ++v) mix_tap(wq[0][v], 0, v, 0);
+                for (int v = 0; v < 3; ++v) mix_tap(wq[0][v], 0, v, ai0);
+            }
         }
         load_words(0, 2, wq[0]);
         lds_barrier();  // stage buffer 0 and tile 0 complete
@@ -356,15 +369,16 @@ __global__ __launch_bounds__(kWvThreads) void conv_fused_wave_kernel(const uint1
                 // with the mixing of group g + 1's tap 0
 #pragma unroll
                 for (int pb = 0; pb < NPB; ++pb) mfma_pb(left_neighbour(acur[pb]), bcur[0], pb);
-                const int cm = u < 2 ? c : c + 1;  // chunk of group g + 1
-                mix_tap(wn[0], nb, 0, cm);
+                f32x2_t ai[4];
+                read_ain(u < 2 ? c : c + 1, ai);  // chunk of group g + 1
+                mix_tap(wn[0], nb, 0, ai);
                 __builtin_amdgcn_sched_barrier(0);
                 // tap 1 (centre) with the rest; then the words of group g + 3
                 // load into the buffer just used
 #pragma unroll
                 for (int pb = 0; pb < NPB; ++pb) mfma_pb(acur[pb], bcur[1], pb);
-                mix_tap(wn[1], nb, 1, cm);
-                mix_tap(wn[2], nb, 2, cm);
+                mix_tap(wn[1], nb, 1, ai);
+                mix_tap(wn[2], nb, 2, ai);
                 __builtin_amdgcn_sched_barrier(0);
                 // group g + 3 is (chunk c + 1, row u)
                 load_words(c + 1, u, wn);

@@ -131,6 +131,13 @@ WORKLOADS: Dict[str, Workload] = {
         title="FMDConv multi-attention on the ResNet-18-shaped 3x3, B=32, 64->64, 56x56, n=4, softmax(z/4), bf16",
         B=32, n=4, dtype="bf16", route_mode=SOFTMAX, temperature=4.0, attention=True,
         layers=(Layer(64, 64, 56, 56, 3, 1, 1),)),
+    # the same attentions on the ResNet-50-shaped layer, where they ride the
+    # fused path (W_b never in memory)
+    "fmdconv_resnet50_3x3": Workload(
+        key="fmdconv_resnet50_3x3",
+        title="FMDConv multi-attention on the ResNet-50-shaped 3x3, B=256, 256->256, 14x14, n=4, softmax(z/4), bf16",
+        B=256, n=4, dtype="bf16", route_mode=SOFTMAX, temperature=4.0, attention=True, x_relu=True,
+        layers=(Layer(256, 256, 14, 14, 3, 1, 1),)),
     # spatially sparse evaluation: a gate selects a quarter of the positions of
     # a residual ResNet-18-shaped layer; not one of the five configurations
     "sparse_resnet18_3x3": Workload(

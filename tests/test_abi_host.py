@@ -160,6 +160,11 @@ def test_policy_choice_per_workload():
             got.append(bd.dynconv_forward_policy(d))
             assert bd.dynconv_forward_workspace_bytes(d) >= 0
         assert got == pol, key
+    # the attention layers follow the plain layer's policy where the fused kernel takes them
+    r50 = inputs.WORKLOADS["fmdconv_resnet50_3x3"].layers[0]
+    d50 = bd.make_desc(256, r50.Cin, r50.H, r50.W, r50.Cout, 3, 3, 1, 1, 1, 4, bd.DYNCONV_BF16)
+    assert bd.dynconv_forward_attn_workspace_bytes(d50) == bd.dynconv_forward_workspace_bytes(
+        d50, bd.DYNCONV_POLICY_FUSED)
 
 
 def test_invalid_call_writes_nothing_and_sets_message():

@@ -157,3 +157,24 @@ def test_attention_of_ones_is_bitwise_the_plain_layer(case):
     y0 = bd.dynconv_forward(xd, ed, ad, st, p, g, policy=pol)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+def test_fmdconv_resnet50_layer_full_size_sampled():
+    """The ResNet-50-shaped FMDConv layer at its full batch on the fused path (AUTO resolves there); sampled
+    examples against the oracle, with uniform attentions so every example differs."""
+    w = inputs.WORKLOADS["fmdconv_resnet50_3x3"]
+    d = inputs.make_inputs(w)
+    L, e = w.layers[0], d["experts"][0]
+    rng = np.random.default_rng(21)
+    alpha = inputs.forced_alpha(w.B, w.n, "uniform")
+    a_in = rng.uniform(0.05, 1.0, (w.B, L.Cin)).astype(np.float32)
+    a_out = rng.uniform(0.05, 1.0, (w.B, L.Cout)).astype(np.float32)
+    say("fmdconv resnet50 full size")
+    y = bd.dynconv_forward_attn(to_dev(d["x"], "bf16"), to_dev(e, "bf16"), to_dev(alpha, "f32"),
+                                to_dev(a_in, "f32"), to_dev(a_out, "f32"), L.stride, L.pad, L.groups)
+    torch.cuda.synchronize()
+    got = from_dev(y)
+    for b in (0, 1, 130, 255):
+        ref = oracle.forward_attn(d["x"][b:b + 1], e, alpha[b:b + 1], a_in[b:b + 1], a_out[b:b + 1],
+                                  L.stride, L.pad, L.groups)
+        check(got[b:b + 1], ref, TOL["bf16"], f"fmdconv resnet50 example {b}")
