@@ -344,13 +344,19 @@ hipError_t launch_gap_vec(const T *x, float *gap, long rows, int hw, hipStream_t
 
 
 // Several FC heads on the channel means, for FMDConv's kernel, input and
-// output attentions. Workgroup (b, j): chunk j of the heads' logits of
-// example b. A head with the softmax (its normalisation spans all its
-// logits) is one chunk of up to 256 logits; a sigmoid head is cut into
-// chunks of 64. Wave w computes the chunk's logits w, w + 4, ..., four at a
-// time with the lanes over channels (coalesced rows of fc_w) and a fixed
-// butterfly per logit; the nonlinearity runs after a barrier.
+// output attentions. Workgroup (e, j): chunk j of the heads' logits of
+// examples 8 e .. 8 e + 7. A head with the softmax (its normalisation spans
+// all its logits) is one chunk of up to 256 logits (four passes of 64 rows);
+// a sigmoid head is cut into chunks of 64. Per pass of 64 logit rows and per
+// tile of 128 channels, the rows of fc_w and the 8 examples' channel means
+// are staged in LDS with coalesced loads; thread t then owns row t & 63 for
+// examples 2 (t >> 6) and 2 (t >> 6) + 1 and walks the tile's channels in
+// order (16-byte LDS reads), so each fc_w value serves 8 examples and every
+// logit is one fixed-order sum. The nonlinearity runs after a barrier.
 constexpr int kHeadsMax = 3;
+constexpr int kHeadsEB = 8;    // examples per workgroup
+constexpr int kHeadsCT = 128;  // channels per staged tile
+constexpr int kHeadsWP = kHeadsCT + 4;  // padded row (16-byte reads of 64 rows on distinct banks)
 struct RouteHeads {
     const float *w[kHeadsMax];
     const float *b[kHeadsMax];
@@ -358,60 +364,114 @@ struct RouteHeads {
     int n[kHeadsMax], mode[kHeadsMax], first[kHeadsMax + 1];  // first chunk of each head
     int heads;
 };
-__global__ __launch_bounds__(256) void route_heads_kernel(const float *__restrict__ gap, RouteHeads hp,
+__global__ __launch_bounds__(256) void route_heads_kernel(const float *__restrict__ gap, RouteHeads hp, int B,
                                                           int C, float temp) {
-    __shared__ float z[256];
-    const int b = blockIdx.x, j = blockIdx.y;
+    __shared__ __attribute__((aligned(16))) float sW[64][kHeadsWP];
+    __shared__ __attribute__((aligned(16))) float sG[kHeadsEB][kHeadsCT];
+    __shared__ float z[kHeadsEB][256];
+    const int b0 = blockIdx.x * kHeadsEB, j = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int h = 0;
     while (h + 1 < hp.heads && j >= hp.first[h + 1]) ++h;
     const int n = hp.n[h], mode = hp.mode[h];
     const int per = mode == 1 ? n : 64;
     const int i0 = (j - hp.first[h]) * per, cnt = min(per, n - i0);
-    const float *gb = gap + (long)b * C;
     const float *W = hp.w[h];
-    for (int q = wave * 4; q < cnt; q += 16) {
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int c = lane; c < C; c += 64) {
-            const float gc = gb[c];
+    const int r = lane, e0 = 2 * wave;
+    for (int rp = 0; rp < cnt; rp += 64) {  // passes of 64 logit rows
+        float acc0 = 0.f, acc1 = 0.f;
+        for (int c0 = 0; c0 < C; c0 += kHeadsCT) {
+            // every load of the tile in flight before the first LDS store
+            constexpr int kW4 = 64 * kHeadsCT / 4 / 256;  // 16-byte pieces of fc_w per thread
+            f32x4_t wq[kW4];
+            f32x4_t gq;
+            if ((C & 3) == 0) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                part[k] = fmaf(W[(long)(i0 + min(q + k, cnt - 1)) * C + c], gc, part[k]);
+                for (int i = 0; i < kW4; ++i) {
+                    const int idx = tid + 256 * i, row = idx / (kHeadsCT / 4), c = 4 * (idx % (kHeadsCT / 4));
+                    const bool in = rp + row < cnt && c0 + c < C;
+                    wq[i] = in ? *reinterpret_cast<const f32x4_t *>(&W[(long)(i0 + rp + row) * C + c0 + c])
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+                {
+                    const int e = tid / (kHeadsCT / 4), c = 4 * (tid % (kHeadsCT / 4));
+                    gq = (b0 + e < B && c0 + c < C) ? *reinterpret_cast<const f32x4_t *>(&gap[(long)(b0 + e) * C + c0 + c])
+                                                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kW4; ++i) {
+                    const int idx = tid + 256 * i, row = idx / (kHeadsCT / 4), c = 4 * (idx % (kHeadsCT / 4));
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        wq[i][k] = (rp + row < cnt && c0 + c + k < C) ? W[(long)(i0 + rp + row) * C + c0 + c + k] : 0.f;
+                }
+                const int e = tid / (kHeadsCT / 4), c = 4 * (tid % (kHeadsCT / 4));
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    gq[k] = (b0 + e < B && c0 + c + k < C) ? gap[(long)(b0 + e) * C + c0 + c + k] : 0.f;
+            }
+            __syncthreads();  // the previous tile's reads are done
+#pragma unroll
+            for (int i = 0; i < kW4; ++i) {
+                const int idx = tid + 256 * i, row = idx / (kHeadsCT / 4), c = 4 * (idx % (kHeadsCT / 4));
+                *reinterpret_cast<f32x4_t *>(&sW[row][c]) = wq[i];
+            }
+            *reinterpret_cast<f32x4_t *>(&sG[tid / (kHeadsCT / 4)][4 * (tid % (kHeadsCT / 4))]) = gq;
+            __syncthreads();
+#pragma unroll 4
+            for (int c = 0; c < kHeadsCT; c += 4) {
+                const f32x4_t wv = *reinterpret_cast<const f32x4_t *>(&sW[r][c]);
+                const f32x4_t g0 = *reinterpret_cast<const f32x4_t *>(&sG[e0][c]);
+                const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(&sG[e0 + 1][c]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    acc0 = fmaf(wv[k], g0[k], acc0);
+                    acc1 = fmaf(wv[k], g1[k], acc1);
+                }
+            }
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float t = wave_sum(part[k]);
-            if (lane == 0 && q + k < cnt) z[q + k] = t + (hp.b[h] ? hp.b[h][i0 + q + k] : 0.f);
+        if (rp + r < cnt) {
+            const float bias = hp.b[h] ? hp.b[h][i0 + rp + r] : 0.f;
+            z[e0][rp + r] = acc0 + bias;
+            z[e0 + 1][rp + r] = acc1 + bias;
         }
     }
     __syncthreads();
-    float *out = hp.out[h] + (long)b * n + i0;
     if (mode == 0) {
-        for (int i = tid; i < cnt; i += 256) {
-            const float v = z[i];
-            float a;
-            if (v >= 0.f) {
-                a = 1.f / (1.f + expf(-v));
-            } else {
-                const float e = expf(v);
-                a = e / (1.f + e);
+        for (int e = 0; e < kHeadsEB && b0 + e < B; ++e) {
+            float *out = hp.out[h] + (long)(b0 + e) * n + i0;
+            for (int i = tid; i < cnt; i += 256) {
+                const float v = z[e][i];
+                float a;
+                if (v >= 0.f) {
+                    a = 1.f / (1.f + expf(-v));
+                } else {
+                    const float ev = expf(v);
+                    a = ev / (1.f + ev);
+                }
+                out[i] = a;
             }
-            out[i] = a;
         }
-    } else if (wave == 0) {
-        float m = -INFINITY;
-        for (int i = lane; i < cnt; i += 64) m = fmaxf(m, z[i] / temp);
-        m = wave_max(m);
-        float s = 0.f;
-        for (int i = lane; i < cnt; i += 64) s += expf(z[i] / temp - m);
-        s = wave_sum(s);
-        for (int i = lane; i < cnt; i += 64) out[i] = expf(z[i] / temp - m) / s;
+    } else {
+        // softmax(z / T) over the head's logits, one wave per example
+        for (int e = wave; e < kHeadsEB && b0 + e < B; e += 4) {
+            float *out = hp.out[h] + (long)(b0 + e) * n + i0;
+            float m = -INFINITY;
+            for (int i = lane; i < cnt; i += 64) m = fmaxf(m, z[e][i] / temp);
+            m = wave_max(m);
+            float sum = 0.f;
+            for (int i = lane; i < cnt; i += 64) sum += expf(z[e][i] / temp - m);
+            sum = wave_sum(sum);
+            for (int i = lane; i < cnt; i += 64) out[i] = expf(z[e][i] / temp - m) / sum;
+        }
     }
 }
 
 }  // namespace
 
 static_assert(kMaxJ * 64 >= 256, "route kernel covers n <= 256");
+static_assert(kHeadsEB * kHeadsCT == 4 * 256, "one 16-byte piece of channel means per thread and tile");
 
 bool route_single_kernel(const Geom &g) {
     // planes up to 64 lanes x kRouteMaxK vectors (bf16: 8192 elements with 16-byte loads)
@@ -488,8 +548,8 @@ hipError_t launch_route_heads(const Geom &g, const void *x, int heads, const flo
         chunks += mode[h] == 1 ? 1 : ceil_div(nout[h], 64);
     }
     hp.first[heads] = chunks;
-    hipLaunchKernelGGL(route_heads_kernel, dim3((unsigned)g.B, (unsigned)chunks), dim3(256), 0, stream, gap,
-                       hp, g.Cin, temperature);
+    hipLaunchKernelGGL(route_heads_kernel, dim3((unsigned)ceil_div(g.B, kHeadsEB), (unsigned)chunks), dim3(256), 0,
+                       stream, gap, hp, g.B, g.Cin, temperature);
     return hipGetLastError();
 }
 
