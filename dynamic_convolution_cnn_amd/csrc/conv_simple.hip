@@ -675,6 +675,10 @@ static hipError_t launch_dw2(const Geom &g, const uint16_t *x, const uint16_t *e
 hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
                                  const float *alpha, const void *wmixed, void *y,
                                  hipStream_t stream, ChanAttn att) {
+    if (depthwise_mfma_ok(g, wmixed != nullptr))
+        return launch_depthwise_mfma(g, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(experts),
+                                     alpha, static_cast<const uint16_t *>(wmixed), static_cast<uint16_t *>(y),
+                                     stream, att);
     if (dw2_ok(g))
         return launch_dw2(g, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(experts), alpha,
                           static_cast<const uint16_t *>(wmixed), static_cast<uint16_t *>(y), stream, att);

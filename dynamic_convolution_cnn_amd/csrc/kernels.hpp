@@ -119,6 +119,11 @@ bool depthwise_supported(const Geom &g);
 hipError_t launch_conv_depthwise(const Geom &g, const void *x, const void *experts,
                                  const float *alpha, const void *wmixed, void *y,
                                  hipStream_t stream, ChanAttn att = {});
+// The matrix-core form of it (bf16, stride 1, square 3/5/7 taps, output
+// planes of at most 32 x 32); launch_conv_depthwise picks it where it applies.
+bool depthwise_mfma_ok(const Geom &g, bool premixed);
+hipError_t launch_depthwise_mfma(const Geom &g, const uint16_t *x, const uint16_t *experts, const float *alpha,
+                                 const uint16_t *wmixed, uint16_t *y, hipStream_t stream, ChanAttn att);
 
 // ---- gated (spatially sparse) evaluation ----------------------------------
 // y = (residual ? x : 0) + [mask != 0] * conv(x, W_b) with W_b premixed in

@@ -63,7 +63,9 @@ FWD_CASES = [
     (3, 96, 40, 12, 12, 1, 1, 0, 1, 2, "bf16"),     # 1x1, persistent three-chunk path
     (2, 24, 40, 13, 13, 5, 1, 2, 1, 7, "bf16"),     # 5x5 on 16x16x32 MFMA
     (2, 16, 16, 15, 15, 3, 2, 1, 1, 2, "bf16"),     # stride 2 on 16x16x32 MFMA
-    (6, 24, 24, 28, 28, 5, 1, 2, 24, 8, "bf16"),    # depthwise, channel-major kernel
+    (6, 24, 24, 28, 28, 5, 1, 2, 24, 8, "bf16"),    # depthwise, matrix-core kernel
+    (3, 16, 16, 14, 14, 3, 1, 1, 16, 12, "bf16"),   # depthwise, matrix-core kernel on premixed taps (n > 8)
+    (4, 16, 16, 16, 16, 3, 2, 1, 16, 6, "bf16"),    # depthwise stride 2, channel-major kernel
     (3, 16, 16, 14, 14, 3, 2, 1, 16, 12, "bf16"),   # depthwise, plane-per-wave kernel (n > 8)
     (2, 8, 8, 9, 7, 3, 1, 1, 8, 3, "bf16"),         # depthwise, odd W (general kernel)
     (2, 12, 20, 9, 9, 3, 1, 1, 1, 3, "f32"),        # float32 direct
@@ -96,12 +98,12 @@ def test_forward_attn_matches_oracle(case):
 
 
 @pytest.mark.parametrize("which", ["in", "out"])
-@pytest.mark.parametrize("case", [FWD_CASES[0], FWD_CASES[2], FWD_CASES[6], FWD_CASES[9]])
+@pytest.mark.parametrize("case", [FWD_CASES[0], FWD_CASES[2], FWD_CASES[6], FWD_CASES[11]])
 def test_forward_attn_one_side(case, which):
     _forward_case(case, which)
 
 
-@pytest.mark.parametrize("case", [FWD_CASES[6], FWD_CASES[7]])
+@pytest.mark.parametrize("case", [FWD_CASES[6], FWD_CASES[7], FWD_CASES[9]])
 def test_forward_attn_depthwise_premixed_taps(case):
     """Depthwise with the taps materialised first (PREMIX) scales them the same way."""
     _forward_case(case, "both", bd.DYNCONV_POLICY_PREMIX)

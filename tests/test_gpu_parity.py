@@ -314,7 +314,14 @@ DW = [(3, 16, 9, 11, 5, 1, 2, 4), (2, 24, 28, 28, 3, 2, 1, 3), (4, 8, 7, 7, 7, 1
       # batch not a multiple of 16, a plane past the lanes' prefetched pieces, pad 0
       (3, 12, 10, 10, 5, 1, 2, 4), (2, 8, 14, 14, 3, 1, 1, 12), (2, 10, 16, 16, 5, 2, 2, 5),
       (2, 6, 12, 12, 7, 1, 3, 8), (5, 7, 28, 28, 5, 1, 2, 8), (1, 2, 56, 56, 3, 1, 1, 4),
-      (2, 4, 12, 12, 3, 2, 0, 4), (17, 3, 8, 8, 7, 2, 3, 2)]
+      (2, 4, 12, 12, 3, 2, 0, 4), (17, 3, 8, 8, 7, 2, 3, 2),
+      # matrix-core kernel (stride 1, output planes up to 32 x 32): 32 output
+      # rows, pad 0, 7x7 with 24-wide rows, rows not a multiple of 4, a batch
+      # of 19 (one wave of the second example group busy), pad beyond K - 1,
+      # planes of 84 elements (8-byte pieces)
+      (3, 5, 32, 28, 5, 1, 2, 6), (2, 4, 18, 18, 3, 1, 0, 3), (2, 3, 32, 24, 7, 1, 3, 5),
+      (4, 6, 14, 6, 3, 1, 1, 7), (19, 3, 16, 16, 5, 1, 2, 8), (2, 3, 4, 4, 7, 1, 5, 2),
+      (2, 5, 7, 12, 3, 1, 1, 4)]
 
 
 @pytest.mark.parametrize("case", DW)
