@@ -172,11 +172,11 @@ def main():
     for L, e in zip(w.layers, experts):
         desc = bd.make_desc(w.B, L.Cin, L.H, L.W, L.Cout, L.k, L.k, L.stride, L.pad, L.groups, w.n,
                             bd.DYNCONV_BF16 if w.dtype == "bf16" else bd.DYNCONV_F32)
-        if w.mask_density > 0:  # gated residual layer: the sparse entry point mixes itself
+        if w.mask_density > 0:  # gated residual layer: bank packed once, W_b mixed in the step
             descs.append(desc)
             pols.append(bd.DYNCONV_POLICY_PREMIX)
-            packed.append(None)
-            nb = bd.dynconv_forward_sparse_workspace_bytes(desc)
+            packed.append(torch.empty(bd.dynconv_packed_experts_bytes(desc), dtype=torch.uint8, device=dev))
+            nb = bd.dynconv_forward_sparse_packed_workspace_bytes(desc)
             ws.append(torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
             outs.append([torch.empty((w.B, L.Cout, L.Ho, L.Wo), dtype=x0.dtype, device=dev)
                          for _ in range(R)])
@@ -224,8 +224,8 @@ def main():
     def forward(li, h, s):
         L = w.layers[li]
         if w.mask_density > 0:
-            bd.dynconv_forward_sparse(h, experts[li], alphas[s], mask_dev, L.stride, L.pad, L.groups,
-                                      residual=True, y=outs[li][s], workspace=ws[li])
+            bd.dynconv_forward_sparse_packed(descs[li], h, packed[li], alphas[s], mask_dev, residual=True,
+                                             y=outs[li][s], workspace=ws[li])
         elif w.attention:
             bd.dynconv_forward_attn(h, experts[li], alphas[s], a_ins[s], a_outs[s], L.stride, L.pad,
                                     L.groups, policy=pols[li], y=outs[li][s], workspace=ws[li])

@@ -47,6 +47,7 @@ EXPORTED = (
     "dynconv_backward_weights_workspace_bytes", "dynconv_route_backward",
     "dynconv_route_backward_workspace_bytes", "dynconv_forward_sparse",
     "dynconv_forward_sparse_workspace_bytes", "dynconv_forward_noalloc",
+    "dynconv_forward_sparse_packed", "dynconv_forward_sparse_packed_workspace_bytes",
 )
 
 
@@ -128,6 +129,10 @@ def lib():
     L.dynconv_forward_sparse.restype = i32
     L.dynconv_forward_sparse_workspace_bytes.argtypes = [D]
     L.dynconv_forward_sparse_workspace_bytes.restype = sz
+    L.dynconv_forward_sparse_packed.argtypes = [D, P, P, P, P, i32, P, P, sz, P]
+    L.dynconv_forward_sparse_packed.restype = i32
+    L.dynconv_forward_sparse_packed_workspace_bytes.argtypes = [D]
+    L.dynconv_forward_sparse_packed_workspace_bytes.restype = sz
     L.dynconv_forward_noalloc.argtypes = [D, i32, P, P, P, P, P]
     L.dynconv_forward_noalloc.restype = i32
     _lib = L
@@ -614,4 +619,30 @@ def dynconv_forward_sparse(x: torch.Tensor, experts: torch.Tensor, alpha: torch.
     _check(lib().dynconv_forward_sparse(ctypes.byref(desc), _ptr(x), _ptr(experts), _ptr(alpha), _ptr(mask),
                                         int(bool(residual)), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "dynconv_forward_sparse")
+    return y
+
+
+def dynconv_forward_sparse_packed_workspace_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_forward_sparse_packed_workspace_bytes(ctypes.byref(desc)))
+
+
+def dynconv_forward_sparse_packed(desc: dynconv_desc_t, x: torch.Tensor, packed: torch.Tensor,
+                                  alpha: torch.Tensor, mask: torch.Tensor, residual: bool = False,
+                                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                  stream=None) -> torch.Tensor:
+    """dynconv_forward_sparse with a bank packed by dynconv_pack_experts."""
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, desc.stride, desc.pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W), torch.bfloat16)
+    _need_bytes(packed, "packed", dynconv_packed_experts_bytes(desc))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(mask, "mask", (desc.B, Ho, Wo), torch.uint8)
+    _need(y, "y", (desc.B, desc.Cout, Ho, Wo), x.dtype, optional=True)
+    _same_gpu(x=x, packed=packed, alpha=alpha, mask=mask, y=y)
+    if y is None:
+        y = torch.empty((desc.B, desc.Cout, Ho, Wo), dtype=x.dtype, device=x.device)
+    ws, ws_bytes = _workspace(dynconv_forward_sparse_packed_workspace_bytes(desc), x.device, workspace)
+    _check(lib().dynconv_forward_sparse_packed(ctypes.byref(desc), _ptr(x), _ptr(packed), _ptr(alpha), _ptr(mask),
+                                               int(bool(residual)), _ptr(y), _ptr(ws), ws_bytes,
+                                               _stream(stream)),
+           "dynconv_forward_sparse_packed")
     return y

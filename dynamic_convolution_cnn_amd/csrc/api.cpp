@@ -302,12 +302,48 @@ size_t route_backward_ws(const dynconv::Geom &g) {
 }
 
 // Workspace of dynconv_forward_sparse: W_b in the premix layout (through
-// the packed bank for n <= 16, the wide bank otherwise), then the compacted
-// active positions.
-size_t sparse_ws(const dynconv::Geom &g) {
-    const size_t bank = wide(g) ? dynconv::wide_bank_bytes(g) : dynconv::packed_experts_bytes(g);
-    return round_up(bank, kWsAlign) + round_up(dynconv::premixed_bytes(g), kWsAlign) +
-           round_up(dynconv::sparse_index_bytes(g), kWsAlign);
+// the packed bank for n <= 16, the wide bank otherwise), then, unless the
+// one-pass band kernel takes the layer, the compacted active positions and
+// the channel-innermost copy of x.
+size_t sparse_tail_ws(const dynconv::Geom &g) {
+    return round_up(dynconv::premixed_bytes(g), kWsAlign) +
+           (dynconv::gated_one_pass(g) ? 0 : round_up(dynconv::sparse_index_bytes(g), kWsAlign));
+}
+size_t sparse_bank_bytes(const dynconv::Geom &g) {
+    return round_up(wide(g) ? dynconv::wide_bank_bytes(g) : dynconv::packed_experts_bytes(g), kWsAlign);
+}
+size_t sparse_ws(const dynconv::Geom &g) { return sparse_bank_bytes(g) + sparse_tail_ws(g); }
+
+// Pointer and overlap checks shared by the gated entry points (`bank` is the
+// experts or the packed bank).
+dynconv_status_t check_sparse_ptrs(const dynconv::Geom &g, const void *x, const void *bank, const float *alpha,
+                                   const uint8_t *mask, const void *y) {
+    if (!x || !bank || !alpha || !mask || !y)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, the experts, alpha, mask and y must not be NULL");
+    const void *ptrs[] = {x, bank, alpha, mask, y};
+    for (const void *q : ptrs)
+        if (!aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t xn = (uintptr_t)g.B * g.Cin * g.H * g.W * 2, yn = (uintptr_t)g.B * g.Cout * g.P * 2;
+    if (x0 < y0 + yn && y0 < x0 + xn) return fail(DYNCONV_ERR_INVALID_ARG, "y must not overlap x");
+    if (!dynconv::premix_conv_supported(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "the mixed kernels' layout does not fit this layer");
+    return DYNCONV_OK;
+}
+
+// W_b from a bank in the premix kernels' layout (packed for n <= 16, wide
+// otherwise) into `tail`, then the gated kernels (their index scratch after
+// W_b).
+dynconv_status_t sparse_from_bank(const dynconv::Geom &g, const void *x, const uint16_t *bank, const float *alpha,
+                                  const uint8_t *mask, int32_t residual, void *y, char *tail, hipStream_t st) {
+    uint16_t *wt = reinterpret_cast<uint16_t *>(tail);
+    int *idx = reinterpret_cast<int *>(tail + round_up(dynconv::premixed_bytes(g), kWsAlign));
+    const hipError_t e = wide(g) ? dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st)
+                                 : dynconv::launch_premix(g, alpha, bank, wt, st);
+    if (e != hipSuccess) return hip_status(e, "gated evaluation mix launch");
+    return hip_status(dynconv::launch_conv_sparse(g, static_cast<const uint16_t *>(x), wt, mask, residual, idx,
+                                                  static_cast<uint16_t *>(y), st),
+                      "gated evaluation launch");
 }
 
 dynconv_status_t check_sparse(const dynconv_desc_t *desc, dynconv::Geom &g, int32_t residual) {
@@ -749,38 +785,42 @@ dynconv_status_t dynconv_forward_sparse(const dynconv_desc_t *desc, const void *
     dynconv::Geom g;
     dynconv_status_t s = check_sparse(desc, g, residual);
     if (s != DYNCONV_OK) return s;
-    if (!x || !experts || !alpha || !mask || !y)
-        return fail(DYNCONV_ERR_INVALID_ARG, "x, experts, alpha, mask and y must not be NULL");
-    const void *ptrs[] = {x, experts, alpha, mask, y};
-    for (const void *q : ptrs)
-        if (!aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
-    const uintptr_t xn = (uintptr_t)g.B * g.Cin * g.H * g.W * 2, yn = (uintptr_t)g.B * g.Cout * g.P * 2;
-    if (x0 < y0 + yn && y0 < x0 + xn) return fail(DYNCONV_ERR_INVALID_ARG, "y must not overlap x");
-    if (!dynconv::premix_conv_supported(g))
-        return fail(DYNCONV_ERR_UNSUPPORTED, "the mixed kernels' layout does not fit this layer");
+    s = check_sparse_ptrs(g, x, experts, alpha, mask, y);
+    if (s != DYNCONV_OK) return s;
     const size_t need = sparse_ws(g);
     if (workspace_bytes < need || !workspace || !aligned16(workspace))
         return fail(DYNCONV_ERR_WORKSPACE, "forward_sparse needs %zu bytes of 16-byte aligned workspace (got %zu)",
                     need, workspace_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
-    const size_t bank_b = round_up(wide(g) ? dynconv::wide_bank_bytes(g) : dynconv::packed_experts_bytes(g), kWsAlign);
     uint16_t *bank = reinterpret_cast<uint16_t *>(ws);
-    uint16_t *wt = reinterpret_cast<uint16_t *>(ws + bank_b);
-    int *idx = reinterpret_cast<int *>(ws + bank_b + round_up(dynconv::premixed_bytes(g), kWsAlign));
-    hipError_t e;
-    if (wide(g)) {
-        e = dynconv::launch_pack_wide(g, static_cast<const uint16_t *>(experts), bank, st);
-        if (e == hipSuccess) e = dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st);
-    } else {
-        e = dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), bank, st);
-        if (e == hipSuccess) e = dynconv::launch_premix(g, alpha, bank, wt, st);
-    }
-    if (e != hipSuccess) return hip_status(e, "dynconv_forward_sparse mix launch");
-    return hip_status(dynconv::launch_conv_sparse(g, static_cast<const uint16_t *>(x), wt, mask, residual, idx,
-                                                  static_cast<uint16_t *>(y), st),
-                      "dynconv_forward_sparse launch");
+    const hipError_t e = wide(g) ? dynconv::launch_pack_wide(g, static_cast<const uint16_t *>(experts), bank, st)
+                                 : dynconv::launch_pack_experts(g, static_cast<const uint16_t *>(experts), bank, st);
+    if (e != hipSuccess) return hip_status(e, "dynconv_forward_sparse pack launch");
+    return sparse_from_bank(g, x, bank, alpha, mask, residual, y, ws + sparse_bank_bytes(g), st);
+}
+
+size_t dynconv_forward_sparse_packed_workspace_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_sparse(desc, g, 0) != DYNCONV_OK) return 0;
+    return sparse_tail_ws(g);
+}
+
+dynconv_status_t dynconv_forward_sparse_packed(const dynconv_desc_t *desc, const void *x, const void *packed,
+                                               const float *alpha, const uint8_t *mask, int32_t residual, void *y,
+                                               void *workspace, size_t workspace_bytes, void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_sparse(desc, g, residual);
+    if (s != DYNCONV_OK) return s;
+    s = check_sparse_ptrs(g, x, packed, alpha, mask, y);
+    if (s != DYNCONV_OK) return s;
+    const size_t need = sparse_tail_ws(g);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE,
+                    "forward_sparse_packed needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
+                    workspace_bytes);
+    return sparse_from_bank(g, x, static_cast<const uint16_t *>(packed), alpha, mask, residual, y,
+                            static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

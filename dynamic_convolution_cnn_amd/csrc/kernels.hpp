@@ -131,6 +131,9 @@ hipError_t launch_depthwise_mfma(const Geom &g, const uint16_t *x, const uint16_
 // positions; idx: sparse_index_bytes(g) of scratch (the compacted positions
 // and their counts, then a channel-innermost copy of x). y must not overlap x.
 size_t sparse_index_bytes(const Geom &g);
+// True where the one-pass band kernel takes the layer (3x3, stride 1, pad 1,
+// Cin and Cout up to 64, W a multiple of 8); it needs no index scratch.
+bool gated_one_pass(const Geom &g);
 hipError_t launch_conv_sparse(const Geom &g, const uint16_t *x, const uint16_t *wt, const uint8_t *mask, int residual,
                               int *idx, uint16_t *y, hipStream_t stream);
 

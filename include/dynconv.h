@@ -256,6 +256,19 @@ dynconv_status_t dynconv_forward_sparse(const dynconv_desc_t *desc, const void *
                                         void *workspace, size_t workspace_bytes, void *stream);
 size_t dynconv_forward_sparse_workspace_bytes(const dynconv_desc_t *desc);
 
+/* dynconv_forward_sparse with an expert bank already packed by
+ * dynconv_pack_experts (so the static experts are laid out once, not on
+ * every call). Same arguments, checks, results and determinism as
+ * dynconv_forward_sparse, with packed in place of experts. workspace: at
+ * least dynconv_forward_sparse_packed_workspace_bytes(desc) bytes (the mixed
+ * kernels and, outside the one-pass band kernel's shapes, the compacted
+ * positions; 0 for an unsupported layer). Results are bitwise those of
+ * dynconv_forward_sparse. */
+dynconv_status_t dynconv_forward_sparse_packed(const dynconv_desc_t *desc, const void *x, const void *packed,
+                                               const float *alpha, const uint8_t *mask, int32_t residual,
+                                               void *y, void *workspace, size_t workspace_bytes, void *stream);
+size_t dynconv_forward_sparse_packed_workspace_bytes(const dynconv_desc_t *desc);
+
 /* ---- gradients ------------------------------------------------------------
  * The pages train dynamic convolutions end to end (CondConv: Conditionally
  * Parameterized Convolutions, abstract, where the per-example kernels are

@@ -388,10 +388,14 @@ def test_forward_sparse_checks():
             wsb = bd.dynconv_forward_sparse_workspace_bytes(desc)
         return L.dynconv_forward_sparse(ctypes.byref(desc), x, e, a, m, res, y, wsp, wsb, None)
 
-    # packed bank, W_b in the premix layout, then B*P positions and B counts
-    # ... followed by x channel-innermost with Cin padded to 32
-    want = (r256(9 * 16 * 32 * 4 * 2) + r256(2 * 9 * 16 * 32 * 2) + r256(r256((2 * 64 + 2) * 4) + 2 * 64 * 32 * 2))
+    # packed bank and W_b in the premix layout; the one-pass band kernel
+    # (3x3, stride 1, pad 1, W % 8 == 0, Cin and Cout <= 64) needs nothing more
+    want = r256(9 * 16 * 32 * 4 * 2) + r256(2 * 9 * 16 * 32 * 2)
     assert bd.dynconv_forward_sparse_workspace_bytes(d) == want
+    # other layers add B*P positions and B counts, then x channel-innermost
+    # with Cin padded to 32 (here 7-wide rows: P = 56)
+    assert bd.dynconv_forward_sparse_workspace_bytes(good_desc(W=7)) == (
+        r256(9 * 16 * 32 * 4 * 2) + r256(2 * 9 * 16 * 32 * 2) + r256(r256((2 * 56 + 2) * 4) + 2 * 56 * 32 * 2))
     assert fs(m=None) == bd.DYNCONV_ERR_INVALID_ARG
     assert fs(res=2) == bd.DYNCONV_ERR_INVALID_ARG
     assert fs(y=X) == bd.DYNCONV_ERR_INVALID_ARG                                   # y overlaps x
@@ -405,6 +409,33 @@ def test_forward_sparse_checks():
     assert bd.dynconv_forward_sparse_workspace_bytes(good_desc(groups=16, Cin=16, Cout=16)) == 0
 
 
+def test_forward_sparse_packed_checks():
+    L = _lib()
+    d = good_desc()
+    r256 = lambda v: (v + 255) // 256 * 256
+    X, Y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+
+    def fs(desc=d, x=X, pk=FAKE, a=FAKE, m=FAKE, res=0, y=Y, wsp=FAKE, wsb=None):
+        if wsb is None:
+            wsb = bd.dynconv_forward_sparse_packed_workspace_bytes(desc)
+        return L.dynconv_forward_sparse_packed(ctypes.byref(desc), x, pk, a, m, res, y, wsp, wsb, None)
+
+    # W_b in the premix layout only (the bank is the caller's); the layers the
+    # one-pass band kernel does not take add the compacted positions and x
+    want = r256(2 * 9 * 16 * 32 * 2)
+    assert bd.dynconv_forward_sparse_packed_workspace_bytes(d) == want
+    assert bd.dynconv_forward_sparse_packed_workspace_bytes(good_desc(W=7)) == (
+        want + r256(r256((2 * 56 + 2) * 4) + 2 * 56 * 32 * 2))
+    assert fs(pk=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fs(pk=ctypes.c_void_p(FAKE.value + 8)) == bd.DYNCONV_ERR_INVALID_ARG  # misaligned bank
+    assert fs(res=2) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fs(y=X) == bd.DYNCONV_ERR_INVALID_ARG
+    assert fs(wsb=want - 1) == bd.DYNCONV_ERR_WORKSPACE
+    assert fs(desc=good_desc(dtype=bd.DYNCONV_F32), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert fs(desc=good_desc(Cout=32), res=1, wsb=1 << 30) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bd.dynconv_forward_sparse_packed_workspace_bytes(good_desc(groups=16, Cin=16, Cout=16)) == 0
+
+
 # ---- the binding's argument checks ---------------------------------------
 # The C ABI reads and writes through raw pointers sized from the descriptor,
 # so the binding checks every tensor against the call before handing it
@@ -416,7 +447,7 @@ COMPUTE_ENTRY_POINTS = {
     "dynconv_route", "dynconv_mix", "dynconv_forward", "dynconv_pack_experts",
     "dynconv_forward_packed", "dynconv_route_attn", "dynconv_forward_attn",
     "dynconv_backward_data", "dynconv_backward_weights", "dynconv_route_backward",
-    "dynconv_forward_sparse",
+    "dynconv_forward_sparse", "dynconv_forward_sparse_packed",
 }
 
 
@@ -507,6 +538,12 @@ def test_binding_rejects_mismatched_attention_and_sparse_arguments(no_compute):
         bd.dynconv_forward_sparse(x, e, a, _t((2, 8, 8), f32), 1, 1)   # mask must be uint8
     with pytest.raises(ValueError, match="mask"):
         bd.dynconv_forward_sparse(x, e, a, _t((2, 8, 7), torch.uint8), 1, 1)
+    d = good_desc()
+    pk = torch.zeros(bd.dynconv_packed_experts_bytes(d), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="packed"):
+        bd.dynconv_forward_sparse_packed(d, x, pk[:-16], a, _t((2, 8, 8), torch.uint8))
+    with pytest.raises(ValueError, match="mask"):
+        bd.dynconv_forward_sparse_packed(d, x, pk, a, _t((2, 8, 8), f32))
 
 
 def test_binding_rejects_mismatched_gradient_arguments(no_compute):
