@@ -16,9 +16,11 @@
 // its channels and flipped in its taps (flip_experts_kernel) and padding
 // k - 1 - p. The kernel gradient is a GEMM per example (M = output
 // channels, N = kernel columns (c, u, v), reduction over output positions)
-// on the matrix cores (depthwise: per-plane tap sums on the VALU); dW_b goes
-// to an fp32 workspace, and one pass over it (contract_kernel) yields dE
-// and per-chunk partial sums of dalpha, which a small kernel reduces.
+// on the matrix cores (depthwise: per-plane tap sums on the VALU). For bf16
+// stride-1 layers with n <= 4 and 1 x 1 or k x 3 kernels the contraction is
+// fused into that GEMM (wgrad_fused.hip); elsewhere dW_b goes to an fp32
+// workspace, and one pass over it (contract_kernel) yields dE and per-chunk
+// partial sums of dalpha, which a small kernel reduces.
 #include <algorithm>
 
 #include "common.hpp"
@@ -425,13 +427,16 @@ __global__ __launch_bounds__(256) void dE_reduce_kernel(const float *__restrict_
     de[j] = s;
 }
 
-// dalpha[b][i] = sum over chunks of dpart[b][i][ch]: one wave per (b, i);
-// lane l adds chunks l, l + 64, ... in order, then a fixed-tree wave sum.
+// dalpha[b][i] = sum over chunks of dpart[b * rows + i][ch] (rows >= n
+// expert rows per example): one wave per (b, i); lane l adds chunks l,
+// l + 64, ... in order, then a fixed-tree wave sum.
 __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float *__restrict__ dpart,
-                                                            float *__restrict__ dalpha, int total, int nch) {
+                                                            float *__restrict__ dalpha, int total, int nch, int n,
+                                                            int rows) {
     const int idx = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (idx >= total) return;
-    const float *p = dpart + (long)idx * nch;
+    const int b = idx / n, i = idx - b * n;
+    const float *p = dpart + ((long)b * rows + i) * nch;
     float s = 0.f;
     for (int c = lane; c < nch; c += 64) s += p[c];
     s = wave_sum(s);
@@ -596,13 +601,17 @@ hipError_t launch_contract(const Geom &g, const float *dwb, const void *experts,
 }
 }  // namespace
 
-size_t wgrad_bytes(const Geom &g) { return dwb_bytes(g) + dpart_bytes(g) + dep_bytes(g); }
+size_t wgrad_bytes(const Geom &g) {
+    if (const size_t f = wgrad_fused_bytes(g)) return f;
+    return dwb_bytes(g) + dpart_bytes(g) + dep_bytes(g);
+}
 
 bool wgrad_dw_supported(const Geom &g) { return g.KT <= kDwTaps; }
 
 hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy, const void *experts,
                                    const float *alpha, float *dwb, float *dalpha, float *dexperts,
                                    hipStream_t stream) {
+    if (wgrad_fused_bytes(g)) return launch_wgrad_fused(g, x, dy, experts, alpha, dwb, dalpha, dexperts, stream);
     WgArgs a;
     a.B = g.B; a.Cin = g.Cin; a.H = g.H; a.W = g.W; a.Cout = g.Cout; a.KW = g.KW;
     a.stride = g.stride; a.pad = g.pad; a.Ho = g.Ho; a.Wo = g.Wo; a.P = g.P; a.KT = g.KT;
@@ -654,16 +663,23 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
                : launch_contract<float>(g, dwb, experts, alpha, dep, dpart, stream);
     if (e != hipSuccess) return e;
     if (dexperts && groups > 1) {
-        const long total = (long)g.n * bank_elems(g);
-        hipLaunchKernelGGL(dE_reduce_kernel, dim3(blocks_for(total)), dim3(256), 0, stream, dep, dexperts, total,
-                           groups);
-        e = hipGetLastError();
+        e = launch_dE_reduce(dep, dexperts, (long)g.n * bank_elems(g), groups, stream);
         if (e != hipSuccess) return e;
     }
     if (!dalpha) return hipSuccess;
-    const int total = g.B * g.n;
+    return launch_dalpha_reduce(dpart, dalpha, g.B, g.n, g.n, contract_chunks(g), stream);
+}
+
+hipError_t launch_dE_reduce(const float *dep, float *de, long total, int groups, hipStream_t stream) {
+    hipLaunchKernelGGL(dE_reduce_kernel, dim3(blocks_for(total)), dim3(256), 0, stream, dep, de, total, groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_dalpha_reduce(const float *dpart, float *dalpha, int B, int n, int rows, int nch,
+                                hipStream_t stream) {
+    const int total = B * n;
     hipLaunchKernelGGL(dalpha_reduce_kernel, dim3((unsigned)ceil_div(total, 4)), dim3(256), 0, stream, dpart, dalpha,
-                       total, contract_chunks(g));
+                       total, nch, n, rows);
     return hipGetLastError();
 }
 

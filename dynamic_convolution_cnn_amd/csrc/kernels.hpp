@@ -158,6 +158,18 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
                                    const float *alpha, float *dwb, float *dalpha, float *dexperts,
                                    hipStream_t stream);
 
+// The fused kernel gradient (wgrad_fused.hip: bf16, groups == 1, stride 1,
+// n <= 4, 1 x 1 or k x 3 kernels; dW_b never stored): its scratch bytes,
+// 0 where it does not apply, and its launch with that scratch.
+size_t wgrad_fused_bytes(const Geom &g);
+hipError_t launch_wgrad_fused(const Geom &g, const void *x, const void *dy, const void *experts, const float *alpha,
+                              float *scratch, float *dalpha, float *dexperts, hipStream_t stream);
+// de[j] = sum over groups of dep[g * total + j]; dalpha[b * n + i] = sum over
+// chunks ch < nch of dpart[(b * rows + i) * nch + ch] (in chunk order).
+hipError_t launch_dE_reduce(const float *dep, float *de, long total, int groups, hipStream_t stream);
+hipError_t launch_dalpha_reduce(const float *dpart, float *dalpha, int B, int n, int rows, int nch,
+                                hipStream_t stream);
+
 // Routing gradient: gap (B*Cin), dz (B*n) and dgap (B*Cin) are scratch;
 // dfc_w[n][Cin], dfc_b[n] (may be null) are written; when dx is not null,
 // dgap[b][c] / (H W) is added to every position of dx[b][c] (one rounding

@@ -68,6 +68,12 @@ BWD_CASES = [
     (2, 10, 10, 12, 12, 5, 3, 2, 10, 4, "bf16"),    # depthwise 5x5, stride 3
     (2, 8, 8, 12, 12, 7, 1, 3, 8, 3, "bf16"),       # depthwise 7x7 (bounds-checked kernel)
     (2, 64, 64, 20, 20, 3, 1, 1, 1, 4, "bf16"),     # 3x3 kernel gradient in two row bands (12 + 8 rows)
+    # the fused kernel gradient (bf16, stride 1, n <= 4, Wo even): 5x5 with 3
+    # experts, one expert over two 64-channel output tiles, a 1x1 layer whose
+    # 72 columns span two column tiles
+    (2, 24, 40, 13, 12, 5, 1, 2, 1, 3, "bf16"),
+    (3, 20, 70, 9, 10, 3, 1, 1, 1, 1, "bf16"),
+    (5, 72, 16, 6, 6, 1, 1, 0, 1, 2, "bf16"),
 ]
 
 # Batches of 9 or more examples split the contraction of dW_b into example
@@ -111,6 +117,24 @@ def test_backward_data_both_policies(policy):
     torch.cuda.synchronize()
     rx, _, _ = oracle.backward(x, e, a, dy, 1, 1, 1, want=("dx",))
     check(from_dev(dx), rx, TOL["bf16"], f"dx policy {policy}")
+
+
+def test_fused_kernel_gradient_partial_outputs():
+    """dalpha alone and dexperts alone are bitwise the full call's (fused kernel gradient)."""
+    case = (12, 40, 72, 16, 16, 3, 1, 1, 1, 4, "bf16")
+    B, Cin, Cout, H, W, k, st, p, g, n, dtype = case
+    x, e, a, dy = _layer_inputs(case, seed=21)
+    say("fused kernel gradient partial outputs")
+    xd, ed, ad, dyd = to_dev(x, dtype), to_dev(e, dtype), to_dev(a, "f32"), to_dev(dy, dtype)
+    da, de = bd.dynconv_backward_weights(xd, dyd, ed, ad, st, p, g)
+    da_only, none1 = bd.dynconv_backward_weights(xd, dyd, ed, ad, st, p, g, want=("dalpha",))
+    none2, de_only = bd.dynconv_backward_weights(xd, dyd, ed, ad, st, p, g, want=("dexperts",))
+    torch.cuda.synchronize()
+    assert none1 is None and none2 is None
+    assert torch.equal(da, da_only) and torch.equal(de, de_only)
+    _, ra, re = oracle.backward(x, e, a, dy, st, p, g)
+    check(from_dev(da), ra, GRAD_TOL[dtype], "dalpha fused")
+    check(from_dev(de), re, GRAD_TOL[dtype], "dexperts fused")
 
 
 def test_backward_weights_stride2_and_partial_outputs():
