@@ -140,10 +140,14 @@ __device__ __forceinline__ float add_ror(float k, int ctrl4or8) {
     return k + __builtin_bit_cast(float, r);
 }
 
+// LDS pitch (elements) of a staged dy row of a chunk: an odd number of
+// 16-byte units, so that the A reads of 16 consecutive rows hit distinct banks
+constexpr int wf_apitch(int ns) { return ns * 16 + 8; }
+
 // NS products of 16 positions per stage, KW kernel columns, XL staged x
-// chunks per thread per stage. Dynamic LDS: the x copies [KW][CS], the E
-// slots, then the row sums of <dW_b, E_i> of the group's examples
-// [example][wave][row][i].
+// chunks per thread per stage. Dynamic LDS: the x copies [KW][CS], the dy
+// rows of the workgroup's 64 output channels [64][wf_apitch(NS)], then the
+// row sums of <dW_b, E_i> of the group's examples [example][wave][row][i].
 template <int NS, int KW, int XL>
 __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__restrict__ xq,
                                                           const uint16_t *__restrict__ dyq,
@@ -151,8 +155,15 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
                                                           const float *__restrict__ alpha, float *__restrict__ de,
                                                           float *__restrict__ dpart, WfArgs a) {
     constexpr int NE = kWfNE;
-    constexpr int LEN = NS * 16;  // padded positions of a chunk
+    constexpr int LEN = NS * 16;             // padded positions of a chunk
+    constexpr int AP = wf_apitch(NS);        // LDS pitch of a dy row
+    constexpr int JW = NS == 14 ? 32 : 16;   // threads per dy row in the staging (LEN / 8 of them load)
+    constexpr int RSTEP = 256 / JW;          // rows per staging step
+    constexpr int NDY = kWfOT / RSTEP;       // staging steps (16-byte dy chunks per thread)
+    static_assert(LEN / 8 <= JW && NDY * RSTEP == kWfOT, "dy staging layout");
     extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];
+    uint16_t *s_a = s_x + KW * a.CS;
+    float *s_p = reinterpret_cast<float *>(s_a + kWfOT * AP);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     // XCD-aware: consecutive logical ids (one example group's tiles) share an XCD
     const int total = a.ntiles * a.groups;
@@ -175,35 +186,30 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
     const int c = col_ok ? col / a.KT : c_lo, t = col_ok ? col - c * a.KT : 0;
     const int u = t / KW, v = t - u * KW;
     const int boff = (v * a.CS + (c - c_lo) * a.PL + u * a.Wp + 8 * hh) * 2;  // bytes
-    // the lane's A row: output channel o (rows past Cout read channel Cout - 1; E is 0 there)
-    const int oa = min(o0 + 32 * ob + l32, a.Cout - 1);
+    // the lane's A row: staged dy row 32 ob + l32 (output channel o0 + 32 ob + l32)
+    const int aoff = ((32 * ob + l32) * AP + 8 * hh) * 2;  // bytes
     // D(lane, 4j + q): output channel o0 + 32 ob + 8j + 4hh + q, column col.
-    // The lane's E values, as bf16 pairs (element 2k in the low half), sit in
-    // LDS after the x copies: 16-byte slot (i, h) of thread tid holds pairs
-    // 4h .. 4h + 3 of expert i (zeros for i >= n). Masked buffer reads (zeros
-    // outside the bank) let all the loads issue together.
-    u32x4_t *s_e = reinterpret_cast<u32x4_t *>(s_x + KW * a.CS);
-    float *s_p = reinterpret_cast<float *>(s_e + 2 * NE * 256);
+    // The lane's E values as bf16 pairs (element 2k in the low half); masked
+    // buffer reads (zeros outside the bank) so that all the loads issue together.
+    uint32_t er[NE][8];
     float dea[NE][16];
     {
         const auto rs_e = wf_rsrc(ex, (long)a.n * a.Cout * a.Kdim * 2);
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
-            uint32_t w[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                w[k] = 0u;
+                uint32_t w = 0u;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int kk = 2 * k + h;
                     const int o = o0 + 32 * ob + 8 * (kk >> 2) + 4 * hh + (kk & 3);
                     const int off =
                         o < a.Cout && col_ok && i < a.n ? ((i * a.Cout + o) * a.Kdim + col) * 2 : kWfMasked;
-                    w[k] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs_e, off, 0, 0) << (16 * h);
+                    w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs_e, off, 0, 0) << (16 * h);
                 }
+                er[i][k] = w;
             }
-            s_e[(2 * i) * 256 + tid] = u32x4_t{w[0], w[1], w[2], w[3]};
-            s_e[(2 * i + 1) * 256 + tid] = u32x4_t{w[4], w[5], w[6], w[7]};
 #pragma unroll
             for (int k = 0; k < 16; ++k) dea[i][k] = 0.f;
         }
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
     // whose dy is zero) and the slots of channels past Cin hold zeros
     for (int i = tid; i < KW * a.CS / 8; i += 256) reinterpret_cast<u32x4_t *>(s_x)[i] = u32x4_t{0u, 0u, 0u, 0u};
 
-    // the thread's staging items (channel slot, 16-byte chunk); threads past
+    // the thread's x staging items (channel slot, 16-byte chunk); threads past
     // the items load a repeated one (in bounds) and store nothing
     int xl_off[XL], xs_off[XL];  // global (bytes, within the stage's window) and LDS (elements) offsets
 #pragma unroll
@@ -225,41 +231,42 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
         xl_off[m] = (cl * Px + 8 * k) * 2;
         xs_off[m] = cl * a.PL + 8 * k;
     }
-    int dl_off = (oa * a.nchunk * LEN + 8 * hh) * 2;  // the lane's dy row, bytes
+    // the thread's dy staging: chunk j of rows r0 + RSTEP m (rows past Cout
+    // repeat row Cout - 1; lanes with j >= LEN / 8 read zeros and store nothing)
+    const int dj = tid % JW, dr = tid / JW;
+    const bool dj_ok = dj < LEN / 8;
+    const int rowb = a.nchunk * LEN * 2;  // bytes between dy rows of one example
+    int dl_off[NDY];
+#pragma unroll
+    for (int m = 0; m < NDY; ++m)
+        dl_off[m] = dj_ok ? min(o0 + dr + RSTEP * m, a.Cout - 1) * rowb + dj * 16 : kWfMasked;
+    const int ds_off = dr * AP + 8 * dj;  // LDS elements
     // stage (b, ch): uniform byte offsets of its x window and dy runs
     auto x_soff = [&](int b, int ch) { return (int)((((long)b * a.Cin + c_lo) * Px + (long)ch * a.R * a.Wp) * 2); };
     auto dy_soff = [&](int b, int ch) { return (int)((((long)b * a.Cout * a.nchunk) + ch) * LEN * 2); };
     // chunk k of the window, and for KW == 3 the first word of chunk k + 1
-    // (all that the shifts by 1 and 2 take from it)
+    // (all that the shifts by 1 and 2 take from it); the dy chunks
     u32x4_t xv[XL];
     uint32_t xw[XL];
-    auto load_x = [&](int so) {
+    u32x4_t dv[NDY];
+    auto load_stage = [&](int b, int ch) {
+        const int so = x_soff(b, ch);
 #pragma unroll
         for (int m = 0; m < XL; ++m) {
             xv[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xl_off[m], so, 0));
             if (KW == 3) xw[m] = __builtin_amdgcn_raw_buffer_load_b32(rs_x, xl_off[m] + 16, so, 0);
         }
+        const int sd = dy_soff(b, ch);
+#pragma unroll
+        for (int m = 0; m < NDY; ++m)
+            dv[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_dy, dl_off[m], sd, 0));
     };
     const int nstages = (b_hi - b_lo) * a.nchunk;
-    // the first stage's operands, issued in the loop's order (x, then dy)
-    u32x4_t av[NS];
-    load_x(x_soff(b_lo, 0));
-    __builtin_amdgcn_sched_barrier(0);
-    {
-        const int so = dy_soff(b_lo, 0);
-#pragma unroll
-        for (int k = 0; k < NS; ++k)
-            av[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_dy, dl_off + 32 * k, so, 0));
-    }
+    load_stage(b_lo, 0);
     f32x16_t acc = {};
     int b = b_lo, ch = 0;
     for (int st = 0; st < nstages; ++st) {
-        // opaque each stage, so that offset + constant stays one register and
-        // an instruction offset instead of a hoisted register per constant
-        asm volatile("" : "+v"(dl_off));
-#pragma unroll
-        for (int m = 0; m < XL; ++m) asm volatile("" : "+v"(xl_off[m]));
-        __syncthreads();  // zero fill / the previous stage's x reads are done
+        __syncthreads();  // zero fill / the previous stage's LDS reads are done
 #pragma unroll
         for (int m = 0; m < XL; ++m) {
             if (tid + 256 * m < nitems) {
@@ -276,40 +283,52 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
                 }
             }
         }
+        if (dj_ok) {
+#pragma unroll
+            for (int m = 0; m < NDY; ++m) *reinterpret_cast<u32x4_t *>(s_a + ds_off + RSTEP * m * AP) = dv[m];
+        }
         __syncthreads();
-        // the next stage (past the last one: the group's first again, never used):
-        // its x chunks and, product by product, its dy operands
+        // the next stage's operands (past the last stage: the group's first
+        // again, never used) load during this stage's products
         const bool last = ch + 1 == a.nchunk;
         int b1 = last ? b + 1 : b, ch1 = last ? 0 : ch + 1;
         if (st + 1 == nstages) b1 = b_lo;
-        load_x(x_soff(b1, ch1));
-        const int so1 = dy_soff(b1, ch1);
+        load_stage(b1, ch1);
+        __builtin_amdgcn_sched_barrier(0);
+        const char *pa = reinterpret_cast<const char *>(s_a) + aoff;
         const char *pb = reinterpret_cast<const char *>(s_x) + boff;
-        bf16x8_t fb0 = *reinterpret_cast<const bf16x8_t *>(pb);
-        bf16x8_t fb1 = *reinterpret_cast<const bf16x8_t *>(pb + 32);
+        bf16x8_t fa0 = *reinterpret_cast<const bf16x8_t *>(pa), fb0 = *reinterpret_cast<const bf16x8_t *>(pb);
+        bf16x8_t fa1 = *reinterpret_cast<const bf16x8_t *>(pa + 32), fb1 = *reinterpret_cast<const bf16x8_t *>(pb + 32);
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            const bf16x8_t cb = fb0;
+            const bf16x8_t ca = fa0, cb = fb0;
+            fa0 = fa1;
             fb0 = fb1;
-            if (k + 2 < NS) fb1 = *reinterpret_cast<const bf16x8_t *>(pb + 32 * (k + 2));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[k]), cb, acc, 0, 0, 0);
-            av[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_dy, dl_off + 32 * k, so1, 0));
+            if (k + 2 < NS) {
+                fa1 = *reinterpret_cast<const bf16x8_t *>(pa + 32 * (k + 2));
+                fb1 = *reinterpret_cast<const bf16x8_t *>(pb + 32 * (k + 2));
+            }
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, cb, acc, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (last) {
-            // contraction with example b's attentions (zero for i >= n)
+            // contraction with example b's attentions (zero for i >= n); the
+            // packed E words count as changed here, so that their unpacking
+            // stays in the contraction instead of living as 16 NE floats
+#pragma unroll
+            for (int i = 0; i < NE; ++i)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(er[i][k]));
             float p[NE];
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
                 const float al0 = alpha[(long)b * a.n + min(i, a.n - 1)];
                 const float al = i < a.n ? al0 : 0.f;
-                const u32x4_t e0 = s_e[(2 * i) * 256 + tid], e1 = s_e[(2 * i + 1) * 256 + tid];
-                const uint32_t er[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
                 float s = 0.f;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
                     dea[i][k] = fmaf(al, acc[k], dea[i][k]);
-                    s = fmaf(acc[k], (k & 1) ? bf16_hi(er[k >> 1]) : bf16_lo(er[k >> 1]), s);
+                    s = fmaf(acc[k], (k & 1) ? bf16_hi(er[i][k >> 1]) : bf16_lo(er[i][k >> 1]), s);
                 }
                 p[i] = s;
             }
@@ -361,8 +380,7 @@ struct WfPlan {
     size_t lds;
     int ns, xl;
 };
-constexpr size_t kWfLds = 80 * 1024;             // two workgroups per compute unit
-constexpr size_t kWfE = (size_t)kWfNE * 2 * 256 * 16;  // LDS bytes of the E slots
+constexpr size_t kWfLds = 80 * 1024;  // two workgroups per compute unit
 
 // Worst bank-conflict degree of the B reads (64 banks of 4 bytes, 16 lanes
 // per pass) over the first k-tiles, for window stride PL and copy stride CS.
@@ -401,7 +419,8 @@ bool wf_plan_uncached(const Geom &g, WfPlan &pl) {
         for (int R = std::min(g.Ho, NS * 16 / a.Wp); R >= 1; --R) {
             const int pln = (g.KH - 1) * a.Wp + 16 * NS;
             const int xchunks = (R + g.KH - 1) * a.Wp / 8;
-            if ((size_t)g.KW * (a.nch * (pln + 64) + 64) * 2 + kWfE + 64 * 256 > kWfLds || a.nch * xchunks > 256 * 2)
+            if ((size_t)g.KW * (a.nch * (pln + 64) + 64) * 2 + (size_t)kWfOT * wf_apitch(NS) * 2 + 64 * 256 > kWfLds ||
+                a.nch * xchunks > 256 * 2)
                 continue;
             const long cost = (long)ceil_div(g.Ho, R) * NS;
             if (best < 0 || cost < best) {
@@ -429,7 +448,7 @@ bool wf_plan_uncached(const Geom &g, WfPlan &pl) {
             const int cf = wf_conflicts(a, PL, CS);
             if (cf < bestc) { bestc = cf; a.PL = PL; a.CS = CS; }
         }
-    const size_t fixed = (size_t)g.KW * a.CS * 2 + kWfE;
+    const size_t fixed = (size_t)g.KW * a.CS * 2 + (size_t)kWfOT * wf_apitch(pl.ns) * 2;
     // row sums of at most this many examples fit beside the windows
     const int bmax = (int)((kWfLds - fixed) / 256);
     // one group's dE partial sums (written, then read) in example-steps of
