@@ -429,7 +429,8 @@ __global__ __launch_bounds__(256) void dE_reduce_kernel(const float *__restrict_
 
 // dalpha[b][i] = sum over chunks of dpart[b * rows + i][ch] (rows >= n
 // expert rows per example): one wave per (b, i); lane l adds chunks l,
-// l + 64, ... in order, then a fixed-tree wave sum.
+// l + 64, ... into four partial sums (chunk l + 64 m goes to sum m % 4) in
+// order, then adds them and a fixed-tree wave sum.
 __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float *__restrict__ dpart,
                                                             float *__restrict__ dalpha, int total, int nch, int n,
                                                             int rows) {
@@ -437,9 +438,17 @@ __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float *__restr
     if (idx >= total) return;
     const int b = idx / n, i = idx - b * n;
     const float *p = dpart + ((long)b * rows + i) * nch;
-    float s = 0.f;
-    for (int c = lane; c < nch; c += 64) s += p[c];
-    s = wave_sum(s);
+    // four independent partial sums (their loads in flight together), fixed order
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int c = lane;
+    for (; c + 192 < nch; c += 256) {
+        s0 += p[c];
+        s1 += p[c + 64];
+        s2 += p[c + 128];
+        s3 += p[c + 192];
+    }
+    for (; c < nch; c += 64) s0 += p[c];
+    float s = wave_sum((s0 + s1) + (s2 + s3));
     if (lane == 0) dalpha[idx] = s;
 }
 

@@ -65,7 +65,8 @@ struct WfArgs {
 
 // dyq[b][o][ch][j] (j < len = NS * 16): dy[b][o][ch R + j / Wp][j % Wp]
 // where j < R Wp, the row is below Ho and j % Wp < Wo, else 0; one thread per
-// 8 output elements.
+// 8 output elements (one row segment: Wp is a multiple of 8), read as 4
+// element pairs (Wo is even, so a pair is all in the row or all out).
 __global__ __launch_bounds__(256) void pad_dy_kernel(const uint16_t *__restrict__ dy, uint16_t *__restrict__ dyq,
                                                      long nvec, int Ho, int Wo, int Wp, int R, int nchunk, int len) {
     const long v = (long)blockIdx.x * 256 + threadIdx.x;
@@ -75,43 +76,53 @@ __global__ __launch_bounds__(256) void pad_dy_kernel(const uint16_t *__restrict_
     const int j0 = (int)(v - run * per_chunk) * 8;
     const long bo = run / nchunk;
     const int ch = (int)(run - bo * nchunk);
-    const uint16_t *src = dy + bo * Ho * Wo;
+    const int r = j0 / Wp, s0 = j0 - r * Wp, row = ch * R + r;
+    const bool rin = j0 < R * Wp && row < Ho;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(dy + bo * Ho * Wo + (long)(rin ? row : 0) * Wo);
     uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t pr = 0u;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int j = j0 + 2 * k + h;
-            const int r = j / Wp, sc = j - r * Wp, row = ch * R + r;
-            const uint32_t e = (j < R * Wp && row < Ho && sc < Wo) ? src[row * Wo + sc] : 0u;
-            pr |= e << (16 * h);
-        }
-        w[k] = pr;
-    }
+    for (int k = 0; k < 4; ++k) w[k] = rin && s0 + 2 * k < Wo ? src[(s0 >> 1) + k] : 0u;
     reinterpret_cast<u32x4_t *>(dyq)[v] = u32x4_t{w[0], w[1], w[2], w[3]};
 }
 
 // xq[b][c][h'][w'] = x[b][c][h' - pad][w' - pad] inside the image, else 0
-// (Hx rows of Wp); one thread per 8 output elements.
+// (Hx rows of Wp); one thread per 8 output elements. For even W the source
+// is read as element pairs (and, for odd pad, each output pair joins the
+// halves of two source pairs).
 __global__ __launch_bounds__(256) void pad_x_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ xq,
                                                     long nvec, int H, int W, int Hx, int Wp, int pad) {
     const long v = (long)blockIdx.x * 256 + threadIdx.x;
     if (v >= nvec) return;
     const int per_row = Wp / 8;
     const long row = v / per_row;  // (b, c, h')
-    const int w0 = (int)(v - row * per_row) * 8 - pad;
+    const int w0 = (int)(v - row * per_row) * 8 - pad;  // source column of output element 0
     const long bc = row / Hx;
     const int h = (int)(row - bc * Hx) - pad;
     const bool hin = h >= 0 && h < H;
     const uint16_t *src = x + (bc * H + (hin ? h : 0)) * W;
     uint32_t w[4];
+    if ((W & 1) == 0) {
+        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src);
+        // source pairs starting at an even column e: all in or all out of the row
+        auto pr = [&](int e) { return hin && e >= 0 && e < W ? s32[e >> 1] : 0u; };
+        if ((pad & 1) == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int a0 = w0 + 2 * j, a1 = a0 + 1;
-        const uint32_t lo = hin && a0 >= 0 && a0 < W ? src[a0] : 0u;
-        const uint32_t hi = hin && a1 >= 0 && a1 < W ? src[a1] : 0u;
-        w[j] = lo | (hi << 16);
+            for (int j = 0; j < 4; ++j) w[j] = pr(w0 + 2 * j);
+        } else {
+            uint32_t d[5];
+#pragma unroll
+            for (int m = 0; m < 5; ++m) d[m] = pr(w0 - 1 + 2 * m);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_alignbit(d[j + 1], d[j], 16);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int a0 = w0 + 2 * j, a1 = a0 + 1;
+            const uint32_t lo = hin && a0 >= 0 && a0 < W ? src[a0] : 0u;
+            const uint32_t hi = hin && a1 >= 0 && a1 < W ? src[a1] : 0u;
+            w[j] = lo | (hi << 16);
+        }
     }
     reinterpret_cast<u32x4_t *>(xq)[v] = u32x4_t{w[0], w[1], w[2], w[3]};
 }
@@ -155,6 +166,7 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
                                                           const float *__restrict__ alpha, float *__restrict__ de,
                                                           float *__restrict__ dpart, WfArgs a) {
     constexpr int NE = kWfNE;
+    constexpr bool EF32 = NS == 14 && KW == 3;  // E unpacked once (fits two waves per SIMD here)
     constexpr int LEN = NS * 16;             // padded positions of a chunk
     constexpr int AP = wf_apitch(NS);        // LDS pitch of a dy row
     constexpr int JW = NS == 14 ? 32 : 16;   // threads per dy row in the staging (LEN / 8 of them load)
@@ -308,17 +320,24 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
                 fa1 = *reinterpret_cast<const bf16x8_t *>(pa + 32 * (k + 2));
                 fb1 = *reinterpret_cast<const bf16x8_t *>(pb + 32 * (k + 2));
             }
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, cb, acc, 0, 0, 0);
+            if (k == 0 && a.nchunk == 1)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, cb, f32x16_t{}, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, cb, acc, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (last) {
-            // contraction with example b's attentions (zero for i >= n); the
-            // packed E words count as changed here, so that their unpacking
-            // stays in the contraction instead of living as 16 NE floats
+            // contraction with example b's attentions (zero for i >= n). With
+            // EF32 the unpacked E values stay live across the loop (fewer
+            // instructions per example); otherwise the packed words count as
+            // changed here, so that their unpacking stays in the contraction
+            // instead of living as 16 NE floats
+            if (!EF32) {
 #pragma unroll
-            for (int i = 0; i < NE; ++i)
+                for (int i = 0; i < NE; ++i)
 #pragma unroll
-                for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(er[i][k]));
+                    for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(er[i][k]));
+            }
             float p[NE];
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
@@ -342,7 +361,7 @@ __global__ __launch_bounds__(256) void wgrad_fused_kernel(const uint16_t *__rest
             r = add_ror(r, 4);
             r = add_ror(r, 8);
             if ((lane & 12) == 0) s_p[(((b - b_lo) * 4 + wave) * 4 + (lane >> 4)) * 4 + (lane & 3)] = r;
-            acc = f32x16_t{};
+            if (a.nchunk > 1) acc = f32x16_t{};
         }
         b = b1;
         ch = ch1;
