@@ -431,7 +431,9 @@ bool wf_plan_uncached(const Geom &g, WfPlan &pl) {
     a.B = g.B; a.Cin = g.Cin; a.H = g.H; a.W = g.W; a.Cout = g.Cout; a.KH = g.KH; a.KW = g.KW; a.pad = g.pad;
     a.Ho = g.Ho; a.Wo = g.Wo; a.KT = g.KT; a.Kdim = g.Cin * g.KT; a.n = g.n;
     a.Wp = (g.W + 2 * g.pad + 7) / 8 * 8;
-    a.nch = std::min(g.Cin, (kWfKT - 1) / g.KT + 2);
+    // the most channels 64 consecutive columns can span: the first starts at
+    // tap KT - 1 of its channel at worst, so 62 / KT + 2
+    a.nch = std::min(g.Cin, (kWfKT - 2) / g.KT + 2);
     long best = -1;
     int plane = 0;
     for (int NS : {14, 8}) {
