@@ -612,7 +612,7 @@ def train_main(args):
         "tflops_step": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "pct_bf16_peak_step": round(100 * step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "kernels_us": per,
-        "roofline": {"kernel": "dynconv_backward_weights (kernel-gradient GEMM; contraction of dW_b into dalpha, dE)",
+        "roofline": {"kernel": "dynconv_backward_weights (kernel-gradient GEMM with its contraction into dalpha, dE)",
                      "bound": "mfma", "achieved": round(bw_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bw_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }
