@@ -88,9 +88,10 @@ def _load():
     lib.oracle_forward_points.argtypes = [i32] * 11 + [P, P, P, i64, P, P]
     lib.oracle_forward_attn.argtypes = [i32] * 11 + [P, P, P, P, P, P]
     lib.oracle_backward.argtypes = [i32] * 11 + [P, P, P, P, P, P, P]
+    lib.oracle_backward_attn.argtypes = [i32] * 11 + [P] * 11
     for f in (lib.oracle_gap, lib.oracle_route, lib.oracle_mix, lib.oracle_conv,
               lib.oracle_forward, lib.oracle_forward_points, lib.oracle_forward_attn,
-              lib.oracle_backward):
+              lib.oracle_backward, lib.oracle_backward_attn):
         f.restype = i32
     _lib = lib
     return lib
@@ -275,6 +276,42 @@ def backward(x, experts, alpha, dy, stride: int = 1, pad: int = 0, groups: int =
                                  None if de is None else _ptr(de))
     _check(rc, "backward")
     return dx, da, de
+
+
+def backward_attn(x, experts, alpha, dy, a_in=None, a_out=None, stride: int = 1, pad: int = 0,
+                  groups: int = 1, want=("dx", "dalpha", "dexperts", "da_in", "da_out")):
+    """Gradients of the layer with FMDConv's channel attentions
+    (``forward_attn``; FMDConv: Fast multi-attention dynamic convolution,
+    abstract) for the output gradient dy: returns (dx, dalpha, dexperts,
+    da_in [B,Cin], da_out [B,Cout]) in float64, None where not in ``want``.
+    The derivative of y = a_out * conv(a_in * x, W_b), written out term by
+    term in ``dynconv_oracle.c``; a_in or a_out None means all ones."""
+    x = _f32(x)
+    experts = _f32(experts)
+    alpha = _f64(alpha)
+    dy = _f32(dy)
+    B, Cin, H, W = x.shape
+    n, Cout, cpg, kh, kw = experts.shape
+    assert alpha.shape == (B, n) and cpg * groups == Cin
+    ai = None if a_in is None else _f64(a_in)
+    ao = None if a_out is None else _f64(a_out)
+    if ai is not None:
+        assert ai.shape == (B, Cin)
+    if ao is not None:
+        assert ao.shape == (B, Cout)
+    Ho, Wo = out_size(H, kh, stride, pad), out_size(W, kw, stride, pad)
+    assert dy.shape == (B, Cout, Ho, Wo)
+    dx = np.empty(x.shape, np.float64) if "dx" in want else None
+    da = np.empty((B, n), np.float64) if "dalpha" in want else None
+    de = np.empty(experts.shape, np.float64) if "dexperts" in want else None
+    dai = np.empty((B, Cin), np.float64) if "da_in" in want else None
+    dao = np.empty((B, Cout), np.float64) if "da_out" in want else None
+    p = lambda a: None if a is None else _ptr(a)
+    rc = _load().oracle_backward_attn(B, Cin, H, W, Cout, kh, kw, stride, pad, groups, n,
+                                      _ptr(x), _ptr(experts), _ptr(alpha), p(ai), p(ao), _ptr(dy),
+                                      p(dx), p(da), p(de), p(dai), p(dao))
+    _check(rc, "backward_attn")
+    return dx, da, de, dai, dao
 
 
 def route_backward(x, fc_w, fc_b, dalpha, mode: int = SIGMOID, temperature: float = 1.0):

@@ -478,3 +478,115 @@ int oracle_backward(int B, int Cin, int H, int W, int Cout, int kh, int kw,
     free(wb);
     return ORACLE_OK;
 }
+
+/*
+ * Gradients of the layer with FMDConv's channel attentions
+ * (oracle_forward_attn; FMDConv: Fast multi-attention dynamic convolution,
+ * abstract) for a given output gradient dy. With
+ *   z[b,o,r,s] = sum_{c,u,v} W_b[o,c,u,v] * a_in[b,gc] * x[b,gc,h,w],
+ *   y[b,o,r,s] = a_out[b,o] * z[b,o,r,s],   W_b = sum_i alpha[b,i] E_i,
+ * the derivative of the loss sum(dy * y), term by term:
+ *   dW_b[o,c,u,v] = a_out[b,o] * a_in[b,gc] * sum_{r,s} dy[b,o,r,s] * x[b,gc,h,w]
+ *   dalpha[b,i]   = sum_e dW_b[e] * E_i[e],   dE_i[e] = sum_b alpha[b,i] * dW_b[e]
+ *   da_out[b,o]   = sum_{r,s} dy[b,o,r,s] * z[b,o,r,s]
+ *   da_in[b,gc]   = sum over (o, r, s, u, v) of dy[b,o,r,s] * a_out[b,o] * W_b[o,c,u,v] * x[b,gc,h,w]
+ *   dx[b,gc,h,w]  = a_in[b,gc] * sum over the (o, r, s, u, v) whose output read x[b,gc,h,w]
+ *                   of a_out[b,o] * W_b[o,c,u,v] * dy[b,o,r,s]
+ * (h = r*stride - pad + u, w = s*stride - pad + v; positions outside the image
+ * take no part). a_in or a_out may be NULL (all ones); each output may be
+ * NULL (not computed). da_in: [B,Cin]; da_out: [B,Cout]; the rest as
+ * oracle_backward.
+ */
+int oracle_backward_attn(int B, int Cin, int H, int W, int Cout, int kh, int kw,
+                         int stride, int pad, int groups, int n, const float *x,
+                         const float *experts, const double *alpha, const double *a_in,
+                         const double *a_out, const float *dy, double *dx,
+                         double *dalpha, double *dexperts, double *da_in, double *da_out)
+{
+    if (B < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || kh < 1 || kw < 1 ||
+        stride < 1 || pad < 0 || groups < 1 || n < 1 || !x || !experts ||
+        !alpha || !dy)
+        return ORACLE_BAD_ARG;
+    if (Cin % groups || Cout % groups) return ORACLE_BAD_ARG;
+    int Ho = out_size(H, kh, stride, pad), Wo = out_size(W, kw, stride, pad);
+    if (Ho < 1 || Wo < 1) return ORACLE_BAD_ARG;
+    int cpg = Cin / groups, opg = Cout / groups;
+    long per_o = (long)cpg * kh * kw;
+    long wsz = (long)Cout * per_o;
+    double *dwb = (double *)calloc((size_t)B * wsz, sizeof(double));
+    double *wb = (double *)malloc(sizeof(double) * (size_t)B * wsz);
+    if (!dwb || !wb) { free(dwb); free(wb); return ORACLE_BAD_ARG; }
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < B; ++b) {
+        double *w = wb + (long)b * wsz;
+        for (long e = 0; e < wsz; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i)
+                acc += alpha[(long)b * n + i] * (double)experts[(long)i * wsz + e];
+            w[e] = acc;
+        }
+        double *dw = dwb + (long)b * wsz;
+        double *dxb = dx ? dx + (long)b * Cin * H * W : NULL;
+        if (dxb)
+            for (long j = 0; j < (long)Cin * H * W; ++j) dxb[j] = 0.0;
+        if (da_in)
+            for (int c = 0; c < Cin; ++c) da_in[(long)b * Cin + c] = 0.0;
+        for (int o = 0; o < Cout; ++o) {
+            int g = o / opg;
+            double so = a_out ? a_out[(long)b * Cout + o] : 1.0;
+            double dso = 0.0; /* sum over (r, s) of dy * z */
+            for (int r = 0; r < Ho; ++r) {
+                for (int s = 0; s < Wo; ++s) {
+                    double d = (double)dy[(((long)b * Cout + o) * Ho + r) * Wo + s];
+                    double z = 0.0;
+                    for (int c = 0; c < cpg; ++c) {
+                        int gc = g * cpg + c;
+                        double si = a_in ? a_in[(long)b * Cin + gc] : 1.0;
+                        long xoff = (((long)b * Cin + gc) * H) * W;
+                        double dsi = 0.0;
+                        for (int u = 0; u < kh; ++u) {
+                            int h = r * stride - pad + u;
+                            if (h < 0 || h >= H) continue;
+                            for (int v = 0; v < kw; ++v) {
+                                int ww = s * stride - pad + v;
+                                if (ww < 0 || ww >= W) continue;
+                                long e = (long)o * per_o + ((long)c * kh + u) * kw + v;
+                                double xv = (double)x[xoff + (long)h * W + ww];
+                                z += w[e] * si * xv;
+                                dw[e] += so * si * d * xv;
+                                dsi += d * so * w[e] * xv;
+                                if (dxb)
+                                    dxb[xoff - (long)b * Cin * H * W + (long)h * W + ww] += si * so * w[e] * d;
+                            }
+                        }
+                        if (da_in) da_in[(long)b * Cin + gc] += dsi;
+                    }
+                    dso += d * z;
+                }
+            }
+            if (da_out) da_out[(long)b * Cout + o] = dso;
+        }
+        if (dalpha) {
+            for (int i = 0; i < n; ++i) {
+                double acc = 0.0;
+                for (long e = 0; e < wsz; ++e)
+                    acc += dw[e] * (double)experts[(long)i * wsz + e];
+                dalpha[(long)b * n + i] = acc;
+            }
+        }
+    }
+    if (dexperts) {
+#pragma omp parallel for schedule(static)
+        for (long e = 0; e < wsz; ++e) {
+            for (int i = 0; i < n; ++i) {
+                double acc = 0.0;
+                for (int b = 0; b < B; ++b)
+                    acc += alpha[(long)b * n + i] * dwb[(long)b * wsz + e];
+                dexperts[(long)i * wsz + e] = acc;
+            }
+        }
+    }
+    free(dwb);
+    free(wb);
+    return ORACLE_OK;
+}

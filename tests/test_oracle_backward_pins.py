@@ -14,7 +14,12 @@ operand fails at least one test:
 * Euler's identity for the bilinear layer:
   <dy, y> = <dx, x> = <dalpha, alpha> = <dE, E>;
 * closed forms of the routing derivative (sigmoid at zero logits, softmax
-  gradients that sum to zero, a constant attention gradient under softmax).
+  gradients that sum to zero, a constant attention gradient under softmax);
+* for the layer with FMDConv's channel attentions (``backward_attn``): torch
+  autograd through x * a_in, the mixed kernels, ``conv2d`` and * a_out,
+  Euler's identity over all five gradients (the layer is linear in each of
+  x, alpha, E, a_in and a_out), and the plain ``backward`` when both
+  attentions are ones.
 """
 import numpy as np
 import pytest
@@ -189,3 +194,63 @@ def test_route_backward_closed_forms():
     dfw, dfb, dgap, dx = oracle.route_backward(x, fw, None, const, oracle.SOFTMAX, 2.0)
     for v in (dfw, dfb, dgap, dx):
         assert np.max(np.abs(v)) < 1e-14
+
+
+# ---- FMDConv channel attentions -------------------------------------------------
+
+def _attn_inputs(case, seed=0):
+    B, Cin, Cout = case[0], case[1], case[2]
+    x, e, a, dy = _inputs(case, seed)
+    rng = np.random.default_rng(seed + 5)
+    return x, e, a, dy, rng.random((B, Cin)) + 0.5, rng.random((B, Cout)) + 0.5
+
+
+def _torch_attn_grads(x, e, a, dy, ai, ao, st, p, g):
+    """Reference gradients of <dy, a_out * conv(a_in * x, W_b)> from torch
+    autograd in float64 on the CPU."""
+    f64 = lambda v: torch.tensor(np.asarray(v, np.float64), requires_grad=True)
+    xt, et, at, it, ot = f64(x), f64(e), f64(a), f64(ai), f64(ao)
+    wb = torch.einsum("bi,i...->b...", at, et)
+    xs = xt * it[:, :, None, None]
+    ys = [F.conv2d(xs[b:b + 1], wb[b], stride=st, padding=p, groups=g) for b in range(x.shape[0])]
+    y = torch.cat(ys) * ot[:, :, None, None]
+    (y * torch.from_numpy(np.asarray(dy, np.float64))).sum().backward()
+    return xt.grad.numpy(), at.grad.numpy(), et.grad.numpy(), it.grad.numpy(), ot.grad.numpy()
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_backward_attn_matches_torch_autograd(case):
+    *_, st, p, g, n = case
+    x, e, a, dy, ai, ao = _attn_inputs(case, seed=30)
+    got = oracle.backward_attn(x, e, a, dy, ai, ao, st, p, g)
+    ref = _torch_attn_grads(x, e, a, dy, ai, ao, st, p, g)
+    for name, v, r in zip(("dx", "dalpha", "dexperts", "da_in", "da_out"), got, ref):
+        assert _rel(v, r) < 1e-12, name
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_backward_attn_euler_identity(case):
+    *_, st, p, g, n = case
+    x, e, a, dy, ai, ao = _attn_inputs(case, seed=40)
+    dx, da, de, dai, dao = oracle.backward_attn(x, e, a, dy, ai, ao, st, p, g)
+    y = oracle.forward_attn(x, e, a, ai, ao, st, p, g)
+    ref = float(np.sum(dy.astype(np.float64) * y))
+    scale = float(np.sum(np.abs(dy.astype(np.float64) * y)))
+    for v in (np.sum(dx * x), np.sum(da * a), np.sum(de * e), np.sum(dai * ai), np.sum(dao * ao)):
+        assert abs(float(v) - ref) <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("case", BWD_CASES[:4])
+def test_backward_attn_with_unit_attentions_is_backward(case):
+    *_, st, p, g, n = case
+    B, Cin, Cout = case[0], case[1], case[2]
+    x, e, a, dy = _inputs(case, seed=50)
+    plain = oracle.backward(x, e, a, dy, st, p, g)
+    none = oracle.backward_attn(x, e, a, dy, None, None, st, p, g)
+    ones = oracle.backward_attn(x, e, a, dy, np.ones((B, Cin)), np.ones((B, Cout)), st, p, g)
+    for u, v, w in zip(plain, none[:3], ones[:3]):
+        assert np.array_equal(u, v) and np.array_equal(u, w)
+    assert np.array_equal(none[3], ones[3]) and np.array_equal(none[4], ones[4])
+    # with unit attentions, da_out[b,o] is <dy, y> over channel o
+    y = oracle.forward(x, e, a, st, p, g)
+    assert _rel(none[4], np.sum(dy.astype(np.float64) * y, axis=(2, 3))) < 1e-12
