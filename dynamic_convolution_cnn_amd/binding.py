@@ -48,6 +48,8 @@ EXPORTED = (
     "dynconv_route_backward_workspace_bytes", "dynconv_forward_sparse",
     "dynconv_forward_sparse_workspace_bytes", "dynconv_forward_noalloc",
     "dynconv_forward_sparse_packed", "dynconv_forward_sparse_packed_workspace_bytes",
+    "dynconv_backward_weights_attn", "dynconv_backward_weights_attn_workspace_bytes",
+    "dynconv_backward_data_attn", "dynconv_backward_data_attn_workspace_bytes",
 )
 
 
@@ -135,6 +137,14 @@ def lib():
     L.dynconv_forward_sparse_packed_workspace_bytes.restype = sz
     L.dynconv_forward_noalloc.argtypes = [D, i32, P, P, P, P, P]
     L.dynconv_forward_noalloc.restype = i32
+    L.dynconv_backward_weights_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.dynconv_backward_weights_attn.restype = i32
+    L.dynconv_backward_weights_attn_workspace_bytes.argtypes = [D]
+    L.dynconv_backward_weights_attn_workspace_bytes.restype = sz
+    L.dynconv_backward_data_attn.argtypes = [D, i32, P, P, P, P, P, P, P, sz, P]
+    L.dynconv_backward_data_attn.restype = i32
+    L.dynconv_backward_data_attn_workspace_bytes.argtypes = [D, i32]
+    L.dynconv_backward_data_attn_workspace_bytes.restype = sz
     _lib = L
     return L
 
@@ -559,6 +569,72 @@ def dynconv_backward_weights(x: torch.Tensor, dy: torch.Tensor, experts: torch.T
                                           _ptr(alpha), _ptr(dalpha), _ptr(dexperts), _ptr(ws), ws_bytes,
                                           _stream(stream)), "dynconv_backward_weights")
     return dalpha, dexperts
+
+
+def dynconv_backward_weights_attn_workspace_bytes(desc: dynconv_desc_t) -> int:
+    return int(lib().dynconv_backward_weights_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def dynconv_backward_weights_attn(x: torch.Tensor, dy: torch.Tensor, experts: torch.Tensor,
+                                  alpha: torch.Tensor, a_in: Optional[torch.Tensor],
+                                  a_out: Optional[torch.Tensor], stride: int = 1, pad: int = 0,
+                                  groups: int = 1, want=("dalpha", "dexperts", "da_in", "da_out"),
+                                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """(dalpha [B, n], dexperts, da_in [B, Cin], da_out [B, Cout]), float32, of the layer
+    with channel attentions; an entry not in ``want`` is None."""
+    desc = layer_desc(x, experts, stride, pad, groups)
+    Ho, Wo = _out_hw(desc.H, desc.W, desc.kh, desc.kw, stride, pad)
+    _need(x, "x", (desc.B, desc.Cin, desc.H, desc.W))
+    _need(dy, "dy", (desc.B, desc.Cout, Ho, Wo), x.dtype)
+    _need(experts, "experts", tuple(experts.shape))
+    _need(alpha, "alpha", (desc.B, desc.n), F32)
+    _need(a_in, "a_in", (desc.B, desc.Cin), F32, optional=True)
+    _need(a_out, "a_out", (desc.B, desc.Cout), F32, optional=True)
+    _same_gpu(x=x, dy=dy, experts=experts, alpha=alpha, a_in=a_in, a_out=a_out)
+    mk = lambda name, shape: (torch.empty(shape, dtype=torch.float32, device=x.device)
+                              if name in want else None)
+    dalpha = mk("dalpha", (desc.B, desc.n))
+    dexperts = mk("dexperts", tuple(experts.shape))
+    da_in = mk("da_in", (desc.B, desc.Cin))
+    da_out = mk("da_out", (desc.B, desc.Cout))
+    ws, ws_bytes = _workspace(dynconv_backward_weights_attn_workspace_bytes(desc), x.device, workspace)
+    _check(lib().dynconv_backward_weights_attn(ctypes.byref(desc), _ptr(x), _ptr(dy), _ptr(experts),
+                                               _ptr(alpha), _ptr(a_in), _ptr(a_out), _ptr(dalpha),
+                                               _ptr(dexperts), _ptr(da_in), _ptr(da_out), _ptr(ws),
+                                               ws_bytes, _stream(stream)), "dynconv_backward_weights_attn")
+    return dalpha, dexperts, da_in, da_out
+
+
+def dynconv_backward_data_attn_workspace_bytes(desc: dynconv_desc_t, policy: int = DYNCONV_POLICY_AUTO) -> int:
+    return int(lib().dynconv_backward_data_attn_workspace_bytes(ctypes.byref(desc), int(policy)))
+
+
+def dynconv_backward_data_attn(dy: torch.Tensor, experts: torch.Tensor, alpha: torch.Tensor,
+                               a_in: Optional[torch.Tensor], a_out: Optional[torch.Tensor], H: int, W: int,
+                               stride: int = 1, pad: int = 0, groups: int = 1,
+                               policy: int = DYNCONV_POLICY_AUTO, dx: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Input gradient dx [B, Cin, H, W] of the layer with channel attentions."""
+    if dy.dim() != 4 or experts.dim() != 5:
+        raise ValueError("dy must be [B, Cout, Ho, Wo] and experts [n, Cout, Cin/groups, kh, kw]")
+    B = dy.shape[0]
+    n, Cout, cpg, kh, kw = experts.shape
+    desc = make_desc(B, cpg * groups, H, W, Cout, kh, kw, stride, pad, groups, n, _dtype_code(dy))
+    Ho, Wo = _out_hw(H, W, kh, kw, stride, pad)
+    _need(dy, "dy", (B, Cout, Ho, Wo))
+    _need(experts, "experts", (n, Cout, cpg, kh, kw), dy.dtype)
+    _need(alpha, "alpha", (B, n), F32)
+    _need(a_in, "a_in", (B, cpg * groups), F32, optional=True)
+    _need(a_out, "a_out", (B, Cout), F32, optional=True)
+    _need(dx, "dx", (B, cpg * groups, H, W), dy.dtype, optional=True)
+    _same_gpu(dy=dy, experts=experts, alpha=alpha, a_in=a_in, a_out=a_out, dx=dx)
+    if dx is None:
+        dx = torch.empty((B, cpg * groups, H, W), dtype=dy.dtype, device=dy.device)
+    ws, ws_bytes = _workspace(dynconv_backward_data_attn_workspace_bytes(desc, policy), dy.device, workspace)
+    _check(lib().dynconv_backward_data_attn(ctypes.byref(desc), int(policy), _ptr(dy), _ptr(experts),
+                                            _ptr(alpha), _ptr(a_in), _ptr(a_out), _ptr(dx), _ptr(ws), ws_bytes,
+                                            _stream(stream)), "dynconv_backward_data_attn")
+    return dx
 
 
 def dynconv_route_backward_workspace_bytes(desc: dynconv_desc_t) -> int:

@@ -736,6 +736,100 @@ dynconv_status_t dynconv_backward_weights(const dynconv_desc_t *desc, const void
                       "dynconv_backward_weights launch");
 }
 
+size_t dynconv_backward_data_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t policy) {
+    dynconv::Geom g;
+    dynconv_desc_t t;
+    if (backward_data_desc(desc, g, t) != DYNCONV_OK || !backward_data_via_forward(g)) return 0;
+    const size_t fw = dynconv_forward_attn_workspace_bytes(&t, policy);
+    dynconv::Geom gt;
+    if (check_desc(&t, gt, true) != DYNCONV_OK || wide(gt)) return 0;
+    int32_t p;
+    const bool ok = (!depthwise(gt) && gt.bf16) ? resolve_attn_policy(gt, policy, p) == DYNCONV_OK
+                                                 : resolve_policy(gt, policy, p) == DYNCONV_OK;
+    return ok ? flipped_bytes(g) + fw : 0;
+}
+
+dynconv_status_t dynconv_backward_data_attn(const dynconv_desc_t *desc, int32_t policy, const void *dy,
+                                            const void *experts, const float *alpha, const float *a_in,
+                                            const float *a_out, void *dx, void *workspace, size_t workspace_bytes,
+                                            void *stream) {
+    dynconv::Geom g;
+    dynconv_desc_t t;
+    dynconv_status_t s = backward_data_desc(desc, g, t);
+    if (s != DYNCONV_OK) return s;
+    if (!dy || !experts || !alpha || !dx)
+        return fail(DYNCONV_ERR_INVALID_ARG, "dy, experts, alpha and dx must not be NULL");
+    const void *ptrs[] = {dy, experts, alpha, dx, a_in, a_out};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (!backward_data_via_forward(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED,
+                    "backward_data_attn needs stride 1, a square kernel and pad <= k - 1 (the transposed layer)");
+    const size_t flip = flipped_bytes(g);
+    const size_t need = dynconv_backward_data_attn_workspace_bytes(desc, policy);
+    if (need == 0) {
+        // report the reason the transposed layer has no attention path
+        dynconv::Geom gt;
+        s = check_desc(&t, gt, true);
+        if (s != DYNCONV_OK) return s;
+        if (wide(gt))
+            return fail(DYNCONV_ERR_UNSUPPORTED, "channel attentions support n <= 16 experts on bf16 groups == 1 layers");
+        int32_t p;
+        return (!depthwise(gt) && gt.bf16) ? resolve_attn_policy(gt, policy, p) : resolve_policy(gt, policy, p);
+    }
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE,
+                    "backward_data_attn needs %zu bytes of 16-byte aligned workspace (got %zu)", need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    s = hip_status(dynconv::launch_flip_experts(g, experts, ws, st), "backward_data_attn flip launch");
+    if (s != DYNCONV_OK) return s;
+    // the transposed layer reads dy's channels (the layer's outputs, scaled by
+    // a_out) and writes dx's channels (the layer's inputs, scaled by a_in)
+    dynconv::ChanAttn att;
+    att.in = a_out;
+    att.out = a_in;
+    return forward_impl(&t, policy, dy, ws, alpha, dx, ws + flip, workspace_bytes - flip, stream, att);
+}
+
+size_t dynconv_backward_weights_attn_workspace_bytes(const dynconv_desc_t *desc) {
+    dynconv::Geom g;
+    if (check_desc(desc, g, true) != DYNCONV_OK) return 0;
+    return round_up(dynconv::wgrad_attn_bytes(g), kWsAlign);
+}
+
+dynconv_status_t dynconv_backward_weights_attn(const dynconv_desc_t *desc, const void *x, const void *dy,
+                                               const void *experts, const float *alpha, const float *a_in,
+                                               const float *a_out, float *dalpha, float *dexperts, float *da_in,
+                                               float *da_out, void *workspace, size_t workspace_bytes,
+                                               void *stream) {
+    dynconv::Geom g;
+    dynconv_status_t s = check_desc(desc, g, true);
+    if (s != DYNCONV_OK) return s;
+    if (!x || !dy || !experts || !alpha)
+        return fail(DYNCONV_ERR_INVALID_ARG, "x, dy, experts and alpha must not be NULL");
+    if (!dalpha && !dexperts && !da_in && !da_out)
+        return fail(DYNCONV_ERR_INVALID_ARG, "dalpha, dexperts, da_in and da_out are all NULL: nothing to compute");
+    const void *ptrs[] = {x, dy, experts, alpha, a_in, a_out, dalpha, dexperts, da_in, da_out};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(DYNCONV_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (g.B > 65535) return fail(DYNCONV_ERR_UNSUPPORTED, "backward_weights_attn supports B <= 65535 (got %d)", g.B);
+    if (depthwise(g) && !dynconv::wgrad_dw_supported(g))
+        return fail(DYNCONV_ERR_UNSUPPORTED, "depthwise backward_weights_attn supports up to 64 kernel taps");
+    const size_t need = round_up(dynconv::wgrad_attn_bytes(g), kWsAlign);
+    if (workspace_bytes < need || !workspace || !aligned16(workspace))
+        return fail(DYNCONV_ERR_WORKSPACE,
+                    "backward_weights_attn needs %zu bytes of 16-byte aligned workspace (got %zu)", need,
+                    workspace_bytes);
+    dynconv::ChanAttn att;
+    att.in = a_in;
+    att.out = a_out;
+    return hip_status(dynconv::launch_backward_weights_attn(g, x, dy, experts, alpha, att,
+                                                            static_cast<float *>(workspace), dalpha, dexperts,
+                                                            da_in, da_out, static_cast<hipStream_t>(stream)),
+                      "dynconv_backward_weights_attn launch");
+}
+
 size_t dynconv_route_backward_workspace_bytes(const dynconv_desc_t *desc) {
     dynconv::Geom g;
     if (check_desc(desc, g, false) != DYNCONV_OK) return 0;

@@ -452,6 +452,81 @@ __global__ __launch_bounds__(256) void dalpha_reduce_kernel(const float *__restr
     if (lane == 0) dalpha[idx] = s;
 }
 
+// ---- gradients of FMDConv's channel attentions -------------------------------
+// With G = dW_b formed from x and dy alone (launch_wgrad_gemm) and
+// y = a_out * conv(a_in * x, W_b) (FMDConv: Fast multi-attention dynamic
+// convolution, abstract):
+//   H[b][o][c]   = sum_t G[b][o][c][t] * W_b[o][c][t]
+//   da_out[b,o]  = sum_c a_in[b, g(o) cpg + c] * H[b][o][c]
+//   da_in[b,gc]  = sum over o of gc's group of a_out[b,o] * H[b][o][c]
+//   dW'_b        = a_out[b,o] * a_in[b,gc] * G   (then the usual contraction)
+// W_b is mixed on the fly in float32 (experts in order), so no rounding of the
+// mixed kernels enters these gradients. Every sum runs in a fixed order.
+
+// one thread per (b, o, c)
+template <typename T>
+__global__ __launch_bounds__(256) void attn_h_kernel(const float *__restrict__ G, const T *__restrict__ ex,
+                                                     const float *__restrict__ alpha, float *__restrict__ H,
+                                                     long total, int Cout, int cpg, int KT, int n, long wsize) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const long per_b = (long)Cout * cpg;
+    const int b = (int)(idx / per_b);
+    const long oc = idx - (long)b * per_b;  // o * cpg + c
+    const long e0 = oc * KT;
+    const float *al = alpha + (long)b * n;
+    const float *g = G + (long)b * wsize + e0;
+    float h = 0.f;
+    for (int t = 0; t < KT; ++t) {
+        float w = 0.f;
+        for (int i = 0; i < n; ++i) w = fmaf(al[i], Elem<T>::to_f32(ex[(long)i * wsize + e0 + t]), w);
+        h = fmaf(g[t], w, h);
+    }
+    H[idx] = h;
+}
+
+// one thread per (b, o); a_in may be null (ones)
+__global__ __launch_bounds__(256) void attn_dout_kernel(const float *__restrict__ H, const float *__restrict__ a_in,
+                                                        float *__restrict__ da_out, int B, int Cin, int Cout, int cpg,
+                                                        int opg) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)B * Cout) return;
+    const int b = (int)(idx / Cout), o = (int)(idx - (long)b * Cout);
+    const int c0 = (o / opg) * cpg;
+    const float *h = H + idx * cpg;
+    float s = 0.f;
+    for (int c = 0; c < cpg; ++c) s = fmaf(a_in ? a_in[(long)b * Cin + c0 + c] : 1.f, h[c], s);
+    da_out[idx] = s;
+}
+
+// one thread per (b, gc); a_out may be null (ones)
+__global__ __launch_bounds__(256) void attn_din_kernel(const float *__restrict__ H, const float *__restrict__ a_out,
+                                                       float *__restrict__ da_in, int B, int Cin, int Cout, int cpg,
+                                                       int opg) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)B * Cin) return;
+    const int b = (int)(idx / Cin), gc = (int)(idx - (long)b * Cin);
+    const int grp = gc / cpg, c = gc - grp * cpg;
+    float s = 0.f;
+    for (int o = grp * opg; o < (grp + 1) * opg; ++o)
+        s = fmaf(a_out ? a_out[(long)b * Cout + o] : 1.f, H[((long)b * Cout + o) * cpg + c], s);
+    da_in[idx] = s;
+}
+
+// G[b][e] *= a_out[b,o] * a_in[b,gc] (either may be null: ones)
+__global__ __launch_bounds__(256) void attn_scale_kernel(float *__restrict__ G, const float *__restrict__ a_in,
+                                                         const float *__restrict__ a_out, long total, long wsize,
+                                                         int Cin, int Cout, int cpg, int opg, int KT) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int b = (int)(idx / wsize);
+    const long e = idx - (long)b * wsize;
+    const int o = (int)(e / ((long)cpg * KT)), c = (int)((e / KT) % cpg);
+    const float fo = a_out ? a_out[(long)b * Cout + o] : 1.f;
+    const float fi = a_in ? a_in[(long)b * Cin + (o / opg) * cpg + c] : 1.f;
+    G[idx] *= fo * fi;
+}
+
 // ---- routing gradient -----------------------------------------------------------
 // Workgroup per example: dz from alpha and dalpha (sigmoid:
 // dalpha * alpha * (1 - alpha); softmax(z/T): alpha * (dalpha - <alpha,
@@ -617,10 +692,9 @@ size_t wgrad_bytes(const Geom &g) {
 
 bool wgrad_dw_supported(const Geom &g) { return g.KT <= kDwTaps; }
 
-hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy, const void *experts,
-                                   const float *alpha, float *dwb, float *dalpha, float *dexperts,
-                                   hipStream_t stream) {
-    if (wgrad_fused_bytes(g)) return launch_wgrad_fused(g, x, dy, experts, alpha, dwb, dalpha, dexperts, stream);
+namespace {
+// dW_b of every example into dwb (float32, [B][Cout][Cin/g][KH][KW]).
+hipError_t launch_wgrad_gemm(const Geom &g, const void *x, const void *dy, float *dwb, hipStream_t stream) {
     WgArgs a;
     a.B = g.B; a.Cin = g.Cin; a.H = g.H; a.W = g.W; a.Cout = g.Cout; a.KW = g.KW;
     a.stride = g.stride; a.pad = g.pad; a.Ho = g.Ho; a.Wo = g.Wo; a.P = g.P; a.KT = g.KT;
@@ -660,9 +734,14 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
                                static_cast<const float *>(dy), dwb, a);
         }
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // scratch: dW_b | dalpha partial sums | dE per example group
+    return hipGetLastError();
+}
+
+// dalpha and dexperts from dW_b in dwb; the partial sums follow dW_b in the
+// scratch: dW_b | dalpha partial sums | dE per example group.
+hipError_t launch_contract_all(const Geom &g, float *dwb, const void *experts, const float *alpha, float *dalpha,
+                               float *dexperts, hipStream_t stream) {
+    hipError_t e;
     char *base = reinterpret_cast<char *>(dwb);
     float *dpart = reinterpret_cast<float *>(base + dwb_bytes(g));
     const int groups = contract_groups(g);
@@ -677,6 +756,58 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
     }
     if (!dalpha) return hipSuccess;
     return launch_dalpha_reduce(dpart, dalpha, g.B, g.n, g.n, contract_chunks(g), stream);
+}
+}  // namespace
+
+hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy, const void *experts,
+                                   const float *alpha, float *dwb, float *dalpha, float *dexperts,
+                                   hipStream_t stream) {
+    if (wgrad_fused_bytes(g)) return launch_wgrad_fused(g, x, dy, experts, alpha, dwb, dalpha, dexperts, stream);
+    hipError_t e = launch_wgrad_gemm(g, x, dy, dwb, stream);
+    if (e != hipSuccess) return e;
+    return launch_contract_all(g, dwb, experts, alpha, dalpha, dexperts, stream);
+}
+
+size_t wgrad_attn_bytes(const Geom &g) {
+    return dwb_bytes(g) + dpart_bytes(g) + dep_bytes(g) + align256((size_t)g.B * g.Cout * g.cpg * sizeof(float));
+}
+
+hipError_t launch_backward_weights_attn(const Geom &g, const void *x, const void *dy, const void *experts,
+                                        const float *alpha, ChanAttn att, float *ws, float *dalpha,
+                                        float *dexperts, float *da_in, float *da_out, hipStream_t stream) {
+    // scratch: dW_b | dalpha partial sums | dE per example group | H
+    hipError_t e = launch_wgrad_gemm(g, x, dy, ws, stream);
+    if (e != hipSuccess) return e;
+    const long wsize = bank_elems(g);
+    const int opg = g.Cout / g.groups;
+    if (da_in || da_out) {
+        float *h = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + dwb_bytes(g) + dpart_bytes(g) +
+                                             dep_bytes(g));
+        const long nh = (long)g.B * g.Cout * g.cpg;
+        if (g.bf16)
+            hipLaunchKernelGGL(attn_h_kernel<uint16_t>, dim3(blocks_for(nh)), dim3(256), 0, stream, ws,
+                               static_cast<const uint16_t *>(experts), alpha, h, nh, g.Cout, g.cpg, g.KT, g.n, wsize);
+        else
+            hipLaunchKernelGGL(attn_h_kernel<float>, dim3(blocks_for(nh)), dim3(256), 0, stream, ws,
+                               static_cast<const float *>(experts), alpha, h, nh, g.Cout, g.cpg, g.KT, g.n, wsize);
+        if (da_out)
+            hipLaunchKernelGGL(attn_dout_kernel, dim3(blocks_for((long)g.B * g.Cout)), dim3(256), 0, stream, h,
+                               att.in, da_out, g.B, g.Cin, g.Cout, g.cpg, opg);
+        if (da_in)
+            hipLaunchKernelGGL(attn_din_kernel, dim3(blocks_for((long)g.B * g.Cin)), dim3(256), 0, stream, h,
+                               att.out, da_in, g.B, g.Cin, g.Cout, g.cpg, opg);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!dalpha && !dexperts) return hipSuccess;
+    if (att.in || att.out) {
+        const long total = (long)g.B * wsize;
+        hipLaunchKernelGGL(attn_scale_kernel, dim3(blocks_for(total)), dim3(256), 0, stream, ws, att.in, att.out,
+                           total, wsize, g.Cin, g.Cout, g.cpg, opg, g.KT);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_contract_all(g, ws, experts, alpha, dalpha, dexperts, stream);
 }
 
 hipError_t launch_dE_reduce(const float *dep, float *de, long total, int groups, hipStream_t stream) {

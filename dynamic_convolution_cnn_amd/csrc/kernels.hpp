@@ -158,6 +158,15 @@ hipError_t launch_backward_weights(const Geom &g, const void *x, const void *dy,
                                    const float *alpha, float *dwb, float *dalpha, float *dexperts,
                                    hipStream_t stream);
 
+// The kernel gradient of the layer with FMDConv's channel attentions (att.in
+// [B*Cin], att.out [B*Cout], either null = ones): dalpha and dexperts of
+// y = a_out * conv(a_in * x, W_b) through dW_b in the workspace, and
+// da_in [B*Cin], da_out [B*Cout] (float32). Any output may be null.
+size_t wgrad_attn_bytes(const Geom &g);
+hipError_t launch_backward_weights_attn(const Geom &g, const void *x, const void *dy, const void *experts,
+                                        const float *alpha, ChanAttn att, float *ws, float *dalpha,
+                                        float *dexperts, float *da_in, float *da_out, hipStream_t stream);
+
 // The fused kernel gradient (wgrad_fused.hip: bf16, groups == 1, stride 1,
 // n <= 4, 1 x 1 or k x 3 kernels; dW_b never stored): its scratch bytes,
 // 0 where it does not apply, and its launch with that scratch.

@@ -319,6 +319,50 @@ dynconv_status_t dynconv_backward_weights(const dynconv_desc_t *desc, const void
                                           void *stream);
 size_t dynconv_backward_weights_workspace_bytes(const dynconv_desc_t *desc);
 
+/* Gradients of the layer with FMDConv's channel attentions (FMDConv: Fast
+ * multi-attention dynamic convolution, abstract; the forward is
+ * dynconv_forward_attn: y = a_out * conv(a_in * x, W_b), a_in [B,Cin] scaling
+ * input channels, a_out [B,Cout] output channels, float32, either NULL
+ * meaning all ones). With G_b = the dW_b of dynconv_backward_weights formed
+ * from x and dy alone:
+ *   dW'_b[o,c',u,v] = a_out[b,o] * a_in[b,gc] * G_b[o,c',u,v]
+ *   dalpha[b,i]     = sum_e dW'_b[e] * E_i[e]        (float32 [B,n])
+ *   dexperts[i,e]   = sum_b alpha[b,i] * dW'_b[e]    (float32 [n,Cout,Cin/g,kh,kw])
+ *   da_in[b,gc]     = sum over the o of gc's group and (u,v) of a_out[b,o] * G_b[o,c',u,v] * W_b[o,c',u,v]
+ *   da_out[b,o]     = sum over (c',u,v) of a_in[b,gc] * G_b[o,c',u,v] * W_b[o,c',u,v]
+ * (float32 [B,Cin] and [B,Cout]; gc = (o / (Cout/g)) * (Cin/g) + c'). W_b is
+ * mixed in float32 for these sums, the attention factors multiply G_b in
+ * float32: no rounding to the element type enters. Any output may be NULL
+ * (not computed), not all four. Any stride and padding; groups 1 or depthwise
+ * (at most 64 taps); B <= 65535. workspace: at least
+ * dynconv_backward_weights_attn_workspace_bytes(desc) bytes (G_b in float32,
+ * the partial sums, and B * Cout * (Cin/g) floats); outputs written, not
+ * accumulated; deterministic. Other arguments and errors as
+ * dynconv_backward_weights. */
+dynconv_status_t dynconv_backward_weights_attn(const dynconv_desc_t *desc, const void *x, const void *dy,
+                                               const void *experts, const float *alpha, const float *a_in,
+                                               const float *a_out, float *dalpha, float *dexperts, float *da_in,
+                                               float *da_out, void *workspace, size_t workspace_bytes,
+                                               void *stream);
+size_t dynconv_backward_weights_attn_workspace_bytes(const dynconv_desc_t *desc);
+
+/* Input gradient of the layer with FMDConv's channel attentions:
+ *   dx[b,gc,h,w] = a_in[b,gc] * (the transposed convolution of a_out[b,:] * dy[b] with W_b)
+ * computed as dynconv_forward_attn of the transposed layer (stride 1, kh ==
+ * kw and pad <= kh - 1 only; else DYNCONV_ERR_UNSUPPORTED): the bank
+ * transposed and flipped as in dynconv_backward_data, a_out as that layer's
+ * input attention and a_in as its output attention, with the policies and
+ * roundings of dynconv_forward_attn (bf16 groups == 1 layers: at most 16
+ * experts). workspace: at least dynconv_backward_data_attn_workspace_bytes(
+ * desc, policy) bytes (the flipped bank, then the forward's workspace; 0 for
+ * an unsupported layer or policy). Other arguments as
+ * dynconv_backward_data. */
+dynconv_status_t dynconv_backward_data_attn(const dynconv_desc_t *desc, int32_t policy, const void *dy,
+                                            const void *experts, const float *alpha, const float *a_in,
+                                            const float *a_out, void *dx, void *workspace, size_t workspace_bytes,
+                                            void *stream);
+size_t dynconv_backward_data_attn_workspace_bytes(const dynconv_desc_t *desc, int32_t policy);
+
 /* Gradient of the routing (dynconv_route) for the attention gradient dalpha:
  *   sigmoid:      dz = dalpha * alpha * (1 - alpha)
  *   softmax(z/T): dz_i = alpha_i * (dalpha_i - sum_k alpha_k dalpha_k) / T

@@ -594,3 +594,35 @@ def test_binding_rejects_short_packed_bank_and_workspace(no_compute):
     ws_need = bd.dynconv_forward_workspace_bytes(desc)
     with pytest.raises(ValueError, match="device|workspace"):
         bd.dynconv_forward(x, e, a, 1, 1, workspace=torch.empty(max(ws_need - 16, 0), dtype=torch.uint8))
+
+
+def test_backward_attn_checks():
+    """Argument checks and workspace sizes of the attention gradients (no launch)."""
+    L = _lib()
+    d = good_desc(B=2, Cin=16, Cout=16, n=4)
+    r256 = lambda v: (v + 255) // 256 * 256
+    wsize = 16 * 16 * 9
+    # dW_b in float32, the dalpha partial sums (1024-element chunks), then H (B * Cout * Cin floats)
+    assert bd.dynconv_backward_weights_attn_workspace_bytes(d) == (
+        r256(2 * wsize * 4) + r256(2 * 4 * 3 * 4) + r256(2 * 16 * 16 * 4))
+
+    def bw(desc=d, x=FAKE, dy=FAKE, e=FAKE, a=FAKE, ai=FAKE, ao=FAKE, da=FAKE, de=FAKE, dai=FAKE, dao=FAKE,
+           wsp=FAKE, wsb=1 << 30):
+        return L.dynconv_backward_weights_attn(ctypes.byref(desc), x, dy, e, a, ai, ao, da, de, dai, dao, wsp,
+                                               wsb, None)
+    assert bw(x=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bw(da=None, de=None, dai=None, dao=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bw(ai=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bw(wsb=16) == bd.DYNCONV_ERR_WORKSPACE
+    assert bw(desc=good_desc(groups=2), wsb=1 << 30) == bd.DYNCONV_ERR_UNSUPPORTED
+
+    def bdat(desc=d, policy=0, dy=FAKE, e=FAKE, a=FAKE, ai=FAKE, ao=FAKE, dx=FAKE, wsp=FAKE, wsb=1 << 30):
+        return L.dynconv_backward_data_attn(ctypes.byref(desc), policy, dy, e, a, ai, ao, dx, wsp, wsb, None)
+    assert bdat(dx=None) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bdat(ao=MISALIGNED) == bd.DYNCONV_ERR_INVALID_ARG
+    assert bdat(desc=good_desc(stride=2)) == bd.DYNCONV_ERR_UNSUPPORTED
+    assert bd.dynconv_backward_data_attn_workspace_bytes(good_desc(stride=2)) == 0
+    assert bd.dynconv_backward_data_attn_workspace_bytes(good_desc(n=40)) == 0   # more than 16 experts
+    assert bdat(wsb=16) == bd.DYNCONV_ERR_WORKSPACE
+    need = bd.dynconv_backward_data_attn_workspace_bytes(d)
+    assert need >= bd.dynconv_backward_data_workspace_bytes(d) - 1024 and need > 0
