@@ -11,6 +11,7 @@
 // VGPRs (the contraction reads them directly).
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -472,16 +473,24 @@ bool wf_plan_uncached(const Geom &g, WfPlan &pl) {
     const size_t fixed = (size_t)g.KW * a.CS * 2 + (size_t)kWfOT * wf_apitch(pl.ns) * 2;
     // row sums of at most this many examples fit beside the windows
     const int bmax = (int)((kWfLds - fixed) / 256);
-    // one group's dE partial sums (written, then read) in example-steps of
-    // about 0.35 us at 5 TB/s
-    const double pen = std::max(0.5, (double)g.n * g.Cout * a.Kdim * 8 / 5e12 / 0.35e-6);
-    int G = 0;
-    double cost = 0;
-    for (int c = 1; c <= std::min(g.B, 64); ++c) {
+    // Cost of c example groups in units of one workgroup's example (about
+    // 2.1 us per 14 products with two workgroups per compute unit): rounds of
+    // 512 resident workgroups times the examples per workgroup, plus each
+    // group's dE partial sums (written, then read again, at 5 TB/s). The
+    // fewest groups within 10 % of the cheapest win (fewer partial sums).
+    const double t_ex = 2.1e-6 * (double)(a.nchunk * pl.ns) / 14.0;
+    const double pen = (double)g.n * g.Cout * a.Kdim * 8 / 5e12 / t_ex;
+    const int cmax = std::min(g.B, 64);
+    std::vector<double> cost(cmax + 1, -1.0);
+    double cheapest = -1.0;
+    for (int c = 1; c <= cmax; ++c) {
         if (ceil_div(g.B, c) > bmax) continue;
-        const double c2 = (double)ceil_div(a.ntiles * c, 256) * ceil_div(g.B, c) + (c > 1 ? c * pen : 0.0);
-        if (G == 0 || c2 < cost) { cost = c2; G = c; }
+        cost[c] = (double)ceil_div(a.ntiles * c, 512) * ceil_div(g.B, c) + (c > 1 ? c * pen : 0.0);
+        if (cheapest < 0 || cost[c] < cheapest) cheapest = cost[c];
     }
+    int G = 0;
+    for (int c = 1; c <= cmax && G == 0; ++c)
+        if (cost[c] >= 0 && cost[c] <= 1.1 * cheapest) G = c;
     if (G == 0) return false;
     a.bper = ceil_div(g.B, G);
     a.groups = ceil_div(g.B, a.bper);

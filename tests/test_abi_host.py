@@ -303,13 +303,13 @@ def test_backward_weights_checks():
 
     r256 = lambda v: (v + 255) // 256 * 256
     # bf16, stride 1, n <= 4 (the fused kernel gradient): partial sums of
-    # dalpha, 4 expert rows per example, per (64 x 64 tile, wave); no dE
-    # partial sums (one example group: 3 tiles of 144 columns); dy as one
-    # zero-padded run of 8 x 16 positions per (example, channel); x as
-    # zero-bordered 10 x 16 planes
+    # dalpha, 4 expert rows per example, per (64 x 64 tile, wave); dE partial
+    # sums of 2 example groups (one example each: 3 tiles of 144 columns);
+    # dy as one zero-padded run of 8 x 16 positions per (example, channel); x
+    # as zero-bordered 10 x 16 planes
     wsize = 16 * 16 * 9
     assert bd.dynconv_backward_weights_workspace_bytes(d) == (
-        r256(2 * 4 * 3 * 4 * 4) + r256(2 * 16 * 8 * 16 * 2) + r256(2 * 16 * 10 * 16 * 2))
+        r256(2 * 4 * 3 * 4 * 4) + r256(2 * 4 * wsize * 4) + r256(2 * 16 * 8 * 16 * 2) + r256(2 * 16 * 10 * 16 * 2))
     # other layers: dW_b in float32, then B * n partial sums of dalpha per
     # 1024-element chunk of the bank
     wide = good_desc(n=8)
