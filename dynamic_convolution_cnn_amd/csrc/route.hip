@@ -298,6 +298,80 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(
     route_finish(gsh, zsh, fc_w, fc_b, alpha, b, C, n, mode, temp, pre);
 }
 
+// The same single-kernel router for bf16 planes of an even number of
+// elements that is not a multiple of 8 (14 x 14): 16-byte loads through a
+// buffer descriptor over x (dword-aligned planes; the last vector of a plane
+// runs into the next plane, or past the tensor, where the read returns 0),
+// its elements past the plane left out of the sum. Half the load
+// instructions of 8-byte vectors, twice the bytes per request.
+constexpr int kRouteMaxK16 = 8;  // 16-byte loads per lane and plane
+template <int LPR>
+__global__ __launch_bounds__(kRouteThreads) void route_fused16_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ fc_w, const float *__restrict__ fc_b,
+    float *__restrict__ alpha, int C, int hw, int n, int mode, float temp, int x_bytes) {
+    __shared__ float gsh[kRouteMaxC];
+    __shared__ float zsh[64 * kMaxJ];
+    constexpr int kPlanes = kRouteThreads / LPR;  // planes per pass
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int grp = tid / LPR, lane_in = tid % LPR;
+    const int nvec = (hw + 7) / 8;              // at most LPR * kRouteMaxK16
+    const int tail_words = (hw - 8 * (nvec - 1)) / 2;  // valid words of the last vector (1..4)
+    const uint64_t q = reinterpret_cast<uint64_t>(x);
+    const uint64_t qs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)q) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(q >> 32)) << 32);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(qs), 0,
+                                                      __builtin_amdgcn_readfirstlane(x_bytes), 0x00020000);
+    const FcPre pre = route_prefetch_fc(fc_w, fc_b, C, n);
+    for (int c0 = 0; c0 < C; c0 += kPlanes) {
+        const int c = c0 + grp;
+        const int base = (((b * C) + min(c, C - 1)) * hw) * 2;  // bytes (x_bytes < 2^31)
+        // every load before the first sum (clamped vector index, no branch)
+        u32x4_t v[kRouteMaxK16];
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK16; ++k)
+            v[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs, base + 16 * min(lane_in + LPR * k, nvec - 1), 0, 0));
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK16; ++k) {
+            const int vi = lane_in + LPR * k;
+            const int words = vi < nvec - 1 ? 4 : (vi == nvec - 1 ? tail_words : 0);
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t += j < words ? bf16_lo(w[j]) + bf16_hi(w[j]) : 0.f;
+            s += t;
+        }
+        s = group_sum<LPR>(s);
+        if (lane_in == 0 && c < C) gsh[c] = s / (float)hw;
+    }
+    __syncthreads();
+    route_finish(gsh, zsh, fc_w, fc_b, alpha, b, C, n, mode, temp, pre);
+}
+
+hipError_t launch_route_fused16(const uint16_t *x, const float *fc_w, const float *fc_b, float *alpha, int B, int C,
+                                int hw, int n, int mode, float temp, hipStream_t s) {
+    const int nvec = (hw + 7) / 8;
+    int lpr = 1;
+    while (lpr * kRouteMaxK16 < nvec) lpr *= 2;
+    const int x_bytes = (int)((long)B * C * hw * 2);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(B), dim3(kRouteThreads), 0, s, x, fc_w, fc_b, alpha, C, hw, n, mode, temp,
+                           x_bytes);
+        return hipGetLastError();
+    };
+    switch (lpr) {
+    case 1: return go(route_fused16_kernel<1>);
+    case 2: return go(route_fused16_kernel<2>);
+    case 4: return go(route_fused16_kernel<4>);
+    case 8: return go(route_fused16_kernel<8>);
+    case 16: return go(route_fused16_kernel<16>);
+    case 32: return go(route_fused16_kernel<32>);
+    default: return go(route_fused16_kernel<64>);
+    }
+}
+
 template <typename T, int VEC>
 hipError_t launch_route_fused_vec(const T *x, const float *fc_w, const float *fc_b, float *alpha,
                                   int B, int C, int hw, int n, int mode, float temp,
@@ -488,6 +562,8 @@ hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const f
         if (g.bf16) {
             const uint16_t *xb = static_cast<const uint16_t *>(x);
             if (hw % 8 == 0) return launch_route_fused_vec<uint16_t, 8>(xb, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
+            if (hw % 2 == 0 && hw <= 8 * 64 * kRouteMaxK16 && (long)g.B * g.Cin * hw * 2 < (1L << 31) - 64)
+                return launch_route_fused16(xb, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
             if (hw % 4 == 0) return launch_route_fused_vec<uint16_t, 4>(xb, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
             return launch_route_fused_vec<uint16_t, 1>(xb, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
         }
