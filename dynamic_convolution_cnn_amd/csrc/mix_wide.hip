@@ -9,9 +9,11 @@
 //     (double-buffered, the next chunk's loads in flight during the current
 //     chunk's MFMAs) and read as A fragments with LDS transpose reads, two
 //     groups of 16 experts per chunk;
-//   * the chunk's attentions are split into three bf16 parts (24 bits, a
-//     float32 significand), so the exact products summed in fp32 equal a
-//     float32 mix before its one bf16 rounding;
+//   * the chunk's attentions of the workgroup's 32*MT examples arrive with
+//     coalesced 16-byte loads, staged in LDS beside the expert slice; each
+//     lane's are split into three bf16 parts (24 bits, a float32
+//     significand), so the exact products summed in fp32 equal a float32 mix
+//     before its one bf16 rounding;
 //   * results leave through LDS as 16-byte row stores.
 // The weights are whatever order the bank is stored in: the natural layout
 // for dynconv_mix, or the convolution's [t][o][cp] order (pack_wide_kernel)
@@ -34,7 +36,16 @@ __global__ __launch_bounds__(256) void mix_mfma_wide_kernel(const float *__restr
     constexpr int KC = kWideChunk;
     constexpr int NV = KC * (kMixWW / 8) / 256;  // 16-byte staging vectors per thread per chunk
     __shared__ __attribute__((aligned(16))) uint16_t s_e[2][KC][kMixWW];
-    __shared__ __attribute__((aligned(16))) uint16_t s_o[32 * MT][kMixWPitch];
+    // the output rows share their storage with the attentions of the
+    // workgroup's examples, [buffer][example][expert] (rows padded by 4
+    // floats against bank conflicts of the 16-byte reads), which are dead once
+    // the last chunk is done
+    __shared__ __attribute__((aligned(16))) union {
+        uint16_t o[32 * MT][kMixWPitch];
+        float a[2][32 * MT][KC + 4];
+    } s_u;
+    auto &s_o = s_u.o;
+    auto &s_a = s_u.a;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     const long w0 = (long)blockIdx.x * kMixWW;
     const int bc0 = blockIdx.y * 32 * MT;
@@ -57,21 +68,48 @@ __global__ __launch_bounds__(256) void mix_mfma_wide_kernel(const float *__restr
             *reinterpret_cast<u32x4_t *>(&s_e[buf][k][8 * c]) = in ? q[it] : u32x4_t{0u, 0u, 0u, 0u};
         }
     };
-    // this lane's attentions for a chunk: example bc0 + 32 mt + l32, experts
-    // KC ch + 16 g + 8 lh + (0..7)
-    auto load_alpha = [&](int ch, float (&av)[MT][2][8]) {
+    // the chunk's attentions, 32 MT examples x KC experts: coalesced 16-byte
+    // loads (thread t: example t / 8 (+ 32 per round), experts 4 (t % 8) ..
+    // + 3; clamped, masked where stored) staged in s_a next to the expert slice
+    constexpr int NA = 32 * MT * KC / 4 / 256;  // 16-byte attention pieces per thread per chunk
+    const bool a16 = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(alpha) & 15) == 0;
+    auto load_alpha = [&](int ch, f32x4_t (&ga)[NA]) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int b = bc0 + 32 * mt + l32;
-            const float *ab = alpha + (long)min(b, B - 1) * n;
+        for (int it = 0; it < NA; ++it) {
+            const int v = tid + 256 * it, r = v >> 3, kq = 4 * (v & 7);
+            const int b = min(bc0 + r, B - 1), k = KC * ch + kq;
+            if (a16) {
+                ga[it] = *reinterpret_cast<const f32x4_t *>(alpha + (long)b * n + min(k, n - 4));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ga[it][j] = alpha[(long)b * n + min(k + j, n - 1)];
+            }
+        }
+    };
+    auto store_alpha = [&](int buf, int ch, const f32x4_t (&ga)[NA]) {
+#pragma unroll
+        for (int it = 0; it < NA; ++it) {
+            const int v = tid + 256 * it, r = v >> 3, kq = 4 * (v & 7);
+            f32x4_t val = ga[it];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!(bc0 + r < B && KC * ch + kq + j < n)) val[j] = 0.f;
+            *reinterpret_cast<f32x4_t *>(&s_a[buf][r][kq]) = val;
+        }
+    };
+    // this lane's attentions for a chunk from s_a: example 32 mt + l32, experts
+    // 16 g + 8 lh + (0..7) of the chunk
+    auto read_alpha = [&](int buf, float (&av)[MT][2][8]) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int g = 0; g < 2; ++g)
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int k = KC * ch + 16 * g + 8 * lh + q;
-                    av[mt][g][q] = (b < B && k < n) ? ab[k] : 0.f;
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4_t t = *reinterpret_cast<const f32x4_t *>(&s_a[buf][32 * mt + l32][16 * g + 8 * lh + 4 * h]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) av[mt][g][4 * h + j] = t[j];
                 }
-        }
     };
     f32x16_t acc[MT][2];
 #pragma unroll
@@ -81,19 +119,21 @@ __global__ __launch_bounds__(256) void mix_mfma_wide_kernel(const float *__restr
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
     u32x4_t q[NV];
+    f32x4_t ga[NA];
     float av[MT][2][8];
     load(0, q);
-    load_alpha(0, av);
+    load_alpha(0, ga);
     store(0, 0, q);
+    store_alpha(0, 0, ga);
     const int si = lane & 15;
     for (int ch = 0; ch < nchunks; ++ch) {
         const int buf = ch & 1;
-        float avn[MT][2][8];
         if (ch + 1 < nchunks) {
             load(ch + 1, q);
-            load_alpha(ch + 1, avn);
+            load_alpha(ch + 1, ga);
         }
-        __syncthreads();  // chunk ch is in s_e[buf]; the reads of s_e[buf ^ 1] are done
+        __syncthreads();  // chunk ch is in s_e[buf] and s_a[buf]; the reads of the other buffers are done
+        read_alpha(buf, av);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             // expert operands (A: rows = weights): experts 16 g + 8 lh + (0..7)
@@ -147,14 +187,10 @@ __global__ __launch_bounds__(256) void mix_mfma_wide_kernel(const float *__restr
         }
         if (ch + 1 < nchunks) {
             store(buf ^ 1, ch + 1, q);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) av[mt][g][k] = avn[mt][g][k];
+            store_alpha(buf ^ 1, ch + 1, ga);
         }
     }
+    __syncthreads();  // every wave's reads of the attentions, which s_o overwrites, are done
     // weights as the rows: D(lane, 4 j + r) = weight 64 wave + 32 nt + 8 j + 4 lh + r,
     // example 32 mt + l32: 4 consecutive weights of one W_b row (one 8-byte LDS write)
 #pragma unroll
