@@ -29,7 +29,9 @@ def _gpu(device):
 
 @pytest.mark.parametrize("n,B,wshape", [(65, 3, (16, 8, 3, 3)), (100, 33, (24, 16, 3, 3)),
                                         (128, 70, (40, 24, 1, 1)), (256, 5, (8, 8, 5, 5)),
-                                        (129, 64, (16, 16, 3, 3))])
+                                        (129, 64, (16, 16, 3, 3)),
+                                        # 576 weight tiles: 64 examples per workgroup
+                                        (72, 65, (128, 128, 3, 3)), (67, 100, (128, 128, 3, 3))])
 def test_mix_many_experts(n, B, wshape):
     rng = np.random.default_rng(70 + n)
     e = inputs.bf16_round(rng.standard_normal((n,) + wshape, dtype=np.float32))
