@@ -201,7 +201,7 @@ def main():
         descs.append(desc)
         pols.append(pol)
     alphas = [torch.empty((w.B, w.n), dtype=torch.float32, device=dev) for _ in range(R)]
-    route_ws = torch.empty(bd.dynconv_route_workspace_bytes(descs[0]), dtype=torch.uint8, device=dev)
+    route_ws = torch.zeros(max(16, bd.dynconv_route_workspace_bytes(descs[0])), dtype=torch.uint8, device=dev)
     if w.attention:
         L0 = w.layers[0]
         heads = [to_dev(d[k], "f32") for k in ("fc_w_in", "fc_b_in", "fc_w_out", "fc_b_out")]
@@ -507,7 +507,7 @@ def train_main(args):
     ws_w = torch.empty(max(16, bd.dynconv_backward_weights_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(16, bd.dynconv_backward_data_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
     rdesc = bd.make_desc(w.B, L.Cin, L.H, L.W, n=w.n, dtype=desc.dtype)
-    ws_r = torch.empty(max(16, bd.dynconv_route_workspace_bytes(rdesc)), dtype=torch.uint8, device=dev)
+    ws_r = torch.zeros(max(16, bd.dynconv_route_workspace_bytes(rdesc)), dtype=torch.uint8, device=dev)
     ws_rb = torch.empty(max(16, bd.dynconv_route_backward_workspace_bytes(rdesc)), dtype=torch.uint8, device=dev)
 
     def bwd_weights(i):

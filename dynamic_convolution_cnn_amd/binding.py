@@ -263,7 +263,7 @@ def _check(status: int, where: str):
         raise DynconvError(status, where, last_error())
 
 
-def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor], zeroed: bool = False):
     if given is not None:
         _need_bytes(given, "workspace", nbytes)
         _same_gpu(workspace=given)
@@ -273,7 +273,8 @@ def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
         return given, 0
     if given is not None:
         return given, given.numel() * given.element_size()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    alloc = torch.zeros if zeroed else torch.empty
+    return alloc(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def layer_desc(x: torch.Tensor, experts: torch.Tensor, stride: int, pad: int,
@@ -324,7 +325,10 @@ def dynconv_route(x: torch.Tensor, fc_w: torch.Tensor, fc_b: Optional[torch.Tens
     _same_gpu(x=x, fc_w=fc_w, fc_b=fc_b, alpha=alpha)
     if alpha is None:
         alpha = torch.empty((B, n), dtype=torch.float32, device=x.device)
-    ws, ws_bytes = _workspace(dynconv_route_workspace_bytes(desc), x.device, workspace)
+    # a workspace made here starts zero-filled, as the router's ticket
+    # counters need; one passed in must have been zero-filled once (each call
+    # leaves the counters zero)
+    ws, ws_bytes = _workspace(dynconv_route_workspace_bytes(desc), x.device, workspace, zeroed=True)
     _check(lib().dynconv_route(ctypes.byref(desc), _ptr(x), _ptr(fc_w), _ptr(fc_b), int(mode),
                                float(temperature), _ptr(alpha), _ptr(ws), ws_bytes,
                                _stream(stream)), "dynconv_route")

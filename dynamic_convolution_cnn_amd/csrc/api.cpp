@@ -416,8 +416,7 @@ const char *dynconv_last_error(void) { return g_err; }
 size_t dynconv_route_workspace_bytes(const dynconv_desc_t *desc) {
     dynconv::Geom g;
     if (check_desc(desc, g, false) != DYNCONV_OK) return 0;
-    if (dynconv::route_single_kernel(g)) return 0;
-    return round_up((size_t)g.B * g.Cin * sizeof(float), kWsAlign);
+    return round_up(dynconv::route_workspace_bytes(g), kWsAlign);
 }
 
 dynconv_status_t dynconv_route(const dynconv_desc_t *desc, const void *x, const float *fc_w,
@@ -440,8 +439,7 @@ dynconv_status_t dynconv_route(const dynconv_desc_t *desc, const void *x, const 
         return fail(DYNCONV_ERR_WORKSPACE, "route needs %zu bytes of 16-byte aligned workspace (got %zu)",
                     need, workspace_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return hip_status(dynconv::launch_route(g, x, fc_w, fc_b, mode, temperature,
-                                            static_cast<float *>(workspace), alpha, st),
+    return hip_status(dynconv::launch_route(g, x, fc_w, fc_b, mode, temperature, workspace, alpha, st),
                       "dynconv_route launch");
 }
 

@@ -31,14 +31,15 @@ struct ChanAttn {
 };
 
 // ---- routing -------------------------------------------------------------
-// gap[B*Cin] (float) = channel means of x; then alpha[B,n] from the FC and
-// the nonlinearity. `gap` is caller-provided scratch of B*Cin floats.
-// True when routing runs as one kernel (one workgroup per example) and
-// needs no `gap` scratch.
+// alpha[B,n] from the channel means of x, the FC and the nonlinearity.
+// `workspace` holds route_workspace_bytes(g) bytes: none for one workgroup
+// per example; tickets (zero on entry, left zero) and B*Cin channel means for
+// the split router; B*Cin means for the two-kernel path.
 bool route_single_kernel(const Geom &g);
+size_t route_workspace_bytes(const Geom &g);
 hipError_t launch_route(const Geom &g, const void *x, const float *fc_w,
                         const float *fc_b, int mode, float temperature,
-                        float *gap, float *alpha, hipStream_t stream);
+                        void *workspace, float *alpha, hipStream_t stream);
 // Channel means of x into gap[B*Cin] (float).
 hipError_t launch_gap(const Geom &g, const void *x, float *gap, hipStream_t stream);
 // GAP into `gap` (B*Cin floats), then nout[h] logits per example for each of

@@ -6,12 +6,13 @@
 //   z[b,i]   = sum_c fc_w[i,c] gap[b,c] + fc_b[i]
 //   alpha    = sigmoid(z)  or  softmax_i(z / T)
 //
-// Two kernels. The pooling kernel streams x once from HBM with 8-16 byte
-// vector loads: every channel plane is reduced by a group of lanes (16-64
-// lanes, sized to the plane) so that many planes are in flight per CU and
-// the chip is filled even at small batch. The FC kernel is tiny (one wave
-// per example). No atomics: sums run in a fixed order, so the result is
-// deterministic.
+// One launch in the common cases: one workgroup per example from 64
+// examples up, several per example below that (the split router, whose last
+// workgroup per example finishes the FC). Planes too large for those take
+// two kernels: a pooling kernel that streams x once with 8-16 byte vector
+// loads (16-64 lanes per plane), then a small FC kernel (one wave per
+// example). Every sum runs in a fixed order, so the result is deterministic.
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,8 +20,15 @@ namespace dynconv {
 namespace {
 
 constexpr int kGapThreads = 256;
-// batches at least this large route with one workgroup per example
-constexpr int kRouteMinB = 64;
+// batches below this route with several workgroups per example (split
+// router), larger ones with one workgroup per example
+constexpr int kRouteSplitMaxB = 64;
+constexpr int kSplitThreads = 512;
+// s_waitcnt operand: vector memory count 0, the other counters unconstrained
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+// bytes of tickets at the start of the split router's workspace
+constexpr size_t kRouteTicketBytes(int B) { return ((size_t)B * sizeof(unsigned) + 255) / 256 * 256; }
 
 // VEC elements per load (VEC * sizeof(T) bytes); LPR lanes per plane.
 template <typename T, int VEC, int LPR>
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(256) void route_fc_kernel(const float *__restrict__
     }
 }
 
-// Single-kernel routing for batches of at least kRouteMinB examples: one
+// Single-kernel routing for batches of at least kRouteSplitMaxB examples: one
 // workgroup of 1024 threads per example. Phase 1 reduces the example's
 // channel planes into channel means in LDS: LPR lanes per plane, and every
 // lane issues all of its (at most kRouteMaxK) vector loads of a plane before
@@ -203,12 +211,12 @@ __device__ __forceinline__ FcPre route_prefetch_fc(const float *__restrict__ fc_
     f.bias = fc_b ? fc_b[i] : 0.f;
     return f;
 }
-__device__ __forceinline__ void route_finish(const float *gsh, float *zsh, const float *__restrict__ fc_w,
-                                             const float *__restrict__ fc_b, float *__restrict__ alpha,
-                                             int b, int C, int n, int mode, float temp, const FcPre &pre) {
+template <int NT = kRouteThreads>
+__device__ __forceinline__ void route_logits(const float *gsh, float *zsh, const float *__restrict__ fc_w,
+                                             const float *__restrict__ fc_b, int C, int n, const FcPre &pre) {
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
-    for (int i = wave; i < n; i += kRouteThreads / 64) {
+    for (int i = wave; i < n; i += NT / 64) {
         float part = 0.f;
         int c0 = 0;
         if (i == wave) {  // first expert of this wave: prefetched weights
@@ -223,7 +231,13 @@ __device__ __forceinline__ void route_finish(const float *gsh, float *zsh, const
         part = wave_sum(part);
         if (lane == 0) zsh[i] = part + (i == wave ? pre.bias : (fc_b ? fc_b[i] : 0.f));
     }
-    __syncthreads();
+}
+
+// The nonlinearity of router phase 3, in wave 0, from the logits in zsh
+// (after a barrier).
+__device__ __forceinline__ void route_activate(const float *zsh, float *__restrict__ alpha, int b, int n, int mode,
+                                               float temp) {
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     if (wave != 0) return;
     float z[kMaxJ];
 #pragma unroll
@@ -263,6 +277,16 @@ __device__ __forceinline__ void route_finish(const float *gsh, float *zsh, const
             if (i < n) alpha[(long)b * n + i] = e[j] / ssum;
         }
     }
+}
+
+
+template <int NT = kRouteThreads>
+__device__ __forceinline__ void route_finish(const float *gsh, float *zsh, const float *__restrict__ fc_w,
+                                             const float *__restrict__ fc_b, float *__restrict__ alpha,
+                                             int b, int C, int n, int mode, float temp, const FcPre &pre) {
+    route_logits<NT>(gsh, zsh, fc_w, fc_b, C, n, pre);
+    __syncthreads();
+    route_activate(zsh, alpha, b, n, mode, temp);
 }
 
 template <typename T, int VEC, int LPR>
@@ -348,6 +372,128 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused16_kernel(
     }
     __syncthreads();
     route_finish(gsh, zsh, fc_w, fc_b, alpha, b, C, n, mode, temp, pre);
+}
+
+// Split router for batches below kRouteSplitMaxB. The channel planes of
+// example b are pooled by S workgroups of 512 threads, one pass of 512 / LPR
+// planes each with every lane's loads in flight before its first add, so
+// that B * S workgroups spread the loads over the chip at B = 32 (one
+// workgroup per example would leave most CUs idle). Each workgroup stores its channel
+// means to the workspace and draws a ticket from the example's counter; the
+// one that draws ticket S - 1 holds the last piece, reads all of the
+// example's means back and finishes the FC and the nonlinearity exactly as
+// the one-workgroup router does (same fixed order of every sum), then puts
+// the counter back to zero for the next call. The ticket only decides which
+// workgroup finishes, so the result is deterministic. The means are written
+// and read back with device-scope atomic accesses (coherent across the XCDs'
+// separate L2 caches) and each workgroup takes its ticket only after its
+// means stores have completed, so the finishing workgroup, which reads them
+// after drawing the last ticket, sees every workgroup's means.
+template <typename T, int VEC, int LPR, bool EVEN16>
+__global__ __launch_bounds__(kSplitThreads) void route_split_kernel(
+    const T *__restrict__ x, const float *__restrict__ fc_w, const float *__restrict__ fc_b,
+    float *__restrict__ alpha, float *__restrict__ means, unsigned *__restrict__ tickets, int C, int hw, int n,
+    int mode, float temp, int S, int x_bytes) {
+    __shared__ float gsh[kRouteMaxC];
+    __shared__ float zsh[64 * kMaxJ];
+    __shared__ int is_last;
+    constexpr int kPlanes = kSplitThreads / LPR;  // planes per workgroup
+    const int b = blockIdx.x / S, part = blockIdx.x - b * S;
+    const int tid = threadIdx.x;
+    const int grp = tid / LPR, lane_in = tid % LPR;
+    const int c = part * kPlanes + grp;
+    const FcPre pre = route_prefetch_fc(fc_w, fc_b, C, n);
+    float s = 0.f;
+    if constexpr (EVEN16) {
+        // bf16 planes of an even size that is not a multiple of 8: 16-byte
+        // loads through a buffer descriptor (reads past the tensor return 0),
+        // elements past the plane left out of the sum
+        const int nvec = (hw + 7) / 8;
+        const int tail_words = (hw - 8 * (nvec - 1)) / 2;
+        const uint64_t q = reinterpret_cast<uint64_t>(x);
+        const uint64_t qs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)q) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(q >> 32)) << 32);
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(qs), 0,
+                                                          __builtin_amdgcn_readfirstlane(x_bytes), 0x00020000);
+        const int base = (((b * C) + min(c, C - 1)) * hw) * 2;  // bytes (x_bytes < 2^31)
+        u32x4_t v[kRouteMaxK16];
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK16; ++k)
+            v[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs, base + 16 * min(lane_in + LPR * k, nvec - 1), 0, 0));
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK16; ++k) {
+            const int vi = lane_in + LPR * k;
+            const int words = vi < nvec - 1 ? 4 : (vi == nvec - 1 ? tail_words : 0);
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t += j < words ? bf16_lo(w[j]) + bf16_hi(w[j]) : 0.f;
+            s += t;
+        }
+    } else {
+        const int nvec = hw / VEC;
+        using L = VecLoad<T, VEC>;
+        const typename L::V *pv =
+            reinterpret_cast<const typename L::V *>(x + ((long)b * C + min(c, C - 1)) * hw);
+        typename L::V q[kRouteMaxK];
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK; ++k) q[k] = pv[min(lane_in + LPR * k, nvec - 1)];
+#pragma unroll
+        for (int k = 0; k < kRouteMaxK; ++k) s += lane_in + LPR * k < nvec ? L::sum(q[k]) : 0.f;
+    }
+    s = group_sum<LPR>(s);
+    if (lane_in == 0 && c < C)
+        __hip_atomic_store(&means[(long)b * C + c], s / (float)hw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every wave waits until its means stores are complete at device scope
+    // before the barrier, so the ticket below is taken after all of them
+    // (a device-scope fence would instead write back and invalidate the
+    // whole L2 of the XCD, in every workgroup)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned t = __hip_atomic_fetch_add(&tickets[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = t == (unsigned)(S - 1);
+    }
+    __syncthreads();
+    if (!is_last) return;  // uniform over the workgroup
+    for (int i = tid; i < C; i += kSplitThreads)
+        gsh[i] = __hip_atomic_load(&means[(long)b * C + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&tickets[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    route_finish<kSplitThreads>(gsh, zsh, fc_w, fc_b, alpha, b, C, n, mode, temp, pre);
+}
+
+// lanes per plane for the split router: the fewest that keep a lane's loads
+// within its per-plane limit, or 0 when a plane needs more than 64 lanes
+int split_lpr(int nvec, int maxk) {
+    int lpr = 1;
+    while (lpr * maxk < nvec) lpr *= 2;
+    return lpr <= 64 ? lpr : 0;
+}
+
+template <typename T, int VEC, bool EVEN16>
+hipError_t launch_route_split_t(const T *x, const float *fc_w, const float *fc_b, float *alpha, float *means,
+                                unsigned *tickets, int B, int C, int hw, int n, int mode, float temp,
+                                hipStream_t s) {
+    const int nvec = EVEN16 ? (hw + 7) / 8 : hw / VEC;
+    const int lpr = split_lpr(nvec, EVEN16 ? kRouteMaxK16 : kRouteMaxK);
+    const int S = ceil_div(C, kSplitThreads / lpr);
+    const int x_bytes = EVEN16 ? (int)((long)B * C * hw * 2) : 0;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)(B * S)), dim3(kSplitThreads), 0, s, x, fc_w, fc_b, alpha, means,
+                           tickets, C, hw, n, mode, temp, S, x_bytes);
+        return hipGetLastError();
+    };
+    switch (lpr) {
+    case 1: return go(route_split_kernel<T, VEC, 1, EVEN16>);
+    case 2: return go(route_split_kernel<T, VEC, 2, EVEN16>);
+    case 4: return go(route_split_kernel<T, VEC, 4, EVEN16>);
+    case 8: return go(route_split_kernel<T, VEC, 8, EVEN16>);
+    case 16: return go(route_split_kernel<T, VEC, 16, EVEN16>);
+    case 32: return go(route_split_kernel<T, VEC, 32, EVEN16>);
+    default: return go(route_split_kernel<T, VEC, 64, EVEN16>);
+    }
 }
 
 hipError_t launch_route_fused16(const uint16_t *x, const float *fc_w, const float *fc_b, float *alpha, int B, int C,
@@ -547,17 +693,48 @@ __global__ __launch_bounds__(256) void route_heads_kernel(const float *__restric
 static_assert(kMaxJ * 64 >= 256, "route kernel covers n <= 256");
 static_assert(kHeadsEB * kHeadsCT == 4 * 256, "one 16-byte piece of channel means per thread and tile");
 
+namespace {
+
+// Load variant of the split router for this layer: 8 = 16-byte vectors of 8
+// bf16, 16 = 16-byte loads over even-sized bf16 planes, 4 / 1 = vectors of 4
+// or single elements (either dtype); 0 when a plane is too large for one
+// pass of at most 64 lanes.
+int split_variant(const Geom &g) {
+    const int hw = g.H * g.W;
+    if (g.bf16) {
+        if (hw % 8 == 0) return split_lpr(hw / 8, kRouteMaxK) ? 8 : 0;
+        if (hw % 2 == 0 && (long)g.B * g.Cin * hw * 2 < (1L << 31) - 64 && split_lpr((hw + 7) / 8, kRouteMaxK16))
+            return 16;
+    }
+    if (hw % 4 == 0) return split_lpr(hw / 4, kRouteMaxK) ? 4 : 0;
+    return split_lpr(hw, kRouteMaxK) ? 1 : 0;
+}
+
+bool route_split(const Geom &g) {
+    return g.B < kRouteSplitMaxB && g.Cin <= kRouteMaxC && split_variant(g) != 0;
+}
+
+}  // namespace
+
 bool route_single_kernel(const Geom &g) {
     // planes up to 64 lanes x kRouteMaxK vectors (bf16: 8192 elements with 16-byte loads)
-    return g.B >= kRouteMinB && g.Cin <= kRouteMaxC && g.H * g.W <= 64 * kRouteMaxK;
+    return g.B >= kRouteSplitMaxB && g.Cin <= kRouteMaxC && g.H * g.W <= 64 * kRouteMaxK;
+}
+
+size_t route_workspace_bytes(const Geom &g) {
+    if (route_single_kernel(g)) return 0;
+    const size_t means = (size_t)g.B * g.Cin * sizeof(float);
+    if (route_split(g)) return kRouteTicketBytes(g.B) + means;
+    return means;
 }
 
 hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const float *fc_b,
-                        int mode, float temperature, float *gap, float *alpha,
+                        int mode, float temperature, void *workspace, float *alpha,
                         hipStream_t stream) {
     const long rows = (long)g.B * g.Cin;
     const int hw = g.H * g.W;
     const float tp = mode == 1 ? temperature : 1.0f;
+    float *gap = static_cast<float *>(workspace);
     if (route_single_kernel(g)) {
         if (g.bf16) {
             const uint16_t *xb = static_cast<const uint16_t *>(x);
@@ -570,6 +747,22 @@ hipError_t launch_route(const Geom &g, const void *x, const float *fc_w, const f
         const float *xf = static_cast<const float *>(x);
         if (hw % 4 == 0) return launch_route_fused_vec<float, 4>(xf, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
         return launch_route_fused_vec<float, 1>(xf, fc_w, fc_b, alpha, g.B, g.Cin, hw, g.n, mode, tp, stream);
+    }
+    if (route_split(g)) {
+        // workspace: the tickets, then the channel means
+        unsigned *tickets = static_cast<unsigned *>(workspace);
+        float *means = reinterpret_cast<float *>(static_cast<char *>(workspace) + kRouteTicketBytes(g.B));
+        const int var = split_variant(g);
+        if (g.bf16) {
+            const uint16_t *xb = static_cast<const uint16_t *>(x);
+            if (var == 8) return launch_route_split_t<uint16_t, 8, false>(xb, fc_w, fc_b, alpha, means, tickets, g.B, g.Cin, hw, g.n, mode, tp, stream);
+            if (var == 16) return launch_route_split_t<uint16_t, 8, true>(xb, fc_w, fc_b, alpha, means, tickets, g.B, g.Cin, hw, g.n, mode, tp, stream);
+            if (var == 4) return launch_route_split_t<uint16_t, 4, false>(xb, fc_w, fc_b, alpha, means, tickets, g.B, g.Cin, hw, g.n, mode, tp, stream);
+            return launch_route_split_t<uint16_t, 1, false>(xb, fc_w, fc_b, alpha, means, tickets, g.B, g.Cin, hw, g.n, mode, tp, stream);
+        }
+        const float *xf = static_cast<const float *>(x);
+        if (var == 4) return launch_route_split_t<float, 4, false>(xf, fc_w, fc_b, alpha, means, tickets, g.B, g.Cin, hw, g.n, mode, tp, stream);
+        return launch_route_split_t<float, 1, false>(xf, fc_w, fc_b, alpha, means, tickets, g.B, g.Cin, hw, g.n, mode, tp, stream);
     }
     hipError_t e;
     if (g.bf16) {

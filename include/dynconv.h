@@ -103,10 +103,19 @@ typedef struct {
  * NULL for no bias, temperature > 0 (ignored for sigmoid), alpha [B,n]
  * float32 (written). workspace: device memory of at least
  * dynconv_route_workspace_bytes(desc) bytes (may be NULL when that is 0,
- * which is the case for batches large enough to route with one workgroup
- * per example);
- * its contents on entry do not matter and are clobbered. Only desc->B, Cin,
- * H, W, n and dtype are read. The result is deterministic: no atomics. */
+ * which is the case from 64 examples up, routed with one workgroup per
+ * example). Below 64 examples the workspace starts with one 32-bit ticket
+ * counter per example (the size rounded up to 256 bytes), followed by the
+ * B*Cin channel means: the counters MUST be zero when a workspace is first
+ * used (allocate it zero-filled, e.g. hipMemset once); every call leaves
+ * them zero again, so a workspace can be reused by later calls (also from a
+ * captured graph) without clearing. Two calls that run at the same time
+ * must not share a workspace. Planes too large for the one-launch routers
+ * (more than 8192 bf16 or 4096 float32 elements) use the workspace as
+ * B*Cin channel means only, whose contents on entry do not matter. Only
+ * desc->B, Cin, H, W, n and dtype are read. The result is deterministic:
+ * the counters only pick which workgroup finishes an example, and every sum
+ * runs in a fixed order. */
 dynconv_status_t dynconv_route(const dynconv_desc_t *desc, const void *x,
                                const float *fc_w, const float *fc_b,
                                int32_t mode, float temperature, float *alpha,

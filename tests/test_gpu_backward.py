@@ -311,7 +311,7 @@ def test_training_graph_replay_matches_eager(key, B):
     dx = torch.empty_like(x)
     ws_w = torch.empty(bd.dynconv_backward_weights_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(bd.dynconv_backward_data_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
-    ws_r = torch.empty(max(16, bd.dynconv_route_workspace_bytes(rdesc)), dtype=torch.uint8, device="cuda")
+    ws_r = torch.zeros(max(16, bd.dynconv_route_workspace_bytes(rdesc)), dtype=torch.uint8, device="cuda")
     ws_rb = torch.empty(bd.dynconv_route_backward_workspace_bytes(rdesc), dtype=torch.uint8, device="cuda")
 
     def step():

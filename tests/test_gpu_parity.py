@@ -82,7 +82,10 @@ def test_route_full_size(key):
 
 @pytest.mark.parametrize("shape", [(3, 5, 7, 9, 6), (2, 3, 1, 1, 300 // 2), (5, 33, 13, 11, 256),
                                    (1, 8, 56, 56, 17), (130, 7, 5, 3, 9), (128, 33, 8, 8, 40),
-                                   (200, 3, 14, 14, 256), (70, 6, 2, 6, 5), (64, 130, 14, 14, 3)])
+                                   (200, 3, 14, 14, 256), (70, 6, 2, 6, 5), (64, 130, 14, 14, 3),
+                                   (3, 1100, 3, 3, 4),     # split router: 3 workgroups per example
+                                   (2, 3, 100, 100, 5),    # planes too large for one pass: two kernels
+                                   (256, 9, 8, 8, 5), (257, 3, 7, 7, 3)])  # one workgroup per example
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_route_ragged(shape, dtype, mode):
@@ -98,6 +101,30 @@ def test_route_ragged(shape, dtype, mode):
     torch.cuda.synchronize()
     ref, _, _ = oracle.route(x, fc_w, fc_b, mode, 2.5)
     check(from_dev(a), ref, ALPHA_TOL, f"route ragged {shape}")
+
+
+@pytest.mark.parametrize("shape", [(32, 64, 56, 56, 4), (6, 40, 14, 14, 16), (5, 12, 9, 7, 3)])
+def test_route_workspace_reuse(shape):
+    """The split router's ticket counters go back to zero after each call:
+    consecutive calls on one zero-filled workspace, on different inputs, all
+    match the oracle, and the counters read zero afterwards."""
+    B, C, H, W, n = shape
+    rng = np.random.default_rng(B + C)
+    fc_w = rng.standard_normal((n, C), dtype=np.float32)
+    fc_b = rng.standard_normal((n,), dtype=np.float32)
+    desc = bd.make_desc(B, C, H, W, n=n, dtype=bd.DYNCONV_BF16)
+    nb = bd.dynconv_route_workspace_bytes(desc)
+    assert nb >= 256 + B * C * 4
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    fw, fb = to_dev(fc_w, "f32"), to_dev(fc_b, "f32")
+    for r in range(3):
+        x = inputs.bf16_round(rng.standard_normal((B, C, H, W), dtype=np.float32) + np.float32(0.1 * r))
+        say("route reuse", shape, r)
+        a = bd.dynconv_route(to_dev(x, "bf16"), fw, fb, r % 2, 2.0, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.route(x, fc_w, fc_b, r % 2, 2.0)
+        check(from_dev(a), ref, ALPHA_TOL, f"route reuse {shape} call {r}")
+        assert int(ws[: 4 * B].view(torch.int32).abs().sum().item()) == 0, "ticket counters not reset"
 
 
 def test_route_without_bias():
@@ -410,7 +437,7 @@ def test_graph_replay_matches_eager(key, B):
     packed = torch.empty(bd.dynconv_packed_experts_bytes(desc), dtype=torch.uint8, device="cuda")
     ws = torch.empty(max(bd.dynconv_forward_packed_workspace_bytes(desc, pol), 16), dtype=torch.uint8,
                      device="cuda")
-    rws = torch.empty(max(bd.dynconv_route_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
+    rws = torch.zeros(max(bd.dynconv_route_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
     y = torch.empty((B, L.Cout, L.Ho, L.Wo), dtype=torch.bfloat16, device="cuda")
 
     def step():
