@@ -93,13 +93,19 @@ __global__ __launch_bounds__(256) void conv_pm3w_kernel(const uint16_t *__restri
         for (int u = 0; u < 3; ++u) aoff[u][pb] = (q + u * a.ncols) * kQPos + 16 * lh;
     }
 
-    // ---- input staging: task k = channel quad k / per_g, staged row, column
-    // pair; 4 dword loads (one per channel, both positions), two 8-byte writes
+    // ---- input staging: task p = (channel octet p / per_g, staged row, column
+    // pair), taken by a pair of adjacent lanes: lane half h loads channels
+    // 4 h .. 4 h + 3 of the octet (4 dword loads, one per channel, both
+    // positions), the pair swaps one 8-byte half (DPP), and lane h writes the
+    // octet of position 2 kp + h as one 16-byte piece. The pieces of 8
+    // consecutive lanes (4 column pairs, 96 bytes apart) fall on distinct
+    // banks; as 8-byte writes of channel quads they met 4 to a bank.
     const uint16_t *xb = x + (long)b * a.x_bstride;
     const int HW = a.H * a.W, plane = HW * 2, pairs = a.W >> 1;
     const int nrows = max(1, h_hi - h_lo);
     const int per_g = nrows * pairs;
-    const int ntask = 4 * per_g;
+    const int npt = 2 * per_g;  // pair tasks per chunk
+    const int half = tid & 1;
     // (k + 0.5) * fl(1 / d) rounded down is k / d exactly in float32 for
     // k < 8192 and d <= 4096 (checked exhaustively), which the launch
     // conditions guarantee; it avoids integer division in the prologue.
@@ -107,11 +113,12 @@ __global__ __launch_bounds__(256) void conv_pm3w_kernel(const uint16_t *__restri
     int xsrc[XR], xdst[XR];
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
-        const int k = min(256 * i + tid, ntask - 1);
-        const int g4 = (int)(((float)k + 0.5f) * inv_g), rr = k - g4 * per_g;
+        // lanes past the last task repeat it (same data to the same place)
+        const int k = min(128 * i + (tid >> 1), npt - 1);
+        const int g8 = (int)(((float)k + 0.5f) * inv_g), rr = k - g8 * per_g;
         const int row = (int)(((float)rr + 0.5f) * inv_pairs), kp = rr - row * pairs;
-        xsrc[i] = 4 * g4 * plane + (row * a.W + 2 * kp) * 2;
-        xdst[i] = ((h_lo - h_tile0 + row) * a.ncols + 2 * kp + a.pad) * kQPos + 8 * g4;
+        xsrc[i] = (8 * g8 + 4 * half) * plane + (row * a.W + 2 * kp) * 2;
+        xdst[i] = ((h_lo - h_tile0 + row) * a.ncols + 2 * kp + a.pad + half) * kQPos + 16 * g8;
     }
     auto x_rsrc = [&](int c) {
         const int c0 = min(c * kQChunk, a.Cin - 1);
@@ -123,13 +130,18 @@ __global__ __launch_bounds__(256) void conv_pm3w_kernel(const uint16_t *__restri
         for (int j = 0; j < 4; ++j) r[i][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, xsrc[i] + j * plane, 0, 0);
     };
     auto x_store1 = [&](char *t, int i, const uint32_t (&r)[XR][4]) {
-        u32x2_t q0, q1;
-        q0.x = __builtin_amdgcn_perm(r[i][1], r[i][0], 0x05040100u);
-        q0.y = __builtin_amdgcn_perm(r[i][3], r[i][2], 0x05040100u);
-        q1.x = __builtin_amdgcn_perm(r[i][1], r[i][0], 0x07060302u);
-        q1.y = __builtin_amdgcn_perm(r[i][3], r[i][2], 0x07060302u);
-        *reinterpret_cast<u32x2_t *>(t + xdst[i]) = q0;
-        *reinterpret_cast<u32x2_t *>(t + xdst[i] + kQPos) = q1;
+        // q0: this lane's 4 channels at position 2 kp, q1: at 2 kp + 1
+        uint32_t q0x = __builtin_amdgcn_perm(r[i][1], r[i][0], 0x05040100u);
+        uint32_t q0y = __builtin_amdgcn_perm(r[i][3], r[i][2], 0x05040100u);
+        uint32_t q1x = __builtin_amdgcn_perm(r[i][1], r[i][0], 0x07060302u);
+        uint32_t q1y = __builtin_amdgcn_perm(r[i][3], r[i][2], 0x07060302u);
+        // the even lane sends its position-1 quad, the odd lane its
+        // position-0 quad (quad_perm [1, 0, 3, 2] swaps adjacent lanes)
+        const uint32_t sx = half ? q0x : q1x, sy = half ? q0y : q1y;
+        const uint32_t rx = (uint32_t)__builtin_amdgcn_mov_dpp((int)sx, 0xB1, 0xF, 0xF, false);
+        const uint32_t ry = (uint32_t)__builtin_amdgcn_mov_dpp((int)sy, 0xB1, 0xF, 0xF, false);
+        const u32x4_t o = half ? u32x4_t{rx, ry, q1x, q1y} : u32x4_t{q0x, q0y, rx, ry};
+        *reinterpret_cast<u32x4_t *>(t + xdst[i]) = o;
     };
     auto x_load = [&](__amdgpu_buffer_rsrc_t rs, uint32_t (&r)[XR][4]) {
 #pragma unroll
