@@ -211,25 +211,59 @@ __device__ __forceinline__ FcPre route_prefetch_fc(const float *__restrict__ fc_
     f.bias = fc_b ? fc_b[i] : 0.f;
     return f;
 }
+// Logits of one example (NT threads, the channel means in gsh). Wave w takes
+// experts w, w + NT / 64, ...: its first expert from the weights prefetched
+// before the pooling, the rest in batches of kLogitEB whose weights (up to
+// kLogitCB blocks of 64 channels each) are all loaded before the first
+// multiply, so one memory round trip serves a batch instead of one per
+// expert. Every logit sums c = lane + 64 j in ascending j, then the wave's
+// fixed butterfly, whatever the batching.
+constexpr int kLogitEB = 8;
+constexpr int kLogitCB = 2;
 template <int NT = kRouteThreads>
 __device__ __forceinline__ void route_logits(const float *gsh, float *zsh, const float *__restrict__ fc_w,
                                              const float *__restrict__ fc_b, int C, int n, const FcPre &pre) {
+    constexpr int NW = NT / 64;
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
-    for (int i = wave; i < n; i += NT / 64) {
+    if (wave < n) {  // first expert of this wave: prefetched weights
         float part = 0.f;
-        int c0 = 0;
-        if (i == wave) {  // first expert of this wave: prefetched weights
 #pragma unroll
-            for (int k = 0; k < kFcPre; ++k) {
-                const int c = lane + 64 * k;
-                if (c < C) part = fmaf(pre.w[k], gsh[c], part);
-            }
-            c0 = 64 * kFcPre;
+        for (int k = 0; k < kFcPre; ++k) {
+            const int c = lane + 64 * k;
+            if (c < C) part = fmaf(pre.w[k], gsh[c], part);
         }
-        for (int c = c0 + lane; c < C; c += 64) part = fmaf(fc_w[(long)i * C + c], gsh[c], part);
+        for (int c = 64 * kFcPre + lane; c < C; c += 64) part = fmaf(fc_w[(long)wave * C + c], gsh[c], part);
         part = wave_sum(part);
-        if (lane == 0) zsh[i] = part + (i == wave ? pre.bias : (fc_b ? fc_b[i] : 0.f));
+        if (lane == 0) zsh[wave] = part + pre.bias;
+    }
+    for (int i0 = wave + NW; i0 < n; i0 += kLogitEB * NW) {
+        float part[kLogitEB];
+#pragma unroll
+        for (int e = 0; e < kLogitEB; ++e) part[e] = 0.f;
+        for (int c0 = 0; c0 < C; c0 += 64 * kLogitCB) {
+            float wv[kLogitEB][kLogitCB];
+#pragma unroll
+            for (int e = 0; e < kLogitEB; ++e)
+#pragma unroll
+                for (int j = 0; j < kLogitCB; ++j)
+                    wv[e][j] = i0 + NW * e < n ? fc_w[(long)(i0 + NW * e) * C + min(c0 + lane + 64 * j, C - 1)] : 0.f;
+#pragma unroll
+            for (int e = 0; e < kLogitEB; ++e)
+#pragma unroll
+                for (int j = 0; j < kLogitCB; ++j) {
+                    const int c = c0 + lane + 64 * j;
+                    if (c < C) part[e] = fmaf(wv[e][j], gsh[c], part[e]);
+                }
+        }
+#pragma unroll
+        for (int e = 0; e < kLogitEB; ++e) {
+            const int i = i0 + NW * e;
+            if (i < n) {
+                const float t = wave_sum(part[e]);
+                if (lane == 0) zsh[i] = t + (fc_b ? fc_b[i] : 0.f);
+            }
+        }
     }
 }
 

@@ -84,6 +84,9 @@ def test_route_full_size(key):
                                    (1, 8, 56, 56, 17), (130, 7, 5, 3, 9), (128, 33, 8, 8, 40),
                                    (200, 3, 14, 14, 256), (70, 6, 2, 6, 5), (64, 130, 14, 14, 3),
                                    (3, 1100, 3, 3, 4),     # split router: 3 workgroups per example
+                                   (63, 96, 14, 14, 256),  # split router, 16-byte loads, n = 256
+                                   (1, 4096, 2, 2, 5),     # split router, Cin at its limit (8 workgroups)
+                                   (40, 3, 90, 90, 7),     # planes past one pass: two kernels
                                    (2, 3, 100, 100, 5),    # planes too large for one pass: two kernels
                                    (256, 9, 8, 8, 5), (257, 3, 7, 7, 3)])  # one workgroup per example
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
