@@ -399,12 +399,16 @@ __global__ __launch_bounds__(256) void conv_pm3_kernel(const uint16_t *__restric
 // 16-byte fragment piece per thread. Both load at the start of the previous
 // chunk and go to the other LDS buffer at its end; one barrier per chunk.
 // Outputs leave through LDS as 16-byte row stores.
-constexpr int kPm1Resident = 3;       // workgroups per CU (LDS: 3 x 41 KB)
+// CB blocks of 32 output channels per tile: 2 (64 channels) or 3 (96, for
+// layers such as the MBConv project layer's 80 channels, which then fit one
+// tile instead of two).
 constexpr int kCUs = 256;             // compute units of the MI355X
 constexpr int kPm1Tile = kPmMT * 32;  // bf16 per x tile buffer (32 channels x 256 positions)
-constexpr int kPm1LdsBytes = 64 * kPmOutPitch * 2 > 2 * kPm1Tile * 2 ? 64 * kPmOutPitch * 2 : 2 * kPm1Tile * 2;
-__shared__ __attribute__((aligned(16))) u32x4_t s_pm1x[kPm1LdsBytes / 16];  // 2 x 16 KB tiles, or the epilogue rows
-__shared__ __attribute__((aligned(16))) u32x4_t s_pm1w[2 * 4 * 64];        // 2 x 4 fragments
+constexpr int pm1_lds_bytes(int CB) {  // 2 x 16 KB tiles, or the epilogue rows
+    return 32 * CB * kPmOutPitch * 2 > 2 * kPm1Tile * 2 ? 32 * CB * kPmOutPitch * 2 : 2 * kPm1Tile * 2;
+}
+// workgroups per CU (LDS: 3 x 41 KB with 2 blocks, 2 x 63 KB with 3)
+constexpr int pm1_resident(int CB) { return CB == 2 ? 3 : 2; }
 
 // byte offset of position q of channel row c in a [32][256] tile: the
 // 16-byte pieces of rows 8..15 and 24..31 are XOR-swapped by 4 pieces, so
@@ -414,17 +418,21 @@ __device__ __forceinline__ int pm1_off(int c, int q) {
     return c * (kPmMT * 2) + ((((q >> 3) ^ (((c >> 3) & 1) << 2))) << 4) + ((q & 7) << 1);
 }
 
+template <int CB>
 __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restrict__ x,
                                                        const uint16_t *__restrict__ wt,
                                                        uint16_t *__restrict__ y, ConvArgs a,
                                                        const float *__restrict__ a_out) {
-    constexpr int CB = 2;
+    constexpr int NF = 2 * CB;             // W_b fragments per chunk (block, K half)
+    constexpr int NFW = (NF + 3) / 4;      // fragments staged per thread
+    __shared__ __attribute__((aligned(16))) u32x4_t s_pm1x[pm1_lds_bytes(CB) / 16];
+    __shared__ __attribute__((aligned(16))) u32x4_t s_pm1w[2 * NF * 64];
     constexpr int kLoads = 32 * kPmMT * 2 / 16 / 256;  // 16-byte x loads per thread per chunk (4)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
     auto xtile = [&](int par) { return reinterpret_cast<char *>(s_pm1x + par * (kPm1Tile / 8)); };
-    auto wslot = [&](int par, int f) { return s_pm1w + (par * 4 + f) * 64; };
+    auto wslot = [&](int par, int f) { return s_pm1w + (par * NF + f) * 64; };
     const int nchunks = a.Cin_pad / kChunk;
     const int plane = a.P * 2;  // bytes per channel plane (H W = P)
     // Persistent workgroups: tiles (example b, position tile pt, channel tile
@@ -447,19 +455,20 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
         const int rem = t - ti.b * per_b;
         const int pt = rem / a.n_otiles;
         ti.p0 = pt * kPmMT;
-        ti.o0 = (rem - pt * a.n_otiles) * 64;
+        ti.o0 = (rem - pt * a.n_otiles) * 32 * CB;
         ti.npos = min(kPmMT, a.P - ti.p0);
         return ti;
     };
     struct Stage {
         u32x4_t r[kLoads];
-        u32x4_t w;
+        u32x4_t w[NFW];
     };
     // Chunk c of tile ti. x: load u = 256 k + tid is piece u & 31 (8
     // positions) of channel row u >> 5; rows past Cin read as zeros, and
     // pieces at positions past the plane's end take an offset beyond the
     // buffer's extent (zeros, with no memory traffic). W: thread tid holds
-    // lane tid & 63 of fragment f = tid >> 6 (block f >> 1, K half f & 1).
+    // lane tid & 63 of fragments f = (tid >> 6) + 4 k (block f >> 1, K half
+    // f & 1) for f < NF.
     // (The descriptor's fields go through readfirstlane: scalar registers.)
     auto load = [&](const Tile &ti, int c, Stage &st) {
         const int cc = c * kChunk;
@@ -475,8 +484,12 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
             const int off = 8 * (u & 31) < ti.npos ? (u >> 5) * plane + ((u & 31) << 4) : 0x7ffffff0;
             st.r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
-        const long wrow = (long)min(ti.o0 + 32 * (wave >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (wave & 1) + 8 * lh;
-        st.w = *reinterpret_cast<const u32x4_t *>(wt + (long)ti.b * a.Cout * a.Cin_pad + wrow + cc);
+#pragma unroll
+        for (int k = 0; k < NFW; ++k) {
+            const int f = min(wave + 4 * k, NF - 1);
+            const long wrow = (long)min(ti.o0 + 32 * (f >> 1) + l32, a.Cout - 1) * a.Cin_pad + 16 * (f & 1) + 8 * lh;
+            st.w[k] = *reinterpret_cast<const u32x4_t *>(wt + (long)ti.b * a.Cout * a.Cin_pad + wrow + cc);
+        }
     };
     auto store = [&](int par, const Stage &st) {
         char *t = xtile(par);
@@ -485,7 +498,9 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
             const int u = 256 * k + tid;
             *reinterpret_cast<u32x4_t *>(t + pm1_off(u >> 5, (u & 31) << 3)) = st.r[k];
         }
-        wslot(par, wave)[lane] = st.w;
+#pragma unroll
+        for (int k = 0; k < NFW; ++k)
+            if (wave + 4 * k < NF) wslot(par, wave + 4 * k)[lane] = st.w[k];
     };
     // A fragment: position q, channels 8 g .. 8 g + 7 of the chunk
     auto afrag = [&](const char *t, int q, int g) {
@@ -568,7 +583,7 @@ __global__ __launch_bounds__(256) void conv_pm1_kernel(const uint16_t *__restric
                 }
         lds_barrier();
         constexpr int kRowVec = kPmMT / 8;
-        for (int v = tid; v < 64 * kRowVec; v += 256) {
+        for (int v = tid; v < 32 * CB * kRowVec; v += 256) {
             const int ch = v / kRowVec, cv = v - ch * kRowVec;
             const int o = ti.o0 + ch;
             if (o < a.Cout && 8 * cv < ti.npos)
@@ -814,14 +829,19 @@ hipError_t launch_conv_premix(const Geom &g, const uint16_t *x, const uint16_t *
         return hipGetLastError();
     }
     if (pm1_ok(g)) {
+        // tiles of 96 output channels where they pad less than tiles of 64
+        const bool cb3 = ceil_div(g.Cout, 96) * 96 < ceil_div(g.Cout, 64) * 64;
         ConvArgs a = base_args(g);
         a.n_ptiles = ceil_div(g.P, kPmMT);
-        a.n_otiles = ceil_div(g.Cout, 64);
-        // persistent: at most kPm1Resident workgroups per CU, a multiple of 8
+        a.n_otiles = ceil_div(g.Cout, cb3 ? 96 : 64);
+        // persistent: at most pm1_resident workgroups per CU, a multiple of 8
         const long tiles = (long)g.B * a.n_ptiles * a.n_otiles;
         const long blocks = std::min(ceil_div((int)std::min(tiles, (long)INT32_MAX - 8), 8) * 8L,
-                                     (long)kCUs * kPm1Resident);
-        hipLaunchKernelGGL(conv_pm1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
+                                     (long)kCUs * pm1_resident(cb3 ? 3 : 2));
+        if (cb3)
+            hipLaunchKernelGGL(conv_pm1_kernel<3>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
+        else
+            hipLaunchKernelGGL(conv_pm1_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, x, wt, y, a, att.out);
         return hipGetLastError();
     }
     if (pm3w_ok(g)) return launch_conv_pm3w(g, x, wt, y, stream, att.out);

@@ -293,6 +293,8 @@ RAGGED = [
     (2, 64, 130, 18, 16, (1, 1), 1, 0, 4),   # 1x1, Cin <= 64: three output tiles (tail 2), position tail 32
     (3, 20, 33, 10, 8, (1, 1), 1, 0, 3),     # 1x1, one partial chunk, odd Cout
     (3, 96, 40, 12, 12, (1, 1), 1, 0, 2),    # 1x1, three chunks (odd count) on the persistent path
+    (3, 96, 90, 12, 12, (1, 1), 1, 0, 3),    # 1x1 persistent path, one 96-channel tile (Cout tail 6)
+    (2, 80, 270, 9, 8, (1, 1), 1, 0, 2),     # 1x1, three 96-channel tiles, partial position tile
     # 3x3 pad-1 layers up to 14x14 with n <= 4 (the fused path's one-wave-per-example kernel)
     (1, 20, 70, 14, 12, (3, 3), 1, 1, 2),    # one example, 16-channel chunk tail, Cout tail, two experts
     (6, 256, 256, 14, 14, (3, 3), 1, 1, 1),  # one expert
