@@ -248,7 +248,7 @@ dynconv_status_t forward_impl(const dynconv_desc_t *desc, int32_t policy, const 
         uint16_t *wt = reinterpret_cast<uint16_t *>(ws + round_up(dynconv::wide_bank_bytes(g), kWsAlign));
         e = dynconv::launch_pack_wide(g, static_cast<const uint16_t *>(experts), bank, st);
         if (e != hipSuccess) return hip_status(e, "dynconv_forward wide pack launch");
-        e = dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st);
+        e = dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st, true);
         if (e != hipSuccess) return hip_status(e, "dynconv_forward wide mix launch");
         return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
                                                       static_cast<uint16_t *>(y), st),
@@ -338,7 +338,7 @@ dynconv_status_t sparse_from_bank(const dynconv::Geom &g, const void *x, const u
                                   const uint8_t *mask, int32_t residual, void *y, char *tail, hipStream_t st) {
     uint16_t *wt = reinterpret_cast<uint16_t *>(tail);
     int *idx = reinterpret_cast<int *>(tail + round_up(dynconv::premixed_bytes(g), kWsAlign));
-    const hipError_t e = wide(g) ? dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st)
+    const hipError_t e = wide(g) ? dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha, bank, wt, st, true)
                                  : dynconv::launch_premix(g, alpha, bank, wt, st);
     if (e != hipSuccess) return hip_status(e, "gated evaluation mix launch");
     return hip_status(dynconv::launch_conv_sparse(g, static_cast<const uint16_t *>(x), wt, mask, residual, idx,
@@ -634,7 +634,7 @@ dynconv_status_t dynconv_forward_packed(const dynconv_desc_t *desc, int32_t poli
         // many experts: W_b from the wide bank on the matrix cores, then the premix convolution
         uint16_t *wt = static_cast<uint16_t *>(workspace);
         hipError_t e = dynconv::launch_mix_wide(g, (long)g.KT * g.Cout * g.Cin_pad, alpha,
-                                                static_cast<const uint16_t *>(packed), wt, st);
+                                                static_cast<const uint16_t *>(packed), wt, st, true);
         if (e != hipSuccess) return hip_status(e, "dynconv_forward_packed wide mix launch");
         return hip_status(dynconv::launch_conv_premix(g, static_cast<const uint16_t *>(x), wt,
                                                       static_cast<uint16_t *>(y), st),

@@ -66,8 +66,9 @@ hipError_t launch_pack_experts(const Geom &g, const uint16_t *experts,
 // of n rows of wsize weights (wsize a multiple of 8), on the matrix cores
 // with the experts as the reduction dimension; any n.
 bool mix_wide_supported(long wsize);
+// conv_feed: the mix writes W_b for the premix convolution that runs next.
 hipError_t launch_mix_wide(const Geom &g, long wsize, const float *alpha, const uint16_t *experts, uint16_t *mixed,
-                           hipStream_t stream);
+                           hipStream_t stream, bool conv_feed = false);
 // The natural bank in the convolution's weight order, wide[i][t][o][cp]
 // (bf16, zeros for cp >= Cin): the forward's bank for n > 16.
 size_t wide_bank_bytes(const Geom &g);

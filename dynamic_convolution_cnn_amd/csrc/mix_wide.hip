@@ -257,12 +257,16 @@ __global__ __launch_bounds__(256) void pack_wide_kernel(const uint16_t *__restri
 bool mix_wide_supported(long wsize) { return wsize >= 8 && wsize % 8 == 0 && wsize < kWideMaxW; }
 
 hipError_t launch_mix_wide(const Geom &g, long wsize, const float *alpha, const uint16_t *experts, uint16_t *mixed,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool conv_feed) {
     if (!mix_wide_supported(wsize)) return hipErrorInvalidValue;
     const unsigned tiles = (unsigned)((wsize + kMixWW - 1) / kMixWW);
-    // 64 examples per workgroup only when the grid still has four workgroups per CU
+    // 64 examples per workgroup only when the grid still has four workgroups
+    // per CU; for the forward's mix (W_b in the premix layout, read by the
+    // convolution next) from two per CU: at n = 128, B = 64 that forward took
+    // 44.6-45.1 us back to back against 46.0-46.1 us with 32 examples, while
+    // the stand-alone mix lost (21.7-21.9 against 19.8 us)
     const bool a16 = g.n % 4 == 0 && reinterpret_cast<uintptr_t>(alpha) % 16 == 0;
-    const bool mt2 = g.B > 32 && (long)tiles * ceil_div(g.B, 64) >= 1024;
+    const bool mt2 = g.B > 32 && (long)tiles * ceil_div(g.B, 64) >= (conv_feed ? 512 : 1024);
     const dim3 grid(tiles, (unsigned)ceil_div(g.B, mt2 ? 64 : 32));
     // more register sets than one would cost MT = 2 its second wave per SIMD
     auto k = mt2 ? (a16 ? mix_mfma_wide_kernel<2, true, 1> : mix_mfma_wide_kernel<2, false, 1>)
