@@ -576,6 +576,76 @@ hipError_t launch_route_fused_vec(const T *x, const float *fc_w, const float *fc
     }
 }
 
+// The pooling kernel for bf16 planes of an even size that is not a multiple
+// of 8 (14 x 14): 16-byte loads through a buffer descriptor over x (the last
+// vector of a plane reads into the next plane, or past the tensor, where the
+// read returns 0; its elements past the plane are left out of the sum), LPR
+// lanes per plane with at most kGap16Loads loads each, all in flight before
+// the first add.
+constexpr int kGap16Loads = 4;
+template <int LPR>
+__global__ __launch_bounds__(kGapThreads) void gap16_kernel(const uint16_t *__restrict__ x, float *__restrict__ gap,
+                                                            long rows, int hw, int x_bytes) {
+    constexpr int kRowsPerBlock = kGapThreads / LPR;
+    const int lane_in = threadIdx.x % LPR;
+    const long row = (long)blockIdx.x * kRowsPerBlock + threadIdx.x / LPR;
+    const bool active = row < rows;
+    const long r = active ? row : rows - 1;
+    const int nvec = (hw + 7) / 8;
+    const int tail_words = (hw - 8 * (nvec - 1)) / 2;
+    const uint64_t q = reinterpret_cast<uint64_t>(x);
+    const uint64_t qs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)q) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(q >> 32)) << 32);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(qs), 0,
+                                                      __builtin_amdgcn_readfirstlane(x_bytes), 0x00020000);
+    const int base = (int)(r * hw * 2);  // bytes (x_bytes < 2^31)
+    u32x4_t v[kGap16Loads];
+#pragma unroll
+    for (int k = 0; k < kGap16Loads; ++k)
+        v[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rs, base + 16 * min(lane_in + LPR * k, nvec - 1), 0, 0));
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kGap16Loads; ++k) {
+        const int vi = lane_in + LPR * k;
+        const int words = vi < nvec - 1 ? 4 : (vi == nvec - 1 ? tail_words : 0);
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t += j < words ? bf16_lo(w[j]) + bf16_hi(w[j]) : 0.f;
+        s += t;
+    }
+    s = group_sum<LPR>(s);
+    if (active && lane_in == 0) gap[row] = s / (float)hw;
+}
+
+// lanes per plane for gap16_kernel, or 0 when a plane needs more than 64
+int gap16_lpr(int hw) {
+    const int nvec = (hw + 7) / 8;
+    int lpr = 1;
+    while (lpr * kGap16Loads < nvec) lpr *= 2;
+    return lpr <= 64 ? lpr : 0;
+}
+
+hipError_t launch_gap16(const uint16_t *x, float *gap, long rows, int hw, hipStream_t s) {
+    const int lpr = gap16_lpr(hw);
+    const int x_bytes = (int)(rows * hw * 2);
+    auto go = [&](auto kern, int l) {
+        const long blocks = (rows + (kGapThreads / l) - 1) / (kGapThreads / l);
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kGapThreads), 0, s, x, gap, rows, hw, x_bytes);
+        return hipGetLastError();
+    };
+    switch (lpr) {
+    case 1: return go(gap16_kernel<1>, 1);
+    case 2: return go(gap16_kernel<2>, 2);
+    case 4: return go(gap16_kernel<4>, 4);
+    case 8: return go(gap16_kernel<8>, 8);
+    case 16: return go(gap16_kernel<16>, 16);
+    case 32: return go(gap16_kernel<32>, 32);
+    default: return go(gap16_kernel<64>, 64);
+    }
+}
+
 template <typename T, int VEC>
 hipError_t launch_gap_vec(const T *x, float *gap, long rows, int hw, hipStream_t s) {
     const int nvec = hw / VEC;
@@ -822,6 +892,8 @@ hipError_t launch_gap(const Geom &g, const void *x, float *gap, hipStream_t stre
     if (g.bf16) {
         const uint16_t *xb = static_cast<const uint16_t *>(x);
         if (hw % 8 == 0) return launch_gap_vec<uint16_t, 8>(xb, gap, rows, hw, stream);
+        if (hw % 2 == 0 && gap16_lpr(hw) && rows * hw * 2 < (1L << 31) - 64)
+            return launch_gap16(xb, gap, rows, hw, stream);
         if (hw % 4 == 0) return launch_gap_vec<uint16_t, 4>(xb, gap, rows, hw, stream);
         return launch_gap_vec<uint16_t, 1>(xb, gap, rows, hw, stream);
     }
